@@ -1,0 +1,609 @@
+/*
+ * moe_oracle.c -- plain, slow CPU oracle of the routed-expert FFN.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the tests, the smoke check and the CPU
+ * baseline leg of the benchmark may load this library.  It shares no code,
+ * header, table or constant with the HIP library and never calls it.
+ *
+ * What it computes (one MoE layer, per token t):
+ *   router logits  l[t,e] = sum_i Wr[e,i] * x[t,i] (+ b[e])         fp64
+ *       (the router runs per layer on the resident input: Pulsar README,
+ *        'How the streaming works'; the router stays in VRAM: Strata summary,
+ *        three-tier offload paragraph)
+ *   top-k          the k experts first under the order (l desc, index asc)
+ *   gating         softmax over the selected k (Qwen-style softmax router,
+ *                  Pulsar README 'What it does today'), softmax over all E
+ *                  (variant), or sigmoid over the selected k renormalised
+ *                  (sigmoid-gated router with a shared expert, RRLab digest of
+ *                  Pulsar, section 2, Ornith-397B entry)
+ *   q8_K(x)        int8 per 256-block, fp32 scale, per-16 sums (activations
+ *                  quantised to q8_K before integer dots: Pulsar README,
+ *                  'Fidelity notes')
+ *   gate/up        g = Wg[e] xhat, u = Wu[e] xhat with the dequantised weights
+ *   SwiGLU         h = fl32(silu(g) * u)
+ *   down           y_p = Wd[e] q8_K(h)^
+ *   combine        y[t] = fl32(sum_slot w_slot y_p + s_t y_shared)
+ *                  (top-k of E plus an always-on shared expert: Pulsar README,
+ *                  model table)
+ *
+ * Floating point: everything after the integer codes is fp64 with sequential
+ * sums, except the three fp32 rounding points the method fixes: q8_K
+ * arithmetic, h and y.  Build with -O2 -fno-fast-math -ffp-contract=off.
+ *
+ * Block formats (exchange layout; the pages name the formats but print no
+ * byte layout, so this layout is the repository's own, little-endian):
+ *   q8_K  292 B : f32 d | i8 qs[256] | i16 bsums[16]
+ *   Q4_K  144 B : f16 d | f16 dmin | u8 sm[12] | u8 qs[128]
+ *                 sm = bit stream: 8 six-bit scales (bits 0..47) then 8 six-bit
+ *                 mins (bits 48..95); qs: byte 32g+i holds element 64g+i (low
+ *                 nibble) and 64g+32+i (high nibble); sub-blocks of 32
+ *                 w = d*sc_j*q - dmin*m_j
+ *   Q2_K   84 B : f16 d | f16 dmin | u8 sm[16] (low nibble sc_j, high m_j) |
+ *                 u8 qs[64]: byte 32h+i holds element 128h+32s+i in bits 2s..2s+1;
+ *                 sub-blocks of 16;  w = d*sc_j*q - dmin*m_j
+ *   Q6_K  210 B : f16 d | i8 sc[16] | u8 ql[128] | u8 qh[64]
+ *                 ql byte 64h+i: low 4 bits of element 128h+i (low nibble) and
+ *                 128h+64+i (high nibble); qh byte 32h+i: high 2 bits of element
+ *                 128h+32s+i in bits 2s..2s+1; sub-blocks of 16; w = d*sc_j*(q-32)
+ *   Q8_0   34 B : f16 d | i8 qs[32];  w = d*q
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+enum { F_Q4_K = 1, F_Q6_K = 2, F_Q2_K = 3, F_Q8_0 = 4 };
+enum { G_SOFTMAX_TOPK = 0, G_SOFTMAX_ALL = 1, G_SIGMOID_TOPK = 2 };
+
+/* ------------------------------------------------------------------ fp16 */
+
+/* IEEE binary16 to double, exact. */
+double orc_half_to_double(uint16_t h)
+{
+    int sign = (h >> 15) & 1;
+    int ex = (h >> 10) & 31;
+    int man = h & 1023;
+    double v;
+    if (ex == 0)
+        v = ldexp((double)man, -24);
+    else if (ex == 31)
+        v = man ? NAN : INFINITY;
+    else
+        v = ldexp((double)(1024 + man), ex - 25);
+    return sign ? -v : v;
+}
+
+static uint16_t rd16(const uint8_t* p) { return (uint16_t)(p[0] | (p[1] << 8)); }
+
+/* ----------------------------------------------------------- block codes */
+
+int orc_block_bytes(int fmt)
+{
+    switch (fmt) {
+    case F_Q4_K: return 144;
+    case F_Q6_K: return 210;
+    case F_Q2_K: return 84;
+    case F_Q8_0: return 34;
+    }
+    return 0;
+}
+
+int orc_block_weights(int fmt) { return fmt == F_Q8_0 ? 32 : 256; }
+
+/* Elements per sub-block: the unit that carries one scale (and min). */
+int orc_subblock(int fmt)
+{
+    switch (fmt) {
+    case F_Q4_K: return 32;
+    case F_Q6_K: return 16;
+    case F_Q2_K: return 16;
+    case F_Q8_0: return 32;
+    }
+    return 0;
+}
+
+/*
+ * Decode one block into integer codes.  q[] gets the quant code of every
+ * element (Q6_K: 0..63 before the -32 offset; Q8_0: signed), sc[]/m[] the
+ * per-sub-block scale and min codes (m = 0 where the format has none),
+ * d/dmin the fp16 super-scales as doubles.
+ */
+int orc_block_codes(int fmt, const uint8_t* b, double* d, double* dmin, int* sc, int* m, int* q)
+{
+    int i, j, g, h, s;
+    switch (fmt) {
+    case F_Q4_K: {
+        const uint8_t* sm = b + 4;
+        const uint8_t* qs = b + 16;
+        *d = orc_half_to_double(rd16(b));
+        *dmin = orc_half_to_double(rd16(b + 2));
+        for (j = 0; j < 8; j++) {
+            int vs = 0, vm = 0, bit;
+            for (bit = 0; bit < 6; bit++) {
+                int ns = 6 * j + bit, nm = 48 + 6 * j + bit;
+                vs |= ((sm[ns >> 3] >> (ns & 7)) & 1) << bit;
+                vm |= ((sm[nm >> 3] >> (nm & 7)) & 1) << bit;
+            }
+            sc[j] = vs;
+            m[j] = vm;
+        }
+        for (g = 0; g < 4; g++)
+            for (i = 0; i < 32; i++) {
+                q[64 * g + i] = qs[32 * g + i] & 15;
+                q[64 * g + 32 + i] = qs[32 * g + i] >> 4;
+            }
+        return 0;
+    }
+    case F_Q2_K: {
+        const uint8_t* sm = b + 4;
+        const uint8_t* qs = b + 20;
+        *d = orc_half_to_double(rd16(b));
+        *dmin = orc_half_to_double(rd16(b + 2));
+        for (j = 0; j < 16; j++) {
+            sc[j] = sm[j] & 15;
+            m[j] = sm[j] >> 4;
+        }
+        for (h = 0; h < 2; h++)
+            for (s = 0; s < 4; s++)
+                for (i = 0; i < 32; i++)
+                    q[128 * h + 32 * s + i] = (qs[32 * h + i] >> (2 * s)) & 3;
+        return 0;
+    }
+    case F_Q6_K: {
+        const uint8_t* scb = b + 2;
+        const uint8_t* ql = b + 18;
+        const uint8_t* qh = b + 146;
+        *d = orc_half_to_double(rd16(b));
+        *dmin = 0.0;
+        for (j = 0; j < 16; j++) {
+            sc[j] = (int)(int8_t)scb[j];
+            m[j] = 0;
+        }
+        for (h = 0; h < 2; h++)
+            for (i = 0; i < 64; i++) {
+                q[128 * h + i] = ql[64 * h + i] & 15;
+                q[128 * h + 64 + i] = ql[64 * h + i] >> 4;
+            }
+        for (h = 0; h < 2; h++)
+            for (s = 0; s < 4; s++)
+                for (i = 0; i < 32; i++)
+                    q[128 * h + 32 * s + i] |= ((qh[32 * h + i] >> (2 * s)) & 3) << 4;
+        return 0;
+    }
+    case F_Q8_0: {
+        *d = orc_half_to_double(rd16(b));
+        *dmin = 0.0;
+        sc[0] = 1;
+        m[0] = 0;
+        for (i = 0; i < 32; i++)
+            q[i] = (int)(int8_t)b[2 + i];
+        return 0;
+    }
+    }
+    return -1;
+}
+
+/* Dequantise one block to fp64 with the format's closed form. */
+static int dequant_block(int fmt, const uint8_t* b, double* out)
+{
+    double d, dmin;
+    int sc[16], m[16], q[256], i;
+    int nw = orc_block_weights(fmt), sb = orc_subblock(fmt);
+    if (orc_block_codes(fmt, b, &d, &dmin, sc, m, q))
+        return -1;
+    for (i = 0; i < nw; i++) {
+        int j = i / sb;
+        switch (fmt) {
+        case F_Q4_K:
+        case F_Q2_K: out[i] = d * (double)sc[j] * (double)q[i] - dmin * (double)m[j]; break;
+        case F_Q6_K: out[i] = d * (double)sc[j] * (double)(q[i] - 32); break;
+        case F_Q8_0: out[i] = d * (double)q[i]; break;
+        }
+    }
+    return 0;
+}
+
+/* Dequantise a row of `cols` weights (cols / block_weights blocks back to back). */
+int orc_dequant_row(int fmt, const uint8_t* row, int64_t cols, double* out)
+{
+    int bw = orc_block_weights(fmt), bb = orc_block_bytes(fmt);
+    int64_t b;
+    if (!bw || cols % bw)
+        return -1;
+    for (b = 0; b < cols / bw; b++)
+        if (dequant_block(fmt, row + b * bb, out + b * bw))
+            return -1;
+    return 0;
+}
+
+/* ------------------------------------------------------------------ q8_K */
+
+/*
+ * q8_K of one row (cols % 256 == 0), fp32 arithmetic, round half to even:
+ *   amax = max |x|; a block is all-zero if amax == 0 or 127/amax overflows;
+ *   otherwise id = fl32(127/amax), q = clamp(rint(fl32(x*id)), -127, 127),
+ *   d = fl32(amax/127), bsums[j] = sum of q over elements 16j..16j+15.
+ */
+void orc_quantize_q8K_row(const float* x, int64_t cols, uint8_t* out)
+{
+    int64_t b;
+    int i, j;
+    for (b = 0; b < cols / 256; b++) {
+        const float* xb = x + b * 256;
+        uint8_t* o = out + b * 292;
+        float amax = 0.0f, id, d;
+        int8_t qs[256];
+        int16_t bs[16];
+        for (i = 0; i < 256; i++) {
+            float a = fabsf(xb[i]);
+            if (a > amax)
+                amax = a;
+        }
+        id = (amax == 0.0f) ? 0.0f : 127.0f / amax;
+        if (amax == 0.0f || isinf(id)) {
+            memset(o, 0, 292);
+            continue;
+        }
+        d = amax / 127.0f;
+        for (i = 0; i < 256; i++) {
+            float v = rintf(xb[i] * id);
+            if (v > 127.0f) v = 127.0f;
+            if (v < -127.0f) v = -127.0f;
+            qs[i] = (int8_t)v;
+        }
+        for (j = 0; j < 16; j++) {
+            int s = 0;
+            for (i = 0; i < 16; i++)
+                s += qs[16 * j + i];
+            bs[j] = (int16_t)s;
+        }
+        memcpy(o, &d, 4);
+        memcpy(o + 4, qs, 256);
+        memcpy(o + 260, bs, 32);
+    }
+}
+
+void orc_quantize_q8K(const float* x, int64_t rows, int64_t cols, uint8_t* out)
+{
+    int64_t r;
+    for (r = 0; r < rows; r++)
+        orc_quantize_q8K_row(x + r * cols, cols, out + r * (cols / 256) * 292);
+}
+
+/* xhat = d * q per element, fp64. */
+void orc_dequant_q8K_row(const uint8_t* q8, int64_t cols, double* out)
+{
+    int64_t b;
+    int i;
+    for (b = 0; b < cols / 256; b++) {
+        float d;
+        memcpy(&d, q8 + b * 292, 4);
+        for (i = 0; i < 256; i++)
+            out[b * 256 + i] = (double)d * (double)(int8_t)q8[b * 292 + 4 + i];
+    }
+}
+
+/* ---------------------------------------------------------------- router */
+
+static const double* g_sort_key;
+static int cmp_rank(const void* a, const void* b)
+{
+    int ia = *(const int*)a, ib = *(const int*)b;
+    double la = g_sort_key[ia], lb = g_sort_key[ib];
+    if (la > lb) return -1;
+    if (la < lb) return 1;
+    return ia < ib ? -1 : (ia > ib);
+}
+
+/*
+ * Router for T tokens: logits (fp64, sequential sum, bias added last), the
+ * top-k ids in rank order and fp32 gate weights (computed in fp64, times
+ * `scale`, rounded once).  logits may be NULL.
+ */
+int orc_route(int64_t T, int64_t H, int64_t E, int k, int gating, double scale,
+              const float* x, const float* Wr, const float* bias,
+              double* logits, int32_t* ids, float* w)
+{
+    int64_t t;
+    if (k < 1 || k > E)
+        return -1;
+    double* l = (double*)malloc(sizeof(double) * E);
+    int* order = (int*)malloc(sizeof(int) * E);
+    for (t = 0; t < T; t++) {
+        int64_t e, i;
+        int s;
+        for (e = 0; e < E; e++) {
+            double acc = 0.0;
+            for (i = 0; i < H; i++)
+                acc += (double)Wr[e * H + i] * (double)x[t * H + i];
+            if (bias)
+                acc += (double)bias[e];
+            l[e] = acc;
+            if (logits)
+                logits[t * E + e] = acc;
+        }
+        for (e = 0; e < E; e++)
+            order[e] = (int)e;
+        g_sort_key = l;
+        qsort(order, (size_t)E, sizeof(int), cmp_rank);
+        for (s = 0; s < k; s++)
+            ids[t * k + s] = order[s];
+        if (gating == G_SOFTMAX_TOPK) {
+            double mx = l[order[0]], z = 0.0;
+            for (s = 0; s < k; s++)
+                z += exp(l[order[s]] - mx);
+            for (s = 0; s < k; s++)
+                w[t * k + s] = (float)(exp(l[order[s]] - mx) / z * scale);
+        } else if (gating == G_SOFTMAX_ALL) {
+            double mx = l[order[0]], z = 0.0;
+            for (e = 0; e < E; e++)
+                z += exp(l[e] - mx);
+            for (s = 0; s < k; s++)
+                w[t * k + s] = (float)(exp(l[order[s]] - mx) / z * scale);
+        } else if (gating == G_SIGMOID_TOPK) {
+            double z = 0.0;
+            for (s = 0; s < k; s++)
+                z += 1.0 / (1.0 + exp(-l[order[s]]));
+            for (s = 0; s < k; s++)
+                w[t * k + s] = (float)(1.0 / (1.0 + exp(-l[order[s]])) / z * scale);
+        } else {
+            free(l);
+            free(order);
+            return -1;
+        }
+    }
+    free(l);
+    free(order);
+    return 0;
+}
+
+/*
+ * Token x expert lists: offsets[e]..offsets[e+1] index `pairs`, which holds
+ * t*k+slot for every pair routed to e, in increasing t.  active[0] = number
+ * of experts with at least one pair, active[1..] = those experts ascending.
+ */
+void orc_lists(int64_t T, int k, int64_t E, const int32_t* ids,
+               int32_t* offsets, int32_t* pairs, int32_t* active)
+{
+    int64_t e, t, pos = 0, na = 0;
+    int s;
+    for (e = 0; e < E; e++) {
+        offsets[e] = (int32_t)pos;
+        for (t = 0; t < T; t++)
+            for (s = 0; s < k; s++)
+                if (ids[t * k + s] == e)
+                    pairs[pos++] = (int32_t)(t * k + s);
+        if (pos > offsets[e])
+            active[1 + na++] = (int32_t)e;
+    }
+    offsets[E] = (int32_t)pos;
+    active[0] = (int32_t)na;
+}
+
+/* ------------------------------------------------------------- integers */
+
+/*
+ * Exact int32 dot of each sub-block of each weight row with each q8_K row:
+ * out[n][r][j] = sum over sub-block j of (weight code) * q_x, where the weight
+ * code is q (Q4_K, Q2_K), q-32 (Q6_K) or the signed q (Q8_0).
+ */
+int orc_subdots(int fmt, const uint8_t* w, int64_t rows, int64_t cols,
+                const uint8_t* xq, int64_t n_x, int32_t* out)
+{
+    int bw = orc_block_weights(fmt), bb = orc_block_bytes(fmt), sbw = orc_subblock(fmt);
+    int64_t nsub = cols / sbw, nblk = cols / bw, n, r, b;
+    if (!bw || cols % 256)
+        return -1;
+    for (n = 0; n < n_x; n++)
+        for (r = 0; r < rows; r++)
+            for (b = 0; b < nblk; b++) {
+                double d, dmin;
+                int sc[16], m[16], q[256], i;
+                const uint8_t* blk = w + (r * nblk + b) * bb;
+                orc_block_codes(fmt, blk, &d, &dmin, sc, m, q);
+                for (i = 0; i < bw / sbw; i++) {
+                    int32_t acc = 0;
+                    int e;
+                    for (e = 0; e < sbw; e++) {
+                        int64_t col = b * bw + i * sbw + e;
+                        int code = (fmt == F_Q6_K) ? q[i * sbw + e] - 32 : q[i * sbw + e];
+                        int qx = (int8_t)xq[n * (cols / 256) * 292 + (col / 256) * 292 + 4 + col % 256];
+                        acc += code * qx;
+                    }
+                    out[(n * rows + r) * nsub + b * (bw / sbw) + i] = acc;
+                }
+            }
+    return 0;
+}
+
+/*
+ * The integer formulation of one row dot, summed per 256 super-block in fp64:
+ *   Q4_K/Q2_K: d_x * (d * sum_j sc_j isum_j - dmin * sum_j m_j bsum_j)
+ *   Q6_K:      d_x * d * sum_j sc_j isum_j
+ *   Q8_0:      d_x * sum_b d_b isum_b
+ * Used only to check that it equals the fp64 dequantised dot.
+ */
+double orc_dot_intform(int fmt, const uint8_t* wrow, int64_t cols, const uint8_t* xq)
+{
+    int64_t sb;
+    double total = 0.0;
+    for (sb = 0; sb < cols / 256; sb++) {
+        float dxf;
+        const uint8_t* xb = xq + sb * 292;
+        const int8_t* qx = (const int8_t*)(xb + 4);
+        int16_t bsums[16];
+        double dx;
+        memcpy(&dxf, xb, 4);
+        memcpy(bsums, xb + 260, 32);
+        dx = (double)dxf;
+        if (fmt == F_Q8_0) {
+            double acc = 0.0;
+            int b;
+            for (b = 0; b < 8; b++) {
+                double d, dmin;
+                int sc[1], m[1], q[32], e;
+                int32_t is = 0;
+                orc_block_codes(fmt, wrow + (sb * 8 + b) * 34, &d, &dmin, sc, m, q);
+                for (e = 0; e < 32; e++)
+                    is += q[e] * qx[b * 32 + e];
+                acc += d * (double)is;
+            }
+            total += dx * acc;
+        } else {
+            double d, dmin;
+            int sc[16], m[16], q[256], j, e;
+            int sbw = orc_subblock(fmt);
+            int64_t S1 = 0, S2 = 0;
+            orc_block_codes(fmt, wrow + sb * orc_block_bytes(fmt), &d, &dmin, sc, m, q);
+            for (j = 0; j < 256 / sbw; j++) {
+                int32_t is = 0, bs = 0;
+                for (e = 0; e < sbw; e++) {
+                    int code = (fmt == F_Q6_K) ? q[j * sbw + e] - 32 : q[j * sbw + e];
+                    is += code * qx[j * sbw + e];
+                }
+                for (e = 0; e < sbw / 16; e++)
+                    bs += bsums[j * sbw / 16 + e];
+                S1 += (int64_t)sc[j] * is;
+                S2 += (int64_t)m[j] * bs;
+            }
+            total += dx * (d * (double)S1 - dmin * (double)S2);
+        }
+    }
+    return total;
+}
+
+/* ------------------------------------------------------------------- FFN */
+
+/* out[r] = sum_c W[r,c] * v[c], fp64, sequential; W dequantised row by row. */
+static void matvec(int fmt, const uint8_t* W, int64_t rows, int64_t cols, const double* v,
+                   double* out, double* rowbuf)
+{
+    int64_t r, c;
+    int64_t rb = cols / orc_block_weights(fmt) * orc_block_bytes(fmt);
+    for (r = 0; r < rows; r++) {
+        double acc = 0.0;
+        orc_dequant_row(fmt, W + r * rb, cols, rowbuf);
+        for (c = 0; c < cols; c++)
+            acc += rowbuf[c] * v[c];
+        out[r] = acc;
+    }
+}
+
+int orc_matvec(int fmt, const uint8_t* W, int64_t rows, int64_t cols, const double* v, double* out)
+{
+    double* rowbuf = (double*)malloc(sizeof(double) * cols);
+    if (cols % orc_block_weights(fmt)) {
+        free(rowbuf);
+        return -1;
+    }
+    matvec(fmt, W, rows, cols, v, out, rowbuf);
+    free(rowbuf);
+    return 0;
+}
+
+static double silu64(double z) { return z / (1.0 + exp(-z)); }
+
+/*
+ * One expert on one token.  xhat: dequantised q8_K(x) [H].  Writes
+ * hq (q8_K(h), F/256 blocks), yp [H], and optionally g, u, h [F].
+ */
+static void expert_one(int64_t H, int64_t F, int fg, int fu, int fd,
+                       const uint8_t* Wg, const uint8_t* Wu, const uint8_t* Wd,
+                       const double* xhat, uint8_t* hq, double* yp,
+                       double* g_out, double* u_out, float* h_out)
+{
+    double* g = (double*)malloc(sizeof(double) * F);
+    double* u = (double*)malloc(sizeof(double) * F);
+    float* h = (float*)malloc(sizeof(float) * F);
+    double* hhat = (double*)malloc(sizeof(double) * F);
+    double* rowbuf = (double*)malloc(sizeof(double) * (H > F ? H : F));
+    int64_t f;
+    matvec(fg, Wg, F, H, xhat, g, rowbuf);
+    matvec(fu, Wu, F, H, xhat, u, rowbuf);
+    for (f = 0; f < F; f++)
+        h[f] = (float)(silu64(g[f]) * u[f]);
+    orc_quantize_q8K_row(h, F, hq);
+    orc_dequant_q8K_row(hq, F, hhat);
+    matvec(fd, Wd, H, F, hhat, yp, rowbuf);
+    if (g_out) memcpy(g_out, g, sizeof(double) * F);
+    if (u_out) memcpy(u_out, u, sizeof(double) * F);
+    if (h_out) memcpy(h_out, h, sizeof(float) * F);
+    free(g); free(u); free(h); free(hhat); free(rowbuf);
+}
+
+/*
+ * Expert FFN for the tokens listed in sel[0..n_sel).  Per selected token:
+ *   y[n,:]    fp32 [H]
+ *   hq[n, s]  q8_K(h) of slot s (s = k is the shared expert), F_s/256 blocks,
+ *             laid out with a stride of (Fmax/256)*292 bytes per slot; zero
+ *             for a slot whose expert is absent
+ *   g,u,h     (optional, may be NULL) [n, k+1, Fmax] diagnostics
+ * gate/up/down: host arrays [E] of AoS matrices; NULL = not resident (its
+ * pairs contribute nothing).  sh_*: shared expert or NULL.  shared_scale:
+ * [T] or NULL (= 1).  ids / w: the router's output [T, k].
+ */
+int orc_expert_ffn(int64_t T, int64_t H, int64_t F, int64_t E, int k,
+                   int fg, int fu, int fd,
+                   const uint8_t* const* gate, const uint8_t* const* up, const uint8_t* const* down,
+                   int64_t Fs, int sfg, int sfu, int sfd,
+                   const uint8_t* sh_gate, const uint8_t* sh_up, const uint8_t* sh_down,
+                   const float* x, const int32_t* ids, const float* w, const float* shared_scale,
+                   const int64_t* sel, int64_t n_sel,
+                   float* y, uint8_t* hq, double* g_diag, double* u_diag, float* h_diag)
+{
+    int64_t n;
+    int64_t Fmax = (sh_gate && Fs > F) ? Fs : F;
+    int64_t hq_stride = Fmax / 256 * 292;
+    (void)E;
+    if (H % 256 || F % 256 || (sh_gate && Fs % 256))
+        return -1;
+    for (n = 0; n < n_sel; n++)
+        if (sel[n] < 0 || sel[n] >= T)
+            return -1;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (n = 0; n < n_sel; n++) {
+        int64_t t = sel[n], i;
+        int s;
+        uint8_t* xq = (uint8_t*)malloc((size_t)(H / 256 * 292));
+        double* xhat = (double*)malloc(sizeof(double) * H);
+        double* acc = (double*)calloc((size_t)H, sizeof(double));
+        double* yp = (double*)malloc(sizeof(double) * H);
+        orc_quantize_q8K_row(x + t * H, H, xq);
+        orc_dequant_q8K_row(xq, H, xhat);
+        for (s = 0; s <= k; s++) {
+            int64_t slot_base = (n * (k + 1) + s);
+            uint8_t* hqs = hq ? hq + slot_base * hq_stride : NULL;
+            uint8_t* tmp_hq = (uint8_t*)calloc((size_t)hq_stride, 1);
+            double* gd = g_diag ? g_diag + slot_base * Fmax : NULL;
+            double* ud = u_diag ? u_diag + slot_base * Fmax : NULL;
+            float* hd = h_diag ? h_diag + slot_base * Fmax : NULL;
+            double wt;
+            if (s < k) {
+                int e = ids[t * k + s];
+                if (!gate[e] || !up[e] || !down[e]) {
+                    if (hqs) memset(hqs, 0, (size_t)hq_stride);
+                    free(tmp_hq);
+                    continue;
+                }
+                expert_one(H, F, fg, fu, fd, gate[e], up[e], down[e], xhat, tmp_hq, yp, gd, ud, hd);
+                wt = (double)w[t * k + s];
+            } else {
+                if (!sh_gate || !sh_up || !sh_down) {
+                    if (hqs) memset(hqs, 0, (size_t)hq_stride);
+                    free(tmp_hq);
+                    continue;
+                }
+                expert_one(H, Fs, sfg, sfu, sfd, sh_gate, sh_up, sh_down, xhat, tmp_hq, yp, gd, ud, hd);
+                wt = shared_scale ? (double)shared_scale[t] : 1.0;
+            }
+            for (i = 0; i < H; i++)
+                acc[i] += wt * yp[i];
+            if (hqs) memcpy(hqs, tmp_hq, (size_t)hq_stride);
+            free(tmp_hq);
+        }
+        for (i = 0; i < H; i++)
+            y[n * H + i] = (float)acc[i];
+        free(xq); free(xhat); free(acc); free(yp);
+    }
+    return 0;
+}

@@ -1,0 +1,72 @@
+"""Test-side encoder: integer codes -> exchange-format block bytes.
+
+Written from the block layout independently of the oracle's decoder, so a
+round trip (encode here, decode in the oracle) checks the decoder against the
+layout, and hand-built special blocks (unit scales, zero mins) can be made.
+Layouts (little-endian):
+  Q4_K 144 B: f16 d, f16 dmin, 12 B bit stream (eight 6-bit scales, then eight
+              6-bit mins), 128 B quants: byte 32g+i = element 64g+i | element 64g+32+i << 4
+  Q2_K  84 B: f16 d, f16 dmin, 16 B (sc | m << 4), 64 B quants:
+              byte 32h+i bits 2s..2s+1 = element 128h+32s+i
+  Q6_K 210 B: f16 d, 16 x int8 scales, 128 B low nibbles
+              (byte 64h+i = lo(128h+i) | lo(128h+64+i) << 4), 64 B high pairs
+              (byte 32h+i bits 2s..2s+1 = hi(128h+32s+i))
+  Q8_0  34 B: f16 d, 32 x int8
+"""
+import numpy as np
+
+Q4_K, Q6_K, Q2_K, Q8_0 = 1, 2, 3, 4
+
+
+def f16_bytes(v: float) -> bytes:
+    return np.array([v], dtype=np.float16).tobytes()
+
+
+def pack_q4k(d, dmin, sc, m, q) -> bytes:
+    assert len(sc) == 8 and len(m) == 8 and len(q) == 256
+    bits = 0
+    for j in range(8):
+        bits |= (int(sc[j]) & 63) << (6 * j)
+        bits |= (int(m[j]) & 63) << (48 + 6 * j)
+    sm = bits.to_bytes(12, "little")
+    qs = bytearray(128)
+    for g in range(4):
+        for i in range(32):
+            qs[32 * g + i] = (int(q[64 * g + i]) & 15) | ((int(q[64 * g + 32 + i]) & 15) << 4)
+    return f16_bytes(d) + f16_bytes(dmin) + sm + bytes(qs)
+
+
+def pack_q2k(d, dmin, sc, m, q) -> bytes:
+    assert len(sc) == 16 and len(m) == 16 and len(q) == 256
+    sm = bytes(((int(sc[j]) & 15) | ((int(m[j]) & 15) << 4)) for j in range(16))
+    qs = bytearray(64)
+    for h in range(2):
+        for s in range(4):
+            for i in range(32):
+                qs[32 * h + i] |= (int(q[128 * h + 32 * s + i]) & 3) << (2 * s)
+    return f16_bytes(d) + f16_bytes(dmin) + sm + bytes(qs)
+
+
+def pack_q6k(d, sc, q) -> bytes:
+    assert len(sc) == 16 and len(q) == 256
+    scb = np.array(sc, dtype=np.int8).tobytes()
+    ql = bytearray(128)
+    qh = bytearray(64)
+    for h in range(2):
+        for i in range(64):
+            ql[64 * h + i] = (int(q[128 * h + i]) & 15) | ((int(q[128 * h + 64 + i]) & 15) << 4)
+        for s in range(4):
+            for i in range(32):
+                qh[32 * h + i] |= ((int(q[128 * h + 32 * s + i]) >> 4) & 3) << (2 * s)
+    return f16_bytes(d) + scb + bytes(ql) + bytes(qh)
+
+
+def pack_q80(d, q) -> bytes:
+    assert len(q) == 32
+    return f16_bytes(d) + np.array(q, dtype=np.int8).tobytes()
+
+
+def pack_row(fmt, blocks) -> np.ndarray:
+    """blocks: list of per-block argument tuples for the format's packer."""
+    fn = {Q4_K: pack_q4k, Q2_K: pack_q2k, Q6_K: pack_q6k, Q8_0: pack_q80}[fmt]
+    return np.frombuffer(b"".join(fn(*b) for b in blocks), dtype=np.uint8).copy()
