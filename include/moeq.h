@@ -1,0 +1,204 @@
+/*
+ * moeq.h -- C ABI of libmoeq.so: the routed-expert FFN of one MoE layer on an
+ * AMD MI355X (gfx950), over quantised expert weights resident in HBM.
+ *
+ * The path (router -> top-k gating -> q8_K activations -> dequant-dot gate/up
+ * -> SwiGLU -> q8_K(h) -> dequant-dot down -> gate-weighted sum with a shared
+ * expert) is the per-layer MoE step of the SSD/RAM-tiered engines on the
+ * pages; here every expert of the layer sits in device memory, so the
+ * streaming tiers are not part of it.
+ *
+ * Conventions for every entry point:
+ *   - Pointers are device memory unless marked (host).  `stream` is a
+ *     hipStream_t (NULL = the null stream).  Work is enqueued asynchronously
+ *     on `stream`; nothing synchronises, allocates device memory, or reads the
+ *     environment.  Calls that take a workspace use only that workspace for
+ *     scratch; concurrent calls must not share one.
+ *   - The caller owns every buffer; nothing is retained after the call.
+ *   - Return value: MOEQ_OK (0) or a negative moeq_status.  All argument
+ *     checks (sizes, NULLs, alignment, workspace size, supported formats)
+ *     happen on the host before anything is enqueued; a failed check leaves
+ *     the outputs untouched.  MOEQ_E_HIP means a launch failed.
+ *   - Integer outputs (q8_K bytes, ids, lists, sub-block dots) are
+ *     deterministic.  Floating outputs are deterministic for a given input
+ *     and launch shape.
+ *   - Inputs must be finite.
+ *
+ * Block formats.  The pages name the formats (Pulsar README, 'Get a model':
+ * q2_K, q4_K, q6_K expert tensors, dense tensors requantised to q8_0;
+ * 'Fidelity notes': activations quantised to q8_K with integer dots) but print
+ * no byte layout, so the exchange layout is this library's own (little-endian):
+ *   q8_K  292 B / 256 : f32 d | i8 q[256] | i16 bsums[16]          x ~ d*q
+ *   Q4_K  144 B / 256 : f16 d | f16 dmin | 12 B six-bit scales then mins
+ *                       (bit stream) | 128 B quants (byte 32g+i = element
+ *                       64g+i low nibble, 64g+32+i high nibble)
+ *                                                      w = d*sc_j*q - dmin*m_j
+ *   Q2_K   84 B / 256 : f16 d | f16 dmin | 16 B (sc_j | m_j << 4) | 64 B quants
+ *                       (byte 32h+i bits 2s..2s+1 = element 128h+32s+i)
+ *                                                      w = d*sc_j*q - dmin*m_j
+ *   Q6_K  210 B / 256 : f16 d | i8 sc[16] | 128 B low nibbles (byte 64h+i =
+ *                       element 128h+i low, 128h+64+i high) | 64 B high pairs
+ *                       (byte 32h+i bits 2s..2s+1 = element 128h+32s+i)
+ *                                                      w = d*sc_j*(q-32)
+ *   Q8_0   34 B /  32 : f16 d | i8 q[32]                w = d*q
+ * A matrix [rows, cols] is rows of blocks back to back.  Kernels read a
+ * repacked ("packed") form made once by moeq_pack_experts.
+ */
+#ifndef MOEQ_H
+#define MOEQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    MOEQ_OK = 0,
+    MOEQ_E_INVALID = -1,      /* bad size, NULL pointer, misalignment */
+    MOEQ_E_UNSUPPORTED = -2,  /* format / gating / path / shape not supported */
+    MOEQ_E_WORKSPACE = -3,    /* workspace smaller than the query returns */
+    MOEQ_E_HIP = -4           /* a HIP launch or API call failed */
+} moeq_status;
+
+typedef enum { MOEQ_Q4_K = 1, MOEQ_Q6_K = 2, MOEQ_Q2_K = 3, MOEQ_Q8_0 = 4 } moeq_wfmt;
+
+typedef enum {
+    MOEQ_SOFTMAX_TOPK = 0,   /* softmax over the k selected logits */
+    MOEQ_SOFTMAX_ALL = 1,    /* softmax over all E logits, not renormalised */
+    MOEQ_SIGMOID_TOPK = 2    /* sigmoid of the k selected, divided by their sum */
+} moeq_gating;
+
+typedef enum { MOEQ_PATH_AUTO = 0, MOEQ_PATH_GEMV = 1, MOEQ_PATH_MFMA = 2 } moeq_path;
+
+/* Human-readable name of a status code (host, static string). */
+const char* moeq_status_string(int status);
+
+/*
+ * q8_K quantisation of activation rows (Pulsar README, 'Fidelity notes':
+ * activations go to q8_K before integer dots).  x: fp32 [rows, cols],
+ * row-major, 4-byte aligned; cols % 256 == 0.  out: rows * cols/256 blocks of
+ * 292 B, 4-byte aligned.  Per 256-block, in fp32 with round-half-even:
+ * amax = max|x|; if amax == 0 or 127/amax overflows the block is all zero;
+ * else id = 127/amax, q = clamp(rint(x*id), -127, 127), d = amax/127,
+ * bsums[j] = sum of q[16j..16j+15].  rows == 0 is a no-op.
+ */
+int moeq_quantize_q8K(const float* x, int64_t rows, int64_t cols, void* out, void* stream);
+
+/* Router descriptor.  1 <= k <= min(E, 32); E <= 4096; H % 4 == 0. */
+typedef struct {
+    int64_t T, H, E;
+    int32_t k;
+    int32_t gating;   /* moeq_gating */
+    float scale;      /* multiplies every gate weight (1.0 for plain gating) */
+} moeq_route_desc;
+
+/* Workspace bytes moeq_route needs for this descriptor (host). */
+size_t moeq_route_workspace(const moeq_route_desc* d);
+
+/*
+ * Router, top-k gating and token x expert lists for T tokens (the router runs
+ * per layer on device: Pulsar README, 'How the streaming works'; one expert
+ * union per chunk-layer: Pulsar README, DeepSeek-V4-Flash paragraph; the
+ * softmax router of Qwen3 MoE models and the sigmoid router with a shared
+ * expert: Pulsar README, 'What it does today', RRLab digest of Pulsar,
+ * section 2).
+ *   x        fp32 [T, H]        w_router fp32 [E, H]      bias fp32 [E] or NULL
+ *   logits   fp64 [T, E] or NULL: l = sum_i w_router[e,i]*x[t,i] (+ bias[e]),
+ *            accumulated in fp64
+ *   topk_ids int32 [T, k]: the k experts first under (l desc, index asc), in
+ *            that order (ties go to the lower index)
+ *   topk_w   fp32 [T, k]: gate weights (computed in fp64, times scale)
+ *   expert_offsets int32 [E+1], pairs int32 [T*k]: pairs[offsets[e] ..
+ *            offsets[e+1]) holds t*k+slot for every pair routed to e, t rising
+ *   active   int32 [1 + min(E, T*k)]: active[0] = n experts with a pair,
+ *            active[1..n] = those experts, ascending (the expert union)
+ * T == 0 writes offsets = 0 and active[0] = 0.  ws: moeq_route_workspace bytes,
+ * 256-byte aligned.
+ */
+int moeq_route(const moeq_route_desc* d, const float* x, const float* w_router, const float* bias,
+               double* logits, int32_t* topk_ids, float* topk_w, int32_t* expert_offsets,
+               int32_t* pairs, int32_t* active, void* ws, size_t ws_bytes, void* stream);
+
+/* Bytes of one packed [rows, cols] matrix of format fmt (0 if unsupported). */
+size_t moeq_packed_bytes(int32_t fmt, int64_t rows, int64_t cols);
+
+/*
+ * One-time repack of n_mats exchange-format matrices [rows, cols] (stored
+ * back to back in `aos`, any alignment) into the kernels' packed form
+ * (n_mats * moeq_packed_bytes, back to back, 256-byte aligned).  cols % 256 == 0.
+ */
+int moeq_pack_experts(int32_t fmt, const void* aos, int64_t n_mats, int64_t rows, int64_t cols,
+                      void* packed, void* stream);
+
+/*
+ * FFN descriptor.  gate/up: [F, H] per expert, down: [H, F]; H, F % 256 == 0.
+ * gate, up, down: device arrays of E pointers to packed matrices; a NULL entry
+ * means the expert is not resident in this call, so its pairs add nothing
+ * (each launch gets explicit per-expert pointers and a NULL slot means "not
+ * mine": Pulsar README, 'How the streaming works').  fmt_gate must equal
+ * fmt_up.  sh_*: packed shared-expert matrices ([F_shared, H] / [H, F_shared])
+ * or all NULL for no shared expert (top-k plus an always-on shared expert:
+ * Pulsar README model table).
+ */
+typedef struct {
+    int64_t T, H, F, E;
+    int32_t k;
+    int32_t fmt_gate, fmt_up, fmt_down;
+    const void* const* gate;
+    const void* const* up;
+    const void* const* down;
+    int64_t F_shared;
+    int32_t sh_fmt_gate, sh_fmt_up, sh_fmt_down;
+    const void* sh_gate;
+    const void* sh_up;
+    const void* sh_down;
+    int32_t path;        /* moeq_path */
+    int32_t accumulate;  /* 0: y = result, 1: y += result */
+} moeq_ffn_desc;
+
+/* Workspace bytes moeq_expert_ffn needs for this descriptor (host). */
+size_t moeq_expert_ffn_workspace(const moeq_ffn_desc* d);
+
+/*
+ * Routed-expert FFN over the token x expert lists from moeq_route.
+ *   x_q8K   q8_K rows of x [T, H/256 blocks]
+ *   topk_w  fp32 [T, k]; expert_offsets, pairs, active as moeq_route writes them
+ *   shared_scale fp32 [T] or NULL (= 1.0 per token)
+ *   y       fp32 [T, H]:  y[t] (=|+=) sum_slot topk_w[t,slot] * down_e(q8K(h))
+ *                                    + shared_scale[t] * down_sh(q8K(h_sh))
+ *           with h = fl32(silu(g) * u), g = gate_e . xhat, u = up_e . xhat;
+ *           per-super-block integer dots combined in fp64, sums in fp64,
+ *           y rounded to fp32 once.
+ * ws: moeq_expert_ffn_workspace bytes, 256-byte aligned; contents on entry
+ * are ignored.
+ */
+int moeq_expert_ffn(const moeq_ffn_desc* d, const void* x_q8K, const float* topk_w,
+                    const int32_t* expert_offsets, const int32_t* pairs, const int32_t* active,
+                    const float* shared_scale, float* y, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Where a finished moeq_expert_ffn call left q8_K(h) inside `ws` (host
+ * arithmetic only).  *hq_routed: [T*k] rows of F/256 blocks, row p = pair
+ * t*k+slot (rows of absent experts are unspecified); *hq_shared: [T] rows of
+ * F_shared/256 blocks, or NULL without a shared expert.
+ */
+int moeq_ffn_h_view(const moeq_ffn_desc* d, void* ws, size_t ws_bytes, void** hq_routed,
+                    void** hq_shared);
+
+/*
+ * Test hook: the exact int32 sub-block dots of a packed matrix with q8_K rows,
+ * computed by the same device dot routines the FFN uses.
+ *   packed_w [rows, cols] packed fmt; x_q8K [n_x, cols/256 blocks]
+ *   out int32 [n_x, rows, cols/sub]: sum over sub-block j of code * q_x, where
+ *   sub = 32 (Q4_K, Q8_0) or 16 (Q2_K, Q6_K) and code = q (Q4_K, Q2_K),
+ *   q-32 (Q6_K), signed q (Q8_0).
+ */
+int moeq_debug_subdots(int32_t fmt, const void* packed_w, int64_t rows, int64_t cols,
+                       const void* x_q8K, int64_t n_x, int32_t* out, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOEQ_H */

@@ -1,0 +1,252 @@
+// C ABI of libmoeq: argument validation on the host, workspace layout, and
+// kernel dispatch.  Every check runs before anything is enqueued.
+#include <algorithm>
+
+#include "../../include/moeq.h"
+#include "formats.hpp"
+#include "launch.hpp"
+
+using namespace moeq;
+
+namespace {
+
+constexpr int64_t kMaxE = 4096;
+constexpr int kMaxK = 32;
+constexpr int kRowBlock = 64;     // rows per down work item (= combine block)
+
+bool fmt_ok(int f) { return f == MOEQ_Q4_K || f == MOEQ_Q6_K || f == MOEQ_Q2_K || f == MOEQ_Q8_0; }
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+int hip_status(int rc) { return rc == 0 ? MOEQ_OK : (rc == -2 ? MOEQ_E_UNSUPPORTED : MOEQ_E_HIP); }
+
+int next_pow2(int v) {
+  int p = 1;
+  while (p < v) p <<= 1;
+  return p;
+}
+
+// Lane geometry of a GEMV over matrices with `cols` columns in format fmt.
+struct LaneGeo {
+  int cpr, lpr, rps, cpl;
+};
+bool lane_geo(int fmt, int64_t cols, LaneGeo* g) {
+  const int wpc = geo_of(fmt).wpc;
+  const int64_t cpr = cols / wpc;
+  if (cpr < 1 || cpr > 256) return false;
+  g->cpr = (int)cpr;
+  if (cpr <= 64) {
+    g->lpr = next_pow2((int)cpr);
+    g->cpl = 1;
+  } else {
+    g->lpr = 64;
+    g->cpl = cpr <= 128 ? 2 : 4;
+  }
+  g->rps = 64 / g->lpr;
+  return true;
+}
+
+struct FfnLayout {
+  int64_t Fmax, nrows;
+  size_t off_h, off_yp, off_hq, off_hqs, off_cnt, total;
+};
+FfnLayout ffn_layout(const moeq_ffn_desc* d) {
+  FfnLayout L{};
+  const bool sh = d->sh_gate != nullptr;
+  L.Fmax = sh ? std::max(d->F, d->F_shared) : d->F;
+  L.nrows = d->T * d->k + d->T;
+  size_t o = 0;
+  L.off_h = o;   o += align256((size_t)L.nrows * L.Fmax * sizeof(float));
+  L.off_yp = o;  o += align256((size_t)L.nrows * d->H * sizeof(double));
+  L.off_hq = o;  o += align256((size_t)d->T * d->k * (d->F / 256) * kQ8KBytes);
+  L.off_hqs = o; o += align256(sh ? (size_t)d->T * (d->F_shared / 256) * kQ8KBytes : 0);
+  L.off_cnt = o; o += align256((size_t)(d->H / kRowBlock + 1) * sizeof(int32_t));
+  L.total = o;
+  return L;
+}
+
+int check_ffn_desc(const moeq_ffn_desc* d) {
+  if (!d) return MOEQ_E_INVALID;
+  if (d->T < 0 || d->H <= 0 || d->F <= 0 || d->E < 1 || d->E > kMaxE) return MOEQ_E_INVALID;
+  if (d->H % 256 || d->F % 256) return MOEQ_E_INVALID;
+  if (d->k < 1 || d->k > kMaxK || d->k > d->E) return MOEQ_E_INVALID;
+  if (d->T * d->k > INT32_MAX / 2) return MOEQ_E_INVALID;
+  if (!fmt_ok(d->fmt_gate) || !fmt_ok(d->fmt_up) || !fmt_ok(d->fmt_down)) return MOEQ_E_UNSUPPORTED;
+  if (d->fmt_gate != d->fmt_up) return MOEQ_E_UNSUPPORTED;
+  if (!d->gate || !d->up || !d->down) return MOEQ_E_INVALID;
+  const int nsh = (d->sh_gate != nullptr) + (d->sh_up != nullptr) + (d->sh_down != nullptr);
+  if (nsh != 0 && nsh != 3) return MOEQ_E_INVALID;
+  if (nsh == 3) {
+    if (d->F_shared <= 0 || d->F_shared % 256) return MOEQ_E_INVALID;
+    if (!fmt_ok(d->sh_fmt_gate) || !fmt_ok(d->sh_fmt_up) || !fmt_ok(d->sh_fmt_down)) return MOEQ_E_UNSUPPORTED;
+    if (d->sh_fmt_gate != d->sh_fmt_up) return MOEQ_E_UNSUPPORTED;
+  }
+  if (d->path != MOEQ_PATH_AUTO && d->path != MOEQ_PATH_GEMV && d->path != MOEQ_PATH_MFMA)
+    return MOEQ_E_INVALID;
+  if (d->path == MOEQ_PATH_MFMA) return MOEQ_E_UNSUPPORTED;
+  if (d->accumulate != 0 && d->accumulate != 1) return MOEQ_E_INVALID;
+  LaneGeo g;
+  if (!lane_geo(d->fmt_gate, d->H, &g) || !lane_geo(d->fmt_down, d->F, &g)) return MOEQ_E_UNSUPPORTED;
+  if (nsh == 3 && (!lane_geo(d->sh_fmt_gate, d->H, &g) || !lane_geo(d->sh_fmt_down, d->F_shared, &g)))
+    return MOEQ_E_UNSUPPORTED;
+  return MOEQ_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* moeq_status_string(int status) {
+  switch (status) {
+    case MOEQ_OK: return "ok";
+    case MOEQ_E_INVALID: return "invalid argument";
+    case MOEQ_E_UNSUPPORTED: return "unsupported format, gating, path or shape";
+    case MOEQ_E_WORKSPACE: return "workspace too small";
+    case MOEQ_E_HIP: return "HIP launch failed";
+  }
+  return "unknown status";
+}
+
+int moeq_quantize_q8K(const float* x, int64_t rows, int64_t cols, void* out, void* stream) {
+  if (rows < 0 || cols <= 0 || cols % 256) return MOEQ_E_INVALID;
+  if (rows == 0) return MOEQ_OK;
+  if (!x || !out || !aligned(x, 4) || !aligned(out, 4)) return MOEQ_E_INVALID;
+  return hip_status(launch_quantize_q8K(x, rows, cols, out, (hipStream_t)stream));
+}
+
+size_t moeq_route_workspace(const moeq_route_desc* d) {
+  if (!d || d->T < 0 || d->E < 1) return 0;
+  return route_ws_bytes(d->T, d->E);
+}
+
+int moeq_route(const moeq_route_desc* d, const float* x, const float* w_router, const float* bias,
+               double* logits, int32_t* topk_ids, float* topk_w, int32_t* expert_offsets, int32_t* pairs,
+               int32_t* active, void* ws, size_t ws_bytes, void* stream) {
+  if (!d) return MOEQ_E_INVALID;
+  if (d->T < 0 || d->H <= 0 || d->H % 4 || d->E < 1 || d->E > kMaxE) return MOEQ_E_INVALID;
+  if (d->k < 1 || d->k > kMaxK || d->k > d->E) return MOEQ_E_INVALID;
+  if (d->gating < MOEQ_SOFTMAX_TOPK || d->gating > MOEQ_SIGMOID_TOPK) return MOEQ_E_UNSUPPORTED;
+  if (d->T * (int64_t)d->k > INT32_MAX / 2) return MOEQ_E_INVALID;
+  if (!expert_offsets || !active) return MOEQ_E_INVALID;
+  if (d->T > 0) {
+    if (!x || !w_router || !topk_ids || !topk_w || !pairs) return MOEQ_E_INVALID;
+    if (!aligned(x, 16) || !aligned(w_router, 16) || (bias && !aligned(bias, 4))) return MOEQ_E_INVALID;
+    if (logits && !aligned(logits, 8)) return MOEQ_E_INVALID;
+    if (!ws || !aligned(ws, 256)) return MOEQ_E_INVALID;
+    if (ws_bytes < route_ws_bytes(d->T, d->E)) return MOEQ_E_WORKSPACE;
+  }
+  return hip_status(launch_route(d->T, d->H, d->E, d->k, d->gating, d->scale, x, w_router, bias, logits,
+                                 topk_ids, topk_w, expert_offsets, pairs, active, ws, (hipStream_t)stream));
+}
+
+size_t moeq_packed_bytes(int32_t fmt, int64_t rows, int64_t cols) {
+  if (!fmt_ok(fmt) || rows <= 0 || cols <= 0 || cols % 256) return 0;
+  return packed_bytes_of(fmt, rows, cols);
+}
+
+int moeq_pack_experts(int32_t fmt, const void* aos, int64_t n_mats, int64_t rows, int64_t cols, void* packed,
+                      void* stream) {
+  if (!fmt_ok(fmt)) return MOEQ_E_UNSUPPORTED;
+  if (n_mats < 0 || rows <= 0 || cols <= 0 || cols % 256) return MOEQ_E_INVALID;
+  if (n_mats == 0) return MOEQ_OK;
+  if (!aos || !packed || !aligned(packed, 256)) return MOEQ_E_INVALID;
+  return hip_status(launch_pack(fmt, aos, n_mats, rows, cols, packed, (hipStream_t)stream));
+}
+
+size_t moeq_expert_ffn_workspace(const moeq_ffn_desc* d) {
+  if (check_ffn_desc(d) != MOEQ_OK) return 0;
+  return ffn_layout(d).total;
+}
+
+int moeq_expert_ffn(const moeq_ffn_desc* d, const void* x_q8K, const float* topk_w,
+                    const int32_t* expert_offsets, const int32_t* pairs, const int32_t* active,
+                    const float* shared_scale, float* y, void* ws, size_t ws_bytes, void* stream) {
+  int rc = check_ffn_desc(d);
+  if (rc != MOEQ_OK) return rc;
+  if (d->T == 0) return MOEQ_OK;
+  if (!x_q8K || !topk_w || !expert_offsets || !pairs || !active || !y) return MOEQ_E_INVALID;
+  if (!aligned(x_q8K, 4) || !aligned(y, 4) || !aligned(topk_w, 4)) return MOEQ_E_INVALID;
+  if (!ws || !aligned(ws, 256)) return MOEQ_E_INVALID;
+  const FfnLayout L = ffn_layout(d);
+  if (ws_bytes < L.total) return MOEQ_E_WORKSPACE;
+
+  hipStream_t s = (hipStream_t)stream;
+  uint8_t* wsb = (uint8_t*)ws;
+  const bool sh = d->sh_gate != nullptr;
+  const bool both = sh && d->sh_fmt_gate == d->fmt_gate && d->sh_fmt_down == d->fmt_down && d->F_shared == d->F;
+  const int tt = d->T == 1 ? 1 : 4;
+  const int max_union = (int)std::min<int64_t>(d->E, d->T * d->k);
+  int32_t* cnt = (int32_t*)(wsb + L.off_cnt);
+  const int n_cnt = (int)(d->H / kRowBlock);
+
+  // ---- gate/up
+  auto gateup = [&](int mode, int fmt, int64_t F, int n_slots, int32_t* zero_cnt) -> int {
+    LaneGeo g;
+    lane_geo(fmt, d->H, &g);
+    GateUpArgs a{};
+    a.gate = d->gate; a.up = d->up; a.down = d->down;
+    a.sh_gate = (const uint8_t*)d->sh_gate; a.sh_up = (const uint8_t*)d->sh_up;
+    a.mode = mode; a.T = d->T; a.H = d->H; a.F = F; a.k = d->k;
+    a.xq = (const uint8_t*)x_q8K; a.offsets = expert_offsets; a.pairs = pairs; a.active = active;
+    a.max_union = max_union;
+    a.hbuf = (float*)(wsb + L.off_h); a.hstride = L.Fmax;
+    a.lpr = g.lpr; a.cpr = g.cpr; a.steps = std::max(1, 4 / g.rps);
+    a.cnt = zero_cnt; a.n_cnt = n_cnt;
+    const int rows_per_wg = 4 * a.steps * g.rps;
+    dim3 grid((unsigned)((F + rows_per_wg - 1) / rows_per_wg), (unsigned)n_slots);
+    return launch_gateup(fmt, tt, g.cpl, grid, a, s);
+  };
+  auto down = [&](int mode, int fmt, int64_t F, int n_slots) -> int {
+    LaneGeo g;
+    lane_geo(fmt, F, &g);
+    DownArgs a{};
+    a.gate = d->gate; a.up = d->up; a.down = d->down; a.sh_down = (const uint8_t*)d->sh_down;
+    a.mode = mode; a.T = d->T; a.H = d->H; a.F = F; a.k = d->k;
+    a.topk_w = topk_w; a.shared_scale = shared_scale;
+    a.offsets = expert_offsets; a.pairs = pairs; a.active = active; a.max_union = max_union;
+    a.hbuf = (const float*)(wsb + L.off_h); a.hstride = L.Fmax;
+    a.yp = (double*)(wsb + L.off_yp);
+    a.hq = wsb + L.off_hq;
+    a.hq_sh = sh ? wsb + L.off_hqs : nullptr;
+    a.hq_stride = (F / 256) * kQ8KBytes;
+    a.lpr = g.lpr; a.cpr = g.cpr; a.rb = kRowBlock; a.steps = kRowBlock / (4 * g.rps);
+    a.cnt = cnt; a.has_shared = sh ? 1 : 0;
+    a.y = y; a.accumulate = d->accumulate;
+    dim3 grid((unsigned)n_cnt, (unsigned)n_slots);
+    return launch_down(fmt, tt, g.cpl, grid, a, s);
+  };
+  if (both) {
+    if ((rc = gateup(kModeBoth, d->fmt_gate, d->F, max_union + 1, cnt))) return hip_status(rc);
+  } else {
+    if ((rc = gateup(kModeRouted, d->fmt_gate, d->F, max_union, cnt))) return hip_status(rc);
+    if (sh && (rc = gateup(kModeShared, d->sh_fmt_gate, d->F_shared, 1, nullptr))) return hip_status(rc);
+  }
+  if (both) {
+    if ((rc = down(kModeBoth, d->fmt_down, d->F, max_union + 1))) return hip_status(rc);
+  } else {
+    if ((rc = down(kModeRouted, d->fmt_down, d->F, max_union))) return hip_status(rc);
+    if (sh && (rc = down(kModeShared, d->sh_fmt_down, d->F_shared, 1))) return hip_status(rc);
+  }
+  return MOEQ_OK;
+}
+
+int moeq_ffn_h_view(const moeq_ffn_desc* d, void* ws, size_t ws_bytes, void** hq_routed, void** hq_shared) {
+  int rc = check_ffn_desc(d);
+  if (rc != MOEQ_OK) return rc;
+  if (!ws || !hq_routed || !hq_shared) return MOEQ_E_INVALID;
+  const FfnLayout L = ffn_layout(d);
+  if (ws_bytes < L.total) return MOEQ_E_WORKSPACE;
+  *hq_routed = (uint8_t*)ws + L.off_hq;
+  *hq_shared = d->sh_gate ? (uint8_t*)ws + L.off_hqs : nullptr;
+  return MOEQ_OK;
+}
+
+int moeq_debug_subdots(int32_t fmt, const void* packed_w, int64_t rows, int64_t cols, const void* x_q8K,
+                       int64_t n_x, int32_t* out, void* stream) {
+  if (!fmt_ok(fmt)) return MOEQ_E_UNSUPPORTED;
+  if (rows <= 0 || cols <= 0 || cols % 256 || n_x < 0) return MOEQ_E_INVALID;
+  if (n_x == 0) return MOEQ_OK;
+  if (!packed_w || !x_q8K || !out || !aligned(packed_w, 256) || !aligned(x_q8K, 4) || !aligned(out, 4))
+    return MOEQ_E_INVALID;
+  return hip_status(launch_subdots(fmt, packed_w, rows, cols, x_q8K, n_x, out, (hipStream_t)stream));
+}
+
+}  // extern "C"

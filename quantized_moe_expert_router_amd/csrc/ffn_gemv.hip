@@ -1,0 +1,338 @@
+// Expert-grouped dequant GEMV for decode and verify rows (a few tokens per
+// expert).  Each expert's weights are read once for all of its tokens (rows
+// that share an expert share one weight read: Pulsar README, ThinkingCap
+// paragraph; the per-chunk expert union: DeepSeek-V4-Flash paragraph).
+//
+// Work item = (expert slot of the union, block of output rows).  A wave covers
+// rps = 64/lpr rows per step, lpr lanes per row, each lane one or more 16-byte
+// quant chunks at fixed column positions, so the activation chunks it needs
+// stay in registers for every row it visits.  Integer sub-block dots are
+// exact (v_dot4_i32_i8); the per-super-block scale/min combine and all sums
+// are fp64; the only fp32 roundings are h = fl32(silu(g) u), the q8_K
+// arithmetic and y.
+//
+// gate/up: h[pair, f] = fl32(silu(g) * u) with g, u the fp64 dots.
+// down:    q8_K(h) is rebuilt in registers by every wave that needs it (it is a
+//          pure function of h, so all waves agree bit for bit); each work item
+//          writes w * (W_d h^) in fp64 to a per-pair staging row, counts its
+//          arrival on its row block, and the last arrival sums the pairs of
+//          every token in slot order (then the shared expert) and rounds y.
+#include "formats.hpp"
+#include "launch.hpp"
+
+namespace moeq {
+
+struct Slot {
+  int valid, shared, e, n;
+  int64_t list_off;
+};
+
+__device__ __forceinline__ Slot decode_slot(int slot, int mode, int max_union, const int32_t* active,
+                                            const int32_t* offsets, int64_t T) {
+  Slot s{0, 0, -1, 0, 0};
+  if (mode == kModeShared || (mode == kModeBoth && slot == max_union)) {
+    s.valid = 1; s.shared = 1; s.n = (int)T;
+    return s;
+  }
+  if (slot >= active[0]) return s;
+  s.e = active[1 + slot];
+  s.list_off = offsets[s.e];
+  s.n = offsets[s.e + 1] - offsets[s.e];
+  s.valid = s.n > 0;
+  return s;
+}
+
+// token i of a slot: (token index, pair row)
+__device__ __forceinline__ void slot_token(const Slot& s, int i, const int32_t* pairs, int64_t T, int k,
+                                           int& tok, int64_t& prow) {
+  if (s.shared) { tok = i; prow = T * k + i; return; }
+  const int p = pairs[s.list_off + i];
+  tok = p / k;
+  prow = p;
+}
+
+template <int FMT, int TT, int CPL, int UNR>
+__global__ __launch_bounds__(256) void k_gateup(GateUpArgs a) {
+  using L = Fmt<FMT>;
+  if (a.cnt != nullptr && blockIdx.x == 0 && blockIdx.y == 0)
+    for (int i = threadIdx.x; i < a.n_cnt; i += blockDim.x) a.cnt[i] = 0;
+  const Slot sl = decode_slot(blockIdx.y, a.mode, a.max_union, a.active, a.offsets, a.T);
+  if (!sl.valid) return;
+  const uint8_t* Wg = sl.shared ? a.sh_gate : (const uint8_t*)a.gate[sl.e];
+  const uint8_t* Wu = sl.shared ? a.sh_up : (const uint8_t*)a.up[sl.e];
+  if (Wg == nullptr || Wu == nullptr) return;   // not resident: its pairs add nothing
+  if (!sl.shared && a.down[sl.e] == nullptr) return;
+
+  const int wave = threadIdx.x >> 6, lane = lane_id();
+  const int lpr = a.lpr, rps = kWave / lpr, rig = lane / lpr, lir = lane % lpr;
+  const int64_t nb = a.H / 256, nsb = a.F * nb, xrow = nb * kQ8KBytes;
+  const int64_t row0 = (int64_t)blockIdx.x * (4 * a.steps * rps) + (int64_t)wave * a.steps * rps + rig;
+
+  for (int tile = 0; tile < sl.n; tile += TT) {
+    int tok[TT];
+    int64_t prow[TT];
+    int xw[TT][CPL][L::XDW], bs[TT][CPL][L::NBS];
+    double dx[TT][CPL];
+#pragma unroll
+    for (int i = 0; i < TT; ++i) {
+      tok[i] = -1; prow[i] = 0;
+      if (tile + i < sl.n) slot_token(sl, tile + i, a.pairs, a.T, a.k, tok[i], prow[i]);
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) {
+        const int ch = lir + lpr * c;
+        if (tok[i] >= 0 && ch < a.cpr) {
+          load_x_chunk<FMT>(a.xq + tok[i] * xrow, ch, xw[i][c], bs[i][c], dx[i][c]);
+        } else {
+#pragma unroll
+          for (int q = 0; q < L::XDW; ++q) xw[i][c][q] = 0;
+#pragma unroll
+          for (int q = 0; q < L::NBS; ++q) bs[i][c][q] = 0;
+          dx[i][c] = 0.0;
+        }
+      }
+    }
+    for (int st = 0; st < a.steps; st += UNR) {
+      typename L::W wg[UNR][CPL], wu[UNR][CPL];
+      int64_t row[UNR];
+      bool ok[UNR][CPL];
+#pragma unroll
+      for (int u = 0; u < UNR; ++u) {
+        row[u] = row0 + (int64_t)(st + u) * rps;
+        const bool rv = (st + u) < a.steps && row[u] < a.F;
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) {
+          const int ch = lir + lpr * c;
+          ok[u][c] = rv && ch < a.cpr;
+          if (ok[u][c]) {
+            const size_t sbi = (size_t)(row[u] * nb + ch / L::CPS);
+            wg[u][c] = L::load(Wg, (size_t)nsb, sbi, ch % L::CPS);
+            wu[u][c] = L::load(Wu, (size_t)nsb, sbi, ch % L::CPS);
+          }
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < UNR; ++u) {
+        double ag[TT], au[TT];
+#pragma unroll
+        for (int i = 0; i < TT; ++i) { ag[i] = 0.0; au[i] = 0.0; }
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) {
+          if (!ok[u][c]) continue;
+          const int j = (lir + lpr * c) % L::CPS;
+#pragma unroll
+          for (int i = 0; i < TT; ++i) {
+            if (tok[i] < 0) continue;
+            int is[L::SPC];
+            L::isums(wg[u][c], xw[i][c], bs[i][c], is);
+            ag[i] += L::term(wg[u][c], j, is, bs[i][c], dx[i][c]);
+            L::isums(wu[u][c], xw[i][c], bs[i][c], is);
+            au[i] += L::term(wu[u][c], j, is, bs[i][c], dx[i][c]);
+          }
+        }
+#pragma unroll
+        for (int i = 0; i < TT; ++i) {
+          const double g = group_sum(ag[i], lpr);
+          const double uu = group_sum(au[i], lpr);
+          if (lir == 0 && tok[i] >= 0 && (st + u) < a.steps && row[u] < a.F)
+            a.hbuf[prow[i] * a.hstride + row[u]] = (float)(silu64(g) * uu);
+        }
+      }
+    }
+  }
+}
+
+// q8_K of the chunk(s) this lane holds, from fp32 h, identical to the
+// definition: the block amax is reduced over the 256/WPC lanes of the block.
+template <int FMT, int CPL>
+__device__ __forceinline__ void quant_h_chunks(const float* __restrict__ hrow, int lir, int lpr, int cpr,
+                                               bool have, int xw[CPL][Fmt<FMT>::XDW],
+                                               int bs[CPL][Fmt<FMT>::NBS], double dx[CPL],
+                                               uint8_t* dbg) {
+  using L = Fmt<FMT>;
+  constexpr int GW = 256 / L::WPC;   // lanes per 256-block
+#pragma unroll
+  for (int c = 0; c < CPL; ++c) {
+    const int ch = lir + lpr * c;
+    const bool v = have && ch < cpr;
+    float hv[L::WPC];
+    float amax = 0.0f;
+#pragma unroll
+    for (int q = 0; q < L::WPC / 4; ++q) {
+      float4 f = v ? reinterpret_cast<const float4*>(hrow + ch * L::WPC)[q] : make_float4(0.f, 0.f, 0.f, 0.f);
+      hv[4 * q] = f.x; hv[4 * q + 1] = f.y; hv[4 * q + 2] = f.z; hv[4 * q + 3] = f.w;
+      amax = fmaxf(amax, fmaxf(fmaxf(fabsf(f.x), fabsf(f.y)), fmaxf(fabsf(f.z), fabsf(f.w))));
+    }
+    amax = group_max(amax, GW);
+    const float id = amax == 0.0f ? 0.0f : __fdiv_rn(127.0f, amax);
+    const bool zero = amax == 0.0f || __builtin_isinf(id);
+#pragma unroll
+    for (int q = 0; q < L::WPC / 4; ++q) {
+      int q0 = 0, q1 = 0, q2 = 0, q3 = 0;
+      if (!zero) {
+        q0 = q8_code(hv[4 * q], id); q1 = q8_code(hv[4 * q + 1], id);
+        q2 = q8_code(hv[4 * q + 2], id); q3 = q8_code(hv[4 * q + 3], id);
+      }
+      xw[c][q] = (int)((uint32_t)(q0 & 255) | ((uint32_t)(q1 & 255) << 8) | ((uint32_t)(q2 & 255) << 16) |
+                       ((uint32_t)(q3 & 255) << 24));
+      const int s4 = q0 + q1 + q2 + q3;
+      if ((q & 3) == 0) bs[c][q >> 2] = s4; else bs[c][q >> 2] += s4;
+    }
+    dx[c] = zero ? 0.0 : (double)__fdiv_rn(amax, 127.0f);
+    if (dbg != nullptr && v) {
+      const int e0 = ch * L::WPC;
+      uint8_t* blk = dbg + (size_t)(e0 >> 8) * kQ8KBytes;
+      const int o = e0 & 255;
+#pragma unroll
+      for (int q = 0; q < L::XDW; ++q) *reinterpret_cast<int*>(blk + 4 + o + 4 * q) = xw[c][q];
+#pragma unroll
+      for (int q = 0; q < L::NBS; ++q) *reinterpret_cast<int16_t*>(blk + 260 + 2 * ((o >> 4) + q)) = (int16_t)bs[c][q];
+      if (o == 0) *reinterpret_cast<float*>(blk) = (float)dx[c];
+    }
+  }
+}
+
+template <int FMT, int TT, int CPL, int UNR>
+__global__ __launch_bounds__(256) void k_down(DownArgs a) {
+  using L = Fmt<FMT>;
+  __shared__ int s_last;
+  const Slot sl = decode_slot(blockIdx.y, a.mode, a.max_union, a.active, a.offsets, a.T);
+  if (!sl.valid) return;
+  // An expert is resident only if all three of its matrices are present.
+  const uint8_t* Wd = sl.shared ? a.sh_down : (const uint8_t*)a.down[sl.e];
+  if (!sl.shared && (a.gate[sl.e] == nullptr || a.up[sl.e] == nullptr)) Wd = nullptr;
+
+  const int wave = threadIdx.x >> 6, lane = lane_id();
+  const int lpr = a.lpr, rps = kWave / lpr, rig = lane / lpr, lir = lane % lpr;
+  const int64_t nb = a.F / 256, nsb = a.H * nb;
+  const int64_t row0 = (int64_t)blockIdx.x * a.rb + (int64_t)wave * a.steps * rps + rig;
+  const bool dbg_writer = blockIdx.x == 0 && wave == 0 && rig == 0;
+
+  for (int tile = 0; tile < sl.n; tile += TT) {
+    int tok[TT];
+    int64_t prow[TT];
+    double wt[TT];
+    int xw[TT][CPL][L::XDW], bs[TT][CPL][L::NBS];
+    double dx[TT][CPL];
+#pragma unroll
+    for (int i = 0; i < TT; ++i) {
+      tok[i] = -1; prow[i] = 0; wt[i] = 0.0;
+      if (tile + i < sl.n) {
+        slot_token(sl, tile + i, a.pairs, a.T, a.k, tok[i], prow[i]);
+        wt[i] = sl.shared ? (a.shared_scale ? (double)a.shared_scale[tok[i]] : 1.0) : (double)a.topk_w[prow[i]];
+      }
+      if (Wd != nullptr) {
+        const float* hrow = a.hbuf + (tok[i] >= 0 ? prow[i] : 0) * a.hstride;
+        uint8_t* dbg = nullptr;
+        uint8_t* hq_base = sl.shared ? a.hq_sh : a.hq;
+        if (dbg_writer && tok[i] >= 0 && hq_base != nullptr)
+          dbg = hq_base + (sl.shared ? (int64_t)tok[i] : prow[i]) * a.hq_stride;
+        quant_h_chunks<FMT, CPL>(hrow, lir, lpr, a.cpr, tok[i] >= 0, xw[i], bs[i], dx[i], dbg);
+      }
+    }
+    for (int st = 0; st < a.steps; st += UNR) {
+      typename L::W wd[UNR][CPL];
+      int64_t row[UNR];
+      bool ok[UNR][CPL];
+#pragma unroll
+      for (int u = 0; u < UNR; ++u) {
+        row[u] = row0 + (int64_t)(st + u) * rps;
+        const bool rv = (st + u) < a.steps && row[u] < a.H && Wd != nullptr;
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) {
+          const int ch = lir + lpr * c;
+          ok[u][c] = rv && ch < a.cpr;
+          if (ok[u][c])
+            wd[u][c] = L::load(Wd, (size_t)nsb, (size_t)(row[u] * nb + ch / L::CPS), ch % L::CPS);
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < UNR; ++u) {
+        double ay[TT];
+#pragma unroll
+        for (int i = 0; i < TT; ++i) ay[i] = 0.0;
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) {
+          if (!ok[u][c]) continue;
+          const int j = (lir + lpr * c) % L::CPS;
+#pragma unroll
+          for (int i = 0; i < TT; ++i) {
+            if (tok[i] < 0) continue;
+            int is[L::SPC];
+            L::isums(wd[u][c], xw[i][c], bs[i][c], is);
+            ay[i] += L::term(wd[u][c], j, is, bs[i][c], dx[i][c]);
+          }
+        }
+#pragma unroll
+        for (int i = 0; i < TT; ++i) {
+          const double yv = group_sum(ay[i], lpr);
+          if (lir == 0 && tok[i] >= 0 && (st + u) < a.steps && row[u] < a.H)
+            a.yp[prow[i] * a.H + row[u]] = wt[i] * yv;
+        }
+      }
+    }
+  }
+
+  // Arrive on this row block; the last arrival combines it.
+  __threadfence();
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const int total = a.active[0] + a.has_shared;
+    const int old = atomicAdd(&a.cnt[blockIdx.x], 1);
+    s_last = old == total - 1;
+  }
+  __syncthreads();
+  if (!s_last) return;
+  __threadfence();
+  const int64_t r0 = (int64_t)blockIdx.x * a.rb;
+  for (int64_t idx = threadIdx.x; idx < a.T * a.rb; idx += blockDim.x) {
+    const int64_t t = idx / a.rb, r = r0 + idx % a.rb;
+    if (r >= a.H) continue;
+    double acc = 0.0;
+    for (int s = 0; s < a.k; ++s) acc += a.yp[(t * a.k + s) * a.H + r];
+    if (a.has_shared) acc += a.yp[(a.T * a.k + t) * a.H + r];
+    float* yo = a.y + t * a.H + r;
+    *yo = a.accumulate ? (float)((double)*yo + acc) : (float)acc;
+  }
+  if (threadIdx.x == 0) a.cnt[blockIdx.x] = 0;
+}
+
+// ------------------------------------------------------------ dispatch
+
+#define MOEQ_GU(F, TT, C) \
+  hipLaunchKernelGGL((k_gateup<F, TT, C, 2>), grid, dim3(256), 0, s, a)
+#define MOEQ_DN(F, TT, C) \
+  hipLaunchKernelGGL((k_down<F, TT, C, 2>), grid, dim3(256), 0, s, a)
+
+#define MOEQ_SWITCH_CPL(M, F, TT)            \
+  switch (cpl) {                             \
+    case 1: M(F, TT, 1); break;              \
+    case 2: M(F, TT, 2); break;              \
+    case 4: M(F, TT, 4); break;              \
+    default: return -2;                      \
+  }
+#define MOEQ_SWITCH_TT(M, F)                                  \
+  if (tt == 1) { MOEQ_SWITCH_CPL(M, F, 1) }                   \
+  else if (tt == 4) { MOEQ_SWITCH_CPL(M, F, 4) }              \
+  else return -2;
+#define MOEQ_SWITCH_FMT(M)                                    \
+  switch (fmt) {                                              \
+    case FQ4K: { MOEQ_SWITCH_TT(M, FQ4K) } break;             \
+    case FQ6K: { MOEQ_SWITCH_TT(M, FQ6K) } break;             \
+    case FQ2K: { MOEQ_SWITCH_TT(M, FQ2K) } break;             \
+    case FQ80: { MOEQ_SWITCH_TT(M, FQ80) } break;             \
+    default: return -2;                                       \
+  }
+
+int launch_gateup(int fmt, int tt, int cpl, dim3 grid, const GateUpArgs& a, hipStream_t s) {
+  if (grid.x == 0 || grid.y == 0) return 0;
+  MOEQ_SWITCH_FMT(MOEQ_GU)
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+int launch_down(int fmt, int tt, int cpl, dim3 grid, const DownArgs& a, hipStream_t s) {
+  if (grid.x == 0 || grid.y == 0) return 0;
+  MOEQ_SWITCH_FMT(MOEQ_DN)
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+}  // namespace moeq

@@ -1,0 +1,210 @@
+// Packed (kernel-side) layouts of the quantised weight formats, their per-lane
+// dot routines and the exchange->packed repack.
+//
+// A packed matrix of nsb = rows * cols/256 super-blocks is a set of planes, each
+// contiguous over super-blocks in row-major order and 256-byte aligned.  A wave
+// lane works on one "chunk" of a super-block: 16 contiguous bytes of the main
+// quant plane, so a wave reads 1 KiB of quants per load instruction, fully
+// coalesced.  The element order inside a chunk is chosen so that one 32-bit
+// word, after a mask or a shift, holds four consecutive elements of one
+// sub-block, matching four consecutive q8_K bytes of the activation: one
+// v_dot4_i32_i8.
+//
+//   Q4_K  plane Q 128 B/sb: chunk j (sub-block j, 32 elements), byte b =
+//           elem 32j+b (low nibble) | elem 32j+16+b (high nibble)
+//         plane H  16 B/sb: the exchange header as is (d, dmin, 12 B scales)
+//   Q6_K  plane L 128 B/sb: chunk j (elements 32j..32j+31, sub-blocks 2j, 2j+1),
+//           byte b = low4(32j+b) | low4(32j+16+b) << 4
+//         plane X  64 B/sb: chunk j = 2 words; word a, byte b, bits 2s..2s+1 =
+//           high2(elem 32j + 4(4a+s) + b)
+//         plane S  16 B/sb: int8 scales;  plane D 2 B/sb: fp16 d
+//   Q2_K  plane Q  64 B/sb: chunk c (elements 64c..64c+63, sub-blocks 4c..4c+3),
+//           word a, byte b, bits 2s..2s+1 = elem 64c + 16s + 4a + b
+//         plane S  16 B/sb: (sc | m << 4) per sub-block;  plane D 4 B/sb: d, dmin
+//   Q8_0  plane Q 256 B/sb: chunk b = the 32 int8 quants of block b
+//         plane D  16 B/sb: eight fp16 d
+#pragma once
+#include "common.hpp"
+
+namespace moeq {
+
+template <int FMT> struct Fmt;
+
+// Host-side geometry shared by every format.
+struct Geo {
+  int wpc;          // weights per lane chunk
+  int nplanes;
+  int pb[4];        // bytes per super-block of each plane
+};
+
+__host__ __device__ inline Geo geo_of(int fmt) {
+  switch (fmt) {
+    case FQ4K: return Geo{32, 2, {128, 16, 0, 0}};
+    case FQ6K: return Geo{32, 4, {128, 64, 16, 2}};
+    case FQ2K: return Geo{64, 3, {64, 16, 4, 0}};
+    case FQ80: return Geo{32, 2, {256, 16, 0, 0}};
+  }
+  return Geo{0, 0, {0, 0, 0, 0}};
+}
+
+__host__ __device__ inline size_t packed_bytes_of(int fmt, int64_t rows, int64_t cols) {
+  Geo g = geo_of(fmt);
+  size_t nsb = (size_t)rows * (size_t)(cols / 256), tot = 0;
+  for (int p = 0; p < g.nplanes; ++p) tot += align256(nsb * g.pb[p]);
+  return tot;
+}
+
+__device__ __forceinline__ const uint8_t* plane(const uint8_t* m, size_t nsb, int fmt, int p) {
+  Geo g = geo_of(fmt);
+  size_t off = 0;
+  for (int q = 0; q < p; ++q) off += align256(nsb * g.pb[q]);
+  return m + off;
+}
+
+// ---------------------------------------------------------------- Q4_K
+template <> struct Fmt<FQ4K> {
+  static constexpr int WPC = 32, CPS = 8, XDW = 8, NBS = 2, SPC = 1;
+  struct W { uint4 q; uint4 h; };
+  __device__ static W load(const uint8_t* m, size_t nsb, size_t sbi, int j) {
+    W w;
+    w.q = *reinterpret_cast<const uint4*>(m + sbi * 128 + 16 * j);
+    w.h = *reinterpret_cast<const uint4*>(m + align256(nsb * 128) + sbi * 16);
+    return w;
+  }
+  __device__ static void isums(const W& w, const int* xw, const int*, int* is) {
+    const uint32_t q[4] = {w.q.x, w.q.y, w.q.z, w.q.w};
+    int s = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      s = dot4((int)(q[i] & 0x0F0F0F0Fu), xw[i], s);
+      s = dot4((int)((q[i] >> 4) & 0x0F0F0F0Fu), xw[4 + i], s);
+    }
+    is[0] = s;
+  }
+  __device__ static double term(const W& w, int j, const int* is, const int* bs, double dx) {
+    uint64_t lo = (uint64_t)w.h.y | ((uint64_t)w.h.z << 32);   // stream bits 0..63
+    uint64_t hi = (uint64_t)w.h.z | ((uint64_t)w.h.w << 32);   // stream bits 32..95
+    int sc = (int)((lo >> (6 * j)) & 63);
+    int mn = (int)((hi >> (16 + 6 * j)) & 63);
+    double d = half_bits_to_float(w.h.x & 0xFFFF), dmin = half_bits_to_float(w.h.x >> 16);
+    int s1 = sc * is[0], s2 = mn * (bs[0] + bs[1]);
+    return dx * (d * (double)s1 - dmin * (double)s2);
+  }
+};
+
+// ---------------------------------------------------------------- Q6_K
+template <> struct Fmt<FQ6K> {
+  static constexpr int WPC = 32, CPS = 8, XDW = 8, NBS = 2, SPC = 2;
+  struct W { uint4 l; uint2 x; uint32_t sc; uint32_t d; };
+  __device__ static W load(const uint8_t* m, size_t nsb, size_t sbi, int j) {
+    W w;
+    const uint8_t* px = m + align256(nsb * 128);
+    const uint8_t* ps = px + align256(nsb * 64);
+    const uint8_t* pd = ps + align256(nsb * 16);
+    w.l = *reinterpret_cast<const uint4*>(m + sbi * 128 + 16 * j);
+    w.x = *reinterpret_cast<const uint2*>(px + sbi * 64 + 8 * j);
+    w.sc = ld_u16(ps + sbi * 16 + 2 * j);
+    w.d = ld_u16(pd + sbi * 2);
+    return w;
+  }
+  __device__ static void isums(const W& w, const int* xw, const int* bs, int* is) {
+    const uint32_t l[4] = {w.l.x, w.l.y, w.l.z, w.l.w};
+    int a = 0, b = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      uint32_t ha = ((w.x.x >> (2 * i)) & 0x03030303u) << 4;
+      uint32_t hb = ((w.x.y >> (2 * i)) & 0x03030303u) << 4;
+      a = dot4((int)((l[i] & 0x0F0F0F0Fu) | ha), xw[i], a);
+      b = dot4((int)(((l[i] >> 4) & 0x0F0F0F0Fu) | hb), xw[4 + i], b);
+    }
+    is[0] = a - 32 * bs[0];   // sum (q - 32) q_x = sum q q_x - 32 sum q_x
+    is[1] = b - 32 * bs[1];
+  }
+  __device__ static double term(const W& w, int, const int* is, const int*, double dx) {
+    int sa = (int)(int8_t)(w.sc & 0xFF), sb = (int)(int8_t)(w.sc >> 8);
+    int s1 = sa * is[0] + sb * is[1];
+    double d = half_bits_to_float(w.d);
+    return dx * (d * (double)s1);
+  }
+};
+
+// ---------------------------------------------------------------- Q2_K
+template <> struct Fmt<FQ2K> {
+  static constexpr int WPC = 64, CPS = 4, XDW = 16, NBS = 4, SPC = 4;
+  struct W { uint4 q; uint32_t sm; uint32_t dd; };
+  __device__ static W load(const uint8_t* m, size_t nsb, size_t sbi, int c) {
+    W w;
+    const uint8_t* ps = m + align256(nsb * 64);
+    const uint8_t* pd = ps + align256(nsb * 16);
+    w.q = *reinterpret_cast<const uint4*>(m + sbi * 64 + 16 * c);
+    w.sm = ld_u32(ps + sbi * 16 + 4 * c);
+    w.dd = ld_u32(pd + sbi * 4);
+    return w;
+  }
+  __device__ static void isums(const W& w, const int* xw, const int*, int* is) {
+    const uint32_t q[4] = {w.q.x, w.q.y, w.q.z, w.q.w};
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      int acc = 0;
+#pragma unroll
+      for (int a = 0; a < 4; ++a) acc = dot4((int)((q[a] >> (2 * s)) & 0x03030303u), xw[4 * s + a], acc);
+      is[s] = acc;
+    }
+  }
+  __device__ static double term(const W& w, int, const int* is, const int* bs, double dx) {
+    int s1 = 0, s2 = 0;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      uint32_t v = (w.sm >> (8 * s)) & 0xFF;
+      s1 += (int)(v & 15) * is[s];
+      s2 += (int)(v >> 4) * bs[s];
+    }
+    double d = half_bits_to_float(w.dd & 0xFFFF), dmin = half_bits_to_float(w.dd >> 16);
+    return dx * (d * (double)s1 - dmin * (double)s2);
+  }
+};
+
+// ---------------------------------------------------------------- Q8_0
+template <> struct Fmt<FQ80> {
+  static constexpr int WPC = 32, CPS = 8, XDW = 8, NBS = 2, SPC = 1;
+  struct W { uint4 q0, q1; uint32_t d; };
+  __device__ static W load(const uint8_t* m, size_t nsb, size_t sbi, int b) {
+    W w;
+    const uint8_t* pd = m + align256(nsb * 256);
+    w.q0 = *reinterpret_cast<const uint4*>(m + sbi * 256 + 32 * b);
+    w.q1 = *reinterpret_cast<const uint4*>(m + sbi * 256 + 32 * b + 16);
+    w.d = ld_u16(pd + sbi * 16 + 2 * b);
+    return w;
+  }
+  __device__ static void isums(const W& w, const int* xw, const int*, int* is) {
+    const uint32_t q[8] = {w.q0.x, w.q0.y, w.q0.z, w.q0.w, w.q1.x, w.q1.y, w.q1.z, w.q1.w};
+    int s = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) s = dot4((int)q[i], xw[i], s);
+    is[0] = s;
+  }
+  __device__ static double term(const W& w, int, const int* is, const int*, double dx) {
+    double d = half_bits_to_float(w.d);
+    return dx * (d * (double)is[0]);
+  }
+};
+
+// Element positions inside a lane chunk, in x-word order: word i of a chunk
+// holds chunk elements xoff(i)..xoff(i)+3.  For every format here the x words
+// are simply the chunk's elements in order (4 per word).
+
+// Load the activation side of one chunk from a q8_K row.
+template <int FMT>
+__device__ __forceinline__ void load_x_chunk(const uint8_t* xrow, int c, int* xw, int* bs, double& dx) {
+  using L = Fmt<FMT>;
+  int e0 = c * L::WPC;
+  const uint8_t* blk = xrow + (size_t)(e0 >> 8) * kQ8KBytes;
+  int o = e0 & 255;
+  dx = (double)*reinterpret_cast<const float*>(blk);
+#pragma unroll
+  for (int i = 0; i < L::XDW; ++i) xw[i] = (int)ld_u32(blk + 4 + o + 4 * i);
+#pragma unroll
+  for (int i = 0; i < L::NBS; ++i) bs[i] = (int)(int16_t)ld_u16(blk + 260 + 2 * ((o >> 4) + i));
+}
+
+}  // namespace moeq

@@ -1,0 +1,73 @@
+// Host-side launchers of libmoeq's kernels (internal; the public surface is moeq.h).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace moeq {
+
+// Which slots a FFN launch covers: the routed union, the shared expert, or both
+// (the shared expert as one more slot when it has the routed shape and format).
+constexpr int kModeRouted = 0, kModeShared = 1, kModeBoth = 2;
+
+struct GateUpArgs {
+  const void* const* gate;
+  const void* const* up;
+  const void* const* down;      // only checked for residency
+  const uint8_t* sh_gate;
+  const uint8_t* sh_up;
+  int mode;
+  int64_t T, H, F;              // F: rows of this launch's gate/up matrices
+  int k;
+  const uint8_t* xq;            // q8_K(x) [T, H/256]
+  const int32_t* offsets;
+  const int32_t* pairs;
+  const int32_t* active;
+  int max_union;
+  float* hbuf;                  // fp32 [T*k + T, hstride]
+  int64_t hstride;
+  int lpr, cpr, steps;
+  int32_t* cnt;                 // down-combine counters zeroed by block (0,0), or null
+  int n_cnt;
+};
+
+struct DownArgs {
+  const void* const* gate;
+  const void* const* up;
+  const void* const* down;
+  const uint8_t* sh_down;
+  int mode;
+  int64_t T, H, F;              // F: inner size of this launch's down matrices
+  int k;
+  const float* topk_w;
+  const float* shared_scale;
+  const int32_t* offsets;
+  const int32_t* pairs;
+  const int32_t* active;
+  int max_union;
+  const float* hbuf;
+  int64_t hstride;
+  double* yp;                   // fp64 [T*k + T, H] weighted per-pair outputs
+  uint8_t* hq;                  // q8_K(h) rows of routed pairs [T*k], or null
+  uint8_t* hq_sh;               // q8_K(h) rows of the shared expert [T], or null
+  int64_t hq_stride;            // bytes per row for this launch's F
+  int lpr, cpr, steps, rb;      // rb = rows per work item = 4 * steps * (64 / lpr)
+  int32_t* cnt;                 // [H / rb] arrival counters
+  int has_shared;
+  float* y;
+  int accumulate;
+};
+
+int launch_quantize_q8K(const float* x, int64_t rows, int64_t cols, void* out, hipStream_t s);
+int launch_pack(int fmt, const void* aos, int64_t n_mats, int64_t rows, int64_t cols, void* packed,
+                hipStream_t s);
+int launch_subdots(int fmt, const void* w, int64_t rows, int64_t cols, const void* xq, int64_t n_x,
+                   int32_t* out, hipStream_t s);
+size_t route_ws_bytes(int64_t T, int64_t E);
+int launch_route(int64_t T, int64_t H, int64_t E, int k, int gating, float scale, const float* x,
+                 const float* W, const float* bias, double* logits, int32_t* ids, float* w,
+                 int32_t* offsets, int32_t* pairs, int32_t* active, void* ws, hipStream_t s);
+int launch_gateup(int fmt, int tt, int cpl, dim3 grid, const GateUpArgs& a, hipStream_t s);
+int launch_down(int fmt, int tt, int cpl, dim3 grid, const DownArgs& a, hipStream_t s);
+
+}  // namespace moeq

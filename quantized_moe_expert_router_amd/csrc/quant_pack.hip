@@ -1,0 +1,198 @@
+// q8_K activation quantisation and the one-time exchange->packed weight repack.
+#include "formats.hpp"
+#include "launch.hpp"
+
+namespace moeq {
+
+// One wave per 256-block: 4 elements per lane.  fp32 arithmetic identical to
+// the definition: amax, id = 127/amax (correctly rounded), q = rint(x*id)
+// clamped to +-127, d = amax/127, per-16 sums.  A block with amax == 0 or an
+// infinite id is written as zeros.
+__global__ __launch_bounds__(256) void k_quantize_q8K(const float* __restrict__ x, int64_t rows,
+                                                      int64_t cols, uint8_t* __restrict__ out) {
+  const int64_t nb = cols / 256;
+  const int64_t g = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (g >= rows * nb) return;
+  const int lane = lane_id();
+  const int64_t row = g / nb, b = g % nb;
+  const float* xb = x + row * cols + b * 256 + 4 * lane;
+  float v0 = xb[0], v1 = xb[1], v2 = xb[2], v3 = xb[3];
+  float amax = fmaxf(fmaxf(fabsf(v0), fabsf(v1)), fmaxf(fabsf(v2), fabsf(v3)));
+  amax = group_max(amax, kWave);
+  uint8_t* o = out + g * kQ8KBytes;
+  float id = amax == 0.0f ? 0.0f : __fdiv_rn(127.0f, amax);
+  if (amax == 0.0f || __builtin_isinf(id)) {
+    *reinterpret_cast<uint32_t*>(o + 4 + 4 * lane) = 0u;
+    if ((lane & 3) == 0) *reinterpret_cast<int16_t*>(o + 260 + 2 * (lane >> 2)) = 0;
+    if (lane == 0) *reinterpret_cast<float*>(o) = 0.0f;
+    return;
+  }
+  int q0 = q8_code(v0, id), q1 = q8_code(v1, id), q2 = q8_code(v2, id), q3 = q8_code(v3, id);
+  uint32_t packed = (uint32_t)(q0 & 255) | ((uint32_t)(q1 & 255) << 8) | ((uint32_t)(q2 & 255) << 16) |
+                    ((uint32_t)(q3 & 255) << 24);
+  *reinterpret_cast<uint32_t*>(o + 4 + 4 * lane) = packed;
+  int s = q0 + q1 + q2 + q3;
+  s += __shfl_xor(s, 1, kWave);
+  s += __shfl_xor(s, 2, kWave);
+  if ((lane & 3) == 0) *reinterpret_cast<int16_t*>(o + 260 + 2 * (lane >> 2)) = (int16_t)s;
+  if (lane == 0) *reinterpret_cast<float*>(o) = __fdiv_rn(amax, 127.0f);
+}
+
+int launch_quantize_q8K(const float* x, int64_t rows, int64_t cols, void* out, hipStream_t s) {
+  int64_t nblk = rows * (cols / 256);
+  if (nblk == 0) return 0;
+  int64_t grid = (nblk + 3) / 4;
+  hipLaunchKernelGGL(k_quantize_q8K, dim3((unsigned)grid), dim3(256), 0, s, x, rows, cols,
+                     (uint8_t*)out);
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+// ------------------------------------------------------------------ repack
+
+__device__ __forceinline__ int q4k_code(const uint8_t* b, int e) {   // exchange Q4_K element
+  int g = e >> 6, i = e & 63;
+  uint8_t v = b[16 + 32 * g + (i & 31)];
+  return i < 32 ? (v & 15) : (v >> 4);
+}
+__device__ __forceinline__ int q2k_code(const uint8_t* b, int e) {
+  int h = e >> 7, r = e & 127, s = r >> 5, i = r & 31;
+  return (b[20 + 32 * h + i] >> (2 * s)) & 3;
+}
+__device__ __forceinline__ int q6k_low4(const uint8_t* b, int e) {
+  int h = e >> 7, r = e & 127;
+  uint8_t v = b[18 + 64 * h + (r & 63)];
+  return r < 64 ? (v & 15) : (v >> 4);
+}
+__device__ __forceinline__ int q6k_high2(const uint8_t* b, int e) {
+  int h = e >> 7, r = e & 127, s = r >> 5, i = r & 31;
+  return (b[146 + 32 * h + i] >> (2 * s)) & 3;
+}
+
+__device__ __forceinline__ void st_u32(uint8_t* p, uint32_t v) { *reinterpret_cast<uint32_t*>(p) = v; }
+
+template <int FMT>
+__global__ __launch_bounds__(256) void k_pack(const uint8_t* __restrict__ aos, int64_t n_mats,
+                                              int64_t rows, int64_t cols, uint8_t* __restrict__ packed,
+                                              size_t mat_bytes, int64_t sb_bytes_aos) {
+  const int64_t nb = cols / 256, nsb = rows * nb;
+  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (gid >= n_mats * nsb) return;
+  const int64_t mat = gid / nsb, sbi = gid % nsb;
+  const uint8_t* src = aos + gid * sb_bytes_aos;   // (mat*rows + r)*nb + s == gid
+  uint8_t* m = packed + mat * mat_bytes;
+  if (FMT == FQ4K) {
+    for (int j = 0; j < 8; ++j)
+      for (int w = 0; w < 4; ++w) {
+        uint32_t v = 0;
+        for (int bb = 0; bb < 4; ++bb) {
+          int b = 4 * w + bb;
+          v |= (uint32_t)(q4k_code(src, 32 * j + b) | (q4k_code(src, 32 * j + 16 + b) << 4)) << (8 * bb);
+        }
+        st_u32(m + sbi * 128 + 16 * j + 4 * w, v);
+      }
+    uint8_t* ph = m + align256(nsb * 128) + sbi * 16;
+    for (int i = 0; i < 16; ++i) ph[i] = src[i];
+  } else if (FMT == FQ6K) {
+    uint8_t* px = m + align256(nsb * 128);
+    uint8_t* ps = px + align256(nsb * 64);
+    uint8_t* pd = ps + align256(nsb * 16);
+    for (int j = 0; j < 8; ++j) {
+      for (int w = 0; w < 4; ++w) {
+        uint32_t v = 0;
+        for (int bb = 0; bb < 4; ++bb) {
+          int b = 4 * w + bb;
+          v |= (uint32_t)(q6k_low4(src, 32 * j + b) | (q6k_low4(src, 32 * j + 16 + b) << 4)) << (8 * bb);
+        }
+        st_u32(m + sbi * 128 + 16 * j + 4 * w, v);
+      }
+      for (int a = 0; a < 2; ++a) {
+        uint32_t v = 0;
+        for (int s = 0; s < 4; ++s)
+          for (int b = 0; b < 4; ++b)
+            v |= (uint32_t)q6k_high2(src, 32 * j + 4 * (4 * a + s) + b) << (8 * b + 2 * s);
+        st_u32(px + sbi * 64 + 8 * j + 4 * a, v);
+      }
+    }
+    for (int i = 0; i < 16; ++i) ps[sbi * 16 + i] = src[2 + i];
+    pd[sbi * 2] = src[0];
+    pd[sbi * 2 + 1] = src[1];
+  } else if (FMT == FQ2K) {
+    uint8_t* ps = m + align256(nsb * 64);
+    uint8_t* pd = ps + align256(nsb * 16);
+    for (int c = 0; c < 4; ++c)
+      for (int a = 0; a < 4; ++a) {
+        uint32_t v = 0;
+        for (int s = 0; s < 4; ++s)
+          for (int b = 0; b < 4; ++b)
+            v |= (uint32_t)q2k_code(src, 64 * c + 16 * s + 4 * a + b) << (8 * b + 2 * s);
+        st_u32(m + sbi * 64 + 16 * c + 4 * a, v);
+      }
+    for (int i = 0; i < 16; ++i) ps[sbi * 16 + i] = src[4 + i];
+    for (int i = 0; i < 4; ++i) pd[sbi * 4 + i] = src[i];
+  } else {  // Q8_0: eight 34-byte blocks per super-block
+    uint8_t* pd = m + align256(nsb * 256);
+    for (int b = 0; b < 8; ++b) {
+      const uint8_t* blk = src + 34 * b;
+      for (int i = 0; i < 32; ++i) m[sbi * 256 + 32 * b + i] = blk[2 + i];
+      pd[sbi * 16 + 2 * b] = blk[0];
+      pd[sbi * 16 + 2 * b + 1] = blk[1];
+    }
+  }
+}
+
+int launch_pack(int fmt, const void* aos, int64_t n_mats, int64_t rows, int64_t cols, void* packed,
+                hipStream_t s) {
+  const int64_t total = n_mats * rows * (cols / 256);
+  if (total == 0) return 0;
+  const size_t mb = packed_bytes_of(fmt, rows, cols);
+  const unsigned grid = (unsigned)((total + 255) / 256);
+  const uint8_t* a = (const uint8_t*)aos;
+  uint8_t* p = (uint8_t*)packed;
+  switch (fmt) {
+    case FQ4K: hipLaunchKernelGGL(k_pack<FQ4K>, dim3(grid), dim3(256), 0, s, a, n_mats, rows, cols, p, mb, (int64_t)144); break;
+    case FQ6K: hipLaunchKernelGGL(k_pack<FQ6K>, dim3(grid), dim3(256), 0, s, a, n_mats, rows, cols, p, mb, (int64_t)210); break;
+    case FQ2K: hipLaunchKernelGGL(k_pack<FQ2K>, dim3(grid), dim3(256), 0, s, a, n_mats, rows, cols, p, mb, (int64_t)84); break;
+    case FQ80: hipLaunchKernelGGL(k_pack<FQ80>, dim3(grid), dim3(256), 0, s, a, n_mats, rows, cols, p, mb, (int64_t)272); break;
+    default: return -2;
+  }
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+// --------------------------------------------------------------- subdots
+
+template <int FMT>
+__global__ __launch_bounds__(256) void k_subdots(const uint8_t* __restrict__ w, int64_t rows, int64_t cols,
+                                                 const uint8_t* __restrict__ xq, int64_t n_x,
+                                                 int32_t* __restrict__ out) {
+  using L = Fmt<FMT>;
+  const int64_t cpr = cols / L::WPC, nb = cols / 256, nsb = rows * nb;
+  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (gid >= n_x * rows * cpr) return;
+  const int64_t c = gid % cpr, r = (gid / cpr) % rows, n = gid / (cpr * rows);
+  int xw[L::XDW], bs[L::NBS], is[L::SPC];
+  double dx;
+  load_x_chunk<FMT>(xq + n * nb * kQ8KBytes, (int)c, xw, bs, dx);
+  typename L::W wv = L::load(w, (size_t)nsb, (size_t)(r * nb + c / L::CPS), (int)(c % L::CPS));
+  L::isums(wv, xw, bs, is);
+  for (int i = 0; i < L::SPC; ++i) out[(n * rows + r) * (cpr * L::SPC) + c * L::SPC + i] = is[i];
+}
+
+int launch_subdots(int fmt, const void* w, int64_t rows, int64_t cols, const void* xq, int64_t n_x,
+                   int32_t* out, hipStream_t s) {
+  const Geo g = geo_of(fmt);
+  const int64_t total = n_x * rows * (cols / g.wpc);
+  if (total == 0) return 0;
+  const unsigned grid = (unsigned)((total + 255) / 256);
+  const uint8_t* W = (const uint8_t*)w;
+  const uint8_t* X = (const uint8_t*)xq;
+  switch (fmt) {
+    case FQ4K: hipLaunchKernelGGL(k_subdots<FQ4K>, dim3(grid), dim3(256), 0, s, W, rows, cols, X, n_x, out); break;
+    case FQ6K: hipLaunchKernelGGL(k_subdots<FQ6K>, dim3(grid), dim3(256), 0, s, W, rows, cols, X, n_x, out); break;
+    case FQ2K: hipLaunchKernelGGL(k_subdots<FQ2K>, dim3(grid), dim3(256), 0, s, W, rows, cols, X, n_x, out); break;
+    case FQ80: hipLaunchKernelGGL(k_subdots<FQ80>, dim3(grid), dim3(256), 0, s, W, rows, cols, X, n_x, out); break;
+    default: return -2;
+  }
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+}  // namespace moeq

@@ -216,3 +216,18 @@ def shared_bytes(cfg: LayerConfig) -> int:
     Fs = cfg.F_shared
     return (matrix_bytes(cfg.sh_fmt_gate, Fs, cfg.H) + matrix_bytes(cfg.sh_fmt_up, Fs, cfg.H)
             + matrix_bytes(cfg.sh_fmt_down, cfg.H, Fs))
+
+
+def gen_weight_blocks_device(fmt: int, rows: int, cols: int, generator, device) -> "torch.Tensor":
+    """The same recipe as gen_weight_blocks (uniform random bytes, fp16 scale
+    fields drawn from their ranges) drawn with torch's seeded device generator;
+    used to fill many layers quickly.  Returns uint8 [rows * bytes_per_row]."""
+    import torch
+    bb = BLOCK_BYTES[fmt]
+    nblk = rows * (cols // BLOCK_WEIGHTS[fmt])
+    raw = torch.randint(0, 256, (nblk, bb), dtype=torch.uint8, device=device, generator=generator)
+    for off, mult, base in _FP16_FIELDS[fmt]:
+        u = torch.rand(nblk, dtype=torch.float64, device=device, generator=generator) + 1.0
+        h = (mult * u * base).to(torch.float16)
+        raw[:, off:off + 2] = h.view(torch.uint8).view(nblk, 2)
+    return raw.reshape(-1)

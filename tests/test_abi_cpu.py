@@ -1,0 +1,118 @@
+"""Host-side checks of the C ABI: the library loads without a GPU, exports
+every symbol include/moeq.h declares, and rejects bad arguments before any
+launch (no compute calls here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from quantized_moe_expert_router_amd import moeq
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_symbols():
+    src = open(os.path.join(ROOT, "include", "moeq.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(moeq_[a-zA-Z0-9_]+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_symbol():
+    syms = _declared_symbols()
+    assert len(syms) >= 10
+    L = moeq.lib()
+    for s in syms:
+        assert hasattr(L, s), s
+    assert set(syms) == set(moeq.SYMBOLS)
+
+
+def test_status_strings():
+    for st in (0, -1, -2, -3, -4):
+        assert moeq.status_string(st) != "unknown status"
+    assert moeq.status_string(7) == "unknown status"
+
+
+def test_packed_bytes_and_workspace_queries():
+    assert moeq.moeq_packed_bytes(moeq.Q4_K, 512, 2048) == 512 * 8 * 144
+    assert moeq.moeq_packed_bytes(moeq.Q6_K, 2048, 512) == 2048 * 2 * 210
+    assert moeq.moeq_packed_bytes(moeq.Q2_K, 1, 256) == 256 * 3          # three planes, each padded
+    assert moeq.moeq_packed_bytes(9, 1, 256) == 0
+    assert moeq.moeq_packed_bytes(moeq.Q4_K, 1, 100) == 0
+    assert moeq.moeq_route_workspace(1, 2048, 256, 8, 0) > 0
+
+
+def _desc(**kw):
+    d = moeq.FfnDesc()
+    d.T, d.H, d.F, d.E, d.k = 1, 2048, 512, 256, 8
+    d.fmt_gate = d.fmt_up = moeq.Q4_K
+    d.fmt_down = moeq.Q6_K
+    d.gate = d.up = d.down = 0x1000
+    for k, v in kw.items():
+        setattr(d, k, v)
+    return d
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(H=2000), moeq.MOEQ_E_INVALID),
+    (dict(F=300), moeq.MOEQ_E_INVALID),
+    (dict(k=0), moeq.MOEQ_E_INVALID),
+    (dict(k=33), moeq.MOEQ_E_INVALID),
+    (dict(E=4097), moeq.MOEQ_E_INVALID),
+    (dict(fmt_down=7), moeq.MOEQ_E_UNSUPPORTED),
+    (dict(fmt_up=moeq.Q2_K), moeq.MOEQ_E_UNSUPPORTED),
+    (dict(gate=0), moeq.MOEQ_E_INVALID),
+    (dict(sh_gate=0x2000, F_shared=512, sh_fmt_gate=1, sh_fmt_up=1, sh_fmt_down=1), moeq.MOEQ_E_INVALID),
+    (dict(path=5), moeq.MOEQ_E_INVALID),
+    (dict(accumulate=2), moeq.MOEQ_E_INVALID),
+    (dict(H=256 * 40), moeq.MOEQ_E_UNSUPPORTED),
+])
+def test_ffn_rejects_bad_descriptors(kw, status):
+    d = _desc(**kw)
+    L = moeq.lib()
+    assert L.moeq_expert_ffn_workspace(ctypes.byref(d)) == 0
+    rc = L.moeq_expert_ffn(ctypes.byref(d), 0x1000, 0x1000, 0x1000, 0x1000, 0x1000, None, 0x1000, 0x100000,
+                           1 << 30, None)
+    assert rc == status
+
+
+def test_ffn_rejects_small_or_misaligned_workspace_and_null_inputs():
+    d = _desc()
+    L = moeq.lib()
+    need = L.moeq_expert_ffn_workspace(ctypes.byref(d))
+    assert need > 0
+    args = [0x1000, 0x1000, 0x1000, 0x1000, 0x1000, None, 0x1000]
+    assert L.moeq_expert_ffn(ctypes.byref(d), *args, 0x100000, need - 1, None) == moeq.MOEQ_E_WORKSPACE
+    assert L.moeq_expert_ffn(ctypes.byref(d), *args, 0x100010, need, None) == moeq.MOEQ_E_INVALID
+    bad = list(args)
+    bad[0] = None
+    assert L.moeq_expert_ffn(ctypes.byref(d), *bad, 0x100000, need, None) == moeq.MOEQ_E_INVALID
+    # T == 0 is a valid no-op
+    d0 = _desc(T=0)
+    assert L.moeq_expert_ffn(ctypes.byref(d0), None, None, None, None, None, None, None, None, 0, None) == 0
+
+
+def test_route_and_quantize_validation():
+    L = moeq.lib()
+    d = moeq.RouteDesc(4, 2048, 256, 8, 0, 1.0)
+    ws = L.moeq_route_workspace(ctypes.byref(d))
+    ok = dict(x=0x1000, w=0x2000, b=None, lg=None, ids=0x3000, tw=0x4000, off=0x5000, pairs=0x6000, act=0x7000)
+
+    def call(desc, ws_bytes=ws, wsp=0x100000, **over):
+        a = dict(ok, **over)
+        return L.moeq_route(ctypes.byref(desc), a["x"], a["w"], a["b"], a["lg"], a["ids"], a["tw"], a["off"],
+                            a["pairs"], a["act"], wsp, ws_bytes, None)
+
+    assert call(d, ws_bytes=ws - 1) == moeq.MOEQ_E_WORKSPACE
+    assert call(d, x=0x1004) == moeq.MOEQ_E_INVALID            # x must be 16-byte aligned
+    assert call(d, ids=None) == moeq.MOEQ_E_INVALID
+    assert call(moeq.RouteDesc(4, 2048, 256, 0, 0, 1.0)) == moeq.MOEQ_E_INVALID
+    assert call(moeq.RouteDesc(4, 2048, 4, 5, 0, 1.0)) == moeq.MOEQ_E_INVALID
+    assert call(moeq.RouteDesc(4, 2046, 256, 8, 0, 1.0)) == moeq.MOEQ_E_INVALID
+    assert call(moeq.RouteDesc(4, 2048, 256, 8, 3, 1.0)) == moeq.MOEQ_E_UNSUPPORTED
+    assert L.moeq_quantize_q8K(0x1000, 2, 300, 0x2000, None) == moeq.MOEQ_E_INVALID
+    assert L.moeq_quantize_q8K(None, 2, 256, 0x2000, None) == moeq.MOEQ_E_INVALID
+    assert L.moeq_quantize_q8K(0x1000, 0, 256, 0x2000, None) == 0
+    assert L.moeq_pack_experts(9, 0x1000, 1, 1, 256, 0x2000, None) == moeq.MOEQ_E_UNSUPPORTED
+    assert L.moeq_pack_experts(1, 0x1000, 1, 1, 256, 0x2010, None) == moeq.MOEQ_E_INVALID
+    assert L.moeq_debug_subdots(1, 0x1000, 1, 300, 0x2000, 1, 0x3000, None) == moeq.MOEQ_E_INVALID
