@@ -139,8 +139,7 @@ def main():
     def layer_step(l, stream=None):
         lay = layers[l]
         moeq.moeq_route(xs[l], lay["w_router"], None, cfg.k, cfg.gating, out=route_out, ws=route_ws,
-                        stream=stream)
-        moeq.moeq_quantize_q8K(xs[l], xq, stream)
+                        stream=stream, x_q8K=xq)
         moeq.moeq_expert_ffn(lay["desc"], xq, route_out.w, route_out.offsets, route_out.pairs,
                              route_out.active, None, y, ffn_ws, stream)
 

@@ -78,7 +78,7 @@ const char* moeq_status_string(int status);
 /*
  * q8_K quantisation of activation rows (Pulsar README, 'Fidelity notes':
  * activations go to q8_K before integer dots).  x: fp32 [rows, cols],
- * row-major, 4-byte aligned; cols % 256 == 0.  out: rows * cols/256 blocks of
+ * row-major, 16-byte aligned; cols % 256 == 0.  out: rows * cols/256 blocks of
  * 292 B, 4-byte aligned.  Per 256-block, in fp32 with round-half-even:
  * amax = max|x|; if amax == 0 or 127/amax overflows the block is all zero;
  * else id = 127/amax, q = clamp(rint(x*id), -127, 127), d = amax/127,
@@ -114,12 +114,14 @@ size_t moeq_route_workspace(const moeq_route_desc* d);
  *            offsets[e+1]) holds t*k+slot for every pair routed to e, t rising
  *   active   int32 [1 + min(E, T*k)]: active[0] = n experts with a pair,
  *            active[1..n] = those experts, ascending (the expert union)
+ *   x_q8K    q8_K rows of x [T, H/256 blocks] or NULL: when given (H % 256 == 0),
+ *            the router launch also quantises x exactly as moeq_quantize_q8K
  * T == 0 writes offsets = 0 and active[0] = 0.  ws: moeq_route_workspace bytes,
  * 256-byte aligned.
  */
 int moeq_route(const moeq_route_desc* d, const float* x, const float* w_router, const float* bias,
                double* logits, int32_t* topk_ids, float* topk_w, int32_t* expert_offsets,
-               int32_t* pairs, int32_t* active, void* ws, size_t ws_bytes, void* stream);
+               int32_t* pairs, int32_t* active, void* x_q8K, void* ws, size_t ws_bytes, void* stream);
 
 /* Bytes of one packed [rows, cols] matrix of format fmt (0 if unsupported). */
 size_t moeq_packed_bytes(int32_t fmt, int64_t rows, int64_t cols);

@@ -12,7 +12,7 @@ namespace {
 
 constexpr int64_t kMaxE = 4096;
 constexpr int kMaxK = 32;
-constexpr int kRowBlock = 64;     // rows per down work item (= combine block)
+constexpr int kRowBlock = 64;     // rows per expert-major down work item
 
 bool fmt_ok(int f) { return f == MOEQ_Q4_K || f == MOEQ_Q6_K || f == MOEQ_Q2_K || f == MOEQ_Q8_0; }
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
@@ -46,7 +46,7 @@ bool lane_geo(int fmt, int64_t cols, LaneGeo* g) {
 
 struct FfnLayout {
   int64_t Fmax, nrows;
-  size_t off_h, off_yp, off_hq, off_hqs, off_cnt, total;
+  size_t off_h, off_yp, off_hq, off_hqs, total;
 };
 FfnLayout ffn_layout(const moeq_ffn_desc* d) {
   FfnLayout L{};
@@ -58,7 +58,6 @@ FfnLayout ffn_layout(const moeq_ffn_desc* d) {
   L.off_yp = o;  o += align256((size_t)L.nrows * d->H * sizeof(double));
   L.off_hq = o;  o += align256((size_t)d->T * d->k * (d->F / 256) * kQ8KBytes);
   L.off_hqs = o; o += align256(sh ? (size_t)d->T * (d->F_shared / 256) * kQ8KBytes : 0);
-  L.off_cnt = o; o += align256((size_t)(d->H / kRowBlock + 1) * sizeof(int32_t));
   L.total = o;
   return L;
 }
@@ -108,7 +107,7 @@ const char* moeq_status_string(int status) {
 int moeq_quantize_q8K(const float* x, int64_t rows, int64_t cols, void* out, void* stream) {
   if (rows < 0 || cols <= 0 || cols % 256) return MOEQ_E_INVALID;
   if (rows == 0) return MOEQ_OK;
-  if (!x || !out || !aligned(x, 4) || !aligned(out, 4)) return MOEQ_E_INVALID;
+  if (!x || !out || !aligned(x, 16) || !aligned(out, 4)) return MOEQ_E_INVALID;
   return hip_status(launch_quantize_q8K(x, rows, cols, out, (hipStream_t)stream));
 }
 
@@ -119,7 +118,7 @@ size_t moeq_route_workspace(const moeq_route_desc* d) {
 
 int moeq_route(const moeq_route_desc* d, const float* x, const float* w_router, const float* bias,
                double* logits, int32_t* topk_ids, float* topk_w, int32_t* expert_offsets, int32_t* pairs,
-               int32_t* active, void* ws, size_t ws_bytes, void* stream) {
+               int32_t* active, void* x_q8K, void* ws, size_t ws_bytes, void* stream) {
   if (!d) return MOEQ_E_INVALID;
   if (d->T < 0 || d->H <= 0 || d->H % 4 || d->E < 1 || d->E > kMaxE) return MOEQ_E_INVALID;
   if (d->k < 1 || d->k > kMaxK || d->k > d->E) return MOEQ_E_INVALID;
@@ -130,11 +129,13 @@ int moeq_route(const moeq_route_desc* d, const float* x, const float* w_router, 
     if (!x || !w_router || !topk_ids || !topk_w || !pairs) return MOEQ_E_INVALID;
     if (!aligned(x, 16) || !aligned(w_router, 16) || (bias && !aligned(bias, 4))) return MOEQ_E_INVALID;
     if (logits && !aligned(logits, 8)) return MOEQ_E_INVALID;
+    if (x_q8K && (d->H % 256 || !aligned(x_q8K, 4))) return MOEQ_E_INVALID;
     if (!ws || !aligned(ws, 256)) return MOEQ_E_INVALID;
     if (ws_bytes < route_ws_bytes(d->T, d->E)) return MOEQ_E_WORKSPACE;
   }
   return hip_status(launch_route(d->T, d->H, d->E, d->k, d->gating, d->scale, x, w_router, bias, logits,
-                                 topk_ids, topk_w, expert_offsets, pairs, active, ws, (hipStream_t)stream));
+                                 topk_ids, topk_w, expert_offsets, pairs, active, x_q8K, ws,
+                                 (hipStream_t)stream));
 }
 
 size_t moeq_packed_bytes(int32_t fmt, int64_t rows, int64_t cols) {
@@ -171,14 +172,14 @@ int moeq_expert_ffn(const moeq_ffn_desc* d, const void* x_q8K, const float* topk
   hipStream_t s = (hipStream_t)stream;
   uint8_t* wsb = (uint8_t*)ws;
   const bool sh = d->sh_gate != nullptr;
-  const bool both = sh && d->sh_fmt_gate == d->fmt_gate && d->sh_fmt_down == d->fmt_down && d->F_shared == d->F;
+  const bool same_shape = sh && d->sh_fmt_gate == d->fmt_gate && d->sh_fmt_down == d->fmt_down &&
+                          d->F_shared == d->F;
+  const bool both = same_shape;
   const int tt = d->T == 1 ? 1 : 4;
   const int max_union = (int)std::min<int64_t>(d->E, d->T * d->k);
-  int32_t* cnt = (int32_t*)(wsb + L.off_cnt);
-  const int n_cnt = (int)(d->H / kRowBlock);
 
-  // ---- gate/up
-  auto gateup = [&](int mode, int fmt, int64_t F, int n_slots, int32_t* zero_cnt) -> int {
+  // ---- gate/up: h[pair, f] = fl32(silu(g) u)
+  auto gateup = [&](int mode, int fmt, int64_t F, int n_slots) -> int {
     LaneGeo g;
     lane_geo(fmt, d->H, &g);
     GateUpArgs a{};
@@ -189,14 +190,12 @@ int moeq_expert_ffn(const moeq_ffn_desc* d, const void* x_q8K, const float* topk
     a.max_union = max_union;
     a.hbuf = (float*)(wsb + L.off_h); a.hstride = L.Fmax;
     a.lpr = g.lpr; a.cpr = g.cpr; a.steps = std::max(1, 4 / g.rps);
-    a.cnt = zero_cnt; a.n_cnt = n_cnt;
     const int rows_per_wg = 4 * a.steps * g.rps;
     dim3 grid((unsigned)((F + rows_per_wg - 1) / rows_per_wg), (unsigned)n_slots);
     return launch_gateup(fmt, tt, g.cpl, grid, a, s);
   };
-  auto down = [&](int mode, int fmt, int64_t F, int n_slots) -> int {
-    LaneGeo g;
-    lane_geo(fmt, F, &g);
+  auto down_args = [&](int mode, int fmt, int64_t F, LaneGeo* g) {
+    lane_geo(fmt, F, g);
     DownArgs a{};
     a.gate = d->gate; a.up = d->up; a.down = d->down; a.sh_down = (const uint8_t*)d->sh_down;
     a.mode = mode; a.T = d->T; a.H = d->H; a.F = F; a.k = d->k;
@@ -207,17 +206,30 @@ int moeq_expert_ffn(const moeq_ffn_desc* d, const void* x_q8K, const float* topk
     a.hq = wsb + L.off_hq;
     a.hq_sh = sh ? wsb + L.off_hqs : nullptr;
     a.hq_stride = (F / 256) * kQ8KBytes;
-    a.lpr = g.lpr; a.cpr = g.cpr; a.rb = kRowBlock; a.steps = kRowBlock / (4 * g.rps);
-    a.cnt = cnt; a.has_shared = sh ? 1 : 0;
+    a.lpr = g->lpr; a.cpr = g->cpr; a.rb = kRowBlock; a.steps = kRowBlock / (4 * g->rps);
+    a.has_shared = sh ? 1 : 0;
     a.y = y; a.accumulate = d->accumulate;
-    dim3 grid((unsigned)n_cnt, (unsigned)n_slots);
+    return a;
+  };
+  auto down = [&](int mode, int fmt, int64_t F, int n_slots) -> int {
+    LaneGeo g;
+    DownArgs a = down_args(mode, fmt, F, &g);
+    dim3 grid((unsigned)(d->H / kRowBlock), (unsigned)n_slots);
     return launch_down(fmt, tt, g.cpl, grid, a, s);
   };
+
   if (both) {
-    if ((rc = gateup(kModeBoth, d->fmt_gate, d->F, max_union + 1, cnt))) return hip_status(rc);
+    if ((rc = gateup(kModeBoth, d->fmt_gate, d->F, max_union + 1))) return hip_status(rc);
   } else {
-    if ((rc = gateup(kModeRouted, d->fmt_gate, d->F, max_union, cnt))) return hip_status(rc);
-    if (sh && (rc = gateup(kModeShared, d->sh_fmt_gate, d->F_shared, 1, nullptr))) return hip_status(rc);
+    if ((rc = gateup(kModeRouted, d->fmt_gate, d->F, max_union))) return hip_status(rc);
+    if (sh && (rc = gateup(kModeShared, d->sh_fmt_gate, d->F_shared, 1))) return hip_status(rc);
+  }
+  if (d->T == 1 && (!sh || same_shape) && d->k < 33) {
+    // one token: row-major down with the combine inside each workgroup
+    LaneGeo g;
+    DownArgs a = down_args(kModeBoth, d->fmt_down, d->F, &g);
+    dim3 grid((unsigned)((d->H + g.rps - 1) / g.rps));
+    return hip_status(launch_down_rows1(d->fmt_down, g.cpl, grid, a, s));
   }
   if (both) {
     if ((rc = down(kModeBoth, d->fmt_down, d->F, max_union + 1))) return hip_status(rc);
@@ -225,7 +237,8 @@ int moeq_expert_ffn(const moeq_ffn_desc* d, const void* x_q8K, const float* topk
     if ((rc = down(kModeRouted, d->fmt_down, d->F, max_union))) return hip_status(rc);
     if (sh && (rc = down(kModeShared, d->sh_fmt_down, d->F_shared, 1))) return hip_status(rc);
   }
-  return MOEQ_OK;
+  return hip_status(launch_combine((const double*)(wsb + L.off_yp), d->T, d->H, d->k, sh ? 1 : 0, y,
+                                   d->accumulate, s));
 }
 
 int moeq_ffn_h_view(const moeq_ffn_desc* d, void* ws, size_t ws_bytes, void** hq_routed, void** hq_shared) {

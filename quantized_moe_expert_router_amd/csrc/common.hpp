@@ -40,6 +40,64 @@ __device__ __forceinline__ uint32_t ld_u16(const uint8_t* p) {
   return *reinterpret_cast<const uint16_t*>(p);
 }
 
+// ---- DPP cross-lane moves (register to register, no LDS round trip).
+// Control codes of the gfx9 DPP encoding.
+constexpr int kDppXor1 = 0xB1;       // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4E;       // quad_perm [2,3,0,1]
+constexpr int kDppRowRor4 = 0x124;
+constexpr int kDppRowRor8 = 0x128;
+constexpr int kDppRowBcast15 = 0x142;
+constexpr int kDppRowBcast31 = 0x143;
+
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ int dpp_i(int old, int v) {
+  return __builtin_amdgcn_update_dpp(old, v, CTRL, ROW_MASK, 0xF, false);
+}
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ double dpp_d(double old, double v) {
+  int2 o = *reinterpret_cast<int2*>(&old), x = *reinterpret_cast<int2*>(&v), r;
+  r.x = __builtin_amdgcn_update_dpp(o.x, x.x, CTRL, ROW_MASK, 0xF, false);
+  r.y = __builtin_amdgcn_update_dpp(o.y, x.y, CTRL, ROW_MASK, 0xF, false);
+  return *reinterpret_cast<double*>(&r);
+}
+__device__ __forceinline__ double readlane_d(double v, int lane) {
+  int2 x = *reinterpret_cast<int2*>(&v), r;
+  r.x = __builtin_amdgcn_readlane(x.x, lane);
+  r.y = __builtin_amdgcn_readlane(x.y, lane);
+  return *reinterpret_cast<double*>(&r);
+}
+
+// (value, index) that comes first under (value desc, index asc).
+__device__ __forceinline__ void better(double& v, int& i, double ov, int oi) {
+  if (ov > v || (ov == v && oi < i)) { v = ov; i = oi; }
+}
+
+// Wave-wide arg-max under (value desc, index asc); every lane gets the winner.
+// Each step combines a lane with a partner from another lane set; lanes a
+// DPP move does not write keep their own value (neutral for the max).
+__device__ __forceinline__ void wave_argmax(double& v, int& i) {
+  better(v, i, dpp_d<kDppXor1>(v, v), dpp_i<kDppXor1>(i, i));
+  better(v, i, dpp_d<kDppXor2>(v, v), dpp_i<kDppXor2>(i, i));
+  better(v, i, dpp_d<kDppRowRor4>(v, v), dpp_i<kDppRowRor4>(i, i));
+  better(v, i, dpp_d<kDppRowRor8>(v, v), dpp_i<kDppRowRor8>(i, i));
+  better(v, i, dpp_d<kDppRowBcast15, 0xA>(v, v), dpp_i<kDppRowBcast15, 0xA>(i, i));
+  better(v, i, dpp_d<kDppRowBcast31, 0xC>(v, v), dpp_i<kDppRowBcast31, 0xC>(i, i));
+  v = readlane_d(v, 63);
+  i = __builtin_amdgcn_readlane(i, 63);
+}
+
+// Wave-wide fp64 sum; every lane gets the total.  The order of additions is
+// fixed by the lane pattern, so the result is deterministic.
+__device__ __forceinline__ double wave_sum(double v) {
+  v += dpp_d<kDppXor1>(0.0, v);
+  v += dpp_d<kDppXor2>(0.0, v);
+  v += dpp_d<kDppRowRor4>(0.0, v);
+  v += dpp_d<kDppRowRor8>(0.0, v);
+  v += dpp_d<kDppRowBcast15, 0xA>(0.0, v);
+  v += dpp_d<kDppRowBcast31, 0xC>(0.0, v);
+  return readlane_d(v, 63);
+}
+
 // SiLU in fp64: z / (1 + e^-z).
 __device__ __forceinline__ double silu64(double z) { return z / (1.0 + exp(-z)); }
 
@@ -48,6 +106,33 @@ __device__ __forceinline__ int q8_code(float x, float id) {
   float v = __builtin_rintf(__fmul_rn(x, id));
   v = fminf(fmaxf(v, -127.0f), 127.0f);
   return (int)v;
+}
+
+// q8_K of 256-block g of a row-major fp32 matrix with `cols` columns, by one
+// wave (4 elements per lane), identical to the definition: amax, then
+// id = 127/amax (correctly rounded), q = rint(x*id) clamped to +-127,
+// d = amax/127, per-16 sums; amax == 0 or an infinite id gives a zero block.
+__device__ __forceinline__ void quantize_block_wave(const float* __restrict__ x, int64_t cols, int64_t g,
+                                                    int64_t nblocks, uint8_t* __restrict__ out) {
+  if (g >= nblocks) return;
+  const int lane = lane_id();
+  const int64_t nb = cols / 256, row = g / nb, b = g % nb;
+  const float* xb = x + row * cols + b * 256 + 4 * lane;
+  const float4 v = *reinterpret_cast<const float4*>(xb);
+  float amax = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
+  amax = group_max(amax, kWave);
+  uint8_t* o = out + g * kQ8KBytes;
+  const float id = amax == 0.0f ? 0.0f : __fdiv_rn(127.0f, amax);
+  const bool zero = amax == 0.0f || __builtin_isinf(id);
+  int q0 = 0, q1 = 0, q2 = 0, q3 = 0;
+  if (!zero) { q0 = q8_code(v.x, id); q1 = q8_code(v.y, id); q2 = q8_code(v.z, id); q3 = q8_code(v.w, id); }
+  *reinterpret_cast<uint32_t*>(o + 4 + 4 * lane) =
+      (uint32_t)(q0 & 255) | ((uint32_t)(q1 & 255) << 8) | ((uint32_t)(q2 & 255) << 16) | ((uint32_t)(q3 & 255) << 24);
+  int s = q0 + q1 + q2 + q3;
+  s += __shfl_xor(s, 1, kWave);
+  s += __shfl_xor(s, 2, kWave);
+  if ((lane & 3) == 0) *reinterpret_cast<int16_t*>(o + 260 + 2 * (lane >> 2)) = (int16_t)s;
+  if (lane == 0) *reinterpret_cast<float*>(o) = zero ? 0.0f : __fdiv_rn(amax, 127.0f);
 }
 
 __host__ __device__ constexpr size_t align256(size_t n) { return (n + 255) & ~size_t(255); }

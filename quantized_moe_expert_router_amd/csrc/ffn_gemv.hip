@@ -54,29 +54,44 @@ __device__ __forceinline__ void slot_token(const Slot& s, int i, const int32_t* 
 template <int FMT, int TT, int CPL, int UNR>
 __global__ __launch_bounds__(256) void k_gateup(GateUpArgs a) {
   using L = Fmt<FMT>;
-  if (a.cnt != nullptr && blockIdx.x == 0 && blockIdx.y == 0)
-    for (int i = threadIdx.x; i < a.n_cnt; i += blockDim.x) a.cnt[i] = 0;
+  const int wave = threadIdx.x >> 6, lane = lane_id();
+  const int lpr = a.lpr, rps = kWave / lpr, rig = lane / lpr, lir = lane % lpr;
+  const int64_t nb = a.H / 256, nsb = a.F * nb, xrow = nb * kQ8KBytes;
+  int xw[TT][CPL][L::XDW], bs[TT][CPL][L::NBS];
+  double dx[TT][CPL];
+  if (TT == 1) {
+    // One token: its activation chunks do not depend on the routing, so their
+    // loads are issued before the slot lookup.
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) {
+      const int ch = lir + lpr * c;
+      if (ch < a.cpr) {
+        load_x_chunk<FMT>(a.xq, ch, xw[0][c], bs[0][c], dx[0][c]);
+      } else {
+#pragma unroll
+        for (int q = 0; q < L::XDW; ++q) xw[0][c][q] = 0;
+#pragma unroll
+        for (int q = 0; q < L::NBS; ++q) bs[0][c][q] = 0;
+        dx[0][c] = 0.0;
+      }
+    }
+  }
   const Slot sl = decode_slot(blockIdx.y, a.mode, a.max_union, a.active, a.offsets, a.T);
   if (!sl.valid) return;
   const uint8_t* Wg = sl.shared ? a.sh_gate : (const uint8_t*)a.gate[sl.e];
   const uint8_t* Wu = sl.shared ? a.sh_up : (const uint8_t*)a.up[sl.e];
   if (Wg == nullptr || Wu == nullptr) return;   // not resident: its pairs add nothing
   if (!sl.shared && a.down[sl.e] == nullptr) return;
-
-  const int wave = threadIdx.x >> 6, lane = lane_id();
-  const int lpr = a.lpr, rps = kWave / lpr, rig = lane / lpr, lir = lane % lpr;
-  const int64_t nb = a.H / 256, nsb = a.F * nb, xrow = nb * kQ8KBytes;
   const int64_t row0 = (int64_t)blockIdx.x * (4 * a.steps * rps) + (int64_t)wave * a.steps * rps + rig;
 
   for (int tile = 0; tile < sl.n; tile += TT) {
     int tok[TT];
     int64_t prow[TT];
-    int xw[TT][CPL][L::XDW], bs[TT][CPL][L::NBS];
-    double dx[TT][CPL];
 #pragma unroll
     for (int i = 0; i < TT; ++i) {
       tok[i] = -1; prow[i] = 0;
       if (tile + i < sl.n) slot_token(sl, tile + i, a.pairs, a.T, a.k, tok[i], prow[i]);
+      if (TT == 1) continue;   // already loaded (token 0)
 #pragma unroll
       for (int c = 0; c < CPL; ++c) {
         const int ch = lir + lpr * c;
@@ -194,7 +209,6 @@ __device__ __forceinline__ void quant_h_chunks(const float* __restrict__ hrow, i
 template <int FMT, int TT, int CPL, int UNR>
 __global__ __launch_bounds__(256) void k_down(DownArgs a) {
   using L = Fmt<FMT>;
-  __shared__ int s_last;
   const Slot sl = decode_slot(blockIdx.y, a.mode, a.max_union, a.active, a.offsets, a.T);
   if (!sl.valid) return;
   // An expert is resident only if all three of its matrices are present.
@@ -272,34 +286,95 @@ __global__ __launch_bounds__(256) void k_down(DownArgs a) {
     }
   }
 
-  // Arrive on this row block; the last arrival combines it.
-  __threadfence();
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    const int total = a.active[0] + a.has_shared;
-    const int old = atomicAdd(&a.cnt[blockIdx.x], 1);
-    s_last = old == total - 1;
+}
+
+// y[t] (=|+=) fl32(sum_slot yp[t*k+slot] + yp[T*k+t]), slots in rank order,
+// then the shared expert: the per-pair outputs were staged by k_down.
+__global__ __launch_bounds__(256) void k_combine(const double* __restrict__ yp, int64_t T, int64_t H, int k,
+                                                 int has_shared, float* __restrict__ y, int accumulate) {
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= T * H) return;
+  const int64_t t = idx / H, r = idx % H;
+  double acc = 0.0;
+  for (int s = 0; s < k; ++s) acc += yp[(t * k + s) * H + r];
+  if (has_shared) acc += yp[(T * k + t) * H + r];
+  y[idx] = accumulate ? (float)((double)y[idx] + acc) : (float)acc;
+}
+
+// One token (decode).  A workgroup owns rps output rows (one wave step) for
+// every selected expert and the shared one: waves take slots round-robin,
+// rebuild q8_K(h) of their slot in registers, and leave w * (W_d h^) per
+// (slot rank, row) in LDS; the sum over slots in rank order, then the shared
+// expert, happens in the workgroup.  No data crosses workgroups.
+template <int FMT, int CPL>
+__global__ __launch_bounds__(256) void k_down_rows1(DownArgs a) {
+  using L = Fmt<FMT>;
+  constexpr int kMaxSlots = 33, kMaxRps = 16;
+  __shared__ double yps[kMaxSlots][kMaxRps];
+  const int wave = threadIdx.x >> 6, lane = lane_id();
+  const int lpr = a.lpr, rps = kWave / lpr, rig = lane / lpr, lir = lane % lpr;
+  const int64_t nb = a.F / 256, nsb = a.H * nb;
+  const int64_t row = (int64_t)blockIdx.x * rps + rig;
+  const int n_routed = a.active[0];
+  const int n_slots = n_routed + a.has_shared;
+  for (int s = wave; s < n_slots; s += 4) {
+    const bool shared = s >= n_routed;
+    int64_t prow;
+    double wt;
+    const uint8_t* Wd;
+    if (shared) {
+      prow = a.k;
+      wt = a.shared_scale ? (double)a.shared_scale[0] : 1.0;
+      Wd = a.sh_down;
+    } else {
+      const int e = a.active[1 + s];
+      prow = a.pairs[a.offsets[e]];
+      wt = (double)a.topk_w[prow];
+      Wd = (const uint8_t*)a.down[e];
+      if (a.gate[e] == nullptr || a.up[e] == nullptr) Wd = nullptr;
+    }
+    typename L::W wd[CPL];
+    bool ok[CPL];
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) {
+      const int ch = lir + lpr * c;
+      ok[c] = Wd != nullptr && ch < a.cpr && row < a.H;
+      if (ok[c]) wd[c] = L::load(Wd, (size_t)nsb, (size_t)(row * nb + ch / L::CPS), ch % L::CPS);
+    }
+    int xw[CPL][L::XDW], bs[CPL][L::NBS];
+    double dx[CPL];
+    uint8_t* dbg = nullptr;
+    uint8_t* hq_base = shared ? a.hq_sh : a.hq;
+    if (blockIdx.x == 0 && rig == 0 && hq_base != nullptr && Wd != nullptr)
+      dbg = hq_base + (shared ? 0 : prow) * a.hq_stride;
+    quant_h_chunks<FMT, CPL>(a.hbuf + prow * a.hstride, lir, lpr, a.cpr, Wd != nullptr, xw, bs, dx, dbg);
+    double ay = 0.0;
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) {
+      if (!ok[c]) continue;
+      int is[L::SPC];
+      L::isums(wd[c], xw[c], bs[c], is);
+      ay += L::term(wd[c], (lir + lpr * c) % L::CPS, is, bs[c], dx[c]);
+    }
+    const double yv = group_sum(ay, lpr);
+    if (lir == 0) yps[shared ? a.k : prow][rig] = wt * yv;
   }
   __syncthreads();
-  if (!s_last) return;
-  __threadfence();
-  const int64_t r0 = (int64_t)blockIdx.x * a.rb;
-  for (int64_t idx = threadIdx.x; idx < a.T * a.rb; idx += blockDim.x) {
-    const int64_t t = idx / a.rb, r = r0 + idx % a.rb;
-    if (r >= a.H) continue;
-    double acc = 0.0;
-    for (int s = 0; s < a.k; ++s) acc += a.yp[(t * a.k + s) * a.H + r];
-    if (a.has_shared) acc += a.yp[(a.T * a.k + t) * a.H + r];
-    float* yo = a.y + t * a.H + r;
-    *yo = a.accumulate ? (float)((double)*yo + acc) : (float)acc;
+  if (threadIdx.x < rps) {
+    const int64_t r = (int64_t)blockIdx.x * rps + threadIdx.x;
+    if (r < a.H) {
+      double acc = 0.0;
+      for (int p = 0; p < a.k; ++p) acc += yps[p][threadIdx.x];
+      if (a.has_shared) acc += yps[a.k][threadIdx.x];
+      a.y[r] = a.accumulate ? (float)((double)a.y[r] + acc) : (float)acc;
+    }
   }
-  if (threadIdx.x == 0) a.cnt[blockIdx.x] = 0;
 }
 
 // ------------------------------------------------------------ dispatch
 
 #define MOEQ_GU(F, TT, C) \
-  hipLaunchKernelGGL((k_gateup<F, TT, C, 2>), grid, dim3(256), 0, s, a)
+  hipLaunchKernelGGL((k_gateup<F, TT, C, (TT == 1 ? 4 : 2)>), grid, dim3(256), 0, s, a)
 #define MOEQ_DN(F, TT, C) \
   hipLaunchKernelGGL((k_down<F, TT, C, 2>), grid, dim3(256), 0, s, a)
 
@@ -332,6 +407,24 @@ int launch_gateup(int fmt, int tt, int cpl, dim3 grid, const GateUpArgs& a, hipS
 int launch_down(int fmt, int tt, int cpl, dim3 grid, const DownArgs& a, hipStream_t s) {
   if (grid.x == 0 || grid.y == 0) return 0;
   MOEQ_SWITCH_FMT(MOEQ_DN)
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+#define MOEQ_R1(F, TT, C) hipLaunchKernelGGL((k_down_rows1<F, C>), grid, dim3(256), 0, s, a)
+
+int launch_down_rows1(int fmt, int cpl, dim3 grid, const DownArgs& a, hipStream_t s) {
+  if (grid.x == 0) return 0;
+  const int tt = 1;
+  MOEQ_SWITCH_FMT(MOEQ_R1)
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+int launch_combine(const double* yp, int64_t T, int64_t H, int k, int has_shared, float* y, int accumulate,
+                   hipStream_t s) {
+  const int64_t n = T * H;
+  if (n == 0) return 0;
+  hipLaunchKernelGGL(k_combine, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, yp, T, H, k, has_shared, y,
+                     accumulate);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 

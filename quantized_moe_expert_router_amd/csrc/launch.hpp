@@ -27,8 +27,6 @@ struct GateUpArgs {
   float* hbuf;                  // fp32 [T*k + T, hstride]
   int64_t hstride;
   int lpr, cpr, steps;
-  int32_t* cnt;                 // down-combine counters zeroed by block (0,0), or null
-  int n_cnt;
 };
 
 struct DownArgs {
@@ -52,7 +50,6 @@ struct DownArgs {
   uint8_t* hq_sh;               // q8_K(h) rows of the shared expert [T], or null
   int64_t hq_stride;            // bytes per row for this launch's F
   int lpr, cpr, steps, rb;      // rb = rows per work item = 4 * steps * (64 / lpr)
-  int32_t* cnt;                 // [H / rb] arrival counters
   int has_shared;
   float* y;
   int accumulate;
@@ -66,8 +63,11 @@ int launch_subdots(int fmt, const void* w, int64_t rows, int64_t cols, const voi
 size_t route_ws_bytes(int64_t T, int64_t E);
 int launch_route(int64_t T, int64_t H, int64_t E, int k, int gating, float scale, const float* x,
                  const float* W, const float* bias, double* logits, int32_t* ids, float* w,
-                 int32_t* offsets, int32_t* pairs, int32_t* active, void* ws, hipStream_t s);
+                 int32_t* offsets, int32_t* pairs, int32_t* active, void* xq, void* ws, hipStream_t s);
 int launch_gateup(int fmt, int tt, int cpl, dim3 grid, const GateUpArgs& a, hipStream_t s);
 int launch_down(int fmt, int tt, int cpl, dim3 grid, const DownArgs& a, hipStream_t s);
+int launch_down_rows1(int fmt, int cpl, dim3 grid, const DownArgs& a, hipStream_t s);
+int launch_combine(const double* yp, int64_t T, int64_t H, int k, int has_shared, float* y, int accumulate,
+                   hipStream_t s);
 
 }  // namespace moeq

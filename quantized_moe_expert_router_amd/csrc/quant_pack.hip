@@ -4,38 +4,9 @@
 
 namespace moeq {
 
-// One wave per 256-block: 4 elements per lane.  fp32 arithmetic identical to
-// the definition: amax, id = 127/amax (correctly rounded), q = rint(x*id)
-// clamped to +-127, d = amax/127, per-16 sums.  A block with amax == 0 or an
-// infinite id is written as zeros.
 __global__ __launch_bounds__(256) void k_quantize_q8K(const float* __restrict__ x, int64_t rows,
                                                       int64_t cols, uint8_t* __restrict__ out) {
-  const int64_t nb = cols / 256;
-  const int64_t g = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (g >= rows * nb) return;
-  const int lane = lane_id();
-  const int64_t row = g / nb, b = g % nb;
-  const float* xb = x + row * cols + b * 256 + 4 * lane;
-  float v0 = xb[0], v1 = xb[1], v2 = xb[2], v3 = xb[3];
-  float amax = fmaxf(fmaxf(fabsf(v0), fabsf(v1)), fmaxf(fabsf(v2), fabsf(v3)));
-  amax = group_max(amax, kWave);
-  uint8_t* o = out + g * kQ8KBytes;
-  float id = amax == 0.0f ? 0.0f : __fdiv_rn(127.0f, amax);
-  if (amax == 0.0f || __builtin_isinf(id)) {
-    *reinterpret_cast<uint32_t*>(o + 4 + 4 * lane) = 0u;
-    if ((lane & 3) == 0) *reinterpret_cast<int16_t*>(o + 260 + 2 * (lane >> 2)) = 0;
-    if (lane == 0) *reinterpret_cast<float*>(o) = 0.0f;
-    return;
-  }
-  int q0 = q8_code(v0, id), q1 = q8_code(v1, id), q2 = q8_code(v2, id), q3 = q8_code(v3, id);
-  uint32_t packed = (uint32_t)(q0 & 255) | ((uint32_t)(q1 & 255) << 8) | ((uint32_t)(q2 & 255) << 16) |
-                    ((uint32_t)(q3 & 255) << 24);
-  *reinterpret_cast<uint32_t*>(o + 4 + 4 * lane) = packed;
-  int s = q0 + q1 + q2 + q3;
-  s += __shfl_xor(s, 1, kWave);
-  s += __shfl_xor(s, 2, kWave);
-  if ((lane & 3) == 0) *reinterpret_cast<int16_t*>(o + 260 + 2 * (lane >> 2)) = (int16_t)s;
-  if (lane == 0) *reinterpret_cast<float*>(o) = __fdiv_rn(amax, 127.0f);
+  quantize_block_wave(x, cols, (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6), rows * (cols / 256), out);
 }
 
 int launch_quantize_q8K(const float* x, int64_t rows, int64_t cols, void* out, hipStream_t s) {

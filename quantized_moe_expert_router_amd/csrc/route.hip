@@ -15,101 +15,121 @@ constexpr int kChunkT = 256;        // tokens per chunk of the multi-kernel list
 
 // logits[t, e] = sum_i W[e, i] * x[t, i] (+ bias[e]) in fp64.  The fp32*fp32
 // products are exact in fp64, so fma and mul+add agree; only the summation
-// order differs from a sequential sum.  One wave per expert, 16 tokens per tile.
+// order differs from a sequential sum.  One workgroup per expert: each of its
+// four waves sums a quarter of the row (all loads of a step in flight), then
+// the four partials are added in wave order.  Extra workgroups past the
+// experts quantise x to q8_K (one wave per 256-block), so the router and the
+// activation quantisation share one launch.
 __global__ __launch_bounds__(256) void k_logits(const float* __restrict__ x, const float* __restrict__ W,
                                                 const float* __restrict__ bias, int64_t T, int64_t H,
-                                                int64_t E, double* __restrict__ logits) {
-  const int64_t e = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (e >= E) return;
-  const int lane = lane_id();
-  const int64_t t0 = (int64_t)blockIdx.y * kLogitTok;
-  const int nt = (int)((T - t0) < kLogitTok ? (T - t0) : kLogitTok);
-  double acc[kLogitTok];
-#pragma unroll
-  for (int t = 0; t < kLogitTok; ++t) acc[t] = 0.0;
+                                                int64_t E, double* __restrict__ logits,
+                                                uint8_t* __restrict__ xq) {
+  const int wave = threadIdx.x >> 6, lane = lane_id();
+  if ((int64_t)blockIdx.x >= E) {
+    if (xq != nullptr && blockIdx.y == 0) quantize_block_wave(x, H, (int64_t)(blockIdx.x - E) * 4 + wave, T * (H / 256), xq);
+    return;
+  }
+  __shared__ double part[4][kLogitTok];
+  const int64_t e = blockIdx.x;
+  const int64_t n4 = H / 4, q4 = (n4 + 3) / 4;             // float4s per wave
+  const int64_t i0 = wave * q4, i1 = (i0 + q4) < n4 ? (i0 + q4) : n4;
   const float4* w4 = reinterpret_cast<const float4*>(W + e * H);
-  const int64_t n4 = H / 4;
-  for (int64_t i = lane; i < n4; i += kWave) {
-    const float4 w = w4[i];
+  for (int64_t t0 = (int64_t)blockIdx.y * kLogitTok; t0 < T; t0 += (int64_t)gridDim.y * kLogitTok) {
+    const int nt = (int)((T - t0) < kLogitTok ? (T - t0) : kLogitTok);
+    double acc[kLogitTok];
 #pragma unroll
-    for (int t = 0; t < kLogitTok; ++t) {
-      if (t < nt) {
-        const float4 xv = reinterpret_cast<const float4*>(x + (t0 + t) * H)[i];
-        double a = acc[t];
-        a = fma((double)w.x, (double)xv.x, a);
-        a = fma((double)w.y, (double)xv.y, a);
-        a = fma((double)w.z, (double)xv.z, a);
-        a = fma((double)w.w, (double)xv.w, a);
-        acc[t] = a;
+    for (int t = 0; t < kLogitTok; ++t) acc[t] = 0.0;
+    for (int64_t i = i0 + lane; i < i1; i += 4 * kWave) {
+      float4 w[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) w[u] = (i + u * kWave < i1) ? w4[i + u * kWave] : make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+      for (int t = 0; t < kLogitTok; ++t) {
+        if (t < nt) {
+          const float4* x4 = reinterpret_cast<const float4*>(x + (t0 + t) * H);
+          double a = acc[t];
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            if (i + u * kWave < i1) {
+              const float4 xv = x4[i + u * kWave];
+              a = fma((double)w[u].x, (double)xv.x, a);
+              a = fma((double)w[u].y, (double)xv.y, a);
+              a = fma((double)w[u].z, (double)xv.z, a);
+              a = fma((double)w[u].w, (double)xv.w, a);
+            }
+          }
+          acc[t] = a;
+        }
       }
     }
-  }
-  const double b = bias ? (double)bias[e] : 0.0;
 #pragma unroll
-  for (int t = 0; t < kLogitTok; ++t) {
-    double v = group_sum(acc[t], kWave);
-    if (lane == 0 && t < nt) logits[(t0 + t) * E + e] = bias ? v + b : v;
+    for (int t = 0; t < kLogitTok; ++t) {
+      const double v = wave_sum(acc[t]);
+      if (lane == 0) part[wave][t] = v;
+    }
+    __syncthreads();
+    if (threadIdx.x < nt) {
+      const int t = threadIdx.x;
+      double v = ((part[0][t] + part[1][t]) + part[2][t]) + part[3][t];
+      if (bias) v += (double)bias[e];
+      logits[(t0 + t) * E + e] = v;
+    }
+    __syncthreads();
   }
 }
 
-// Top-k of one logits row by one wave; writes ids and gate weights.  The k
-// winners are found one at a time: each lane scans its stripe (elements lane,
-// lane+64, ...), skipping taken ones, then a butterfly keeps the larger logit,
-// the lower index on a tie.
+// Top-k of one logits row by one wave, logits held in registers (NPER per
+// lane, element lane + 64*i).  Each round takes the first remaining element
+// under (logit desc, index asc) with a DPP arg-max.  Lane s ends holding the
+// s-th winner; gate weights are computed in fp64 in parallel over the k lanes
+// and normalised by a fixed-order wave sum.
+template <int NPER>
 __device__ void topk_row_wave(const double* __restrict__ row, int64_t E, int k, int gating, float scale,
-                              int32_t* __restrict__ ids_out, float* __restrict__ w_out, double* sel_v,
-                              int* sel_i, int32_t* ids_lds) {
+                              int32_t* __restrict__ ids_out, float* __restrict__ w_out, int32_t* ids_lds) {
   const int lane = lane_id();
-  const int nper = (int)((E + kWave - 1) / kWave);
+  double v[NPER];
+#pragma unroll
+  for (int i = 0; i < NPER; ++i) {
+    const int64_t e = lane + (int64_t)kWave * i;
+    v[i] = e < E ? row[e] : -INFINITY;
+  }
   uint64_t taken = 0;
+  double my_v = 0.0;
+  int my_i = 0;
   for (int s = 0; s < k; ++s) {
     double best = -INFINITY;
     int bi = INT_MAX;
-    for (int i = 0; i < nper; ++i) {
-      const int64_t e = lane + (int64_t)kWave * i;
-      if (e < E && !((taken >> i) & 1ull)) {
-        const double v = row[e];
-        if (v > best || (v == best && (int)e < bi)) { best = v; bi = (int)e; }
-      }
-    }
 #pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-      const double ov = __shfl_xor(best, o, kWave);
-      const int oi = __shfl_xor(bi, o, kWave);
-      if (ov > best || (ov == best && oi < bi)) { best = ov; bi = oi; }
+    for (int i = 0; i < NPER; ++i) {
+      const int e = lane + kWave * i;
+      if (e < E && !((taken >> i) & 1ull)) better(best, bi, v[i], e);
     }
+    wave_argmax(best, bi);
     if ((bi & (kWave - 1)) == lane) taken |= 1ull << (bi / kWave);
-    if (lane == 0) { sel_v[s] = best; sel_i[s] = bi; }
+    if (lane == s) { my_v = best; my_i = bi; }
   }
-  // softmax-all needs the partition function over every logit.
-  double zall = 0.0;
+  const double mx = readlane_d(my_v, 0);
+  double num = 0.0;
+  if (lane < k) num = gating == 2 ? 1.0 / (1.0 + exp(-my_v)) : exp(my_v - mx);
+  double z;
   if (gating == 1) {
-    const double mx = __shfl(sel_v[0], 0, kWave);
     double part = 0.0;
-    for (int i = 0; i < nper; ++i) {
+#pragma unroll
+    for (int i = 0; i < NPER; ++i) {
       const int64_t e = lane + (int64_t)kWave * i;
-      if (e < E) part += exp(row[e] - mx);
+      if (e < E) part += exp(v[i] - mx);
     }
-    zall = group_sum(part, kWave);
+    z = wave_sum(part);
+  } else {
+    z = wave_sum(num);
   }
-  if (lane == 0) {
-    const double mx = sel_v[0];
-    double z = 0.0;
-    if (gating == 0) {
-      for (int s = 0; s < k; ++s) z += exp(sel_v[s] - mx);
-    } else if (gating == 1) {
-      z = zall;
-    } else {
-      for (int s = 0; s < k; ++s) z += 1.0 / (1.0 + exp(-sel_v[s]));
-    }
-    for (int s = 0; s < k; ++s) {
-      const double num = gating == 2 ? 1.0 / (1.0 + exp(-sel_v[s])) : exp(sel_v[s] - mx);
-      ids_out[s] = sel_i[s];
-      w_out[s] = (float)(num / z * (double)scale);
-      if (ids_lds) ids_lds[s] = sel_i[s];
-    }
+  if (lane < k) {
+    ids_out[lane] = my_i;
+    w_out[lane] = (float)(num / z * (double)scale);
+    if (ids_lds) ids_lds[lane] = my_i;
   }
 }
+
 
 // Exclusive scan over a block of blockDim.x threads (a multiple of 64).
 __device__ int block_exclusive_scan(int v, int* tmp /* >= 16 ints */, int* total) {
@@ -168,20 +188,18 @@ __device__ void offsets_and_union(int* cnt, int64_t E, int32_t* offsets, int32_t
 }
 
 // T <= kSmallT: top-k for every token, then the lists, in one workgroup.
+template <int NPER>
 __global__ __launch_bounds__(1024) void k_select_small(const double* __restrict__ logits, int64_t T, int64_t E,
                                                        int k, int gating, float scale, int32_t* __restrict__ ids,
                                                        float* __restrict__ w, int32_t* __restrict__ offsets,
                                                        int32_t* __restrict__ pairs, int32_t* __restrict__ active) {
-  extern __shared__ double lds_d[];
-  double* sel_v = lds_d;                                      // [16][32]
-  int* sel_i = reinterpret_cast<int*>(sel_v + 16 * 32);       // [16][32]
-  int* ids_s = sel_i + 16 * 32;                               // [T*k]
+  extern __shared__ int lds[];
+  int* ids_s = lds;                                           // [T*k]
   int* cnt = ids_s + T * k;                                   // [E]
   int* scan_tmp = cnt + E;                                    // [64]
   const int wv = threadIdx.x >> 6, nw = blockDim.x >> 6;
   for (int64_t t = wv; t < T; t += nw)
-    topk_row_wave(logits + t * E, E, k, gating, scale, ids + t * k, w + t * k, sel_v + 32 * wv,
-                  sel_i + 32 * wv, ids_s + t * k);
+    topk_row_wave<NPER>(logits + t * E, E, k, gating, scale, ids + t * k, w + t * k, ids_s + t * k);
   for (int64_t e = threadIdx.x; e < E; e += blockDim.x) cnt[e] = 0;
   __syncthreads();
   for (int64_t p = threadIdx.x; p < T * k; p += blockDim.x) atomicAdd(&cnt[ids_s[p]], 1);
@@ -203,15 +221,13 @@ __global__ __launch_bounds__(1024) void k_select_small(const double* __restrict_
 }
 
 // ---- multi-kernel path for large T
+template <int NPER>
 __global__ __launch_bounds__(256) void k_topk(const double* __restrict__ logits, int64_t T, int64_t E, int k,
                                               int gating, float scale, int32_t* __restrict__ ids,
                                               float* __restrict__ w) {
-  __shared__ double sel_v[4][32];
-  __shared__ int sel_i[4][32];
-  const int wv = threadIdx.x >> 6;
-  const int64_t t = (int64_t)blockIdx.x * 4 + wv;
+  const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
-  topk_row_wave(logits + t * E, E, k, gating, scale, ids + t * k, w + t * k, sel_v[wv], sel_i[wv], nullptr);
+  topk_row_wave<NPER>(logits + t * E, E, k, gating, scale, ids + t * k, w + t * k, nullptr);
 }
 
 __global__ __launch_bounds__(256) void k_hist(const int32_t* __restrict__ ids, int64_t T, int k, int64_t E,
@@ -279,24 +295,36 @@ size_t route_ws_bytes(int64_t T, int64_t E) {
 
 int launch_route(int64_t T, int64_t H, int64_t E, int k, int gating, float scale, const float* x,
                  const float* W, const float* bias, double* logits, int32_t* ids, float* w,
-                 int32_t* offsets, int32_t* pairs, int32_t* active, void* ws, hipStream_t s) {
+                 int32_t* offsets, int32_t* pairs, int32_t* active, void* xq, void* ws, hipStream_t s) {
   if (T == 0) {
     hipLaunchKernelGGL(k_empty_lists, dim3(1), dim3(256), 0, s, E, offsets, active);
     return hipGetLastError() == hipSuccess ? 0 : -1;
   }
   uint8_t* wsb = (uint8_t*)ws;
   double* lg = logits ? logits : reinterpret_cast<double*>(wsb);
-  dim3 g1((unsigned)((E + 3) / 4), (unsigned)((T + kLogitTok - 1) / kLogitTok));
-  hipLaunchKernelGGL(k_logits, g1, dim3(256), 0, s, x, W, bias, T, H, E, lg);
+  const int64_t nq = xq ? (T * (H / 256) + 3) / 4 : 0;
+  const int64_t tiles = (T + kLogitTok - 1) / kLogitTok;
+  dim3 g1((unsigned)(E + nq), (unsigned)(tiles < 64 ? tiles : 64));
+  hipLaunchKernelGGL(k_logits, g1, dim3(256), 0, s, x, W, bias, T, H, E, lg, (uint8_t*)xq);
   if (T <= kSmallT) {
-    size_t lds = (size_t)(T * k + E + 64) * sizeof(int) + 16 * 32 * (sizeof(double) + sizeof(int));
-    hipLaunchKernelGGL(k_select_small, dim3(1), dim3(1024), lds, s, lg, T, E, k, gating, scale, ids, w,
-                       offsets, pairs, active);
+    size_t lds = (size_t)(T * k + E + 64) * sizeof(int);
+#define MOEQ_SEL(N) hipLaunchKernelGGL(k_select_small<N>, dim3(1), dim3(1024), lds, s, lg, T, E, k, gating, \
+                                        scale, ids, w, offsets, pairs, active)
+    if (E <= 256) MOEQ_SEL(4);
+    else if (E <= 512) MOEQ_SEL(8);
+    else if (E <= 1024) MOEQ_SEL(16);
+    else MOEQ_SEL(64);
+#undef MOEQ_SEL
   } else {
     const int64_t nch = (T + kChunkT - 1) / kChunkT;
     int32_t* hist = reinterpret_cast<int32_t*>(wsb + align256((size_t)T * E * sizeof(double)));
-    hipLaunchKernelGGL(k_topk, dim3((unsigned)((T + 3) / 4)), dim3(256), 0, s, lg, T, E, k, gating, scale,
-                       ids, w);
+#define MOEQ_TOPK(N) hipLaunchKernelGGL(k_topk<N>, dim3((unsigned)((T + 3) / 4)), dim3(256), 0, s, lg, T, E, k, \
+                                         gating, scale, ids, w)
+    if (E <= 256) MOEQ_TOPK(4);
+    else if (E <= 512) MOEQ_TOPK(8);
+    else if (E <= 1024) MOEQ_TOPK(16);
+    else MOEQ_TOPK(64);
+#undef MOEQ_TOPK
     hipLaunchKernelGGL(k_hist, dim3((unsigned)nch), dim3(256), (size_t)E * sizeof(int), s, ids, T, k, E, hist);
     hipLaunchKernelGGL(k_scan, dim3(1), dim3(1024), (size_t)(E + 64) * sizeof(int), s, hist, nch, E, offsets,
                        active);

@@ -64,7 +64,7 @@ def lib() -> ctypes.CDLL:
         L.moeq_quantize_q8K.argtypes = [vp, i64, i64, vp, vp]
         L.moeq_route_workspace.restype = sz
         L.moeq_route_workspace.argtypes = [ctypes.POINTER(RouteDesc)]
-        L.moeq_route.argtypes = [ctypes.POINTER(RouteDesc), vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.moeq_route.argtypes = [ctypes.POINTER(RouteDesc), vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         L.moeq_packed_bytes.restype = sz
         L.moeq_packed_bytes.argtypes = [i32, i64, i64]
         L.moeq_pack_experts.argtypes = [i32, vp, i64, i64, i64, vp, vp]
@@ -133,7 +133,8 @@ def moeq_route_workspace(T: int, H: int, E: int, k: int, gating: int, scale: flo
 
 def moeq_route(x: torch.Tensor, w_router: torch.Tensor, bias: Optional[torch.Tensor], k: int, gating: int,
                scale: float = 1.0, out: Optional[RouteOut] = None, ws: Optional[torch.Tensor] = None,
-               stream=None) -> RouteOut:
+               stream=None, x_q8K: Optional[torch.Tensor] = None) -> RouteOut:
+    """Router + top-k + lists; with x_q8K given, the same launch also writes q8_K(x)."""
     _need(x, torch.float32, "x")
     _need(w_router, torch.float32, "w_router")
     if bias is not None:
@@ -147,8 +148,8 @@ def moeq_route(x: torch.Tensor, w_router: torch.Tensor, bias: Optional[torch.Ten
     if ws is None:
         ws = torch.empty(max(nws, 256), dtype=torch.uint8, device=x.device)
     rc = lib().moeq_route(ctypes.byref(d), _ptr(x), _ptr(w_router), _ptr(bias), _ptr(out.logits), _ptr(out.ids),
-                          _ptr(out.w), _ptr(out.offsets), _ptr(out.pairs), _ptr(out.active), _ptr(ws),
-                          ws.numel(), _stream(stream))
+                          _ptr(out.w), _ptr(out.offsets), _ptr(out.pairs), _ptr(out.active), _ptr(x_q8K),
+                          _ptr(ws), ws.numel(), _stream(stream))
     _check("moeq_route", rc)
     return out
 
@@ -297,14 +298,14 @@ class LayerRunner:
         self.y = torch.empty((T, c.H), dtype=torch.float32, device=dev)
         self.shared_scale = shared_scale
 
-    def route(self, x: torch.Tensor, stream=None):
+    def route(self, x: torch.Tensor, stream=None, with_q8K: bool = True):
         c = self.dl.cfg
         return moeq_route(x, self.dl.w_router, self.dl.bias, c.k, c.gating, out=self.route_out, ws=self.route_ws,
-                          stream=stream)
+                          stream=stream, x_q8K=self.xq if with_q8K else None)
 
     def forward(self, x: torch.Tensor, stream=None) -> torch.Tensor:
+        """route (+ q8_K(x) in the same launch) then the expert FFN."""
         self.route(x, stream)
-        moeq_quantize_q8K(x, self.xq, stream)
         return self.ffn(stream)
 
     def ffn(self, stream=None) -> torch.Tensor:

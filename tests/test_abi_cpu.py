@@ -96,22 +96,25 @@ def test_route_and_quantize_validation():
     L = moeq.lib()
     d = moeq.RouteDesc(4, 2048, 256, 8, 0, 1.0)
     ws = L.moeq_route_workspace(ctypes.byref(d))
-    ok = dict(x=0x1000, w=0x2000, b=None, lg=None, ids=0x3000, tw=0x4000, off=0x5000, pairs=0x6000, act=0x7000)
+    ok = dict(x=0x1000, w=0x2000, b=None, lg=None, ids=0x3000, tw=0x4000, off=0x5000, pairs=0x6000, act=0x7000,
+              xq=None)
 
     def call(desc, ws_bytes=ws, wsp=0x100000, **over):
         a = dict(ok, **over)
         return L.moeq_route(ctypes.byref(desc), a["x"], a["w"], a["b"], a["lg"], a["ids"], a["tw"], a["off"],
-                            a["pairs"], a["act"], wsp, ws_bytes, None)
+                            a["pairs"], a["act"], a["xq"], wsp, ws_bytes, None)
 
     assert call(d, ws_bytes=ws - 1) == moeq.MOEQ_E_WORKSPACE
     assert call(d, x=0x1004) == moeq.MOEQ_E_INVALID            # x must be 16-byte aligned
     assert call(d, ids=None) == moeq.MOEQ_E_INVALID
+    assert call(d, xq=0x8002) == moeq.MOEQ_E_INVALID           # q8_K output must be 4-byte aligned
     assert call(moeq.RouteDesc(4, 2048, 256, 0, 0, 1.0)) == moeq.MOEQ_E_INVALID
     assert call(moeq.RouteDesc(4, 2048, 4, 5, 0, 1.0)) == moeq.MOEQ_E_INVALID
     assert call(moeq.RouteDesc(4, 2046, 256, 8, 0, 1.0)) == moeq.MOEQ_E_INVALID
     assert call(moeq.RouteDesc(4, 2048, 256, 8, 3, 1.0)) == moeq.MOEQ_E_UNSUPPORTED
     assert L.moeq_quantize_q8K(0x1000, 2, 300, 0x2000, None) == moeq.MOEQ_E_INVALID
     assert L.moeq_quantize_q8K(None, 2, 256, 0x2000, None) == moeq.MOEQ_E_INVALID
+    assert L.moeq_quantize_q8K(0x1004, 2, 256, 0x2000, None) == moeq.MOEQ_E_INVALID   # x 16-byte aligned
     assert L.moeq_quantize_q8K(0x1000, 0, 256, 0x2000, None) == 0
     assert L.moeq_pack_experts(9, 0x1000, 1, 1, 256, 0x2000, None) == moeq.MOEQ_E_UNSUPPORTED
     assert L.moeq_pack_experts(1, 0x1000, 1, 1, 256, 0x2010, None) == moeq.MOEQ_E_INVALID

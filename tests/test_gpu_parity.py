@@ -240,7 +240,7 @@ def _custom_cfg(**kw):
 
 
 @pytest.mark.parametrize("variant", ["one_expert_all_tokens", "k_equals_E", "k1", "ties", "softmax_all",
-                                     "sigmoid", "q2k_q6k_q80_mix"])
+                                     "sigmoid", "q2k_q6k_q80_mix", "t1_mixed_shared", "t1_k32"])
 def test_edge_layers(variant):
     say("edge", variant)
     kw = {}
@@ -256,6 +256,12 @@ def test_edge_layers(variant):
     elif variant == "q2k_q6k_q80_mix":
         kw = dict(fmt_gate=syn.Q2_K, fmt_up=syn.Q2_K, fmt_down=syn.Q6_K, H=768, F=1536, T=5, E=9, k=3,
                   shared=True, F_shared=256, sh_fmt_gate=syn.Q6_K, sh_fmt_up=syn.Q6_K, sh_fmt_down=syn.Q8_0)
+    elif variant == "t1_mixed_shared":
+        kw = dict(T=1, E=12, k=4, fmt_down=syn.Q2_K, shared=True, F_shared=512, sh_fmt_gate=syn.Q8_0,
+                  sh_fmt_up=syn.Q8_0, sh_fmt_down=syn.Q6_K)
+    elif variant == "t1_k32":
+        kw = dict(T=1, E=40, k=32, fmt_down=syn.Q6_K, shared=True, F_shared=256, sh_fmt_gate=syn.Q4_K,
+                  sh_fmt_up=syn.Q4_K, sh_fmt_down=syn.Q6_K)
     cfg = _custom_cfg(**kw)
     layer = syn.gen_layer(cfg)
     if variant == "one_expert_all_tokens":
