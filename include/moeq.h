@@ -166,7 +166,8 @@ size_t moeq_expert_ffn_workspace(const moeq_ffn_desc* d);
 /*
  * Routed-expert FFN over the token x expert lists from moeq_route.
  *   x_q8K   q8_K rows of x [T, H/256 blocks]
- *   topk_w  fp32 [T, k]; expert_offsets, pairs, active as moeq_route writes them
+ *   topk_ids, topk_w  int32 / fp32 [T, k]; expert_offsets, pairs, active: all
+ *           as moeq_route writes them (the FFN trusts their consistency)
  *   shared_scale fp32 [T] or NULL (= 1.0 per token)
  *   y       fp32 [T, H]:  y[t] (=|+=) sum_slot topk_w[t,slot] * down_e(q8K(h))
  *                                    + shared_scale[t] * down_sh(q8K(h_sh))
@@ -176,9 +177,27 @@ size_t moeq_expert_ffn_workspace(const moeq_ffn_desc* d);
  * ws: moeq_expert_ffn_workspace bytes, 256-byte aligned; contents on entry
  * are ignored.
  */
-int moeq_expert_ffn(const moeq_ffn_desc* d, const void* x_q8K, const float* topk_w,
+int moeq_expert_ffn(const moeq_ffn_desc* d, const void* x_q8K, const int32_t* topk_ids, const float* topk_w,
                     const int32_t* expert_offsets, const int32_t* pairs, const int32_t* active,
                     const float* shared_scale, float* y, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * The whole hot path of one MoE layer in one call: moeq_route (with q8_K(x)
+ * into the workspace) followed by moeq_expert_ffn, with the same outputs and
+ * the same conventions.  r and f must agree on T, H, E and k.  For one token
+ * it enqueues three kernels: router logits with q8_K(x); gate/up, where every
+ * workgroup takes the top-k from the logits itself and one workgroup writes
+ * the routing outputs; down with the weighted combine.  Each launch boundary
+ * is the only synchronisation (per-layer launches are the floor of a decode
+ * step: Strata summary, execution paragraph).  For more tokens it runs the two
+ * calls back to back.  logits may be NULL; the FFN's q8_K(h) view
+ * (moeq_ffn_h_view with f and this ws) stays valid after the call.
+ */
+size_t moeq_moe_layer_workspace(const moeq_route_desc* r, const moeq_ffn_desc* f);
+int moeq_moe_layer(const moeq_route_desc* r, const moeq_ffn_desc* f, const float* x, const float* w_router,
+                   const float* bias, double* logits, int32_t* topk_ids, float* topk_w, int32_t* expert_offsets,
+                   int32_t* pairs, int32_t* active, const float* shared_scale, float* y, void* ws,
+                   size_t ws_bytes, void* stream);
 
 /*
  * Where a finished moeq_expert_ffn call left q8_K(h) inside `ws` (host

@@ -157,31 +157,34 @@ size_t moeq_expert_ffn_workspace(const moeq_ffn_desc* d) {
   return ffn_layout(d).total;
 }
 
-int moeq_expert_ffn(const moeq_ffn_desc* d, const void* x_q8K, const float* topk_w,
-                    const int32_t* expert_offsets, const int32_t* pairs, const int32_t* active,
-                    const float* shared_scale, float* y, void* ws, size_t ws_bytes, void* stream) {
-  int rc = check_ffn_desc(d);
-  if (rc != MOEQ_OK) return rc;
-  if (d->T == 0) return MOEQ_OK;
-  if (!x_q8K || !topk_w || !expert_offsets || !pairs || !active || !y) return MOEQ_E_INVALID;
-  if (!aligned(x_q8K, 4) || !aligned(y, 4) || !aligned(topk_w, 4)) return MOEQ_E_INVALID;
-  if (!ws || !aligned(ws, 256)) return MOEQ_E_INVALID;
-  const FfnLayout L = ffn_layout(d);
-  if (ws_bytes < L.total) return MOEQ_E_WORKSPACE;
+namespace {
 
-  hipStream_t s = (hipStream_t)stream;
-  uint8_t* wsb = (uint8_t*)ws;
+// Routing the one-token gate/up kernel does itself from the logits (fused
+// layer path); null when the routing comes from moeq_route.
+struct InlineRoute {
+  const double* logits;
+  int gating;
+  float scale;
+  int32_t *ids, *offsets, *pairs, *active;
+  float* w;
+};
+
+int nper_of(int64_t E) { return E <= 256 ? 4 : E <= 512 ? 8 : E <= 1024 ? 16 : 64; }
+
+// Enqueue the expert FFN (everything after the routing) on `s`.
+int ffn_enqueue(const moeq_ffn_desc* d, const void* x_q8K, const int32_t* topk_ids, const float* topk_w,
+                const int32_t* expert_offsets, const int32_t* pairs, const int32_t* active,
+                const float* shared_scale, float* y, uint8_t* wsb, const InlineRoute* ir, hipStream_t s) {
+  const FfnLayout L = ffn_layout(d);
   const bool sh = d->sh_gate != nullptr;
   const bool same_shape = sh && d->sh_fmt_gate == d->fmt_gate && d->sh_fmt_down == d->fmt_down &&
                           d->F_shared == d->F;
-  const bool both = same_shape;
-  const int tt = d->T == 1 ? 1 : 4;
+  const bool one = d->T == 1;
+  const int tt = one ? 1 : 4;
   const int max_union = (int)std::min<int64_t>(d->E, d->T * d->k);
+  int rc;
 
-  // ---- gate/up: h[pair, f] = fl32(silu(g) u)
-  auto gateup = [&](int mode, int fmt, int64_t F, int n_slots) -> int {
-    LaneGeo g;
-    lane_geo(fmt, d->H, &g);
+  auto gu_args = [&](int mode, int64_t F, const LaneGeo& g) {
     GateUpArgs a{};
     a.gate = d->gate; a.up = d->up; a.down = d->down;
     a.sh_gate = (const uint8_t*)d->sh_gate; a.sh_up = (const uint8_t*)d->sh_up;
@@ -190,13 +193,30 @@ int moeq_expert_ffn(const moeq_ffn_desc* d, const void* x_q8K, const float* topk
     a.max_union = max_union;
     a.hbuf = (float*)(wsb + L.off_h); a.hstride = L.Fmax;
     a.lpr = g.lpr; a.cpr = g.cpr; a.steps = std::max(1, 4 / g.rps);
+    a.topk_ids = topk_ids; a.E = d->E;
+    if (ir != nullptr) {
+      a.logits = ir->logits; a.gating = ir->gating; a.scale = ir->scale;
+      a.ids_out = ir->ids; a.w_out = ir->w; a.offsets_out = ir->offsets; a.pairs_out = ir->pairs;
+      a.active_out = ir->active;
+    }
+    return a;
+  };
+  auto gateup = [&](int mode, int fmt, int64_t F, int n_slots) -> int {
+    LaneGeo g;
+    lane_geo(fmt, d->H, &g);
+    GateUpArgs a = gu_args(mode, F, g);
     const int rows_per_wg = 4 * a.steps * g.rps;
     dim3 grid((unsigned)((F + rows_per_wg - 1) / rows_per_wg), (unsigned)n_slots);
+    if (one) {
+      const int nper = (ir != nullptr && mode != kModeShared) ? nper_of(d->E) : 0;
+      return launch_gateup1(fmt, nper, g.cpl, grid, a, s);
+    }
     return launch_gateup(fmt, tt, g.cpl, grid, a, s);
   };
   auto down_args = [&](int mode, int fmt, int64_t F, LaneGeo* g) {
     lane_geo(fmt, F, g);
     DownArgs a{};
+    a.topk_ids = topk_ids;
     a.gate = d->gate; a.up = d->up; a.down = d->down; a.sh_down = (const uint8_t*)d->sh_down;
     a.mode = mode; a.T = d->T; a.H = d->H; a.F = F; a.k = d->k;
     a.topk_w = topk_w; a.shared_scale = shared_scale;
@@ -218,27 +238,109 @@ int moeq_expert_ffn(const moeq_ffn_desc* d, const void* x_q8K, const float* topk
     return launch_down(fmt, tt, g.cpl, grid, a, s);
   };
 
-  if (both) {
-    if ((rc = gateup(kModeBoth, d->fmt_gate, d->F, max_union + 1))) return hip_status(rc);
+  // gate/up: h[pair, f] = fl32(silu(g) u)
+  const int n_routed_slots = one ? d->k : max_union;
+  if (same_shape) {
+    if ((rc = gateup(kModeBoth, d->fmt_gate, d->F, n_routed_slots + 1))) return rc;
   } else {
-    if ((rc = gateup(kModeRouted, d->fmt_gate, d->F, max_union))) return hip_status(rc);
-    if (sh && (rc = gateup(kModeShared, d->sh_fmt_gate, d->F_shared, 1))) return hip_status(rc);
+    if ((rc = gateup(kModeRouted, d->fmt_gate, d->F, n_routed_slots))) return rc;
+    if (sh && (rc = gateup(kModeShared, d->sh_fmt_gate, d->F_shared, 1))) return rc;
   }
-  if (d->T == 1 && (!sh || same_shape) && d->k < 33) {
-    // one token: row-major down with the combine inside each workgroup
+  // down and the weighted combine
+  if (one && (!sh || same_shape)) {
     LaneGeo g;
     DownArgs a = down_args(kModeBoth, d->fmt_down, d->F, &g);
     dim3 grid((unsigned)((d->H + g.rps - 1) / g.rps));
-    return hip_status(launch_down_rows1(d->fmt_down, g.cpl, grid, a, s));
+    return launch_down_rows1(d->fmt_down, g.cpl, grid, a, s);
   }
-  if (both) {
-    if ((rc = down(kModeBoth, d->fmt_down, d->F, max_union + 1))) return hip_status(rc);
+  if (same_shape) {
+    if ((rc = down(kModeBoth, d->fmt_down, d->F, max_union + 1))) return rc;
   } else {
-    if ((rc = down(kModeRouted, d->fmt_down, d->F, max_union))) return hip_status(rc);
-    if (sh && (rc = down(kModeShared, d->sh_fmt_down, d->F_shared, 1))) return hip_status(rc);
+    if ((rc = down(kModeRouted, d->fmt_down, d->F, max_union))) return rc;
+    if (sh && (rc = down(kModeShared, d->sh_fmt_down, d->F_shared, 1))) return rc;
   }
-  return hip_status(launch_combine((const double*)(wsb + L.off_yp), d->T, d->H, d->k, sh ? 1 : 0, y,
-                                   d->accumulate, s));
+  return launch_combine((const double*)(wsb + L.off_yp), d->T, d->H, d->k, sh ? 1 : 0, y, d->accumulate, s);
+}
+
+}  // namespace
+
+int moeq_expert_ffn(const moeq_ffn_desc* d, const void* x_q8K, const int32_t* topk_ids, const float* topk_w,
+                    const int32_t* expert_offsets, const int32_t* pairs, const int32_t* active,
+                    const float* shared_scale, float* y, void* ws, size_t ws_bytes, void* stream) {
+  int rc = check_ffn_desc(d);
+  if (rc != MOEQ_OK) return rc;
+  if (d->T == 0) return MOEQ_OK;
+  if (!x_q8K || !topk_ids || !topk_w || !expert_offsets || !pairs || !active || !y) return MOEQ_E_INVALID;
+  if (!aligned(x_q8K, 4) || !aligned(y, 4) || !aligned(topk_w, 4)) return MOEQ_E_INVALID;
+  if (!ws || !aligned(ws, 256)) return MOEQ_E_INVALID;
+  if (ws_bytes < ffn_layout(d).total) return MOEQ_E_WORKSPACE;
+  return hip_status(ffn_enqueue(d, x_q8K, topk_ids, topk_w, expert_offsets, pairs, active, shared_scale, y,
+                                (uint8_t*)ws, nullptr, (hipStream_t)stream));
+}
+
+namespace {
+struct LayerLayout {
+  size_t off_ffn, off_route, off_xq, total;
+};
+LayerLayout layer_layout(const moeq_route_desc* r, const moeq_ffn_desc* f) {
+  LayerLayout L{};
+  size_t o = 0;
+  L.off_ffn = o;   o += align256(ffn_layout(f).total);
+  L.off_route = o; o += align256(route_ws_bytes(r->T, r->E));
+  L.off_xq = o;    o += align256((size_t)r->T * (r->H / 256) * kQ8KBytes);
+  L.total = o;
+  return L;
+}
+int check_layer(const moeq_route_desc* r, const moeq_ffn_desc* f) {
+  if (!r || !f) return MOEQ_E_INVALID;
+  int rc = check_ffn_desc(f);
+  if (rc != MOEQ_OK) return rc;
+  if (r->T != f->T || r->H != f->H || r->E != f->E || r->k != f->k) return MOEQ_E_INVALID;
+  if (r->gating < MOEQ_SOFTMAX_TOPK || r->gating > MOEQ_SIGMOID_TOPK) return MOEQ_E_UNSUPPORTED;
+  return MOEQ_OK;
+}
+}  // namespace
+
+size_t moeq_moe_layer_workspace(const moeq_route_desc* r, const moeq_ffn_desc* f) {
+  if (check_layer(r, f) != MOEQ_OK) return 0;
+  return layer_layout(r, f).total;
+}
+
+int moeq_moe_layer(const moeq_route_desc* r, const moeq_ffn_desc* f, const float* x, const float* w_router,
+                   const float* bias, double* logits, int32_t* topk_ids, float* topk_w, int32_t* expert_offsets,
+                   int32_t* pairs, int32_t* active, const float* shared_scale, float* y, void* ws,
+                   size_t ws_bytes, void* stream) {
+  int rc = check_layer(r, f);
+  if (rc != MOEQ_OK) return rc;
+  if (r->T == 0) {
+    if (!expert_offsets || !active) return MOEQ_E_INVALID;
+    return hip_status(launch_route(0, r->H, r->E, r->k, r->gating, r->scale, nullptr, nullptr, nullptr, nullptr,
+                                   nullptr, nullptr, expert_offsets, nullptr, active, nullptr, nullptr,
+                                   (hipStream_t)stream));
+  }
+  if (!x || !w_router || !topk_ids || !topk_w || !expert_offsets || !pairs || !active || !y) return MOEQ_E_INVALID;
+  if (!aligned(x, 16) || !aligned(w_router, 16) || (bias && !aligned(bias, 4)) || !aligned(y, 4))
+    return MOEQ_E_INVALID;
+  if (logits && !aligned(logits, 8)) return MOEQ_E_INVALID;
+  if (!ws || !aligned(ws, 256)) return MOEQ_E_INVALID;
+  const LayerLayout L = layer_layout(r, f);
+  if (ws_bytes < L.total) return MOEQ_E_WORKSPACE;
+  uint8_t* wsb = (uint8_t*)ws;
+  hipStream_t s = (hipStream_t)stream;
+  void* xq = wsb + L.off_xq;
+  if (r->T == 1) {
+    // one token: logits + q8_K(x) in one launch, then gate/up routes inline
+    double* lg = logits ? logits : (double*)(wsb + L.off_route);
+    if ((rc = launch_logits(1, r->H, r->E, x, w_router, bias, lg, xq, s))) return hip_status(rc);
+    InlineRoute ir{lg, r->gating, r->scale, topk_ids, expert_offsets, pairs, active, topk_w};
+    return hip_status(ffn_enqueue(f, xq, topk_ids, topk_w, expert_offsets, pairs, active, shared_scale, y, wsb, &ir,
+                                  s));
+  }
+  if ((rc = launch_route(r->T, r->H, r->E, r->k, r->gating, r->scale, x, w_router, bias, logits, topk_ids, topk_w,
+                         expert_offsets, pairs, active, xq, wsb + L.off_route, s)))
+    return hip_status(rc);
+  return hip_status(ffn_enqueue(f, xq, topk_ids, topk_w, expert_offsets, pairs, active, shared_scale, y, wsb,
+                                nullptr, s));
 }
 
 int moeq_ffn_h_view(const moeq_ffn_desc* d, void* ws, size_t ws_bytes, void** hq_routed, void** hq_shared) {

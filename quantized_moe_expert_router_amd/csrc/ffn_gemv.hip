@@ -19,6 +19,7 @@
 //          every token in slot order (then the shared expert) and rounds y.
 #include "formats.hpp"
 #include "launch.hpp"
+#include "topk.hpp"
 
 namespace moeq {
 
@@ -152,6 +153,123 @@ __global__ __launch_bounds__(256) void k_gateup(GateUpArgs a) {
             a.hbuf[prow[i] * a.hstride + row[u]] = (float)(silu64(g) * uu);
         }
       }
+    }
+  }
+}
+
+// The routing outputs of one token, written by one wave that holds the
+// winners in rank order (lane s < k: expert my_i, weight my_w): ids and
+// weights, then the lists (pairs ordered by expert; for one token the pair of
+// slot s is s) and the expert union.
+__device__ void write_routing_t1(const GateUpArgs& a, int my_i, float my_w) {
+  const int lane = lane_id(), k = a.k;
+  int pos = 0;
+  for (int j = 0; j < k; ++j) {
+    const int idj = __builtin_amdgcn_readlane(my_i, j);
+    pos += (lane < k && idj < my_i) ? 1 : 0;
+  }
+  if (lane < k) {
+    a.ids_out[lane] = my_i;
+    a.w_out[lane] = my_w;
+    a.active_out[1 + pos] = my_i;
+    a.pairs_out[pos] = lane;
+  }
+  if (lane == 0) a.active_out[0] = k;
+  for (int64_t e0 = 0; e0 <= a.E; e0 += kWave) {
+    const int64_t e = e0 + lane;
+    int c = 0;
+    for (int j = 0; j < k; ++j) c += __builtin_amdgcn_readlane(my_i, j) < e ? 1 : 0;
+    if (e <= a.E) a.offsets_out[e] = c;
+  }
+}
+
+// One token.  Slot u is the u-th ranked expert (u == k: the shared expert);
+// with NPER > 0 the workgroup routes inline from the logits (every wave runs
+// the same register top-k, so all workgroups agree), otherwise it reads
+// topk_ids.  The token's activation chunks are loaded before anything that
+// depends on the routing.
+template <int FMT, int CPL, int NPER>
+__global__ __launch_bounds__(256) void k_gateup1(GateUpArgs a) {
+  using L = Fmt<FMT>;
+  constexpr int UNR = 4;
+  const int wave = threadIdx.x >> 6, lane = lane_id();
+  const int lpr = a.lpr, rps = kWave / lpr, rig = lane / lpr, lir = lane % lpr;
+  const int64_t nb = a.H / 256, nsb = a.F * nb;
+  int xw[CPL][L::XDW], bs[CPL][L::NBS];
+  double dx[CPL];
+#pragma unroll
+  for (int c = 0; c < CPL; ++c) {
+    const int ch = lir + lpr * c;
+    if (ch < a.cpr) {
+      load_x_chunk<FMT>(a.xq, ch, xw[c], bs[c], dx[c]);
+    } else {
+#pragma unroll
+      for (int q = 0; q < L::XDW; ++q) xw[c][q] = 0;
+#pragma unroll
+      for (int q = 0; q < L::NBS; ++q) bs[c][q] = 0;
+      dx[c] = 0.0;
+    }
+  }
+  const int slot = blockIdx.y;
+  const bool shared = a.mode == kModeShared || (a.mode == kModeBoth && slot == a.k);
+  const uint8_t *Wg, *Wu;
+  int64_t prow;
+  if (shared) {
+    Wg = a.sh_gate; Wu = a.sh_up; prow = a.k;
+  } else {
+    int e;
+    if constexpr (NPER > 0) {
+      int my_i;
+      float my_w;
+      topk_wave_regs<NPER>(a.logits, a.E, a.k, a.gating, a.scale, my_i, my_w);
+      if (blockIdx.x == 0 && slot == 0 && wave == 0) write_routing_t1(a, my_i, my_w);
+      e = __builtin_amdgcn_readlane(my_i, slot);
+    } else {
+      e = a.topk_ids[slot];
+    }
+    Wg = (const uint8_t*)a.gate[e];
+    Wu = (const uint8_t*)a.up[e];
+    if (a.down[e] == nullptr) Wg = nullptr;
+    prow = slot;
+  }
+  if (Wg == nullptr || Wu == nullptr) return;   // not resident: its pair adds nothing
+  const int64_t row0 = (int64_t)blockIdx.x * (4 * a.steps * rps) + (int64_t)wave * a.steps * rps + rig;
+  for (int st = 0; st < a.steps; st += UNR) {
+    typename L::W wg[UNR][CPL], wu[UNR][CPL];
+    int64_t row[UNR];
+    bool ok[UNR][CPL];
+#pragma unroll
+    for (int u = 0; u < UNR; ++u) {
+      row[u] = row0 + (int64_t)(st + u) * rps;
+      const bool rv = (st + u) < a.steps && row[u] < a.F;
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) {
+        const int ch = lir + lpr * c;
+        ok[u][c] = rv && ch < a.cpr;
+        if (ok[u][c]) {
+          const size_t sbi = (size_t)(row[u] * nb + ch / L::CPS);
+          wg[u][c] = L::load(Wg, (size_t)nsb, sbi, ch % L::CPS);
+          wu[u][c] = L::load(Wu, (size_t)nsb, sbi, ch % L::CPS);
+        }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < UNR; ++u) {
+      double ag = 0.0, au = 0.0;
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) {
+        if (!ok[u][c]) continue;
+        const int j = (lir + lpr * c) % L::CPS;
+        int is[L::SPC];
+        L::isums(wg[u][c], xw[c], bs[c], is);
+        ag += L::term(wg[u][c], j, is, bs[c], dx[c]);
+        L::isums(wu[u][c], xw[c], bs[c], is);
+        au += L::term(wu[u][c], j, is, bs[c], dx[c]);
+      }
+      const double g = group_sum(ag, lpr);
+      const double uu = group_sum(au, lpr);
+      if (lir == 0 && (st + u) < a.steps && row[u] < a.F)
+        a.hbuf[prow * a.hstride + row[u]] = (float)(silu64(g) * uu);
     }
   }
 }
@@ -315,7 +433,7 @@ __global__ __launch_bounds__(256) void k_down_rows1(DownArgs a) {
   const int lpr = a.lpr, rps = kWave / lpr, rig = lane / lpr, lir = lane % lpr;
   const int64_t nb = a.F / 256, nsb = a.H * nb;
   const int64_t row = (int64_t)blockIdx.x * rps + rig;
-  const int n_routed = a.active[0];
+  const int n_routed = a.k;
   const int n_slots = n_routed + a.has_shared;
   for (int s = wave; s < n_slots; s += 4) {
     const bool shared = s >= n_routed;
@@ -327,9 +445,9 @@ __global__ __launch_bounds__(256) void k_down_rows1(DownArgs a) {
       wt = a.shared_scale ? (double)a.shared_scale[0] : 1.0;
       Wd = a.sh_down;
     } else {
-      const int e = a.active[1 + s];
-      prow = a.pairs[a.offsets[e]];
-      wt = (double)a.topk_w[prow];
+      const int e = a.topk_ids[s];   // one token: slot s is the s-th ranked expert
+      prow = s;
+      wt = (double)a.topk_w[s];
       Wd = (const uint8_t*)a.down[e];
       if (a.gate[e] == nullptr || a.up[e] == nullptr) Wd = nullptr;
     }
@@ -401,6 +519,36 @@ __global__ __launch_bounds__(256) void k_down_rows1(DownArgs a) {
 int launch_gateup(int fmt, int tt, int cpl, dim3 grid, const GateUpArgs& a, hipStream_t s) {
   if (grid.x == 0 || grid.y == 0) return 0;
   MOEQ_SWITCH_FMT(MOEQ_GU)
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+#define MOEQ_G1(F, NP, C) hipLaunchKernelGGL((k_gateup1<F, C, NP>), grid, dim3(256), 0, s, a)
+#define MOEQ_G1_CPL(F, NP)                    \
+  switch (cpl) {                              \
+    case 1: MOEQ_G1(F, NP, 1); break;         \
+    case 2: MOEQ_G1(F, NP, 2); break;         \
+    case 4: MOEQ_G1(F, NP, 4); break;         \
+    default: return -2;                       \
+  }
+#define MOEQ_G1_NP(F)                                            \
+  switch (nper) {                                                \
+    case 0: { MOEQ_G1_CPL(F, 0) } break;                         \
+    case 4: { MOEQ_G1_CPL(F, 4) } break;                         \
+    case 8: { MOEQ_G1_CPL(F, 8) } break;                         \
+    case 16: { MOEQ_G1_CPL(F, 16) } break;                       \
+    case 64: { MOEQ_G1_CPL(F, 64) } break;                       \
+    default: return -2;                                          \
+  }
+
+int launch_gateup1(int fmt, int nper, int cpl, dim3 grid, const GateUpArgs& a, hipStream_t s) {
+  if (grid.x == 0 || grid.y == 0) return 0;
+  switch (fmt) {
+    case FQ4K: { MOEQ_G1_NP(FQ4K) } break;
+    case FQ6K: { MOEQ_G1_NP(FQ6K) } break;
+    case FQ2K: { MOEQ_G1_NP(FQ2K) } break;
+    case FQ80: { MOEQ_G1_NP(FQ80) } break;
+    default: return -2;
+  }
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 

@@ -27,9 +27,21 @@ struct GateUpArgs {
   float* hbuf;                  // fp32 [T*k + T, hstride]
   int64_t hstride;
   int lpr, cpr, steps;
+  // one token (k_gateup1)
+  const int32_t* topk_ids;      // rank-ordered experts (when not routing inline)
+  const double* logits;         // [E] logits to route inline from, or null
+  int64_t E;
+  int gating;
+  float scale;
+  int32_t* ids_out;             // routing outputs written when routing inline
+  float* w_out;
+  int32_t* offsets_out;
+  int32_t* pairs_out;
+  int32_t* active_out;
 };
 
 struct DownArgs {
+  const int32_t* topk_ids;
   const void* const* gate;
   const void* const* up;
   const void* const* down;
@@ -61,10 +73,13 @@ int launch_pack(int fmt, const void* aos, int64_t n_mats, int64_t rows, int64_t 
 int launch_subdots(int fmt, const void* w, int64_t rows, int64_t cols, const void* xq, int64_t n_x,
                    int32_t* out, hipStream_t s);
 size_t route_ws_bytes(int64_t T, int64_t E);
+int launch_logits(int64_t T, int64_t H, int64_t E, const float* x, const float* W, const float* bias,
+                  double* logits, void* xq, hipStream_t s);
 int launch_route(int64_t T, int64_t H, int64_t E, int k, int gating, float scale, const float* x,
                  const float* W, const float* bias, double* logits, int32_t* ids, float* w,
                  int32_t* offsets, int32_t* pairs, int32_t* active, void* xq, void* ws, hipStream_t s);
 int launch_gateup(int fmt, int tt, int cpl, dim3 grid, const GateUpArgs& a, hipStream_t s);
+int launch_gateup1(int fmt, int nper, int cpl, dim3 grid, const GateUpArgs& a, hipStream_t s);
 int launch_down(int fmt, int tt, int cpl, dim3 grid, const DownArgs& a, hipStream_t s);
 int launch_down_rows1(int fmt, int cpl, dim3 grid, const DownArgs& a, hipStream_t s);
 int launch_combine(const double* yp, int64_t T, int64_t H, int k, int has_shared, float* y, int accumulate,

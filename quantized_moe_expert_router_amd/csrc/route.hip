@@ -6,6 +6,7 @@
 
 #include "common.hpp"
 #include "launch.hpp"
+#include "topk.hpp"
 
 namespace moeq {
 
@@ -78,58 +79,19 @@ __global__ __launch_bounds__(256) void k_logits(const float* __restrict__ x, con
   }
 }
 
-// Top-k of one logits row by one wave, logits held in registers (NPER per
-// lane, element lane + 64*i).  Each round takes the first remaining element
-// under (logit desc, index asc) with a DPP arg-max.  Lane s ends holding the
-// s-th winner; gate weights are computed in fp64 in parallel over the k lanes
-// and normalised by a fixed-order wave sum.
 template <int NPER>
 __device__ void topk_row_wave(const double* __restrict__ row, int64_t E, int k, int gating, float scale,
                               int32_t* __restrict__ ids_out, float* __restrict__ w_out, int32_t* ids_lds) {
+  int my_i;
+  float my_w;
+  topk_wave_regs<NPER>(row, E, k, gating, scale, my_i, my_w);
   const int lane = lane_id();
-  double v[NPER];
-#pragma unroll
-  for (int i = 0; i < NPER; ++i) {
-    const int64_t e = lane + (int64_t)kWave * i;
-    v[i] = e < E ? row[e] : -INFINITY;
-  }
-  uint64_t taken = 0;
-  double my_v = 0.0;
-  int my_i = 0;
-  for (int s = 0; s < k; ++s) {
-    double best = -INFINITY;
-    int bi = INT_MAX;
-#pragma unroll
-    for (int i = 0; i < NPER; ++i) {
-      const int e = lane + kWave * i;
-      if (e < E && !((taken >> i) & 1ull)) better(best, bi, v[i], e);
-    }
-    wave_argmax(best, bi);
-    if ((bi & (kWave - 1)) == lane) taken |= 1ull << (bi / kWave);
-    if (lane == s) { my_v = best; my_i = bi; }
-  }
-  const double mx = readlane_d(my_v, 0);
-  double num = 0.0;
-  if (lane < k) num = gating == 2 ? 1.0 / (1.0 + exp(-my_v)) : exp(my_v - mx);
-  double z;
-  if (gating == 1) {
-    double part = 0.0;
-#pragma unroll
-    for (int i = 0; i < NPER; ++i) {
-      const int64_t e = lane + (int64_t)kWave * i;
-      if (e < E) part += exp(v[i] - mx);
-    }
-    z = wave_sum(part);
-  } else {
-    z = wave_sum(num);
-  }
   if (lane < k) {
     ids_out[lane] = my_i;
-    w_out[lane] = (float)(num / z * (double)scale);
+    w_out[lane] = my_w;
     if (ids_lds) ids_lds[lane] = my_i;
   }
 }
-
 
 // Exclusive scan over a block of blockDim.x threads (a multiple of 64).
 __device__ int block_exclusive_scan(int v, int* tmp /* >= 16 ints */, int* total) {
@@ -287,6 +249,15 @@ __global__ void k_empty_lists(int64_t E, int32_t* offsets, int32_t* active) {
   if (threadIdx.x == 0) active[0] = 0;
 }
 
+int launch_logits(int64_t T, int64_t H, int64_t E, const float* x, const float* W, const float* bias,
+                  double* logits, void* xq, hipStream_t s) {
+  const int64_t nq = xq ? (T * (H / 256) + 3) / 4 : 0;
+  const int64_t tiles = (T + kLogitTok - 1) / kLogitTok;
+  dim3 g1((unsigned)(E + nq), (unsigned)(tiles < 64 ? tiles : 64));
+  hipLaunchKernelGGL(k_logits, g1, dim3(256), 0, s, x, W, bias, T, H, E, logits, (uint8_t*)xq);
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
 size_t route_ws_bytes(int64_t T, int64_t E) {
   size_t b = align256((size_t)T * E * sizeof(double));
   if (T > kSmallT) b += align256((size_t)((T + kChunkT - 1) / kChunkT) * E * sizeof(int32_t));
@@ -302,10 +273,7 @@ int launch_route(int64_t T, int64_t H, int64_t E, int k, int gating, float scale
   }
   uint8_t* wsb = (uint8_t*)ws;
   double* lg = logits ? logits : reinterpret_cast<double*>(wsb);
-  const int64_t nq = xq ? (T * (H / 256) + 3) / 4 : 0;
-  const int64_t tiles = (T + kLogitTok - 1) / kLogitTok;
-  dim3 g1((unsigned)(E + nq), (unsigned)(tiles < 64 ? tiles : 64));
-  hipLaunchKernelGGL(k_logits, g1, dim3(256), 0, s, x, W, bias, T, H, E, lg, (uint8_t*)xq);
+  launch_logits(T, H, E, x, W, bias, lg, xq, s);
   if (T <= kSmallT) {
     size_t lds = (size_t)(T * k + E + 64) * sizeof(int);
 #define MOEQ_SEL(N) hipLaunchKernelGGL(k_select_small<N>, dim3(1), dim3(1024), lds, s, lg, T, E, k, gating, \

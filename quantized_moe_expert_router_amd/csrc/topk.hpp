@@ -1,0 +1,58 @@
+// Top-k routing of one logits row by one wave (shared by the router kernels
+// and the one-token FFN kernel, which routes inline).
+#pragma once
+#include <limits.h>
+
+#include "common.hpp"
+
+namespace moeq {
+
+// Top-k of one logits row by one wave, logits held in registers (NPER per
+// lane, element lane + 64*i).  Each round takes the first remaining element
+// under (logit desc, index asc) with a DPP arg-max.  Lane s < k ends holding
+// the s-th winner (id) and its gate weight: computed in fp64 in parallel over
+// the k lanes and normalised by a fixed-order wave sum.
+template <int NPER>
+__device__ void topk_wave_regs(const double* __restrict__ row, int64_t E, int k, int gating, float scale,
+                               int& my_i, float& my_w) {
+  const int lane = lane_id();
+  double v[NPER];
+#pragma unroll
+  for (int i = 0; i < NPER; ++i) {
+    const int64_t e = lane + (int64_t)kWave * i;
+    v[i] = e < E ? row[e] : -INFINITY;
+  }
+  uint64_t taken = 0;
+  double my_v = 0.0;
+  my_i = 0;
+  for (int s = 0; s < k; ++s) {
+    double best = -INFINITY;
+    int bi = INT_MAX;
+#pragma unroll
+    for (int i = 0; i < NPER; ++i) {
+      const int e = lane + kWave * i;
+      if (e < E && !((taken >> i) & 1ull)) better(best, bi, v[i], e);
+    }
+    wave_argmax(best, bi);
+    if ((bi & (kWave - 1)) == lane) taken |= 1ull << (bi / kWave);
+    if (lane == s) { my_v = best; my_i = bi; }
+  }
+  const double mx = readlane_d(my_v, 0);
+  double num = 0.0;
+  if (lane < k) num = gating == 2 ? 1.0 / (1.0 + exp(-my_v)) : exp(my_v - mx);
+  double z;
+  if (gating == 1) {
+    double part = 0.0;
+#pragma unroll
+    for (int i = 0; i < NPER; ++i) {
+      const int64_t e = lane + (int64_t)kWave * i;
+      if (e < E) part += exp(v[i] - mx);
+    }
+    z = wave_sum(part);
+  } else {
+    z = wave_sum(num);
+  }
+  my_w = (float)(num / z * (double)scale);
+}
+
+}  // namespace moeq

@@ -25,7 +25,7 @@ SUBBLOCK = {Q4_K: 32, Q6_K: 16, Q2_K: 16, Q8_0: 32}
 
 SYMBOLS = ["moeq_status_string", "moeq_quantize_q8K", "moeq_route_workspace", "moeq_route",
            "moeq_packed_bytes", "moeq_pack_experts", "moeq_expert_ffn_workspace", "moeq_expert_ffn",
-           "moeq_ffn_h_view", "moeq_debug_subdots"]
+           "moeq_moe_layer_workspace", "moeq_moe_layer", "moeq_ffn_h_view", "moeq_debug_subdots"]
 
 
 class MoeqError(RuntimeError):
@@ -70,11 +70,15 @@ def lib() -> ctypes.CDLL:
         L.moeq_pack_experts.argtypes = [i32, vp, i64, i64, i64, vp, vp]
         L.moeq_expert_ffn_workspace.restype = sz
         L.moeq_expert_ffn_workspace.argtypes = [ctypes.POINTER(FfnDesc)]
-        L.moeq_expert_ffn.argtypes = [ctypes.POINTER(FfnDesc), vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.moeq_expert_ffn.argtypes = [ctypes.POINTER(FfnDesc), vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.moeq_moe_layer_workspace.restype = sz
+        L.moeq_moe_layer_workspace.argtypes = [ctypes.POINTER(RouteDesc), ctypes.POINTER(FfnDesc)]
+        L.moeq_moe_layer.argtypes = [ctypes.POINTER(RouteDesc), ctypes.POINTER(FfnDesc), vp, vp, vp, vp, vp, vp,
+                                     vp, vp, vp, vp, vp, vp, sz, vp]
         L.moeq_ffn_h_view.argtypes = [ctypes.POINTER(FfnDesc), vp, sz, ctypes.POINTER(vp), ctypes.POINTER(vp)]
         L.moeq_debug_subdots.argtypes = [i32, vp, i64, i64, vp, i64, vp, vp]
-        for s in ("moeq_quantize_q8K", "moeq_route", "moeq_pack_experts", "moeq_expert_ffn", "moeq_ffn_h_view",
-                  "moeq_debug_subdots"):
+        for s in ("moeq_quantize_q8K", "moeq_route", "moeq_pack_experts", "moeq_expert_ffn", "moeq_moe_layer",
+                  "moeq_ffn_h_view", "moeq_debug_subdots"):
             getattr(L, s).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -177,12 +181,29 @@ def moeq_expert_ffn_workspace(desc: FfnDesc) -> int:
     return lib().moeq_expert_ffn_workspace(ctypes.byref(desc))
 
 
-def moeq_expert_ffn(desc: FfnDesc, x_q8K: torch.Tensor, topk_w: torch.Tensor, expert_offsets: torch.Tensor,
-                    pairs: torch.Tensor, active: torch.Tensor, shared_scale: Optional[torch.Tensor],
-                    y: torch.Tensor, ws: torch.Tensor, stream=None) -> torch.Tensor:
-    rc = lib().moeq_expert_ffn(ctypes.byref(desc), _ptr(x_q8K), _ptr(topk_w), _ptr(expert_offsets), _ptr(pairs),
-                               _ptr(active), _ptr(shared_scale), _ptr(y), _ptr(ws), ws.numel(), _stream(stream))
+def moeq_expert_ffn(desc: FfnDesc, x_q8K: torch.Tensor, topk_ids: torch.Tensor, topk_w: torch.Tensor,
+                    expert_offsets: torch.Tensor, pairs: torch.Tensor, active: torch.Tensor,
+                    shared_scale: Optional[torch.Tensor], y: torch.Tensor, ws: torch.Tensor,
+                    stream=None) -> torch.Tensor:
+    rc = lib().moeq_expert_ffn(ctypes.byref(desc), _ptr(x_q8K), _ptr(topk_ids), _ptr(topk_w), _ptr(expert_offsets),
+                               _ptr(pairs), _ptr(active), _ptr(shared_scale), _ptr(y), _ptr(ws), ws.numel(),
+                               _stream(stream))
     _check("moeq_expert_ffn", rc)
+    return y
+
+
+def moeq_moe_layer_workspace(rdesc: RouteDesc, fdesc: FfnDesc) -> int:
+    return lib().moeq_moe_layer_workspace(ctypes.byref(rdesc), ctypes.byref(fdesc))
+
+
+def moeq_moe_layer(rdesc: RouteDesc, fdesc: FfnDesc, x: torch.Tensor, w_router: torch.Tensor,
+                   bias: Optional[torch.Tensor], out: "RouteOut", shared_scale: Optional[torch.Tensor],
+                   y: torch.Tensor, ws: torch.Tensor, stream=None) -> torch.Tensor:
+    """The whole layer (route, q8_K(x), expert FFN) in one library call."""
+    rc = lib().moeq_moe_layer(ctypes.byref(rdesc), ctypes.byref(fdesc), _ptr(x), _ptr(w_router), _ptr(bias),
+                              _ptr(out.logits), _ptr(out.ids), _ptr(out.w), _ptr(out.offsets), _ptr(out.pairs),
+                              _ptr(out.active), _ptr(shared_scale), _ptr(y), _ptr(ws), ws.numel(), _stream(stream))
+    _check("moeq_moe_layer", rc)
     return y
 
 
@@ -297,6 +318,7 @@ class LayerRunner:
         self.ffn_ws = torch.empty(n, dtype=torch.uint8, device=dev)
         self.y = torch.empty((T, c.H), dtype=torch.float32, device=dev)
         self.shared_scale = shared_scale
+        self.layer_ws = None
 
     def route(self, x: torch.Tensor, stream=None, with_q8K: bool = True):
         c = self.dl.cfg
@@ -310,5 +332,21 @@ class LayerRunner:
 
     def ffn(self, stream=None) -> torch.Tensor:
         r = self.route_out
-        return moeq_expert_ffn(self.desc, self.xq, r.w, r.offsets, r.pairs, r.active, self.shared_scale, self.y,
-                               self.ffn_ws, stream)
+        return moeq_expert_ffn(self.desc, self.xq, r.ids, r.w, r.offsets, r.pairs, r.active, self.shared_scale,
+                               self.y, self.ffn_ws, stream)
+
+    def layer(self, x: torch.Tensor, stream=None) -> torch.Tensor:
+        """The fused whole-layer call (moeq_moe_layer)."""
+        c = self.dl.cfg
+        if self.layer_ws is None:
+            self.rdesc = RouteDesc(self.T, c.H, c.E, c.k, c.gating, 1.0)
+            n = moeq_moe_layer_workspace(self.rdesc, self.desc)
+            if n == 0:
+                raise MoeqError("moeq_moe_layer_workspace", MOEQ_E_UNSUPPORTED)
+            self.layer_ws = torch.empty(n, dtype=torch.uint8, device=x.device)
+        return moeq_moe_layer(self.rdesc, self.desc, x, self.dl.w_router, self.dl.bias, self.route_out,
+                              self.shared_scale, self.y, self.layer_ws, stream)
+
+    def layer_h_view(self):
+        """q8_K(h) views after layer(): the FFN region sits at the start of the layer workspace."""
+        return moeq_ffn_h_view(self.desc, self.layer_ws)

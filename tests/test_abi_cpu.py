@@ -71,7 +71,7 @@ def test_ffn_rejects_bad_descriptors(kw, status):
     d = _desc(**kw)
     L = moeq.lib()
     assert L.moeq_expert_ffn_workspace(ctypes.byref(d)) == 0
-    rc = L.moeq_expert_ffn(ctypes.byref(d), 0x1000, 0x1000, 0x1000, 0x1000, 0x1000, None, 0x1000, 0x100000,
+    rc = L.moeq_expert_ffn(ctypes.byref(d), 0x1000, 0x1000, 0x1000, 0x1000, 0x1000, 0x1000, None, 0x1000, 0x100000,
                            1 << 30, None)
     assert rc == status
 
@@ -81,7 +81,7 @@ def test_ffn_rejects_small_or_misaligned_workspace_and_null_inputs():
     L = moeq.lib()
     need = L.moeq_expert_ffn_workspace(ctypes.byref(d))
     assert need > 0
-    args = [0x1000, 0x1000, 0x1000, 0x1000, 0x1000, None, 0x1000]
+    args = [0x1000, 0x1000, 0x1000, 0x1000, 0x1000, 0x1000, None, 0x1000]
     assert L.moeq_expert_ffn(ctypes.byref(d), *args, 0x100000, need - 1, None) == moeq.MOEQ_E_WORKSPACE
     assert L.moeq_expert_ffn(ctypes.byref(d), *args, 0x100010, need, None) == moeq.MOEQ_E_INVALID
     bad = list(args)
@@ -89,7 +89,26 @@ def test_ffn_rejects_small_or_misaligned_workspace_and_null_inputs():
     assert L.moeq_expert_ffn(ctypes.byref(d), *bad, 0x100000, need, None) == moeq.MOEQ_E_INVALID
     # T == 0 is a valid no-op
     d0 = _desc(T=0)
-    assert L.moeq_expert_ffn(ctypes.byref(d0), None, None, None, None, None, None, None, None, 0, None) == 0
+    assert L.moeq_expert_ffn(ctypes.byref(d0), None, None, None, None, None, None, None, None, None, 0, None) == 0
+    bad = list(args)
+    bad[1] = None                                               # topk_ids is required
+    assert L.moeq_expert_ffn(ctypes.byref(d), *bad, 0x100000, need, None) == moeq.MOEQ_E_INVALID
+
+
+def test_layer_call_validation():
+    L = moeq.lib()
+    f = _desc()
+    r = moeq.RouteDesc(1, 2048, 256, 8, 0, 1.0)
+    need = L.moeq_moe_layer_workspace(ctypes.byref(r), ctypes.byref(f))
+    assert need >= L.moeq_expert_ffn_workspace(ctypes.byref(f))
+    ptrs = [0x1000] * 11
+    ptrs[2] = None                                              # no bias
+    assert L.moeq_moe_layer(ctypes.byref(r), ctypes.byref(f), *ptrs, 0x100000, need - 1, None) == \
+        moeq.MOEQ_E_WORKSPACE
+    r2 = moeq.RouteDesc(1, 2048, 256, 6, 0, 1.0)               # k disagrees with the FFN descriptor
+    assert L.moeq_moe_layer_workspace(ctypes.byref(r2), ctypes.byref(f)) == 0
+    assert L.moeq_moe_layer(ctypes.byref(r2), ctypes.byref(f), *ptrs, 0x100000, 1 << 30, None) == \
+        moeq.MOEQ_E_INVALID
 
 
 def test_route_and_quantize_validation():

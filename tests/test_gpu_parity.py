@@ -46,7 +46,10 @@ def check_w(w_gpu, w_orc):
 
 
 class GpuRun:
-    def __init__(self, layer, path=moeq.PATH_AUTO, present=None, shared_scale=None, x=None):
+    """One layer on the GPU: separate route + FFN calls, or (fused=True) the
+    single whole-layer call."""
+
+    def __init__(self, layer, path=moeq.PATH_AUTO, present=None, shared_scale=None, x=None, fused=False):
         cfg = layer.cfg
         self.dl = moeq.DeviceLayer(layer, present=present)
         xs = layer.x if x is None else x
@@ -54,7 +57,10 @@ class GpuRun:
         T = xs.shape[0]
         ss = None if shared_scale is None else dev(shared_scale)
         self.runner = moeq.LayerRunner(self.dl, T, path=path, shared_scale=ss)
-        self.y = self.runner.forward(self.x)
+        if fused:
+            self.y = self.runner.layer(self.x)
+        else:
+            self.y = self.runner.forward(self.x)
         torch.cuda.synchronize()
         r = self.runner.route_out
         self.ids = r.ids.cpu().numpy()
@@ -64,8 +70,8 @@ class GpuRun:
         self.pairs = r.pairs.cpu().numpy()[:T * cfg.k]
         act = r.active.cpu().numpy()
         self.active = act[:1 + act[0]]
-        self.xq = self.runner.xq.cpu().numpy()
-        hr, hs = moeq.moeq_ffn_h_view(self.runner.desc, self.runner.ffn_ws)
+        self.xq = None if fused else self.runner.xq.cpu().numpy()
+        hr, hs = self.runner.layer_h_view() if fused else moeq.moeq_ffn_h_view(self.runner.desc, self.runner.ffn_ws)
         self.hq_r = None if hr is None else hr.cpu().numpy()
         self.hq_s = None if hs is None else hs.cpu().numpy()
         self.yv = self.y.cpu().numpy()
@@ -159,19 +165,21 @@ def check_route(run, layer, sel):
     return ids, w
 
 
+@pytest.mark.parametrize("fused", [False, True], ids=["calls", "layer"])
 @pytest.mark.parametrize("name", syn.CONFIG_ORDER)
-def test_layer_parity(name):
+def test_layer_parity(name, fused):
     layer = layer_of(name)
     cfg = layer.cfg
-    say("layer", name, cfg)
-    run = GpuRun(layer, path=moeq.PATH_GEMV)
+    say("layer", name, "fused" if fused else "calls", cfg)
+    run = GpuRun(layer, path=moeq.PATH_GEMV, fused=fused)
     sel = sample_tokens(cfg.T, 24)
     ids, w = check_route(run, layer, sel)
     full_ids = run.ids.copy()
     full_ids[sel] = ids
     full_w = run.w.copy()
     full_w[sel] = w
-    assert np.array_equal(run.xq[sel], oracle.quantize_q8K(layer.x[sel]))
+    if run.xq is not None:
+        assert np.array_equal(run.xq[sel], oracle.quantize_q8K(layer.x[sel]))
     r = oracle.expert_ffn(layer, full_ids, full_w, sel)
     check_y(run.yv[sel], r.y, name)
     nbF = cfg.F // 256 * 292
@@ -226,7 +234,7 @@ def test_accumulate_and_shared_scale():
     y0 = rng.standard_normal((cfg.T, cfg.H)).astype(np.float32)
     yt = dev(y0)
     ro = run.runner.route_out
-    moeq.moeq_expert_ffn(desc, run.runner.xq, ro.w, ro.offsets, ro.pairs, ro.active, dev(ss), yt,
+    moeq.moeq_expert_ffn(desc, run.runner.xq, ro.ids, ro.w, ro.offsets, ro.pairs, ro.active, dev(ss), yt,
                          run.runner.ffn_ws)
     torch.cuda.synchronize()
     check_y(yt.cpu().numpy(), y0.astype(np.float64) + run.yv.astype(np.float64), "accumulate")
@@ -239,10 +247,12 @@ def _custom_cfg(**kw):
     return syn.LayerConfig(**base)
 
 
+@pytest.mark.parametrize("fused", [False, True], ids=["calls", "layer"])
 @pytest.mark.parametrize("variant", ["one_expert_all_tokens", "k_equals_E", "k1", "ties", "softmax_all",
-                                     "sigmoid", "q2k_q6k_q80_mix", "t1_mixed_shared", "t1_k32"])
-def test_edge_layers(variant):
-    say("edge", variant)
+                                     "sigmoid", "q2k_q6k_q80_mix", "t1_mixed_shared", "t1_k32", "t1_ties",
+                                     "t1_softmax_all", "t1_sigmoid_e600"])
+def test_edge_layers(variant, fused):
+    say("edge", variant, fused)
     kw = {}
     if variant == "k_equals_E":
         kw = dict(E=4, k=4)
@@ -262,17 +272,33 @@ def test_edge_layers(variant):
     elif variant == "t1_k32":
         kw = dict(T=1, E=40, k=32, fmt_down=syn.Q6_K, shared=True, F_shared=256, sh_fmt_gate=syn.Q4_K,
                   sh_fmt_up=syn.Q4_K, sh_fmt_down=syn.Q6_K)
+    elif variant == "t1_softmax_all":
+        kw = dict(T=1, gating=syn.SOFTMAX_ALL, E=40, k=5)
+    elif variant == "t1_sigmoid_e600":
+        kw = dict(T=1, gating=syn.SIGMOID_TOPK, E=600, k=6)
     cfg = _custom_cfg(**kw)
     layer = syn.gen_layer(cfg)
+    if variant == "t1_ties":
+        cfg = _custom_cfg(T=1, E=70, k=8)
+        layer = syn.gen_layer(cfg)
+        x0 = layer.x[0]
+        layer.w_router[69] = layer.w_router[3]                 # exact ties, straddling lanes
+        layer.w_router[64] = layer.w_router[0]
+        layer.w_router[3] = x0 * 0.01
+        layer.w_router[69] = x0 * 0.01
+        layer.w_router[0] = x0 * 0.005
+        layer.w_router[64] = x0 * 0.005
     if variant == "one_expert_all_tokens":
         layer.w_router[3] = layer.x.mean(axis=0) * 10            # expert 3 wins for every token
     if variant == "ties":
         cfg = _custom_cfg(E=3, k=2, T=4)
         layer = syn.gen_layer(cfg)
         layer.w_router[2] = layer.w_router[0]                  # exact ties between experts 0 and 2
-    run = GpuRun(layer, path=moeq.PATH_GEMV)
+    run = GpuRun(layer, path=moeq.PATH_GEMV, fused=fused)
     sel = list(range(cfg.T))
     ids, w = check_route(run, layer, sel)
+    if variant == "t1_ties":
+        assert list(ids[0][:4]) == [3, 69, 0, 64]
     if variant == "one_expert_all_tokens":
         assert np.all(ids[:, 0] == 3)
     if variant == "ties":
