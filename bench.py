@@ -9,9 +9,9 @@ gate/up dequant-dot, SwiGLU, q8_K(h), down dequant-dot, weighted combine with
 the shared expert) over one token.  Steps cycle through `--layers` distinct
 synthetic layers resident in HBM, so, as in a real decoder stack, a step's
 weights were last touched many steps earlier and stream from HBM rather than
-from the 256 MB Infinity Cache.  Each layer is captured once as a HIP graph
-(the per-layer graph of the Strata summary's execution paragraph) and
-replayed.
+from the 256 MB Infinity Cache.  The layers are captured as HIP graphs (per-layer
+graphs as in the Strata summary's execution paragraph, and one graph for the
+whole cycle, the way a decode step runs the stack) and replayed.
 
 Output: one JSON line (metric, value = MoE-layer tokens/s, roofline of the
 expert FFN, cpu_baseline = the CPU oracle on the host cores).
@@ -150,7 +150,8 @@ def main():
         moeq.moeq_expert_ffn(lay["desc"], xq, route_out.ids, route_out.w, route_out.offsets, route_out.pairs,
                              route_out.active, None, y, ffn_ws, stream)
 
-    # Eager warm-up of every layer, then one HIP graph per layer.
+    # Eager warm-up of every layer, then HIP graphs: one per layer and one for
+    # the whole cycle of L layers (a decode step through the stack).
     for l in range(L):
         layer_step(l)
     torch.cuda.synchronize()
@@ -162,16 +163,24 @@ def main():
             with torch.cuda.graph(g, stream=stream):
                 layer_step(l, stream)
             graphs.append(g)
+        cycle = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(cycle, stream=stream):
+            for l in range(L):
+                layer_step(l, stream)
     torch.cuda.synchronize()
     setup_s = time.time() - t_setup
 
-    # ---- timed region: whole layers (value)
-    for i in range(args.warmup):
-        graphs[i % L].replay()
+    def run_steps(n):
+        for _ in range(n // L):
+            cycle.replay()
+        for l in range(n % L):
+            graphs[l].replay()
+
+    # ---- timed region: exactly `steps` whole layers (value)
+    run_steps(args.warmup)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(args.steps):
-        graphs[i % L].replay()
+    run_steps(args.steps)
     torch.cuda.synchronize()
     dt = time.perf_counter() - t0
     ms_per_step = dt * 1e3 / args.steps

@@ -46,7 +46,7 @@ bool lane_geo(int fmt, int64_t cols, LaneGeo* g) {
 
 struct FfnLayout {
   int64_t Fmax, nrows;
-  size_t off_h, off_yp, off_hq, off_hqs, total;
+  size_t off_h, off_yp, off_hq, off_hqs, off_slots, total;
 };
 FfnLayout ffn_layout(const moeq_ffn_desc* d) {
   FfnLayout L{};
@@ -58,6 +58,7 @@ FfnLayout ffn_layout(const moeq_ffn_desc* d) {
   L.off_yp = o;  o += align256((size_t)L.nrows * d->H * sizeof(double));
   L.off_hq = o;  o += align256((size_t)d->T * d->k * (d->F / 256) * kQ8KBytes);
   L.off_hqs = o; o += align256(sh ? (size_t)d->T * (d->F_shared / 256) * kQ8KBytes : 0);
+  L.off_slots = o; o += align256((size_t)(d->k + 1) * sizeof(SlotRec));
   L.total = o;
   return L;
 }
@@ -193,7 +194,10 @@ int ffn_enqueue(const moeq_ffn_desc* d, const void* x_q8K, const int32_t* topk_i
     a.max_union = max_union;
     a.hbuf = (float*)(wsb + L.off_h); a.hstride = L.Fmax;
     a.lpr = g.lpr; a.cpr = g.cpr; a.steps = std::max(1, 4 / g.rps);
-    a.topk_ids = topk_ids; a.E = d->E;
+    a.topk_ids = topk_ids; a.topk_w = topk_w; a.E = d->E;
+    a.slots = (SlotRec*)(wsb + L.off_slots);
+    a.shared_scale = shared_scale;
+    a.sh_down_rec = d->sh_down;
     if (ir != nullptr) {
       a.logits = ir->logits; a.gating = ir->gating; a.scale = ir->scale;
       a.ids_out = ir->ids; a.w_out = ir->w; a.offsets_out = ir->offsets; a.pairs_out = ir->pairs;
@@ -216,6 +220,7 @@ int ffn_enqueue(const moeq_ffn_desc* d, const void* x_q8K, const int32_t* topk_i
   auto down_args = [&](int mode, int fmt, int64_t F, LaneGeo* g) {
     lane_geo(fmt, F, g);
     DownArgs a{};
+    a.slots = (const SlotRec*)(wsb + L.off_slots);
     a.topk_ids = topk_ids;
     a.gate = d->gate; a.up = d->up; a.down = d->down; a.sh_down = (const uint8_t*)d->sh_down;
     a.mode = mode; a.T = d->T; a.H = d->H; a.F = F; a.k = d->k;

@@ -53,6 +53,16 @@ template <int CTRL, int ROW_MASK = 0xF>
 __device__ __forceinline__ int dpp_i(int old, int v) {
   return __builtin_amdgcn_update_dpp(old, v, CTRL, ROW_MASK, 0xF, false);
 }
+// Full-row patterns write every lane: no "old" operand needed.
+template <int CTRL>
+__device__ __forceinline__ int dpp_all_i(int v) { return __builtin_amdgcn_mov_dpp(v, CTRL, 0xF, 0xF, false); }
+template <int CTRL>
+__device__ __forceinline__ double dpp_all_d(double v) {
+  int2 x = *reinterpret_cast<int2*>(&v), r;
+  r.x = __builtin_amdgcn_mov_dpp(x.x, CTRL, 0xF, 0xF, false);
+  r.y = __builtin_amdgcn_mov_dpp(x.y, CTRL, 0xF, 0xF, false);
+  return *reinterpret_cast<double*>(&r);
+}
 template <int CTRL, int ROW_MASK = 0xF>
 __device__ __forceinline__ double dpp_d(double old, double v) {
   int2 o = *reinterpret_cast<int2*>(&old), x = *reinterpret_cast<int2*>(&v), r;
@@ -67,19 +77,22 @@ __device__ __forceinline__ double readlane_d(double v, int lane) {
   return *reinterpret_cast<double*>(&r);
 }
 
-// (value, index) that comes first under (value desc, index asc).
+// (value, index) that comes first under (value desc, index asc); branch-free
+// (selects, no exec-mask branches).
 __device__ __forceinline__ void better(double& v, int& i, double ov, int oi) {
-  if (ov > v || (ov == v && oi < i)) { v = ov; i = oi; }
+  const bool take = (ov > v) | ((ov == v) & (oi < i));
+  v = take ? ov : v;
+  i = take ? oi : i;
 }
 
 // Wave-wide arg-max under (value desc, index asc); every lane gets the winner.
 // Each step combines a lane with a partner from another lane set; lanes a
 // DPP move does not write keep their own value (neutral for the max).
 __device__ __forceinline__ void wave_argmax(double& v, int& i) {
-  better(v, i, dpp_d<kDppXor1>(v, v), dpp_i<kDppXor1>(i, i));
-  better(v, i, dpp_d<kDppXor2>(v, v), dpp_i<kDppXor2>(i, i));
-  better(v, i, dpp_d<kDppRowRor4>(v, v), dpp_i<kDppRowRor4>(i, i));
-  better(v, i, dpp_d<kDppRowRor8>(v, v), dpp_i<kDppRowRor8>(i, i));
+  better(v, i, dpp_all_d<kDppXor1>(v), dpp_all_i<kDppXor1>(i));
+  better(v, i, dpp_all_d<kDppXor2>(v), dpp_all_i<kDppXor2>(i));
+  better(v, i, dpp_all_d<kDppRowRor4>(v), dpp_all_i<kDppRowRor4>(i));
+  better(v, i, dpp_all_d<kDppRowRor8>(v), dpp_all_i<kDppRowRor8>(i));
   better(v, i, dpp_d<kDppRowBcast15, 0xA>(v, v), dpp_i<kDppRowBcast15, 0xA>(i, i));
   better(v, i, dpp_d<kDppRowBcast31, 0xC>(v, v), dpp_i<kDppRowBcast31, 0xC>(i, i));
   v = readlane_d(v, 63);
@@ -89,10 +102,10 @@ __device__ __forceinline__ void wave_argmax(double& v, int& i) {
 // Wave-wide fp64 sum; every lane gets the total.  The order of additions is
 // fixed by the lane pattern, so the result is deterministic.
 __device__ __forceinline__ double wave_sum(double v) {
-  v += dpp_d<kDppXor1>(0.0, v);
-  v += dpp_d<kDppXor2>(0.0, v);
-  v += dpp_d<kDppRowRor4>(0.0, v);
-  v += dpp_d<kDppRowRor8>(0.0, v);
+  v += dpp_all_d<kDppXor1>(v);
+  v += dpp_all_d<kDppXor2>(v);
+  v += dpp_all_d<kDppRowRor4>(v);
+  v += dpp_all_d<kDppRowRor8>(v);
   v += dpp_d<kDppRowBcast15, 0xA>(0.0, v);
   v += dpp_d<kDppRowBcast31, 0xC>(0.0, v);
   return readlane_d(v, 63);

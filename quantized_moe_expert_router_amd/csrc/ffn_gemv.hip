@@ -214,8 +214,12 @@ __global__ __launch_bounds__(256) void k_gateup1(GateUpArgs a) {
   const bool shared = a.mode == kModeShared || (a.mode == kModeBoth && slot == a.k);
   const uint8_t *Wg, *Wu;
   int64_t prow;
+  const void* Wd;
+  double wt;
   if (shared) {
     Wg = a.sh_gate; Wu = a.sh_up; prow = a.k;
+    Wd = a.sh_down_rec;
+    wt = a.shared_scale ? (double)a.shared_scale[0] : 1.0;
   } else {
     int e;
     if constexpr (NPER > 0) {
@@ -224,13 +228,20 @@ __global__ __launch_bounds__(256) void k_gateup1(GateUpArgs a) {
       topk_wave_regs<NPER>(a.logits, a.E, a.k, a.gating, a.scale, my_i, my_w);
       if (blockIdx.x == 0 && slot == 0 && wave == 0) write_routing_t1(a, my_i, my_w);
       e = __builtin_amdgcn_readlane(my_i, slot);
+      wt = (double)__builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, my_w), slot));
     } else {
       e = a.topk_ids[slot];
+      wt = (double)a.topk_w[slot];
     }
     Wg = (const uint8_t*)a.gate[e];
     Wu = (const uint8_t*)a.up[e];
-    if (a.down[e] == nullptr) Wg = nullptr;
+    Wd = a.down[e];
+    if (Wd == nullptr || Wu == nullptr) Wg = nullptr;
     prow = slot;
+  }
+  if (a.slots != nullptr && blockIdx.x == 0 && threadIdx.x == 0) {
+    a.slots[shared ? a.k : slot].wd = (Wg == nullptr || Wu == nullptr) ? nullptr : Wd;
+    a.slots[shared ? a.k : slot].wt = wt;
   }
   if (Wg == nullptr || Wu == nullptr) return;   // not resident: its pair adds nothing
   const int64_t row0 = (int64_t)blockIdx.x * (4 * a.steps * rps) + (int64_t)wave * a.steps * rps + rig;
@@ -436,21 +447,12 @@ __global__ __launch_bounds__(256) void k_down_rows1(DownArgs a) {
   const int n_routed = a.k;
   const int n_slots = n_routed + a.has_shared;
   for (int s = wave; s < n_slots; s += 4) {
+    // one token: slot s is the s-th ranked expert (slot k: the shared one);
+    // the gate/up kernel left its down matrix and weight in the slot table
     const bool shared = s >= n_routed;
-    int64_t prow;
-    double wt;
-    const uint8_t* Wd;
-    if (shared) {
-      prow = a.k;
-      wt = a.shared_scale ? (double)a.shared_scale[0] : 1.0;
-      Wd = a.sh_down;
-    } else {
-      const int e = a.topk_ids[s];   // one token: slot s is the s-th ranked expert
-      prow = s;
-      wt = (double)a.topk_w[s];
-      Wd = (const uint8_t*)a.down[e];
-      if (a.gate[e] == nullptr || a.up[e] == nullptr) Wd = nullptr;
-    }
+    const int64_t prow = shared ? a.k : s;
+    const double wt = a.slots[s].wt;
+    const uint8_t* Wd = (const uint8_t*)a.slots[s].wd;
     typename L::W wd[CPL];
     bool ok[CPL];
 #pragma unroll

@@ -10,6 +10,13 @@ namespace moeq {
 // (the shared expert as one more slot when it has the routed shape and format).
 constexpr int kModeRouted = 0, kModeShared = 1, kModeBoth = 2;
 
+// One token: what the down kernel needs per slot (slot k = shared expert),
+// written by the gate/up kernel.
+struct SlotRec {
+  const void* wd;   // packed down matrix, null when the expert is not resident
+  double wt;        // gate weight (shared: shared_scale or 1)
+};
+
 struct GateUpArgs {
   const void* const* gate;
   const void* const* up;
@@ -38,9 +45,14 @@ struct GateUpArgs {
   int32_t* offsets_out;
   int32_t* pairs_out;
   int32_t* active_out;
+  SlotRec* slots;               // per-slot records for the one-token down kernel
+  const float* shared_scale;
+  const float* topk_w;
+  const void* sh_down_rec;      // shared down matrix, recorded in the slot table
 };
 
 struct DownArgs {
+  const SlotRec* slots;
   const int32_t* topk_ids;
   const void* const* gate;
   const void* const* up;
