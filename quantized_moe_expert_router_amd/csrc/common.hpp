@@ -23,16 +23,6 @@ __device__ __forceinline__ float half_bits_to_float(uint32_t bits16) {
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
 
-// Butterfly sum over groups of `width` consecutive lanes (width a power of two <= 64).
-__device__ __forceinline__ double group_sum(double v, int width) {
-  for (int o = width >> 1; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
-  return v;
-}
-__device__ __forceinline__ float group_max(float v, int width) {
-  for (int o = width >> 1; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
-  return v;
-}
-
 __device__ __forceinline__ uint32_t ld_u32(const uint8_t* p) {
   return *reinterpret_cast<const uint32_t*>(p);
 }
@@ -46,6 +36,8 @@ constexpr int kDppXor1 = 0xB1;       // quad_perm [1,0,3,2]
 constexpr int kDppXor2 = 0x4E;       // quad_perm [2,3,0,1]
 constexpr int kDppRowRor4 = 0x124;
 constexpr int kDppRowRor8 = 0x128;
+constexpr int kDppRowMirror = 0x140;     // lane i <- lane 15-i within a 16-lane row
+constexpr int kDppHalfMirror = 0x141;    // lane i <- lane 7-i within each 8-lane half row
 constexpr int kDppRowBcast15 = 0x142;
 constexpr int kDppRowBcast31 = 0x143;
 
@@ -99,6 +91,50 @@ __device__ __forceinline__ void wave_argmax(double& v, int& i) {
   i = __builtin_amdgcn_readlane(i, 63);
 }
 
+template <int CTRL>
+__device__ __forceinline__ float dpp_all_f(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+
+// fp64 sum over aligned groups of `width` lanes (a power of two <= 64, uniform
+// across the wave).  The total is valid in the group's last lane (in every
+// lane of the group for width <= 16); the addition order is fixed.
+__device__ __forceinline__ double group_sum_dpp(double v, int width) {
+  if (width >= 2) v += dpp_all_d<kDppXor1>(v);
+  if (width >= 4) v += dpp_all_d<kDppXor2>(v);
+  if (width >= 8) v += dpp_all_d<kDppHalfMirror>(v);
+  if (width >= 16) v += dpp_all_d<kDppRowMirror>(v);
+  if (width >= 32) v += dpp_d<kDppRowBcast15, 0xA>(0.0, v);
+  if (width >= 64) v += dpp_d<kDppRowBcast31, 0xC>(0.0, v);
+  return v;
+}
+
+// Max over aligned groups of GW lanes (GW = 4 or 8); every lane of the group
+// gets the result.
+template <int GW>
+__device__ __forceinline__ float group_max_dpp(float v) {
+  v = fmaxf(v, dpp_all_f<kDppXor1>(v));
+  v = fmaxf(v, dpp_all_f<kDppXor2>(v));
+  if constexpr (GW >= 8) v = fmaxf(v, dpp_all_f<kDppHalfMirror>(v));
+  static_assert(GW == 4 || GW == 8, "group width");
+  return v;
+}
+
+// Max over the whole wave, broadcast to every lane.
+__device__ __forceinline__ float wave_max_f(float v) {
+  v = fmaxf(v, dpp_all_f<kDppXor1>(v));
+  v = fmaxf(v, dpp_all_f<kDppXor2>(v));
+  v = fmaxf(v, dpp_all_f<kDppHalfMirror>(v));
+  v = fmaxf(v, dpp_all_f<kDppRowMirror>(v));
+  v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, v),
+                                                                    __builtin_bit_cast(int, v),
+                                                                    kDppRowBcast15, 0xA, 0xF, false)));
+  v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, v),
+                                                                    __builtin_bit_cast(int, v),
+                                                                    kDppRowBcast31, 0xC, 0xF, false)));
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
+}
+
 // Wave-wide fp64 sum; every lane gets the total.  The order of additions is
 // fixed by the lane pattern, so the result is deterministic.
 __device__ __forceinline__ double wave_sum(double v) {
@@ -133,7 +169,7 @@ __device__ __forceinline__ void quantize_block_wave(const float* __restrict__ x,
   const float* xb = x + row * cols + b * 256 + 4 * lane;
   const float4 v = *reinterpret_cast<const float4*>(xb);
   float amax = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
-  amax = group_max(amax, kWave);
+  amax = wave_max_f(amax);
   uint8_t* o = out + g * kQ8KBytes;
   const float id = amax == 0.0f ? 0.0f : __fdiv_rn(127.0f, amax);
   const bool zero = amax == 0.0f || __builtin_isinf(id);
@@ -142,8 +178,8 @@ __device__ __forceinline__ void quantize_block_wave(const float* __restrict__ x,
   *reinterpret_cast<uint32_t*>(o + 4 + 4 * lane) =
       (uint32_t)(q0 & 255) | ((uint32_t)(q1 & 255) << 8) | ((uint32_t)(q2 & 255) << 16) | ((uint32_t)(q3 & 255) << 24);
   int s = q0 + q1 + q2 + q3;
-  s += __shfl_xor(s, 1, kWave);
-  s += __shfl_xor(s, 2, kWave);
+  s += dpp_all_i<kDppXor1>(s);
+  s += dpp_all_i<kDppXor2>(s);
   if ((lane & 3) == 0) *reinterpret_cast<int16_t*>(o + 260 + 2 * (lane >> 2)) = (int16_t)s;
   if (lane == 0) *reinterpret_cast<float*>(o) = zero ? 0.0f : __fdiv_rn(amax, 127.0f);
 }

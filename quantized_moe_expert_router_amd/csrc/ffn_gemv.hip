@@ -147,9 +147,9 @@ __global__ __launch_bounds__(256) void k_gateup(GateUpArgs a) {
         }
 #pragma unroll
         for (int i = 0; i < TT; ++i) {
-          const double g = group_sum(ag[i], lpr);
-          const double uu = group_sum(au[i], lpr);
-          if (lir == 0 && tok[i] >= 0 && (st + u) < a.steps && row[u] < a.F)
+          const double g = group_sum_dpp(ag[i], lpr);
+          const double uu = group_sum_dpp(au[i], lpr);
+          if (lir == lpr - 1 && tok[i] >= 0 && (st + u) < a.steps && row[u] < a.F)
             a.hbuf[prow[i] * a.hstride + row[u]] = (float)(silu64(g) * uu);
         }
       }
@@ -277,61 +277,73 @@ __global__ __launch_bounds__(256) void k_gateup1(GateUpArgs a) {
         L::isums(wu[u][c], xw[c], bs[c], is);
         au += L::term(wu[u][c], j, is, bs[c], dx[c]);
       }
-      const double g = group_sum(ag, lpr);
-      const double uu = group_sum(au, lpr);
-      if (lir == 0 && (st + u) < a.steps && row[u] < a.F)
+      const double g = group_sum_dpp(ag, lpr);
+      const double uu = group_sum_dpp(au, lpr);
+      if (lir == lpr - 1 && (st + u) < a.steps && row[u] < a.F)
         a.hbuf[prow * a.hstride + row[u]] = (float)(silu64(g) * uu);
     }
   }
 }
 
-// q8_K of the chunk(s) this lane holds, from fp32 h, identical to the
-// definition: the block amax is reduced over the 256/WPC lanes of the block.
+// q8_K of one lane chunk of h (WPC fp32 values in registers), identical to
+// the definition: the block amax is reduced over the GW = 256/WPC lanes of
+// the block (aligned lane groups), then id = 127/amax (correctly rounded),
+// q = rint(h*id) clamped, d = amax/127, per-16 sums.  Lanes whose chunk is
+// absent pass have = false (their values do not enter any valid block).
+// dbg (optional): q8_K row the chunk's bytes are also written to.
+template <int FMT, int GW>
+__device__ __forceinline__ void quant_h_regs(const float* hv, bool have, int ch, int* xw, int* bs, double& dx,
+                                             uint8_t* dbg) {
+  using L = Fmt<FMT>;
+  float amax = 0.0f;
+#pragma unroll
+  for (int q = 0; q < L::WPC; ++q) amax = fmaxf(amax, have ? fabsf(hv[q]) : 0.0f);
+  amax = group_max_dpp<GW>(amax);
+  const float id = amax == 0.0f ? 0.0f : __fdiv_rn(127.0f, amax);
+  const bool zero = amax == 0.0f || __builtin_isinf(id);
+#pragma unroll
+  for (int q = 0; q < L::WPC / 4; ++q) {
+    int q0 = 0, q1 = 0, q2 = 0, q3 = 0;
+    if (!zero) {
+      q0 = q8_code(hv[4 * q], id); q1 = q8_code(hv[4 * q + 1], id);
+      q2 = q8_code(hv[4 * q + 2], id); q3 = q8_code(hv[4 * q + 3], id);
+    }
+    xw[q] = (int)((uint32_t)(q0 & 255) | ((uint32_t)(q1 & 255) << 8) | ((uint32_t)(q2 & 255) << 16) |
+                  ((uint32_t)(q3 & 255) << 24));
+    const int s4 = q0 + q1 + q2 + q3;
+    if ((q & 3) == 0) bs[q >> 2] = s4; else bs[q >> 2] += s4;
+  }
+  dx = zero ? 0.0 : (double)__fdiv_rn(amax, 127.0f);
+  if (dbg != nullptr && have) {
+    const int e0 = ch * L::WPC;
+    uint8_t* blk = dbg + (size_t)(e0 >> 8) * kQ8KBytes;
+    const int o = e0 & 255;
+#pragma unroll
+    for (int q = 0; q < L::XDW; ++q) *reinterpret_cast<int*>(blk + 4 + o + 4 * q) = xw[q];
+#pragma unroll
+    for (int q = 0; q < L::NBS; ++q) *reinterpret_cast<int16_t*>(blk + 260 + 2 * ((o >> 4) + q)) = (int16_t)bs[q];
+    if (o == 0) *reinterpret_cast<float*>(blk) = (float)dx;
+  }
+}
+
+// q8_K of the chunk(s) this lane holds, loading the fp32 h row first.
 template <int FMT, int CPL>
 __device__ __forceinline__ void quant_h_chunks(const float* __restrict__ hrow, int lir, int lpr, int cpr,
                                                bool have, int xw[CPL][Fmt<FMT>::XDW],
                                                int bs[CPL][Fmt<FMT>::NBS], double dx[CPL],
                                                uint8_t* dbg) {
   using L = Fmt<FMT>;
-  constexpr int GW = 256 / L::WPC;   // lanes per 256-block
 #pragma unroll
   for (int c = 0; c < CPL; ++c) {
     const int ch = lir + lpr * c;
     const bool v = have && ch < cpr;
     float hv[L::WPC];
-    float amax = 0.0f;
 #pragma unroll
     for (int q = 0; q < L::WPC / 4; ++q) {
       float4 f = v ? reinterpret_cast<const float4*>(hrow + ch * L::WPC)[q] : make_float4(0.f, 0.f, 0.f, 0.f);
       hv[4 * q] = f.x; hv[4 * q + 1] = f.y; hv[4 * q + 2] = f.z; hv[4 * q + 3] = f.w;
-      amax = fmaxf(amax, fmaxf(fmaxf(fabsf(f.x), fabsf(f.y)), fmaxf(fabsf(f.z), fabsf(f.w))));
     }
-    amax = group_max(amax, GW);
-    const float id = amax == 0.0f ? 0.0f : __fdiv_rn(127.0f, amax);
-    const bool zero = amax == 0.0f || __builtin_isinf(id);
-#pragma unroll
-    for (int q = 0; q < L::WPC / 4; ++q) {
-      int q0 = 0, q1 = 0, q2 = 0, q3 = 0;
-      if (!zero) {
-        q0 = q8_code(hv[4 * q], id); q1 = q8_code(hv[4 * q + 1], id);
-        q2 = q8_code(hv[4 * q + 2], id); q3 = q8_code(hv[4 * q + 3], id);
-      }
-      xw[c][q] = (int)((uint32_t)(q0 & 255) | ((uint32_t)(q1 & 255) << 8) | ((uint32_t)(q2 & 255) << 16) |
-                       ((uint32_t)(q3 & 255) << 24));
-      const int s4 = q0 + q1 + q2 + q3;
-      if ((q & 3) == 0) bs[c][q >> 2] = s4; else bs[c][q >> 2] += s4;
-    }
-    dx[c] = zero ? 0.0 : (double)__fdiv_rn(amax, 127.0f);
-    if (dbg != nullptr && v) {
-      const int e0 = ch * L::WPC;
-      uint8_t* blk = dbg + (size_t)(e0 >> 8) * kQ8KBytes;
-      const int o = e0 & 255;
-#pragma unroll
-      for (int q = 0; q < L::XDW; ++q) *reinterpret_cast<int*>(blk + 4 + o + 4 * q) = xw[c][q];
-#pragma unroll
-      for (int q = 0; q < L::NBS; ++q) *reinterpret_cast<int16_t*>(blk + 260 + 2 * ((o >> 4) + q)) = (int16_t)bs[c][q];
-      if (o == 0) *reinterpret_cast<float*>(blk) = (float)dx[c];
-    }
+    quant_h_regs<FMT, 256 / L::WPC>(hv, v, ch, xw[c], bs[c], dx[c], dbg);
   }
 }
 
@@ -407,8 +419,8 @@ __global__ __launch_bounds__(256) void k_down(DownArgs a) {
         }
 #pragma unroll
         for (int i = 0; i < TT; ++i) {
-          const double yv = group_sum(ay[i], lpr);
-          if (lir == 0 && tok[i] >= 0 && (st + u) < a.steps && row[u] < a.H)
+          const double yv = group_sum_dpp(ay[i], lpr);
+          if (lir == lpr - 1 && tok[i] >= 0 && (st + u) < a.steps && row[u] < a.H)
             a.yp[prow[i] * a.H + row[u]] = wt[i] * yv;
         }
       }
@@ -439,6 +451,8 @@ template <int FMT, int CPL>
 __global__ __launch_bounds__(256) void k_down_rows1(DownArgs a) {
   using L = Fmt<FMT>;
   constexpr int kMaxSlots = 33, kMaxRps = 16;
+  constexpr int SG = CPL == 1 ? 3 : 1;      // slots whose loads are in flight together
+  constexpr int GW = 256 / L::WPC;
   __shared__ double yps[kMaxSlots][kMaxRps];
   const int wave = threadIdx.x >> 6, lane = lane_id();
   const int lpr = a.lpr, rps = kWave / lpr, rig = lane / lpr, lir = lane % lpr;
@@ -446,38 +460,67 @@ __global__ __launch_bounds__(256) void k_down_rows1(DownArgs a) {
   const int64_t row = (int64_t)blockIdx.x * rps + rig;
   const int n_routed = a.k;
   const int n_slots = n_routed + a.has_shared;
-  for (int s = wave; s < n_slots; s += 4) {
-    // one token: slot s is the s-th ranked expert (slot k: the shared one);
-    // the gate/up kernel left its down matrix and weight in the slot table
-    const bool shared = s >= n_routed;
-    const int64_t prow = shared ? a.k : s;
-    const double wt = a.slots[s].wt;
-    const uint8_t* Wd = (const uint8_t*)a.slots[s].wd;
-    typename L::W wd[CPL];
-    bool ok[CPL];
+  // one token: slot s is the s-th ranked expert (slot k: the shared one); the
+  // gate/up kernel left its down matrix and weight in the slot table
+  for (int s0 = wave; s0 < n_slots; s0 += 4 * SG) {
+    const uint8_t* Wd[SG];
+    double wt[SG];
+    bool sv[SG];
 #pragma unroll
-    for (int c = 0; c < CPL; ++c) {
-      const int ch = lir + lpr * c;
-      ok[c] = Wd != nullptr && ch < a.cpr && row < a.H;
-      if (ok[c]) wd[c] = L::load(Wd, (size_t)nsb, (size_t)(row * nb + ch / L::CPS), ch % L::CPS);
+    for (int j = 0; j < SG; ++j) {
+      const int s = s0 + 4 * j;
+      sv[j] = s < n_slots;
+      Wd[j] = sv[j] ? (const uint8_t*)a.slots[s].wd : nullptr;
+      wt[j] = sv[j] ? a.slots[s].wt : 0.0;
     }
-    int xw[CPL][L::XDW], bs[CPL][L::NBS];
-    double dx[CPL];
-    uint8_t* dbg = nullptr;
-    uint8_t* hq_base = shared ? a.hq_sh : a.hq;
-    if (blockIdx.x == 0 && rig == 0 && hq_base != nullptr && Wd != nullptr)
-      dbg = hq_base + (shared ? 0 : prow) * a.hq_stride;
-    quant_h_chunks<FMT, CPL>(a.hbuf + prow * a.hstride, lir, lpr, a.cpr, Wd != nullptr, xw, bs, dx, dbg);
-    double ay = 0.0;
+    // every load of the group first: weights and the fp32 h chunks
+    typename L::W wd[SG][CPL];
+    bool ok[SG][CPL];
+    float hv[SG][CPL][L::WPC];
 #pragma unroll
-    for (int c = 0; c < CPL; ++c) {
-      if (!ok[c]) continue;
-      int is[L::SPC];
-      L::isums(wd[c], xw[c], bs[c], is);
-      ay += L::term(wd[c], (lir + lpr * c) % L::CPS, is, bs[c], dx[c]);
+    for (int j = 0; j < SG; ++j) {
+      const int s = s0 + 4 * j;
+      const int64_t prow = s >= n_routed ? a.k : s;
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) {
+        const int ch = lir + lpr * c;
+        ok[j][c] = Wd[j] != nullptr && ch < a.cpr && row < a.H;
+        if (ok[j][c]) wd[j][c] = L::load(Wd[j], (size_t)nsb, (size_t)(row * nb + ch / L::CPS), ch % L::CPS);
+        const bool hvld = Wd[j] != nullptr && ch < a.cpr;
+        const float4* hp = reinterpret_cast<const float4*>(a.hbuf + prow * a.hstride + ch * L::WPC);
+#pragma unroll
+        for (int q = 0; q < L::WPC / 4; ++q) {
+          const float4 f = hvld ? hp[q] : make_float4(0.f, 0.f, 0.f, 0.f);
+          hv[j][c][4 * q] = f.x; hv[j][c][4 * q + 1] = f.y; hv[j][c][4 * q + 2] = f.z; hv[j][c][4 * q + 3] = f.w;
+        }
+      }
     }
-    const double yv = group_sum(ay, lpr);
-    if (lir == 0) yps[shared ? a.k : prow][rig] = wt * yv;
+#pragma unroll
+    for (int j = 0; j < SG; ++j) {
+      const int s = s0 + 4 * j;
+      const bool shared = s >= n_routed;
+      const int64_t prow = shared ? a.k : s;
+      int xw[CPL][L::XDW], bs[CPL][L::NBS];
+      double dx[CPL];
+      uint8_t* dbg = nullptr;
+      uint8_t* hq_base = shared ? a.hq_sh : a.hq;
+      if (blockIdx.x == 0 && rig == 0 && hq_base != nullptr && Wd[j] != nullptr)
+        dbg = hq_base + (shared ? 0 : prow) * a.hq_stride;
+#pragma unroll
+      for (int c = 0; c < CPL; ++c)
+        quant_h_regs<FMT, GW>(hv[j][c], Wd[j] != nullptr && lir + lpr * c < a.cpr, lir + lpr * c, xw[c], bs[c],
+                              dx[c], dbg);
+      double ay = 0.0;
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) {
+        if (!ok[j][c]) continue;
+        int is[L::SPC];
+        L::isums(wd[j][c], xw[c], bs[c], is);
+        ay += L::term(wd[j][c], (lir + lpr * c) % L::CPS, is, bs[c], dx[c]);
+      }
+      const double yv = group_sum_dpp(ay, lpr);
+      if (sv[j] && lir == lpr - 1) yps[shared ? a.k : prow][rig] = wt[j] * yv;
+    }
   }
   __syncthreads();
   if (threadIdx.x < rps) {
