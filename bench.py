@@ -37,10 +37,78 @@ def parse():
     ap.add_argument("--layers", type=int, default=32)
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU oracle sample time")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-verify", action="store_true", help="skip the verify (4-token) measurement")
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="first run a device copy of this many MiB (counter calibration for rocprofv3 --pmc)")
+    ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="no GPU work: turn two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of this bench "
+                         "into profiles/decode_ffn_hbm_traffic.json")
     return ap.parse_args()
 
 
-def build_layers(cfg, L, device):
+KERNEL_SOURCES = ["common.hpp", "formats.hpp", "topk.hpp", "ffn_gemv.hip", "route.hip"]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_ffn_hbm_traffic.json")
+
+
+def kernel_source_hash():
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        h.update(open(os.path.join(ROOT, "quantized_moe_expert_router_amd", "csrc", f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per expert-FFN launch from the committed counter summary,
+    or None when the kernels changed since the counters were taken."""
+    try:
+        t = json.load(open(TRAFFIC_FILE))
+    except (OSError, ValueError):
+        return None
+    return t["traffic_bytes_per_ffn"] if t.get("source_hash") == kernel_source_hash() else None
+
+
+def summarize_pmc(fetch_dir, write_dir, calib_mib):
+    """Per-dispatch FETCH_SIZE / WRITE_SIZE (KiB) of the decode layer's gate/up
+    and down launches, scaled by what the same counters read for the copy of
+    known size, summed per expert-FFN launch."""
+    import csv
+    import glob
+
+    def load(d, counter):
+        rows = []
+        for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            rows += [r for r in csv.DictReader(open(f)) if r.get("Counter_Name") == counter]
+        return rows
+
+    out = {}
+    for d, counter in ((fetch_dir, "FETCH_SIZE"), (write_dir, "WRITE_SIZE")):
+        rows = load(d, counter)
+        per = {}
+        for r in rows:
+            per.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+        copy = [v for n, vs in per.items() if "copy" in n.lower() for v in vs]
+        copy_kib = max(copy) if copy else None
+        factor = (calib_mib * 1024.0 / copy_kib) if copy_kib else 1.0
+
+        def med(key):
+            vs = sorted(v for n, vv in per.items() if key in n for v in vv)
+            vs = vs[len(vs) // 4:]                     # steady state: drop the first (setup) dispatches
+            return vs[len(vs) // 2] * factor if vs else None
+
+        out[counter] = {"gateup_kib": med("k_gateup1<1, 1, 4>"), "down_kib": med("k_down_rows1"),
+                        "logits_kib": med("k_logits"), "copy_kib_raw": copy_kib, "scale": factor}
+    f, w = out["FETCH_SIZE"], out["WRITE_SIZE"]
+    traffic = (f["gateup_kib"] + f["down_kib"] + w["gateup_kib"] + w["down_kib"]) * 1024.0
+    res = {"source_hash": kernel_source_hash(), "calib_copy_mib": calib_mib, "counters": out,
+           "traffic_bytes_per_ffn": traffic,
+           "note": "median per dispatch over the steady-state decode layers; gate/up launch includes the inline "
+                   "top-k logits read (E*8 bytes)"}
+    json.dump(res, open(TRAFFIC_FILE, "w"), indent=1)
+    print(json.dumps(res, indent=1))
+
+
+def build_layers(cfg, L, device, T):
     """Layer 0 from the numpy generator (the parity-tested one); layers 1..L-1
     from the same recipe drawn with torch's seeded device generator."""
     import torch
@@ -50,7 +118,7 @@ def build_layers(cfg, L, device):
     layers = []
     lay0 = syn.gen_layer(cfg)
     dl0 = moeq.DeviceLayer(lay0, device=device)
-    layers.append(dict(w_router=dl0.w_router, desc=dl0.ffn_desc(1), keep=dl0))
+    layers.append(dict(w_router=dl0.w_router, bias=dl0.bias, desc=dl0.ffn_desc(T), keep=dl0))
     gen = torch.Generator(device=device)
     for l in range(1, L):
         gen.manual_seed(cfg.seed * 1000 + l)
@@ -69,20 +137,79 @@ def build_layers(cfg, L, device):
             return t
 
         g, u, d = table(cfg.fmt_gate, cfg.F, cfg.H), table(cfg.fmt_up, cfg.F, cfg.H), table(cfg.fmt_down, cfg.H, cfg.F)
-        sg, _ = packed(cfg.sh_fmt_gate, cfg.F_shared, cfg.H, 1)
-        su, _ = packed(cfg.sh_fmt_up, cfg.F_shared, cfg.H, 1)
-        sd, _ = packed(cfg.sh_fmt_down, cfg.H, cfg.F_shared, 1)
         wr = torch.randn((cfg.E, cfg.H), generator=gen, device=device, dtype=torch.float32) * 0.02
         desc = moeq.FfnDesc()
-        desc.T, desc.H, desc.F, desc.E, desc.k = 1, cfg.H, cfg.F, cfg.E, cfg.k
+        desc.T, desc.H, desc.F, desc.E, desc.k = T, cfg.H, cfg.F, cfg.E, cfg.k
         desc.fmt_gate, desc.fmt_up, desc.fmt_down = cfg.fmt_gate, cfg.fmt_up, cfg.fmt_down
         desc.gate, desc.up, desc.down = g.data_ptr(), u.data_ptr(), d.data_ptr()
-        desc.F_shared = cfg.F_shared
-        desc.sh_fmt_gate, desc.sh_fmt_up, desc.sh_fmt_down = cfg.sh_fmt_gate, cfg.sh_fmt_up, cfg.sh_fmt_down
-        desc.sh_gate, desc.sh_up, desc.sh_down = sg.data_ptr(), su.data_ptr(), sd.data_ptr()
-        layers.append(dict(w_router=wr, desc=desc, keep=keep))
+        if cfg.shared:
+            sg, _ = packed(cfg.sh_fmt_gate, cfg.F_shared, cfg.H, 1)
+            su, _ = packed(cfg.sh_fmt_up, cfg.F_shared, cfg.H, 1)
+            sd, _ = packed(cfg.sh_fmt_down, cfg.H, cfg.F_shared, 1)
+            desc.F_shared = cfg.F_shared
+            desc.sh_fmt_gate, desc.sh_fmt_up, desc.sh_fmt_down = cfg.sh_fmt_gate, cfg.sh_fmt_up, cfg.sh_fmt_down
+            desc.sh_gate, desc.sh_up, desc.sh_down = sg.data_ptr(), su.data_ptr(), sd.data_ptr()
+        layers.append(dict(w_router=wr, bias=dl0.bias, desc=desc, keep=keep))
     torch.cuda.synchronize()
     return layers
+
+
+class LayerCycle:
+    """L synthetic layers of one shape with T tokens each, their per-layer HIP
+    graphs and one graph for the whole cycle; run(n) replays exactly n layer
+    steps (one step = the whole hot path of one layer over its T tokens)."""
+
+    def __init__(self, cfg, T, L, device):
+        import numpy as np
+        import torch
+        from quantized_moe_expert_router_amd import moeq
+        self.cfg, self.T, self.L = cfg, T, L
+        self.layers = build_layers(cfg, L, device, T)
+        rng = np.random.default_rng(7)
+        self.xs = [torch.from_numpy(rng.standard_normal((T, cfg.H)).astype(np.float32)).to(device)
+                   for _ in range(L)]
+        self.route_out = moeq.RouteOut(T, cfg.E, cfg.k, device)
+        self.y = torch.empty((T, cfg.H), dtype=torch.float32, device=device)
+        self.rdesc = moeq.RouteDesc(T, cfg.H, cfg.E, cfg.k, cfg.gating, 1.0)
+        self.ws = torch.empty(moeq.moeq_moe_layer_workspace(self.rdesc, self.layers[0]["desc"]), dtype=torch.uint8,
+                              device=device)
+        for l in range(L):
+            self.step(l)
+        torch.cuda.synchronize()
+        stream = torch.cuda.Stream()
+        self.graphs = []
+        with torch.cuda.stream(stream):
+            for l in range(L):
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g, stream=stream):
+                    self.step(l, stream)
+                self.graphs.append(g)
+            self.cycle = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(self.cycle, stream=stream):
+                for l in range(L):
+                    self.step(l, stream)
+        torch.cuda.synchronize()
+
+    def step(self, l, stream=None):
+        from quantized_moe_expert_router_amd import moeq
+        lay = self.layers[l]
+        moeq.moeq_moe_layer(self.rdesc, lay["desc"], self.xs[l], lay["w_router"], lay["bias"], self.route_out, None,
+                            self.y, self.ws, stream)
+
+    def run(self, n):
+        for _ in range(n // self.L):
+            self.cycle.replay()
+        for l in range(n % self.L):
+            self.graphs[l].replay()
+
+    def time(self, steps, warmup):
+        import torch
+        self.run(warmup)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        self.run(steps)
+        torch.cuda.synchronize()
+        return time.perf_counter() - t0
 
 
 def cpu_baseline(cfg, seconds):
@@ -112,6 +239,9 @@ def cpu_baseline(cfg, seconds):
 
 def main():
     args = parse()
+    if args.summarize_pmc:
+        summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], args.calib_copy_mib or 256)
+        return
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path (run with --gpus 1)",
               file=sys.stderr)
@@ -123,66 +253,31 @@ def main():
 
     dev = "cuda:0"
     torch.cuda.set_device(0)
+    if args.calib_copy_mib:
+        a = torch.empty(args.calib_copy_mib << 20, dtype=torch.uint8, device=dev).fill_(1)
+        b = torch.empty_like(a)
+        b.copy_(a)
+        torch.cuda.synchronize()
+        del a, b
     cfg = syn.CONFIGS["decode"]
     L = args.layers
     t_setup = time.time()
-    layers = build_layers(cfg, L, dev)
-    rng = np.random.default_rng(7)
-    xs = [torch.from_numpy(rng.standard_normal((1, cfg.H)).astype(np.float32)).to(dev) for _ in range(L)]
-    route_out = moeq.RouteOut(1, cfg.E, cfg.k, dev)
+    cyc = LayerCycle(cfg, 1, L, dev)
+    layers, xs, route_out, y = cyc.layers, cyc.xs, cyc.route_out, cyc.y
     route_ws = torch.empty(max(256, moeq.moeq_route_workspace(1, cfg.H, cfg.E, cfg.k, cfg.gating)),
                            dtype=torch.uint8, device=dev)
     xq = torch.empty((1, cfg.H // 256 * moeq.Q8K_BYTES), dtype=torch.uint8, device=dev)
     ffn_ws = torch.empty(moeq.moeq_expert_ffn_workspace(layers[0]["desc"]), dtype=torch.uint8, device=dev)
-    y = torch.empty((1, cfg.H), dtype=torch.float32, device=dev)
-
-    rdesc = moeq.RouteDesc(1, cfg.H, cfg.E, cfg.k, cfg.gating, 1.0)
-    layer_ws = torch.empty(moeq.moeq_moe_layer_workspace(rdesc, layers[0]["desc"]), dtype=torch.uint8,
-                           device=dev)
-
-    def layer_step(l, stream=None):
-        lay = layers[l]
-        moeq.moeq_moe_layer(rdesc, lay["desc"], xs[l], lay["w_router"], None, route_out, None, y, layer_ws,
-                            stream)
 
     def ffn_only(l, stream=None):
         lay = layers[l]
         moeq.moeq_expert_ffn(lay["desc"], xq, route_out.ids, route_out.w, route_out.offsets, route_out.pairs,
                              route_out.active, None, y, ffn_ws, stream)
 
-    # Eager warm-up of every layer, then HIP graphs: one per layer and one for
-    # the whole cycle of L layers (a decode step through the stack).
-    for l in range(L):
-        layer_step(l)
-    torch.cuda.synchronize()
-    stream = torch.cuda.Stream()
-    graphs = []
-    with torch.cuda.stream(stream):
-        for l in range(L):
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g, stream=stream):
-                layer_step(l, stream)
-            graphs.append(g)
-        cycle = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(cycle, stream=stream):
-            for l in range(L):
-                layer_step(l, stream)
-    torch.cuda.synchronize()
     setup_s = time.time() - t_setup
 
-    def run_steps(n):
-        for _ in range(n // L):
-            cycle.replay()
-        for l in range(n % L):
-            graphs[l].replay()
-
     # ---- timed region: exactly `steps` whole layers (value)
-    run_steps(args.warmup)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    run_steps(args.steps)
-    torch.cuda.synchronize()
-    dt = time.perf_counter() - t0
+    dt = cyc.time(args.steps, args.warmup)
     ms_per_step = dt * 1e3 / args.steps
     tokens_per_s = args.steps / dt
 
@@ -218,6 +313,25 @@ def main():
     layer_bytes = ffn_bytes + cfg.E * cfg.H * 4 + cfg.H * 4
     achieved = ffn_bytes / (ffn_us * 1e-6) / 1e9
 
+    # ---- secondary: MTP verify rows (4 tokens per step, union of experts)
+    verify = None
+    if not args.no_verify:
+        del cyc
+        torch.cuda.empty_cache()
+        vcfg = syn.CONFIGS["verify"]
+        vL = max(4, L // 4)
+        vc = LayerCycle(vcfg, 4, vL, dev)
+        vsteps = max(vL, args.steps // 4)
+        vdt = vc.time(vsteps, max(vL, args.warmup // 4))
+        vms = vdt * 1e3 / vsteps
+        ids = vc.route_out.ids.cpu().numpy()
+        union = len(set(ids.reshape(-1).tolist()))
+        vbytes = union * syn.expert_bytes(vcfg) + vcfg.E * vcfg.H * 4 + 2 * 4 * vcfg.H * 4
+        verify = {"workload": vcfg.name, "T": 4, "tokens_per_s": 4 * vsteps / vdt, "ms_per_step": vms,
+                  "layers_cycled": vL, "union_last_step": union,
+                  "layer_hbm_gbs_est": vbytes / (vms * 1e-3) / 1e9}
+        del vc
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(cfg, args.cpu_seconds)
@@ -241,9 +355,10 @@ def main():
         "layer_hbm_gbs": layer_bytes / (ms_per_step * 1e-3) / 1e9,
         "roofline": {"bound": "hbm", "kernel": "expert FFN (gate/up GEMV + down GEMV)",
                      "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic(),
                      "bytes_per_launch": ffn_bytes, "avg_launch_us": ffn_us},
         "cpu_baseline": cpu,
+        "verify_b4": verify,
         "setup_s": setup_s,
     }
     print(json.dumps(out), flush=True)
