@@ -93,17 +93,16 @@ def summarize_pmc(fetch_dir, write_dir, calib_mib):
 
         def med(key):
             vs = sorted(v for n, vv in per.items() if key in n for v in vv)
-            vs = vs[len(vs) // 4:]                     # steady state: drop the first (setup) dispatches
             return vs[len(vs) // 2] * factor if vs else None
 
-        out[counter] = {"gateup_kib": med("k_gateup1<1, 1, 4>"), "down_kib": med("k_down_rows1"),
+        out[counter] = {"gateup_kib": med("k_gateup1<1, 1, 0>"), "down_kib": med("k_down_rows1"),
                         "logits_kib": med("k_logits"), "copy_kib_raw": copy_kib, "scale": factor}
     f, w = out["FETCH_SIZE"], out["WRITE_SIZE"]
     traffic = (f["gateup_kib"] + f["down_kib"] + w["gateup_kib"] + w["down_kib"]) * 1024.0
     res = {"source_hash": kernel_source_hash(), "calib_copy_mib": calib_mib, "counters": out,
            "traffic_bytes_per_ffn": traffic,
-           "note": "median per dispatch over the steady-state decode layers; gate/up launch includes the inline "
-                   "top-k logits read (E*8 bytes)"}
+           "note": "median per dispatch of the expert-FFN-only launches (k_gateup1 with given ids, then k_down_rows1) "
+                   "over 32 cycled layers"}
     json.dump(res, open(TRAFFIC_FILE, "w"), indent=1)
     print(json.dumps(res, indent=1))
 
