@@ -1,6 +1,7 @@
 // C ABI of libmoeq: argument validation on the host, workspace layout, and
 // kernel dispatch.  Every check runs before anything is enqueued.
 #include <algorithm>
+#include <climits>
 
 #include "../../include/moeq.h"
 #include "formats.hpp"
@@ -44,21 +45,43 @@ bool lane_geo(int fmt, int64_t cols, LaneGeo* g) {
   return true;
 }
 
+// Rows per expert up to which the dot-product (GEMV) kernels run in AUTO mode;
+// experts with more rows (and the shared expert when T exceeds it) go to the
+// int8 MFMA grouped GEMM.
+constexpr int kGemvMaxRows = 4;
+
+int gemv_max_of(int32_t path) {
+  return path == MOEQ_PATH_GEMV ? INT32_MAX : path == MOEQ_PATH_MFMA ? 0 : kGemvMaxRows;
+}
+
+// Upper bound on the MFMA tiles of the routed experts: sum over experts with
+// more than thr rows of ceil(n_e / 32) <= (T*k + 31 * U) / 32, with U the
+// number of such experts.
+int64_t mfma_max_tiles(const moeq_ffn_desc* d, int thr) {
+  const int64_t P = d->T * d->k;
+  if (d->T <= thr) return 0;
+  const int64_t U = std::min<int64_t>(d->E, P / (thr + 1));
+  return (P + 31 * U) / 32 + 1;
+}
+
 struct FfnLayout {
-  int64_t Fmax, nrows;
-  size_t off_h, off_yp, off_hq, off_hqs, off_slots, total;
+  int64_t Fmax, nrows, max_tiles;
+  size_t off_h, off_yp, off_hq, off_hqs, off_slots, off_tiles, off_count, total;
 };
 FfnLayout ffn_layout(const moeq_ffn_desc* d) {
   FfnLayout L{};
   const bool sh = d->sh_gate != nullptr;
   L.Fmax = sh ? std::max(d->F, d->F_shared) : d->F;
   L.nrows = d->T * d->k + d->T;
+  L.max_tiles = mfma_max_tiles(d, gemv_max_of(d->path));
   size_t o = 0;
   L.off_h = o;   o += align256((size_t)L.nrows * L.Fmax * sizeof(float));
-  L.off_yp = o;  o += align256((size_t)L.nrows * d->H * sizeof(double));
+  L.off_yp = o;  o += align256((size_t)L.nrows * d->H * sizeof(float));
   L.off_hq = o;  o += align256((size_t)d->T * d->k * (d->F / 256) * kQ8KBytes);
   L.off_hqs = o; o += align256(sh ? (size_t)d->T * (d->F_shared / 256) * kQ8KBytes : 0);
   L.off_slots = o; o += align256((size_t)(d->k + 1) * sizeof(SlotRec));
+  L.off_tiles = o; o += align256((size_t)L.max_tiles * sizeof(int4));
+  L.off_count = o; o += 256;
   L.total = o;
   return L;
 }
@@ -81,7 +104,6 @@ int check_ffn_desc(const moeq_ffn_desc* d) {
   }
   if (d->path != MOEQ_PATH_AUTO && d->path != MOEQ_PATH_GEMV && d->path != MOEQ_PATH_MFMA)
     return MOEQ_E_INVALID;
-  if (d->path == MOEQ_PATH_MFMA) return MOEQ_E_UNSUPPORTED;
   if (d->accumulate != 0 && d->accumulate != 1) return MOEQ_E_INVALID;
   LaneGeo g;
   if (!lane_geo(d->fmt_gate, d->H, &g) || !lane_geo(d->fmt_down, d->F, &g)) return MOEQ_E_UNSUPPORTED;
@@ -180,7 +202,10 @@ int ffn_enqueue(const moeq_ffn_desc* d, const void* x_q8K, const int32_t* topk_i
   const bool sh = d->sh_gate != nullptr;
   const bool same_shape = sh && d->sh_fmt_gate == d->fmt_gate && d->sh_fmt_down == d->fmt_down &&
                           d->F_shared == d->F;
-  const bool one = d->T == 1;
+  const int thr = gemv_max_of(d->path);
+  const bool one = d->T == 1 && thr >= 1;       // the one-token dot-product kernels
+  const bool gemv = thr >= 1;                    // any expert on the dot-product path
+  const bool mfma = d->T > thr;                  // any expert on the MFMA path
   const int tt = one ? 1 : 4;
   const int max_union = (int)std::min<int64_t>(d->E, d->T * d->k);
   int rc;
@@ -194,6 +219,7 @@ int ffn_enqueue(const moeq_ffn_desc* d, const void* x_q8K, const int32_t* topk_i
     a.max_union = max_union;
     a.hbuf = (float*)(wsb + L.off_h); a.hstride = L.Fmax;
     a.lpr = g.lpr; a.cpr = g.cpr; a.steps = std::max(1, 4 / g.rps);
+    a.gemv_max = thr;
     a.topk_ids = topk_ids; a.topk_w = topk_w; a.E = d->E;
     a.slots = (SlotRec*)(wsb + L.off_slots);
     a.shared_scale = shared_scale;
@@ -227,11 +253,12 @@ int ffn_enqueue(const moeq_ffn_desc* d, const void* x_q8K, const int32_t* topk_i
     a.topk_w = topk_w; a.shared_scale = shared_scale;
     a.offsets = expert_offsets; a.pairs = pairs; a.active = active; a.max_union = max_union;
     a.hbuf = (const float*)(wsb + L.off_h); a.hstride = L.Fmax;
-    a.yp = (double*)(wsb + L.off_yp);
+    a.yp = (float*)(wsb + L.off_yp);
     a.hq = wsb + L.off_hq;
     a.hq_sh = sh ? wsb + L.off_hqs : nullptr;
     a.hq_stride = (F / 256) * kQ8KBytes;
     a.lpr = g->lpr; a.cpr = g->cpr; a.rb = kRowBlock; a.steps = kRowBlock / (4 * g->rps);
+    a.gemv_max = thr;
     a.has_shared = sh ? 1 : 0;
     a.y = y; a.accumulate = d->accumulate;
     return a;
@@ -242,14 +269,58 @@ int ffn_enqueue(const moeq_ffn_desc* d, const void* x_q8K, const int32_t* topk_i
     dim3 grid((unsigned)(d->H / kRowBlock), (unsigned)n_slots);
     return launch_down(fmt, tt, g.cpl, grid, a, s);
   };
+  // int8 MFMA tiles: mode 0 = gate/up (+ q8_K(h)), mode 1 = down
+  int4* tiles = (int4*)(wsb + L.off_tiles);
+  int32_t* tcount = (int32_t*)(wsb + L.off_count);
+  auto mfma_launch = [&](int mode, bool shared_exp) -> int {
+    MfmaArgs a{};
+    a.shared = shared_exp ? 1 : 0;
+    a.tiles = tiles; a.count = tcount;
+    a.pairs = pairs; a.k = d->k; a.T = d->T;
+    a.topk_w = topk_w; a.shared_scale = shared_scale;
+    a.yp = (float*)(wsb + L.off_yp);
+    const int64_t Fx = shared_exp ? d->F_shared : d->F;
+    const int64_t hq_stride = (Fx / 256) * kQ8KBytes;
+    uint8_t* hq = shared_exp ? wsb + L.off_hqs : wsb + L.off_hq;
+    int fmt;
+    unsigned gx = shared_exp ? (unsigned)((d->T + 31) / 32) : (unsigned)L.max_tiles;
+    unsigned gy;
+    a.gate = d->gate; a.up = d->up; a.down = d->down;
+    if (mode == 0) {
+      fmt = shared_exp ? d->sh_fmt_gate : d->fmt_gate;
+      a.sh_w0 = (const uint8_t*)d->sh_gate; a.sh_w1 = (const uint8_t*)d->sh_up;
+      a.N = Fx; a.K = d->H;
+      a.src = (const uint8_t*)x_q8K; a.src_stride = (d->H / 256) * kQ8KBytes;
+      a.hq = hq; a.hq_stride = hq_stride;
+      gy = (unsigned)(Fx / 256);
+    } else {
+      fmt = shared_exp ? d->sh_fmt_down : d->fmt_down;
+      a.sh_w0 = (const uint8_t*)d->sh_down;
+      a.N = d->H; a.K = Fx;
+      a.src = hq; a.src_stride = hq_stride;
+      gy = (unsigned)(d->H / 256);
+    }
+    return launch_mfma(fmt, mode, dim3(gx, gy), a, s);
+  };
 
-  // gate/up: h[pair, f] = fl32(silu(g) u)
+  if (mfma) {
+    if ((rc = launch_mfma_plan(active, expert_offsets, thr, (int)L.max_tiles, tiles, tcount, s)))
+      return rc;
+  }
+  // gate/up: h[pair, f] = fl32(silu(g) u)  (dot-product path: fp32 h rows;
+  // MFMA path: q8_K(h) rows straight away)
   const int n_routed_slots = one ? d->k : max_union;
-  if (same_shape) {
-    if ((rc = gateup(kModeBoth, d->fmt_gate, d->F, n_routed_slots + 1))) return rc;
-  } else {
-    if ((rc = gateup(kModeRouted, d->fmt_gate, d->F, n_routed_slots))) return rc;
-    if (sh && (rc = gateup(kModeShared, d->sh_fmt_gate, d->F_shared, 1))) return rc;
+  if (gemv) {
+    if (same_shape) {
+      if ((rc = gateup(kModeBoth, d->fmt_gate, d->F, n_routed_slots + 1))) return rc;
+    } else {
+      if ((rc = gateup(kModeRouted, d->fmt_gate, d->F, n_routed_slots))) return rc;
+      if (sh && (rc = gateup(kModeShared, d->sh_fmt_gate, d->F_shared, 1))) return rc;
+    }
+  }
+  if (mfma) {
+    if ((rc = mfma_launch(0, false))) return rc;
+    if (sh && (rc = mfma_launch(0, true))) return rc;
   }
   // down and the weighted combine
   if (one && (!sh || same_shape)) {
@@ -258,13 +329,19 @@ int ffn_enqueue(const moeq_ffn_desc* d, const void* x_q8K, const int32_t* topk_i
     dim3 grid((unsigned)((d->H + g.rps - 1) / g.rps));
     return launch_down_rows1(d->fmt_down, g.cpl, grid, a, s);
   }
-  if (same_shape) {
-    if ((rc = down(kModeBoth, d->fmt_down, d->F, max_union + 1))) return rc;
-  } else {
-    if ((rc = down(kModeRouted, d->fmt_down, d->F, max_union))) return rc;
-    if (sh && (rc = down(kModeShared, d->sh_fmt_down, d->F_shared, 1))) return rc;
+  if (gemv) {
+    if (same_shape) {
+      if ((rc = down(kModeBoth, d->fmt_down, d->F, max_union + 1))) return rc;
+    } else {
+      if ((rc = down(kModeRouted, d->fmt_down, d->F, max_union))) return rc;
+      if (sh && (rc = down(kModeShared, d->sh_fmt_down, d->F_shared, 1))) return rc;
+    }
   }
-  return launch_combine((const double*)(wsb + L.off_yp), d->T, d->H, d->k, sh ? 1 : 0, y, d->accumulate, s);
+  if (mfma) {
+    if ((rc = mfma_launch(1, false))) return rc;
+    if (sh && (rc = mfma_launch(1, true))) return rc;
+  }
+  return launch_combine((const float*)(wsb + L.off_yp), d->T, d->H, d->k, sh ? 1 : 0, y, d->accumulate, s);
 }
 
 }  // namespace
@@ -333,7 +410,7 @@ int moeq_moe_layer(const moeq_route_desc* r, const moeq_ffn_desc* f, const float
   uint8_t* wsb = (uint8_t*)ws;
   hipStream_t s = (hipStream_t)stream;
   void* xq = wsb + L.off_xq;
-  if (r->T == 1) {
+  if (r->T == 1 && gemv_max_of(f->path) >= 1) {
     // one token: logits + q8_K(x) in one launch, then gate/up routes inline
     double* lg = logits ? logits : (double*)(wsb + L.off_route);
     if ((rc = launch_logits(1, r->H, r->E, x, w_router, bias, lg, xq, s))) return hip_status(rc);

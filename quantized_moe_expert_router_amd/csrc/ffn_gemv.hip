@@ -28,18 +28,20 @@ struct Slot {
   int64_t list_off;
 };
 
+// Slot of the union (or the shared expert); experts with more than gemv_max
+// rows belong to the MFMA path and are not valid here.
 __device__ __forceinline__ Slot decode_slot(int slot, int mode, int max_union, const int32_t* active,
-                                            const int32_t* offsets, int64_t T) {
+                                            const int32_t* offsets, int64_t T, int gemv_max) {
   Slot s{0, 0, -1, 0, 0};
   if (mode == kModeShared || (mode == kModeBoth && slot == max_union)) {
-    s.valid = 1; s.shared = 1; s.n = (int)T;
+    s.valid = T <= gemv_max; s.shared = 1; s.n = (int)T;
     return s;
   }
   if (slot >= active[0]) return s;
   s.e = active[1 + slot];
   s.list_off = offsets[s.e];
   s.n = offsets[s.e + 1] - offsets[s.e];
-  s.valid = s.n > 0;
+  s.valid = s.n > 0 && s.n <= gemv_max;
   return s;
 }
 
@@ -77,7 +79,7 @@ __global__ __launch_bounds__(256) void k_gateup(GateUpArgs a) {
       }
     }
   }
-  const Slot sl = decode_slot(blockIdx.y, a.mode, a.max_union, a.active, a.offsets, a.T);
+  const Slot sl = decode_slot(blockIdx.y, a.mode, a.max_union, a.active, a.offsets, a.T, a.gemv_max);
   if (!sl.valid) return;
   const uint8_t* Wg = sl.shared ? a.sh_gate : (const uint8_t*)a.gate[sl.e];
   const uint8_t* Wu = sl.shared ? a.sh_up : (const uint8_t*)a.up[sl.e];
@@ -350,7 +352,7 @@ __device__ __forceinline__ void quant_h_chunks(const float* __restrict__ hrow, i
 template <int FMT, int TT, int CPL, int UNR>
 __global__ __launch_bounds__(256) void k_down(DownArgs a) {
   using L = Fmt<FMT>;
-  const Slot sl = decode_slot(blockIdx.y, a.mode, a.max_union, a.active, a.offsets, a.T);
+  const Slot sl = decode_slot(blockIdx.y, a.mode, a.max_union, a.active, a.offsets, a.T, a.gemv_max);
   if (!sl.valid) return;
   // An expert is resident only if all three of its matrices are present.
   const uint8_t* Wd = sl.shared ? a.sh_down : (const uint8_t*)a.down[sl.e];
@@ -421,7 +423,7 @@ __global__ __launch_bounds__(256) void k_down(DownArgs a) {
         for (int i = 0; i < TT; ++i) {
           const double yv = group_sum_dpp(ay[i], lpr);
           if (lir == lpr - 1 && tok[i] >= 0 && (st + u) < a.steps && row[u] < a.H)
-            a.yp[prow[i] * a.H + row[u]] = wt[i] * yv;
+            a.yp[prow[i] * a.H + row[u]] = (float)(wt[i] * yv);
         }
       }
     }
@@ -429,16 +431,19 @@ __global__ __launch_bounds__(256) void k_down(DownArgs a) {
 
 }
 
-// y[t] (=|+=) fl32(sum_slot yp[t*k+slot] + yp[T*k+t]), slots in rank order,
-// then the shared expert: the per-pair outputs were staged by k_down.
-__global__ __launch_bounds__(256) void k_combine(const double* __restrict__ yp, int64_t T, int64_t H, int k,
+// y[t] (=|+=) fl32(sum_slot yp[t*k+slot] + yp[T*k+t]) summed in fp64, slots in
+// rank order, then the shared expert: the weighted per-pair outputs were
+// staged in fp32 by the down kernels (rounding each of the k+1 terms to fp32
+// first moves y by about 1e-7 relative, far inside the y tolerance; the
+// bit-exact q8_K(h) lies upstream of it).
+__global__ __launch_bounds__(256) void k_combine(const float* __restrict__ yp, int64_t T, int64_t H, int k,
                                                  int has_shared, float* __restrict__ y, int accumulate) {
   const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (idx >= T * H) return;
   const int64_t t = idx / H, r = idx % H;
   double acc = 0.0;
-  for (int s = 0; s < k; ++s) acc += yp[(t * k + s) * H + r];
-  if (has_shared) acc += yp[(T * k + t) * H + r];
+  for (int s = 0; s < k; ++s) acc += (double)yp[(t * k + s) * H + r];
+  if (has_shared) acc += (double)yp[(T * k + t) * H + r];
   y[idx] = accumulate ? (float)((double)y[idx] + acc) : (float)acc;
 }
 
@@ -612,7 +617,7 @@ int launch_down_rows1(int fmt, int cpl, dim3 grid, const DownArgs& a, hipStream_
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
-int launch_combine(const double* yp, int64_t T, int64_t H, int k, int has_shared, float* y, int accumulate,
+int launch_combine(const float* yp, int64_t T, int64_t H, int k, int has_shared, float* y, int accumulate,
                    hipStream_t s) {
   const int64_t n = T * H;
   if (n == 0) return 0;

@@ -1,0 +1,529 @@
+// int8 MFMA grouped GEMM for experts with many rows (multi-token chunks:
+// verify unions and prefill).  The pages send such chunks to int8 matrix
+// cores instead of per-row dot products (Pulsar README, 'Verify' and
+// DeepSeek-V4-Flash paragraphs: quantized int8 tensor-core prefill; Strata
+// article, chunked prefill through quantized matmuls), while a single token
+// stays memory-bound on the dot-product path.
+//
+// Tile = one expert x 32 of its rows (tokens, or pairs for down) x 256 weight
+// rows: a 512-thread workgroup of 8 waves, each wave 32 weight rows.  The
+// activation side (q8_K rows of the tile, one 256-block at a time) is staged
+// in LDS once and shared by the 8 waves; each wave reads its weights straight
+// from HBM into registers (each weight byte is read once per tile).
+//
+// MFMA roles: C[m = token][n = weight row] = sum_k A[m][k] * B[k][n] with
+// v_mfma_i32_32x32x32_i8, so a lane's 16 results share one weight row
+// (n = lane % 32) and its per-row scales stay in that lane.  Lane l holds
+// K bytes 16*(l/32) .. +15 of both operands, the same assignment on both
+// sides, so only the output layout is fixed by the hardware: lane l, value r
+// is C[8*(r/4) + 4*(l/32) + r%4][l%32].
+//
+// Exactness per super-block (the integer parts of the dequant-dot are exact,
+// the combine is fp64):
+//   Q4_K  w = d*sc_j*q - dmin*m_j, sc, m < 64, q < 16.  sc*q does not fit in
+//         int8, so sc = 8*sh + sl (sh, sl < 8) and two exact int32 sums run
+//         over the whole super-block on pre-scaled weights q*sl, q*sh (< 106):
+//         S1 = sum_j sc_j isum_j = P_lo + 8*P_hi.
+//   Q2_K  w = d*sc_j*q - dmin*m_j, sc*q < 46: one sum on q*sc.
+//   Min term S2 = sum_j m_j * bsum_j(x): each block sum is split as
+//         64*bh + bl (bl < 64, |bh| <= 64) so one MFMA over [bl | bh] against
+//         [m | 0] and one against [0 | m] give S2 = X_l + 64*X_h exactly.
+//   Q6_K  w = d*sc_j*(q-32), signed 8-bit sc: one 16-deep MFMA per sub-block
+//         (exact int32 dot of q with x), scaled by sc_j in int32; the -32 part
+//         is 32 * sum_j sc_j bsum_j, from the same split-sum MFMA pair.
+//   Q8_0  w = d_b*q: one MFMA per 32-block, scaled by d_b in fp64.
+// term per super-block = d_x * (d * S1 - dmin * S2) in fp64, summed over the
+// super-blocks in order; h = fl32(silu(g) * u); y rows in fp32.
+#include "formats.hpp"
+#include "launch.hpp"
+
+namespace moeq {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v16i __attribute__((ext_vector_type(16)));
+
+constexpr int kTileT = 32;         // activation rows (tokens / pairs) per tile
+constexpr int kMfWaves = 8;        // waves per workgroup, 32 weight rows each
+constexpr int kMfRows = 32 * kMfWaves;
+constexpr int kQsStride = 272;     // LDS bytes per staged row: 256 + 16 (bank spread)
+
+struct __align__(16) StageLds {
+  uint8_t qs[kTileT][kQsStride];   // q8_K quants of the tile rows, current 256-block
+  uint8_t bsp[kTileT][2][16];      // split block sums: [0] = bl entries, [1] = bh entries
+  float dx[kTileT];                // q8_K scales
+};
+
+__device__ __forceinline__ v16i mfma_k32(v4i a, v4i b, v16i c) {
+  return __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ v16i mfma_k16(long a, long b, v16i c) {
+  return __builtin_amdgcn_mfma_i32_32x32x16_i8(a, b, c, 0, 0, 0);
+}
+
+// Four packed bytes times a small factor s: every byte product stays below
+// 256, so two bytes per 16-bit half multiply without carries (v_pk_mul_lo_u16).
+__device__ __forceinline__ uint32_t bytes_times(uint32_t v, uint32_t s) {
+  typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+  const u16x2 a = __builtin_bit_cast(u16x2, v);
+  const u16x2 b = __builtin_bit_cast(u16x2, s * 0x00010001u);
+  return __builtin_bit_cast(uint32_t, a * b);
+}
+
+__device__ __forceinline__ v4i lds_v4(const uint8_t* p) { return *reinterpret_cast<const v4i*>(p); }
+
+// Token row m of the lane's results for value r.
+__device__ __forceinline__ int out_row(int r, int g) { return 8 * (r >> 2) + 4 * g + (r & 3); }
+
+// ------------------------------------------------------------ per-format W side
+//
+// A trait per weight format:
+//   NBSP      entries of the split block sums the min / offset term needs (0: none)
+//   Wt        the weight registers of one lane for one super-block
+//   load      global loads of lane (row, half g) for super-block sbi
+//   mac       MFMAs and the fp64 combine into acc[16]; A fragments from LDS
+
+template <int FMT> struct Mf;
+
+template <> struct Mf<FQ4K> {
+  static constexpr bool kLateSecond = false;
+  static constexpr int NBSP = 8;   // one sum per 32-sub-block: bsums[2j] + bsums[2j+1]
+  struct Wt { uint4 c[4]; uint4 h; };
+  __device__ static Wt load(const uint8_t* W, size_t nsb, size_t sbi, int g) {
+    Wt w;
+#pragma unroll
+    for (int p = 0; p < 4; ++p) w.c[p] = *reinterpret_cast<const uint4*>(W + sbi * 128 + 16 * (2 * p + g));
+    w.h = *reinterpret_cast<const uint4*>(W + align256(nsb * 128) + sbi * 16);
+    return w;
+  }
+  // MFMA 2p+s: lane half g holds sub-block 2p+g, nibble s (elements 64p+32g+16s .. +15).
+  __device__ static void mac(const Wt& w, int g, const uint8_t* qrow, const v4i abs, double dxv[16],
+                             double acc[16]) {
+    const uint64_t lo = (uint64_t)w.h.y | ((uint64_t)w.h.z << 32);
+    const uint64_t hi = (uint64_t)w.h.z | ((uint64_t)w.h.w << 32);
+    v16i plo = {0}, phi = {0};
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const uint32_t sc = (uint32_t)(lo >> (6 * (2 * p + g))) & 63;
+      const uint32_t c[4] = {w.c[p].x, w.c[p].y, w.c[p].z, w.c[p].w};
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        v4i bl, bh;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const uint32_t q = (c[i] >> (4 * s)) & 0x0F0F0F0Fu;
+          bl[i] = (int)bytes_times(q, sc & 7);
+          bh[i] = (int)bytes_times(q, sc >> 3);
+        }
+        const v4i a = lds_v4(qrow + 64 * p + 32 * g + 16 * s);
+        plo = mfma_k32(a, bl, plo);
+        phi = mfma_k32(a, bh, phi);
+      }
+    }
+    // min term: bytes m_0..m_7 of this row against the split block sums
+    uint32_t m0 = 0, m1 = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      m0 |= (uint32_t)((hi >> (16 + 6 * j)) & 63) << (8 * j);
+      m1 |= (uint32_t)((hi >> (16 + 6 * (j + 4))) & 63) << (8 * j);
+    }
+    const v4i bm = {(int)m0, (int)m1, 0, 0}, zero = {0, 0, 0, 0};
+    const v16i z16 = {0};
+    const v16i xl = mfma_k32(abs, g == 0 ? bm : zero, z16);
+    const v16i xh = mfma_k32(abs, g == 1 ? bm : zero, z16);
+    const double d = half_bits_to_float(w.h.x & 0xFFFF), dmin = half_bits_to_float(w.h.x >> 16);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int s1 = plo[r] + 8 * phi[r];
+      const int s2 = xl[r] + 64 * xh[r];
+      acc[r] += dxv[r] * (d * (double)s1 - dmin * (double)s2);
+    }
+  }
+};
+
+template <> struct Mf<FQ2K> {
+  static constexpr bool kLateSecond = false;
+  static constexpr int NBSP = 16;  // one sum per 16-sub-block: bsums[j]
+  struct Wt { uint4 c[4]; uint4 sm; uint32_t dd; };
+  __device__ static Wt load(const uint8_t* W, size_t nsb, size_t sbi, int) {
+    Wt w;
+    const uint8_t* ps = W + align256(nsb * 64);
+    const uint8_t* pd = ps + align256(nsb * 16);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) w.c[c] = *reinterpret_cast<const uint4*>(W + sbi * 64 + 16 * c);
+    w.sm = *reinterpret_cast<const uint4*>(ps + sbi * 16);
+    w.dd = ld_u32(pd + sbi * 4);
+    return w;
+  }
+  // MFMA p: lane half g holds sub-block 2p+g (elements 32p+16g .. +15).
+  __device__ static void mac(const Wt& w, int g, const uint8_t* qrow, const v4i abs, double dxv[16],
+                             double acc[16]) {
+    const uint32_t sm[4] = {w.sm.x, w.sm.y, w.sm.z, w.sm.w};
+    v16i P = {0};
+#pragma unroll
+    for (int p = 0; p < 8; ++p) {
+      const int j = 2 * p + g, cc = j >> 2, s = j & 3;
+      const uint32_t sc = (sm[j >> 2] >> (8 * (j & 3))) & 15;
+      const uint32_t c[4] = {w.c[cc].x, w.c[cc].y, w.c[cc].z, w.c[cc].w};
+      v4i b;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) b[i] = (int)bytes_times((c[i] >> (2 * s)) & 0x03030303u, sc);
+      P = mfma_k32(lds_v4(qrow + 32 * p + 16 * g), b, P);
+    }
+    v4i bm;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) bm[i] = (int)((sm[i] >> 4) & 0x0F0F0F0Fu);
+    const v4i zero = {0, 0, 0, 0};
+    const v16i z16 = {0};
+    const v16i xl = mfma_k32(abs, g == 0 ? bm : zero, z16);
+    const v16i xh = mfma_k32(abs, g == 1 ? bm : zero, z16);
+    const double d = half_bits_to_float(w.dd & 0xFFFF), dmin = half_bits_to_float(w.dd >> 16);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int s2 = xl[r] + 64 * xh[r];
+      acc[r] += dxv[r] * (d * (double)P[r] - dmin * (double)s2);
+    }
+  }
+};
+
+template <> struct Mf<FQ6K> {
+  static constexpr int NBSP = 16;
+  static constexpr bool kLateSecond = true;   // register budget: load up after the gate MACs
+  struct Wt { uint2 l[8]; uint4 x[4]; uint4 sc; uint32_t d; };
+  // Lane half g needs words 2g, 2g+1 of every low-nibble chunk and all of the
+  // high-pair row.
+  __device__ static Wt load(const uint8_t* W, size_t nsb, size_t sbi, int g) {
+    Wt w;
+    const uint8_t* px = W + align256(nsb * 128);
+    const uint8_t* ps = px + align256(nsb * 64);
+    const uint8_t* pd = ps + align256(nsb * 16);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) w.l[j] = *reinterpret_cast<const uint2*>(W + sbi * 128 + 16 * j + 8 * g);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) w.x[j] = *reinterpret_cast<const uint4*>(px + sbi * 64 + 16 * j);
+    w.sc = *reinterpret_cast<const uint4*>(ps + sbi * 16);
+    w.d = ld_u16(pd + sbi * 2);
+    return w;
+  }
+  // One 16-deep MFMA per sub-block jj: lane half g holds elements 16jj+8g .. +7
+  // (low nibbles: word i = 2g+t of chunk jj/2, nibble jj%2; high pairs: word
+  // jj%2 of chunk jj/2 in the high-pair plane, bits 2i).
+  __device__ static void mac(const Wt& w, int g, const uint8_t* qrow, const v4i abs, double dxv[16],
+                             double acc[16]) {
+    const uint32_t scw[4] = {w.sc.x, w.sc.y, w.sc.z, w.sc.w};
+    int S1[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) S1[r] = 0;
+    const v16i z16 = {0};
+#pragma unroll
+    for (int jj = 0; jj < 16; ++jj) {
+      const int j = jj >> 1, s = jj & 1;
+      const uint32_t l2[2] = {w.l[j].x, w.l[j].y};
+      const uint4 xv = w.x[j >> 1];
+      const uint32_t xs = (j & 1) ? (s ? xv.w : xv.z) : (s ? xv.y : xv.x);
+      uint32_t q[2];
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const int i = 2 * g + t;
+        q[t] = ((l2[t] >> (4 * s)) & 0x0F0F0F0Fu) | (((xs >> (2 * i)) & 0x03030303u) << 4);
+      }
+      const long b = (long)(((uint64_t)q[1] << 32) | q[0]);
+      const long a = *reinterpret_cast<const long*>(qrow + 16 * jj + 8 * g);
+      const v16i P = mfma_k16(a, b, z16);
+      const int sc = (int)(int8_t)((scw[jj >> 2] >> (8 * (jj & 3))) & 0xFF);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) S1[r] += __mul24(sc, P[r]);   // |P| < 2^17: 24-bit multiply is exact
+      __builtin_amdgcn_sched_barrier(0);   // keep one sub-block's results live at a time
+    }
+    const v4i bm = {(int)scw[0], (int)scw[1], (int)scw[2], (int)scw[3]}, zero = {0, 0, 0, 0};
+    const v16i xl = mfma_k32(abs, g == 0 ? bm : zero, z16);
+    const v16i xh = mfma_k32(abs, g == 1 ? bm : zero, z16);
+    const double d = half_bits_to_float(w.d);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int s1 = S1[r] - 32 * (xl[r] + 64 * xh[r]);
+      acc[r] += dxv[r] * (d * (double)s1);
+    }
+  }
+};
+
+template <> struct Mf<FQ80> {
+  static constexpr bool kLateSecond = false;
+  static constexpr int NBSP = 0;
+  struct Wt { uint4 q[8]; uint4 d; };
+  __device__ static Wt load(const uint8_t* W, size_t nsb, size_t sbi, int g) {
+    Wt w;
+#pragma unroll
+    for (int b = 0; b < 8; ++b) w.q[b] = *reinterpret_cast<const uint4*>(W + sbi * 256 + 32 * b + 16 * g);
+    w.d = *reinterpret_cast<const uint4*>(W + align256(nsb * 256) + sbi * 16);
+    return w;
+  }
+  __device__ static void mac(const Wt& w, int g, const uint8_t* qrow, const v4i, double dxv[16],
+                             double acc[16]) {
+    const uint32_t dw[4] = {w.d.x, w.d.y, w.d.z, w.d.w};
+    double inner[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) inner[r] = 0.0;
+    const v16i z16 = {0};
+#pragma unroll
+    for (int b = 0; b < 8; ++b) {
+      const v4i bq = {(int)w.q[b].x, (int)w.q[b].y, (int)w.q[b].z, (int)w.q[b].w};
+      const v16i P = mfma_k32(lds_v4(qrow + 32 * b + 16 * g), bq, z16);
+      const double db = half_bits_to_float(dw[b >> 1] >> (16 * (b & 1)));
+#pragma unroll
+      for (int r = 0; r < 16; ++r) inner[r] += db * (double)P[r];
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[r] += dxv[r] * inner[r];
+  }
+};
+
+// ------------------------------------------------------------ staging
+
+// Stage 256-block sb of the tile's activation rows: thread (m, piece) copies
+// 16 quant bytes; piece 0 also the scale, piece 1 the split block sums.
+template <int NBSP>
+__device__ __forceinline__ void stage_block(StageLds& L, const uint8_t* srow, int sb, int m, int piece) {
+  const uint8_t* blk = srow != nullptr ? srow + (size_t)sb * kQ8KBytes : nullptr;
+  uint4 v = make_uint4(0u, 0u, 0u, 0u);
+  if (blk != nullptr) {
+    const uint8_t* p = blk + 4 + 16 * piece;
+    v = make_uint4(ld_u32(p), ld_u32(p + 4), ld_u32(p + 8), ld_u32(p + 12));
+  }
+  *reinterpret_cast<uint4*>(&L.qs[m][16 * piece]) = v;
+  if (piece == 0) L.dx[m] = blk != nullptr ? *reinterpret_cast<const float*>(blk) : 0.0f;
+  if (NBSP > 0 && piece == 1) {
+    int bs[16];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const uint32_t wv = blk != nullptr ? ld_u32(blk + 260 + 4 * i) : 0u;
+      bs[2 * i] = (int)(int16_t)(wv & 0xFFFF);
+      bs[2 * i + 1] = (int)(int16_t)(wv >> 16);
+    }
+    uint32_t lo[4] = {0, 0, 0, 0}, hi[4] = {0, 0, 0, 0};
+#pragma unroll
+    for (int j = 0; j < NBSP; ++j) {
+      const int s = NBSP == 8 ? bs[2 * j] + bs[2 * j + 1] : bs[j];
+      lo[j >> 2] |= (uint32_t)(s & 63) << (8 * (j & 3));
+      hi[j >> 2] |= (uint32_t)((s >> 6) & 255) << (8 * (j & 3));
+    }
+    *reinterpret_cast<uint4*>(&L.bsp[m][0][0]) = make_uint4(lo[0], lo[1], lo[2], lo[3]);
+    *reinterpret_cast<uint4*>(&L.bsp[m][1][0]) = make_uint4(hi[0], hi[1], hi[2], hi[3]);
+  }
+}
+
+// q8_K of one 256-wide fp32 row held in LDS, by one wave (4 values per lane),
+// identical to the definition (amax; id = 127/amax correctly rounded;
+// q = rint(h*id) clamped; d = amax/127; per-16 sums; amax == 0 or an infinite
+// id gives a zero block).
+__device__ __forceinline__ void quantize_row_lds(const float* hrow, uint8_t* __restrict__ o) {
+  const int lane = lane_id();
+  const float4 v = *reinterpret_cast<const float4*>(hrow + 4 * lane);
+  float amax = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
+  amax = wave_max_f(amax);
+  const float id = amax == 0.0f ? 0.0f : __fdiv_rn(127.0f, amax);
+  const bool zero = amax == 0.0f || __builtin_isinf(id);
+  int q0 = 0, q1 = 0, q2 = 0, q3 = 0;
+  if (!zero) { q0 = q8_code(v.x, id); q1 = q8_code(v.y, id); q2 = q8_code(v.z, id); q3 = q8_code(v.w, id); }
+  *reinterpret_cast<uint32_t*>(o + 4 + 4 * lane) =
+      (uint32_t)(q0 & 255) | ((uint32_t)(q1 & 255) << 8) | ((uint32_t)(q2 & 255) << 16) | ((uint32_t)(q3 & 255) << 24);
+  int s = q0 + q1 + q2 + q3;
+  s += dpp_all_i<kDppXor1>(s);
+  s += dpp_all_i<kDppXor2>(s);
+  if ((lane & 3) == 0) *reinterpret_cast<int16_t*>(o + 260 + 2 * (lane >> 2)) = (int16_t)s;
+  if (lane == 0) *reinterpret_cast<float*>(o) = zero ? 0.0f : __fdiv_rn(amax, 127.0f);
+}
+
+// ------------------------------------------------------------ the kernel
+//
+// MODE 0 (gate/up): A = q8_K(x) rows of the tile's tokens, W0 = gate, W1 = up;
+//   epilogue h = fl32(silu(g) u) into LDS, then q8_K(h) of the 256-wide block
+//   (one q8_K block per tile row) into hq.
+// MODE 1 (down): A = q8_K(h) rows of the tile's pairs, W0 = down; epilogue
+//   yp[row] = fl32(gate weight * y).
+template <int FMT, int MODE>
+__global__ __launch_bounds__(512) void k_mfma(MfmaArgs a) {
+  using M = Mf<FMT>;
+  __shared__ StageLds L;
+  __shared__ int64_t orow[kTileT];
+  __shared__ double owt[kTileT];
+
+  // ---- tile: expert (or the shared expert) and its rows t0 .. t0+n-1
+  int e = -1, t0, n;
+  int64_t list_off = 0;
+  if (a.shared) {
+    t0 = (int)blockIdx.x * kTileT;
+    if (t0 >= a.T) return;
+    n = (int)((a.T - t0) < kTileT ? (a.T - t0) : kTileT);
+  } else {
+    if ((int)blockIdx.x >= *a.count) return;
+    const int4 tl = a.tiles[blockIdx.x];
+    e = tl.x; t0 = tl.y; n = tl.z; list_off = tl.w;
+  }
+  const uint8_t *W0, *W1 = nullptr;
+  if (a.shared) {
+    W0 = a.sh_w0;
+    W1 = a.sh_w1;
+  } else {
+    const void *pg = a.gate[e], *pu = a.up[e], *pd = a.down[e];
+    const bool resident = pg != nullptr && pu != nullptr && pd != nullptr;
+    W0 = (const uint8_t*)(MODE == 0 ? pg : pd);
+    W1 = (const uint8_t*)pu;
+    if (!resident) {
+      // not resident: its pairs add exactly nothing (their down rows are zero)
+      if (MODE == 1) {
+        for (int i = threadIdx.x; i < n * kMfRows; i += blockDim.x) {
+          const int p = a.pairs[list_off + t0 + i / kMfRows];
+          a.yp[(int64_t)p * a.N + (int64_t)blockIdx.y * kMfRows + i % kMfRows] = 0.0f;
+        }
+      }
+      return;
+    }
+  }
+
+  // ---- per-row bookkeeping and the staging thread's source row
+  const int tid = threadIdx.x, wave = tid >> 6, lane = lane_id(), g = lane >> 5;
+  const int ms = tid >> 4, piece = tid & 15;
+  const uint8_t* srow = nullptr;
+  if (ms < n) {
+    int64_t ridx;
+    if (a.shared) {
+      ridx = t0 + ms;
+    } else {
+      const int p = a.pairs[list_off + t0 + ms];
+      ridx = MODE == 0 ? p / a.k : p;
+    }
+    srow = a.src + ridx * a.src_stride;
+  }
+  if (tid < kTileT) {
+    int64_t orr = -1;
+    double wt = 0.0;
+    if (tid < n) {
+      if (a.shared) {
+        orr = MODE == 0 ? (int64_t)(t0 + tid) : a.T * a.k + t0 + tid;
+        wt = a.shared_scale != nullptr ? (double)a.shared_scale[t0 + tid] : 1.0;
+      } else {
+        const int p = a.pairs[list_off + t0 + tid];
+        orr = p;
+        wt = MODE == 1 ? (double)a.topk_w[p] : 0.0;
+      }
+    }
+    orow[tid] = orr;
+    owt[tid] = wt;
+  }
+
+  // ---- main loop over the 256-blocks of K
+  const int64_t nbK = a.K / 256, nsb = a.N * nbK;
+  const int64_t wrow = (int64_t)blockIdx.y * kMfRows + wave * 32 + (lane & 31);
+  double acc0[16], acc1[16];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) { acc0[r] = 0.0; acc1[r] = 0.0; }
+  const uint8_t* qrow = &L.qs[lane & 31][0];
+  for (int64_t sb = 0; sb < nbK; ++sb) {
+    const size_t sbi = (size_t)(wrow * nbK + sb);
+    typename M::Wt w0 = M::load(W0, (size_t)nsb, sbi, g);
+    typename M::Wt w1;
+    if constexpr (MODE == 0 && !M::kLateSecond) w1 = M::load(W1, (size_t)nsb, sbi, g);
+    __syncthreads();                     // the previous block's LDS reads are done
+    stage_block<M::NBSP>(L, srow, (int)sb, ms, piece);
+    __syncthreads();
+    double dxv[16];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float4 f = *reinterpret_cast<const float4*>(&L.dx[8 * q + 4 * g]);
+      dxv[4 * q] = f.x; dxv[4 * q + 1] = f.y; dxv[4 * q + 2] = f.z; dxv[4 * q + 3] = f.w;
+    }
+    v4i abs = {0, 0, 0, 0};
+    if constexpr (M::NBSP > 0) abs = lds_v4(&L.bsp[lane & 31][g][0]);
+    M::mac(w0, g, qrow, abs, dxv, acc0);
+    if constexpr (MODE == 0) {
+      if constexpr (M::kLateSecond) w1 = M::load(W1, (size_t)nsb, sbi, g);
+      M::mac(w1, g, qrow, abs, dxv, acc1);
+    }
+  }
+
+  if constexpr (MODE == 0) {
+    // h = fl32(silu(g) u) -> LDS, then q8_K per tile row over these 256 columns
+    __shared__ float hs[kTileT][kMfRows + 4];
+    const int col = wave * 32 + (lane & 31);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) hs[out_row(r, g)][col] = (float)(silu64(acc0[r]) * acc1[r]);
+    __syncthreads();
+    for (int m = wave; m < n; m += kMfWaves)
+      quantize_row_lds(&hs[m][0], a.hq + orow[m] * a.hq_stride + (int64_t)blockIdx.y * kQ8KBytes);
+  } else {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int m = out_row(r, g);
+      if (m < n) a.yp[orow[m] * a.N + wrow] = (float)(owt[m] * acc0[r]);
+    }
+  }
+}
+
+// Tile list of the routed experts whose row count exceeds `thr`: (expert, first
+// row, rows, list offset), 32 rows per tile, experts in union order (absent
+// experts too: their down tiles write zero rows).  One workgroup; count =
+// number of tiles.
+__global__ __launch_bounds__(1024) void k_mfma_plan(const int32_t* __restrict__ active,
+                                                    const int32_t* __restrict__ offsets, int thr, int max_tiles,
+                                                    int4* __restrict__ tiles, int32_t* __restrict__ count) {
+  __shared__ int part[1024];
+  const int na = active[0];
+  const int per = (na + 1023) / 1024;
+  const int s0 = threadIdx.x * per;
+  int local = 0;
+  for (int i = 0; i < per; ++i) {
+    const int s = s0 + i;
+    if (s < na) {
+      const int e = active[1 + s];
+      const int ne = offsets[e + 1] - offsets[e];
+      if (ne > thr) local += (ne + kTileT - 1) / kTileT;
+    }
+  }
+  part[threadIdx.x] = local;
+  __syncthreads();
+  for (int o = 1; o < 1024; o <<= 1) {   // inclusive scan (Hillis-Steele)
+    const int v = threadIdx.x >= o ? part[threadIdx.x - o] : 0;
+    __syncthreads();
+    part[threadIdx.x] += v;
+    __syncthreads();
+  }
+  int base = part[threadIdx.x] - local;
+  if (threadIdx.x == 1023) *count = part[1023] < max_tiles ? part[1023] : max_tiles;
+  for (int i = 0; i < per; ++i) {
+    const int s = s0 + i;
+    if (s < na) {
+      const int e = active[1 + s];
+      const int ne = offsets[e + 1] - offsets[e];
+      if (ne > thr) {
+        for (int t0 = 0; t0 < ne; t0 += kTileT) {
+          if (base < max_tiles) tiles[base] = make_int4(e, t0, ne - t0 < kTileT ? ne - t0 : kTileT, offsets[e]);
+          ++base;
+        }
+      }
+    }
+  }
+}
+
+int launch_mfma_plan(const int32_t* active, const int32_t* offsets, int thr, int max_tiles, int4* tiles,
+                     int32_t* count, hipStream_t s) {
+  hipLaunchKernelGGL(k_mfma_plan, dim3(1), dim3(1024), 0, s, active, offsets, thr, max_tiles, tiles, count);
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+int launch_mfma(int fmt, int mode, dim3 grid, const MfmaArgs& a, hipStream_t s) {
+  if (grid.x == 0 || grid.y == 0) return 0;
+#define MOEQ_MF(F)                                                                     \
+  if (mode == 0) hipLaunchKernelGGL((k_mfma<F, 0>), grid, dim3(512), 0, s, a);         \
+  else hipLaunchKernelGGL((k_mfma<F, 1>), grid, dim3(512), 0, s, a);
+  switch (fmt) {
+    case FQ4K: MOEQ_MF(FQ4K) break;
+    case FQ6K: MOEQ_MF(FQ6K) break;
+    case FQ2K: MOEQ_MF(FQ2K) break;
+    case FQ80: MOEQ_MF(FQ80) break;
+    default: return -2;
+  }
+#undef MOEQ_MF
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+}  // namespace moeq

@@ -34,6 +34,7 @@ struct GateUpArgs {
   float* hbuf;                  // fp32 [T*k + T, hstride]
   int64_t hstride;
   int lpr, cpr, steps;
+  int gemv_max;                 // experts with more rows than this go to the MFMA path
   // one token (k_gateup1)
   const int32_t* topk_ids;      // rank-ordered experts (when not routing inline)
   const double* logits;         // [E] logits to route inline from, or null
@@ -69,14 +70,40 @@ struct DownArgs {
   int max_union;
   const float* hbuf;
   int64_t hstride;
-  double* yp;                   // fp64 [T*k + T, H] weighted per-pair outputs
+  float* yp;                    // fp32 [T*k + T, H] weighted per-pair outputs
   uint8_t* hq;                  // q8_K(h) rows of routed pairs [T*k], or null
   uint8_t* hq_sh;               // q8_K(h) rows of the shared expert [T], or null
   int64_t hq_stride;            // bytes per row for this launch's F
   int lpr, cpr, steps, rb;      // rb = rows per work item = 4 * steps * (64 / lpr)
+  int gemv_max;                 // experts with more rows than this go to the MFMA path
   int has_shared;
   float* y;
   int accumulate;
+};
+
+// int8 MFMA grouped GEMM (experts with more than gemv_max rows).  Tiles of 32
+// activation rows come from the plan (routed experts) or cover all T tokens
+// (shared expert).
+struct MfmaArgs {
+  int shared;
+  const int4* tiles;            // routed: (expert, first row, rows, list offset)
+  const int32_t* count;         // routed: number of tiles
+  const void* const* gate;      // routed expert tables (an expert is resident only if
+  const void* const* up;        // all three of its matrices are present)
+  const void* const* down;
+  const uint8_t* sh_w0;         // shared: gate (mode 0) or down (mode 1)
+  const uint8_t* sh_w1;         // shared: up (mode 0)
+  const int32_t* pairs;
+  int k;
+  int64_t T;
+  int64_t N, K;                 // weight rows and columns of this launch's matrices
+  const uint8_t* src;           // q8_K rows: x by token (mode 0), h by pair row (mode 1)
+  int64_t src_stride;
+  uint8_t* hq;                  // mode 0: q8_K(h) rows out
+  int64_t hq_stride;
+  const float* topk_w;
+  const float* shared_scale;
+  float* yp;                    // mode 1: fp32 [T*k + T, H]
 };
 
 int launch_quantize_q8K(const float* x, int64_t rows, int64_t cols, void* out, hipStream_t s);
@@ -94,7 +121,10 @@ int launch_gateup(int fmt, int tt, int cpl, dim3 grid, const GateUpArgs& a, hipS
 int launch_gateup1(int fmt, int nper, int cpl, dim3 grid, const GateUpArgs& a, hipStream_t s);
 int launch_down(int fmt, int tt, int cpl, dim3 grid, const DownArgs& a, hipStream_t s);
 int launch_down_rows1(int fmt, int cpl, dim3 grid, const DownArgs& a, hipStream_t s);
-int launch_combine(const double* yp, int64_t T, int64_t H, int k, int has_shared, float* y, int accumulate,
+int launch_mfma_plan(const int32_t* active, const int32_t* offsets, int thr, int max_tiles, int4* tiles,
+                     int32_t* count, hipStream_t s);
+int launch_mfma(int fmt, int mode, dim3 grid, const MfmaArgs& a, hipStream_t s);
+int launch_combine(const float* yp, int64_t T, int64_t H, int k, int has_shared, float* y, int accumulate,
                    hipStream_t s);
 
 }  // namespace moeq

@@ -165,13 +165,17 @@ def check_route(run, layer, sel):
     return ids, w
 
 
+PATHS = {"gemv": moeq.PATH_GEMV, "mfma": moeq.PATH_MFMA, "auto": moeq.PATH_AUTO}
+
+
+@pytest.mark.parametrize("path", ["gemv", "mfma", "auto"])
 @pytest.mark.parametrize("fused", [False, True], ids=["calls", "layer"])
 @pytest.mark.parametrize("name", syn.CONFIG_ORDER)
-def test_layer_parity(name, fused):
+def test_layer_parity(name, fused, path):
     layer = layer_of(name)
     cfg = layer.cfg
-    say("layer", name, "fused" if fused else "calls", cfg)
-    run = GpuRun(layer, path=moeq.PATH_GEMV, fused=fused)
+    say("layer", name, "fused" if fused else "calls", path, cfg)
+    run = GpuRun(layer, path=PATHS[path], fused=fused)
     sel = sample_tokens(cfg.T, 24)
     ids, w = check_route(run, layer, sel)
     full_ids = run.ids.copy()
@@ -201,22 +205,45 @@ def test_auto_equals_gemv_and_is_deterministic():
     assert np.array_equal(a.ids, b.ids) and np.array_equal(a.pairs, b.pairs)
 
 
+@pytest.mark.parametrize("name", ["chunk16", "prefill"])
+def test_mfma_and_gemv_agree_on_every_pair(name):
+    """At full size the oracle checks sampled tokens; here the two device paths
+    (independent integer schemes) must give the same q8_K(h) bytes for every
+    pair and agree on y everywhere, and the MFMA path must be deterministic."""
+    layer = layer_of(name)
+    cfg = layer.cfg
+    say("mfma vs gemv every pair", name)
+    a = GpuRun(layer, path=moeq.PATH_MFMA)
+    b = GpuRun(layer, path=moeq.PATH_GEMV)
+    assert np.array_equal(a.ids, b.ids) and np.array_equal(a.pairs, b.pairs)
+    nbF = cfg.F // 256 * 292
+    assert np.array_equal(a.hq_r[:, :nbF], b.hq_r[:, :nbF])
+    if cfg.shared:
+        nbs = cfg.F_shared // 256 * 292
+        assert np.array_equal(a.hq_s[:, :nbs], b.hq_s[:, :nbs])
+    check_y(a.yv, b.yv, name)
+    c = GpuRun(layer, path=moeq.PATH_MFMA)
+    assert np.array_equal(a.yv, c.yv) and np.array_equal(a.hq_r, c.hq_r)
+
+
 # ---------------------------------------------------------------- FFN semantics
 
-def test_null_partition_sums_to_full():
-    layer = layer_of("decode")
+@pytest.mark.parametrize("name,path", [("decode", "auto"), ("chunk16", "mfma"), ("verify", "gemv")])
+def test_null_partition_sums_to_full(name, path):
+    layer = layer_of(name)
     cfg = layer.cfg
-    say("null partition decode")
-    full = GpuRun(layer)
+    say("null partition", name, path)
+    full = GpuRun(layer, path=PATHS[path])
     lo = [e < cfg.E // 2 for e in range(cfg.E)]
-    a = GpuRun(layer, present=lo)
+    a = GpuRun(layer, present=lo, path=PATHS[path])
     hi_layer = syn.LayerData(cfg=cfg, x=layer.x, w_router=layer.w_router, bias=layer.bias, gate=layer.gate,
                              up=layer.up, down=layer.down)                  # no shared expert in this half
-    b = GpuRun(hi_layer, present=[not v for v in lo])
+    b = GpuRun(hi_layer, present=[not v for v in lo], path=PATHS[path])
     s = a.yv.astype(np.float64) + b.yv.astype(np.float64)
     check_y(s, full.yv, "partition")
-    ro = oracle.expert_ffn(layer, full.ids, full.w, [0], present=lo)
-    check_y(a.yv, ro.y, "half")
+    sel = sample_tokens(cfg.T, 6)
+    ro = oracle.expert_ffn(layer, full.ids, full.w, sel, present=lo)
+    check_y(a.yv[sel], ro.y, "half")
 
 
 def test_accumulate_and_shared_scale():
@@ -247,12 +274,14 @@ def _custom_cfg(**kw):
     return syn.LayerConfig(**base)
 
 
+@pytest.mark.parametrize("path", ["gemv", "mfma"])
 @pytest.mark.parametrize("fused", [False, True], ids=["calls", "layer"])
 @pytest.mark.parametrize("variant", ["one_expert_all_tokens", "k_equals_E", "k1", "ties", "softmax_all",
                                      "sigmoid", "q2k_q6k_q80_mix", "t1_mixed_shared", "t1_k32", "t1_ties",
-                                     "t1_softmax_all", "t1_sigmoid_e600"])
-def test_edge_layers(variant, fused):
-    say("edge", variant, fused)
+                                     "t1_softmax_all", "t1_sigmoid_e600", "ragged_tiles_q4k",
+                                     "ragged_tiles_q2k_q6k_shared_q80", "ragged_tiles_q8_q4"])
+def test_edge_layers(variant, fused, path):
+    say("edge", variant, fused, path)
     kw = {}
     if variant == "k_equals_E":
         kw = dict(E=4, k=4)
@@ -276,6 +305,16 @@ def test_edge_layers(variant, fused):
         kw = dict(T=1, gating=syn.SOFTMAX_ALL, E=40, k=5)
     elif variant == "t1_sigmoid_e600":
         kw = dict(T=1, gating=syn.SIGMOID_TOPK, E=600, k=6)
+    elif variant == "ragged_tiles_q4k":
+        # about 47 tokens per expert: two 32-row tiles each, the second ragged
+        kw = dict(T=70, E=3, k=2, F=512, H=768, shared=True, F_shared=256, sh_fmt_gate=syn.Q4_K,
+                  sh_fmt_up=syn.Q4_K, sh_fmt_down=syn.Q4_K)
+    elif variant == "ragged_tiles_q2k_q6k_shared_q80":
+        kw = dict(T=45, E=5, k=3, F=512, H=512, fmt_gate=syn.Q2_K, fmt_up=syn.Q2_K, fmt_down=syn.Q6_K,
+                  shared=True, F_shared=768, sh_fmt_gate=syn.Q8_0, sh_fmt_up=syn.Q8_0, sh_fmt_down=syn.Q8_0)
+    elif variant == "ragged_tiles_q8_q4":
+        kw = dict(T=33, E=4, k=2, F=256, H=1024, fmt_gate=syn.Q8_0, fmt_up=syn.Q8_0, fmt_down=syn.Q4_K,
+                  gating=syn.SIGMOID_TOPK)
     cfg = _custom_cfg(**kw)
     layer = syn.gen_layer(cfg)
     if variant == "t1_ties":
@@ -294,7 +333,7 @@ def test_edge_layers(variant, fused):
         cfg = _custom_cfg(E=3, k=2, T=4)
         layer = syn.gen_layer(cfg)
         layer.w_router[2] = layer.w_router[0]                  # exact ties between experts 0 and 2
-    run = GpuRun(layer, path=moeq.PATH_GEMV, fused=fused)
+    run = GpuRun(layer, path=PATHS[path], fused=fused)
     sel = list(range(cfg.T))
     ids, w = check_route(run, layer, sel)
     if variant == "t1_ties":
@@ -310,6 +349,9 @@ def test_edge_layers(variant, fused):
     for t in sel:
         for s in range(cfg.k):
             assert np.array_equal(run.hq_r[t * cfg.k + s, :nbF], r.hq[t, s, :nbF])
+        if cfg.shared:
+            nbs = cfg.F_shared // 256 * 292
+            assert np.array_equal(run.hq_s[t, :nbs], r.hq[t, cfg.k, :nbs]), (variant, t, "shared")
 
 
 def test_empty_batch():
