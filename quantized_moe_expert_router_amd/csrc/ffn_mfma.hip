@@ -74,6 +74,22 @@ __device__ __forceinline__ v4i lds_v4(const uint8_t* p) { return *reinterpret_ca
 // Token row m of the lane's results for value r.
 __device__ __forceinline__ int out_row(int r, int g) { return 8 * (r >> 2) + 4 * g + (r & 3); }
 
+// fp64 combine over the lane's 16 results: value r = 4q+i is tile row
+// 8q + 4g + i, whose scale is dxs[8q+4g+i]; groups of 4 rows past the tile's
+// n rows are skipped (uniform over the wave).
+#define MOEQ_COMBINE(STMT)                                                            \
+  _Pragma("unroll") for (int q = 0; q < 4; ++q) {                                    \
+    if (8 * q < n) {                                                                  \
+      const float4 dx4 = *reinterpret_cast<const float4*>(dxs + 8 * q + 4 * g);       \
+      const float dxa[4] = {dx4.x, dx4.y, dx4.z, dx4.w};                             \
+      _Pragma("unroll") for (int i = 0; i < 4; ++i) {                                \
+        const int r = 4 * q + i;                                                      \
+        const double dx = (double)dxa[i];                                             \
+        STMT;                                                                         \
+      }                                                                               \
+    }                                                                                 \
+  }
+
 // ------------------------------------------------------------ per-format W side
 //
 // A trait per weight format:
@@ -85,7 +101,6 @@ __device__ __forceinline__ int out_row(int r, int g) { return 8 * (r >> 2) + 4 *
 template <int FMT> struct Mf;
 
 template <> struct Mf<FQ4K> {
-  static constexpr bool kLateSecond = false;
   static constexpr int NBSP = 8;   // one sum per 32-sub-block: bsums[2j] + bsums[2j+1]
   struct Wt { uint4 c[4]; uint4 h; };
   __device__ static Wt load(const uint8_t* W, size_t nsb, size_t sbi, int g) {
@@ -96,7 +111,7 @@ template <> struct Mf<FQ4K> {
     return w;
   }
   // MFMA 2p+s: lane half g holds sub-block 2p+g, nibble s (elements 64p+32g+16s .. +15).
-  __device__ static void mac(const Wt& w, int g, const uint8_t* qrow, const v4i abs, double dxv[16],
+  __device__ static void mac(const Wt& w, int g, const uint8_t* qrow, const v4i abs, const float* dxs, int n,
                              double acc[16]) {
     const uint64_t lo = (uint64_t)w.h.y | ((uint64_t)w.h.z << 32);
     const uint64_t hi = (uint64_t)w.h.z | ((uint64_t)w.h.w << 32);
@@ -131,17 +146,11 @@ template <> struct Mf<FQ4K> {
     const v16i xl = mfma_k32(abs, g == 0 ? bm : zero, z16);
     const v16i xh = mfma_k32(abs, g == 1 ? bm : zero, z16);
     const double d = half_bits_to_float(w.h.x & 0xFFFF), dmin = half_bits_to_float(w.h.x >> 16);
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int s1 = plo[r] + 8 * phi[r];
-      const int s2 = xl[r] + 64 * xh[r];
-      acc[r] += dxv[r] * (d * (double)s1 - dmin * (double)s2);
-    }
+    MOEQ_COMBINE(acc[r] += dx * (d * (double)(plo[r] + 8 * phi[r]) - dmin * (double)(xl[r] + 64 * xh[r])))
   }
 };
 
 template <> struct Mf<FQ2K> {
-  static constexpr bool kLateSecond = false;
   static constexpr int NBSP = 16;  // one sum per 16-sub-block: bsums[j]
   struct Wt { uint4 c[4]; uint4 sm; uint32_t dd; };
   __device__ static Wt load(const uint8_t* W, size_t nsb, size_t sbi, int) {
@@ -155,7 +164,7 @@ template <> struct Mf<FQ2K> {
     return w;
   }
   // MFMA p: lane half g holds sub-block 2p+g (elements 32p+16g .. +15).
-  __device__ static void mac(const Wt& w, int g, const uint8_t* qrow, const v4i abs, double dxv[16],
+  __device__ static void mac(const Wt& w, int g, const uint8_t* qrow, const v4i abs, const float* dxs, int n,
                              double acc[16]) {
     const uint32_t sm[4] = {w.sm.x, w.sm.y, w.sm.z, w.sm.w};
     v16i P = {0};
@@ -177,17 +186,12 @@ template <> struct Mf<FQ2K> {
     const v16i xl = mfma_k32(abs, g == 0 ? bm : zero, z16);
     const v16i xh = mfma_k32(abs, g == 1 ? bm : zero, z16);
     const double d = half_bits_to_float(w.dd & 0xFFFF), dmin = half_bits_to_float(w.dd >> 16);
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int s2 = xl[r] + 64 * xh[r];
-      acc[r] += dxv[r] * (d * (double)P[r] - dmin * (double)s2);
-    }
+    MOEQ_COMBINE(acc[r] += dx * (d * (double)P[r] - dmin * (double)(xl[r] + 64 * xh[r])))
   }
 };
 
 template <> struct Mf<FQ6K> {
   static constexpr int NBSP = 16;
-  static constexpr bool kLateSecond = true;   // register budget: load up after the gate MACs
   struct Wt { uint2 l[8]; uint4 x[4]; uint4 sc; uint32_t d; };
   // Lane half g needs words 2g, 2g+1 of every low-nibble chunk and all of the
   // high-pair row.
@@ -207,7 +211,7 @@ template <> struct Mf<FQ6K> {
   // One 16-deep MFMA per sub-block jj: lane half g holds elements 16jj+8g .. +7
   // (low nibbles: word i = 2g+t of chunk jj/2, nibble jj%2; high pairs: word
   // jj%2 of chunk jj/2 in the high-pair plane, bits 2i).
-  __device__ static void mac(const Wt& w, int g, const uint8_t* qrow, const v4i abs, double dxv[16],
+  __device__ static void mac(const Wt& w, int g, const uint8_t* qrow, const v4i abs, const float* dxs, int n,
                              double acc[16]) {
     const uint32_t scw[4] = {w.sc.x, w.sc.y, w.sc.z, w.sc.w};
     int S1[16];
@@ -238,16 +242,11 @@ template <> struct Mf<FQ6K> {
     const v16i xl = mfma_k32(abs, g == 0 ? bm : zero, z16);
     const v16i xh = mfma_k32(abs, g == 1 ? bm : zero, z16);
     const double d = half_bits_to_float(w.d);
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int s1 = S1[r] - 32 * (xl[r] + 64 * xh[r]);
-      acc[r] += dxv[r] * (d * (double)s1);
-    }
+    MOEQ_COMBINE(acc[r] += dx * (d * (double)(S1[r] - 32 * (xl[r] + 64 * xh[r]))))
   }
 };
 
 template <> struct Mf<FQ80> {
-  static constexpr bool kLateSecond = false;
   static constexpr int NBSP = 0;
   struct Wt { uint4 q[8]; uint4 d; };
   __device__ static Wt load(const uint8_t* W, size_t nsb, size_t sbi, int g) {
@@ -257,54 +256,59 @@ template <> struct Mf<FQ80> {
     w.d = *reinterpret_cast<const uint4*>(W + align256(nsb * 256) + sbi * 16);
     return w;
   }
-  __device__ static void mac(const Wt& w, int g, const uint8_t* qrow, const v4i, double dxv[16],
+  __device__ static void mac(const Wt& w, int g, const uint8_t* qrow, const v4i, const float* dxs, int n,
                              double acc[16]) {
     const uint32_t dw[4] = {w.d.x, w.d.y, w.d.z, w.d.w};
-    double inner[16];
-#pragma unroll
-    for (int r = 0; r < 16; ++r) inner[r] = 0.0;
     const v16i z16 = {0};
 #pragma unroll
     for (int b = 0; b < 8; ++b) {
       const v4i bq = {(int)w.q[b].x, (int)w.q[b].y, (int)w.q[b].z, (int)w.q[b].w};
       const v16i P = mfma_k32(lds_v4(qrow + 32 * b + 16 * g), bq, z16);
       const double db = half_bits_to_float(dw[b >> 1] >> (16 * (b & 1)));
-#pragma unroll
-      for (int r = 0; r < 16; ++r) inner[r] += db * (double)P[r];
+      MOEQ_COMBINE(acc[r] += (dx * db) * (double)P[r])
     }
-#pragma unroll
-    for (int r = 0; r < 16; ++r) acc[r] += dxv[r] * inner[r];
   }
 };
 
 // ------------------------------------------------------------ staging
 
-// Stage 256-block sb of the tile's activation rows: thread (m, piece) copies
-// 16 quant bytes; piece 0 also the scale, piece 1 the split block sums.
+// Staging of 256-block sb of the tile's activation rows, in two halves so the
+// global loads of block sb+1 overlap the MFMAs of block sb: thread (m, piece)
+// loads 16 quant bytes (piece 0 also the scale, piece 1 the 16 block sums)
+// into registers, then writes them (and the split block sums) to LDS.
+struct StageRegs {
+  uint32_t q[4];
+  float d;
+  uint32_t bs[8];
+};
 template <int NBSP>
-__device__ __forceinline__ void stage_block(StageLds& L, const uint8_t* srow, int sb, int m, int piece) {
-  const uint8_t* blk = srow != nullptr ? srow + (size_t)sb * kQ8KBytes : nullptr;
-  uint4 v = make_uint4(0u, 0u, 0u, 0u);
-  if (blk != nullptr) {
-    const uint8_t* p = blk + 4 + 16 * piece;
-    v = make_uint4(ld_u32(p), ld_u32(p + 4), ld_u32(p + 8), ld_u32(p + 12));
-  }
-  *reinterpret_cast<uint4*>(&L.qs[m][16 * piece]) = v;
-  if (piece == 0) L.dx[m] = blk != nullptr ? *reinterpret_cast<const float*>(blk) : 0.0f;
+__device__ __forceinline__ StageRegs stage_load(const uint8_t* srow, int64_t sb, int piece) {
+  StageRegs r;
+  const uint8_t* blk = srow != nullptr ? srow + sb * kQ8KBytes : nullptr;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) r.q[i] = blk != nullptr ? ld_u32(blk + 4 + 16 * piece + 4 * i) : 0u;
+  r.d = (blk != nullptr && piece == 0) ? *reinterpret_cast<const float*>(blk) : 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) r.bs[i] = (NBSP > 0 && blk != nullptr && piece == 1) ? ld_u32(blk + 260 + 4 * i) : 0u;
+  return r;
+}
+template <int NBSP>
+__device__ __forceinline__ void stage_store(StageLds& L, const StageRegs& r, int m, int piece) {
+  *reinterpret_cast<uint4*>(&L.qs[m][16 * piece]) = make_uint4(r.q[0], r.q[1], r.q[2], r.q[3]);
+  if (piece == 0) L.dx[m] = r.d;
   if (NBSP > 0 && piece == 1) {
     int bs[16];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const uint32_t wv = blk != nullptr ? ld_u32(blk + 260 + 4 * i) : 0u;
-      bs[2 * i] = (int)(int16_t)(wv & 0xFFFF);
-      bs[2 * i + 1] = (int)(int16_t)(wv >> 16);
+      bs[2 * i] = (int)(int16_t)(r.bs[i] & 0xFFFF);
+      bs[2 * i + 1] = (int)(int16_t)(r.bs[i] >> 16);
     }
     uint32_t lo[4] = {0, 0, 0, 0}, hi[4] = {0, 0, 0, 0};
 #pragma unroll
     for (int j = 0; j < NBSP; ++j) {
-      const int s = NBSP == 8 ? bs[2 * j] + bs[2 * j + 1] : bs[j];
-      lo[j >> 2] |= (uint32_t)(s & 63) << (8 * (j & 3));
-      hi[j >> 2] |= (uint32_t)((s >> 6) & 255) << (8 * (j & 3));
+      const int v = NBSP == 8 ? bs[2 * j] + bs[2 * j + 1] : bs[j];
+      lo[j >> 2] |= (uint32_t)(v & 63) << (8 * (j & 3));
+      hi[j >> 2] |= (uint32_t)((v >> 6) & 255) << (8 * (j & 3));
     }
     *reinterpret_cast<uint4*>(&L.bsp[m][0][0]) = make_uint4(lo[0], lo[1], lo[2], lo[3]);
     *reinterpret_cast<uint4*>(&L.bsp[m][1][0]) = make_uint4(hi[0], hi[1], hi[2], hi[3]);
@@ -343,7 +347,7 @@ __device__ __forceinline__ void quantize_row_lds(const float* hrow, uint8_t* __r
 template <int FMT, int MODE>
 __global__ __launch_bounds__(512) void k_mfma(MfmaArgs a) {
   using M = Mf<FMT>;
-  __shared__ StageLds L;
+  __shared__ StageLds L[2];
   __shared__ int64_t orow[kTileT];
   __shared__ double owt[kTileT];
 
@@ -411,33 +415,41 @@ __global__ __launch_bounds__(512) void k_mfma(MfmaArgs a) {
     owt[tid] = wt;
   }
 
-  // ---- main loop over the 256-blocks of K
+  // ---- main loop over the 256-blocks of K, software-pipelined: the k-loop is
+  // a sequence of units (block sb, matrix) and the weight loads of the next
+  // unit are issued before the MFMAs of the current one (gate/up: up of sb
+  // while gate of sb computes, gate of sb+1 while up of sb computes), as are
+  // the activation loads of block sb+1.  The activation stage is
+  // double-buffered, so one barrier per block separates its LDS writes from
+  // every wave's reads (a buffer is rewritten only after all waves passed the
+  // barrier that follows their last read of it).
   const int64_t nbK = a.K / 256, nsb = a.N * nbK;
   const int64_t wrow = (int64_t)blockIdx.y * kMfRows + wave * 32 + (lane & 31);
   double acc0[16], acc1[16];
 #pragma unroll
   for (int r = 0; r < 16; ++r) { acc0[r] = 0.0; acc1[r] = 0.0; }
-  const uint8_t* qrow = &L.qs[lane & 31][0];
+  typename M::Wt wn = M::load(W0, (size_t)nsb, (size_t)(wrow * nbK), g);
+  StageRegs sr = stage_load<M::NBSP>(srow, 0, piece);
   for (int64_t sb = 0; sb < nbK; ++sb) {
-    const size_t sbi = (size_t)(wrow * nbK + sb);
-    typename M::Wt w0 = M::load(W0, (size_t)nsb, sbi, g);
-    typename M::Wt w1;
-    if constexpr (MODE == 0 && !M::kLateSecond) w1 = M::load(W1, (size_t)nsb, sbi, g);
-    __syncthreads();                     // the previous block's LDS reads are done
-    stage_block<M::NBSP>(L, srow, (int)sb, ms, piece);
+    StageLds& S = L[sb & 1];
+    stage_store<M::NBSP>(S, sr, ms, piece);
     __syncthreads();
-    double dxv[16];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const float4 f = *reinterpret_cast<const float4*>(&L.dx[8 * q + 4 * g]);
-      dxv[4 * q] = f.x; dxv[4 * q + 1] = f.y; dxv[4 * q + 2] = f.z; dxv[4 * q + 3] = f.w;
-    }
-    v4i abs = {0, 0, 0, 0};
-    if constexpr (M::NBSP > 0) abs = lds_v4(&L.bsp[lane & 31][g][0]);
-    M::mac(w0, g, qrow, abs, dxv, acc0);
+    const size_t sbi = (size_t)(wrow * nbK + sb);
+    typename M::Wt wc = wn;
     if constexpr (MODE == 0) {
-      if constexpr (M::kLateSecond) w1 = M::load(W1, (size_t)nsb, sbi, g);
-      M::mac(w1, g, qrow, abs, dxv, acc1);
+      wn = M::load(W1, (size_t)nsb, sbi, g);
+    } else if (sb + 1 < nbK) {
+      wn = M::load(W0, (size_t)nsb, sbi + 1, g);
+    }
+    if (sb + 1 < nbK) sr = stage_load<M::NBSP>(srow, sb + 1, piece);
+    const uint8_t* qrow = &S.qs[lane & 31][0];
+    v4i abs = {0, 0, 0, 0};
+    if constexpr (M::NBSP > 0) abs = lds_v4(&S.bsp[lane & 31][g][0]);
+    M::mac(wc, g, qrow, abs, S.dx, n, acc0);
+    if constexpr (MODE == 0) {
+      wc = wn;
+      if (sb + 1 < nbK) wn = M::load(W0, (size_t)nsb, sbi + 1, g);
+      M::mac(wc, g, qrow, abs, S.dx, n, acc1);
     }
   }
 

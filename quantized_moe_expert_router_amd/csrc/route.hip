@@ -13,6 +13,7 @@ namespace moeq {
 constexpr int kLogitTok = 16;       // tokens per logits tile
 constexpr int kSmallT = 256;        // single-workgroup selection + lists up to this many tokens
 constexpr int kChunkT = 256;        // tokens per chunk of the multi-kernel lists path
+constexpr int kMfmaRouteT = 256;    // from this many tokens the logits run on fp64 matrix cores
 
 // logits[t, e] = sum_i W[e, i] * x[t, i] (+ bias[e]) in fp64.  The fp32*fp32
 // products are exact in fp64, so fma and mul+add agree; only the summation
@@ -77,6 +78,73 @@ __global__ __launch_bounds__(256) void k_logits(const float* __restrict__ x, con
     }
     __syncthreads();
   }
+}
+
+// Logits of many tokens as a dense contraction on fp64 matrix cores:
+// v_mfma_f64_16x16x4f64 on exact fp64 copies of the fp32 operands, so every
+// product is exact and only the order of the fp64 additions differs from a
+// sequential sum (as in k_logits).  Workgroup tile 64 tokens x 64 experts,
+// wave tile 32 x 32 (2 x 2 MFMA blocks); K staged through LDS 32 at a time.
+// Operand lanes: A lane l = x[m = l%16][k = l/16], B lane l = W[n = l%16][k = l/16]
+// (the same k on both sides); result lane l, value r = logit[4*r + l/16][l%16].
+typedef double v4d __attribute__((ext_vector_type(4)));
+constexpr int kRt = 64, kRe = 64, kRk = 32, kRpad = 36;
+
+__global__ __launch_bounds__(256) void k_logits_mfma(const float* __restrict__ x, const float* __restrict__ W,
+                                                     const float* __restrict__ bias, int64_t T, int64_t H,
+                                                     int64_t E, double* __restrict__ logits) {
+  __shared__ float xs[kRt][kRpad];
+  __shared__ float ws[kRe][kRpad];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = lane_id();
+  const int64_t t0 = (int64_t)blockIdx.x * kRt, e0 = (int64_t)blockIdx.y * kRe;
+  const int wt = (wave & 1) * 32, we = (wave >> 1) * 32;
+  const int m16 = lane & 15, kq = lane >> 4;
+  v4d acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[i][j] = (v4d){0.0, 0.0, 0.0, 0.0};
+  for (int64_t k0 = 0; k0 < H; k0 += kRk) {
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int idx = tid + 256 * i, row = idx >> 3, c4 = idx & 7;
+      const int64_t kc = k0 + 4 * c4;
+      const int64_t tr = t0 + row, er = e0 + row;
+      const float4 zero = make_float4(0.f, 0.f, 0.f, 0.f);
+      const float4 xv = (tr < T && kc < H) ? *reinterpret_cast<const float4*>(x + tr * H + kc) : zero;
+      const float4 wv = (er < E && kc < H) ? *reinterpret_cast<const float4*>(W + er * H + kc) : zero;
+      *reinterpret_cast<float4*>(&xs[row][4 * c4]) = xv;
+      *reinterpret_cast<float4*>(&ws[row][4 * c4]) = wv;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int kk = 0; kk < kRk / 4; ++kk) {
+      double a[2], b[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        a[i] = (double)xs[wt + 16 * i + m16][4 * kk + kq];
+        b[i] = (double)ws[we + 16 * i + m16][4 * kk + kq];
+      }
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j] = __builtin_amdgcn_mfma_f64_16x16x4f64(a[i], b[j], acc[i][j], 0, 0, 0);
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int64_t e = e0 + we + 16 * j + m16;
+      if (e >= E) continue;
+      const double bv = bias ? (double)bias[e] : 0.0;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int64_t t = t0 + wt + 16 * i + 4 * r + kq;
+        if (t < T) logits[t * E + e] = acc[i][j][r] + bv;
+      }
+    }
 }
 
 template <int NPER>
@@ -251,6 +319,14 @@ __global__ void k_empty_lists(int64_t E, int32_t* offsets, int32_t* active) {
 
 int launch_logits(int64_t T, int64_t H, int64_t E, const float* x, const float* W, const float* bias,
                   double* logits, void* xq, hipStream_t s) {
+  if (T >= kMfmaRouteT) {
+    // many tokens: the router is a dense contraction (matrix cores); q8_K(x)
+    // in its own launch
+    dim3 g((unsigned)((T + kRt - 1) / kRt), (unsigned)((E + kRe - 1) / kRe));
+    hipLaunchKernelGGL(k_logits_mfma, g, dim3(256), 0, s, x, W, bias, T, H, E, logits);
+    if (hipGetLastError() != hipSuccess) return -1;
+    return xq ? launch_quantize_q8K(x, T, H, xq, s) : 0;
+  }
   const int64_t nq = xq ? (T * (H / 256) + 3) / 4 : 0;
   const int64_t tiles = (T + kLogitTok - 1) / kLogitTok;
   dim3 g1((unsigned)(E + nq), (unsigned)(tiles < 64 ? tiles : 64));

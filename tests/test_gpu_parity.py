@@ -168,6 +168,31 @@ def check_route(run, layer, sel):
 PATHS = {"gemv": moeq.PATH_GEMV, "mfma": moeq.PATH_MFMA, "auto": moeq.PATH_AUTO}
 
 
+@pytest.mark.parametrize("T,E,H,with_bias", [(256, 64, 256, False), (300, 70, 512, True), (1000, 513, 2048, True)])
+def test_route_many_tokens_ragged(T, E, H, with_bias):
+    """Many tokens: the logits run as an fp64 matrix-core contraction with
+    ragged token and expert tiles; logits, ids, weights and lists must match."""
+    say("route many tokens", T, E, H, with_bias)
+    rng = np.random.default_rng(T + E)
+    x = rng.standard_normal((T, H)).astype(np.float32)
+    W = (rng.standard_normal((E, H)) * 0.02).astype(np.float32)
+    b = (rng.standard_normal(E) * 0.1).astype(np.float32) if with_bias else None
+    k = 6
+    out = moeq.moeq_route(dev(x), dev(W), None if b is None else dev(b), k, syn.SOFTMAX_TOPK)
+    xq = moeq.moeq_quantize_q8K(dev(x))
+    torch.cuda.synchronize()
+    lg, ids, w = oracle.route(x, W, b, k, syn.SOFTMAX_TOPK)
+    assert np.allclose(out.logits.cpu().numpy(), lg, rtol=0, atol=1e-12)
+    assert np.array_equal(out.ids.cpu().numpy(), ids)
+    check_w(out.w.cpu().numpy(), w)
+    off, pairs, active = oracle.lists(ids, E)
+    assert np.array_equal(out.offsets.cpu().numpy(), off)
+    assert np.array_equal(out.pairs.cpu().numpy()[:T * k], pairs)
+    act = out.active.cpu().numpy()
+    assert np.array_equal(act[:1 + act[0]], active)
+    assert np.array_equal(xq.cpu().numpy(), oracle.quantize_q8K(x))
+
+
 @pytest.mark.parametrize("path", ["gemv", "mfma", "auto"])
 @pytest.mark.parametrize("fused", [False, True], ids=["calls", "layer"])
 @pytest.mark.parametrize("name", syn.CONFIG_ORDER)
