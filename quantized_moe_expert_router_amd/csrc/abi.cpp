@@ -300,6 +300,12 @@ int ffn_enqueue(const moeq_ffn_desc* d, const void* x_q8K, const int32_t* topk_i
       a.src = hq; a.src_stride = hq_stride;
       gy = (unsigned)(d->H / 256);
     }
+    // Row blocks per workgroup: enough workgroups to fill the chip several
+    // times over, the rest of the rows looped inside (start-up and staging
+    // paid once per workgroup).
+    const int64_t nrb = gy;
+    a.rb = std::max<int64_t>(1, std::min<int64_t>(nrb, (int64_t)gx * nrb / 2048));
+    gy = (unsigned)((nrb + a.rb - 1) / a.rb);
     return launch_mfma(fmt, mode, dim3(gx, gy), a, s);
   };
 

@@ -340,14 +340,23 @@ __device__ __forceinline__ void quantize_row_lds(const float* hrow, uint8_t* __r
 // ------------------------------------------------------------ the kernel
 //
 // MODE 0 (gate/up): A = q8_K(x) rows of the tile's tokens, W0 = gate, W1 = up;
-//   epilogue h = fl32(silu(g) u) into LDS, then q8_K(h) of the 256-wide block
-//   (one q8_K block per tile row) into hq.
+//   epilogue per 256-row block: h = fl32(silu(g) u) into LDS, then q8_K(h) of
+//   the block (one q8_K block per tile row) into hq.
 // MODE 1 (down): A = q8_K(h) rows of the tile's pairs, W0 = down; epilogue
 //   yp[row] = fl32(gate weight * y).
-template <int FMT, int MODE>
+// RES: K has at most kResBlocks 256-blocks, so the whole activation tile is
+//   staged in LDS once and the k-loop runs without barriers; otherwise the
+//   blocks stream through a double-buffered stage (one barrier per block).
+// A workgroup covers `rb` consecutive 256-row blocks of its tile (grid.y =
+// ceil(blocks / rb)), so the staging and start-up are paid once per rb blocks;
+// the weight loads of the next (row block, 256-block, matrix) unit are always
+// in flight while the current unit's MFMAs run.
+constexpr int kResBlocks = 8;
+
+template <int FMT, int MODE, bool RES>
 __global__ __launch_bounds__(512) void k_mfma(MfmaArgs a) {
   using M = Mf<FMT>;
-  __shared__ StageLds L[2];
+  __shared__ StageLds L[RES ? kResBlocks : 2];
   __shared__ int64_t orow[kTileT];
   __shared__ double owt[kTileT];
 
@@ -363,6 +372,10 @@ __global__ __launch_bounds__(512) void k_mfma(MfmaArgs a) {
     const int4 tl = a.tiles[blockIdx.x];
     e = tl.x; t0 = tl.y; n = tl.z; list_off = tl.w;
   }
+  const int64_t nrb = a.N / kMfRows;
+  const int64_t rb0 = (int64_t)blockIdx.y * a.rb;
+  const int64_t rb1 = rb0 + a.rb < nrb ? rb0 + a.rb : nrb;
+  if (rb0 >= nrb) return;
   const uint8_t *W0, *W1 = nullptr;
   if (a.shared) {
     W0 = a.sh_w0;
@@ -375,9 +388,10 @@ __global__ __launch_bounds__(512) void k_mfma(MfmaArgs a) {
     if (!resident) {
       // not resident: its pairs add exactly nothing (their down rows are zero)
       if (MODE == 1) {
-        for (int i = threadIdx.x; i < n * kMfRows; i += blockDim.x) {
-          const int p = a.pairs[list_off + t0 + i / kMfRows];
-          a.yp[(int64_t)p * a.N + (int64_t)blockIdx.y * kMfRows + i % kMfRows] = 0.0f;
+        const int64_t cols = (rb1 - rb0) * kMfRows;
+        for (int64_t i = threadIdx.x; i < n * cols; i += blockDim.x) {
+          const int p = a.pairs[list_off + t0 + i / cols];
+          a.yp[(int64_t)p * a.N + rb0 * kMfRows + i % cols] = 0.0f;
         }
       }
       return;
@@ -415,58 +429,77 @@ __global__ __launch_bounds__(512) void k_mfma(MfmaArgs a) {
     owt[tid] = wt;
   }
 
-  // ---- main loop over the 256-blocks of K, software-pipelined: the k-loop is
-  // a sequence of units (block sb, matrix) and the weight loads of the next
-  // unit are issued before the MFMAs of the current one (gate/up: up of sb
-  // while gate of sb computes, gate of sb+1 while up of sb computes), as are
-  // the activation loads of block sb+1.  The activation stage is
-  // double-buffered, so one barrier per block separates its LDS writes from
-  // every wave's reads (a buffer is rewritten only after all waves passed the
-  // barrier that follows their last read of it).
   const int64_t nbK = a.K / 256, nsb = a.N * nbK;
-  const int64_t wrow = (int64_t)blockIdx.y * kMfRows + wave * 32 + (lane & 31);
-  double acc0[16], acc1[16];
+  const int64_t lrow = wave * 32 + (lane & 31);       // the lane's weight row inside a row block
+  // first unit's weights, in flight during the staging
+  typename M::Wt wn = M::load(W0, (size_t)nsb, (size_t)((rb0 * kMfRows + lrow) * nbK), g);
+  StageRegs sr;
+  if constexpr (RES) {
+    for (int64_t sb0 = 0; sb0 < nbK; sb0 += 4) {
+      StageRegs r4[4];
 #pragma unroll
-  for (int r = 0; r < 16; ++r) { acc0[r] = 0.0; acc1[r] = 0.0; }
-  typename M::Wt wn = M::load(W0, (size_t)nsb, (size_t)(wrow * nbK), g);
-  StageRegs sr = stage_load<M::NBSP>(srow, 0, piece);
-  for (int64_t sb = 0; sb < nbK; ++sb) {
-    StageLds& S = L[sb & 1];
-    stage_store<M::NBSP>(S, sr, ms, piece);
+      for (int j = 0; j < 4; ++j)
+        if (sb0 + j < nbK) r4[j] = stage_load<M::NBSP>(srow, sb0 + j, piece);
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        if (sb0 + j < nbK) stage_store<M::NBSP>(L[sb0 + j], r4[j], ms, piece);
+    }
     __syncthreads();
-    const size_t sbi = (size_t)(wrow * nbK + sb);
-    typename M::Wt wc = wn;
-    if constexpr (MODE == 0) {
-      wn = M::load(W1, (size_t)nsb, sbi, g);
-    } else if (sb + 1 < nbK) {
-      wn = M::load(W0, (size_t)nsb, sbi + 1, g);
-    }
-    if (sb + 1 < nbK) sr = stage_load<M::NBSP>(srow, sb + 1, piece);
-    const uint8_t* qrow = &S.qs[lane & 31][0];
-    v4i abs = {0, 0, 0, 0};
-    if constexpr (M::NBSP > 0) abs = lds_v4(&S.bsp[lane & 31][g][0]);
-    M::mac(wc, g, qrow, abs, S.dx, n, acc0);
-    if constexpr (MODE == 0) {
-      wc = wn;
-      if (sb + 1 < nbK) wn = M::load(W0, (size_t)nsb, sbi + 1, g);
-      M::mac(wc, g, qrow, abs, S.dx, n, acc1);
-    }
   }
 
-  if constexpr (MODE == 0) {
-    // h = fl32(silu(g) u) -> LDS, then q8_K per tile row over these 256 columns
-    __shared__ float hs[kTileT][kMfRows + 4];
-    const int col = wave * 32 + (lane & 31);
+  for (int64_t rb = rb0; rb < rb1; ++rb) {
+    const int64_t wrow = rb * kMfRows + lrow;
+    double acc0[16], acc1[16];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) hs[out_row(r, g)][col] = (float)(silu64(acc0[r]) * acc1[r]);
-    __syncthreads();
-    for (int m = wave; m < n; m += kMfWaves)
-      quantize_row_lds(&hs[m][0], a.hq + orow[m] * a.hq_stride + (int64_t)blockIdx.y * kQ8KBytes);
-  } else {
+    for (int r = 0; r < 16; ++r) { acc0[r] = 0.0; acc1[r] = 0.0; }
+    if constexpr (!RES) sr = stage_load<M::NBSP>(srow, 0, piece);
+    for (int64_t sb = 0; sb < nbK; ++sb) {
+      StageLds& S = RES ? L[sb] : L[sb & 1];
+      if constexpr (!RES) {
+        stage_store<M::NBSP>(S, sr, ms, piece);
+        __syncthreads();
+      }
+      // next unit: up of this block (mode 0), else the next block, else the
+      // first block of the next row block
+      const size_t sbi = (size_t)(wrow * nbK + sb);
+      const bool last_k = sb + 1 == nbK;
+      const bool more = !last_k || rb + 1 < rb1;
+      const size_t next_sbi = last_k ? (size_t)((wrow + kMfRows) * nbK) : sbi + 1;
+      typename M::Wt wc = wn;
+      if constexpr (MODE == 0) {
+        wn = M::load(W1, (size_t)nsb, sbi, g);
+      } else if (more) {
+        wn = M::load(W0, (size_t)nsb, next_sbi, g);
+      }
+      if constexpr (!RES)
+        if (!last_k) sr = stage_load<M::NBSP>(srow, sb + 1, piece);
+      const uint8_t* qrow = &S.qs[lane & 31][0];
+      v4i abs = {0, 0, 0, 0};
+      if constexpr (M::NBSP > 0) abs = lds_v4(&S.bsp[lane & 31][g][0]);
+      M::mac(wc, g, qrow, abs, S.dx, n, acc0);
+      if constexpr (MODE == 0) {
+        wc = wn;
+        if (more) wn = M::load(W0, (size_t)nsb, next_sbi, g);
+        M::mac(wc, g, qrow, abs, S.dx, n, acc1);
+      }
+    }
+
+    if constexpr (MODE == 0) {
+      // h = fl32(silu(g) u) -> LDS, then q8_K per tile row over this row block
+      __shared__ float hs[kTileT][kMfRows + 4];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int m = out_row(r, g);
-      if (m < n) a.yp[orow[m] * a.N + wrow] = (float)(owt[m] * acc0[r]);
+      for (int r = 0; r < 16; ++r) hs[out_row(r, g)][lrow] = (float)(silu64(acc0[r]) * acc1[r]);
+      __syncthreads();
+      for (int m = wave; m < n; m += kMfWaves)
+        quantize_row_lds(&hs[m][0], a.hq + orow[m] * a.hq_stride + rb * kQ8KBytes);
+      __syncthreads();   // hs (and a streamed stage) is rewritten next
+    } else {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int m = out_row(r, g);
+        if (m < n) a.yp[orow[m] * a.N + wrow] = (float)(owt[m] * acc0[r]);
+      }
+      if constexpr (!RES) __syncthreads();   // the streamed stage is rewritten next
     }
   }
 }
@@ -524,9 +557,12 @@ int launch_mfma_plan(const int32_t* active, const int32_t* offsets, int thr, int
 
 int launch_mfma(int fmt, int mode, dim3 grid, const MfmaArgs& a, hipStream_t s) {
   if (grid.x == 0 || grid.y == 0) return 0;
-#define MOEQ_MF(F)                                                                     \
-  if (mode == 0) hipLaunchKernelGGL((k_mfma<F, 0>), grid, dim3(512), 0, s, a);         \
-  else hipLaunchKernelGGL((k_mfma<F, 1>), grid, dim3(512), 0, s, a);
+  const bool res = a.K / 256 <= kResBlocks;
+#define MOEQ_MF(F)                                                                             \
+  if (mode == 0 && res) hipLaunchKernelGGL((k_mfma<F, 0, true>), grid, dim3(512), 0, s, a);    \
+  else if (mode == 0) hipLaunchKernelGGL((k_mfma<F, 0, false>), grid, dim3(512), 0, s, a);     \
+  else if (res) hipLaunchKernelGGL((k_mfma<F, 1, true>), grid, dim3(512), 0, s, a);            \
+  else hipLaunchKernelGGL((k_mfma<F, 1, false>), grid, dim3(512), 0, s, a);
   switch (fmt) {
     case FQ4K: MOEQ_MF(FQ4K) break;
     case FQ6K: MOEQ_MF(FQ6K) break;

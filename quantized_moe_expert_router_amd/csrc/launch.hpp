@@ -97,6 +97,7 @@ struct MfmaArgs {
   int k;
   int64_t T;
   int64_t N, K;                 // weight rows and columns of this launch's matrices
+  int64_t rb;                   // 256-row blocks per workgroup (grid.y = ceil(N/256 / rb))
   const uint8_t* src;           // q8_K rows: x by token (mode 0), h by pair row (mode 1)
   int64_t src_stride;
   uint8_t* hq;                  // mode 0: q8_K(h) rows out
