@@ -38,6 +38,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU oracle sample time")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-verify", action="store_true", help="skip the verify (4-token) measurement")
+    ap.add_argument("--no-prefill", action="store_true", help="skip the 8192-token prefill measurement")
+    ap.add_argument("--prefill-steps", type=int, default=20)
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="first run a device copy of this many MiB (counter calibration for rocprofv3 --pmc)")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -211,6 +213,75 @@ class LayerCycle:
         return time.perf_counter() - t0
 
 
+def ffn_event_us(cyc, n_ev):
+    """Mean duration of expert-FFN-only launches (moeq_expert_ffn on the routing
+    of layer 0, weights cycling over the layers), timed with HIP events on the
+    launch stream while a GPU busy-wait ahead of them hides host launch time."""
+    import numpy as np
+    import torch
+    from quantized_moe_expert_router_amd import moeq
+    cfg, T, L = cyc.cfg, cyc.T, cyc.L
+    dev = cyc.y.device
+    route_ws = torch.empty(max(256, moeq.moeq_route_workspace(T, cfg.H, cfg.E, cfg.k, cfg.gating)),
+                           dtype=torch.uint8, device=dev)
+    xq = torch.empty((T, cfg.H // 256 * moeq.Q8K_BYTES), dtype=torch.uint8, device=dev)
+    ffn_ws = torch.empty(moeq.moeq_expert_ffn_workspace(cyc.layers[0]["desc"]), dtype=torch.uint8, device=dev)
+    ro = cyc.route_out
+    moeq.moeq_route(cyc.xs[0], cyc.layers[0]["w_router"], cyc.layers[0]["bias"], cfg.k, cfg.gating, out=ro,
+                    ws=route_ws, x_q8K=xq)
+    torch.cuda.synchronize()
+    cur = torch.cuda.current_stream()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(n_ev)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(n_ev)]
+    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    c0.record(cur)
+    torch.cuda._sleep(1_000_000)
+    c1.record(cur)
+    torch.cuda.synchronize()
+    per_cycle_ms = max(c0.elapsed_time(c1), 1e-3) / 1_000_000
+    torch.cuda._sleep(int(min(2e9, (0.1 + n_ev * 50e-6) * 1e3 / per_cycle_ms)))
+    for i in range(n_ev):
+        lay = cyc.layers[i % L]
+        starts[i].record(cur)
+        moeq.moeq_expert_ffn(lay["desc"], xq, ro.ids, ro.w, ro.offsets, ro.pairs, ro.active, None, cyc.y,
+                             ffn_ws, None)
+        ends[i].record(cur)
+    torch.cuda.synchronize()
+    return float(np.mean([s.elapsed_time(e) for s, e in zip(starts, ends)])) * 1e3
+
+
+INT8_PEAK_TOPS = 5000.0
+
+
+def secondary(name, L, steps, warmup, dev):
+    """Whole-layer throughput of another workload (layers cycled so weights
+    stream from HBM), its expert-FFN launch time, and the FFN's roofline
+    figures: HBM GB/s over the union's weights, and int8-MFMA fraction of the
+    useful integer work (2 ops per weight x activation product)."""
+    import torch
+    from quantized_moe_expert_router_amd import synthetic as syn
+    cfg = syn.CONFIGS[name]
+    cyc = LayerCycle(cfg, cfg.T, L, dev)
+    dt = cyc.time(steps, warmup)
+    ms = dt * 1e3 / steps
+    ids = cyc.route_out.ids.cpu().numpy()
+    union = len(set(ids.reshape(-1).tolist()))
+    ffn_us = ffn_event_us(cyc, max(steps, 8))
+    w_bytes = union * syn.expert_bytes(cfg) + (syn.shared_bytes(cfg) if cfg.shared else 0)
+    layer_bytes = w_bytes + cfg.E * cfg.H * 4 + 2 * cfg.T * cfg.H * 4
+    pairs = cfg.T * cfg.k + (cfg.T if cfg.shared else 0)
+    Fs = cfg.F_shared if cfg.shared else cfg.F
+    ops = 2 * 3 * cfg.H * (cfg.T * cfg.k * cfg.F + (cfg.T * Fs if cfg.shared else 0))
+    out = {"workload": cfg.name, "T": cfg.T, "tokens_per_s": cfg.T * steps / dt, "ms_per_step": ms,
+           "layers_cycled": L, "union": union, "pairs": pairs, "layer_hbm_gbs": layer_bytes / (ms * 1e-3) / 1e9,
+           "ffn_us": ffn_us, "ffn_weight_gbs": w_bytes / (ffn_us * 1e-6) / 1e9,
+           "ffn_int8_tops": ops / (ffn_us * 1e-6) / 1e12,
+           "ffn_int8_mfma_frac": ops / (ffn_us * 1e-6) / 1e12 / INT8_PEAK_TOPS}
+    del cyc
+    torch.cuda.empty_cache()
+    return out
+
+
 def cpu_baseline(cfg, seconds):
     """The CPU oracle, as it stands, on a bounded sample of decode tokens of layer 0."""
     import numpy as np
@@ -262,17 +333,6 @@ def main():
     L = args.layers
     t_setup = time.time()
     cyc = LayerCycle(cfg, 1, L, dev)
-    layers, xs, route_out, y = cyc.layers, cyc.xs, cyc.route_out, cyc.y
-    route_ws = torch.empty(max(256, moeq.moeq_route_workspace(1, cfg.H, cfg.E, cfg.k, cfg.gating)),
-                           dtype=torch.uint8, device=dev)
-    xq = torch.empty((1, cfg.H // 256 * moeq.Q8K_BYTES), dtype=torch.uint8, device=dev)
-    ffn_ws = torch.empty(moeq.moeq_expert_ffn_workspace(layers[0]["desc"]), dtype=torch.uint8, device=dev)
-
-    def ffn_only(l, stream=None):
-        lay = layers[l]
-        moeq.moeq_expert_ffn(lay["desc"], xq, route_out.ids, route_out.w, route_out.offsets, route_out.pairs,
-                             route_out.active, None, y, ffn_ws, stream)
-
     setup_s = time.time() - t_setup
 
     # ---- timed region: exactly `steps` whole layers (value)
@@ -280,29 +340,8 @@ def main():
     ms_per_step = dt * 1e3 / args.steps
     tokens_per_s = args.steps / dt
 
-    # ---- expert FFN launches timed with HIP events on their stream, GPU kept
-    # busy ahead of them so host launch overhead is hidden.
-    cur = torch.cuda.current_stream()
-    n_ev = args.steps
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(n_ev)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(n_ev)]
-    moeq.moeq_route(xs[0], layers[0]["w_router"], None, cfg.k, cfg.gating, out=route_out, ws=route_ws,
-                    x_q8K=xq)                # routing of layer 0 feeds every timed launch
-    torch.cuda.synchronize()
-    # calibrate a GPU busy-wait long enough for the host to enqueue all launches
-    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    c0.record(cur)
-    torch.cuda._sleep(1_000_000)
-    c1.record(cur)
-    torch.cuda.synchronize()
-    per_cycle_ms = max(c0.elapsed_time(c1), 1e-3) / 1_000_000
-    torch.cuda._sleep(int(min(2e9, (0.1 + n_ev * 50e-6) * 1e3 / per_cycle_ms)))
-    for i in range(n_ev):
-        starts[i].record(cur)
-        ffn_only(i % L)
-        ends[i].record(cur)
-    torch.cuda.synchronize()
-    ffn_us = float(np.mean([s.elapsed_time(e) for s, e in zip(starts, ends)])) * 1e3
+    # ---- expert FFN launches timed with HIP events on their stream
+    ffn_us = ffn_event_us(cyc, args.steps)
 
     # Algorithmic bytes of one expert FFN launch: the weights of the 8 selected
     # experts and the shared one, read once, plus q8_K(x) in and y out.
@@ -311,25 +350,17 @@ def main():
     ffn_bytes = cfg.k * eb + sb + cfg.H // 256 * 292 + cfg.H * 4
     layer_bytes = ffn_bytes + cfg.E * cfg.H * 4 + cfg.H * 4
     achieved = ffn_bytes / (ffn_us * 1e-6) / 1e9
+    del cyc
+    torch.cuda.empty_cache()
 
     # ---- secondary: MTP verify rows (4 tokens per step, union of experts)
     verify = None
     if not args.no_verify:
-        del cyc
-        torch.cuda.empty_cache()
-        vcfg = syn.CONFIGS["verify"]
-        vL = max(4, L // 4)
-        vc = LayerCycle(vcfg, 4, vL, dev)
-        vsteps = max(vL, args.steps // 4)
-        vdt = vc.time(vsteps, max(vL, args.warmup // 4))
-        vms = vdt * 1e3 / vsteps
-        ids = vc.route_out.ids.cpu().numpy()
-        union = len(set(ids.reshape(-1).tolist()))
-        vbytes = union * syn.expert_bytes(vcfg) + vcfg.E * vcfg.H * 4 + 2 * 4 * vcfg.H * 4
-        verify = {"workload": vcfg.name, "T": 4, "tokens_per_s": 4 * vsteps / vdt, "ms_per_step": vms,
-                  "layers_cycled": vL, "union_last_step": union,
-                  "layer_hbm_gbs_est": vbytes / (vms * 1e-3) / 1e9}
-        del vc
+        verify = secondary("verify", max(4, L // 4), max(8, args.steps // 4), max(4, args.warmup // 4), dev)
+    # ---- secondary: 8192-token prefill chunk (int8 MFMA grouped GEMM)
+    prefill = None
+    if not args.no_prefill:
+        prefill = secondary("prefill", 2, args.prefill_steps, 2, dev)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -358,6 +389,7 @@ def main():
                      "bytes_per_launch": ffn_bytes, "avg_launch_us": ffn_us},
         "cpu_baseline": cpu,
         "verify_b4": verify,
+        "prefill_8192": prefill,
         "setup_s": setup_s,
     }
     print(json.dumps(out), flush=True)
