@@ -45,13 +45,17 @@ bool lane_geo(int fmt, int64_t cols, LaneGeo* g) {
   return true;
 }
 
-// Rows per expert up to which the dot-product (GEMV) kernels run in AUTO mode;
-// experts with more rows (and the shared expert when T exceeds it) go to the
-// int8 MFMA grouped GEMM.
-constexpr int kGemvMaxRows = 4;
-
-int gemv_max_of(int32_t path) {
-  return path == MOEQ_PATH_GEMV ? INT32_MAX : path == MOEQ_PATH_MFMA ? 0 : kGemvMaxRows;
+// Rows per expert up to which the dot-product (GEMV) kernels run; experts with
+// more rows (and the shared expert when T exceeds it) go to the int8 MFMA
+// grouped GEMM.  AUTO: one token runs the one-token dot-product kernels; more
+// tokens run every expert on matrix cores (8-row tiles for experts with at
+// most 8 rows).  Measured on MI355X, the MFMA tiles beat the dot-product
+// kernels from one row per expert up whenever T > 1 (verify, 16-token chunk,
+// prefill), because the per-token dot products leave the vector ALUs.
+int gemv_max_of(const moeq_ffn_desc* d) {
+  if (d->path == MOEQ_PATH_GEMV) return INT32_MAX;
+  if (d->path == MOEQ_PATH_MFMA) return 0;
+  return d->T == 1 ? INT32_MAX : 0;
 }
 
 // Upper bound on the MFMA tiles of the routed experts: sum over experts with
@@ -63,17 +67,26 @@ int64_t mfma_max_tiles(const moeq_ffn_desc* d, int thr) {
   const int64_t U = std::min<int64_t>(d->E, P / (thr + 1));
   return (P + 31 * U) / 32 + 1;
 }
+// Upper bound on the experts with more than thr rows (one 8-row tile each when
+// they have at most 8).
+int64_t mfma_max_experts(const moeq_ffn_desc* d, int thr) {
+  const int64_t P = d->T * d->k;
+  if (d->T <= thr) return 0;
+  return std::min<int64_t>(d->E, P / (thr + 1));
+}
+constexpr int kThinT = 8;   // rows of the MFMA tiles of experts with at most 8 rows
 
 struct FfnLayout {
-  int64_t Fmax, nrows, max_tiles;
-  size_t off_h, off_yp, off_hq, off_hqs, off_slots, off_tiles, off_count, total;
+  int64_t Fmax, nrows, max_tiles, max_thin;
+  size_t off_h, off_yp, off_hq, off_hqs, off_slots, off_tiles, off_thin, off_count, total;
 };
 FfnLayout ffn_layout(const moeq_ffn_desc* d) {
   FfnLayout L{};
   const bool sh = d->sh_gate != nullptr;
   L.Fmax = sh ? std::max(d->F, d->F_shared) : d->F;
   L.nrows = d->T * d->k + d->T;
-  L.max_tiles = mfma_max_tiles(d, gemv_max_of(d->path));
+  L.max_tiles = mfma_max_tiles(d, gemv_max_of(d));
+  L.max_thin = mfma_max_experts(d, gemv_max_of(d));
   size_t o = 0;
   L.off_h = o;   o += align256((size_t)L.nrows * L.Fmax * sizeof(float));
   L.off_yp = o;  o += align256((size_t)L.nrows * d->H * sizeof(float));
@@ -81,7 +94,8 @@ FfnLayout ffn_layout(const moeq_ffn_desc* d) {
   L.off_hqs = o; o += align256(sh ? (size_t)d->T * (d->F_shared / 256) * kQ8KBytes : 0);
   L.off_slots = o; o += align256((size_t)(d->k + 1) * sizeof(SlotRec));
   L.off_tiles = o; o += align256((size_t)L.max_tiles * sizeof(int4));
-  L.off_count = o; o += 256;
+  L.off_thin = o;  o += align256((size_t)L.max_thin * sizeof(int4));
+  L.off_count = o; o += 256;                     // [0]: 32-row tiles, [1]: 8-row tiles
   L.total = o;
   return L;
 }
@@ -202,7 +216,7 @@ int ffn_enqueue(const moeq_ffn_desc* d, const void* x_q8K, const int32_t* topk_i
   const bool sh = d->sh_gate != nullptr;
   const bool same_shape = sh && d->sh_fmt_gate == d->fmt_gate && d->sh_fmt_down == d->fmt_down &&
                           d->F_shared == d->F;
-  const int thr = gemv_max_of(d->path);
+  const int thr = gemv_max_of(d);
   const bool one = d->T == 1 && thr >= 1;       // the one-token dot-product kernels
   const bool gemv = thr >= 1;                    // any expert on the dot-product path
   const bool mfma = d->T > thr;                  // any expert on the MFMA path
@@ -271,11 +285,13 @@ int ffn_enqueue(const moeq_ffn_desc* d, const void* x_q8K, const int32_t* topk_i
   };
   // int8 MFMA tiles: mode 0 = gate/up (+ q8_K(h)), mode 1 = down
   int4* tiles = (int4*)(wsb + L.off_tiles);
+  int4* thin_tiles = (int4*)(wsb + L.off_thin);
   int32_t* tcount = (int32_t*)(wsb + L.off_count);
-  auto mfma_launch = [&](int mode, bool shared_exp) -> int {
+  auto mfma_launch = [&](int mode, bool shared_exp, bool thin) -> int {
     MfmaArgs a{};
     a.shared = shared_exp ? 1 : 0;
-    a.tiles = tiles; a.count = tcount;
+    a.tiles = thin ? thin_tiles : tiles;
+    a.count = thin ? tcount + 1 : tcount;
     a.pairs = pairs; a.k = d->k; a.T = d->T;
     a.topk_w = topk_w; a.shared_scale = shared_scale;
     a.yp = (float*)(wsb + L.off_yp);
@@ -283,7 +299,8 @@ int ffn_enqueue(const moeq_ffn_desc* d, const void* x_q8K, const int32_t* topk_i
     const int64_t hq_stride = (Fx / 256) * kQ8KBytes;
     uint8_t* hq = shared_exp ? wsb + L.off_hqs : wsb + L.off_hq;
     int fmt;
-    unsigned gx = shared_exp ? (unsigned)((d->T + 31) / 32) : (unsigned)L.max_tiles;
+    const int tm = thin ? kThinT : 32;
+    unsigned gx = shared_exp ? (unsigned)((d->T + tm - 1) / tm) : (unsigned)(thin ? L.max_thin : L.max_tiles);
     unsigned gy;
     a.gate = d->gate; a.up = d->up; a.down = d->down;
     if (mode == 0) {
@@ -306,11 +323,12 @@ int ffn_enqueue(const moeq_ffn_desc* d, const void* x_q8K, const int32_t* topk_i
     const int64_t nrb = gy;
     a.rb = std::max<int64_t>(1, std::min<int64_t>(nrb, (int64_t)gx * nrb / 2048));
     gy = (unsigned)((nrb + a.rb - 1) / a.rb);
-    return launch_mfma(fmt, mode, dim3(gx, gy), a, s);
+    return launch_mfma(fmt, mode, thin, dim3(gx, gy), a, s);
   };
 
   if (mfma) {
-    if ((rc = launch_mfma_plan(active, expert_offsets, thr, (int)L.max_tiles, tiles, tcount, s)))
+    if ((rc = launch_mfma_plan(active, expert_offsets, thr, (int)L.max_tiles, tiles, tcount, thin_tiles, tcount + 1,
+                               s)))
       return rc;
   }
   // gate/up: h[pair, f] = fl32(silu(g) u)  (dot-product path: fp32 h rows;
@@ -325,8 +343,9 @@ int ffn_enqueue(const moeq_ffn_desc* d, const void* x_q8K, const int32_t* topk_i
     }
   }
   if (mfma) {
-    if ((rc = mfma_launch(0, false))) return rc;
-    if (sh && (rc = mfma_launch(0, true))) return rc;
+    if (d->T > kThinT && (rc = mfma_launch(0, false, false))) return rc;
+    if ((rc = mfma_launch(0, false, true))) return rc;
+    if (sh && (rc = mfma_launch(0, true, d->T <= kThinT))) return rc;
   }
   // down and the weighted combine
   if (one && (!sh || same_shape)) {
@@ -344,8 +363,9 @@ int ffn_enqueue(const moeq_ffn_desc* d, const void* x_q8K, const int32_t* topk_i
     }
   }
   if (mfma) {
-    if ((rc = mfma_launch(1, false))) return rc;
-    if (sh && (rc = mfma_launch(1, true))) return rc;
+    if (d->T > kThinT && (rc = mfma_launch(1, false, false))) return rc;
+    if ((rc = mfma_launch(1, false, true))) return rc;
+    if (sh && (rc = mfma_launch(1, true, d->T <= kThinT))) return rc;
   }
   return launch_combine((const float*)(wsb + L.off_yp), d->T, d->H, d->k, sh ? 1 : 0, y, d->accumulate, s);
 }
@@ -416,7 +436,7 @@ int moeq_moe_layer(const moeq_route_desc* r, const moeq_ffn_desc* f, const float
   uint8_t* wsb = (uint8_t*)ws;
   hipStream_t s = (hipStream_t)stream;
   void* xq = wsb + L.off_xq;
-  if (r->T == 1 && gemv_max_of(f->path) >= 1) {
+  if (r->T == 1 && gemv_max_of(f) >= 1) {
     // one token: logits + q8_K(x) in one launch, then gate/up routes inline
     double* lg = logits ? logits : (double*)(wsb + L.off_route);
     if ((rc = launch_logits(1, r->H, r->E, x, w_router, bias, lg, xq, s))) return hip_status(rc);

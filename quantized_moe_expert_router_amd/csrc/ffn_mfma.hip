@@ -47,10 +47,11 @@ constexpr int kMfWaves = 8;        // waves per workgroup, 32 weight rows each
 constexpr int kMfRows = 32 * kMfWaves;
 constexpr int kQsStride = 272;     // LDS bytes per staged row: 256 + 16 (bank spread)
 
+template <int TM>
 struct __align__(16) StageLds {
-  uint8_t qs[kTileT][kQsStride];   // q8_K quants of the tile rows, current 256-block
-  uint8_t bsp[kTileT][2][16];      // split block sums: [0] = bl entries, [1] = bh entries
-  float dx[kTileT];                // q8_K scales
+  uint8_t qs[TM][kQsStride];       // q8_K quants of the tile rows, one 256-block
+  uint8_t bsp[TM][2][16];          // split block sums: [0] = bl entries, [1] = bh entries
+  float dx[TM];                    // q8_K scales
 };
 
 __device__ __forceinline__ v16i mfma_k32(v4i a, v4i b, v16i c) {
@@ -70,15 +71,21 @@ __device__ __forceinline__ uint32_t bytes_times(uint32_t v, uint32_t s) {
 }
 
 __device__ __forceinline__ v4i lds_v4(const uint8_t* p) { return *reinterpret_cast<const v4i*>(p); }
+// A fragment of a lane whose tile row may lie beyond the staged rows (zero).
+__device__ __forceinline__ v4i lda(const uint8_t* p, bool arow) {
+  const v4i z = {0, 0, 0, 0};
+  return arow ? lds_v4(p) : z;
+}
 
 // Token row m of the lane's results for value r.
 __device__ __forceinline__ int out_row(int r, int g) { return 8 * (r >> 2) + 4 * g + (r & 3); }
 
-// fp64 combine over the lane's 16 results: value r = 4q+i is tile row
-// 8q + 4g + i, whose scale is dxs[8q+4g+i]; groups of 4 rows past the tile's
-// n rows are skipped (uniform over the wave).
+// fp64 combine over the lane's results: value r = 4q+i is tile row 8q + 4g + i,
+// whose scale is dxs[8q+4g+i]; only the first NQ groups of 8 rows exist in the
+// stage (NQ = 4 for 32-row tiles, 1 for 8-row tiles) and groups past the
+// tile's n rows are skipped (uniform over the wave).
 #define MOEQ_COMBINE(STMT)                                                            \
-  _Pragma("unroll") for (int q = 0; q < 4; ++q) {                                    \
+  _Pragma("unroll") for (int q = 0; q < NQ; ++q) {                                   \
     if (8 * q < n) {                                                                  \
       const float4 dx4 = *reinterpret_cast<const float4*>(dxs + 8 * q + 4 * g);       \
       const float dxa[4] = {dx4.x, dx4.y, dx4.z, dx4.w};                             \
@@ -111,8 +118,9 @@ template <> struct Mf<FQ4K> {
     return w;
   }
   // MFMA 2p+s: lane half g holds sub-block 2p+g, nibble s (elements 64p+32g+16s .. +15).
-  __device__ static void mac(const Wt& w, int g, const uint8_t* qrow, const v4i abs, const float* dxs, int n,
-                             double acc[16]) {
+  template <int NQ>
+  __device__ static void mac(const Wt& w, int g, const uint8_t* qrow, bool arow, const v4i abs, const float* dxs,
+                             int n, double* acc) {
     const uint64_t lo = (uint64_t)w.h.y | ((uint64_t)w.h.z << 32);
     const uint64_t hi = (uint64_t)w.h.z | ((uint64_t)w.h.w << 32);
     v16i plo = {0}, phi = {0};
@@ -129,7 +137,7 @@ template <> struct Mf<FQ4K> {
           bl[i] = (int)bytes_times(q, sc & 7);
           bh[i] = (int)bytes_times(q, sc >> 3);
         }
-        const v4i a = lds_v4(qrow + 64 * p + 32 * g + 16 * s);
+        const v4i a = lda(qrow + 64 * p + 32 * g + 16 * s, arow);
         plo = mfma_k32(a, bl, plo);
         phi = mfma_k32(a, bh, phi);
       }
@@ -164,8 +172,9 @@ template <> struct Mf<FQ2K> {
     return w;
   }
   // MFMA p: lane half g holds sub-block 2p+g (elements 32p+16g .. +15).
-  __device__ static void mac(const Wt& w, int g, const uint8_t* qrow, const v4i abs, const float* dxs, int n,
-                             double acc[16]) {
+  template <int NQ>
+  __device__ static void mac(const Wt& w, int g, const uint8_t* qrow, bool arow, const v4i abs, const float* dxs,
+                             int n, double* acc) {
     const uint32_t sm[4] = {w.sm.x, w.sm.y, w.sm.z, w.sm.w};
     v16i P = {0};
 #pragma unroll
@@ -176,7 +185,7 @@ template <> struct Mf<FQ2K> {
       v4i b;
 #pragma unroll
       for (int i = 0; i < 4; ++i) b[i] = (int)bytes_times((c[i] >> (2 * s)) & 0x03030303u, sc);
-      P = mfma_k32(lds_v4(qrow + 32 * p + 16 * g), b, P);
+      P = mfma_k32(lda(qrow + 32 * p + 16 * g, arow), b, P);
     }
     v4i bm;
 #pragma unroll
@@ -211,8 +220,9 @@ template <> struct Mf<FQ6K> {
   // One 16-deep MFMA per sub-block jj: lane half g holds elements 16jj+8g .. +7
   // (low nibbles: word i = 2g+t of chunk jj/2, nibble jj%2; high pairs: word
   // jj%2 of chunk jj/2 in the high-pair plane, bits 2i).
-  __device__ static void mac(const Wt& w, int g, const uint8_t* qrow, const v4i abs, const float* dxs, int n,
-                             double acc[16]) {
+  template <int NQ>
+  __device__ static void mac(const Wt& w, int g, const uint8_t* qrow, bool arow, const v4i abs, const float* dxs,
+                             int n, double* acc) {
     const uint32_t scw[4] = {w.sc.x, w.sc.y, w.sc.z, w.sc.w};
     int S1[16];
 #pragma unroll
@@ -231,7 +241,7 @@ template <> struct Mf<FQ6K> {
         q[t] = ((l2[t] >> (4 * s)) & 0x0F0F0F0Fu) | (((xs >> (2 * i)) & 0x03030303u) << 4);
       }
       const long b = (long)(((uint64_t)q[1] << 32) | q[0]);
-      const long a = *reinterpret_cast<const long*>(qrow + 16 * jj + 8 * g);
+      const long a = arow ? *reinterpret_cast<const long*>(qrow + 16 * jj + 8 * g) : 0l;
       const v16i P = mfma_k16(a, b, z16);
       const int sc = (int)(int8_t)((scw[jj >> 2] >> (8 * (jj & 3))) & 0xFF);
 #pragma unroll
@@ -256,14 +266,15 @@ template <> struct Mf<FQ80> {
     w.d = *reinterpret_cast<const uint4*>(W + align256(nsb * 256) + sbi * 16);
     return w;
   }
-  __device__ static void mac(const Wt& w, int g, const uint8_t* qrow, const v4i, const float* dxs, int n,
-                             double acc[16]) {
+  template <int NQ>
+  __device__ static void mac(const Wt& w, int g, const uint8_t* qrow, bool arow, const v4i, const float* dxs,
+                             int n, double* acc) {
     const uint32_t dw[4] = {w.d.x, w.d.y, w.d.z, w.d.w};
     const v16i z16 = {0};
 #pragma unroll
     for (int b = 0; b < 8; ++b) {
       const v4i bq = {(int)w.q[b].x, (int)w.q[b].y, (int)w.q[b].z, (int)w.q[b].w};
-      const v16i P = mfma_k32(lds_v4(qrow + 32 * b + 16 * g), bq, z16);
+      const v16i P = mfma_k32(lda(qrow + 32 * b + 16 * g, arow), bq, z16);
       const double db = half_bits_to_float(dw[b >> 1] >> (16 * (b & 1)));
       MOEQ_COMBINE(acc[r] += (dx * db) * (double)P[r])
     }
@@ -292,8 +303,8 @@ __device__ __forceinline__ StageRegs stage_load(const uint8_t* srow, int64_t sb,
   for (int i = 0; i < 8; ++i) r.bs[i] = (NBSP > 0 && blk != nullptr && piece == 1) ? ld_u32(blk + 260 + 4 * i) : 0u;
   return r;
 }
-template <int NBSP>
-__device__ __forceinline__ void stage_store(StageLds& L, const StageRegs& r, int m, int piece) {
+template <int NBSP, int TM>
+__device__ __forceinline__ void stage_store(StageLds<TM>& L, const StageRegs& r, int m, int piece) {
   *reinterpret_cast<uint4*>(&L.qs[m][16 * piece]) = make_uint4(r.q[0], r.q[1], r.q[2], r.q[3]);
   if (piece == 0) L.dx[m] = r.d;
   if (NBSP > 0 && piece == 1) {
@@ -344,29 +355,33 @@ __device__ __forceinline__ void quantize_row_lds(const float* hrow, uint8_t* __r
 //   the block (one q8_K block per tile row) into hq.
 // MODE 1 (down): A = q8_K(h) rows of the tile's pairs, W0 = down; epilogue
 //   yp[row] = fl32(gate weight * y).
-// RES: K has at most kResBlocks 256-blocks, so the whole activation tile is
-//   staged in LDS once and the k-loop runs without barriers; otherwise the
-//   blocks stream through a double-buffered stage (one barrier per block).
+// TM: activation rows a tile stages (32; or 8 for experts with at most 8 rows,
+//   whose MFMA rows 8..31 are zero and whose combine covers only 8 rows).
+// RES: the whole activation tile fits in LDS (K up to kRes(TM) 256-blocks), so
+//   the k-loop runs without barriers; otherwise the blocks stream through a
+//   double-buffered stage (one barrier per block).
 // A workgroup covers `rb` consecutive 256-row blocks of its tile (grid.y =
 // ceil(blocks / rb)), so the staging and start-up are paid once per rb blocks;
 // the weight loads of the next (row block, 256-block, matrix) unit are always
 // in flight while the current unit's MFMAs run.
-constexpr int kResBlocks = 8;
+__host__ __device__ constexpr int kRes(int TM) { return TM == 32 ? 8 : 16; }
 
-template <int FMT, int MODE, bool RES>
-__global__ __launch_bounds__(512) void k_mfma(MfmaArgs a) {
+template <int FMT, int MODE, bool RES, int TM>
+__device__ __forceinline__ void mfma_tile(const MfmaArgs& a) {
   using M = Mf<FMT>;
-  __shared__ StageLds L[RES ? kResBlocks : 2];
-  __shared__ int64_t orow[kTileT];
-  __shared__ double owt[kTileT];
+  constexpr int NQ = TM / 8;
+  __shared__ StageLds<TM> L[RES ? kRes(TM) : 2];
+  __shared__ int64_t orow[TM];
+  __shared__ double owt[TM];
+  __shared__ const uint8_t* srows[TM];
 
   // ---- tile: expert (or the shared expert) and its rows t0 .. t0+n-1
   int e = -1, t0, n;
   int64_t list_off = 0;
   if (a.shared) {
-    t0 = (int)blockIdx.x * kTileT;
+    t0 = (int)blockIdx.x * TM;
     if (t0 >= a.T) return;
-    n = (int)((a.T - t0) < kTileT ? (a.T - t0) : kTileT);
+    n = (int)((a.T - t0) < TM ? (a.T - t0) : TM);
   } else {
     if ((int)blockIdx.x >= *a.count) return;
     const int4 tl = a.tiles[blockIdx.x];
@@ -398,65 +413,75 @@ __global__ __launch_bounds__(512) void k_mfma(MfmaArgs a) {
     }
   }
 
-  // ---- per-row bookkeeping and the staging thread's source row
+  // ---- per-row bookkeeping: source rows, output rows, gate weights
   const int tid = threadIdx.x, wave = tid >> 6, lane = lane_id(), g = lane >> 5;
-  const int ms = tid >> 4, piece = tid & 15;
-  const uint8_t* srow = nullptr;
-  if (ms < n) {
-    int64_t ridx;
-    if (a.shared) {
-      ridx = t0 + ms;
-    } else {
-      const int p = a.pairs[list_off + t0 + ms];
-      ridx = MODE == 0 ? p / a.k : p;
-    }
-    srow = a.src + ridx * a.src_stride;
-  }
-  if (tid < kTileT) {
-    int64_t orr = -1;
+  const bool arow = (lane & 31) < TM;                  // the lane's A row is staged
+  if (tid < TM) {
+    int64_t orr = -1, ridx = 0;
     double wt = 0.0;
+    const uint8_t* sr = nullptr;
     if (tid < n) {
       if (a.shared) {
+        ridx = t0 + tid;
         orr = MODE == 0 ? (int64_t)(t0 + tid) : a.T * a.k + t0 + tid;
         wt = a.shared_scale != nullptr ? (double)a.shared_scale[t0 + tid] : 1.0;
       } else {
         const int p = a.pairs[list_off + t0 + tid];
+        ridx = MODE == 0 ? p / a.k : p;
         orr = p;
         wt = MODE == 1 ? (double)a.topk_w[p] : 0.0;
       }
+      sr = a.src + ridx * a.src_stride;
     }
     orow[tid] = orr;
     owt[tid] = wt;
+    srows[tid] = sr;
   }
+  __syncthreads();
 
   const int64_t nbK = a.K / 256, nsb = a.N * nbK;
   const int64_t lrow = wave * 32 + (lane & 31);       // the lane's weight row inside a row block
   // first unit's weights, in flight during the staging
   typename M::Wt wn = M::load(W0, (size_t)nsb, (size_t)((rb0 * kMfRows + lrow) * nbK), g);
-  StageRegs sr;
+  // staging work item i: 256-block i / (16 TM), row (i / 16) % TM, 16-byte piece i % 16
   if constexpr (RES) {
-    for (int64_t sb0 = 0; sb0 < nbK; sb0 += 4) {
+    const int64_t items = nbK * TM * 16;
+    for (int64_t i0 = tid; i0 < items; i0 += 4 * 512) {
       StageRegs r4[4];
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        if (sb0 + j < nbK) r4[j] = stage_load<M::NBSP>(srow, sb0 + j, piece);
+      for (int j = 0; j < 4; ++j) {
+        const int64_t i = i0 + 512 * j;
+        if (i < items) r4[j] = stage_load<M::NBSP>(srows[(i >> 4) % TM], i / (16 * TM), (int)(i & 15));
+      }
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        if (sb0 + j < nbK) stage_store<M::NBSP>(L[sb0 + j], r4[j], ms, piece);
+      for (int j = 0; j < 4; ++j) {
+        const int64_t i = i0 + 512 * j;
+        if (i < items) stage_store<M::NBSP, TM>(L[i / (16 * TM)], r4[j], (int)((i >> 4) % TM), (int)(i & 15));
+      }
     }
     __syncthreads();
   }
+  const int arw = (lane & 31) < TM ? (lane & 31) : 0;
+  const int64_t nmat = MODE == 0 ? 2 : 1;
 
+  {
+  // One unit of weights ahead (few registers, so more waves per SIMD hide the
+  // latency); activation blocks resident in LDS, or streamed through a
+  // double-buffered stage when K exceeds the resident limit.
+  const int ms = (tid >> 4) % TM, piece = tid & 15;
+  const bool stager = tid < 16 * TM;
+  StageRegs sr;
   for (int64_t rb = rb0; rb < rb1; ++rb) {
     const int64_t wrow = rb * kMfRows + lrow;
-    double acc0[16], acc1[16];
+    double acc0[4 * NQ], acc1[4 * NQ];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) { acc0[r] = 0.0; acc1[r] = 0.0; }
-    if constexpr (!RES) sr = stage_load<M::NBSP>(srow, 0, piece);
+    for (int r = 0; r < 4 * NQ; ++r) { acc0[r] = 0.0; acc1[r] = 0.0; }
+    if constexpr (!RES)
+      if (stager) sr = stage_load<M::NBSP>(srows[ms], 0, piece);
     for (int64_t sb = 0; sb < nbK; ++sb) {
-      StageLds& S = RES ? L[sb] : L[sb & 1];
+      StageLds<TM>& S = RES ? L[sb] : L[sb & 1];
       if constexpr (!RES) {
-        stage_store<M::NBSP>(S, sr, ms, piece);
+        if (stager) stage_store<M::NBSP, TM>(S, sr, ms, piece);
         __syncthreads();
       }
       // next unit: up of this block (mode 0), else the next block, else the
@@ -472,74 +497,101 @@ __global__ __launch_bounds__(512) void k_mfma(MfmaArgs a) {
         wn = M::load(W0, (size_t)nsb, next_sbi, g);
       }
       if constexpr (!RES)
-        if (!last_k) sr = stage_load<M::NBSP>(srow, sb + 1, piece);
-      const uint8_t* qrow = &S.qs[lane & 31][0];
+        if (stager && !last_k) sr = stage_load<M::NBSP>(srows[ms], sb + 1, piece);
+      const uint8_t* qrow = &S.qs[arw][0];
       v4i abs = {0, 0, 0, 0};
-      if constexpr (M::NBSP > 0) abs = lds_v4(&S.bsp[lane & 31][g][0]);
-      M::mac(wc, g, qrow, abs, S.dx, n, acc0);
+      if constexpr (M::NBSP > 0) abs = lda(&S.bsp[arw][g][0], arow);
+      M::template mac<NQ>(wc, g, qrow, arow, abs, S.dx, n, acc0);
       if constexpr (MODE == 0) {
         wc = wn;
         if (more) wn = M::load(W0, (size_t)nsb, next_sbi, g);
-        M::mac(wc, g, qrow, abs, S.dx, n, acc1);
+        M::template mac<NQ>(wc, g, qrow, arow, abs, S.dx, n, acc1);
       }
     }
 
     if constexpr (MODE == 0) {
       // h = fl32(silu(g) u) -> LDS, then q8_K per tile row over this row block
-      __shared__ float hs[kTileT][kMfRows + 4];
+      __shared__ float hs[TM][kMfRows + 4];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) hs[out_row(r, g)][lrow] = (float)(silu64(acc0[r]) * acc1[r]);
+      for (int r = 0; r < 4 * NQ; ++r) hs[out_row(r, g)][lrow] = (float)(silu64(acc0[r]) * acc1[r]);
       __syncthreads();
       for (int m = wave; m < n; m += kMfWaves)
         quantize_row_lds(&hs[m][0], a.hq + orow[m] * a.hq_stride + rb * kQ8KBytes);
       __syncthreads();   // hs (and a streamed stage) is rewritten next
     } else {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
+      for (int r = 0; r < 4 * NQ; ++r) {
         const int m = out_row(r, g);
         if (m < n) a.yp[orow[m] * a.N + wrow] = (float)(owt[m] * acc0[r]);
       }
       if constexpr (!RES) __syncthreads();   // the streamed stage is rewritten next
     }
   }
+  }
 }
 
-// Tile list of the routed experts whose row count exceeds `thr`: (expert, first
-// row, rows, list offset), 32 rows per tile, experts in union order (absent
-// experts too: their down tiles write zero rows).  One workgroup; count =
-// number of tiles.
+// 32-row tiles take every register they can use (2 waves per SIMD); 8-row
+// tiles are held to 128 registers so two workgroups share a CU (4 waves per
+// SIMD), which hides the weight-load latency of these memory-bound tiles
+// (except Q6_K, whose per-sub-block scaling needs more registers).
+template <int FMT, int MODE, bool RES, int TM>
+__global__ __launch_bounds__(512) void k_mfma(MfmaArgs a) { mfma_tile<FMT, MODE, RES, TM>(a); }
+template <int FMT, int MODE, bool RES>
+__global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(4, 8))) void k_mfma_thin(
+    MfmaArgs a) {
+  mfma_tile<FMT, MODE, RES, 8>(a);
+}
+
+// Tile lists of the routed experts whose row count exceeds `thr`: experts
+// with at most kThinRows rows get one 8-row tile, the others 32-row tiles; a
+// tile is (expert, first row, rows, list offset), experts in union order
+// (absent experts too: their down tiles write zero rows).  One workgroup.
+constexpr int kThinRows = 8;
+
 __global__ __launch_bounds__(1024) void k_mfma_plan(const int32_t* __restrict__ active,
                                                     const int32_t* __restrict__ offsets, int thr, int max_tiles,
-                                                    int4* __restrict__ tiles, int32_t* __restrict__ count) {
-  __shared__ int part[1024];
+                                                    int4* __restrict__ tiles, int32_t* __restrict__ count,
+                                                    int4* __restrict__ thin, int32_t* __restrict__ thin_count) {
+  __shared__ int part[1024], tpart[1024];
   const int na = active[0];
   const int per = (na + 1023) / 1024;
   const int s0 = threadIdx.x * per;
-  int local = 0;
-  for (int i = 0; i < per; ++i) {
-    const int s = s0 + i;
-    if (s < na) {
-      const int e = active[1 + s];
-      const int ne = offsets[e + 1] - offsets[e];
-      if (ne > thr) local += (ne + kTileT - 1) / kTileT;
-    }
-  }
-  part[threadIdx.x] = local;
-  __syncthreads();
-  for (int o = 1; o < 1024; o <<= 1) {   // inclusive scan (Hillis-Steele)
-    const int v = threadIdx.x >= o ? part[threadIdx.x - o] : 0;
-    __syncthreads();
-    part[threadIdx.x] += v;
-    __syncthreads();
-  }
-  int base = part[threadIdx.x] - local;
-  if (threadIdx.x == 1023) *count = part[1023] < max_tiles ? part[1023] : max_tiles;
+  int local = 0, tlocal = 0;
   for (int i = 0; i < per; ++i) {
     const int s = s0 + i;
     if (s < na) {
       const int e = active[1 + s];
       const int ne = offsets[e + 1] - offsets[e];
       if (ne > thr) {
+        if (ne <= kThinRows) ++tlocal;
+        else local += (ne + kTileT - 1) / kTileT;
+      }
+    }
+  }
+  part[threadIdx.x] = local;
+  tpart[threadIdx.x] = tlocal;
+  __syncthreads();
+  for (int o = 1; o < 1024; o <<= 1) {   // inclusive scans (Hillis-Steele)
+    const int v = threadIdx.x >= o ? part[threadIdx.x - o] : 0;
+    const int tv = threadIdx.x >= o ? tpart[threadIdx.x - o] : 0;
+    __syncthreads();
+    part[threadIdx.x] += v;
+    tpart[threadIdx.x] += tv;
+    __syncthreads();
+  }
+  int base = part[threadIdx.x] - local, tbase = tpart[threadIdx.x] - tlocal;
+  if (threadIdx.x == 1023) {
+    *count = part[1023] < max_tiles ? part[1023] : max_tiles;
+    *thin_count = tpart[1023];
+  }
+  for (int i = 0; i < per; ++i) {
+    const int s = s0 + i;
+    if (s < na) {
+      const int e = active[1 + s];
+      const int ne = offsets[e + 1] - offsets[e];
+      if (ne > thr && ne <= kThinRows) {
+        thin[tbase++] = make_int4(e, 0, ne, offsets[e]);
+      } else if (ne > thr) {
         for (int t0 = 0; t0 < ne; t0 += kTileT) {
           if (base < max_tiles) tiles[base] = make_int4(e, t0, ne - t0 < kTileT ? ne - t0 : kTileT, offsets[e]);
           ++base;
@@ -550,19 +602,32 @@ __global__ __launch_bounds__(1024) void k_mfma_plan(const int32_t* __restrict__ 
 }
 
 int launch_mfma_plan(const int32_t* active, const int32_t* offsets, int thr, int max_tiles, int4* tiles,
-                     int32_t* count, hipStream_t s) {
-  hipLaunchKernelGGL(k_mfma_plan, dim3(1), dim3(1024), 0, s, active, offsets, thr, max_tiles, tiles, count);
+                     int32_t* count, int4* thin, int32_t* thin_count, hipStream_t s) {
+  hipLaunchKernelGGL(k_mfma_plan, dim3(1), dim3(1024), 0, s, active, offsets, thr, max_tiles, tiles, count, thin,
+                     thin_count);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
-int launch_mfma(int fmt, int mode, dim3 grid, const MfmaArgs& a, hipStream_t s) {
+int launch_mfma(int fmt, int mode, bool thin, dim3 grid, const MfmaArgs& a, hipStream_t s) {
   if (grid.x == 0 || grid.y == 0) return 0;
-  const bool res = a.K / 256 <= kResBlocks;
-#define MOEQ_MF(F)                                                                             \
-  if (mode == 0 && res) hipLaunchKernelGGL((k_mfma<F, 0, true>), grid, dim3(512), 0, s, a);    \
-  else if (mode == 0) hipLaunchKernelGGL((k_mfma<F, 0, false>), grid, dim3(512), 0, s, a);     \
-  else if (res) hipLaunchKernelGGL((k_mfma<F, 1, true>), grid, dim3(512), 0, s, a);            \
-  else hipLaunchKernelGGL((k_mfma<F, 1, false>), grid, dim3(512), 0, s, a);
+  const int64_t nbK = a.K / 256;
+#define MOEQ_MF1(F, MD, TM)                                                                             \
+  if (TM == 8 && F != FQ6K) {                                                                         \
+    if (nbK <= kRes(TM)) hipLaunchKernelGGL((k_mfma_thin<F, MD, true>), grid, dim3(512), 0, s, a);    \
+    else hipLaunchKernelGGL((k_mfma_thin<F, MD, false>), grid, dim3(512), 0, s, a);                   \
+  } else if (nbK <= kRes(TM)) {                                                                       \
+    hipLaunchKernelGGL((k_mfma<F, MD, true, TM>), grid, dim3(512), 0, s, a);                          \
+  } else {                                                                                            \
+    hipLaunchKernelGGL((k_mfma<F, MD, false, TM>), grid, dim3(512), 0, s, a);                         \
+  }
+#define MOEQ_MF(F)                                   \
+  if (mode == 0) {                                   \
+    if (thin) { MOEQ_MF1(F, 0, 8) }                  \
+    else { MOEQ_MF1(F, 0, 32) }                      \
+  } else {                                           \
+    if (thin) { MOEQ_MF1(F, 1, 8) }                  \
+    else { MOEQ_MF1(F, 1, 32) }                      \
+  }
   switch (fmt) {
     case FQ4K: MOEQ_MF(FQ4K) break;
     case FQ6K: MOEQ_MF(FQ6K) break;
@@ -571,6 +636,7 @@ int launch_mfma(int fmt, int mode, dim3 grid, const MfmaArgs& a, hipStream_t s) 
     default: return -2;
   }
 #undef MOEQ_MF
+#undef MOEQ_MF1
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 

@@ -123,8 +123,8 @@ int launch_gateup1(int fmt, int nper, int cpl, dim3 grid, const GateUpArgs& a, h
 int launch_down(int fmt, int tt, int cpl, dim3 grid, const DownArgs& a, hipStream_t s);
 int launch_down_rows1(int fmt, int cpl, dim3 grid, const DownArgs& a, hipStream_t s);
 int launch_mfma_plan(const int32_t* active, const int32_t* offsets, int thr, int max_tiles, int4* tiles,
-                     int32_t* count, hipStream_t s);
-int launch_mfma(int fmt, int mode, dim3 grid, const MfmaArgs& a, hipStream_t s);
+                     int32_t* count, int4* thin, int32_t* thin_count, hipStream_t s);
+int launch_mfma(int fmt, int mode, bool thin, dim3 grid, const MfmaArgs& a, hipStream_t s);
 int launch_combine(const float* yp, int64_t T, int64_t H, int k, int has_shared, float* y, int accumulate,
                    hipStream_t s);
 

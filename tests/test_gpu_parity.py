@@ -220,14 +220,23 @@ def test_layer_parity(name, fused, path):
             assert np.array_equal(run.hq_s[t, :nbs], r.hq[n, cfg.k, :nbs]), (name, t, "shared")
 
 
-def test_auto_equals_gemv_and_is_deterministic():
-    layer = layer_of("verify")
-    say("determinism verify")
+@pytest.mark.parametrize("name", ["tiny", "decode", "verify"])
+def test_auto_path_choice_and_determinism(name):
+    """AUTO runs one token on the dot-product kernels and more tokens on the
+    MFMA tiles: bit-identical to the forced path it picks, repeatable, and
+    the other path agrees on every q8_K(h) byte and on y within tolerance."""
+    layer = layer_of(name)
+    say("auto path", name)
     a = GpuRun(layer, path=moeq.PATH_AUTO)
-    b = GpuRun(layer, path=moeq.PATH_GEMV)
-    assert np.array_equal(a.yv, b.yv)
-    assert np.array_equal(a.hq_r, b.hq_r)
-    assert np.array_equal(a.ids, b.ids) and np.array_equal(a.pairs, b.pairs)
+    a2 = GpuRun(layer, path=moeq.PATH_AUTO)
+    picked = moeq.PATH_GEMV if layer.cfg.T == 1 else moeq.PATH_MFMA
+    other = moeq.PATH_MFMA if picked == moeq.PATH_GEMV else moeq.PATH_GEMV
+    b = GpuRun(layer, path=picked)
+    c = GpuRun(layer, path=other)
+    assert np.array_equal(a.yv, a2.yv) and np.array_equal(a.yv, b.yv)
+    assert np.array_equal(a.hq_r, b.hq_r) and np.array_equal(a.hq_r, c.hq_r)
+    assert np.array_equal(a.ids, c.ids) and np.array_equal(a.pairs, c.pairs)
+    check_y(a.yv, c.yv, name)
 
 
 @pytest.mark.parametrize("name", ["chunk16", "prefill"])
