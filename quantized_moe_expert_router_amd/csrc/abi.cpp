@@ -232,7 +232,7 @@ int ffn_enqueue(const moeq_ffn_desc* d, const void* x_q8K, const int32_t* topk_i
     a.xq = (const uint8_t*)x_q8K; a.offsets = expert_offsets; a.pairs = pairs; a.active = active;
     a.max_union = max_union;
     a.hbuf = (float*)(wsb + L.off_h); a.hstride = L.Fmax;
-    a.lpr = g.lpr; a.cpr = g.cpr; a.steps = std::max(1, 4 / g.rps);
+    a.lpr = g.lpr; a.cpr = g.cpr; a.steps = std::max(1, 2 / g.rps);
     a.gemv_max = thr;
     a.topk_ids = topk_ids; a.topk_w = topk_w; a.E = d->E;
     a.slots = (SlotRec*)(wsb + L.off_slots);
@@ -348,10 +348,12 @@ int ffn_enqueue(const moeq_ffn_desc* d, const void* x_q8K, const int32_t* topk_i
     if (sh && (rc = mfma_launch(0, true, d->T <= kThinT))) return rc;
   }
   // down and the weighted combine
-  if (one && (!sh || same_shape)) {
+  if (one && (!sh || same_shape) && (d->k + (sh ? 1 : 0)) * (d->F / 256) <= kLdsQ8Blocks) {
     LaneGeo g;
     DownArgs a = down_args(kModeBoth, d->fmt_down, d->F, &g);
-    dim3 grid((unsigned)((d->H + g.rps - 1) / g.rps));
+    a.steps = kDown1Steps;
+    const int rows_wg = g.rps * a.steps;
+    dim3 grid((unsigned)((d->H + rows_wg - 1) / rows_wg));
     return launch_down_rows1(d->fmt_down, g.cpl, grid, a, s);
   }
   if (gemv) {

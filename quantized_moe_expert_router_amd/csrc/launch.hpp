@@ -10,6 +10,12 @@ namespace moeq {
 // (the shared expert as one more slot when it has the routed shape and format).
 constexpr int kModeRouted = 0, kModeShared = 1, kModeBoth = 2;
 
+// One-token down kernel: q8_K(h) blocks of the k+1 slots staged in LDS (at most
+// 4 waves x kQ8PerWave blocks), output rows per workgroup.
+constexpr int kQ8PerWave = 9;
+constexpr int kLdsQ8Blocks = 4 * kQ8PerWave;
+constexpr int kDown1Steps = 1;
+
 // One token: what the down kernel needs per slot (slot k = shared expert),
 // written by the gate/up kernel.
 struct SlotRec {
