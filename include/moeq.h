@@ -70,6 +70,14 @@ typedef enum {
     MOEQ_SIGMOID_TOPK = 2    /* sigmoid of the k selected, divided by their sum */
 } moeq_gating;
 
+/*
+ * Which kernels compute the expert dot products.  GEMV: per-row integer dot
+ * products on the vector ALUs (the pages' decode path, Pulsar README,
+ * 'Fidelity notes').  MFMA: int8 matrix-core tiles (the pages' quantized
+ * tensor-core prefill, Pulsar README, DeepSeek-V4-Flash paragraph).  AUTO:
+ * GEMV for one token, MFMA for more.  Every path gives the same ids, lists and
+ * q8_K(h) bytes; y differs only by floating summation order.
+ */
 typedef enum { MOEQ_PATH_AUTO = 0, MOEQ_PATH_GEMV = 1, MOEQ_PATH_MFMA = 2 } moeq_path;
 
 /* Human-readable name of a status code (host, static string). */
@@ -172,8 +180,11 @@ size_t moeq_expert_ffn_workspace(const moeq_ffn_desc* d);
  *   y       fp32 [T, H]:  y[t] (=|+=) sum_slot topk_w[t,slot] * down_e(q8K(h))
  *                                    + shared_scale[t] * down_sh(q8K(h_sh))
  *           with h = fl32(silu(g) * u), g = gate_e . xhat, u = up_e . xhat;
- *           per-super-block integer dots combined in fp64, sums in fp64,
- *           y rounded to fp32 once.
+ *           per-super-block integer dots combined in fp64, sums in fp64.
+ *           One token: y is rounded to fp32 once.  More tokens: each
+ *           weighted pair term is rounded to fp32 when staged, then the k+1
+ *           terms of a token are summed in fp64 and rounded (about 1e-7
+ *           relative on y).
  * ws: moeq_expert_ffn_workspace bytes, 256-byte aligned; contents on entry
  * are ignored.
  */
