@@ -74,7 +74,8 @@ typedef enum {
  * Which kernels compute the expert dot products.  GEMV: per-row integer dot
  * products on the vector ALUs (the pages' decode path, Pulsar README,
  * 'Fidelity notes').  MFMA: int8 matrix-core tiles (the pages' quantized
- * tensor-core prefill, Pulsar README, DeepSeek-V4-Flash paragraph).  AUTO:
+ * tensor-core prefill, Pulsar README, 'What it does today', prefill
+ * paragraphs; Strata article, long-prompt section).  AUTO:
  * GEMV for one token, MFMA for more.  Every path gives the same ids, lists and
  * q8_K(h) bytes; y differs only by floating summation order.
  */

@@ -1,9 +1,11 @@
-// int8 MFMA grouped GEMM for experts with many rows (multi-token chunks:
-// verify unions and prefill).  The pages send such chunks to int8 matrix
-// cores instead of per-row dot products (Pulsar README, 'Verify' and
-// DeepSeek-V4-Flash paragraphs: quantized int8 tensor-core prefill; Strata
-// article, chunked prefill through quantized matmuls), while a single token
-// stays memory-bound on the dot-product path.
+// int8 MFMA grouped GEMM for the experts of multi-token calls (verify unions,
+// chunks, prefill).  The pages run multi-token work on int8 matrix units with
+// the weights kept quantized instead of per-row dot products (Pulsar README,
+// 'What it does today', prefill paragraphs: dense int8 GEMM plus a grouped
+// MoE that unpacks each expert super-block once per chunk; Strata article,
+// long-prompt section: quantized MMQ expert kernels beat expanding to FP16;
+// the MoE verify unions already take the int8-MMA path: Pulsar README,
+// ThinkingCap paragraph), while a single token stays on the dot-product path.
 //
 // Tile = one expert x 32 of its rows (tokens, or pairs for down) x 256 weight
 // rows: a 512-thread workgroup of 8 waves, each wave 32 weight rows.  The
