@@ -30,6 +30,39 @@ __device__ __forceinline__ uint32_t ld_u16(const uint8_t* p) {
   return *reinterpret_cast<const uint16_t*>(p);
 }
 
+// Accesses through the global address space (global_load / global_store).
+// Pointers read from tables or argument structs are generic to the compiler,
+// and generic (flat) accesses also count against the LDS wait counter: a wait
+// for an LDS read would then also wait for every weight load in flight.
+#define MOEQ_GLOBAL __attribute__((address_space(1)))
+typedef unsigned int g_u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int g_u32x2 __attribute__((ext_vector_type(2)));
+typedef float g_f32x4 __attribute__((ext_vector_type(4)));
+// 16-byte aligned
+__device__ __forceinline__ uint4 gld_u4(const void* p) {
+  const g_u32x4 v = *(const MOEQ_GLOBAL g_u32x4*)p;
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+// 8-byte aligned
+__device__ __forceinline__ uint2 gld_u2(const void* p) {
+  const g_u32x2 v = *(const MOEQ_GLOBAL g_u32x2*)p;
+  return make_uint2(v.x, v.y);
+}
+__device__ __forceinline__ float4 gld_f4(const void* p) {
+  const g_f32x4 v = *(const MOEQ_GLOBAL g_f32x4*)p;
+  return make_float4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ uint32_t gld_u32(const void* p) { return *(const MOEQ_GLOBAL uint32_t*)p; }
+__device__ __forceinline__ uint32_t gld_u16(const void* p) { return *(const MOEQ_GLOBAL uint16_t*)p; }
+__device__ __forceinline__ float gld_f32(const void* p) { return *(const MOEQ_GLOBAL float*)p; }
+__device__ __forceinline__ double gld_f64(const void* p) { return *(const MOEQ_GLOBAL double*)p; }
+__device__ __forceinline__ uint64_t gld_u64(const void* p) { return *(const MOEQ_GLOBAL uint64_t*)p; }
+__device__ __forceinline__ int32_t gld_i32(const void* p) { return *(const MOEQ_GLOBAL int32_t*)p; }
+__device__ __forceinline__ void gst_f32(void* p, float v) { *(MOEQ_GLOBAL float*)p = v; }
+__device__ __forceinline__ void gst_u32(void* p, uint32_t v) { *(MOEQ_GLOBAL uint32_t*)p = v; }
+__device__ __forceinline__ void gst_i32(void* p, int32_t v) { *(MOEQ_GLOBAL int32_t*)p = v; }
+__device__ __forceinline__ void gst_i16(void* p, int16_t v) { *(MOEQ_GLOBAL int16_t*)p = v; }
+
 // ---- DPP cross-lane moves (register to register, no LDS round trip).
 // Control codes of the gfx9 DPP encoding.
 constexpr int kDppXor1 = 0xB1;       // quad_perm [1,0,3,2]
@@ -167,7 +200,7 @@ __device__ __forceinline__ void quantize_block_wave(const float* __restrict__ x,
   const int lane = lane_id();
   const int64_t nb = cols / 256, row = g / nb, b = g % nb;
   const float* xb = x + row * cols + b * 256 + 4 * lane;
-  const float4 v = *reinterpret_cast<const float4*>(xb);
+  const float4 v = gld_f4(xb);
   float amax = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
   amax = wave_max_f(amax);
   uint8_t* o = out + g * kQ8KBytes;
@@ -175,13 +208,13 @@ __device__ __forceinline__ void quantize_block_wave(const float* __restrict__ x,
   const bool zero = amax == 0.0f || __builtin_isinf(id);
   int q0 = 0, q1 = 0, q2 = 0, q3 = 0;
   if (!zero) { q0 = q8_code(v.x, id); q1 = q8_code(v.y, id); q2 = q8_code(v.z, id); q3 = q8_code(v.w, id); }
-  *reinterpret_cast<uint32_t*>(o + 4 + 4 * lane) =
-      (uint32_t)(q0 & 255) | ((uint32_t)(q1 & 255) << 8) | ((uint32_t)(q2 & 255) << 16) | ((uint32_t)(q3 & 255) << 24);
+  gst_u32(o + 4 + 4 * lane,
+          (uint32_t)(q0 & 255) | ((uint32_t)(q1 & 255) << 8) | ((uint32_t)(q2 & 255) << 16) | ((uint32_t)(q3 & 255) << 24));
   int s = q0 + q1 + q2 + q3;
   s += dpp_all_i<kDppXor1>(s);
   s += dpp_all_i<kDppXor2>(s);
-  if ((lane & 3) == 0) *reinterpret_cast<int16_t*>(o + 260 + 2 * (lane >> 2)) = (int16_t)s;
-  if (lane == 0) *reinterpret_cast<float*>(o) = zero ? 0.0f : __fdiv_rn(amax, 127.0f);
+  if ((lane & 3) == 0) gst_i16(o + 260 + 2 * (lane >> 2), (int16_t)s);
+  if (lane == 0) gst_f32(o, zero ? 0.0f : __fdiv_rn(amax, 127.0f));
 }
 
 __host__ __device__ constexpr size_t align256(size_t n) { return (n + 255) & ~size_t(255); }

@@ -17,9 +17,7 @@
 //          writes w * (W_d h^) in fp64 to a per-pair staging row, counts its
 //          arrival on its row block, and the last arrival sums the pairs of
 //          every token in slot order (then the shared expert) and rounds y.
-#include "formats.hpp"
-#include "launch.hpp"
-#include "topk.hpp"
+#include "one_token.hpp"
 
 namespace moeq {
 
@@ -159,178 +157,10 @@ __global__ __launch_bounds__(256) void k_gateup(GateUpArgs a) {
   }
 }
 
-// The routing outputs of one token, written by one wave that holds the
-// winners in rank order (lane s < k: expert my_i, weight my_w): ids and
-// weights, then the lists (pairs ordered by expert; for one token the pair of
-// slot s is s) and the expert union.
-__device__ void write_routing_t1(const GateUpArgs& a, int my_i, float my_w) {
-  const int lane = lane_id(), k = a.k;
-  int pos = 0;
-  for (int j = 0; j < k; ++j) {
-    const int idj = __builtin_amdgcn_readlane(my_i, j);
-    pos += (lane < k && idj < my_i) ? 1 : 0;
-  }
-  if (lane < k) {
-    a.ids_out[lane] = my_i;
-    a.w_out[lane] = my_w;
-    a.active_out[1 + pos] = my_i;
-    a.pairs_out[pos] = lane;
-  }
-  if (lane == 0) a.active_out[0] = k;
-  for (int64_t e0 = 0; e0 <= a.E; e0 += kWave) {
-    const int64_t e = e0 + lane;
-    int c = 0;
-    for (int j = 0; j < k; ++j) c += __builtin_amdgcn_readlane(my_i, j) < e ? 1 : 0;
-    if (e <= a.E) a.offsets_out[e] = c;
-  }
-}
-
-// One token.  Slot u is the u-th ranked expert (u == k: the shared expert);
-// with NPER > 0 the workgroup routes inline from the logits (every wave runs
-// the same register top-k, so all workgroups agree), otherwise it reads
-// topk_ids.  The token's activation chunks are loaded before anything that
-// depends on the routing.
+// One token: gate/up (routing inline from the logits when NPER > 0).
 template <int FMT, int CPL, int NPER>
 __global__ __launch_bounds__(256) void k_gateup1(GateUpArgs a) {
-  using L = Fmt<FMT>;
-  constexpr int UNR = 4;
-  const int wave = threadIdx.x >> 6, lane = lane_id();
-  const int lpr = a.lpr, rps = kWave / lpr, rig = lane / lpr, lir = lane % lpr;
-  const int64_t nb = a.H / 256, nsb = a.F * nb;
-  int xw[CPL][L::XDW], bs[CPL][L::NBS];
-  double dx[CPL];
-#pragma unroll
-  for (int c = 0; c < CPL; ++c) {
-    const int ch = lir + lpr * c;
-    if (ch < a.cpr) {
-      load_x_chunk<FMT>(a.xq, ch, xw[c], bs[c], dx[c]);
-    } else {
-#pragma unroll
-      for (int q = 0; q < L::XDW; ++q) xw[c][q] = 0;
-#pragma unroll
-      for (int q = 0; q < L::NBS; ++q) bs[c][q] = 0;
-      dx[c] = 0.0;
-    }
-  }
-  const int slot = blockIdx.y;
-  const bool shared = a.mode == kModeShared || (a.mode == kModeBoth && slot == a.k);
-  const uint8_t *Wg, *Wu;
-  int64_t prow;
-  const void* Wd;
-  double wt;
-  if (shared) {
-    Wg = a.sh_gate; Wu = a.sh_up; prow = a.k;
-    Wd = a.sh_down_rec;
-    wt = a.shared_scale ? (double)a.shared_scale[0] : 1.0;
-  } else {
-    int e;
-    if constexpr (NPER > 0) {
-      // One wave routes for the workgroup (the top-k from the logits, the
-      // same in every workgroup); the others wait for its result in LDS.
-      __shared__ uint64_t r_ptr[3];
-      __shared__ double r_wt;
-      if (wave == 0) {
-        uint64_t pg[NPER <= 8 ? NPER : 1], pu[NPER <= 8 ? NPER : 1], pd[NPER <= 8 ? NPER : 1];
-        if constexpr (NPER <= 8) {
-          // candidates' matrix pointers load with the logits; the winner's
-          // owner lane hands them over (no dependent table load)
-#pragma unroll
-          for (int i = 0; i < NPER; ++i) {
-            const int64_t ec = lane + (int64_t)kWave * i;
-            pg[i] = ec < a.E ? (uint64_t)a.gate[ec] : 0;
-            pu[i] = ec < a.E ? (uint64_t)a.up[ec] : 0;
-            pd[i] = ec < a.E ? (uint64_t)a.down[ec] : 0;
-          }
-        }
-        int my_i;
-        float my_w;
-        topk_wave_regs<NPER>(a.logits, a.E, a.k, a.gating, a.scale, my_i, my_w);
-        if (blockIdx.x == 0 && slot == 0) write_routing_t1(a, my_i, my_w);
-        e = __builtin_amdgcn_readlane(my_i, slot);
-        const float wsel = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, my_w), slot));
-        uint64_t g0, u0, d0;
-        if constexpr (NPER <= 8) {
-          const int owner = e & (kWave - 1), idx = e / kWave;
-          g0 = pg[0]; u0 = pu[0]; d0 = pd[0];
-#pragma unroll
-          for (int i = 1; i < NPER; ++i) {
-            g0 = idx == i ? pg[i] : g0;
-            u0 = idx == i ? pu[i] : u0;
-            d0 = idx == i ? pd[i] : d0;
-          }
-          auto bcast = [&](uint64_t v) {
-            const uint32_t lo = __builtin_amdgcn_readlane((int)(uint32_t)v, owner);
-            const uint32_t hi = __builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), owner);
-            return (uint64_t)lo | ((uint64_t)hi << 32);
-          };
-          g0 = bcast(g0); u0 = bcast(u0); d0 = bcast(d0);
-        } else {
-          g0 = (uint64_t)a.gate[e]; u0 = (uint64_t)a.up[e]; d0 = (uint64_t)a.down[e];
-        }
-        if (lane == 0) {
-          r_ptr[0] = g0; r_ptr[1] = u0; r_ptr[2] = d0;
-          r_wt = (double)wsel;
-        }
-      }
-      __syncthreads();
-      Wg = (const uint8_t*)r_ptr[0];
-      Wu = (const uint8_t*)r_ptr[1];
-      Wd = (const void*)r_ptr[2];
-      wt = r_wt;
-    } else {
-      e = a.topk_ids[slot];
-      wt = (double)a.topk_w[slot];
-      Wg = (const uint8_t*)a.gate[e];
-      Wu = (const uint8_t*)a.up[e];
-      Wd = a.down[e];
-    }
-    if (Wd == nullptr || Wu == nullptr) Wg = nullptr;
-    prow = slot;
-  }
-  if (a.slots != nullptr && blockIdx.x == 0 && threadIdx.x == 0) {
-    a.slots[shared ? a.k : slot].wd = (Wg == nullptr || Wu == nullptr) ? nullptr : Wd;
-    a.slots[shared ? a.k : slot].wt = wt;
-  }
-  if (Wg == nullptr || Wu == nullptr) return;   // not resident: its pair adds nothing
-  const int64_t row0 = (int64_t)blockIdx.x * (4 * a.steps * rps) + (int64_t)wave * a.steps * rps + rig;
-  for (int st = 0; st < a.steps; st += UNR) {
-    typename L::W wg[UNR][CPL], wu[UNR][CPL];
-    int64_t row[UNR];
-    bool ok[UNR][CPL];
-#pragma unroll
-    for (int u = 0; u < UNR; ++u) {
-      row[u] = row0 + (int64_t)(st + u) * rps;
-      const bool rv = (st + u) < a.steps && row[u] < a.F;
-#pragma unroll
-      for (int c = 0; c < CPL; ++c) {
-        const int ch = lir + lpr * c;
-        ok[u][c] = rv && ch < a.cpr;
-        if (ok[u][c]) {
-          const size_t sbi = (size_t)(row[u] * nb + ch / L::CPS);
-          wg[u][c] = L::load(Wg, (size_t)nsb, sbi, ch % L::CPS);
-          wu[u][c] = L::load(Wu, (size_t)nsb, sbi, ch % L::CPS);
-        }
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < UNR; ++u) {
-      double ag = 0.0, au = 0.0;
-#pragma unroll
-      for (int c = 0; c < CPL; ++c) {
-        if (!ok[u][c]) continue;
-        const int j = (lir + lpr * c) % L::CPS;
-        int is[L::SPC];
-        L::isums(wg[u][c], xw[c], bs[c], is);
-        ag += L::term(wg[u][c], j, is, bs[c], dx[c]);
-        L::isums(wu[u][c], xw[c], bs[c], is);
-        au += L::term(wu[u][c], j, is, bs[c], dx[c]);
-      }
-      const double g = group_sum_dpp(ag, lpr);
-      const double uu = group_sum_dpp(au, lpr);
-      if (lir == lpr - 1 && (st + u) < a.steps && row[u] < a.F)
-        a.hbuf[prow * a.hstride + row[u]] = (float)(silu64(g) * uu);
-    }
-  }
+  gateup1_body<FMT, CPL, NPER>(a, blockIdx.x, blockIdx.y);
 }
 
 // q8_K of one lane chunk of h (WPC fp32 values in registers), identical to
@@ -493,162 +323,11 @@ __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ yp, i
   y[idx] = accumulate ? (float)((double)y[idx] + acc) : (float)acc;
 }
 
-// One token (decode).  A workgroup owns `steps` wave steps of rps output rows
-// for every selected expert and the shared one.  It first turns the k+1 fp32
-// h rows into q8_K blocks in LDS once (a pure function of h, identical in
-// every workgroup; workgroup 0 also stores them as the q8_K(h) view), while
-// the weight loads of the first round of slots are already in flight.  Waves
-// then take slots round-robin, read their activation chunks from LDS, and
-// leave w * (W_d h^) per (slot rank, row) in LDS; the sum over slots in rank
-// order, then the shared expert, happens in the workgroup.  No data crosses
-// workgroups.
-constexpr int kLdsQ8 = 304;   // LDS q8_K block: f32 d | 12 pad | i8 q[256] | i16 bsums[16]
-
-template <int FMT>
-__device__ __forceinline__ void load_x_chunk_lds(const uint8_t* xrow, int c, int* xw, int* bs, double& dx) {
-  using L = Fmt<FMT>;
-  const int e0 = c * L::WPC;
-  const uint8_t* blk = xrow + (e0 >> 8) * kLdsQ8;
-  const int o = e0 & 255;
-  dx = (double)*reinterpret_cast<const float*>(blk);
-#pragma unroll
-  for (int i = 0; i < L::XDW; i += 4) {
-    const uint4 v = *reinterpret_cast<const uint4*>(blk + 16 + o + 4 * i);
-    xw[i] = (int)v.x; xw[i + 1] = (int)v.y; xw[i + 2] = (int)v.z; xw[i + 3] = (int)v.w;
-  }
-#pragma unroll
-  for (int i = 0; i < L::NBS; ++i) bs[i] = (int)(int16_t)ld_u16(blk + 272 + 2 * ((o >> 4) + i));
-}
-
+// One token (decode): down rows and the weighted combine, slot table from
+// the gate/up kernel.
 template <int FMT, int CPL>
 __global__ __launch_bounds__(256) void k_down_rows1(DownArgs a) {
-  using L = Fmt<FMT>;
-  constexpr int kMaxSlots = 33, kMaxRows = 64;
-  constexpr int SG = CPL == 1 ? 3 : 1;      // slots whose loads are in flight together
-  extern __shared__ __align__(16) uint8_t hq_lds[];   // [n_slots][nbF] q8_K blocks
-  __shared__ double yps[kMaxSlots][kMaxRows];
-  __shared__ const uint8_t* swd[kMaxSlots];
-  __shared__ double swt[kMaxSlots];
-  const int wave = threadIdx.x >> 6, lane = lane_id();
-  const int lpr = a.lpr, rps = kWave / lpr, rig = lane / lpr, lir = lane % lpr;
-  const int64_t nb = a.F / 256, nsb = a.H * nb;
-  const int rows_wg = rps * kDown1Steps;
-  const int64_t row_base = (int64_t)blockIdx.x * rows_wg;
-  const int n_routed = a.k;
-  const int n_slots = n_routed + a.has_shared;
-  const int nblk = n_slots * (int)nb;       // at most kLdsQ8Blocks (checked by the host)
-
-  // this wave's q8_K(h) blocks (wave, wave+4, ...): fp32 loads first
-  float4 hv[kQ8PerWave];
-#pragma unroll
-  for (int j = 0; j < kQ8PerWave; ++j) {
-    const int b = wave + 4 * j;
-    if (b < nblk) {
-      const int s = b / (int)nb, bb = b % (int)nb;
-      hv[j] = reinterpret_cast<const float4*>(a.hbuf + (int64_t)s * a.hstride + bb * 256)[lane];
-    }
-  }
-  // the gate/up kernel left each slot's down matrix and weight in the slot table
-  if (threadIdx.x < n_slots) {
-    swd[threadIdx.x] = (const uint8_t*)a.slots[threadIdx.x].wd;
-    swt[threadIdx.x] = a.slots[threadIdx.x].wt;
-  }
-  __syncthreads();
-
-  // weight loads of one round: SG slots of this wave, every wave step of the
-  // workgroup's rows (all in flight together)
-  constexpr int ST = kDown1Steps;
-  typename L::W w[ST][SG][CPL];
-  bool okk[ST][SG][CPL];
-  auto issue = [&](int s0) {
-#pragma unroll
-    for (int st = 0; st < ST; ++st) {
-      const int64_t row = row_base + (int64_t)st * rps + rig;
-#pragma unroll
-      for (int j = 0; j < SG; ++j) {
-        const int s = s0 + 4 * j;
-        const uint8_t* W = s < n_slots ? swd[s] : nullptr;
-#pragma unroll
-        for (int c = 0; c < CPL; ++c) {
-          const int ch = lir + lpr * c;
-          okk[st][j][c] = W != nullptr && ch < a.cpr && row < a.H;
-          if (okk[st][j][c]) w[st][j][c] = L::load(W, (size_t)nsb, (size_t)(row * nb + ch / L::CPS), ch % L::CPS);
-        }
-      }
-    }
-  };
-  issue(wave);                               // first round in flight during the q8_K(h) work
-
-  // q8_K(h) into LDS (workgroup 0 also stores the q8_K(h) view)
-#pragma unroll
-  for (int j = 0; j < kQ8PerWave; ++j) {
-    const int b = wave + 4 * j;
-    if (b < nblk) {
-      const int s = b / (int)nb, bb = b % (int)nb;
-      uint8_t* o = hq_lds + b * kLdsQ8;
-      float amax = fmaxf(fmaxf(fabsf(hv[j].x), fabsf(hv[j].y)), fmaxf(fabsf(hv[j].z), fabsf(hv[j].w)));
-      amax = wave_max_f(amax);
-      const float id = amax == 0.0f ? 0.0f : __fdiv_rn(127.0f, amax);
-      const bool zero = amax == 0.0f || __builtin_isinf(id);
-      int q0 = 0, q1 = 0, q2 = 0, q3 = 0;
-      if (!zero) {
-        q0 = q8_code(hv[j].x, id); q1 = q8_code(hv[j].y, id);
-        q2 = q8_code(hv[j].z, id); q3 = q8_code(hv[j].w, id);
-      }
-      const uint32_t qw = (uint32_t)(q0 & 255) | ((uint32_t)(q1 & 255) << 8) | ((uint32_t)(q2 & 255) << 16) |
-                          ((uint32_t)(q3 & 255) << 24);
-      int sum4 = q0 + q1 + q2 + q3;
-      sum4 += dpp_all_i<kDppXor1>(sum4);
-      sum4 += dpp_all_i<kDppXor2>(sum4);
-      const float dq = zero ? 0.0f : __fdiv_rn(amax, 127.0f);
-      *reinterpret_cast<uint32_t*>(o + 16 + 4 * lane) = qw;
-      if ((lane & 3) == 0) *reinterpret_cast<int16_t*>(o + 272 + 2 * (lane >> 2)) = (int16_t)sum4;
-      if (lane == 0) *reinterpret_cast<float*>(o) = dq;
-      uint8_t* view = s >= n_routed ? a.hq_sh : a.hq;
-      if (blockIdx.x == 0 && view != nullptr && swd[s] != nullptr) {
-        uint8_t* gq = view + (s >= n_routed ? 0 : (int64_t)s) * a.hq_stride + bb * kQ8KBytes;
-        *reinterpret_cast<uint32_t*>(gq + 4 + 4 * lane) = qw;
-        if ((lane & 3) == 0) *reinterpret_cast<int16_t*>(gq + 260 + 2 * (lane >> 2)) = (int16_t)sum4;
-        if (lane == 0) *reinterpret_cast<float*>(gq) = dq;
-      }
-    }
-  }
-  __syncthreads();
-
-  for (int s0 = wave; s0 < n_slots; s0 += 4 * SG) {
-    if (s0 != wave) issue(s0);
-#pragma unroll
-    for (int st = 0; st < ST; ++st) {
-#pragma unroll
-      for (int j = 0; j < SG; ++j) {
-        const int s = s0 + 4 * j;
-        double ay = 0.0;
-#pragma unroll
-        for (int c = 0; c < CPL; ++c) {
-          if (!okk[st][j][c]) continue;
-          const int ch = lir + lpr * c;
-          int xw[L::XDW], bs[L::NBS];
-          double dx;
-          load_x_chunk_lds<FMT>(hq_lds + (int64_t)s * nb * kLdsQ8, ch, xw, bs, dx);
-          int is[L::SPC];
-          L::isums(w[st][j][c], xw, bs, is);
-          ay += L::term(w[st][j][c], ch % L::CPS, is, bs, dx);
-        }
-        const double yv = group_sum_dpp(ay, lpr);
-        if (s < n_slots && lir == lpr - 1) yps[s][st * rps + rig] = swt[s] * yv;
-      }
-    }
-  }
-  __syncthreads();
-  if (threadIdx.x < rows_wg) {
-    const int64_t r = row_base + threadIdx.x;
-    if (r < a.H) {
-      double acc = 0.0;
-      for (int p = 0; p < n_routed; ++p) acc += yps[p][threadIdx.x];
-      if (a.has_shared) acc += yps[n_routed][threadIdx.x];
-      a.y[r] = a.accumulate ? (float)((double)a.y[r] + acc) : (float)acc;
-    }
-  }
+  down1_body<FMT, CPL, kDown1Steps>(a, blockIdx.x);
 }
 
 // ------------------------------------------------------------ dispatch

@@ -115,8 +115,8 @@ template <> struct Mf<FQ4K> {
   __device__ static Wt load(const uint8_t* W, size_t nsb, size_t sbi, int g) {
     Wt w;
 #pragma unroll
-    for (int p = 0; p < 4; ++p) w.c[p] = *reinterpret_cast<const uint4*>(W + sbi * 128 + 16 * (2 * p + g));
-    w.h = *reinterpret_cast<const uint4*>(W + align256(nsb * 128) + sbi * 16);
+    for (int p = 0; p < 4; ++p) w.c[p] = gld_u4(W + sbi * 128 + 16 * (2 * p + g));
+    w.h = gld_u4(W + align256(nsb * 128) + sbi * 16);
     return w;
   }
   // MFMA 2p+s: lane half g holds sub-block 2p+g, nibble s (elements 64p+32g+16s .. +15).
@@ -168,9 +168,9 @@ template <> struct Mf<FQ2K> {
     const uint8_t* ps = W + align256(nsb * 64);
     const uint8_t* pd = ps + align256(nsb * 16);
 #pragma unroll
-    for (int c = 0; c < 4; ++c) w.c[c] = *reinterpret_cast<const uint4*>(W + sbi * 64 + 16 * c);
-    w.sm = *reinterpret_cast<const uint4*>(ps + sbi * 16);
-    w.dd = ld_u32(pd + sbi * 4);
+    for (int c = 0; c < 4; ++c) w.c[c] = gld_u4(W + sbi * 64 + 16 * c);
+    w.sm = gld_u4(ps + sbi * 16);
+    w.dd = gld_u32(pd + sbi * 4);
     return w;
   }
   // MFMA p: lane half g holds sub-block 2p+g (elements 32p+16g .. +15).
@@ -212,11 +212,11 @@ template <> struct Mf<FQ6K> {
     const uint8_t* ps = px + align256(nsb * 64);
     const uint8_t* pd = ps + align256(nsb * 16);
 #pragma unroll
-    for (int j = 0; j < 8; ++j) w.l[j] = *reinterpret_cast<const uint2*>(W + sbi * 128 + 16 * j + 8 * g);
+    for (int j = 0; j < 8; ++j) w.l[j] = gld_u2(W + sbi * 128 + 16 * j + 8 * g);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) w.x[j] = *reinterpret_cast<const uint4*>(px + sbi * 64 + 16 * j);
-    w.sc = *reinterpret_cast<const uint4*>(ps + sbi * 16);
-    w.d = ld_u16(pd + sbi * 2);
+    for (int j = 0; j < 4; ++j) w.x[j] = gld_u4(px + sbi * 64 + 16 * j);
+    w.sc = gld_u4(ps + sbi * 16);
+    w.d = gld_u16(pd + sbi * 2);
     return w;
   }
   // One 16-deep MFMA per sub-block jj: lane half g holds elements 16jj+8g .. +7
@@ -264,8 +264,8 @@ template <> struct Mf<FQ80> {
   __device__ static Wt load(const uint8_t* W, size_t nsb, size_t sbi, int g) {
     Wt w;
 #pragma unroll
-    for (int b = 0; b < 8; ++b) w.q[b] = *reinterpret_cast<const uint4*>(W + sbi * 256 + 32 * b + 16 * g);
-    w.d = *reinterpret_cast<const uint4*>(W + align256(nsb * 256) + sbi * 16);
+    for (int b = 0; b < 8; ++b) w.q[b] = gld_u4(W + sbi * 256 + 32 * b + 16 * g);
+    w.d = gld_u4(W + align256(nsb * 256) + sbi * 16);
     return w;
   }
   template <int NQ>
@@ -299,10 +299,10 @@ __device__ __forceinline__ StageRegs stage_load(const uint8_t* srow, int64_t sb,
   StageRegs r;
   const uint8_t* blk = srow != nullptr ? srow + sb * kQ8KBytes : nullptr;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) r.q[i] = blk != nullptr ? ld_u32(blk + 4 + 16 * piece + 4 * i) : 0u;
-  r.d = (blk != nullptr && piece == 0) ? *reinterpret_cast<const float*>(blk) : 0.0f;
+  for (int i = 0; i < 4; ++i) r.q[i] = blk != nullptr ? gld_u32(blk + 4 + 16 * piece + 4 * i) : 0u;
+  r.d = (blk != nullptr && piece == 0) ? gld_f32(blk) : 0.0f;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) r.bs[i] = (NBSP > 0 && blk != nullptr && piece == 1) ? ld_u32(blk + 260 + 4 * i) : 0u;
+  for (int i = 0; i < 8; ++i) r.bs[i] = (NBSP > 0 && blk != nullptr && piece == 1) ? gld_u32(blk + 260 + 4 * i) : 0u;
   return r;
 }
 template <int NBSP, int TM>
@@ -341,13 +341,13 @@ __device__ __forceinline__ void quantize_row_lds(const float* hrow, uint8_t* __r
   const bool zero = amax == 0.0f || __builtin_isinf(id);
   int q0 = 0, q1 = 0, q2 = 0, q3 = 0;
   if (!zero) { q0 = q8_code(v.x, id); q1 = q8_code(v.y, id); q2 = q8_code(v.z, id); q3 = q8_code(v.w, id); }
-  *reinterpret_cast<uint32_t*>(o + 4 + 4 * lane) =
-      (uint32_t)(q0 & 255) | ((uint32_t)(q1 & 255) << 8) | ((uint32_t)(q2 & 255) << 16) | ((uint32_t)(q3 & 255) << 24);
+  gst_u32(o + 4 + 4 * lane,
+          (uint32_t)(q0 & 255) | ((uint32_t)(q1 & 255) << 8) | ((uint32_t)(q2 & 255) << 16) | ((uint32_t)(q3 & 255) << 24));
   int s = q0 + q1 + q2 + q3;
   s += dpp_all_i<kDppXor1>(s);
   s += dpp_all_i<kDppXor2>(s);
-  if ((lane & 3) == 0) *reinterpret_cast<int16_t*>(o + 260 + 2 * (lane >> 2)) = (int16_t)s;
-  if (lane == 0) *reinterpret_cast<float*>(o) = zero ? 0.0f : __fdiv_rn(amax, 127.0f);
+  if ((lane & 3) == 0) gst_i16(o + 260 + 2 * (lane >> 2), (int16_t)s);
+  if (lane == 0) gst_f32(o, zero ? 0.0f : __fdiv_rn(amax, 127.0f));
 }
 
 // ------------------------------------------------------------ the kernel
@@ -408,7 +408,7 @@ __device__ __forceinline__ void mfma_tile(const MfmaArgs& a) {
         const int64_t cols = (rb1 - rb0) * kMfRows;
         for (int64_t i = threadIdx.x; i < n * cols; i += blockDim.x) {
           const int p = a.pairs[list_off + t0 + i / cols];
-          a.yp[(int64_t)p * a.N + rb0 * kMfRows + i % cols] = 0.0f;
+          gst_f32(a.yp + (int64_t)p * a.N + rb0 * kMfRows + i % cols, 0.0f);
         }
       }
       return;
@@ -524,7 +524,7 @@ __device__ __forceinline__ void mfma_tile(const MfmaArgs& a) {
 #pragma unroll
       for (int r = 0; r < 4 * NQ; ++r) {
         const int m = out_row(r, g);
-        if (m < n) a.yp[orow[m] * a.N + wrow] = (float)(owt[m] * acc0[r]);
+        if (m < n) gst_f32(a.yp + orow[m] * a.N + wrow, (float)(owt[m] * acc0[r]));
       }
       if constexpr (!RES) __syncthreads();   // the streamed stage is rewritten next
     }

@@ -67,8 +67,8 @@ template <> struct Fmt<FQ4K> {
   struct W { uint4 q; uint4 h; };
   __device__ static W load(const uint8_t* m, size_t nsb, size_t sbi, int j) {
     W w;
-    w.q = *reinterpret_cast<const uint4*>(m + sbi * 128 + 16 * j);
-    w.h = *reinterpret_cast<const uint4*>(m + align256(nsb * 128) + sbi * 16);
+    w.q = gld_u4(m + sbi * 128 + 16 * j);
+    w.h = gld_u4(m + align256(nsb * 128) + sbi * 16);
     return w;
   }
   __device__ static void isums(const W& w, const int* xw, const int*, int* is) {
@@ -101,10 +101,10 @@ template <> struct Fmt<FQ6K> {
     const uint8_t* px = m + align256(nsb * 128);
     const uint8_t* ps = px + align256(nsb * 64);
     const uint8_t* pd = ps + align256(nsb * 16);
-    w.l = *reinterpret_cast<const uint4*>(m + sbi * 128 + 16 * j);
-    w.x = *reinterpret_cast<const uint2*>(px + sbi * 64 + 8 * j);
-    w.sc = ld_u16(ps + sbi * 16 + 2 * j);
-    w.d = ld_u16(pd + sbi * 2);
+    w.l = gld_u4(m + sbi * 128 + 16 * j);
+    w.x = gld_u2(px + sbi * 64 + 8 * j);
+    w.sc = gld_u16(ps + sbi * 16 + 2 * j);
+    w.d = gld_u16(pd + sbi * 2);
     return w;
   }
   __device__ static void isums(const W& w, const int* xw, const int* bs, int* is) {
@@ -136,9 +136,9 @@ template <> struct Fmt<FQ2K> {
     W w;
     const uint8_t* ps = m + align256(nsb * 64);
     const uint8_t* pd = ps + align256(nsb * 16);
-    w.q = *reinterpret_cast<const uint4*>(m + sbi * 64 + 16 * c);
-    w.sm = ld_u32(ps + sbi * 16 + 4 * c);
-    w.dd = ld_u32(pd + sbi * 4);
+    w.q = gld_u4(m + sbi * 64 + 16 * c);
+    w.sm = gld_u32(ps + sbi * 16 + 4 * c);
+    w.dd = gld_u32(pd + sbi * 4);
     return w;
   }
   __device__ static void isums(const W& w, const int* xw, const int*, int* is) {
@@ -171,9 +171,9 @@ template <> struct Fmt<FQ80> {
   __device__ static W load(const uint8_t* m, size_t nsb, size_t sbi, int b) {
     W w;
     const uint8_t* pd = m + align256(nsb * 256);
-    w.q0 = *reinterpret_cast<const uint4*>(m + sbi * 256 + 32 * b);
-    w.q1 = *reinterpret_cast<const uint4*>(m + sbi * 256 + 32 * b + 16);
-    w.d = ld_u16(pd + sbi * 16 + 2 * b);
+    w.q0 = gld_u4(m + sbi * 256 + 32 * b);
+    w.q1 = gld_u4(m + sbi * 256 + 32 * b + 16);
+    w.d = gld_u16(pd + sbi * 16 + 2 * b);
     return w;
   }
   __device__ static void isums(const W& w, const int* xw, const int*, int* is) {
@@ -200,11 +200,11 @@ __device__ __forceinline__ void load_x_chunk(const uint8_t* xrow, int c, int* xw
   int e0 = c * L::WPC;
   const uint8_t* blk = xrow + (size_t)(e0 >> 8) * kQ8KBytes;
   int o = e0 & 255;
-  dx = (double)*reinterpret_cast<const float*>(blk);
+  dx = (double)gld_f32(blk);
 #pragma unroll
-  for (int i = 0; i < L::XDW; ++i) xw[i] = (int)ld_u32(blk + 4 + o + 4 * i);
+  for (int i = 0; i < L::XDW; ++i) xw[i] = (int)gld_u32(blk + 4 + o + 4 * i);
 #pragma unroll
-  for (int i = 0; i < L::NBS; ++i) bs[i] = (int)(int16_t)ld_u16(blk + 260 + 2 * ((o >> 4) + i));
+  for (int i = 0; i < L::NBS; ++i) bs[i] = (int)(int16_t)gld_u16(blk + 260 + 2 * ((o >> 4) + i));
 }
 
 }  // namespace moeq

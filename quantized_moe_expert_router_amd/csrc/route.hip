@@ -112,8 +112,8 @@ __global__ __launch_bounds__(256) void k_logits_mfma(const float* __restrict__ x
       const int64_t kc = k0 + 4 * c4;
       const int64_t tr = t0 + row, er = e0 + row;
       const float4 zero = make_float4(0.f, 0.f, 0.f, 0.f);
-      const float4 xv = (tr < T && kc < H) ? *reinterpret_cast<const float4*>(x + tr * H + kc) : zero;
-      const float4 wv = (er < E && kc < H) ? *reinterpret_cast<const float4*>(W + er * H + kc) : zero;
+      const float4 xv = (tr < T && kc < H) ? gld_f4(x + tr * H + kc) : zero;
+      const float4 wv = (er < E && kc < H) ? gld_f4(W + er * H + kc) : zero;
       *reinterpret_cast<float4*>(&xs[row][4 * c4]) = xv;
       *reinterpret_cast<float4*>(&ws[row][4 * c4]) = wv;
     }
@@ -155,8 +155,8 @@ __device__ void topk_row_wave(const double* __restrict__ row, int64_t E, int k, 
   topk_wave_regs<NPER>(row, E, k, gating, scale, my_i, my_w);
   const int lane = lane_id();
   if (lane < k) {
-    ids_out[lane] = my_i;
-    w_out[lane] = my_w;
+    gst_i32(ids_out + lane, my_i);
+    gst_f32(w_out + lane, my_w);
     if (ids_lds) ids_lds[lane] = my_i;
   }
 }

@@ -21,7 +21,7 @@ __device__ void topk_wave_regs(const double* __restrict__ row, int64_t E, int k,
 #pragma unroll
   for (int i = 0; i < NPER; ++i) {
     const int64_t e = lane + (int64_t)kWave * i;
-    v[i] = e < E ? row[e] : -INFINITY;
+    v[i] = e < E ? gld_f64(row + e) : -INFINITY;
     vi[i] = e < E ? (int)e : INT_MAX;
   }
   double my_v = 0.0;
