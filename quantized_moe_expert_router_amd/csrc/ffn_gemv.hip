@@ -57,7 +57,7 @@ __global__ __launch_bounds__(256) void k_gateup(GateUpArgs a) {
   using L = Fmt<FMT>;
   const int wave = threadIdx.x >> 6, lane = lane_id();
   const int lpr = a.lpr, rps = kWave / lpr, rig = lane / lpr, lir = lane % lpr;
-  const int64_t nb = a.H / 256, nsb = a.F * nb, xrow = nb * kQ8KBytes;
+  const int64_t nb = a.H / 256, xrow = nb * kQ8KBytes;
   int xw[TT][CPL][L::XDW], bs[TT][CPL][L::NBS];
   double dx[TT][CPL];
   if (TT == 1) {
@@ -121,8 +121,8 @@ __global__ __launch_bounds__(256) void k_gateup(GateUpArgs a) {
           ok[u][c] = rv && ch < a.cpr;
           if (ok[u][c]) {
             const size_t sbi = (size_t)(row[u] * nb + ch / L::CPS);
-            wg[u][c] = L::load(Wg, (size_t)nsb, sbi, ch % L::CPS);
-            wu[u][c] = L::load(Wu, (size_t)nsb, sbi, ch % L::CPS);
+            wg[u][c] = L::load(Wg, a.F, nb, row[u], ch / L::CPS, ch % L::CPS);
+            wu[u][c] = L::load(Wu, a.F, nb, row[u], ch / L::CPS, ch % L::CPS);
           }
         }
       }
@@ -193,18 +193,18 @@ __device__ __forceinline__ void quant_h_regs(const float* hv, bool have, int ch,
   }
   dx = zero ? 0.0 : (double)__fdiv_rn(amax, 127.0f);
   if (dbg != nullptr && have) {
-    const int e0 = ch * L::WPC;
-    uint8_t* blk = dbg + (size_t)(e0 >> 8) * kQ8KBytes;
-    const int o = e0 & 255;
+    const int j = ch % L::CPS;
+    uint8_t* blk = dbg + (size_t)(ch / L::CPS) * kQ8KBytes;
 #pragma unroll
-    for (int q = 0; q < L::XDW; ++q) *reinterpret_cast<int*>(blk + 4 + o + 4 * q) = xw[q];
+    for (int q = 0; q < L::XDW; ++q) gst_u32(blk + 4 + L::xoff(j, q), (uint32_t)xw[q]);
 #pragma unroll
-    for (int q = 0; q < L::NBS; ++q) *reinterpret_cast<int16_t*>(blk + 260 + 2 * ((o >> 4) + q)) = (int16_t)bs[q];
-    if (o == 0) *reinterpret_cast<float*>(blk) = (float)dx;
+    for (int t = 0; t < L::NBS; ++t) gst_i16(blk + 260 + 2 * L::bsidx(j, t), (int16_t)bs[t]);
+    if (j == 0) gst_f32(blk, (float)dx);
   }
 }
 
-// q8_K of the chunk(s) this lane holds, loading the fp32 h row first.
+// q8_K of the chunk(s) this lane holds, loading the fp32 h row first (the
+// chunk's elements in the order of its activation dwords).
 template <int FMT, int CPL>
 __device__ __forceinline__ void quant_h_chunks(const float* __restrict__ hrow, int lir, int lpr, int cpr,
                                                bool have, int xw[CPL][Fmt<FMT>::XDW],
@@ -216,9 +216,10 @@ __device__ __forceinline__ void quant_h_chunks(const float* __restrict__ hrow, i
     const int ch = lir + lpr * c;
     const bool v = have && ch < cpr;
     float hv[L::WPC];
+    const float* hb = hrow + (ch / L::CPS) * 256;
 #pragma unroll
     for (int q = 0; q < L::WPC / 4; ++q) {
-      float4 f = v ? reinterpret_cast<const float4*>(hrow + ch * L::WPC)[q] : make_float4(0.f, 0.f, 0.f, 0.f);
+      float4 f = v ? gld_f4(hb + L::xoff(ch % L::CPS, q)) : make_float4(0.f, 0.f, 0.f, 0.f);
       hv[4 * q] = f.x; hv[4 * q + 1] = f.y; hv[4 * q + 2] = f.z; hv[4 * q + 3] = f.w;
     }
     quant_h_regs<FMT, 256 / L::WPC>(hv, v, ch, xw[c], bs[c], dx[c], dbg);
@@ -236,7 +237,7 @@ __global__ __launch_bounds__(256) void k_down(DownArgs a) {
 
   const int wave = threadIdx.x >> 6, lane = lane_id();
   const int lpr = a.lpr, rps = kWave / lpr, rig = lane / lpr, lir = lane % lpr;
-  const int64_t nb = a.F / 256, nsb = a.H * nb;
+  const int64_t nb = a.F / 256;
   const int64_t row0 = (int64_t)blockIdx.x * a.rb + (int64_t)wave * a.steps * rps + rig;
   const bool dbg_writer = blockIdx.x == 0 && wave == 0 && rig == 0;
 
@@ -275,7 +276,7 @@ __global__ __launch_bounds__(256) void k_down(DownArgs a) {
           const int ch = lir + lpr * c;
           ok[u][c] = rv && ch < a.cpr;
           if (ok[u][c])
-            wd[u][c] = L::load(Wd, (size_t)nsb, (size_t)(row[u] * nb + ch / L::CPS), ch % L::CPS);
+            wd[u][c] = L::load(Wd, a.H, nb, row[u], ch / L::CPS, ch % L::CPS);
         }
       }
 #pragma unroll

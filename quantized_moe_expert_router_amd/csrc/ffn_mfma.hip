@@ -72,12 +72,9 @@ __device__ __forceinline__ uint32_t bytes_times(uint32_t v, uint32_t s) {
   return __builtin_bit_cast(uint32_t, a * b);
 }
 
+// A fragments come from LDS unconditionally: a lane whose tile row lies beyond
+// the staged rows reads a zero row instead (no per-step branch or zeroing).
 __device__ __forceinline__ v4i lds_v4(const uint8_t* p) { return *reinterpret_cast<const v4i*>(p); }
-// A fragment of a lane whose tile row may lie beyond the staged rows (zero).
-__device__ __forceinline__ v4i lda(const uint8_t* p, bool arow) {
-  const v4i z = {0, 0, 0, 0};
-  return arow ? lds_v4(p) : z;
-}
 
 // Token row m of the lane's results for value r.
 __device__ __forceinline__ int out_row(int r, int g) { return 8 * (r >> 2) + 4 * g + (r & 3); }
@@ -112,7 +109,8 @@ template <int FMT> struct Mf;
 template <> struct Mf<FQ4K> {
   static constexpr int NBSP = 8;   // one sum per 32-sub-block: bsums[2j] + bsums[2j+1]
   struct Wt { uint4 c[4]; uint4 h; };
-  __device__ static Wt load(const uint8_t* W, size_t nsb, size_t sbi, int g) {
+  __device__ static Wt load(const uint8_t* W, int64_t N, int64_t nbK, int64_t row, int64_t sb, int g) {
+    const size_t nsb = (size_t)(N * nbK), sbi = (size_t)(row * nbK + sb);
     Wt w;
 #pragma unroll
     for (int p = 0; p < 4; ++p) w.c[p] = gld_u4(W + sbi * 128 + 16 * (2 * p + g));
@@ -121,7 +119,7 @@ template <> struct Mf<FQ4K> {
   }
   // MFMA 2p+s: lane half g holds sub-block 2p+g, nibble s (elements 64p+32g+16s .. +15).
   template <int NQ>
-  __device__ static void mac(const Wt& w, int g, const uint8_t* qrow, bool arow, const v4i abs, const float* dxs,
+  __device__ static void mac(const Wt& w, int g, const uint8_t* qrow, const v4i abs, const float* dxs,
                              int n, double* acc) {
     const uint64_t lo = (uint64_t)w.h.y | ((uint64_t)w.h.z << 32);
     const uint64_t hi = (uint64_t)w.h.z | ((uint64_t)w.h.w << 32);
@@ -139,7 +137,7 @@ template <> struct Mf<FQ4K> {
           bl[i] = (int)bytes_times(q, sc & 7);
           bh[i] = (int)bytes_times(q, sc >> 3);
         }
-        const v4i a = lda(qrow + 64 * p + 32 * g + 16 * s, arow);
+        const v4i a = lds_v4(qrow + 64 * p + 32 * g + 16 * s);
         plo = mfma_k32(a, bl, plo);
         phi = mfma_k32(a, bh, phi);
       }
@@ -162,32 +160,37 @@ template <> struct Mf<FQ4K> {
 
 template <> struct Mf<FQ2K> {
   static constexpr int NBSP = 16;  // one sum per 16-sub-block: bsums[j]
-  struct Wt { uint4 c[4]; uint4 sm; uint32_t dd; };
-  __device__ static Wt load(const uint8_t* W, size_t nsb, size_t sbi, int) {
+  struct Wt { uint4 c[2]; uint4 sm; uint32_t dd; };
+  // Tiled layout (32-row units): lane (half g, row r) reads the two 16 B
+  // pieces of its half, each load instruction covering 1 KB contiguously.
+  __device__ static Wt load(const uint8_t* W, int64_t N, int64_t nbK, int64_t row, int64_t sb, int g) {
+    const int64_t units = ((N + 31) >> 5) * nbK, u = (row >> 5) * nbK + sb;
+    const int r = (int)(row & 31);
+    const uint8_t* ps = W + align256((size_t)units * 2048);
+    const uint8_t* pd = ps + align256((size_t)units * 512);
     Wt w;
-    const uint8_t* ps = W + align256(nsb * 64);
-    const uint8_t* pd = ps + align256(nsb * 16);
 #pragma unroll
-    for (int c = 0; c < 4; ++c) w.c[c] = gld_u4(W + sbi * 64 + 16 * c);
-    w.sm = gld_u4(ps + sbi * 16);
-    w.dd = gld_u32(pd + sbi * 4);
+    for (int k = 0; k < 2; ++k) w.c[k] = gld_u4(W + u * 2048 + 1024 * k + 16 * (32 * g + r));
+    w.sm = gld_u4(ps + u * 512 + 16 * r);
+    w.dd = gld_u32(pd + u * 128 + 4 * r);
     return w;
   }
-  // MFMA p: lane half g holds sub-block 2p+g (elements 32p+16g .. +15).
+  // MFMA p: lane half g holds sub-block 2p+g (elements 32p+16g .. +15), whose
+  // 16 codes are word p of the half: element 4i + b at bits 8b + 2i.
   template <int NQ>
-  __device__ static void mac(const Wt& w, int g, const uint8_t* qrow, bool arow, const v4i abs, const float* dxs,
+  __device__ static void mac(const Wt& w, int g, const uint8_t* qrow, const v4i abs, const float* dxs,
                              int n, double* acc) {
     const uint32_t sm[4] = {w.sm.x, w.sm.y, w.sm.z, w.sm.w};
     v16i P = {0};
+    const uint32_t words[8] = {w.c[0].x, w.c[0].y, w.c[0].z, w.c[0].w, w.c[1].x, w.c[1].y, w.c[1].z, w.c[1].w};
 #pragma unroll
     for (int p = 0; p < 8; ++p) {
-      const int j = 2 * p + g, cc = j >> 2, s = j & 3;
+      const int j = 2 * p + g;
       const uint32_t sc = (sm[j >> 2] >> (8 * (j & 3))) & 15;
-      const uint32_t c[4] = {w.c[cc].x, w.c[cc].y, w.c[cc].z, w.c[cc].w};
       v4i b;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) b[i] = (int)bytes_times((c[i] >> (2 * s)) & 0x03030303u, sc);
-      P = mfma_k32(lda(qrow + 32 * p + 16 * g, arow), b, P);
+      for (int i = 0; i < 4; ++i) b[i] = (int)bytes_times((words[p] >> (2 * i)) & 0x03030303u, sc);
+      P = mfma_k32(lds_v4(qrow + 32 * p + 16 * g), b, P);
     }
     v4i bm;
 #pragma unroll
@@ -206,7 +209,8 @@ template <> struct Mf<FQ6K> {
   struct Wt { uint2 l[8]; uint4 x[4]; uint4 sc; uint32_t d; };
   // Lane half g needs words 2g, 2g+1 of every low-nibble chunk and all of the
   // high-pair row.
-  __device__ static Wt load(const uint8_t* W, size_t nsb, size_t sbi, int g) {
+  __device__ static Wt load(const uint8_t* W, int64_t N, int64_t nbK, int64_t row, int64_t sb, int g) {
+    const size_t nsb = (size_t)(N * nbK), sbi = (size_t)(row * nbK + sb);
     Wt w;
     const uint8_t* px = W + align256(nsb * 128);
     const uint8_t* ps = px + align256(nsb * 64);
@@ -223,7 +227,7 @@ template <> struct Mf<FQ6K> {
   // (low nibbles: word i = 2g+t of chunk jj/2, nibble jj%2; high pairs: word
   // jj%2 of chunk jj/2 in the high-pair plane, bits 2i).
   template <int NQ>
-  __device__ static void mac(const Wt& w, int g, const uint8_t* qrow, bool arow, const v4i abs, const float* dxs,
+  __device__ static void mac(const Wt& w, int g, const uint8_t* qrow, const v4i abs, const float* dxs,
                              int n, double* acc) {
     const uint32_t scw[4] = {w.sc.x, w.sc.y, w.sc.z, w.sc.w};
     int S1[16];
@@ -243,7 +247,7 @@ template <> struct Mf<FQ6K> {
         q[t] = ((l2[t] >> (4 * s)) & 0x0F0F0F0Fu) | (((xs >> (2 * i)) & 0x03030303u) << 4);
       }
       const long b = (long)(((uint64_t)q[1] << 32) | q[0]);
-      const long a = arow ? *reinterpret_cast<const long*>(qrow + 16 * jj + 8 * g) : 0l;
+      const long a = *reinterpret_cast<const long*>(qrow + 16 * jj + 8 * g);
       const v16i P = mfma_k16(a, b, z16);
       const int sc = (int)(int8_t)((scw[jj >> 2] >> (8 * (jj & 3))) & 0xFF);
 #pragma unroll
@@ -261,7 +265,8 @@ template <> struct Mf<FQ6K> {
 template <> struct Mf<FQ80> {
   static constexpr int NBSP = 0;
   struct Wt { uint4 q[8]; uint4 d; };
-  __device__ static Wt load(const uint8_t* W, size_t nsb, size_t sbi, int g) {
+  __device__ static Wt load(const uint8_t* W, int64_t N, int64_t nbK, int64_t row, int64_t sb, int g) {
+    const size_t nsb = (size_t)(N * nbK), sbi = (size_t)(row * nbK + sb);
     Wt w;
 #pragma unroll
     for (int b = 0; b < 8; ++b) w.q[b] = gld_u4(W + sbi * 256 + 32 * b + 16 * g);
@@ -269,14 +274,14 @@ template <> struct Mf<FQ80> {
     return w;
   }
   template <int NQ>
-  __device__ static void mac(const Wt& w, int g, const uint8_t* qrow, bool arow, const v4i, const float* dxs,
+  __device__ static void mac(const Wt& w, int g, const uint8_t* qrow, const v4i, const float* dxs,
                              int n, double* acc) {
     const uint32_t dw[4] = {w.d.x, w.d.y, w.d.z, w.d.w};
     const v16i z16 = {0};
 #pragma unroll
     for (int b = 0; b < 8; ++b) {
       const v4i bq = {(int)w.q[b].x, (int)w.q[b].y, (int)w.q[b].z, (int)w.q[b].w};
-      const v16i P = mfma_k32(lda(qrow + 32 * b + 16 * g, arow), bq, z16);
+      const v16i P = mfma_k32(lds_v4(qrow + 32 * b + 16 * g), bq, z16);
       const double db = half_bits_to_float(dw[b >> 1] >> (16 * (b & 1)));
       MOEQ_COMBINE(acc[r] += (dx * db) * (double)P[r])
     }
@@ -368,7 +373,7 @@ __device__ __forceinline__ void quantize_row_lds(const float* hrow, uint8_t* __r
 // in flight while the current unit's MFMAs run.
 __host__ __device__ constexpr int kRes(int TM) { return TM == 32 ? 8 : 16; }
 
-template <int FMT, int MODE, bool RES, int TM>
+template <int FMT, int MODE, bool RES, int TM, int RING>
 __device__ __forceinline__ void mfma_tile(const MfmaArgs& a) {
   using M = Mf<FMT>;
   constexpr int NQ = TM / 8;
@@ -376,6 +381,7 @@ __device__ __forceinline__ void mfma_tile(const MfmaArgs& a) {
   __shared__ int64_t orow[TM];
   __shared__ double owt[TM];
   __shared__ const uint8_t* srows[TM];
+  __shared__ __align__(16) uint8_t zrow[kQsStride];   // A rows beyond the staged ones read zeros
 
   // ---- tile: expert (or the shared expert) and its rows t0 .. t0+n-1
   int e = -1, t0, n;
@@ -418,6 +424,7 @@ __device__ __forceinline__ void mfma_tile(const MfmaArgs& a) {
   // ---- per-row bookkeeping: source rows, output rows, gate weights
   const int tid = threadIdx.x, wave = tid >> 6, lane = lane_id(), g = lane >> 5;
   const bool arow = (lane & 31) < TM;                  // the lane's A row is staged
+  for (int i = tid; i < kQsStride / 4; i += blockDim.x) reinterpret_cast<uint32_t*>(zrow)[i] = 0u;
   if (tid < TM) {
     int64_t orr = -1, ridx = 0;
     double wt = 0.0;
@@ -441,10 +448,10 @@ __device__ __forceinline__ void mfma_tile(const MfmaArgs& a) {
   }
   __syncthreads();
 
-  const int64_t nbK = a.K / 256, nsb = a.N * nbK;
+  const int64_t nbK = a.K / 256;
   const int64_t lrow = wave * 32 + (lane & 31);       // the lane's weight row inside a row block
   // first unit's weights, in flight during the staging
-  typename M::Wt wn = M::load(W0, (size_t)nsb, (size_t)((rb0 * kMfRows + lrow) * nbK), g);
+  typename M::Wt wn = M::load(W0, a.N, nbK, rb0 * kMfRows + lrow, 0, g);
   // staging work item i: 256-block i / (16 TM), row (i / 16) % TM, 16-byte piece i % 16
   if constexpr (RES) {
     const int64_t items = nbK * TM * 16;
@@ -463,10 +470,74 @@ __device__ __forceinline__ void mfma_tile(const MfmaArgs& a) {
     }
     __syncthreads();
   }
-  const int arw = (lane & 31) < TM ? (lane & 31) : 0;
   const int64_t nmat = MODE == 0 ? 2 : 1;
 
-  {
+  if constexpr (RES && RING > 1) {
+  // RING weight units in flight per wave (memory-bound tiles): ring slot j
+  // holds unit u0 + j, and the loop is unrolled by RING so every slot index
+  // is static.  Units run (row block, 256-block, matrix) in the same order in
+  // every wave, so the row-block epilogue (with its barriers) is uniform.
+  static_assert(MODE == 1 || RING % 2 == 0, "gate/up units alternate between the two matrices");
+  const int64_t U = (rb1 - rb0) * nbK * nmat;
+  typename M::Wt ring[RING];
+  ring[0] = wn;
+  int64_t l_rb = rb0, l_sb = 0;
+  int l_mat = 0;
+  auto adv_l = [&]() {
+    if (++l_mat == nmat) {
+      l_mat = 0;
+      if (++l_sb == nbK) { l_sb = 0; ++l_rb; }
+    }
+  };
+  auto load_unit = [&]() { return M::load(l_mat == 0 ? W0 : W1, a.N, nbK, l_rb * kMfRows + lrow, l_sb, g); };
+  adv_l();
+#pragma unroll
+  for (int j = 1; j < RING; ++j)
+    if (l_rb < rb1) { ring[j] = load_unit(); adv_l(); }
+  double acc0[4 * NQ], acc1[4 * NQ];
+#pragma unroll
+  for (int r = 0; r < 4 * NQ; ++r) { acc0[r] = 0.0; acc1[r] = 0.0; }
+  int64_t c_rb = rb0, c_sb = 0;
+  for (int64_t u0 = 0; u0 < U; u0 += RING) {
+#pragma unroll
+    for (int j = 0; j < RING; ++j) {
+      if (u0 + j < U) {
+        const int mat = MODE == 0 ? (j & 1) : 0;
+        const typename M::Wt& wc = ring[j];
+        StageLds<TM>& S = L[c_sb];
+        const uint8_t* qrow = arow ? &S.qs[lane & 31][0] : zrow;
+        v4i abs = {0, 0, 0, 0};
+        if constexpr (M::NBSP > 0) abs = lds_v4(arow ? &S.bsp[lane & 31][g][0] : zrow);
+        if (mat == 0) M::template mac<NQ>(wc, g, qrow, abs, S.dx, n, acc0);
+        else M::template mac<NQ>(wc, g, qrow, abs, S.dx, n, acc1);
+        // the slot is free again: refill it with the unit RING ahead
+        if (l_rb < rb1) { ring[j] = load_unit(); adv_l(); }
+        if (mat == nmat - 1 && ++c_sb == nbK) {
+          const int64_t wrow = c_rb * kMfRows + lrow;
+          if constexpr (MODE == 0) {
+            __shared__ float hs2[TM][kMfRows + 4];
+#pragma unroll
+            for (int r = 0; r < 4 * NQ; ++r) hs2[out_row(r, g)][lrow] = (float)(silu64(acc0[r]) * acc1[r]);
+            __syncthreads();
+            for (int m = wave; m < n; m += kMfWaves)
+              quantize_row_lds(&hs2[m][0], a.hq + orow[m] * a.hq_stride + c_rb * kQ8KBytes);
+            __syncthreads();   // hs2 is rewritten by the next row block
+          } else {
+#pragma unroll
+            for (int r = 0; r < 4 * NQ; ++r) {
+              const int m = out_row(r, g);
+              if (m < n) gst_f32(a.yp + orow[m] * a.N + wrow, (float)(owt[m] * acc0[r]));
+            }
+          }
+#pragma unroll
+          for (int r = 0; r < 4 * NQ; ++r) { acc0[r] = 0.0; acc1[r] = 0.0; }
+          c_sb = 0;
+          ++c_rb;
+        }
+      }
+    }
+  }
+  } else {
   // One unit of weights ahead (few registers, so more waves per SIMD hide the
   // latency); activation blocks resident in LDS, or streamed through a
   // double-buffered stage when K exceeds the resident limit.
@@ -488,26 +559,25 @@ __device__ __forceinline__ void mfma_tile(const MfmaArgs& a) {
       }
       // next unit: up of this block (mode 0), else the next block, else the
       // first block of the next row block
-      const size_t sbi = (size_t)(wrow * nbK + sb);
       const bool last_k = sb + 1 == nbK;
       const bool more = !last_k || rb + 1 < rb1;
-      const size_t next_sbi = last_k ? (size_t)((wrow + kMfRows) * nbK) : sbi + 1;
+      const int64_t next_row = last_k ? wrow + kMfRows : wrow, next_sb = last_k ? 0 : sb + 1;
       typename M::Wt wc = wn;
       if constexpr (MODE == 0) {
-        wn = M::load(W1, (size_t)nsb, sbi, g);
+        wn = M::load(W1, a.N, nbK, wrow, sb, g);
       } else if (more) {
-        wn = M::load(W0, (size_t)nsb, next_sbi, g);
+        wn = M::load(W0, a.N, nbK, next_row, next_sb, g);
       }
       if constexpr (!RES)
         if (stager && !last_k) sr = stage_load<M::NBSP>(srows[ms], sb + 1, piece);
-      const uint8_t* qrow = &S.qs[arw][0];
+      const uint8_t* qrow = arow ? &S.qs[lane & 31][0] : zrow;
       v4i abs = {0, 0, 0, 0};
-      if constexpr (M::NBSP > 0) abs = lda(&S.bsp[arw][g][0], arow);
-      M::template mac<NQ>(wc, g, qrow, arow, abs, S.dx, n, acc0);
+      if constexpr (M::NBSP > 0) abs = lds_v4(arow ? &S.bsp[lane & 31][g][0] : zrow);
+      M::template mac<NQ>(wc, g, qrow, abs, S.dx, n, acc0);
       if constexpr (MODE == 0) {
         wc = wn;
-        if (more) wn = M::load(W0, (size_t)nsb, next_sbi, g);
-        M::template mac<NQ>(wc, g, qrow, arow, abs, S.dx, n, acc1);
+        if (more) wn = M::load(W0, a.N, nbK, next_row, next_sb, g);
+        M::template mac<NQ>(wc, g, qrow, abs, S.dx, n, acc1);
       }
     }
 
@@ -537,11 +607,19 @@ __device__ __forceinline__ void mfma_tile(const MfmaArgs& a) {
 // SIMD), which hides the weight-load latency of these memory-bound tiles
 // (except Q6_K, whose per-sub-block scaling needs more registers).
 template <int FMT, int MODE, bool RES, int TM>
-__global__ __launch_bounds__(512) void k_mfma(MfmaArgs a) { mfma_tile<FMT, MODE, RES, TM>(a); }
+__global__ __launch_bounds__(512) void k_mfma(MfmaArgs a) { mfma_tile<FMT, MODE, RES, TM, 1>(a); }
 template <int FMT, int MODE, bool RES>
 __global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(4, 8))) void k_mfma_thin(
     MfmaArgs a) {
-  mfma_tile<FMT, MODE, RES, 8>(a);
+  mfma_tile<FMT, MODE, RES, 8, 1>(a);
+}
+// 8-row tiles with resident activations and RING weight units in flight per
+// wave (the memory-bound verify unions and small chunks).
+template <int FMT> constexpr int kRing = FMT == FQ80 ? 2 : 4;
+template <int FMT, int MODE>
+__global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2, 8))) void k_mfma_ring(
+    MfmaArgs a) {
+  mfma_tile<FMT, MODE, true, 8, kRing<FMT>>(a);
 }
 
 // Tile lists of the routed experts whose row count exceeds `thr`: experts
@@ -615,7 +693,7 @@ int launch_mfma(int fmt, int mode, bool thin, dim3 grid, const MfmaArgs& a, hipS
   const int64_t nbK = a.K / 256;
 #define MOEQ_MF1(F, MD, TM)                                                                             \
   if (TM == 8 && F != FQ6K) {                                                                         \
-    if (nbK <= kRes(TM)) hipLaunchKernelGGL((k_mfma_thin<F, MD, true>), grid, dim3(512), 0, s, a);    \
+    if (nbK <= kRes(TM)) hipLaunchKernelGGL((k_mfma_ring<F, MD>), grid, dim3(512), 0, s, a);          \
     else hipLaunchKernelGGL((k_mfma_thin<F, MD, false>), grid, dim3(512), 0, s, a);                   \
   } else if (nbK <= kRes(TM)) {                                                                       \
     hipLaunchKernelGGL((k_mfma<F, MD, true, TM>), grid, dim3(512), 0, s, a);                          \

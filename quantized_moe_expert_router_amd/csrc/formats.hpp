@@ -18,9 +18,17 @@
 //         plane X  64 B/sb: chunk j = 2 words; word a, byte b, bits 2s..2s+1 =
 //           high2(elem 32j + 4(4a+s) + b)
 //         plane S  16 B/sb: int8 scales;  plane D 2 B/sb: fp16 d
-//   Q2_K  plane Q  64 B/sb: chunk c (elements 64c..64c+63, sub-blocks 4c..4c+3),
-//           word a, byte b, bits 2s..2s+1 = elem 64c + 16s + 4a + b
-//         plane S  16 B/sb: (sc | m << 4) per sub-block;  plane D 4 B/sb: d, dmin
+//   Q2_K  tiled: unit u = (row / 32) * nb + sb (32 rows x one super-block),
+//         each plane contiguous per unit, so a wave reading the 32 rows of a
+//         unit reads whole lines (and the matrix-core tiles read it with
+//         every load instruction contiguous)
+//         plane Q 2048 B/unit: 16 B at 1024 k + 16 (32 g + row % 32) = the
+//           words of steps 4k..4k+3 of half g; step p of half g is sub-block
+//           2p + g, its word holds element 4i + b of the sub-block at bits
+//           8b + 2i.  A lane chunk j = 2k + g is that 16 B piece: sub-blocks
+//           8k + g + 2t, t = 0..3
+//         plane S  512 B/unit: the row's 16 bytes (sc | m << 4) at 16 (row % 32)
+//         plane D  128 B/unit: d, dmin at 4 (row % 32)
 //   Q8_0  plane Q 256 B/sb: chunk b = the 32 int8 quants of block b
 //         plane D  16 B/sb: eight fp16 d
 #pragma once
@@ -35,37 +43,43 @@ struct Geo {
   int wpc;          // weights per lane chunk
   int nplanes;
   int pb[4];        // bytes per super-block of each plane
+  int tile;         // rows per layout unit (the row count is padded to it)
 };
 
 __host__ __device__ inline Geo geo_of(int fmt) {
   switch (fmt) {
-    case FQ4K: return Geo{32, 2, {128, 16, 0, 0}};
-    case FQ6K: return Geo{32, 4, {128, 64, 16, 2}};
-    case FQ2K: return Geo{64, 3, {64, 16, 4, 0}};
-    case FQ80: return Geo{32, 2, {256, 16, 0, 0}};
+    case FQ4K: return Geo{32, 2, {128, 16, 0, 0}, 1};
+    case FQ6K: return Geo{32, 4, {128, 64, 16, 2}, 1};
+    case FQ2K: return Geo{64, 3, {64, 16, 4, 0}, 32};
+    case FQ80: return Geo{32, 2, {256, 16, 0, 0}, 1};
   }
-  return Geo{0, 0, {0, 0, 0, 0}};
+  return Geo{0, 0, {0, 0, 0, 0}, 1};
 }
 
 __host__ __device__ inline size_t packed_bytes_of(int fmt, int64_t rows, int64_t cols) {
   Geo g = geo_of(fmt);
-  size_t nsb = (size_t)rows * (size_t)(cols / 256), tot = 0;
+  const int64_t prow = (rows + g.tile - 1) / g.tile * g.tile;
+  size_t nsb = (size_t)prow * (size_t)(cols / 256), tot = 0;
   for (int p = 0; p < g.nplanes; ++p) tot += align256(nsb * g.pb[p]);
   return tot;
 }
 
-__device__ __forceinline__ const uint8_t* plane(const uint8_t* m, size_t nsb, int fmt, int p) {
-  Geo g = geo_of(fmt);
-  size_t off = 0;
-  for (int q = 0; q < p; ++q) off += align256(nsb * g.pb[q]);
-  return m + off;
-}
-
 // ---------------------------------------------------------------- Q4_K
-template <> struct Fmt<FQ4K> {
+// Every format: load(m, rows, nb, row, sb, j) reads lane chunk j of super-block
+// sb of a row; chunk j covers sub-blocks sub_of(j, t); its activation dword i
+// sits at byte xoff(j, i) of the q8_K block and its block sum t at bsidx(j, t).
+// Row-major formats: chunk j is elements j*WPC .. (j+1)*WPC - 1.
+template <int WPC_> struct RowMajor {
+  __device__ static constexpr int xoff(int j, int i) { return j * WPC_ + 4 * i; }
+  __device__ static constexpr int bsidx(int j, int t) { return ((j * WPC_) >> 4) + t; }
+};
+
+template <> struct Fmt<FQ4K> : RowMajor<32> {
   static constexpr int WPC = 32, CPS = 8, XDW = 8, NBS = 2, SPC = 1;
+  __device__ static constexpr int sub_of(int j, int t) { return j * SPC + t; }
   struct W { uint4 q; uint4 h; };
-  __device__ static W load(const uint8_t* m, size_t nsb, size_t sbi, int j) {
+  __device__ static W load(const uint8_t* m, int64_t rows, int64_t nb, int64_t row, int64_t sb, int j) {
+    const size_t nsb = (size_t)(rows * nb), sbi = (size_t)(row * nb + sb);
     W w;
     w.q = gld_u4(m + sbi * 128 + 16 * j);
     w.h = gld_u4(m + align256(nsb * 128) + sbi * 16);
@@ -93,10 +107,12 @@ template <> struct Fmt<FQ4K> {
 };
 
 // ---------------------------------------------------------------- Q6_K
-template <> struct Fmt<FQ6K> {
+template <> struct Fmt<FQ6K> : RowMajor<32> {
   static constexpr int WPC = 32, CPS = 8, XDW = 8, NBS = 2, SPC = 2;
+  __device__ static constexpr int sub_of(int j, int t) { return j * SPC + t; }
   struct W { uint4 l; uint2 x; uint32_t sc; uint32_t d; };
-  __device__ static W load(const uint8_t* m, size_t nsb, size_t sbi, int j) {
+  __device__ static W load(const uint8_t* m, int64_t rows, int64_t nb, int64_t row, int64_t sb, int j) {
+    const size_t nsb = (size_t)(rows * nb), sbi = (size_t)(row * nb + sb);
     W w;
     const uint8_t* px = m + align256(nsb * 128);
     const uint8_t* ps = px + align256(nsb * 64);
@@ -131,33 +147,40 @@ template <> struct Fmt<FQ6K> {
 // ---------------------------------------------------------------- Q2_K
 template <> struct Fmt<FQ2K> {
   static constexpr int WPC = 64, CPS = 4, XDW = 16, NBS = 4, SPC = 4;
-  struct W { uint4 q; uint32_t sm; uint32_t dd; };
-  __device__ static W load(const uint8_t* m, size_t nsb, size_t sbi, int c) {
+  __device__ static constexpr int sub_of(int j, int t) { return 8 * (j >> 1) + (j & 1) + 2 * t; }
+  __device__ static constexpr int xoff(int j, int i) { return 16 * sub_of(j, i >> 2) + 4 * (i & 3); }
+  __device__ static constexpr int bsidx(int j, int t) { return sub_of(j, t); }
+  struct W { uint4 q; uint2 sm; uint32_t dd; };
+  __device__ static W load(const uint8_t* m, int64_t rows, int64_t nb, int64_t row, int64_t sb, int j) {
+    const int64_t units = ((rows + 31) >> 5) * nb, u = (row >> 5) * nb + sb;
+    const int r = (int)(row & 31);
+    const uint8_t* ps = m + align256((size_t)units * 2048);
+    const uint8_t* pd = ps + align256((size_t)units * 512);
     W w;
-    const uint8_t* ps = m + align256(nsb * 64);
-    const uint8_t* pd = ps + align256(nsb * 16);
-    w.q = gld_u4(m + sbi * 64 + 16 * c);
-    w.sm = gld_u32(ps + sbi * 16 + 4 * c);
-    w.dd = gld_u32(pd + sbi * 4);
+    w.q = gld_u4(m + u * 2048 + 1024 * (j >> 1) + 16 * (32 * (j & 1) + r));
+    w.sm = gld_u2(ps + u * 512 + 16 * r + 8 * (j >> 1));
+    w.dd = gld_u32(pd + u * 128 + 4 * r);
     return w;
   }
+  // word t: sub-block sub_of(j, t); element 4i + b at bits 8b + 2i
   __device__ static void isums(const W& w, const int* xw, const int*, int* is) {
     const uint32_t q[4] = {w.q.x, w.q.y, w.q.z, w.q.w};
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
+    for (int t = 0; t < 4; ++t) {
       int acc = 0;
 #pragma unroll
-      for (int a = 0; a < 4; ++a) acc = dot4((int)((q[a] >> (2 * s)) & 0x03030303u), xw[4 * s + a], acc);
-      is[s] = acc;
+      for (int i = 0; i < 4; ++i) acc = dot4((int)((q[t] >> (2 * i)) & 0x03030303u), xw[4 * t + i], acc);
+      is[t] = acc;
     }
   }
-  __device__ static double term(const W& w, int, const int* is, const int* bs, double dx) {
+  __device__ static double term(const W& w, int j, const int* is, const int* bs, double dx) {
     int s1 = 0, s2 = 0;
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      uint32_t v = (w.sm >> (8 * s)) & 0xFF;
-      s1 += (int)(v & 15) * is[s];
-      s2 += (int)(v >> 4) * bs[s];
+    for (int t = 0; t < 4; ++t) {
+      const int byte = (j & 1) + 2 * t;                 // sub-block byte inside the 8 loaded
+      const uint32_t v = ((t < 2 ? w.sm.x : w.sm.y) >> (8 * (byte & 3))) & 0xFF;
+      s1 += (int)(v & 15) * is[t];
+      s2 += (int)(v >> 4) * bs[t];
     }
     double d = half_bits_to_float(w.dd & 0xFFFF), dmin = half_bits_to_float(w.dd >> 16);
     return dx * (d * (double)s1 - dmin * (double)s2);
@@ -165,10 +188,12 @@ template <> struct Fmt<FQ2K> {
 };
 
 // ---------------------------------------------------------------- Q8_0
-template <> struct Fmt<FQ80> {
+template <> struct Fmt<FQ80> : RowMajor<32> {
   static constexpr int WPC = 32, CPS = 8, XDW = 8, NBS = 2, SPC = 1;
+  __device__ static constexpr int sub_of(int j, int t) { return j * SPC + t; }
   struct W { uint4 q0, q1; uint32_t d; };
-  __device__ static W load(const uint8_t* m, size_t nsb, size_t sbi, int b) {
+  __device__ static W load(const uint8_t* m, int64_t rows, int64_t nb, int64_t row, int64_t sb, int b) {
+    const size_t nsb = (size_t)(rows * nb), sbi = (size_t)(row * nb + sb);
     W w;
     const uint8_t* pd = m + align256(nsb * 256);
     w.q0 = gld_u4(m + sbi * 256 + 32 * b);
@@ -197,14 +222,13 @@ template <> struct Fmt<FQ80> {
 template <int FMT>
 __device__ __forceinline__ void load_x_chunk(const uint8_t* xrow, int c, int* xw, int* bs, double& dx) {
   using L = Fmt<FMT>;
-  int e0 = c * L::WPC;
-  const uint8_t* blk = xrow + (size_t)(e0 >> 8) * kQ8KBytes;
-  int o = e0 & 255;
+  const int j = c % L::CPS;
+  const uint8_t* blk = xrow + (size_t)(c / L::CPS) * kQ8KBytes;
   dx = (double)gld_f32(blk);
 #pragma unroll
-  for (int i = 0; i < L::XDW; ++i) xw[i] = (int)gld_u32(blk + 4 + o + 4 * i);
+  for (int i = 0; i < L::XDW; ++i) xw[i] = (int)gld_u32(blk + 4 + L::xoff(j, i));
 #pragma unroll
-  for (int i = 0; i < L::NBS; ++i) bs[i] = (int)(int16_t)gld_u16(blk + 260 + 2 * ((o >> 4) + i));
+  for (int t = 0; t < L::NBS; ++t) bs[t] = (int)(int16_t)gld_u16(blk + 260 + 2 * L::bsidx(j, t));
 }
 
 }  // namespace moeq

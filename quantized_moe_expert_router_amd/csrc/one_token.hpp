@@ -45,7 +45,7 @@ __device__ __forceinline__ void gateup1_body(const GateUpArgs& a, int bx, int sl
   constexpr int UNR = 2;   // the host gives at most 2 wave steps (2 / rows per step)
   const int wave = threadIdx.x >> 6, lane = lane_id();
   const int lpr = a.lpr, rps = kWave / lpr, rig = lane / lpr, lir = lane % lpr;
-  const int64_t nb = a.H / 256, nsb = a.F * nb;
+  const int64_t nb = a.H / 256;
   int xw[CPL][L::XDW], bs[CPL][L::NBS];
   double dx[CPL];
 #pragma unroll
@@ -154,9 +154,8 @@ __device__ __forceinline__ void gateup1_body(const GateUpArgs& a, int bx, int sl
         const int ch = lir + lpr * c;
         ok[u][c] = rv && ch < a.cpr;
         if (ok[u][c]) {
-          const size_t sbi = (size_t)(row[u] * nb + ch / L::CPS);
-          wg[u][c] = L::load(Wg, (size_t)nsb, sbi, ch % L::CPS);
-          wu[u][c] = L::load(Wu, (size_t)nsb, sbi, ch % L::CPS);
+          wg[u][c] = L::load(Wg, a.F, nb, row[u], ch / L::CPS, ch % L::CPS);
+          wu[u][c] = L::load(Wu, a.F, nb, row[u], ch / L::CPS, ch % L::CPS);
         }
       }
     }
@@ -188,17 +187,16 @@ constexpr int kLdsQ8 = 304;
 template <int FMT>
 __device__ __forceinline__ void load_x_chunk_lds(const uint8_t* xrow, int c, int* xw, int* bs, double& dx) {
   using L = Fmt<FMT>;
-  const int e0 = c * L::WPC;
-  const uint8_t* blk = xrow + (e0 >> 8) * kLdsQ8;
-  const int o = e0 & 255;
+  const int j = c % L::CPS;
+  const uint8_t* blk = xrow + (c / L::CPS) * kLdsQ8;
   dx = (double)*reinterpret_cast<const float*>(blk);
 #pragma unroll
-  for (int i = 0; i < L::XDW; i += 4) {
-    const uint4 v = *reinterpret_cast<const uint4*>(blk + 16 + o + 4 * i);
+  for (int i = 0; i < L::XDW; i += 4) {   // dwords i .. i+3 are contiguous in every format
+    const uint4 v = *reinterpret_cast<const uint4*>(blk + 16 + L::xoff(j, i));
     xw[i] = (int)v.x; xw[i + 1] = (int)v.y; xw[i + 2] = (int)v.z; xw[i + 3] = (int)v.w;
   }
 #pragma unroll
-  for (int i = 0; i < L::NBS; ++i) bs[i] = (int)(int16_t)ld_u16(blk + 272 + 2 * ((o >> 4) + i));
+  for (int t = 0; t < L::NBS; ++t) bs[t] = (int)(int16_t)ld_u16(blk + 272 + 2 * L::bsidx(j, t));
 }
 
 // One token, down rows of one workgroup (row block bx).  The workgroup owns
@@ -221,7 +219,7 @@ __device__ __forceinline__ void down1_body(const DownArgs& a, int bx) {
   __shared__ double swt[kMaxSlots];
   const int wave = threadIdx.x >> 6, lane = lane_id();
   const int lpr = a.lpr, rps = kWave / lpr, rig = lane / lpr, lir = lane % lpr;
-  const int64_t nb = a.F / 256, nsb = a.H * nb;
+  const int64_t nb = a.F / 256;
   const int rows_wg = rps * ST;            // at most kMaxRows (checked by the host)
   const int64_t row_base = (int64_t)bx * rows_wg;
   const int n_routed = a.k;
@@ -261,7 +259,7 @@ __device__ __forceinline__ void down1_body(const DownArgs& a, int bx) {
         for (int c = 0; c < CPL; ++c) {
           const int ch = lir + lpr * c;
           okk[st][j][c] = W != nullptr && ch < a.cpr && row < a.H;
-          if (okk[st][j][c]) w[st][j][c] = L::load(W, (size_t)nsb, (size_t)(row * nb + ch / L::CPS), ch % L::CPS);
+          if (okk[st][j][c]) w[st][j][c] = L::load(W, a.H, nb, row, ch / L::CPS, ch % L::CPS);
         }
       }
     }

@@ -88,18 +88,21 @@ __global__ __launch_bounds__(256) void k_pack(const uint8_t* __restrict__ aos, i
     pd[sbi * 2] = src[0];
     pd[sbi * 2 + 1] = src[1];
   } else if (FMT == FQ2K) {
-    uint8_t* ps = m + align256(nsb * 64);
-    uint8_t* pd = ps + align256(nsb * 16);
-    for (int c = 0; c < 4; ++c)
-      for (int a = 0; a < 4; ++a) {
+    // tiled (32-row units); see the Q2_K plane description
+    const int64_t row = sbi / nb, sb = sbi % nb, units = ((rows + 31) >> 5) * nb, u = (row >> 5) * nb + sb;
+    const int r = (int)(row & 31);
+    uint8_t* ps = m + align256((size_t)units * 2048);
+    uint8_t* pd = ps + align256((size_t)units * 512);
+    for (int g = 0; g < 2; ++g)
+      for (int p = 0; p < 8; ++p) {
+        const int j = 2 * p + g;                // sub-block of step p, half g
         uint32_t v = 0;
-        for (int s = 0; s < 4; ++s)
-          for (int b = 0; b < 4; ++b)
-            v |= (uint32_t)q2k_code(src, 64 * c + 16 * s + 4 * a + b) << (8 * b + 2 * s);
-        st_u32(m + sbi * 64 + 16 * c + 4 * a, v);
+        for (int i = 0; i < 4; ++i)
+          for (int b = 0; b < 4; ++b) v |= (uint32_t)q2k_code(src, 16 * j + 4 * i + b) << (8 * b + 2 * i);
+        st_u32(m + u * 2048 + 1024 * (p >> 2) + 16 * (32 * g + r) + 4 * (p & 3), v);
       }
-    for (int i = 0; i < 16; ++i) ps[sbi * 16 + i] = src[4 + i];
-    for (int i = 0; i < 4; ++i) pd[sbi * 4 + i] = src[i];
+    for (int i = 0; i < 16; ++i) ps[u * 512 + 16 * r + i] = src[4 + i];
+    for (int i = 0; i < 4; ++i) pd[u * 128 + 4 * r + i] = src[i];
   } else {  // Q8_0: eight 34-byte blocks per super-block
     uint8_t* pd = m + align256(nsb * 256);
     for (int b = 0; b < 8; ++b) {
@@ -136,16 +139,18 @@ __global__ __launch_bounds__(256) void k_subdots(const uint8_t* __restrict__ w, 
                                                  const uint8_t* __restrict__ xq, int64_t n_x,
                                                  int32_t* __restrict__ out) {
   using L = Fmt<FMT>;
-  const int64_t cpr = cols / L::WPC, nb = cols / 256, nsb = rows * nb;
+  const int64_t cpr = cols / L::WPC, nb = cols / 256;
   const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (gid >= n_x * rows * cpr) return;
   const int64_t c = gid % cpr, r = (gid / cpr) % rows, n = gid / (cpr * rows);
   int xw[L::XDW], bs[L::NBS], is[L::SPC];
   double dx;
   load_x_chunk<FMT>(xq + n * nb * kQ8KBytes, (int)c, xw, bs, dx);
-  typename L::W wv = L::load(w, (size_t)nsb, (size_t)(r * nb + c / L::CPS), (int)(c % L::CPS));
+  typename L::W wv = L::load(w, rows, nb, r, c / L::CPS, (int)(c % L::CPS));
   L::isums(wv, xw, bs, is);
-  for (int i = 0; i < L::SPC; ++i) out[(n * rows + r) * (cpr * L::SPC) + c * L::SPC + i] = is[i];
+  // sub-block order of the row (a chunk's sub-blocks need not be adjacent)
+  for (int i = 0; i < L::SPC; ++i)
+    out[(n * rows + r) * (cpr * L::SPC) + (c / L::CPS) * (L::CPS * L::SPC) + L::sub_of((int)(c % L::CPS), i)] = is[i];
 }
 
 int launch_subdots(int fmt, const void* w, int64_t rows, int64_t cols, const void* xq, int64_t n_x,
