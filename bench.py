@@ -48,7 +48,7 @@ def parse():
     return ap.parse_args()
 
 
-KERNEL_SOURCES = ["common.hpp", "formats.hpp", "topk.hpp", "ffn_gemv.hip", "route.hip"]
+KERNEL_SOURCES = ["common.hpp", "formats.hpp", "topk.hpp", "one_token.hpp", "ffn_gemv.hip", "route.hip"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_ffn_hbm_traffic.json")
 
 
