@@ -373,8 +373,13 @@ __device__ __forceinline__ void quantize_row_lds(const float* hrow, uint8_t* __r
 // in flight while the current unit's MFMAs run.
 __host__ __device__ constexpr int kRes(int TM) { return TM == 32 ? 8 : 16; }
 
-template <int FMT, int MODE, bool RES, int TM, int RING>
+// NW = 16 (gate/up of resident 8-row tiles only): waves 0-7 stream gate and
+// waves 8-15 stream up for the same 256 rows, so a CU holds twice the waves;
+// g reaches the up waves through LDS for h.
+template <int FMT, int MODE, bool RES, int TM, int RING, int NW = 8>
 __device__ __forceinline__ void mfma_tile(const MfmaArgs& a) {
+  static_assert(NW == 8 || (NW == 16 && MODE == 0 && RES && RING > 1), "split waves: resident gate/up ring");
+  constexpr int NT = 64 * NW;
   using M = Mf<FMT>;
   constexpr int NQ = TM / 8;
   __shared__ StageLds<TM> L[RES ? kRes(TM) : 2];
@@ -449,35 +454,37 @@ __device__ __forceinline__ void mfma_tile(const MfmaArgs& a) {
   __syncthreads();
 
   const int64_t nbK = a.K / 256;
-  const int64_t lrow = wave * 32 + (lane & 31);       // the lane's weight row inside a row block
+  const int64_t lrow = (wave % kMfWaves) * 32 + (lane & 31);   // the lane's weight row inside a row block
+  const int wmat = NW == 16 ? wave / kMfWaves : 0;              // split waves: the wave's matrix
+  const uint8_t* Wsel = wmat == 0 ? W0 : W1;
   // first unit's weights, in flight during the staging
-  typename M::Wt wn = M::load(W0, a.N, nbK, rb0 * kMfRows + lrow, 0, g);
+  typename M::Wt wn = M::load(Wsel, a.N, nbK, rb0 * kMfRows + lrow, 0, g);
   // staging work item i: 256-block i / (16 TM), row (i / 16) % TM, 16-byte piece i % 16
   if constexpr (RES) {
     const int64_t items = nbK * TM * 16;
-    for (int64_t i0 = tid; i0 < items; i0 += 4 * 512) {
+    for (int64_t i0 = tid; i0 < items; i0 += 4 * NT) {
       StageRegs r4[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const int64_t i = i0 + 512 * j;
+        const int64_t i = i0 + NT * j;
         if (i < items) r4[j] = stage_load<M::NBSP>(srows[(i >> 4) % TM], i / (16 * TM), (int)(i & 15));
       }
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const int64_t i = i0 + 512 * j;
+        const int64_t i = i0 + NT * j;
         if (i < items) stage_store<M::NBSP, TM>(L[i / (16 * TM)], r4[j], (int)((i >> 4) % TM), (int)(i & 15));
       }
     }
     __syncthreads();
   }
-  const int64_t nmat = MODE == 0 ? 2 : 1;
+  const int64_t nmat = MODE == 0 && NW == 8 ? 2 : 1;   // matrices a wave walks
 
   if constexpr (RES && RING > 1) {
   // RING weight units in flight per wave (memory-bound tiles): ring slot j
   // holds unit u0 + j, and the loop is unrolled by RING so every slot index
   // is static.  Units run (row block, 256-block, matrix) in the same order in
   // every wave, so the row-block epilogue (with its barriers) is uniform.
-  static_assert(MODE == 1 || RING % 2 == 0, "gate/up units alternate between the two matrices");
+  static_assert(MODE == 1 || NW == 16 || RING % 2 == 0, "gate/up units alternate between the two matrices");
   const int64_t U = (rb1 - rb0) * nbK * nmat;
   typename M::Wt ring[RING];
   ring[0] = wn;
@@ -489,7 +496,9 @@ __device__ __forceinline__ void mfma_tile(const MfmaArgs& a) {
       if (++l_sb == nbK) { l_sb = 0; ++l_rb; }
     }
   };
-  auto load_unit = [&]() { return M::load(l_mat == 0 ? W0 : W1, a.N, nbK, l_rb * kMfRows + lrow, l_sb, g); };
+  auto load_unit = [&]() {
+    return M::load(NW == 16 ? Wsel : (l_mat == 0 ? W0 : W1), a.N, nbK, l_rb * kMfRows + lrow, l_sb, g);
+  };
   adv_l();
 #pragma unroll
   for (int j = 1; j < RING; ++j)
@@ -502,7 +511,7 @@ __device__ __forceinline__ void mfma_tile(const MfmaArgs& a) {
 #pragma unroll
     for (int j = 0; j < RING; ++j) {
       if (u0 + j < U) {
-        const int mat = MODE == 0 ? (j & 1) : 0;
+        const int mat = MODE == 0 && NW == 8 ? (j & 1) : 0;
         const typename M::Wt& wc = ring[j];
         StageLds<TM>& S = L[c_sb];
         const uint8_t* qrow = arow ? &S.qs[lane & 31][0] : zrow;
@@ -516,12 +525,26 @@ __device__ __forceinline__ void mfma_tile(const MfmaArgs& a) {
           const int64_t wrow = c_rb * kMfRows + lrow;
           if constexpr (MODE == 0) {
             __shared__ float hs2[TM][kMfRows + 4];
+            if constexpr (NW == 16) {
+              __shared__ double gx[TM][kMfRows];
+              if (wmat == 0) {
 #pragma unroll
-            for (int r = 0; r < 4 * NQ; ++r) hs2[out_row(r, g)][lrow] = (float)(silu64(acc0[r]) * acc1[r]);
+                for (int r = 0; r < 4 * NQ; ++r) gx[out_row(r, g)][lrow] = acc0[r];
+              }
+              __syncthreads();
+              if (wmat == 1) {
+#pragma unroll
+                for (int r = 0; r < 4 * NQ; ++r)
+                  hs2[out_row(r, g)][lrow] = (float)(silu64(gx[out_row(r, g)][lrow]) * acc0[r]);
+              }
+            } else {
+#pragma unroll
+              for (int r = 0; r < 4 * NQ; ++r) hs2[out_row(r, g)][lrow] = (float)(silu64(acc0[r]) * acc1[r]);
+            }
             __syncthreads();
-            for (int m = wave; m < n; m += kMfWaves)
+            for (int m = wave; m < n; m += NW)
               quantize_row_lds(&hs2[m][0], a.hq + orow[m] * a.hq_stride + c_rb * kQ8KBytes);
-            __syncthreads();   // hs2 is rewritten by the next row block
+            __syncthreads();   // hs2 (and gx) are rewritten by the next row block
           } else {
 #pragma unroll
             for (int r = 0; r < 4 * NQ; ++r) {
@@ -621,6 +644,11 @@ __global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_pe
     MfmaArgs a) {
   mfma_tile<FMT, MODE, true, 8, kRing<FMT>>(a);
 }
+// gate/up of the same tiles on 16 waves (gate and up on separate waves)
+template <int FMT>
+__global__ __launch_bounds__(1024) void k_mfma_ring16(MfmaArgs a) {
+  mfma_tile<FMT, 0, true, 8, kRing<FMT>, 16>(a);
+}
 
 // Tile lists of the routed experts whose row count exceeds `thr`: experts
 // with at most kThinRows rows get one 8-row tile, the others 32-row tiles; a
@@ -688,35 +716,52 @@ int launch_mfma_plan(const int32_t* active, const int32_t* offsets, int thr, int
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
+namespace {
+
+// Kernel choice for one (format, mode, tile height): 8-row tiles of every
+// format but Q6_K (whose per-sub-block scaling needs more registers) run the
+// ring kernels when their activations fit in LDS, gate/up of Q2_K and Q8_0
+// on 16 waves; everything else runs the one-unit-ahead tiles.
+template <int F, int MD, int TM>
+void launch_tile(dim3 grid, const MfmaArgs& a, int64_t nbK, hipStream_t s) {
+  if constexpr (TM == 8 && F != FQ6K) {
+    if (nbK <= kRes(TM)) {
+      if constexpr (MD == 0 && (F == FQ2K || F == FQ80))
+        hipLaunchKernelGGL((k_mfma_ring16<F>), grid, dim3(1024), 0, s, a);
+      else
+        hipLaunchKernelGGL((k_mfma_ring<F, MD>), grid, dim3(512), 0, s, a);
+    } else {
+      hipLaunchKernelGGL((k_mfma_thin<F, MD, false>), grid, dim3(512), 0, s, a);
+    }
+  } else {
+    if (nbK <= kRes(TM)) hipLaunchKernelGGL((k_mfma<F, MD, true, TM>), grid, dim3(512), 0, s, a);
+    else hipLaunchKernelGGL((k_mfma<F, MD, false, TM>), grid, dim3(512), 0, s, a);
+  }
+}
+
+template <int F>
+void launch_fmt(int mode, bool thin, dim3 grid, const MfmaArgs& a, int64_t nbK, hipStream_t s) {
+  if (mode == 0) {
+    if (thin) launch_tile<F, 0, 8>(grid, a, nbK, s);
+    else launch_tile<F, 0, 32>(grid, a, nbK, s);
+  } else {
+    if (thin) launch_tile<F, 1, 8>(grid, a, nbK, s);
+    else launch_tile<F, 1, 32>(grid, a, nbK, s);
+  }
+}
+
+}  // namespace
+
 int launch_mfma(int fmt, int mode, bool thin, dim3 grid, const MfmaArgs& a, hipStream_t s) {
   if (grid.x == 0 || grid.y == 0) return 0;
   const int64_t nbK = a.K / 256;
-#define MOEQ_MF1(F, MD, TM)                                                                             \
-  if (TM == 8 && F != FQ6K) {                                                                         \
-    if (nbK <= kRes(TM)) hipLaunchKernelGGL((k_mfma_ring<F, MD>), grid, dim3(512), 0, s, a);          \
-    else hipLaunchKernelGGL((k_mfma_thin<F, MD, false>), grid, dim3(512), 0, s, a);                   \
-  } else if (nbK <= kRes(TM)) {                                                                       \
-    hipLaunchKernelGGL((k_mfma<F, MD, true, TM>), grid, dim3(512), 0, s, a);                          \
-  } else {                                                                                            \
-    hipLaunchKernelGGL((k_mfma<F, MD, false, TM>), grid, dim3(512), 0, s, a);                         \
-  }
-#define MOEQ_MF(F)                                   \
-  if (mode == 0) {                                   \
-    if (thin) { MOEQ_MF1(F, 0, 8) }                  \
-    else { MOEQ_MF1(F, 0, 32) }                      \
-  } else {                                           \
-    if (thin) { MOEQ_MF1(F, 1, 8) }                  \
-    else { MOEQ_MF1(F, 1, 32) }                      \
-  }
   switch (fmt) {
-    case FQ4K: MOEQ_MF(FQ4K) break;
-    case FQ6K: MOEQ_MF(FQ6K) break;
-    case FQ2K: MOEQ_MF(FQ2K) break;
-    case FQ80: MOEQ_MF(FQ80) break;
+    case FQ4K: launch_fmt<FQ4K>(mode, thin, grid, a, nbK, s); break;
+    case FQ6K: launch_fmt<FQ6K>(mode, thin, grid, a, nbK, s); break;
+    case FQ2K: launch_fmt<FQ2K>(mode, thin, grid, a, nbK, s); break;
+    case FQ80: launch_fmt<FQ80>(mode, thin, grid, a, nbK, s); break;
     default: return -2;
   }
-#undef MOEQ_MF
-#undef MOEQ_MF1
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
