@@ -66,8 +66,10 @@ __global__ __launch_bounds__(256) void k_logits(const float* __restrict__ x, con
     }
 #pragma unroll
     for (int t = 0; t < kLogitTok; ++t) {
-      const double v = wave_sum(acc[t]);
-      if (lane == 0) part[wave][t] = v;
+      if (t < nt) {                          // only the tile's tokens (one at decode)
+        const double v = wave_sum(acc[t]);
+        if (lane == 0) part[wave][t] = v;
+      }
     }
     __syncthreads();
     if (threadIdx.x < nt) {
