@@ -211,7 +211,8 @@ int nper_of(int64_t E) { return E <= 256 ? 4 : E <= 512 ? 8 : E <= 1024 ? 16 : 6
 // Enqueue the expert FFN (everything after the routing) on `s`.
 int ffn_enqueue(const moeq_ffn_desc* d, const void* x_q8K, const int32_t* topk_ids, const float* topk_w,
                 const int32_t* expert_offsets, const int32_t* pairs, const int32_t* active,
-                const float* shared_scale, float* y, uint8_t* wsb, const InlineRoute* ir, hipStream_t s) {
+                const float* shared_scale, float* y, uint8_t* wsb, const InlineRoute* ir, bool planned,
+                hipStream_t s) {
   const FfnLayout L = ffn_layout(d);
   const bool sh = d->sh_gate != nullptr;
   const bool same_shape = sh && d->sh_fmt_gate == d->fmt_gate && d->sh_fmt_down == d->fmt_down &&
@@ -326,7 +327,7 @@ int ffn_enqueue(const moeq_ffn_desc* d, const void* x_q8K, const int32_t* topk_i
     return launch_mfma(fmt, mode, thin, dim3(gx, gy), a, s);
   };
 
-  if (mfma) {
+  if (mfma && !planned) {
     if ((rc = launch_mfma_plan(active, expert_offsets, thr, (int)L.max_tiles, tiles, tcount, thin_tiles, tcount + 1,
                                s)))
       return rc;
@@ -385,7 +386,7 @@ int moeq_expert_ffn(const moeq_ffn_desc* d, const void* x_q8K, const int32_t* to
   if (!ws || !aligned(ws, 256)) return MOEQ_E_INVALID;
   if (ws_bytes < ffn_layout(d).total) return MOEQ_E_WORKSPACE;
   return hip_status(ffn_enqueue(d, x_q8K, topk_ids, topk_w, expert_offsets, pairs, active, shared_scale, y,
-                                (uint8_t*)ws, nullptr, (hipStream_t)stream));
+                                (uint8_t*)ws, nullptr, false, (hipStream_t)stream));
 }
 
 namespace {
@@ -444,13 +445,20 @@ int moeq_moe_layer(const moeq_route_desc* r, const moeq_ffn_desc* f, const float
     if ((rc = launch_logits(1, r->H, r->E, x, w_router, bias, lg, xq, s))) return hip_status(rc);
     InlineRoute ir{lg, r->gating, r->scale, topk_ids, expert_offsets, pairs, active, topk_w};
     return hip_status(ffn_enqueue(f, xq, topk_ids, topk_w, expert_offsets, pairs, active, shared_scale, y, wsb, &ir,
-                                  s));
+                                  false, s));
   }
+  // the routing kernel also builds the MFMA tile lists of the FFN (one launch fewer)
+  const FfnLayout FL = ffn_layout(f);
+  const int thr = gemv_max_of(f);
+  const bool mfma = f->T > thr;
+  const MfmaPlan plan{thr, (int)FL.max_tiles, (int4*)(wsb + L.off_ffn + FL.off_tiles),
+                      (int32_t*)(wsb + L.off_ffn + FL.off_count), (int4*)(wsb + L.off_ffn + FL.off_thin),
+                      (int32_t*)(wsb + L.off_ffn + FL.off_count) + 1};
   if ((rc = launch_route(r->T, r->H, r->E, r->k, r->gating, r->scale, x, w_router, bias, logits, topk_ids, topk_w,
-                         expert_offsets, pairs, active, xq, wsb + L.off_route, s)))
+                         expert_offsets, pairs, active, xq, wsb + L.off_route, s, mfma ? &plan : nullptr)))
     return hip_status(rc);
   return hip_status(ffn_enqueue(f, xq, topk_ids, topk_w, expert_offsets, pairs, active, shared_scale, y, wsb,
-                                nullptr, s));
+                                nullptr, mfma, s));
 }
 
 int moeq_ffn_h_view(const moeq_ffn_desc* d, void* ws, size_t ws_bytes, void** hq_routed, void** hq_shared) {

@@ -37,6 +37,7 @@
 // term per super-block = d_x * (d * S1 - dmin * S2) in fp64, summed over the
 // super-blocks in order; h = fl32(silu(g) * u); y rows in fp32.
 #include "formats.hpp"
+#include "mfma_plan.hpp"
 #include "launch.hpp"
 
 namespace moeq {
@@ -44,7 +45,6 @@ namespace moeq {
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v16i __attribute__((ext_vector_type(16)));
 
-constexpr int kTileT = 32;         // activation rows (tokens / pairs) per tile
 constexpr int kMfWaves = 8;        // waves per workgroup, 32 weight rows each
 constexpr int kMfRows = 32 * kMfWaves;
 constexpr int kQsStride = 272;     // LDS bytes per staged row: 256 + 16 (bank spread)
@@ -650,68 +650,17 @@ __global__ __launch_bounds__(1024) void k_mfma_ring16(MfmaArgs a) {
   mfma_tile<FMT, 0, true, 8, kRing<FMT>, 16>(a);
 }
 
-// Tile lists of the routed experts whose row count exceeds `thr`: experts
-// with at most kThinRows rows get one 8-row tile, the others 32-row tiles; a
-// tile is (expert, first row, rows, list offset), experts in union order
-// (absent experts too: their down tiles write zero rows).  One workgroup.
-constexpr int kThinRows = 8;
-
-__global__ __launch_bounds__(1024) void k_mfma_plan(const int32_t* __restrict__ active,
+// Tile lists of the routed experts (one workgroup; see mfma_plan.hpp).
+__global__ __launch_bounds__(64) void k_mfma_plan(const int32_t* __restrict__ active,
                                                     const int32_t* __restrict__ offsets, int thr, int max_tiles,
                                                     int4* __restrict__ tiles, int32_t* __restrict__ count,
                                                     int4* __restrict__ thin, int32_t* __restrict__ thin_count) {
-  __shared__ int part[1024], tpart[1024];
-  const int na = active[0];
-  const int per = (na + 1023) / 1024;
-  const int s0 = threadIdx.x * per;
-  int local = 0, tlocal = 0;
-  for (int i = 0; i < per; ++i) {
-    const int s = s0 + i;
-    if (s < na) {
-      const int e = active[1 + s];
-      const int ne = offsets[e + 1] - offsets[e];
-      if (ne > thr) {
-        if (ne <= kThinRows) ++tlocal;
-        else local += (ne + kTileT - 1) / kTileT;
-      }
-    }
-  }
-  part[threadIdx.x] = local;
-  tpart[threadIdx.x] = tlocal;
-  __syncthreads();
-  for (int o = 1; o < 1024; o <<= 1) {   // inclusive scans (Hillis-Steele)
-    const int v = threadIdx.x >= o ? part[threadIdx.x - o] : 0;
-    const int tv = threadIdx.x >= o ? tpart[threadIdx.x - o] : 0;
-    __syncthreads();
-    part[threadIdx.x] += v;
-    tpart[threadIdx.x] += tv;
-    __syncthreads();
-  }
-  int base = part[threadIdx.x] - local, tbase = tpart[threadIdx.x] - tlocal;
-  if (threadIdx.x == 1023) {
-    *count = part[1023] < max_tiles ? part[1023] : max_tiles;
-    *thin_count = tpart[1023];
-  }
-  for (int i = 0; i < per; ++i) {
-    const int s = s0 + i;
-    if (s < na) {
-      const int e = active[1 + s];
-      const int ne = offsets[e + 1] - offsets[e];
-      if (ne > thr && ne <= kThinRows) {
-        thin[tbase++] = make_int4(e, 0, ne, offsets[e]);
-      } else if (ne > thr) {
-        for (int t0 = 0; t0 < ne; t0 += kTileT) {
-          if (base < max_tiles) tiles[base] = make_int4(e, t0, ne - t0 < kTileT ? ne - t0 : kTileT, offsets[e]);
-          ++base;
-        }
-      }
-    }
-  }
+  mfma_plan_block(active, offsets, MfmaPlan{thr, max_tiles, tiles, count, thin, thin_count});
 }
 
 int launch_mfma_plan(const int32_t* active, const int32_t* offsets, int thr, int max_tiles, int4* tiles,
                      int32_t* count, int4* thin, int32_t* thin_count, hipStream_t s) {
-  hipLaunchKernelGGL(k_mfma_plan, dim3(1), dim3(1024), 0, s, active, offsets, thr, max_tiles, tiles, count, thin,
+  hipLaunchKernelGGL(k_mfma_plan, dim3(1), dim3(64), 0, s, active, offsets, thr, max_tiles, tiles, count, thin,
                      thin_count);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }

@@ -90,6 +90,16 @@ struct DownArgs {
 // int8 MFMA grouped GEMM (experts with more than gemv_max rows).  Tiles of 32
 // activation rows come from the plan (routed experts) or cover all T tokens
 // (shared expert).
+// Where and how the MFMA tile lists are built: experts with more than thr
+// rows, at most max_tiles 32-row tiles.
+struct MfmaPlan {
+  int thr, max_tiles;
+  int4* tiles;
+  int32_t* count;
+  int4* thin;
+  int32_t* thin_count;
+};
+
 struct MfmaArgs {
   int shared;
   const int4* tiles;            // routed: (expert, first row, rows, list offset)
@@ -123,7 +133,7 @@ int launch_logits(int64_t T, int64_t H, int64_t E, const float* x, const float* 
                   double* logits, void* xq, hipStream_t s);
 int launch_route(int64_t T, int64_t H, int64_t E, int k, int gating, float scale, const float* x,
                  const float* W, const float* bias, double* logits, int32_t* ids, float* w,
-                 int32_t* offsets, int32_t* pairs, int32_t* active, void* xq, void* ws, hipStream_t s);
+                 int32_t* offsets, int32_t* pairs, int32_t* active, void* xq, void* ws, hipStream_t s, const MfmaPlan* plan = nullptr);
 int launch_gateup(int fmt, int tt, int cpl, dim3 grid, const GateUpArgs& a, hipStream_t s);
 int launch_gateup1(int fmt, int nper, int cpl, dim3 grid, const GateUpArgs& a, hipStream_t s);
 int launch_down(int fmt, int tt, int cpl, dim3 grid, const DownArgs& a, hipStream_t s);

@@ -7,6 +7,7 @@
 #include "common.hpp"
 #include "launch.hpp"
 #include "topk.hpp"
+#include "mfma_plan.hpp"
 
 namespace moeq {
 
@@ -224,7 +225,8 @@ template <int NPER>
 __global__ __launch_bounds__(1024) void k_select_small(const double* __restrict__ logits, int64_t T, int64_t E,
                                                        int k, int gating, float scale, int32_t* __restrict__ ids,
                                                        float* __restrict__ w, int32_t* __restrict__ offsets,
-                                                       int32_t* __restrict__ pairs, int32_t* __restrict__ active) {
+                                                       int32_t* __restrict__ pairs, int32_t* __restrict__ active,
+                                                       MfmaPlan plan) {
   extern __shared__ int lds[];
   int* ids_s = lds;                                           // [T*k]
   int* cnt = ids_s + T * k;                                   // [E]
@@ -249,6 +251,10 @@ __global__ __launch_bounds__(1024) void k_select_small(const double* __restrict_
         pairs[pos] = (int32_t)(t * k + lane);
       }
     }
+  }
+  if (plan.tiles != nullptr) {   // the MFMA tile lists of the FFN that follows
+    __syncthreads();
+    mfma_plan_block(active, offsets, plan);
   }
 }
 
@@ -275,7 +281,8 @@ __global__ __launch_bounds__(256) void k_hist(const int32_t* __restrict__ ids, i
 }
 
 __global__ __launch_bounds__(1024) void k_scan(int32_t* __restrict__ hist, int64_t nchunks, int64_t E,
-                                               int32_t* __restrict__ offsets, int32_t* __restrict__ active) {
+                                               int32_t* __restrict__ offsets, int32_t* __restrict__ active,
+                                               MfmaPlan plan) {
   extern __shared__ int lds[];
   int* tot = lds;              // [E]
   int* scan_tmp = tot + E;     // [64]
@@ -294,6 +301,10 @@ __global__ __launch_bounds__(1024) void k_scan(int32_t* __restrict__ hist, int64
       hist[c * E + e] = run;
       run += h;
     }
+  }
+  if (plan.tiles != nullptr) {   // the MFMA tile lists of the FFN that follows
+    __syncthreads();
+    mfma_plan_block(active, offsets, plan);
   }
 }
 
@@ -344,7 +355,9 @@ size_t route_ws_bytes(int64_t T, int64_t E) {
 
 int launch_route(int64_t T, int64_t H, int64_t E, int k, int gating, float scale, const float* x,
                  const float* W, const float* bias, double* logits, int32_t* ids, float* w,
-                 int32_t* offsets, int32_t* pairs, int32_t* active, void* xq, void* ws, hipStream_t s) {
+                 int32_t* offsets, int32_t* pairs, int32_t* active, void* xq, void* ws, hipStream_t s,
+                 const MfmaPlan* plan) {
+  const MfmaPlan pl = plan != nullptr ? *plan : MfmaPlan{0, 0, nullptr, nullptr, nullptr, nullptr};
   if (T == 0) {
     hipLaunchKernelGGL(k_empty_lists, dim3(1), dim3(256), 0, s, E, offsets, active);
     return hipGetLastError() == hipSuccess ? 0 : -1;
@@ -355,7 +368,7 @@ int launch_route(int64_t T, int64_t H, int64_t E, int k, int gating, float scale
   if (T <= kSmallT) {
     size_t lds = (size_t)(T * k + E + 64) * sizeof(int);
 #define MOEQ_SEL(N) hipLaunchKernelGGL(k_select_small<N>, dim3(1), dim3(1024), lds, s, lg, T, E, k, gating, \
-                                        scale, ids, w, offsets, pairs, active)
+                                        scale, ids, w, offsets, pairs, active, pl)
     if (E <= 256) MOEQ_SEL(4);
     else if (E <= 512) MOEQ_SEL(8);
     else if (E <= 1024) MOEQ_SEL(16);
@@ -373,7 +386,7 @@ int launch_route(int64_t T, int64_t H, int64_t E, int k, int gating, float scale
 #undef MOEQ_TOPK
     hipLaunchKernelGGL(k_hist, dim3((unsigned)nch), dim3(256), (size_t)E * sizeof(int), s, ids, T, k, E, hist);
     hipLaunchKernelGGL(k_scan, dim3(1), dim3(1024), (size_t)(E + 64) * sizeof(int), s, hist, nch, E, offsets,
-                       active);
+                       active, pl);
     hipLaunchKernelGGL(k_scatter, dim3((unsigned)nch), dim3(64), (size_t)E * sizeof(int), s, ids, T, k, E,
                        hist, pairs);
   }
