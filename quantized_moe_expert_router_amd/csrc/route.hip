@@ -46,22 +46,37 @@ __global__ __launch_bounds__(256) void k_logits(const float* __restrict__ x, con
       float4 w[4];
 #pragma unroll
       for (int u = 0; u < 4; ++u) w[u] = (i + u * kWave < i1) ? w4[i + u * kWave] : make_float4(0.f, 0.f, 0.f, 0.f);
+      // four tokens at a time: all their activation loads go out before the
+      // first FMA waits for them
 #pragma unroll
-      for (int t = 0; t < kLogitTok; ++t) {
-        if (t < nt) {
-          const float4* x4 = reinterpret_cast<const float4*>(x + (t0 + t) * H);
-          double a = acc[t];
+      for (int tg = 0; tg < kLogitTok; tg += 4) {
+        if (tg < nt) {
+          float4 xv[4][4];
 #pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            if (i + u * kWave < i1) {
-              const float4 xv = x4[i + u * kWave];
-              a = fma((double)w[u].x, (double)xv.x, a);
-              a = fma((double)w[u].y, (double)xv.y, a);
-              a = fma((double)w[u].z, (double)xv.z, a);
-              a = fma((double)w[u].w, (double)xv.w, a);
+          for (int tt = 0; tt < 4; ++tt) {
+            if (tg + tt < nt) {
+              const float* xr = x + (t0 + tg + tt) * H;
+#pragma unroll
+              for (int u = 0; u < 4; ++u)
+                xv[tt][u] = i + u * kWave < i1 ? gld_f4(xr + 4 * (i + u * kWave)) : make_float4(0.f, 0.f, 0.f, 0.f);
             }
           }
-          acc[t] = a;
+#pragma unroll
+          for (int tt = 0; tt < 4; ++tt) {
+            if (tg + tt < nt) {
+              double a = acc[tg + tt];
+#pragma unroll
+              for (int u = 0; u < 4; ++u) {
+                if (i + u * kWave < i1) {
+                  a = fma((double)w[u].x, (double)xv[tt][u].x, a);
+                  a = fma((double)w[u].y, (double)xv[tt][u].y, a);
+                  a = fma((double)w[u].z, (double)xv[tt][u].z, a);
+                  a = fma((double)w[u].w, (double)xv[tt][u].w, a);
+                }
+              }
+              acc[tg + tt] = a;
+            }
+          }
         }
       }
     }
