@@ -288,7 +288,15 @@ int ffn_enqueue(const moeq_ffn_desc* d, const void* x_q8K, const int32_t* topk_i
   int4* tiles = (int4*)(wsb + L.off_tiles);
   int4* thin_tiles = (int4*)(wsb + L.off_thin);
   int32_t* tcount = (int32_t*)(wsb + L.off_count);
+  // fp32 h between gate/up and down for the 8-row tiles (see launch_mfma)
+  // when both of their launches can take it
+  auto hf_ok = [&](bool shared_exp) {
+    const int fg = shared_exp ? d->sh_fmt_gate : d->fmt_gate, fd = shared_exp ? d->sh_fmt_down : d->fmt_down;
+    const int64_t Fx = shared_exp ? d->F_shared : d->F;
+    return fg != FQ6K && fd != FQ6K && d->H / 256 <= kHfMaxBlocks && Fx / 256 <= kHfMaxBlocks;
+  };
   auto mfma_launch = [&](int mode, bool shared_exp, bool thin) -> int {
+    const bool hf = thin && hf_ok(shared_exp);
     MfmaArgs a{};
     a.shared = shared_exp ? 1 : 0;
     a.tiles = thin ? thin_tiles : tiles;
@@ -299,6 +307,8 @@ int ffn_enqueue(const moeq_ffn_desc* d, const void* x_q8K, const int32_t* topk_i
     const int64_t Fx = shared_exp ? d->F_shared : d->F;
     const int64_t hq_stride = (Fx / 256) * kQ8KBytes;
     uint8_t* hq = shared_exp ? wsb + L.off_hqs : wsb + L.off_hq;
+    a.hf = (float*)(wsb + L.off_h) + (shared_exp ? d->T * d->k * L.Fmax : 0);
+    a.hf_stride = L.Fmax;
     int fmt;
     const int tm = thin ? kThinT : 32;
     unsigned gx = shared_exp ? (unsigned)((d->T + tm - 1) / tm) : (unsigned)(thin ? L.max_thin : L.max_tiles);
@@ -310,12 +320,13 @@ int ffn_enqueue(const moeq_ffn_desc* d, const void* x_q8K, const int32_t* topk_i
       a.N = Fx; a.K = d->H;
       a.src = (const uint8_t*)x_q8K; a.src_stride = (d->H / 256) * kQ8KBytes;
       a.hq = hq; a.hq_stride = hq_stride;
-      gy = (unsigned)(Fx / 256);
+      gy = (unsigned)(Fx / (hf ? kHfRows : 256));
     } else {
       fmt = shared_exp ? d->sh_fmt_down : d->fmt_down;
       a.sh_w0 = (const uint8_t*)d->sh_down;
       a.N = d->H; a.K = Fx;
       a.src = hq; a.src_stride = hq_stride;
+      a.hq = hq; a.hq_stride = hq_stride;   // fp32 h: the q8_K(h) view is written while staging
       gy = (unsigned)(d->H / 256);
     }
     // Row blocks per workgroup: enough workgroups to fill the chip several
@@ -324,7 +335,7 @@ int ffn_enqueue(const moeq_ffn_desc* d, const void* x_q8K, const int32_t* topk_i
     const int64_t nrb = gy;
     a.rb = std::max<int64_t>(1, std::min<int64_t>(nrb, (int64_t)gx * nrb / 2048));
     gy = (unsigned)((nrb + a.rb - 1) / a.rb);
-    return launch_mfma(fmt, mode, thin, dim3(gx, gy), a, s);
+    return launch_mfma(fmt, mode, thin, hf, dim3(gx, gy), a, s);
   };
 
   if (mfma && !planned) {

@@ -36,6 +36,8 @@
 //   Q8_0  w = d_b*q: one MFMA per 32-block, scaled by d_b in fp64.
 // term per super-block = d_x * (d * S1 - dmin * S2) in fp64, summed over the
 // super-blocks in order; h = fl32(silu(g) * u); y rows in fp32.
+#include <type_traits>
+
 #include "formats.hpp"
 #include "mfma_plan.hpp"
 #include "launch.hpp"
@@ -333,6 +335,63 @@ __device__ __forceinline__ void stage_store(StageLds<TM>& L, const StageRegs& r,
   }
 }
 
+// Staging of fp32 h (the fp32-h variant of the down tiles): thread (m, piece)
+// quantises elements 16*piece .. +15 of 256-block sb of tile row m with the
+// amax of the block's 16 threads (one 16-lane DPP row), by the same definition
+// as quantize_row_lds, and writes codes, scale and split block sums to LDS
+// (and, with `view`, the q8_K block to the q8_K(h) rows).  Rows beyond the
+// tile (hrow null) stage as zero blocks.
+struct StageF { float4 v[4]; };
+__device__ __forceinline__ StageF stage_load_f(const float* hrow, int64_t sb, int piece) {
+  StageF r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    r.v[i] = hrow != nullptr ? gld_f4(hrow + sb * 256 + 16 * piece + 4 * i) : make_float4(0.f, 0.f, 0.f, 0.f);
+  return r;
+}
+template <int NBSP, int TM>
+__device__ __forceinline__ void stage_quant(StageLds<TM>& L, const StageF& r, int m, int piece, uint8_t* view) {
+  const float v[16] = {r.v[0].x, r.v[0].y, r.v[0].z, r.v[0].w, r.v[1].x, r.v[1].y, r.v[1].z, r.v[1].w,
+                       r.v[2].x, r.v[2].y, r.v[2].z, r.v[2].w, r.v[3].x, r.v[3].y, r.v[3].z, r.v[3].w};
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(v[i]));
+  amax = fmaxf(amax, dpp_all_f<kDppXor1>(amax));
+  amax = fmaxf(amax, dpp_all_f<kDppXor2>(amax));
+  amax = fmaxf(amax, dpp_all_f<kDppRowRor4>(amax));
+  amax = fmaxf(amax, dpp_all_f<kDppRowRor8>(amax));
+  const float id = amax == 0.0f ? 0.0f : __fdiv_rn(127.0f, amax);
+  const bool zero = amax == 0.0f || __builtin_isinf(id);
+  uint32_t q[4] = {0u, 0u, 0u, 0u};
+  int sum = 0;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int c = zero ? 0 : q8_code(v[i], id);
+    q[i >> 2] |= (uint32_t)(c & 255) << (8 * (i & 3));
+    sum += c;
+  }
+  const float d = zero ? 0.0f : __fdiv_rn(amax, 127.0f);
+  *reinterpret_cast<uint4*>(&L.qs[m][16 * piece]) = make_uint4(q[0], q[1], q[2], q[3]);
+  if (piece == 0) L.dx[m] = d;
+  if constexpr (NBSP == 16) {
+    L.bsp[m][0][piece] = (uint8_t)(sum & 63);
+    L.bsp[m][1][piece] = (uint8_t)((sum >> 6) & 255);
+  } else if constexpr (NBSP == 8) {
+    // entry j = sums of sub-blocks 2j and 2j+1, written by the even thread;
+    // the odd thread clears entry 8 + j
+    const int pair = sum + dpp_all_i<kDppXor1>(sum);
+    const int e = (piece & 1) ? 8 + (piece >> 1) : (piece >> 1);
+    L.bsp[m][0][e] = (piece & 1) ? (uint8_t)0 : (uint8_t)(pair & 63);
+    L.bsp[m][1][e] = (piece & 1) ? (uint8_t)0 : (uint8_t)((pair >> 6) & 255);
+  }
+  if (view != nullptr) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) gst_u32(view + 4 + 16 * piece + 4 * i, q[i]);
+    gst_i16(view + 260 + 2 * piece, (int16_t)sum);
+    if (piece == 0) gst_f32(view, d);
+  }
+}
+
 // q8_K of one 256-wide fp32 row held in LDS, by one wave (4 values per lane),
 // identical to the definition (amax; id = 127/amax correctly rounded;
 // q = rint(h*id) clamped; d = amax/127; per-16 sums; amax == 0 or an infinite
@@ -355,6 +414,59 @@ __device__ __forceinline__ void quantize_row_lds(const float* hrow, uint8_t* __r
   if (lane == 0) gst_f32(o, zero ? 0.0f : __fdiv_rn(amax, 127.0f));
 }
 
+// Staging of the tile's resident activation blocks (all nbK of them) into
+// LDS, in rounds of R items per thread: work item i is 256-block i / (16 n),
+// row (i / 16) % n, 16-byte piece i % 16, so the 16 items of one (block, row)
+// sit in one 16-lane row of a wave.  Only the tile's n real rows are staged:
+// rows n .. TM-1 of the stage hold stale LDS, and every output of those MFMA
+// rows is dropped (the combine, h and y stores all stop at row n), so their
+// values never matter.  QUANT: the rows are fp32 h, quantised to q8_K on the
+// way.  The caller splits the first round into its loads and its stores (the
+// ring of weight loads goes out in between), then stages the rest.
+template <bool QUANT> struct StageRound {
+  static constexpr int R = QUANT ? 2 : 4;   // items per thread and round
+  typename std::conditional<QUANT, StageF, StageRegs>::type v[R];
+};
+template <int NBSP, int NT, bool QUANT>
+__device__ __forceinline__ void stage_round_load(StageRound<QUANT>& b, const uint8_t* const* srows, int i0,
+                                                 int per_blk, int items) {
+#pragma unroll
+  for (int j = 0; j < StageRound<QUANT>::R; ++j) {
+    const int i = i0 + NT * j;
+    if (i < items) {
+      const int blk = i / per_blk, m = (i - blk * per_blk) >> 4;
+      if constexpr (QUANT) b.v[j] = stage_load_f(reinterpret_cast<const float*>(srows[m]), blk, i & 15);
+      else b.v[j] = stage_load<NBSP>(srows[m], blk, i & 15);
+    }
+  }
+}
+template <int NBSP, int TM, int NT, bool QUANT>
+__device__ __forceinline__ void stage_round_store(const StageRound<QUANT>& b, StageLds<TM>* L,
+                                                  uint8_t* const* vrows, int i0, int per_blk, int items) {
+#pragma unroll
+  for (int j = 0; j < StageRound<QUANT>::R; ++j) {
+    const int i = i0 + NT * j;
+    if (i < items) {
+      const int blk = i / per_blk, m = (i - blk * per_blk) >> 4;
+      if constexpr (QUANT)
+        stage_quant<NBSP, TM>(L[blk], b.v[j], m, i & 15, vrows[m] != nullptr ? vrows[m] + blk * kQ8KBytes : nullptr);
+      else
+        stage_store<NBSP, TM>(L[blk], b.v[j], m, i & 15);
+    }
+  }
+}
+template <int NBSP, int TM, int NT, bool QUANT>
+__device__ __forceinline__ void stage_rest(StageLds<TM>* L, const uint8_t* const* srows, uint8_t* const* vrows,
+                                           int tid, int per_blk, int items) {
+  constexpr int R = StageRound<QUANT>::R;
+  for (int i0 = tid + R * NT; i0 < items; i0 += R * NT) {
+    StageRound<QUANT> b;
+    stage_round_load<NBSP, NT, QUANT>(b, srows, i0, per_blk, items);
+    stage_round_store<NBSP, TM, NT, QUANT>(b, L, vrows, i0, per_blk, items);
+  }
+  __syncthreads();
+}
+
 // ------------------------------------------------------------ the kernel
 //
 // MODE 0 (gate/up): A = q8_K(x) rows of the tile's tokens, W0 = gate, W1 = up;
@@ -372,13 +484,25 @@ __device__ __forceinline__ void quantize_row_lds(const float* hrow, uint8_t* __r
 // the weight loads of the next (row block, 256-block, matrix) unit are always
 // in flight while the current unit's MFMAs run.
 __host__ __device__ constexpr int kRes(int TM) { return TM == 32 ? 8 : 16; }
+static_assert(kRes(8) == kHfMaxBlocks, "resident 8-row tiles");
 
 // NW = 16 (gate/up of resident 8-row tiles only): waves 0-7 stream gate and
 // waves 8-15 stream up for the same 256 rows, so a CU holds twice the waves;
 // g reaches the up waves through LDS for h.
-template <int FMT, int MODE, bool RES, int TM, int RING, int NW = 8>
+// HF (fp32 h, resident ring tiles only): mode 0 writes h = fl32(silu(g) u) as
+// fp32 rows, so a workgroup needs no whole 256-row block for q8_K(h) and may
+// cover fewer rows (NW = 4: two gate and two up waves over 64 rows, several
+// workgroups per CU, every CU busy on small unions); mode 1 then quantises
+// the fp32 rows to q8_K while staging them.
+template <int FMT, int MODE, bool RES, int TM, int RING, int NW = 8, bool HF = false>
 __device__ __forceinline__ void mfma_tile(const MfmaArgs& a) {
-  static_assert(NW == 8 || (NW == 16 && MODE == 0 && RES && RING > 1), "split waves: resident gate/up ring");
+  static_assert(NW == 8 || (NW == 16 && MODE == 0 && RES && RING > 1) || (NW == 4 && MODE == 0 && HF),
+                "split waves: resident gate/up ring");
+  static_assert(!HF || (RES && RING > 1), "fp32 h: resident ring tiles");
+  constexpr bool SPLIT = MODE == 0 && NW != 8;        // gate and up on separate waves
+  constexpr int WPM = SPLIT ? NW / 2 : NW;            // waves per matrix
+  constexpr int RB = 32 * WPM;                        // weight rows per row block
+  static_assert(MODE == 1 || HF || RB == 256, "q8_K(h) in the epilogue needs whole 256-row blocks");
   constexpr int NT = 64 * NW;
   using M = Mf<FMT>;
   constexpr int NQ = TM / 8;
@@ -386,7 +510,8 @@ __device__ __forceinline__ void mfma_tile(const MfmaArgs& a) {
   __shared__ int64_t orow[TM];
   __shared__ double owt[TM];
   __shared__ const uint8_t* srows[TM];
-  __shared__ __align__(16) uint8_t zrow[kQsStride];   // A rows beyond the staged ones read zeros
+  __shared__ uint8_t* vrows[TM];                      // HF mode 1: q8_K(h) view rows (workgroup row 0 only)
+  __shared__ __align__(16) uint8_t zrow[kQsStride];   // A rows past the tile height read zeros
 
   // ---- tile: expert (or the shared expert) and its rows t0 .. t0+n-1
   int e = -1, t0, n;
@@ -400,7 +525,7 @@ __device__ __forceinline__ void mfma_tile(const MfmaArgs& a) {
     const int4 tl = a.tiles[blockIdx.x];
     e = tl.x; t0 = tl.y; n = tl.z; list_off = tl.w;
   }
-  const int64_t nrb = a.N / kMfRows;
+  const int64_t nrb = a.N / RB;
   const int64_t rb0 = (int64_t)blockIdx.y * a.rb;
   const int64_t rb1 = rb0 + a.rb < nrb ? rb0 + a.rb : nrb;
   if (rb0 >= nrb) return;
@@ -416,10 +541,10 @@ __device__ __forceinline__ void mfma_tile(const MfmaArgs& a) {
     if (!resident) {
       // not resident: its pairs add exactly nothing (their down rows are zero)
       if (MODE == 1) {
-        const int64_t cols = (rb1 - rb0) * kMfRows;
+        const int64_t cols = (rb1 - rb0) * RB;
         for (int64_t i = threadIdx.x; i < n * cols; i += blockDim.x) {
           const int p = a.pairs[list_off + t0 + i / cols];
-          gst_f32(a.yp + (int64_t)p * a.N + rb0 * kMfRows + i % cols, 0.0f);
+          gst_f32(a.yp + (int64_t)p * a.N + rb0 * RB + i % cols, 0.0f);
         }
       }
       return;
@@ -431,9 +556,10 @@ __device__ __forceinline__ void mfma_tile(const MfmaArgs& a) {
   const bool arow = (lane & 31) < TM;                  // the lane's A row is staged
   for (int i = tid; i < kQsStride / 4; i += blockDim.x) reinterpret_cast<uint32_t*>(zrow)[i] = 0u;
   if (tid < TM) {
-    int64_t orr = -1, ridx = 0;
+    int64_t orr = -1, ridx = 0, vidx = 0;
     double wt = 0.0;
     const uint8_t* sr = nullptr;
+    uint8_t* vr = nullptr;
     if (tid < n) {
       if (a.shared) {
         ridx = t0 + tid;
@@ -445,64 +571,83 @@ __device__ __forceinline__ void mfma_tile(const MfmaArgs& a) {
         orr = p;
         wt = MODE == 1 ? (double)a.topk_w[p] : 0.0;
       }
-      sr = a.src + ridx * a.src_stride;
+      vidx = a.shared ? t0 + tid : ridx;
+      if (HF && MODE == 1) {
+        sr = reinterpret_cast<const uint8_t*>(a.hf + ridx * a.hf_stride);
+        if (a.hq != nullptr && blockIdx.y == 0) vr = a.hq + vidx * a.hq_stride;
+      } else {
+        sr = a.src + ridx * a.src_stride;
+      }
     }
     orow[tid] = orr;
     owt[tid] = wt;
     srows[tid] = sr;
+    vrows[tid] = vr;
   }
   __syncthreads();
 
   const int64_t nbK = a.K / 256;
-  const int64_t lrow = (wave % kMfWaves) * 32 + (lane & 31);   // the lane's weight row inside a row block
-  const int wmat = NW == 16 ? wave / kMfWaves : 0;              // split waves: the wave's matrix
+  const int64_t lrow = (wave % WPM) * 32 + (lane & 31);        // the lane's weight row inside a row block
+  const int wmat = SPLIT ? wave / WPM : 0;                      // split waves: the wave's matrix
   const uint8_t* Wsel = wmat == 0 ? W0 : W1;
-  // first unit's weights, in flight during the staging
-  typename M::Wt wn = M::load(Wsel, a.N, nbK, rb0 * kMfRows + lrow, 0, g);
-  // staging work item i: 256-block i / (16 TM), row (i / 16) % TM, 16-byte piece i % 16
-  if constexpr (RES) {
-    const int64_t items = nbK * TM * 16;
-    for (int64_t i0 = tid; i0 < items; i0 += 4 * NT) {
-      StageRegs r4[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int64_t i = i0 + NT * j;
-        if (i < items) r4[j] = stage_load<M::NBSP>(srows[(i >> 4) % TM], i / (16 * TM), (int)(i & 15));
-      }
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int64_t i = i0 + NT * j;
-        if (i < items) stage_store<M::NBSP, TM>(L[i / (16 * TM)], r4[j], (int)((i >> 4) % TM), (int)(i & 15));
-      }
-    }
-    __syncthreads();
-  }
-  const int64_t nmat = MODE == 0 && NW == 8 ? 2 : 1;   // matrices a wave walks
+  const int64_t nmat = MODE == 0 && !SPLIT ? 2 : 1;   // matrices a wave walks
+  constexpr bool RINGP = RES && RING > 1;
 
-  if constexpr (RES && RING > 1) {
+  if constexpr (RINGP) {
   // RING weight units in flight per wave (memory-bound tiles): ring slot j
   // holds unit u0 + j, and the loop is unrolled by RING so every slot index
   // is static.  Units run (row block, 256-block, matrix) in the same order in
   // every wave, so the row-block epilogue (with its barriers) is uniform.
-  static_assert(MODE == 1 || NW == 16 || RING % 2 == 0, "gate/up units alternate between the two matrices");
-  const int64_t U = (rb1 - rb0) * nbK * nmat;
+  // The fp32-h gate/up tiles (EARLY) fill the ring between the first staging
+  // round's loads and its stores, so the weights are in flight while the
+  // activations arrive (loads return in order: the activations first).  The
+  // other tiles stage first and fill the ring after: with the ring state live
+  // through their staging, scalars spill to scratch.  The ring state and its
+  // lambdas live in this branch, not at function scope, and capture no kernel
+  // argument (either keeps the arguments in scratch).
+  constexpr bool Q = HF && MODE == 1, EARLY = HF && MODE == 0;
+  const int per_blk = 16 * n, items = (int)nbK * per_blk;
+  if constexpr (!EARLY) {
+    StageRound<Q> b;
+    stage_round_load<M::NBSP, NT, Q>(b, srows, tid, per_blk, items);
+    stage_round_store<M::NBSP, TM, NT, Q>(b, L, vrows, tid, per_blk, items);
+    stage_rest<M::NBSP, TM, NT, Q>(L, srows, vrows, tid, per_blk, items);
+  }
   typename M::Wt ring[RING];
-  ring[0] = wn;
   int64_t l_rb = rb0, l_sb = 0;
   int l_mat = 0;
-  auto adv_l = [&]() {
+  auto adv_l = [&]() __attribute__((always_inline)) {
     if (++l_mat == nmat) {
       l_mat = 0;
       if (++l_sb == nbK) { l_sb = 0; ++l_rb; }
     }
   };
-  auto load_unit = [&]() {
-    return M::load(NW == 16 ? Wsel : (l_mat == 0 ? W0 : W1), a.N, nbK, l_rb * kMfRows + lrow, l_sb, g);
+  // Every refill is issued, also past the wave's last unit (it then reloads
+  // that unit, already in cache, and the slot is never consumed): with the
+  // same loads on every path the compiler waits for one unit at a time
+  // (vmcnt of the RING-1 units behind it) instead of for all of them.
+  const int64_t wN = a.N;
+  auto load_unit = [&]() __attribute__((always_inline)) {
+    const bool in = l_rb < rb1;
+    const int64_t rb = in ? l_rb : rb1 - 1, sb = in ? l_sb : nbK - 1;
+    const int mt = in ? l_mat : (int)nmat - 1;
+    return M::load(SPLIT ? Wsel : (mt == 0 ? W0 : W1), wN, nbK, rb * RB + lrow, sb, g);
   };
-  adv_l();
+  auto fill_ring = [&]() __attribute__((always_inline)) {
 #pragma unroll
-  for (int j = 1; j < RING; ++j)
-    if (l_rb < rb1) { ring[j] = load_unit(); adv_l(); }
+    for (int j = 0; j < RING; ++j) { ring[j] = load_unit(); adv_l(); }
+  };
+  if constexpr (EARLY) {
+    StageRound<Q> b;
+    stage_round_load<M::NBSP, NT, Q>(b, srows, tid, per_blk, items);
+    fill_ring();
+    stage_round_store<M::NBSP, TM, NT, Q>(b, L, vrows, tid, per_blk, items);
+    stage_rest<M::NBSP, TM, NT, Q>(L, srows, vrows, tid, per_blk, items);
+  } else {
+    fill_ring();
+  }
+  static_assert(MODE == 1 || SPLIT || RING % 2 == 0, "gate/up units alternate between the two matrices");
+  const int64_t U = (rb1 - rb0) * nbK * nmat;
   double acc0[4 * NQ], acc1[4 * NQ];
 #pragma unroll
   for (int r = 0; r < 4 * NQ; ++r) { acc0[r] = 0.0; acc1[r] = 0.0; }
@@ -511,7 +656,7 @@ __device__ __forceinline__ void mfma_tile(const MfmaArgs& a) {
 #pragma unroll
     for (int j = 0; j < RING; ++j) {
       if (u0 + j < U) {
-        const int mat = MODE == 0 && NW == 8 ? (j & 1) : 0;
+        const int mat = MODE == 0 && !SPLIT ? (j & 1) : 0;
         const typename M::Wt& wc = ring[j];
         StageLds<TM>& S = L[c_sb];
         const uint8_t* qrow = arow ? &S.qs[lane & 31][0] : zrow;
@@ -519,11 +664,33 @@ __device__ __forceinline__ void mfma_tile(const MfmaArgs& a) {
         if constexpr (M::NBSP > 0) abs = lds_v4(arow ? &S.bsp[lane & 31][g][0] : zrow);
         if (mat == 0) M::template mac<NQ>(wc, g, qrow, abs, S.dx, n, acc0);
         else M::template mac<NQ>(wc, g, qrow, abs, S.dx, n, acc1);
-        // the slot is free again: refill it with the unit RING ahead
-        if (l_rb < rb1) { ring[j] = load_unit(); adv_l(); }
         if (mat == nmat - 1 && ++c_sb == nbK) {
-          const int64_t wrow = c_rb * kMfRows + lrow;
-          if constexpr (MODE == 0) {
+          const int64_t wrow = c_rb * RB + lrow;
+          if constexpr (MODE == 0 && HF) {
+            // h = fl32(silu(g) u) straight to the fp32 h rows
+            if constexpr (SPLIT) {
+              __shared__ double gxh[TM][RB];
+              if (wmat == 0) {
+#pragma unroll
+                for (int r = 0; r < 4 * NQ; ++r) gxh[out_row(r, g)][lrow] = acc0[r];
+              }
+              __syncthreads();
+              if (wmat == 1) {
+#pragma unroll
+                for (int r = 0; r < 4 * NQ; ++r) {
+                  const int m = out_row(r, g);
+                  if (m < n) gst_f32(a.hf + orow[m] * a.hf_stride + wrow, (float)(silu64(gxh[m][lrow]) * acc0[r]));
+                }
+              }
+              __syncthreads();   // gxh is rewritten by the next row block
+            } else {
+#pragma unroll
+              for (int r = 0; r < 4 * NQ; ++r) {
+                const int m = out_row(r, g);
+                if (m < n) gst_f32(a.hf + orow[m] * a.hf_stride + wrow, (float)(silu64(acc0[r]) * acc1[r]));
+              }
+            }
+          } else if constexpr (MODE == 0) {
             __shared__ float hs2[TM][kMfRows + 4];
             if constexpr (NW == 16) {
               __shared__ double gx[TM][kMfRows];
@@ -558,12 +725,24 @@ __device__ __forceinline__ void mfma_tile(const MfmaArgs& a) {
           ++c_rb;
         }
       }
+      // the slot is free again: refill it with the unit RING ahead
+      ring[j] = load_unit();
+      adv_l();
     }
   }
   } else {
   // One unit of weights ahead (few registers, so more waves per SIMD hide the
   // latency); activation blocks resident in LDS, or streamed through a
   // double-buffered stage when K exceeds the resident limit.
+  // the first unit's weights, in flight during the staging
+  typename M::Wt wn = M::load(Wsel, a.N, nbK, rb0 * RB + lrow, 0, g);
+  if constexpr (RES) {
+    const int per_blk = 16 * n, items = (int)nbK * per_blk;
+    StageRound<false> b;
+    stage_round_load<M::NBSP, NT, false>(b, srows, tid, per_blk, items);
+    stage_round_store<M::NBSP, TM, NT, false>(b, L, vrows, tid, per_blk, items);
+    stage_rest<M::NBSP, TM, NT, false>(L, srows, vrows, tid, per_blk, items);
+  }
   const int ms = (tid >> 4) % TM, piece = tid & 15;
   const bool stager = tid < 16 * TM;
   StageRegs sr;
@@ -649,6 +828,18 @@ template <int FMT>
 __global__ __launch_bounds__(1024) void k_mfma_ring16(MfmaArgs a) {
   mfma_tile<FMT, 0, true, 8, kRing<FMT>, 16>(a);
 }
+// fp32-h variant: gate/up over 64 rows on 4 waves (two gate, two up; several
+// workgroups per CU), down staging q8_K(h) from the fp32 rows itself
+template <int FMT>
+__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(3, 8))) void k_mfma_hf_gateup(
+    MfmaArgs a) {
+  mfma_tile<FMT, 0, true, 8, FMT == FQ4K ? 3 : kRing<FMT>, 4, true>(a);   // Q4_K: 3 units, no spills
+}
+template <int FMT>
+__global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2, 8))) void k_mfma_hf_down(
+    MfmaArgs a) {
+  mfma_tile<FMT, 1, true, 8, kRing<FMT>, 8, true>(a);
+}
 
 // Tile lists of the routed experts (one workgroup; see mfma_plan.hpp).
 __global__ __launch_bounds__(64) void k_mfma_plan(const int32_t* __restrict__ active,
@@ -672,9 +863,12 @@ namespace {
 // ring kernels when their activations fit in LDS, gate/up of Q2_K and Q8_0
 // on 16 waves; everything else runs the one-unit-ahead tiles.
 template <int F, int MD, int TM>
-void launch_tile(dim3 grid, const MfmaArgs& a, int64_t nbK, hipStream_t s) {
+void launch_tile(dim3 grid, const MfmaArgs& a, int64_t nbK, bool hf, hipStream_t s) {
   if constexpr (TM == 8 && F != FQ6K) {
-    if (nbK <= kRes(TM)) {
+    if (hf) {
+      if constexpr (MD == 0) hipLaunchKernelGGL((k_mfma_hf_gateup<F>), grid, dim3(256), 0, s, a);
+      else hipLaunchKernelGGL((k_mfma_hf_down<F>), grid, dim3(512), 0, s, a);
+    } else if (nbK <= kRes(TM)) {
       if constexpr (MD == 0 && (F == FQ2K || F == FQ80))
         hipLaunchKernelGGL((k_mfma_ring16<F>), grid, dim3(1024), 0, s, a);
       else
@@ -689,26 +883,28 @@ void launch_tile(dim3 grid, const MfmaArgs& a, int64_t nbK, hipStream_t s) {
 }
 
 template <int F>
-void launch_fmt(int mode, bool thin, dim3 grid, const MfmaArgs& a, int64_t nbK, hipStream_t s) {
+void launch_fmt(int mode, bool thin, bool hf, dim3 grid, const MfmaArgs& a, int64_t nbK, hipStream_t s) {
   if (mode == 0) {
-    if (thin) launch_tile<F, 0, 8>(grid, a, nbK, s);
-    else launch_tile<F, 0, 32>(grid, a, nbK, s);
+    if (thin) launch_tile<F, 0, 8>(grid, a, nbK, hf, s);
+    else launch_tile<F, 0, 32>(grid, a, nbK, false, s);
   } else {
-    if (thin) launch_tile<F, 1, 8>(grid, a, nbK, s);
-    else launch_tile<F, 1, 32>(grid, a, nbK, s);
+    if (thin) launch_tile<F, 1, 8>(grid, a, nbK, hf, s);
+    else launch_tile<F, 1, 32>(grid, a, nbK, false, s);
   }
 }
 
 }  // namespace
 
-int launch_mfma(int fmt, int mode, bool thin, dim3 grid, const MfmaArgs& a, hipStream_t s) {
+int launch_mfma(int fmt, int mode, bool thin, bool hf, dim3 grid, const MfmaArgs& a, hipStream_t s) {
   if (grid.x == 0 || grid.y == 0) return 0;
   const int64_t nbK = a.K / 256;
+  // the fp32-h kernels: resident 8-row tiles, not Q6_K (checked by the caller too)
+  if (hf && (!thin || fmt == FQ6K || nbK > kRes(8) || a.hf == nullptr)) return -2;
   switch (fmt) {
-    case FQ4K: launch_fmt<FQ4K>(mode, thin, grid, a, nbK, s); break;
-    case FQ6K: launch_fmt<FQ6K>(mode, thin, grid, a, nbK, s); break;
-    case FQ2K: launch_fmt<FQ2K>(mode, thin, grid, a, nbK, s); break;
-    case FQ80: launch_fmt<FQ80>(mode, thin, grid, a, nbK, s); break;
+    case FQ4K: launch_fmt<FQ4K>(mode, thin, hf, grid, a, nbK, s); break;
+    case FQ6K: launch_fmt<FQ6K>(mode, thin, false, grid, a, nbK, s); break;
+    case FQ2K: launch_fmt<FQ2K>(mode, thin, hf, grid, a, nbK, s); break;
+    case FQ80: launch_fmt<FQ80>(mode, thin, hf, grid, a, nbK, s); break;
     default: return -2;
   }
   return hipGetLastError() == hipSuccess ? 0 : -1;

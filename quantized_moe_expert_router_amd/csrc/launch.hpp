@@ -116,8 +116,10 @@ struct MfmaArgs {
   int64_t rb;                   // 256-row blocks per workgroup (grid.y = ceil(N/256 / rb))
   const uint8_t* src;           // q8_K rows: x by token (mode 0), h by pair row (mode 1)
   int64_t src_stride;
-  uint8_t* hq;                  // mode 0: q8_K(h) rows out
-  int64_t hq_stride;
+  uint8_t* hq;                  // q8_K(h) rows: mode 0 writes them; with fp32 h, mode 1
+  int64_t hq_stride;            //   writes them (the quantised view of its staged rows)
+  float* hf;                    // fp32 h rows (fp32-h launches only): mode 0 writes them,
+  int64_t hf_stride;            //   mode 1 quantises them to q8_K while staging
   const float* topk_w;
   const float* shared_scale;
   float* yp;                    // mode 1: fp32 [T*k + T, H]
@@ -140,7 +142,11 @@ int launch_down(int fmt, int tt, int cpl, dim3 grid, const DownArgs& a, hipStrea
 int launch_down_rows1(int fmt, int cpl, dim3 grid, const DownArgs& a, hipStream_t s);
 int launch_mfma_plan(const int32_t* active, const int32_t* offsets, int thr, int max_tiles, int4* tiles,
                      int32_t* count, int4* thin, int32_t* thin_count, hipStream_t s);
-int launch_mfma(int fmt, int mode, bool thin, dim3 grid, const MfmaArgs& a, hipStream_t s);
+// hf: the fp32-h variant (8-row resident tiles of formats other than Q6_K;
+// mode 0 workgroups then cover kHfRows weight rows instead of 256).
+constexpr int kHfRows = 64;
+constexpr int kHfMaxBlocks = 16;   // K (256-blocks) up to which 8-row tiles keep their activations in LDS
+int launch_mfma(int fmt, int mode, bool thin, bool hf, dim3 grid, const MfmaArgs& a, hipStream_t s);
 int launch_combine(const float* yp, int64_t T, int64_t H, int k, int has_shared, float* y, int accumulate,
                    hipStream_t s);
 
