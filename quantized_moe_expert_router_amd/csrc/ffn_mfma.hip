@@ -829,16 +829,19 @@ __global__ __launch_bounds__(1024) void k_mfma_ring16(MfmaArgs a) {
   mfma_tile<FMT, 0, true, 8, kRing<FMT>, 16>(a);
 }
 // fp32-h variant: gate/up over 64 rows on 4 waves (two gate, two up; several
-// workgroups per CU), down staging q8_K(h) from the fp32 rows itself
+// workgroups per CU), down staging q8_K(h) from the fp32 rows itself.  Two
+// units in flight per wave: every wave asks for its first units at once, and
+// a shallower ring lets the first units of all waves arrive sooner (the
+// stream rate is the same from 2 to 8 units in flight).
 template <int FMT>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(3, 8))) void k_mfma_hf_gateup(
     MfmaArgs a) {
-  mfma_tile<FMT, 0, true, 8, FMT == FQ4K ? 3 : kRing<FMT>, 4, true>(a);   // Q4_K: 3 units, no spills
+  mfma_tile<FMT, 0, true, 8, 2, 4, true>(a);
 }
 template <int FMT>
 __global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2, 8))) void k_mfma_hf_down(
     MfmaArgs a) {
-  mfma_tile<FMT, 1, true, 8, kRing<FMT>, 8, true>(a);
+  mfma_tile<FMT, 1, true, 8, 2, 8, true>(a);
 }
 
 // Tile lists of the routed experts (one workgroup; see mfma_plan.hpp).
