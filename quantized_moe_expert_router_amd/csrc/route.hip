@@ -166,7 +166,7 @@ __global__ __launch_bounds__(256) void k_logits_mfma(const float* __restrict__ x
 }
 
 template <int NPER>
-__device__ void topk_row_wave(const double* __restrict__ row, int64_t E, int k, int gating, float scale,
+__device__ __forceinline__ void topk_row_wave(const double* __restrict__ row, int64_t E, int k, int gating, float scale,
                               int32_t* __restrict__ ids_out, float* __restrict__ w_out, int32_t* ids_lds) {
   int my_i;
   float my_w;
@@ -235,6 +235,59 @@ __device__ void offsets_and_union(int* cnt, int64_t E, int32_t* offsets, int32_t
   }
 }
 
+// Lists of at most 64 (token, slot) pairs p = t*k + slot, from their experts
+// in LDS: ordered by expert and, inside an expert, by p (the counting-sort
+// order), pair p's list position is its rank by the key (expert, p) -- keys
+// are distinct, so the ranks are a permutation.  Wave 0 ranks the pairs
+// (keys broadcast lane by lane), writes the pair list and the sorted keys,
+// and takes the union as the first key of every expert in that order; then
+// every thread finds offsets[e] (the pairs with a smaller expert) by binary
+// search in the sorted keys.  The union and offsets also go to LDS (lact,
+// loff) for the tile lists that may follow.
+constexpr int kSmallPairs = 64;
+__device__ void small_lists(const int* ids_s, int P, int64_t E, int32_t* __restrict__ offsets,
+                            int32_t* __restrict__ pairs, int32_t* __restrict__ active, int* skey, int* loff,
+                            int* lact) {
+  if (threadIdx.x < kWave) {
+    const int lane = lane_id();
+    const int key = lane < P ? ((ids_s[lane] << 6) | lane) : INT_MAX;
+    int rank = 0;
+    for (int q = 0; q < P; ++q) rank += __builtin_amdgcn_readlane(key, q) < key;
+    if (lane < P) {
+      skey[rank] = key;
+      gst_i32(pairs + rank, lane);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    const int ex = lane < P ? skey[lane] >> 6 : -1;
+    const int prev = lane > 0 && lane < P ? skey[lane - 1] >> 6 : -1;
+    const bool first = lane < P && ex != prev;
+    const uint64_t bal = __ballot(first);
+    const int idx = __popcll(bal & ((1ull << lane) - 1ull));
+    if (first) {
+      lact[1 + idx] = ex;
+      gst_i32(active + 1 + idx, ex);
+    }
+    if (lane == 0) {
+      lact[0] = __popcll(bal);
+      gst_i32(active, __popcll(bal));
+    }
+  }
+  __syncthreads();
+  for (int64_t e = threadIdx.x; e <= E; e += blockDim.x) {
+    const int ke = (int)e << 6;
+    int lo = 0, hi = P;                     // first sorted position whose key is >= (e, 0)
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if (skey[mid] < ke) lo = mid + 1;
+      else hi = mid;
+    }
+    loff[e] = lo;
+    gst_i32(offsets + e, lo);
+  }
+}
+
 // T <= kSmallT: top-k for every token, then the lists, in one workgroup.
 template <int NPER>
 __global__ __launch_bounds__(1024) void k_select_small(const double* __restrict__ logits, int64_t T, int64_t E,
@@ -249,6 +302,18 @@ __global__ __launch_bounds__(1024) void k_select_small(const double* __restrict_
   const int wv = threadIdx.x >> 6, nw = blockDim.x >> 6;
   for (int64_t t = wv; t < T; t += nw)
     topk_row_wave<NPER>(logits + t * E, E, k, gating, scale, ids + t * k, w + t * k, ids_s + t * k);
+  if (T * k <= kSmallPairs) {
+    int* skey = ids_s + T * k;                                // [64]
+    int* lact = skey + kSmallPairs;                           // [65]
+    int* loff = lact + kSmallPairs + 1;                       // [E + 1]
+    __syncthreads();
+    small_lists(ids_s, (int)(T * k), E, offsets, pairs, active, skey, loff, lact);
+    if (plan.tiles != nullptr) {
+      __syncthreads();
+      mfma_plan_block(lact, loff, plan);
+    }
+    return;
+  }
   for (int64_t e = threadIdx.x; e < E; e += blockDim.x) cnt[e] = 0;
   __syncthreads();
   for (int64_t p = threadIdx.x; p < T * k; p += blockDim.x) atomicAdd(&cnt[ids_s[p]], 1);
@@ -381,7 +446,7 @@ int launch_route(int64_t T, int64_t H, int64_t E, int k, int gating, float scale
   double* lg = logits ? logits : reinterpret_cast<double*>(wsb);
   launch_logits(T, H, E, x, W, bias, lg, xq, s);
   if (T <= kSmallT) {
-    size_t lds = (size_t)(T * k + E + 64) * sizeof(int);
+    size_t lds = (size_t)(T * k + E + 2 * kSmallPairs + 2) * sizeof(int);   // either list path
 #define MOEQ_SEL(N) hipLaunchKernelGGL(k_select_small<N>, dim3(1), dim3(1024), lds, s, lg, T, E, k, gating, \
                                         scale, ids, w, offsets, pairs, active, pl)
     if (E <= 256) MOEQ_SEL(4);

@@ -7,13 +7,89 @@
 
 namespace moeq {
 
-// Top-k of one logits row by one wave, logits held in registers (NPER per
-// lane, element lane + 64*i).  Each round takes the first remaining element
-// under (logit desc, index asc) with a DPP arg-max.  Lane s < k ends holding
-// the s-th winner (id) and its gate weight: computed in fp64 in parallel over
-// the k lanes and normalised by a fixed-order wave sum.
+// Order-preserving key of (fp32 rounding of v, index): for elements whose
+// fp32 values differ, the larger key comes first under (logit desc, index
+// asc) -- rounding to fp32 never reverses an order, it can only merge values.
+__device__ __forceinline__ uint64_t topk_key(double v, int i) {
+  uint32_t u = __float_as_uint((float)v);
+  u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  return ((uint64_t)u << 32) | (uint64_t)(~(uint32_t)i);
+}
+__device__ __forceinline__ uint64_t as_u64(double d) { return __builtin_bit_cast(uint64_t, d); }
+__device__ __forceinline__ double as_f64(uint64_t u) { return __builtin_bit_cast(double, u); }
+
+// Wave-wide maximum of a 64-bit key (DPP steps as in wave_argmax); every
+// lane gets it.
+__device__ __forceinline__ uint64_t wave_max_key(uint64_t x) {
+  uint64_t o;
+  o = as_u64(dpp_all_d<kDppXor1>(as_f64(x)));    x = o > x ? o : x;
+  o = as_u64(dpp_all_d<kDppXor2>(as_f64(x)));    x = o > x ? o : x;
+  o = as_u64(dpp_all_d<kDppRowRor4>(as_f64(x))); x = o > x ? o : x;
+  o = as_u64(dpp_all_d<kDppRowRor8>(as_f64(x))); x = o > x ? o : x;
+  o = as_u64(dpp_d<kDppRowBcast15, 0xA>(as_f64(x), as_f64(x))); x = o > x ? o : x;
+  o = as_u64(dpp_d<kDppRowBcast31, 0xC>(as_f64(x), as_f64(x))); x = o > x ? o : x;
+  return as_u64(readlane_d(as_f64(x), 63));
+}
+
+// Selection on the fp32 keys: k + 1 rounds of a one-compare arg-max over the
+// lanes' sorted key lists.  The result is the exact (fp64) selection when the
+// first k + 1 winners have pairwise different fp32 values: then every order
+// among them, and between the k-th and everything not selected, is the same
+// in fp64.  Returns false (nothing decided) otherwise -- equal fp32 values
+// among them, e.g. exact ties -- and the caller runs the fp64 rounds.
 template <int NPER>
-__device__ void topk_wave_regs(const double* __restrict__ row, int64_t E, int k, int gating, float scale,
+__device__ __forceinline__ bool topk_fast(const double* v, const int* vi, int k, double& my_v, int& my_i) {
+  const int lane = lane_id();
+  uint64_t key[NPER];
+#pragma unroll
+  for (int i = 0; i < NPER; ++i) key[i] = topk_key(v[i], vi[i]);
+  // the lane's keys in descending order (insertion network)
+#pragma unroll
+  for (int a = 1; a < NPER; ++a)
+#pragma unroll
+    for (int b = a; b > 0; --b) {
+      const uint64_t k0 = key[b - 1], k1 = key[b];
+      key[b - 1] = k1 > k0 ? k1 : k0;
+      key[b] = k1 > k0 ? k0 : k1;
+    }
+  // rounds: every lane offers its first unused key (0 once all are used)
+  int head = 0;
+  uint64_t cand = key[0];
+  uint32_t prev_f = 0;
+  bool clear = true;
+  for (int s = 0; s <= k; ++s) {
+    const uint64_t best = wave_max_key(cand);
+    const uint32_t f = (uint32_t)(best >> 32);
+    clear = clear && (s == 0 || f != prev_f);
+    prev_f = f;
+    my_i = lane == s ? (int)~(uint32_t)best : my_i;
+    head += cand == best ? 1 : 0;
+    uint64_t c = 0;
+#pragma unroll
+    for (int j = NPER - 1; j >= 0; --j) c = head == j ? key[j] : c;
+    cand = c;
+  }
+  // the winners' fp64 logits: element e sits in lane e % 64, slot e / 64
+  const int src = my_i & (kWave - 1), slot = my_i >> 6;
+  double val = 0.0;
+#pragma unroll
+  for (int i = 0; i < NPER; ++i) {
+    const double t = __shfl(v[i], src, kWave);
+    val = slot == i ? t : val;
+  }
+  if (lane < k) my_v = val;
+  return clear;
+}
+
+// Top-k of one logits row by one wave, logits held in registers (NPER per
+// lane, element lane + 64*i), under (logit desc, index asc).  The fp32-key
+// selection above decides nearly every row; rows it leaves open take rounds
+// of an fp64 DPP arg-max over the first remaining element of every lane.
+// Lane s < k ends holding the s-th winner (id) and its gate weight: computed
+// in fp64 in parallel over the k lanes and normalised by a fixed-order wave
+// sum.
+template <int NPER>
+__device__ __forceinline__ void topk_wave_regs(const double* __restrict__ row, int64_t E, int k, int gating, float scale,
                                int& my_i, float& my_w) {
   const int lane = lane_id();
   double v[NPER];
@@ -27,36 +103,42 @@ __device__ void topk_wave_regs(const double* __restrict__ row, int64_t E, int k,
   double my_v = 0.0;
   my_i = 0;
   if constexpr (NPER <= 8) {
-    // Sort the lane's few logits first (same order), so a round only needs
-    // the lane's head: the first of its elements not yet taken.
+    if (!topk_fast<NPER>(v, vi, k, my_v, my_i)) {
+      // Sort copies of the lane's few logits first (same order), so a round
+      // only needs the lane's head: the first of its elements not yet taken.
+      double sv[NPER];
+      int si[NPER];
 #pragma unroll
-    for (int a = 0; a < NPER; ++a)
+      for (int i = 0; i < NPER; ++i) { sv[i] = v[i]; si[i] = vi[i]; }
 #pragma unroll
-      for (int b = NPER - 1; b > a; --b) {
-        double hv = v[b - 1];
-        int hi = vi[b - 1];
-        better(hv, hi, v[b], vi[b]);               // the first of the pair moves up
-        const bool sw = hi != vi[b - 1];
-        const double lv = sw ? v[b - 1] : v[b];
-        const int li = sw ? vi[b - 1] : vi[b];
-        v[b - 1] = hv; vi[b - 1] = hi; v[b] = lv; vi[b] = li;
+      for (int a = 0; a < NPER; ++a)
+#pragma unroll
+        for (int b = NPER - 1; b > a; --b) {
+          double hv = sv[b - 1];
+          int hi = si[b - 1];
+          better(hv, hi, sv[b], si[b]);              // the first of the pair moves up
+          const bool sw = hi != si[b - 1];
+          const double lv = sw ? sv[b - 1] : sv[b];
+          const int li = sw ? si[b - 1] : si[b];
+          sv[b - 1] = hv; si[b - 1] = hi; sv[b] = lv; si[b] = li;
+        }
+      int head = 0;
+      for (int s = 0; s < k; ++s) {
+        double best = sv[0];
+        int bi = si[0];
+#pragma unroll
+        for (int j = 1; j < NPER; ++j) {
+          best = head == j ? sv[j] : best;
+          bi = head == j ? si[j] : bi;
+        }
+        best = head < NPER ? best : -INFINITY;
+        bi = head < NPER ? bi : INT_MAX;
+        const int mine = bi;
+        wave_argmax(best, bi);
+        head += (mine == bi) ? 1 : 0;
+        my_v = lane == s ? best : my_v;
+        my_i = lane == s ? bi : my_i;
       }
-    int head = 0;
-    for (int s = 0; s < k; ++s) {
-      double best = v[0];
-      int bi = vi[0];
-#pragma unroll
-      for (int j = 1; j < NPER; ++j) {
-        best = head == j ? v[j] : best;
-        bi = head == j ? vi[j] : bi;
-      }
-      best = head < NPER ? best : -INFINITY;
-      bi = head < NPER ? bi : INT_MAX;
-      const int mine = bi;
-      wave_argmax(best, bi);
-      head += (mine == bi) ? 1 : 0;
-      my_v = lane == s ? best : my_v;
-      my_i = lane == s ? bi : my_i;
     }
   } else {
     uint64_t taken = 0;
