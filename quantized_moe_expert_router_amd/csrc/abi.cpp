@@ -289,11 +289,15 @@ int ffn_enqueue(const moeq_ffn_desc* d, const void* x_q8K, const int32_t* topk_i
   int4* thin_tiles = (int4*)(wsb + L.off_thin);
   int32_t* tcount = (int32_t*)(wsb + L.off_count);
   // fp32 h between gate/up and down for the 8-row tiles (see launch_mfma)
-  // when both of their launches can take it
+  // when both of their launches can take it and the tiles are few (256-row
+  // gate/up workgroups would not fill the chip; with many tiles the q8_K(h)
+  // epilogue is faster)
   auto hf_ok = [&](bool shared_exp) {
     const int fg = shared_exp ? d->sh_fmt_gate : d->fmt_gate, fd = shared_exp ? d->sh_fmt_down : d->fmt_down;
     const int64_t Fx = shared_exp ? d->F_shared : d->F;
-    return fg != FQ6K && fd != FQ6K && d->H / 256 <= kHfMaxBlocks && Fx / 256 <= kHfMaxBlocks;
+    const int64_t tiles = shared_exp ? (d->T + kThinT - 1) / kThinT : L.max_thin;
+    return fg != FQ6K && fd != FQ6K && d->H / 256 <= kHfMaxBlocks && Fx / 256 <= kHfMaxBlocks &&
+           tiles * (Fx / 256) < kHfMaxWorkgroups;
   };
   auto mfma_launch = [&](int mode, bool shared_exp, bool thin) -> int {
     const bool hf = thin && hf_ok(shared_exp);
