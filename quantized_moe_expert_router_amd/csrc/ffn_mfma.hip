@@ -55,7 +55,7 @@ template <int TM>
 struct __align__(16) StageLds {
   uint8_t qs[TM][kQsStride];       // q8_K quants of the tile rows, one 256-block
   uint8_t bsp[TM][2][16];          // split block sums: [0] = bl entries, [1] = bh entries
-  float dx[TM];                    // q8_K scales
+  double dx[TM];                   // q8_K scales (widened once here, not per unit)
 };
 
 __device__ __forceinline__ v16i mfma_k32(v4i a, v4i b, v16i c) {
@@ -70,7 +70,7 @@ __device__ __forceinline__ v16i mfma_k16(long a, long b, v16i c) {
 __device__ __forceinline__ uint32_t bytes_times(uint32_t v, uint32_t s) {
   typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
   const u16x2 a = __builtin_bit_cast(u16x2, v);
-  const u16x2 b = __builtin_bit_cast(u16x2, s * 0x00010001u);
+  const u16x2 b = (u16x2)((unsigned short)s);   // splat: the multiply reads s's low half twice (op_sel)
   return __builtin_bit_cast(uint32_t, a * b);
 }
 
@@ -88,11 +88,12 @@ __device__ __forceinline__ int out_row(int r, int g) { return 8 * (r >> 2) + 4 *
 #define MOEQ_COMBINE(STMT)                                                            \
   _Pragma("unroll") for (int q = 0; q < NQ; ++q) {                                   \
     if (8 * q < n) {                                                                  \
-      const float4 dx4 = *reinterpret_cast<const float4*>(dxs + 8 * q + 4 * g);       \
-      const float dxa[4] = {dx4.x, dx4.y, dx4.z, dx4.w};                             \
+      const double2 d01 = *reinterpret_cast<const double2*>(dxs + 8 * q + 4 * g);     \
+      const double2 d23 = *reinterpret_cast<const double2*>(dxs + 8 * q + 4 * g + 2); \
+      const double dxa[4] = {d01.x, d01.y, d23.x, d23.y};                            \
       _Pragma("unroll") for (int i = 0; i < 4; ++i) {                                \
         const int r = 4 * q + i;                                                      \
-        const double dx = (double)dxa[i];                                             \
+        const double dx = dxa[i];                                                     \
         STMT;                                                                         \
       }                                                                               \
     }                                                                                 \
@@ -108,20 +109,47 @@ __device__ __forceinline__ int out_row(int r, int g) { return 8 * (r >> 2) + 4 *
 
 template <int FMT> struct Mf;
 
+// A wave's 32 weight rows start at a multiple of 32 (lane row r = row % 32),
+// so row / 32 is the same in every lane: the (row group, super-block) part of
+// an address is put in scalar registers, and each load takes that scalar base
+// plus a 32-bit lane offset that never changes (no 64-bit address arithmetic
+// per lane and load).
+__device__ __forceinline__ int64_t wave_uni(int64_t v) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)v);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)((uint64_t)v >> 32));
+  return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+__device__ __forceinline__ const uint8_t* wave_uni_ptr(const uint8_t* p) {
+  return reinterpret_cast<const uint8_t*>(wave_uni(reinterpret_cast<int64_t>(p)));
+}
+// super-block index of (row group, sb) of a row-major matrix, and the lane row
+struct RowSplit {
+  int64_t su;      // (row & ~31) * nbK + sb, the same in every lane
+  uint32_t r;      // row & 31
+};
+__device__ __forceinline__ RowSplit row_split(int64_t row, int64_t nbK, int64_t sb) {
+  return RowSplit{wave_uni(row >> 5) * 32 * nbK + sb, (uint32_t)row & 31u};
+}
+
 template <> struct Mf<FQ4K> {
   static constexpr int NBSP = 8;   // one sum per 32-sub-block: bsums[2j] + bsums[2j+1]
   struct Wt { uint4 c[4]; uint4 h; };
   __device__ static Wt load(const uint8_t* W, int64_t N, int64_t nbK, int64_t row, int64_t sb, int g) {
-    const size_t nsb = (size_t)(N * nbK), sbi = (size_t)(row * nbK + sb);
+    const size_t nsb = (size_t)(N * nbK);
+    const RowSplit rs = row_split(row, nbK, sb);
+    const uint32_t lr = rs.r * (uint32_t)nbK;              // lane super-block offset
+    const uint8_t* Wb = wave_uni_ptr(W);
+    const uint8_t* qb = Wb + rs.su * 128;
+    const uint8_t* hb = Wb + align256(nsb * 128) + rs.su * 16;
     Wt w;
 #pragma unroll
-    for (int p = 0; p < 4; ++p) w.c[p] = gld_u4(W + sbi * 128 + 16 * (2 * p + g));
-    w.h = gld_u4(W + align256(nsb * 128) + sbi * 16);
+    for (int p = 0; p < 4; ++p) w.c[p] = gld_u4(qb + (lr * 128u + 16u * (uint32_t)(2 * p + g)));
+    w.h = gld_u4(hb + lr * 16u);
     return w;
   }
   // MFMA 2p+s: lane half g holds sub-block 2p+g, nibble s (elements 64p+32g+16s .. +15).
   template <int NQ>
-  __device__ static void mac(const Wt& w, int g, const uint8_t* qrow, const v4i abs, const float* dxs,
+  __device__ static void mac(const Wt& w, int g, const uint8_t* qrow, const v4i abs, const double* dxs,
                              int n, double* acc) {
     const uint64_t lo = (uint64_t)w.h.y | ((uint64_t)w.h.z << 32);
     const uint64_t hi = (uint64_t)w.h.z | ((uint64_t)w.h.w << 32);
@@ -166,32 +194,38 @@ template <> struct Mf<FQ2K> {
   // Tiled layout (32-row units): lane (half g, row r) reads the two 16 B
   // pieces of its half, each load instruction covering 1 KB contiguously.
   __device__ static Wt load(const uint8_t* W, int64_t N, int64_t nbK, int64_t row, int64_t sb, int g) {
-    const int64_t units = ((N + 31) >> 5) * nbK, u = (row >> 5) * nbK + sb;
-    const int r = (int)(row & 31);
-    const uint8_t* ps = W + align256((size_t)units * 2048);
-    const uint8_t* pd = ps + align256((size_t)units * 512);
+    const int64_t units = ((N + 31) >> 5) * nbK, u = wave_uni(row >> 5) * nbK + sb;
+    const uint32_t r = (uint32_t)row & 31u;
+    const uint8_t* Wb = wave_uni_ptr(W);
+    const uint8_t* cb = Wb + u * 2048;
+    const uint8_t* sbp = Wb + align256((size_t)units * 2048) + u * 512;
+    const uint8_t* db = Wb + align256((size_t)units * 2048) + align256((size_t)units * 512) + u * 128;
     Wt w;
 #pragma unroll
-    for (int k = 0; k < 2; ++k) w.c[k] = gld_u4(W + u * 2048 + 1024 * k + 16 * (32 * g + r));
-    w.sm = gld_u4(ps + u * 512 + 16 * r);
-    w.dd = gld_u32(pd + u * 128 + 4 * r);
+    for (int k = 0; k < 2; ++k) w.c[k] = gld_u4(cb + (1024u * (uint32_t)k + 16u * (32u * (uint32_t)g + r)));
+    w.sm = gld_u4(sbp + 16u * r);
+    w.dd = gld_u32(db + 4u * r);
     return w;
   }
   // MFMA p: lane half g holds sub-block 2p+g (elements 32p+16g .. +15), whose
   // 16 codes are word p of the half: element 4i + b at bits 8b + 2i.
   template <int NQ>
-  __device__ static void mac(const Wt& w, int g, const uint8_t* qrow, const v4i abs, const float* dxs,
+  __device__ static void mac(const Wt& w, int g, const uint8_t* qrow, const v4i abs, const double* dxs,
                              int n, double* acc) {
+    typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
     const uint32_t sm[4] = {w.sm.x, w.sm.y, w.sm.z, w.sm.w};
     v16i P = {0};
     const uint32_t words[8] = {w.c[0].x, w.c[0].y, w.c[0].z, w.c[0].w, w.c[1].x, w.c[1].y, w.c[1].z, w.c[1].w};
 #pragma unroll
     for (int p = 0; p < 8; ++p) {
-      const int j = 2 * p + g;
-      const uint32_t sc = (sm[j >> 2] >> (8 * (j & 3))) & 15;
+      // sub-block j = 2p+g: byte 2(p&1)+g of word p/2, so steps 2q and 2q+1
+      // take the two 16-bit halves of one shift and mask (op_sel picks the half)
+      const u16x2 pair = __builtin_bit_cast(u16x2, (sm[p >> 1] >> (8 * g)) & 0x000F000Fu);
+      const u16x2 scv = (p & 1) ? pair.yy : pair.xx;
       v4i b;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) b[i] = (int)bytes_times((words[p] >> (2 * i)) & 0x03030303u, sc);
+      for (int i = 0; i < 4; ++i)
+        b[i] = (int)__builtin_bit_cast(uint32_t, __builtin_bit_cast(u16x2, (words[p] >> (2 * i)) & 0x03030303u) * scv);
       P = mfma_k32(lds_v4(qrow + 32 * p + 16 * g), b, P);
     }
     v4i bm;
@@ -212,24 +246,29 @@ template <> struct Mf<FQ6K> {
   // Lane half g needs words 2g, 2g+1 of every low-nibble chunk and all of the
   // high-pair row.
   __device__ static Wt load(const uint8_t* W, int64_t N, int64_t nbK, int64_t row, int64_t sb, int g) {
-    const size_t nsb = (size_t)(N * nbK), sbi = (size_t)(row * nbK + sb);
+    const size_t nsb = (size_t)(N * nbK);
+    const RowSplit rs = row_split(row, nbK, sb);
+    const uint32_t lr = rs.r * (uint32_t)nbK;
+    const uint8_t* Wb = wave_uni_ptr(W);
     Wt w;
-    const uint8_t* px = W + align256(nsb * 128);
+    const uint8_t* px = Wb + align256(nsb * 128);
     const uint8_t* ps = px + align256(nsb * 64);
     const uint8_t* pd = ps + align256(nsb * 16);
+    const uint8_t* lb = Wb + rs.su * 128;
+    const uint8_t* xb = px + rs.su * 64;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) w.l[j] = gld_u2(W + sbi * 128 + 16 * j + 8 * g);
+    for (int j = 0; j < 8; ++j) w.l[j] = gld_u2(lb + (lr * 128u + 16u * (uint32_t)j + 8u * (uint32_t)g));
 #pragma unroll
-    for (int j = 0; j < 4; ++j) w.x[j] = gld_u4(px + sbi * 64 + 16 * j);
-    w.sc = gld_u4(ps + sbi * 16);
-    w.d = gld_u16(pd + sbi * 2);
+    for (int j = 0; j < 4; ++j) w.x[j] = gld_u4(xb + (lr * 64u + 16u * (uint32_t)j));
+    w.sc = gld_u4(ps + rs.su * 16 + lr * 16u);
+    w.d = gld_u16(pd + rs.su * 2 + lr * 2u);
     return w;
   }
   // One 16-deep MFMA per sub-block jj: lane half g holds elements 16jj+8g .. +7
   // (low nibbles: word i = 2g+t of chunk jj/2, nibble jj%2; high pairs: word
   // jj%2 of chunk jj/2 in the high-pair plane, bits 2i).
   template <int NQ>
-  __device__ static void mac(const Wt& w, int g, const uint8_t* qrow, const v4i abs, const float* dxs,
+  __device__ static void mac(const Wt& w, int g, const uint8_t* qrow, const v4i abs, const double* dxs,
                              int n, double* acc) {
     const uint32_t scw[4] = {w.sc.x, w.sc.y, w.sc.z, w.sc.w};
     int S1[16];
@@ -268,15 +307,19 @@ template <> struct Mf<FQ80> {
   static constexpr int NBSP = 0;
   struct Wt { uint4 q[8]; uint4 d; };
   __device__ static Wt load(const uint8_t* W, int64_t N, int64_t nbK, int64_t row, int64_t sb, int g) {
-    const size_t nsb = (size_t)(N * nbK), sbi = (size_t)(row * nbK + sb);
+    const size_t nsb = (size_t)(N * nbK);
+    const RowSplit rs = row_split(row, nbK, sb);
+    const uint32_t lr = rs.r * (uint32_t)nbK;
+    const uint8_t* Wb = wave_uni_ptr(W);
+    const uint8_t* qb = Wb + rs.su * 256;
     Wt w;
 #pragma unroll
-    for (int b = 0; b < 8; ++b) w.q[b] = gld_u4(W + sbi * 256 + 32 * b + 16 * g);
-    w.d = gld_u4(W + align256(nsb * 256) + sbi * 16);
+    for (int b = 0; b < 8; ++b) w.q[b] = gld_u4(qb + (lr * 256u + 32u * (uint32_t)b + 16u * (uint32_t)g));
+    w.d = gld_u4(Wb + align256(nsb * 256) + rs.su * 16 + lr * 16u);
     return w;
   }
   template <int NQ>
-  __device__ static void mac(const Wt& w, int g, const uint8_t* qrow, const v4i, const float* dxs,
+  __device__ static void mac(const Wt& w, int g, const uint8_t* qrow, const v4i, const double* dxs,
                              int n, double* acc) {
     const uint32_t dw[4] = {w.d.x, w.d.y, w.d.z, w.d.w};
     const v16i z16 = {0};
