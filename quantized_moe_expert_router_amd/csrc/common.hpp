@@ -59,6 +59,9 @@ __device__ __forceinline__ double gld_f64(const void* p) { return *(const MOEQ_G
 __device__ __forceinline__ uint64_t gld_u64(const void* p) { return *(const MOEQ_GLOBAL uint64_t*)p; }
 __device__ __forceinline__ int32_t gld_i32(const void* p) { return *(const MOEQ_GLOBAL int32_t*)p; }
 __device__ __forceinline__ void gst_f32(void* p, float v) { *(MOEQ_GLOBAL float*)p = v; }
+__device__ __forceinline__ void gst_f4(void* p, float4 v) {   // 16-byte aligned
+  *(MOEQ_GLOBAL g_f32x4*)p = g_f32x4{v.x, v.y, v.z, v.w};
+}
 __device__ __forceinline__ void gst_u32(void* p, uint32_t v) { *(MOEQ_GLOBAL uint32_t*)p = v; }
 __device__ __forceinline__ void gst_i32(void* p, int32_t v) { *(MOEQ_GLOBAL int32_t*)p = v; }
 __device__ __forceinline__ void gst_i16(void* p, int16_t v) { *(MOEQ_GLOBAL int16_t*)p = v; }

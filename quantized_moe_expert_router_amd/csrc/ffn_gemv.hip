@@ -313,15 +313,46 @@ __global__ __launch_bounds__(256) void k_down(DownArgs a) {
 // staged in fp32 by the down kernels (rounding each of the k+1 terms to fp32
 // first moves y by about 1e-7 relative, far inside the y tolerance; the
 // bit-exact q8_K(h) lies upstream of it).
+// Four consecutive outputs per thread, a workgroup per (token, 1024 columns):
+// the staged rows of up to kCombineRows slots are loaded before they are
+// added (in slot order), so a thread waits for one round trip per that many
+// slots.
+constexpr int kCombineRows = 12;
 __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ yp, int64_t T, int64_t H, int k,
-                                                 int has_shared, float* __restrict__ y, int accumulate) {
-  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (idx >= T * H) return;
-  const int64_t t = idx / H, r = idx % H;
-  double acc = 0.0;
-  for (int s = 0; s < k; ++s) acc += (double)yp[(t * k + s) * H + r];
-  if (has_shared) acc += (double)yp[(T * k + t) * H + r];
-  y[idx] = accumulate ? (float)((double)y[idx] + acc) : (float)acc;
+                                                 int has_shared, float* __restrict__ y, int accumulate,
+                                                 int blocks_per_row) {
+  const int64_t t = (int64_t)(blockIdx.x / (unsigned)blocks_per_row);
+  const int64_t c = ((int64_t)(blockIdx.x % (unsigned)blocks_per_row) * 256 + threadIdx.x) * 4;
+  if (t >= T || c >= H) return;
+  double a0 = 0.0, a1 = 0.0, a2 = 0.0, a3 = 0.0;
+  const float* base = yp + t * k * H + c;
+  for (int s = 0; s < k; s += kCombineRows) {
+    float4 v[kCombineRows];
+#pragma unroll
+    for (int j = 0; j < kCombineRows; ++j)
+      if (s + j < k) v[j] = gld_f4(base + (int64_t)(s + j) * H);
+#pragma unroll
+    for (int j = 0; j < kCombineRows; ++j) {
+      if (s + j < k) {
+        a0 += (double)v[j].x; a1 += (double)v[j].y; a2 += (double)v[j].z; a3 += (double)v[j].w;
+      }
+    }
+  }
+  if (has_shared) {
+    const float4 v = gld_f4(yp + (T * k + t) * H + c);
+    a0 += (double)v.x; a1 += (double)v.y; a2 += (double)v.z; a3 += (double)v.w;
+  }
+  float* out = y + t * H + c;
+  const bool al = (reinterpret_cast<uintptr_t>(y) & 15) == 0;   // the caller's y may be only 4-byte aligned
+  if (accumulate) {
+    a0 += (double)gld_f32(out); a1 += (double)gld_f32(out + 1);
+    a2 += (double)gld_f32(out + 2); a3 += (double)gld_f32(out + 3);
+  }
+  if (al) {
+    gst_f4(out, make_float4((float)a0, (float)a1, (float)a2, (float)a3));
+  } else {
+    gst_f32(out, (float)a0); gst_f32(out + 1, (float)a1); gst_f32(out + 2, (float)a2); gst_f32(out + 3, (float)a3);
+  }
 }
 
 // One token (decode): down rows and the weighted combine, slot table from
@@ -412,10 +443,11 @@ int launch_down_rows1(int fmt, int cpl, dim3 grid, const DownArgs& a, hipStream_
 
 int launch_combine(const float* yp, int64_t T, int64_t H, int k, int has_shared, float* y, int accumulate,
                    hipStream_t s) {
-  const int64_t n = T * H;
-  if (n == 0) return 0;
-  hipLaunchKernelGGL(k_combine, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, yp, T, H, k, has_shared, y,
-                     accumulate);
+  if (T * H == 0) return 0;
+  if (H % 4 != 0) return -2;                      // (H is a multiple of 256)
+  const int bpr = (int)((H / 4 + 255) / 256);
+  hipLaunchKernelGGL(k_combine, dim3((unsigned)(T * bpr)), dim3(256), 0, s, yp, T, H, k, has_shared, y, accumulate,
+                     bpr);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
