@@ -892,7 +892,8 @@ __global__ __launch_bounds__(64) void k_mfma_plan(const int32_t* __restrict__ ac
                                                     const int32_t* __restrict__ offsets, int thr, int max_tiles,
                                                     int4* __restrict__ tiles, int32_t* __restrict__ count,
                                                     int4* __restrict__ thin, int32_t* __restrict__ thin_count) {
-  mfma_plan_block(active, offsets, MfmaPlan{thr, max_tiles, tiles, count, thin, thin_count});
+  __shared__ int ebase[kPlanMaxE + 1];
+  mfma_plan_block(active, offsets, MfmaPlan{thr, max_tiles, tiles, count, thin, thin_count}, ebase);
 }
 
 int launch_mfma_plan(const int32_t* active, const int32_t* offsets, int thr, int max_tiles, int4* tiles,

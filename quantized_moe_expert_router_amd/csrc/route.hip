@@ -206,9 +206,11 @@ __device__ int block_exclusive_scan(int v, int* tmp /* >= 16 ints */, int* total
   return before + x - v;
 }
 
-// counts[E] -> offsets[E+1] and the active list; `cnt` lives in LDS.
+// counts[E] -> offsets[E+1] and the active list; `cnt` lives in LDS.  With
+// loff / lact (LDS [E+1] each) the offsets and the list are also kept there.
 __device__ void offsets_and_union(int* cnt, int64_t E, int32_t* offsets, int32_t* active,
-                                  int* scan_tmp, int* base_out /* LDS [E] or null */) {
+                                  int* scan_tmp, int* base_out /* LDS [E] or null */, int* loff = nullptr,
+                                  int* lact = nullptr) {
   const int per = (int)((E + blockDim.x - 1) / blockDim.x);
   const int64_t e0 = (int64_t)threadIdx.x * per;
   int local = 0, flags = 0;
@@ -225,13 +227,19 @@ __device__ void offsets_and_union(int* cnt, int64_t E, int32_t* offsets, int32_t
       const int c = cnt[e];   // read before base_out (which may alias cnt) is written
       offsets[e] = run;
       if (base_out) base_out[e] = run;
-      if (c > 0) active[1 + frun++] = (int32_t)e;
+      if (loff) loff[e] = run;
+      if (c > 0) {
+        if (lact) lact[1 + frun] = (int32_t)e;
+        active[1 + frun++] = (int32_t)e;
+      }
       run += c;
     }
   }
   if (threadIdx.x == 0) {
     offsets[E] = tot;
     active[0] = ftot;
+    if (loff) loff[E] = tot;
+    if (lact) lact[0] = ftot;
   }
 }
 
@@ -306,11 +314,12 @@ __global__ __launch_bounds__(1024) void k_select_small(const double* __restrict_
     int* skey = ids_s + T * k;                                // [64]
     int* lact = skey + kSmallPairs;                           // [65]
     int* loff = lact + kSmallPairs + 1;                       // [E + 1]
+    int* ebase = loff + E + 1;                                // [E + 1] tile-list scratch
     __syncthreads();
     small_lists(ids_s, (int)(T * k), E, offsets, pairs, active, skey, loff, lact);
     if (plan.tiles != nullptr) {
       __syncthreads();
-      mfma_plan_block(lact, loff, plan);
+      mfma_plan_block(lact, loff, plan, ebase);
     }
     return;
   }
@@ -334,7 +343,7 @@ __global__ __launch_bounds__(1024) void k_select_small(const double* __restrict_
   }
   if (plan.tiles != nullptr) {   // the MFMA tile lists of the FFN that follows
     __syncthreads();
-    mfma_plan_block(active, offsets, plan);
+    mfma_plan_block(active, offsets, plan, cnt);   // cnt and scan_tmp (E + 64 ints) are free here
   }
 }
 
@@ -366,25 +375,41 @@ __global__ __launch_bounds__(1024) void k_scan(int32_t* __restrict__ hist, int64
   extern __shared__ int lds[];
   int* tot = lds;              // [E]
   int* scan_tmp = tot + E;     // [64]
+  int* loff = scan_tmp + 64;   // [E + 1] offsets and union for the tile lists
+  int* lact = loff + E + 1;    // [E + 1]
+  // the chunk counts of an expert are read kScanBatch at a time, all loads of
+  // a batch in flight before the first is used
+  constexpr int kScanBatch = 16;
   for (int64_t e = threadIdx.x; e < E; e += blockDim.x) {
     int s = 0;
-    for (int64_t c = 0; c < nchunks; ++c) s += hist[c * E + e];
+    for (int64_t c0 = 0; c0 < nchunks; c0 += kScanBatch) {
+      int h[kScanBatch];
+#pragma unroll
+      for (int j = 0; j < kScanBatch; ++j) h[j] = c0 + j < nchunks ? gld_i32(hist + (c0 + j) * E + e) : 0;
+#pragma unroll
+      for (int j = 0; j < kScanBatch; ++j) s += h[j];
+    }
     tot[e] = s;
   }
   __syncthreads();
-  offsets_and_union(tot, E, offsets, active, scan_tmp, tot);   // tot becomes the offsets
+  offsets_and_union(tot, E, offsets, active, scan_tmp, tot, loff, lact);   // tot becomes the offsets
   __syncthreads();
   for (int64_t e = threadIdx.x; e < E; e += blockDim.x) {
     int run = tot[e];
-    for (int64_t c = 0; c < nchunks; ++c) {
-      const int h = hist[c * E + e];
-      hist[c * E + e] = run;
-      run += h;
+    for (int64_t c0 = 0; c0 < nchunks; c0 += kScanBatch) {
+      int h[kScanBatch];
+#pragma unroll
+      for (int j = 0; j < kScanBatch; ++j) h[j] = c0 + j < nchunks ? gld_i32(hist + (c0 + j) * E + e) : 0;
+#pragma unroll
+      for (int j = 0; j < kScanBatch; ++j) {
+        if (c0 + j < nchunks) gst_i32(hist + (c0 + j) * E + e, run);
+        run += h[j];
+      }
     }
   }
-  if (plan.tiles != nullptr) {   // the MFMA tile lists of the FFN that follows
+  if (plan.tiles != nullptr) {   // the MFMA tile lists of the FFN that follows (from the LDS copies)
     __syncthreads();
-    mfma_plan_block(active, offsets, plan);
+    mfma_plan_block(lact, loff, plan, tot);   // tot and scan_tmp (E + 64 ints) are free here
   }
 }
 
@@ -396,11 +421,18 @@ __global__ __launch_bounds__(64) void k_scatter(const int32_t* __restrict__ ids,
   const int lane = lane_id();
   const int64_t t0 = (int64_t)blockIdx.x * kChunkT;
   const int64_t t1 = (t0 + kChunkT) < T ? (t0 + kChunkT) : T;
-  for (int64_t t = t0; t < t1; ++t) {
-    if (lane < k) {
-      const int e = ids[t * k + lane];
-      const int pos = atomicAdd(&cur[e], 1);
-      pairs[pos] = (int32_t)(t * k + lane);
+  // ids of 8 tokens in flight at once; the LDS atomics still go out token by
+  // token (one wave: they complete in issue order, so positions rise with t)
+  for (int64_t t = t0; t < t1; t += 8) {
+    int e[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) e[j] = (lane < k && t + j < t1) ? gld_i32(ids + (t + j) * k + lane) : -1;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      if (e[j] >= 0) {
+        const int pos = atomicAdd(&cur[e[j]], 1);
+        gst_i32(pairs + pos, (int32_t)((t + j) * k + lane));
+      }
     }
   }
 }
@@ -446,7 +478,7 @@ int launch_route(int64_t T, int64_t H, int64_t E, int k, int gating, float scale
   double* lg = logits ? logits : reinterpret_cast<double*>(wsb);
   launch_logits(T, H, E, x, W, bias, lg, xq, s);
   if (T <= kSmallT) {
-    size_t lds = (size_t)(T * k + E + 2 * kSmallPairs + 2) * sizeof(int);   // either list path
+    size_t lds = (size_t)(T * k + 2 * E + 2 * kSmallPairs + 3) * sizeof(int);   // either list path
 #define MOEQ_SEL(N) hipLaunchKernelGGL(k_select_small<N>, dim3(1), dim3(1024), lds, s, lg, T, E, k, gating, \
                                         scale, ids, w, offsets, pairs, active, pl)
     if (E <= 256) MOEQ_SEL(4);
@@ -465,7 +497,7 @@ int launch_route(int64_t T, int64_t H, int64_t E, int k, int gating, float scale
     else MOEQ_TOPK(64);
 #undef MOEQ_TOPK
     hipLaunchKernelGGL(k_hist, dim3((unsigned)nch), dim3(256), (size_t)E * sizeof(int), s, ids, T, k, E, hist);
-    hipLaunchKernelGGL(k_scan, dim3(1), dim3(1024), (size_t)(E + 64) * sizeof(int), s, hist, nch, E, offsets,
+    hipLaunchKernelGGL(k_scan, dim3(1), dim3(1024), (size_t)(3 * E + 66) * sizeof(int), s, hist, nch, E, offsets,
                        active, pl);
     hipLaunchKernelGGL(k_scatter, dim3((unsigned)nch), dim3(64), (size_t)E * sizeof(int), s, ids, T, k, E,
                        hist, pairs);
