@@ -427,13 +427,12 @@ __global__ __launch_bounds__(64) void k_scatter(const int32_t* __restrict__ ids,
     int e[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) e[j] = (lane < k && t + j < t1) ? gld_i32(ids + (t + j) * k + lane) : -1;
+    int pos[8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      if (e[j] >= 0) {
-        const int pos = atomicAdd(&cur[e[j]], 1);
-        gst_i32(pairs + pos, (int32_t)((t + j) * k + lane));
-      }
-    }
+    for (int j = 0; j < 8; ++j) pos[j] = e[j] >= 0 ? atomicAdd(&cur[e[j]], 1) : -1;
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if (pos[j] >= 0) gst_i32(pairs + pos[j], (int32_t)((t + j) * k + lane));
   }
 }
 
