@@ -191,20 +191,18 @@ template <> struct Mf<FQ4K> {
 template <> struct Mf<FQ2K> {
   static constexpr int NBSP = 16;  // one sum per 16-sub-block: bsums[j]
   struct Wt { uint4 c[2]; uint4 sm; uint32_t dd; };
-  // Tiled layout (32-row units): lane (half g, row r) reads the two 16 B
-  // pieces of its half, each load instruction covering 1 KB contiguously.
+  // Tiled layout (2688-byte 32-row units): lane (half g, row r) reads the two
+  // 16 B pieces of its half, each load instruction covering 1 KB contiguously,
+  // then the row's scales and d from the same unit.
   __device__ static Wt load(const uint8_t* W, int64_t N, int64_t nbK, int64_t row, int64_t sb, int g) {
-    const int64_t units = ((N + 31) >> 5) * nbK, u = wave_uni(row >> 5) * nbK + sb;
+    const int64_t u = wave_uni(row >> 5) * nbK + sb;
     const uint32_t r = (uint32_t)row & 31u;
-    const uint8_t* Wb = wave_uni_ptr(W);
-    const uint8_t* cb = Wb + u * 2048;
-    const uint8_t* sbp = Wb + align256((size_t)units * 2048) + u * 512;
-    const uint8_t* db = Wb + align256((size_t)units * 2048) + align256((size_t)units * 512) + u * 128;
+    const uint8_t* cb = wave_uni_ptr(W) + u * kQ2KUnit;   // the unit: codes, scales, d
     Wt w;
 #pragma unroll
     for (int k = 0; k < 2; ++k) w.c[k] = gld_u4(cb + (1024u * (uint32_t)k + 16u * (32u * (uint32_t)g + r)));
-    w.sm = gld_u4(sbp + 16u * r);
-    w.dd = gld_u32(db + 4u * r);
+    w.sm = gld_u4(cb + ((uint32_t)kQ2KScales + 16u * r));
+    w.dd = gld_u32(cb + ((uint32_t)kQ2KD + 4u * r));
     return w;
   }
   // MFMA p: lane half g holds sub-block 2p+g (elements 32p+16g .. +15), whose

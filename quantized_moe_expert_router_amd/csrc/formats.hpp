@@ -19,16 +19,16 @@
 //           high2(elem 32j + 4(4a+s) + b)
 //         plane S  16 B/sb: int8 scales;  plane D 2 B/sb: fp16 d
 //   Q2_K  tiled: unit u = (row / 32) * nb + sb (32 rows x one super-block),
-//         each plane contiguous per unit, so a wave reading the 32 rows of a
-//         unit reads whole lines (and the matrix-core tiles read it with
-//         every load instruction contiguous)
-//         plane Q 2048 B/unit: 16 B at 1024 k + 16 (32 g + row % 32) = the
-//           words of steps 4k..4k+3 of half g; step p of half g is sub-block
-//           2p + g, its word holds element 4i + b of the sub-block at bits
-//           8b + 2i.  A lane chunk j = 2k + g is that 16 B piece: sub-blocks
+//         2688 contiguous bytes at 2688 u, so a wave reading the 32 rows of a
+//         unit reads whole lines of one stretch (and the matrix-core tiles
+//         read it with every load instruction contiguous); inside the unit:
+//         codes 2048 B: 16 B at 1024 k + 16 (32 g + row % 32) = the words of
+//           steps 4k..4k+3 of half g; step p of half g is sub-block 2p + g,
+//           its word holds element 4i + b of the sub-block at bits 8b + 2i.
+//           A lane chunk j = 2k + g is that 16 B piece: sub-blocks
 //           8k + g + 2t, t = 0..3
-//         plane S  512 B/unit: the row's 16 bytes (sc | m << 4) at 16 (row % 32)
-//         plane D  128 B/unit: d, dmin at 4 (row % 32)
+//         scales 512 B at 2048: the row's 16 bytes (sc | m << 4) at 16 (row % 32)
+//         d 128 B at 2560: d, dmin at 4 (row % 32)
 //   Q8_0  plane Q 256 B/sb: chunk b = the 32 int8 quants of block b
 //         plane D  16 B/sb: eight fp16 d
 #pragma once
@@ -37,6 +37,9 @@
 namespace moeq {
 
 template <int FMT> struct Fmt;
+
+// Q2_K unit: 32 rows x one super-block (codes, then scales, then d)
+constexpr int kQ2KUnit = 2688, kQ2KScales = 2048, kQ2KD = 2560;
 
 // Host-side geometry shared by every format.
 struct Geo {
@@ -50,7 +53,7 @@ __host__ __device__ inline Geo geo_of(int fmt) {
   switch (fmt) {
     case FQ4K: return Geo{32, 2, {128, 16, 0, 0}, 1};
     case FQ6K: return Geo{32, 4, {128, 64, 16, 2}, 1};
-    case FQ2K: return Geo{64, 3, {64, 16, 4, 0}, 32};
+    case FQ2K: return Geo{64, 1, {84, 0, 0, 0}, 32};   // one plane of 2688-byte units
     case FQ80: return Geo{32, 2, {256, 16, 0, 0}, 1};
   }
   return Geo{0, 0, {0, 0, 0, 0}, 1};
@@ -152,14 +155,13 @@ template <> struct Fmt<FQ2K> {
   __device__ static constexpr int bsidx(int j, int t) { return sub_of(j, t); }
   struct W { uint4 q; uint2 sm; uint32_t dd; };
   __device__ static W load(const uint8_t* m, int64_t rows, int64_t nb, int64_t row, int64_t sb, int j) {
-    const int64_t units = ((rows + 31) >> 5) * nb, u = (row >> 5) * nb + sb;
+    const int64_t u = (row >> 5) * nb + sb;
     const int r = (int)(row & 31);
-    const uint8_t* ps = m + align256((size_t)units * 2048);
-    const uint8_t* pd = ps + align256((size_t)units * 512);
+    const uint8_t* U = m + u * kQ2KUnit;
     W w;
-    w.q = gld_u4(m + u * 2048 + 1024 * (j >> 1) + 16 * (32 * (j & 1) + r));
-    w.sm = gld_u2(ps + u * 512 + 16 * r + 8 * (j >> 1));
-    w.dd = gld_u32(pd + u * 128 + 4 * r);
+    w.q = gld_u4(U + 1024 * (j >> 1) + 16 * (32 * (j & 1) + r));
+    w.sm = gld_u2(U + kQ2KScales + 16 * r + 8 * (j >> 1));
+    w.dd = gld_u32(U + kQ2KD + 4 * r);
     return w;
   }
   // word t: sub-block sub_of(j, t); element 4i + b at bits 8b + 2i

@@ -89,20 +89,19 @@ __global__ __launch_bounds__(256) void k_pack(const uint8_t* __restrict__ aos, i
     pd[sbi * 2 + 1] = src[1];
   } else if (FMT == FQ2K) {
     // tiled (32-row units); see the Q2_K plane description
-    const int64_t row = sbi / nb, sb = sbi % nb, units = ((rows + 31) >> 5) * nb, u = (row >> 5) * nb + sb;
+    const int64_t row = sbi / nb, sb = sbi % nb, u = (row >> 5) * nb + sb;
     const int r = (int)(row & 31);
-    uint8_t* ps = m + align256((size_t)units * 2048);
-    uint8_t* pd = ps + align256((size_t)units * 512);
+    uint8_t* U = m + u * kQ2KUnit;
     for (int g = 0; g < 2; ++g)
       for (int p = 0; p < 8; ++p) {
         const int j = 2 * p + g;                // sub-block of step p, half g
         uint32_t v = 0;
         for (int i = 0; i < 4; ++i)
           for (int b = 0; b < 4; ++b) v |= (uint32_t)q2k_code(src, 16 * j + 4 * i + b) << (8 * b + 2 * i);
-        st_u32(m + u * 2048 + 1024 * (p >> 2) + 16 * (32 * g + r) + 4 * (p & 3), v);
+        st_u32(U + 1024 * (p >> 2) + 16 * (32 * g + r) + 4 * (p & 3), v);
       }
-    for (int i = 0; i < 16; ++i) ps[u * 512 + 16 * r + i] = src[4 + i];
-    for (int i = 0; i < 4; ++i) pd[u * 128 + 4 * r + i] = src[i];
+    for (int i = 0; i < 16; ++i) U[kQ2KScales + 16 * r + i] = src[4 + i];
+    for (int i = 0; i < 4; ++i) U[kQ2KD + 4 * r + i] = src[i];
   } else {  // Q8_0: eight 34-byte blocks per super-block
     uint8_t* pd = m + align256(nsb * 256);
     for (int b = 0; b < 8; ++b) {

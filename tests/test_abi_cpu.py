@@ -36,8 +36,8 @@ def test_status_strings():
 def test_packed_bytes_and_workspace_queries():
     assert moeq.moeq_packed_bytes(moeq.Q4_K, 512, 2048) == 512 * 8 * 144
     assert moeq.moeq_packed_bytes(moeq.Q6_K, 2048, 512) == 2048 * 2 * 210
-    # Q2_K is laid out in 32-row units: one row pads to a unit, each plane 256-byte aligned
-    assert moeq.moeq_packed_bytes(moeq.Q2_K, 1, 256) == 32 * 64 + 32 * 16 + 256
+    # Q2_K is laid out in 2688-byte 32-row units: one row pads to a unit (256-byte aligned total)
+    assert moeq.moeq_packed_bytes(moeq.Q2_K, 1, 256) == 2816
     assert moeq.moeq_packed_bytes(moeq.Q2_K, 1536, 4096) == 1536 * 16 * 84
     assert moeq.moeq_packed_bytes(9, 1, 256) == 0
     assert moeq.moeq_packed_bytes(moeq.Q4_K, 1, 100) == 0
