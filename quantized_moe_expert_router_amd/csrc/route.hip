@@ -111,8 +111,11 @@ constexpr int kRt = 64, kRe = 64, kRk = 32, kRpad = 36;
 __global__ __launch_bounds__(256) void k_logits_mfma(const float* __restrict__ x, const float* __restrict__ W,
                                                      const float* __restrict__ bias, int64_t T, int64_t H,
                                                      int64_t E, double* __restrict__ logits) {
-  __shared__ float xs[kRt][kRpad];
-  __shared__ float ws[kRe][kRpad];
+  // two LDS stages: block k0 is written while the MFMAs of block k0 - 32 may
+  // still read the other stage, and the global loads of the next block are in
+  // flight during this block's MFMAs (one barrier per block)
+  __shared__ float xs[2][kRt][kRpad];
+  __shared__ float ws[2][kRe][kRpad];
   const int tid = threadIdx.x, wave = tid >> 6, lane = lane_id();
   const int64_t t0 = (int64_t)blockIdx.x * kRt, e0 = (int64_t)blockIdx.y * kRe;
   const int wt = (wave & 1) * 32, we = (wave >> 1) * 32;
@@ -122,27 +125,36 @@ __global__ __launch_bounds__(256) void k_logits_mfma(const float* __restrict__ x
   for (int i = 0; i < 2; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j) acc[i][j] = (v4d){0.0, 0.0, 0.0, 0.0};
-  for (int64_t k0 = 0; k0 < H; k0 += kRk) {
-    __syncthreads();
+  float4 xv[2], wv[2];
+  auto fetch = [&](int64_t k0) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const int idx = tid + 256 * i, row = idx >> 3, c4 = idx & 7;
       const int64_t kc = k0 + 4 * c4;
       const int64_t tr = t0 + row, er = e0 + row;
       const float4 zero = make_float4(0.f, 0.f, 0.f, 0.f);
-      const float4 xv = (tr < T && kc < H) ? gld_f4(x + tr * H + kc) : zero;
-      const float4 wv = (er < E && kc < H) ? gld_f4(W + er * H + kc) : zero;
-      *reinterpret_cast<float4*>(&xs[row][4 * c4]) = xv;
-      *reinterpret_cast<float4*>(&ws[row][4 * c4]) = wv;
+      xv[i] = (tr < T && kc < H) ? gld_f4(x + tr * H + kc) : zero;
+      wv[i] = (er < E && kc < H) ? gld_f4(W + er * H + kc) : zero;
+    }
+  };
+  fetch(0);
+  int buf = 0;
+  for (int64_t k0 = 0; k0 < H; k0 += kRk, buf ^= 1) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int idx = tid + 256 * i, row = idx >> 3, c4 = idx & 7;
+      *reinterpret_cast<float4*>(&xs[buf][row][4 * c4]) = xv[i];
+      *reinterpret_cast<float4*>(&ws[buf][row][4 * c4]) = wv[i];
     }
     __syncthreads();
+    if (k0 + kRk < H) fetch(k0 + kRk);
 #pragma unroll
     for (int kk = 0; kk < kRk / 4; ++kk) {
       double a[2], b[2];
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
-        a[i] = (double)xs[wt + 16 * i + m16][4 * kk + kq];
-        b[i] = (double)ws[we + 16 * i + m16][4 * kk + kq];
+        a[i] = (double)xs[buf][wt + 16 * i + m16][4 * kk + kq];
+        b[i] = (double)ws[buf][we + 16 * i + m16][4 * kk + kq];
       }
 #pragma unroll
       for (int i = 0; i < 2; ++i)
