@@ -313,7 +313,8 @@ def _custom_cfg(**kw):
 @pytest.mark.parametrize("variant", ["one_expert_all_tokens", "k_equals_E", "k1", "ties", "softmax_all",
                                      "sigmoid", "q2k_q6k_q80_mix", "t1_mixed_shared", "t1_k32", "t1_ties",
                                      "t1_softmax_all", "t1_sigmoid_e600", "ragged_tiles_q4k",
-                                     "ragged_tiles_q2k_q6k_shared_q80", "ragged_tiles_q8_q4"])
+                                     "ragged_tiles_q2k_q6k_shared_q80", "ragged_tiles_q8_q4",
+                                     "many_tiles_spanning_lanes", "thin_hf_q80_q4k"])
 def test_edge_layers(variant, fused, path):
     say("edge", variant, fused, path)
     kw = {}
@@ -349,6 +350,16 @@ def test_edge_layers(variant, fused, path):
     elif variant == "ragged_tiles_q8_q4":
         kw = dict(T=33, E=4, k=2, F=256, H=1024, fmt_gate=syn.Q8_0, fmt_up=syn.Q8_0, fmt_down=syn.Q4_K,
                   gating=syn.SIGMOID_TOPK)
+    elif variant == "many_tiles_spanning_lanes":
+        # about 2000 rows per expert: about 190 32-row tiles, so the tile-list
+        # lanes start inside an expert's run of tiles (more than 256 tokens:
+        # the chunked list kernels, tile lists at the tail of the scan)
+        kw = dict(T=3000, E=3, k=2, F=256, H=256)
+    elif variant == "thin_hf_q80_q4k":
+        # a small union of 8-row tiles: the fp32-h gate/up and down kernels with
+        # Q8_0 gate/up and Q4_K down, shared expert likewise
+        kw = dict(T=6, E=8, k=2, F=512, H=512, fmt_gate=syn.Q8_0, fmt_up=syn.Q8_0, fmt_down=syn.Q4_K,
+                  shared=True, F_shared=256, sh_fmt_gate=syn.Q8_0, sh_fmt_up=syn.Q8_0, sh_fmt_down=syn.Q4_K)
     cfg = _custom_cfg(**kw)
     layer = syn.gen_layer(cfg)
     if variant == "t1_ties":
