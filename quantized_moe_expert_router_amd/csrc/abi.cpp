@@ -6,12 +6,14 @@
 #include "../../include/moeq.h"
 #include "formats.hpp"
 #include "launch.hpp"
+#include "mfma_plan.hpp"
 
 using namespace moeq;
 
 namespace {
 
 constexpr int64_t kMaxE = 4096;
+static_assert(kMaxE <= kPlanMaxE, "the tile planner's LDS scratch holds kPlanMaxE + 1 entries");
 constexpr int kMaxK = 32;
 constexpr int kRowBlock = 64;     // rows per expert-major down work item
 

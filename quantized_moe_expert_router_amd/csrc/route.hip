@@ -2,6 +2,7 @@
 // gate weights, and the token x expert lists (counting sort by expert, tokens
 // rising inside an expert) plus the expert union.
 #include <float.h>
+#include <algorithm>
 #include <limits.h>
 
 #include "common.hpp"
@@ -490,7 +491,10 @@ int launch_route(int64_t T, int64_t H, int64_t E, int k, int gating, float scale
   launch_logits(T, H, E, x, W, bias, lg, xq, s);
   if (T <= kSmallT) {
     size_t lds = (size_t)(T * k + 2 * E + 2 * kSmallPairs + 3) * sizeof(int);   // either list path
-#define MOEQ_SEL(N) hipLaunchKernelGGL(k_select_small<N>, dim3(1), dim3(1024), lds, s, lg, T, E, k, gating, \
+    // up to 64 pairs: one wave per token and one for the lists, so fewer
+    // waves (cheaper barriers); more pairs: block scans over 1024 threads
+    const unsigned nt = T * k <= kSmallPairs ? (unsigned)(64 * std::min<int64_t>(16, std::max<int64_t>(4, T))) : 1024u;
+#define MOEQ_SEL(N) hipLaunchKernelGGL(k_select_small<N>, dim3(1), dim3(nt), lds, s, lg, T, E, k, gating, \
                                         scale, ids, w, offsets, pairs, active, pl)
     if (E <= 256) MOEQ_SEL(4);
     else if (E <= 512) MOEQ_SEL(8);
