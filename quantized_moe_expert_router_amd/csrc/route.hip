@@ -14,7 +14,7 @@ namespace moeq {
 
 constexpr int kLogitTok = 16;       // tokens per logits tile
 constexpr int kSmallT = 256;        // single-workgroup selection + lists up to this many tokens
-constexpr int kChunkT = 256;        // tokens per chunk of the multi-kernel lists path
+constexpr int kChunkT = 128;        // tokens per chunk of the multi-kernel lists path
 constexpr int kMfmaRouteT = 256;    // from this many tokens the logits run on fp64 matrix cores
 
 // logits[t, e] = sum_i W[e, i] * x[t, i] (+ bias[e]) in fp64.  The fp32*fp32
