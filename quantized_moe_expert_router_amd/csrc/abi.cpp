@@ -94,7 +94,7 @@ FfnLayout ffn_layout(const moeq_ffn_desc* d) {
   L.off_yp = o;  o += align256((size_t)L.nrows * d->H * sizeof(float));
   L.off_hq = o;  o += align256((size_t)d->T * d->k * (d->F / 256) * kQ8KBytes);
   L.off_hqs = o; o += align256(sh ? (size_t)d->T * (d->F_shared / 256) * kQ8KBytes : 0);
-  L.off_slots = o; o += align256((size_t)(d->k + 1) * sizeof(SlotRec));
+  L.off_slots = o; o += align256((size_t)kSlotCopies * (d->k + 1) * sizeof(SlotRec));
   L.off_tiles = o; o += align256((size_t)L.max_tiles * sizeof(int4));
   L.off_thin = o;  o += align256((size_t)L.max_thin * sizeof(int4));
   L.off_count = o; o += 256;                     // [0]: 32-row tiles, [1]: 8-row tiles

@@ -17,7 +17,12 @@ constexpr int kLdsQ8Blocks = 4 * kQ8PerWave;
 constexpr int kDown1Steps = 1;
 
 // One token: what the down kernel needs per slot (slot k = shared expert),
-// written by the gate/up kernel.
+// written by the gate/up kernel.  The table holds kSlotCopies copies of the
+// k+1 records, copy c written by a gate/up workgroup whose flat index is c
+// modulo 8 and read by the down workgroups with that index modulo 8: workgroups
+// are dealt to the 8 XCDs in turn, so the reader usually finds the record in
+// its own XCD's L2.  Every copy is complete whatever the placement.
+constexpr int kSlotCopies = 8;
 struct SlotRec {
   const void* wd;   // packed down matrix, null when the expert is not resident
   double wt;        // gate weight (shared: shared_scale or 1)

@@ -135,9 +135,17 @@ __device__ __forceinline__ void gateup1_body(const GateUpArgs& a, int bx, int sl
     if (Wd == nullptr || Wu == nullptr) Wg = nullptr;
     prow = slot;
   }
-  if (a.slots != nullptr && bx == 0 && threadIdx.x == 0) {
-    a.slots[shared ? a.k : slot].wd = (Wg == nullptr || Wu == nullptr) ? nullptr : Wd;
-    a.slots[shared ? a.k : slot].wt = wt;
+  if (a.slots != nullptr && threadIdx.x < kSlotCopies) {
+    // copy c of this slot's record comes from the workgroup of this grid row
+    // whose flat index is c modulo 8; when the row has fewer than 8
+    // workgroups, workgroup 0 also writes the copies no workgroup sits on
+    const int gx = (int)gridDim.x, c = (int)threadIdx.x;
+    const int r = (c - gx * (int)blockIdx.y) & (kSlotCopies - 1);
+    if (r == bx || (bx == 0 && r >= gx)) {
+      SlotRec* rec = a.slots + (int64_t)c * (a.k + 1) + (shared ? a.k : slot);
+      rec->wd = (Wg == nullptr || Wu == nullptr) ? nullptr : Wd;
+      rec->wt = wt;
+    }
   }
   if (Wg == nullptr || Wu == nullptr) return;   // not resident: its pair adds nothing
   const int64_t row0 = (int64_t)bx * (4 * a.steps * rps) + (int64_t)wave * a.steps * rps + rig;
@@ -208,6 +216,8 @@ __device__ __forceinline__ void load_x_chunk_lds(const uint8_t* xrow, int c, int
 // activation chunks from LDS, and leave w * (W_d h^) per (slot rank, row) in
 // LDS; the sum over slots in rank order, then the shared expert, happens in
 // the workgroup.
+static_assert(kLdsQ8Blocks * kLdsQ8Blocks < 65536, "the 16-bit reciprocal quotient of down1_body needs b * nb < 2^16");
+
 template <int FMT, int CPL, int ST>
 __device__ __forceinline__ void down1_body(const DownArgs& a, int bx) {
   using L = Fmt<FMT>;
@@ -217,7 +227,7 @@ __device__ __forceinline__ void down1_body(const DownArgs& a, int bx) {
   __shared__ double yps[kMaxSlots][kMaxRows];
   __shared__ const uint8_t* swd[kMaxSlots];
   __shared__ double swt[kMaxSlots];
-  const int wave = threadIdx.x >> 6, lane = lane_id();
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = lane_id();
   const int lpr = a.lpr, rps = kWave / lpr, rig = lane / lpr, lir = lane % lpr;
   const int64_t nb = a.F / 256;
   const int rows_wg = rps * ST;            // at most kMaxRows (checked by the host)
@@ -225,21 +235,27 @@ __device__ __forceinline__ void down1_body(const DownArgs& a, int bx) {
   const int n_routed = a.k;
   const int n_slots = n_routed + a.has_shared;
   const int nblk = n_slots * (int)nb;       // at most kLdsQ8Blocks (checked by the host)
+  // block b of the h rows is block b - s*nb of slot s = b / nb; with
+  // b < kLdsQ8Blocks, nb <= kLdsQ8Blocks the quotient is (b * inv_nb) >> 16
+  const uint32_t inv_nb = (65536u + (uint32_t)nb - 1) / (uint32_t)nb;
 
-  // this wave's q8_K(h) blocks (wave, wave+4, ...): fp32 loads first
+  // The down weight loads wait for the slot table the gate/up kernel left
+  // (each slot's down matrix and weight): read it first, from the copy of
+  // this workgroup's XCD, before the h loads are in flight.
+  if (threadIdx.x < n_slots) {
+    const SlotRec* rec = a.slots + (int64_t)(bx & (kSlotCopies - 1)) * (a.k + 1) + threadIdx.x;
+    swd[threadIdx.x] = (const uint8_t*)rec->wd;
+    swt[threadIdx.x] = rec->wt;
+  }
+  // this wave's q8_K(h) blocks (wave, wave+4, ...): fp32 loads
   float4 hv[kQ8PerWave];
 #pragma unroll
   for (int j = 0; j < kQ8PerWave; ++j) {
     const int b = wave + 4 * j;
     if (b < nblk) {
-      const int s = b / (int)nb, bb = b % (int)nb;
+      const int s = (int)(((uint32_t)b * inv_nb) >> 16), bb = b - s * (int)nb;
       hv[j] = gld_f4(a.hbuf + (int64_t)s * a.hstride + bb * 256 + 4 * lane);
     }
-  }
-  // the gate/up kernel left each slot's down matrix and weight in the slot table
-  if (threadIdx.x < n_slots) {
-    swd[threadIdx.x] = (const uint8_t*)a.slots[threadIdx.x].wd;
-    swt[threadIdx.x] = a.slots[threadIdx.x].wt;
   }
   __syncthreads();
 
@@ -271,7 +287,7 @@ __device__ __forceinline__ void down1_body(const DownArgs& a, int bx) {
   for (int j = 0; j < kQ8PerWave; ++j) {
     const int b = wave + 4 * j;
     if (b < nblk) {
-      const int s = b / (int)nb, bb = b % (int)nb;
+      const int s = (int)(((uint32_t)b * inv_nb) >> 16), bb = b - s * (int)nb;
       uint8_t* o = hq_lds + b * kLdsQ8;
       float amax = fmaxf(fmaxf(fabsf(hv[j].x), fabsf(hv[j].y)), fmaxf(fabsf(hv[j].z), fabsf(hv[j].w)));
       amax = wave_max_f(amax);
