@@ -37,30 +37,15 @@ __device__ void write_routing_t1(const GateUpArgs& a, int my_i, float my_w) {
 // Slot u is the u-th ranked expert (u == k: the shared expert);
 // with NPER > 0 the workgroup routes inline from the logits (every wave runs
 // the same register top-k, so all workgroups agree), otherwise it reads
-// topk_ids.  The token's activation chunks are loaded before anything that
-// depends on the routing.
+// topk_ids.  The token's activation chunks are loaded after the weight
+// loads: during the routing only the logits and pointer tables are in flight.
 template <int FMT, int CPL, int NPER>
 __device__ __forceinline__ void gateup1_body(const GateUpArgs& a, int bx, int slot) {
   using L = Fmt<FMT>;
   constexpr int UNR = 2;   // the host gives at most 2 wave steps (2 / rows per step)
-  const int wave = threadIdx.x >> 6, lane = lane_id();
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = lane_id();
   const int lpr = a.lpr, rps = kWave / lpr, rig = lane / lpr, lir = lane % lpr;
   const int64_t nb = a.H / 256;
-  int xw[CPL][L::XDW], bs[CPL][L::NBS];
-  double dx[CPL];
-#pragma unroll
-  for (int c = 0; c < CPL; ++c) {
-    const int ch = lir + lpr * c;
-    if (ch < a.cpr) {
-      load_x_chunk<FMT>(a.xq, ch, xw[c], bs[c], dx[c]);
-    } else {
-#pragma unroll
-      for (int q = 0; q < L::XDW; ++q) xw[c][q] = 0;
-#pragma unroll
-      for (int q = 0; q < L::NBS; ++q) bs[c][q] = 0;
-      dx[c] = 0.0;
-    }
-  }
   const bool shared = a.mode == kModeShared || (a.mode == kModeBoth && slot == a.k);
   const uint8_t *Wg, *Wu;
   int64_t prow;
@@ -148,43 +133,58 @@ __device__ __forceinline__ void gateup1_body(const GateUpArgs& a, int bx, int sl
     }
   }
   if (Wg == nullptr || Wu == nullptr) return;   // not resident: its pair adds nothing
+  // At most UNR wave steps (the host's bound), so one pass covers the rows:
+  // the weight loads go out first, then the token's activation chunks, which
+  // the dot products need together with them.  Every load is issued (a step
+  // or row past the end reloads the wave's first row, a chunk past the row
+  // the last chunk; none of them is used): a conditional load would leave
+  // the compiler register copies that wait for it before the next loads.
   const int64_t row0 = (int64_t)bx * (4 * a.steps * rps) + (int64_t)wave * a.steps * rps + rig;
-  for (int st = 0; st < a.steps; st += UNR) {
-    typename L::W wg[UNR][CPL], wu[UNR][CPL];
-    int64_t row[UNR];
-    bool ok[UNR][CPL];
+  const int64_t row_dup = row0 < a.F ? row0 : a.F - 1;
+  typename L::W wg[UNR][CPL], wu[UNR][CPL];
+  int64_t row[UNR];
+  bool ok[UNR][CPL];
 #pragma unroll
-    for (int u = 0; u < UNR; ++u) {
-      row[u] = row0 + (int64_t)(st + u) * rps;
-      const bool rv = (st + u) < a.steps && row[u] < a.F;
+  for (int u = 0; u < UNR; ++u) {
+    row[u] = row0 + (int64_t)u * rps;
+    const bool rv = u < a.steps && row[u] < a.F;
+    const int64_t rl = rv ? row[u] : row_dup;
 #pragma unroll
-      for (int c = 0; c < CPL; ++c) {
-        const int ch = lir + lpr * c;
-        ok[u][c] = rv && ch < a.cpr;
-        if (ok[u][c]) {
-          wg[u][c] = L::load(Wg, a.F, nb, row[u], ch / L::CPS, ch % L::CPS);
-          wu[u][c] = L::load(Wu, a.F, nb, row[u], ch / L::CPS, ch % L::CPS);
-        }
-      }
+    for (int c = 0; c < CPL; ++c) {
+      const int ch = lir + lpr * c, cl = ch < a.cpr ? ch : a.cpr - 1;
+      ok[u][c] = rv && ch < a.cpr;
+      wg[u][c] = L::load(Wg, a.F, nb, rl, cl / L::CPS, cl % L::CPS);
+      wu[u][c] = L::load(Wu, a.F, nb, rl, cl / L::CPS, cl % L::CPS);
     }
+  }
+  int xw[CPL][L::XDW], bs[CPL][L::NBS];
+  double dx[CPL];
 #pragma unroll
-    for (int u = 0; u < UNR; ++u) {
-      double ag = 0.0, au = 0.0;
+  for (int c = 0; c < CPL; ++c) {
+    const int ch = lir + lpr * c;
+    load_x_chunk<FMT>(a.xq, ch < a.cpr ? ch : a.cpr - 1, xw[c], bs[c], dx[c]);
+  }
+  __builtin_amdgcn_sched_barrier(0);   // every load above is issued before any arithmetic below
 #pragma unroll
-      for (int c = 0; c < CPL; ++c) {
-        if (!ok[u][c]) continue;
-        const int j = (lir + lpr * c) % L::CPS;
-        int is[L::SPC];
-        L::isums(wg[u][c], xw[c], bs[c], is);
-        ag += L::term(wg[u][c], j, is, bs[c], dx[c]);
-        L::isums(wu[u][c], xw[c], bs[c], is);
-        au += L::term(wu[u][c], j, is, bs[c], dx[c]);
-      }
-      const double g = group_sum_dpp(ag, lpr);
-      const double uu = group_sum_dpp(au, lpr);
-      if (lir == lpr - 1 && (st + u) < a.steps && row[u] < a.F)
-        gst_f32(a.hbuf + prow * a.hstride + row[u], (float)(silu64(g) * uu));
+  for (int u = 0; u < UNR; ++u) {
+    double ag = 0.0, au = 0.0;
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) {
+      // computed on every lane (on the reloaded data where not ok), kept
+      // where ok: a branch here would let the compiler sink loads into it
+      const int ch = lir + lpr * c, j = (ch < a.cpr ? ch : a.cpr - 1) % L::CPS;
+      int is[L::SPC];
+      L::isums(wg[u][c], xw[c], bs[c], is);
+      const double tg = L::term(wg[u][c], j, is, bs[c], dx[c]);
+      L::isums(wu[u][c], xw[c], bs[c], is);
+      const double tu = L::term(wu[u][c], j, is, bs[c], dx[c]);
+      ag += ok[u][c] ? tg : 0.0;
+      au += ok[u][c] ? tu : 0.0;
     }
+    const double g = group_sum_dpp(ag, lpr);
+    const double uu = group_sum_dpp(au, lpr);
+    if (lir == lpr - 1 && u < a.steps && row[u] < a.F)
+      gst_f32(a.hbuf + prow * a.hstride + row[u], (float)(silu64(g) * uu));
   }
 }
 

@@ -44,39 +44,54 @@ __global__ __launch_bounds__(256) void k_logits(const float* __restrict__ x, con
 #pragma unroll
     for (int t = 0; t < kLogitTok; ++t) acc[t] = 0.0;
     for (int64_t i = i0 + lane; i < i1; i += 4 * kWave) {
+      // Every load is issued, a unit past the wave's range reloading unit 0
+      // and left out of the sums by a select after its FMAs: a conditional
+      // load would leave register copies that wait for it before the next
+      // loads go out.
+      bool uv[4];
+      int64_t iu[4];
       float4 w[4];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) w[u] = (i + u * kWave < i1) ? w4[i + u * kWave] : make_float4(0.f, 0.f, 0.f, 0.f);
-      // four tokens at a time: all their activation loads go out before the
-      // first FMA waits for them
+      for (int u = 0; u < 4; ++u) {
+        uv[u] = i + u * kWave < i1;
+        iu[u] = uv[u] ? i + u * kWave : i;
+        w[u] = w4[iu[u]];
+      }
+      // four tokens at a time (a token past the tile reloads the tile's
+      // last one): all their activation loads go out before the first FMA
 #pragma unroll
       for (int tg = 0; tg < kLogitTok; tg += 4) {
         if (tg < nt) {
           float4 xv[4][4];
 #pragma unroll
           for (int tt = 0; tt < 4; ++tt) {
-            if (tg + tt < nt) {
-              const float* xr = x + (t0 + tg + tt) * H;
+            const float* xr = x + (t0 + (tg + tt < nt ? tg + tt : nt - 1)) * H;
 #pragma unroll
-              for (int u = 0; u < 4; ++u)
-                xv[tt][u] = i + u * kWave < i1 ? gld_f4(xr + 4 * (i + u * kWave)) : make_float4(0.f, 0.f, 0.f, 0.f);
-            }
+            for (int u = 0; u < 4; ++u) xv[tt][u] = gld_f4(xr + 4 * iu[u]);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+          // the weights' fp64 conversions stay here, after this group's
+          // loads (shared by the groups, they would be hoisted to the
+          // weight loads and wait there)
+          float4 wv[4];
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            wv[u] = w[u];
+            asm volatile("" : "+v"(wv[u].x), "+v"(wv[u].y), "+v"(wv[u].z), "+v"(wv[u].w));
           }
 #pragma unroll
           for (int tt = 0; tt < 4; ++tt) {
-            if (tg + tt < nt) {
-              double a = acc[tg + tt];
+            if (tg + tt >= nt) continue;
+            double a = acc[tg + tt];
 #pragma unroll
-              for (int u = 0; u < 4; ++u) {
-                if (i + u * kWave < i1) {
-                  a = fma((double)w[u].x, (double)xv[tt][u].x, a);
-                  a = fma((double)w[u].y, (double)xv[tt][u].y, a);
-                  a = fma((double)w[u].z, (double)xv[tt][u].z, a);
-                  a = fma((double)w[u].w, (double)xv[tt][u].w, a);
-                }
-              }
-              acc[tg + tt] = a;
+            for (int u = 0; u < 4; ++u) {
+              double b = fma((double)wv[u].x, (double)xv[tt][u].x, a);
+              b = fma((double)wv[u].y, (double)xv[tt][u].y, b);
+              b = fma((double)wv[u].z, (double)xv[tt][u].z, b);
+              b = fma((double)wv[u].w, (double)xv[tt][u].w, b);
+              a = uv[u] ? b : a;
             }
+            acc[tg + tt] = a;
           }
         }
       }
