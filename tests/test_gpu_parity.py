@@ -314,7 +314,8 @@ def _custom_cfg(**kw):
                                      "sigmoid", "q2k_q6k_q80_mix", "t1_mixed_shared", "t1_k32", "t1_ties",
                                      "t1_softmax_all", "t1_sigmoid_e600", "ragged_tiles_q4k",
                                      "ragged_tiles_q2k_q6k_shared_q80", "ragged_tiles_q8_q4",
-                                     "many_tiles_spanning_lanes", "thin_hf_q80_q4k"])
+                                     "many_tiles_spanning_lanes", "thin_hf_q80_q4k", "t1_36_blocks_q2k",
+                                     "t1_42_blocks_shared_q6k"])
 def test_edge_layers(variant, fused, path):
     say("edge", variant, fused, path)
     kw = {}
@@ -360,6 +361,15 @@ def test_edge_layers(variant, fused, path):
         # Q8_0 gate/up and Q4_K down, shared expert likewise
         kw = dict(T=6, E=8, k=2, F=512, H=512, fmt_gate=syn.Q8_0, fmt_up=syn.Q8_0, fmt_down=syn.Q4_K,
                   shared=True, F_shared=256, sh_fmt_gate=syn.Q8_0, sh_fmt_up=syn.Q8_0, sh_fmt_down=syn.Q4_K)
+    elif variant == "t1_36_blocks_q2k":
+        # one token, 6 slots of F 1536: 36 q8_K(h) blocks, the most the
+        # one-token down kernel stages in LDS
+        kw = dict(T=1, E=20, k=6, F=1536, H=512, fmt_gate=syn.Q2_K, fmt_up=syn.Q2_K, fmt_down=syn.Q2_K)
+    elif variant == "t1_42_blocks_shared_q6k":
+        # 6 routed slots and a shared expert of the same shape: 42 blocks, one
+        # token on the general down kernel and the separate combine
+        kw = dict(T=1, E=16, k=6, F=1536, H=768, fmt_down=syn.Q6_K, shared=True, F_shared=1536,
+                  sh_fmt_gate=syn.Q4_K, sh_fmt_up=syn.Q4_K, sh_fmt_down=syn.Q6_K)
     cfg = _custom_cfg(**kw)
     layer = syn.gen_layer(cfg)
     if variant == "t1_ties":
