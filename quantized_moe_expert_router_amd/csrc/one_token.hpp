@@ -242,10 +242,18 @@ __device__ __forceinline__ void down1_body(const DownArgs& a, int bx) {
   // The down weight loads wait for the slot table the gate/up kernel left
   // (each slot's down matrix and weight): read it first, from the copy of
   // this workgroup's XCD, before the h loads are in flight.
+  __shared__ const uint8_t* sfb;            // first resident slot's down matrix, null if none
+  const uint8_t* my_wd = nullptr;
   if (threadIdx.x < n_slots) {
     const SlotRec* rec = a.slots + (int64_t)(bx & (kSlotCopies - 1)) * (a.k + 1) + threadIdx.x;
-    swd[threadIdx.x] = (const uint8_t*)rec->wd;
+    my_wd = (const uint8_t*)rec->wd;
+    swd[threadIdx.x] = my_wd;
     swt[threadIdx.x] = rec->wt;
+  }
+  if (wave == 0) {                           // n_slots <= kMaxSlots <= 64: all in wave 0
+    const uint64_t res = __ballot(my_wd != nullptr);
+    const uint64_t first = __shfl((uint64_t)my_wd, res ? __builtin_ctzll(res) : 0);
+    if (lane == 0) sfb = res ? (const uint8_t*)first : nullptr;
   }
   // this wave's q8_K(h) blocks (wave, wave+4, ...): fp32 loads
   float4 hv[kQ8PerWave];
@@ -258,31 +266,44 @@ __device__ __forceinline__ void down1_body(const DownArgs& a, int bx) {
     }
   }
   __syncthreads();
+  const uint8_t* const fb = sfb;
+  if (fb == nullptr) {                       // no resident slot: every pair adds nothing
+    if (threadIdx.x < rows_wg) {
+      const int64_t rr = row_base + threadIdx.x;
+      if (rr < a.H) gst_f32(a.y + rr, a.accumulate ? (float)((double)gld_f32(a.y + rr) + 0.0) : 0.0f);
+    }
+    return;
+  }
 
   // weight loads of one round: SG slots of this wave, every wave step of the
-  // workgroup's rows (all in flight together)
+  // workgroup's rows (all in flight together).  Every load is issued (a slot
+  // past the list or not resident reads the first resident slot's rows, a
+  // row or chunk past the end the last one; their products are discarded),
+  // so the q8_K(h) work below waits for the h loads only, not for these.
   typename L::W w[ST][SG][CPL];
   bool okk[ST][SG][CPL];
   auto issue = [&](int s0) {
 #pragma unroll
     for (int st = 0; st < ST; ++st) {
       const int64_t row = row_base + (int64_t)st * rps + rig;
+      const int64_t rl = row < a.H ? row : a.H - 1;
 #pragma unroll
       for (int j = 0; j < SG; ++j) {
         const int s = s0 + 4 * j;
         const uint8_t* W = s < n_slots ? swd[s] : nullptr;
+        const uint8_t* Wl = W != nullptr ? W : fb;
 #pragma unroll
         for (int c = 0; c < CPL; ++c) {
-          const int ch = lir + lpr * c;
+          const int ch = lir + lpr * c, cl = ch < a.cpr ? ch : a.cpr - 1;
           okk[st][j][c] = W != nullptr && ch < a.cpr && row < a.H;
-          if (okk[st][j][c]) w[st][j][c] = L::load(W, a.H, nb, row, ch / L::CPS, ch % L::CPS);
+          w[st][j][c] = L::load(Wl, a.H, nb, rl, cl / L::CPS, cl % L::CPS);
         }
       }
     }
   };
   issue(wave);                               // first round in flight during the q8_K(h) work
 
-  // q8_K(h) into LDS (workgroup 0 also stores the q8_K(h) view)
+  // q8_K(h) into LDS
 #pragma unroll
   for (int j = 0; j < kQ8PerWave; ++j) {
     const int b = wave + 4 * j;
@@ -307,16 +328,24 @@ __device__ __forceinline__ void down1_body(const DownArgs& a, int bx) {
       *reinterpret_cast<uint32_t*>(o + 16 + 4 * lane) = qw;
       if ((lane & 3) == 0) *reinterpret_cast<int16_t*>(o + 272 + 2 * (lane >> 2)) = (int16_t)sum4;
       if (lane == 0) *reinterpret_cast<float*>(o) = dq;
-      uint8_t* view = s >= n_routed ? a.hq_sh : a.hq;
-      if (bx == 0 && view != nullptr && swd[s] != nullptr) {
-        uint8_t* gq = view + (s >= n_routed ? 0 : (int64_t)s) * a.hq_stride + bb * kQ8KBytes;
-        gst_u32(gq + 4 + 4 * lane, qw);
-        if ((lane & 3) == 0) gst_i16(gq + 260 + 2 * (lane >> 2), (int16_t)sum4);
-        if (lane == 0) gst_f32(gq, dq);
-      }
     }
   }
   __syncthreads();
+  // workgroup 0 stores the q8_K(h) view from LDS (here rather than in the
+  // loop above, whose waits would otherwise cover weight loads behind these
+  // stores)
+  if (bx == 0) {
+    for (int b = wave; b < nblk; b += 4) {
+      const int s = (int)(((uint32_t)b * inv_nb) >> 16), bb = b - s * (int)nb;
+      uint8_t* view = s >= n_routed ? a.hq_sh : a.hq;
+      if (view == nullptr || swd[s] == nullptr) continue;
+      const uint8_t* o = hq_lds + b * kLdsQ8;
+      uint8_t* gq = view + (s >= n_routed ? 0 : (int64_t)s) * a.hq_stride + bb * kQ8KBytes;
+      gst_u32(gq + 4 + 4 * lane, *reinterpret_cast<const uint32_t*>(o + 16 + 4 * lane));
+      if (lane < 16) gst_i16(gq + 260 + 2 * lane, *reinterpret_cast<const int16_t*>(o + 272 + 2 * lane));
+      if (lane == 0) gst_f32(gq, *reinterpret_cast<const float*>(o));
+    }
+  }
 
   for (int s0 = wave; s0 < n_slots; s0 += 4 * SG) {
     if (s0 != wave) issue(s0);
@@ -328,14 +357,17 @@ __device__ __forceinline__ void down1_body(const DownArgs& a, int bx) {
         double ay = 0.0;
 #pragma unroll
         for (int c = 0; c < CPL; ++c) {
-          if (!okk[st][j][c]) continue;
-          const int ch = lir + lpr * c;
+          // every lane computes (on the reloaded data where not okk) and
+          // keeps the product where okk: no branch to sink the loads into
+          const int ch = lir + lpr * c, cl = ch < a.cpr ? ch : a.cpr - 1;
+          const int sl = s < n_slots ? s : 0;
           int xw[L::XDW], bs[L::NBS];
           double dx;
-          load_x_chunk_lds<FMT>(hq_lds + (int64_t)s * nb * kLdsQ8, ch, xw, bs, dx);
+          load_x_chunk_lds<FMT>(hq_lds + (int64_t)sl * nb * kLdsQ8, cl, xw, bs, dx);
           int is[L::SPC];
           L::isums(w[st][j][c], xw, bs, is);
-          ay += L::term(w[st][j][c], ch % L::CPS, is, bs, dx);
+          const double t = L::term(w[st][j][c], cl % L::CPS, is, bs, dx);
+          ay += okk[st][j][c] ? t : 0.0;
         }
         const double yv = group_sum_dpp(ay, lpr);
         if (s < n_slots && lir == lpr - 1) yps[s][st * rps + rig] = swt[s] * yv;
