@@ -301,6 +301,29 @@ def test_accumulate_and_shared_scale():
     check_y(yt.cpu().numpy(), y0.astype(np.float64) + run.yv.astype(np.float64), "accumulate")
 
 
+@pytest.mark.parametrize("fused", [False, True], ids=["calls", "layer"])
+def test_one_token_nothing_resident(fused):
+    # one token whose selected experts are all absent (and no shared expert):
+    # every pair adds nothing, so y is zero, and with accumulate y is unchanged
+    cfg = _custom_cfg(T=1, E=12, k=4, F=256, H=512)
+    layer = syn.gen_layer(cfg)
+    say("one token, nothing resident", fused)
+    run = GpuRun(layer, present=[False] * cfg.E, fused=fused)
+    assert np.all(run.yv == 0.0)
+    r = oracle.expert_ffn(layer, run.ids, run.w, [0], present=[False] * cfg.E)
+    assert np.all(r.y == 0.0)
+    if fused:
+        return
+    desc = run.dl.ffn_desc(cfg.T, accumulate=1)
+    y0 = np.random.default_rng(9).standard_normal((cfg.T, cfg.H)).astype(np.float32)
+    yt = dev(y0)
+    ro = run.runner.route_out
+    moeq.moeq_expert_ffn(desc, run.runner.xq, ro.ids, ro.w, ro.offsets, ro.pairs, ro.active, None, yt,
+                         run.runner.ffn_ws)
+    torch.cuda.synchronize()
+    assert np.array_equal(yt.cpu().numpy(), y0)
+
+
 def _custom_cfg(**kw):
     base = dict(name="custom", seed=777, T=8, H=512, E=6, k=2, F=256, gating=syn.SOFTMAX_TOPK,
                 fmt_gate=syn.Q4_K, fmt_up=syn.Q4_K, fmt_down=syn.Q4_K)
