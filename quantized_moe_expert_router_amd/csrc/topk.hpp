@@ -18,17 +18,16 @@ __device__ __forceinline__ uint64_t topk_key(double v, int i) {
 __device__ __forceinline__ uint64_t as_u64(double d) { return __builtin_bit_cast(uint64_t, d); }
 __device__ __forceinline__ double as_f64(uint64_t u) { return __builtin_bit_cast(double, u); }
 
-// Wave-wide maximum of a 64-bit key (DPP steps as in wave_argmax); every
-// lane gets it.
-__device__ __forceinline__ uint64_t wave_max_key(uint64_t x) {
-  uint64_t o;
-  o = as_u64(dpp_all_d<kDppXor1>(as_f64(x)));    x = o > x ? o : x;
-  o = as_u64(dpp_all_d<kDppXor2>(as_f64(x)));    x = o > x ? o : x;
-  o = as_u64(dpp_all_d<kDppRowRor4>(as_f64(x))); x = o > x ? o : x;
-  o = as_u64(dpp_all_d<kDppRowRor8>(as_f64(x))); x = o > x ? o : x;
-  o = as_u64(dpp_d<kDppRowBcast15, 0xA>(as_f64(x), as_f64(x))); x = o > x ? o : x;
-  o = as_u64(dpp_d<kDppRowBcast31, 0xC>(as_f64(x), as_f64(x))); x = o > x ? o : x;
-  return as_u64(readlane_d(as_f64(x), 63));
+// Wave-wide maximum of a 32-bit unsigned value; every lane gets it.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t x) {
+  auto mx = [](uint32_t a, int b) { return a > (uint32_t)b ? a : (uint32_t)b; };
+  x = mx(x, dpp_all_i<kDppXor1>((int)x));
+  x = mx(x, dpp_all_i<kDppXor2>((int)x));
+  x = mx(x, dpp_all_i<kDppRowRor4>((int)x));
+  x = mx(x, dpp_all_i<kDppRowRor8>((int)x));
+  x = mx(x, dpp_i<kDppRowBcast15, 0xA>((int)x, (int)x));
+  x = mx(x, dpp_i<kDppRowBcast31, 0xC>((int)x, (int)x));
+  return (uint32_t)__builtin_amdgcn_readlane((int)x, 63);
 }
 
 // Selection on the fp32 keys: k + 1 rounds of a one-compare arg-max over the
@@ -52,22 +51,28 @@ __device__ __forceinline__ bool topk_fast(const double* v, const int* vi, int k,
       key[b - 1] = k1 > k0 ? k1 : k0;
       key[b] = k1 > k0 ? k0 : k1;
     }
-  // rounds: every lane offers its first unused key (0 once all are used)
+  // rounds: every lane offers the fp32 half of its first unused key (0 once
+  // all are used); the round's maximum is a 32-bit wave max, and the lowest
+  // lane holding it gives up its head and names the index.  Two heads with
+  // the same fp32 value cannot both be decided here: the other one wins the
+  // next round with the same value (or, in round k, is not a winner).
   int head = 0;
-  uint64_t cand = key[0];
+  uint32_t cf = (uint32_t)(key[0] >> 32), ci = (uint32_t)key[0];
   uint32_t prev_f = 0;
   bool clear = true;
   for (int s = 0; s <= k; ++s) {
-    const uint64_t best = wave_max_key(cand);
-    const uint32_t f = (uint32_t)(best >> 32);
+    const uint32_t f = wave_max_u32(cf);
     clear = clear && (s == 0 || f != prev_f);
     prev_f = f;
-    my_i = lane == s ? (int)~(uint32_t)best : my_i;
-    head += cand == best ? 1 : 0;
+    const int w = __builtin_ctzll(__ballot(cf == f));
+    const int idx = (int)~(uint32_t)__builtin_amdgcn_readlane((int)ci, w);
+    my_i = lane == s ? idx : my_i;
+    head += lane == w ? 1 : 0;
     uint64_t c = 0;
 #pragma unroll
     for (int j = NPER - 1; j >= 0; --j) c = head == j ? key[j] : c;
-    cand = c;
+    cf = (uint32_t)(c >> 32);
+    ci = (uint32_t)c;
   }
   // the winners' fp64 logits: element e sits in lane e % 64, slot e / 64
   const int src = my_i & (kWave - 1), slot = my_i >> 6;
