@@ -99,10 +99,18 @@ __device__ __forceinline__ void topk_wave_regs(const double* __restrict__ row, i
   const int lane = lane_id();
   double v[NPER];
   int vi[NPER];
+  // every load is issued (an element past E reloads element E - 1) before
+  // the first wait; then the elements past E become -inf
 #pragma unroll
   for (int i = 0; i < NPER; ++i) {
     const int64_t e = lane + (int64_t)kWave * i;
-    v[i] = e < E ? gld_f64(row + e) : -INFINITY;
+    v[i] = gld_f64(row + (e < E ? e : E - 1));
+  }
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int i = 0; i < NPER; ++i) {
+    const int64_t e = lane + (int64_t)kWave * i;
+    v[i] = e < E ? v[i] : -INFINITY;
     vi[i] = e < E ? (int)e : INT_MAX;
   }
   double my_v = 0.0;
