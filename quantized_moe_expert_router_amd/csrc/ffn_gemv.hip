@@ -308,6 +308,92 @@ __global__ __launch_bounds__(256) void k_down(DownArgs a) {
 
 }
 
+// One token, one chunk per lane: the down rows of one slot's row block, the
+// same work and results as k_down<FMT, 1, 1, UNR>, ordered for latency.  The
+// fp32 h chunk loads go out first, then the weight loads of up to kDownT1Steps
+// wave steps (all issued: a step or row past the end reloads the block's first
+// row, a chunk past the row the last chunk), so the q8_K(h) quantization waits
+// for h only and the weights of every step are in flight together; the dot
+// products then keep only the valid steps' results.
+constexpr int kDownT1Steps = 8;
+template <int FMT>
+__global__ __launch_bounds__(256) void k_down_t1(DownArgs a) {
+  using L = Fmt<FMT>;
+  constexpr int U = kDownT1Steps;
+  const Slot sl = decode_slot(blockIdx.y, a.mode, a.max_union, a.active, a.offsets, a.T, a.gemv_max);
+  if (!sl.valid) return;
+  // An expert is resident only if all three of its matrices are present.
+  const uint8_t* Wd = sl.shared ? a.sh_down : (const uint8_t*)a.down[sl.e];
+  if (!sl.shared && (a.gate[sl.e] == nullptr || a.up[sl.e] == nullptr)) Wd = nullptr;
+
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = lane_id();
+  const int lpr = a.lpr, rps = kWave / lpr, rig = lane / lpr, lir = lane % lpr;
+  const int64_t nb = a.F / 256;
+  const int64_t row0 = (int64_t)blockIdx.x * a.rb + (int64_t)wave * a.steps * rps + rig;
+  const int64_t row_dup = row0 < a.H ? row0 : a.H - 1;
+  const bool dbg_writer = blockIdx.x == 0 && wave == 0 && rig == 0;
+
+  int tok;
+  int64_t prow;
+  slot_token(sl, 0, a.pairs, a.T, a.k, tok, prow);
+  const double wt = sl.shared ? (a.shared_scale ? (double)a.shared_scale[tok] : 1.0) : (double)a.topk_w[prow];
+  if (Wd == nullptr) {                        // not resident: its pair adds nothing
+    for (int st = 0; st < a.steps; ++st) {
+      const int64_t row = row0 + (int64_t)st * rps;
+      if (lir == lpr - 1 && row < a.H) a.yp[prow * a.H + row] = (float)(wt * 0.0);
+    }
+    return;
+  }
+  const int ch = lir, cl = ch < a.cpr ? ch : a.cpr - 1;
+  const bool have = ch < a.cpr;
+  // the lane's fp32 h chunk (elements in the order of its activation dwords)
+  float hv[L::WPC];
+  {
+    const float* hb = a.hbuf + prow * a.hstride + (cl / L::CPS) * 256;
+#pragma unroll
+    for (int q = 0; q < L::WPC / 4; ++q) {
+      const float4 f = gld_f4(hb + L::xoff(cl % L::CPS, q));
+      hv[4 * q] = f.x; hv[4 * q + 1] = f.y; hv[4 * q + 2] = f.z; hv[4 * q + 3] = f.w;
+    }
+  }
+  typename L::W wd[U];
+  auto load_steps = [&](int st0) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t row = row0 + (int64_t)(st0 + u) * rps;
+      const int64_t rl = (st0 + u) < a.steps && row < a.H ? row : row_dup;
+      wd[u] = L::load(Wd, a.H, nb, rl, cl / L::CPS, cl % L::CPS);
+    }
+  };
+  int xw[L::XDW], bs[L::NBS];
+  double dx;
+  auto dot_steps = [&](int st0) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t row = row0 + (int64_t)(st0 + u) * rps;
+      const bool ok = have && (st0 + u) < a.steps && row < a.H;
+      int is[L::SPC];
+      L::isums(wd[u], xw, bs, is);
+      const double t = L::term(wd[u], cl % L::CPS, is, bs, dx);
+      const double yv = group_sum_dpp(ok ? t : 0.0, lpr);
+      if (lir == lpr - 1 && (st0 + u) < a.steps && row < a.H) a.yp[prow * a.H + row] = (float)(wt * yv);
+    }
+  };
+  load_steps(0);
+  __builtin_amdgcn_sched_barrier(0);
+  {
+    uint8_t* dbg = nullptr;
+    uint8_t* hq_base = sl.shared ? a.hq_sh : a.hq;
+    if (dbg_writer && hq_base != nullptr) dbg = hq_base + (sl.shared ? (int64_t)tok : prow) * a.hq_stride;
+    quant_h_regs<FMT, 256 / L::WPC>(hv, have, ch, xw, bs, dx, dbg);
+  }
+  dot_steps(0);
+  for (int st0 = U; st0 < a.steps; st0 += U) {   // more than U wave steps (one row per wave step)
+    load_steps(st0);
+    dot_steps(st0);
+  }
+}
+
 // y[t] (=|+=) fl32(sum_slot yp[t*k+slot] + yp[T*k+t]) summed in fp64, slots in
 // rank order, then the shared expert: the weighted per-pair outputs were
 // staged in fp32 by the down kernels (rounding each of the k+1 terms to fp32
@@ -366,8 +452,9 @@ __global__ __launch_bounds__(256) void k_down_rows1(DownArgs a) {
 
 #define MOEQ_GU(F, TT, C) \
   hipLaunchKernelGGL((k_gateup<F, TT, C, (TT == 1 ? 4 : 2)>), grid, dim3(256), 0, s, a)
-#define MOEQ_DN(F, TT, C) \
-  hipLaunchKernelGGL((k_down<F, TT, C, 2>), grid, dim3(256), 0, s, a)
+#define MOEQ_DN(F, TT, C)                                                   \
+  if (TT == 1 && C == 1) hipLaunchKernelGGL((k_down_t1<F>), grid, dim3(256), 0, s, a); \
+  else hipLaunchKernelGGL((k_down<F, TT, C, 2>), grid, dim3(256), 0, s, a)
 
 #define MOEQ_SWITCH_CPL(M, F, TT)            \
   switch (cpl) {                             \
