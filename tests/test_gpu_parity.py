@@ -324,6 +324,21 @@ def test_one_token_nothing_resident(fused):
     assert np.array_equal(yt.cpu().numpy(), y0)
 
 
+@pytest.mark.parametrize("fused", [False, True], ids=["calls", "layer"])
+def test_one_token_general_down_partial_residency(fused):
+    # one token, 7 slots of F 1536 (42 q8_K(h) blocks: the general one-token
+    # down kernel, 16 row steps per wave in two batches), half the experts
+    # absent: the absent slots' rows are zero, the rest match the oracle
+    cfg = _custom_cfg(T=1, E=16, k=7, F=1536, H=768, fmt_down=syn.Q6_K)
+    layer = syn.gen_layer(cfg)
+    say("one token, general down kernel, partial residency", fused)
+    lo = [e < cfg.E // 2 for e in range(cfg.E)]
+    run = GpuRun(layer, present=lo, fused=fused)
+    r = oracle.expert_ffn(layer, run.ids, run.w, [0], present=lo)
+    check_y(run.yv, r.y, "partial residency")
+    assert any(lo[e] for e in run.ids[0]) and not all(lo[e] for e in run.ids[0])
+
+
 def _custom_cfg(**kw):
     base = dict(name="custom", seed=777, T=8, H=512, E=6, k=2, F=256, gating=syn.SOFTMAX_TOPK,
                 fmt_gate=syn.Q4_K, fmt_up=syn.Q4_K, fmt_down=syn.Q4_K)
