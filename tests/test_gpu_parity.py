@@ -339,6 +339,49 @@ def test_one_token_general_down_partial_residency(fused):
     assert any(lo[e] for e in run.ids[0]) and not all(lo[e] for e in run.ids[0])
 
 
+@pytest.mark.parametrize("variant", ["t1_other_shared", "t300_mfma_shared"])
+def test_graph_replays_match_eager(variant):
+    # the whole layer captured in a HIP graph and replayed several times, with
+    # eager library work between the replays: every replay equals the eager
+    # result bit for bit (same kernels, same order of every sum)
+    if variant == "t1_other_shared":
+        cfg = _custom_cfg(T=1, E=12, k=4, F=256, H=512, shared=True, F_shared=512, sh_fmt_gate=syn.Q8_0,
+                          sh_fmt_up=syn.Q8_0, sh_fmt_down=syn.Q6_K)
+    else:
+        cfg = _custom_cfg(T=300, E=10, k=3, F=512, H=512, shared=True, F_shared=512, sh_fmt_gate=syn.Q4_K,
+                          sh_fmt_up=syn.Q4_K, sh_fmt_down=syn.Q4_K)
+    layer = syn.gen_layer(cfg)
+    say("graph replays", variant)
+    dl = moeq.DeviceLayer(layer)
+    fdesc = dl.ffn_desc(cfg.T)
+    rdesc = moeq.RouteDesc(cfg.T, cfg.H, cfg.E, cfg.k, cfg.gating, 1.0)
+    x = dev(layer.x.astype(np.float32))
+    out = moeq.RouteOut(cfg.T, cfg.E, cfg.k, x.device)
+    ws = torch.empty(moeq.moeq_moe_layer_workspace(rdesc, fdesc), dtype=torch.uint8, device=x.device)
+    y = torch.empty((cfg.T, cfg.H), dtype=torch.float32, device=x.device)
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        moeq.moeq_moe_layer(rdesc, fdesc, x, dl.w_router, dl.bias, out, None, y, ws, stream)
+    torch.cuda.synchronize()
+    ref = y.cpu().numpy().copy()
+    r = oracle.expert_ffn(layer, out.ids.cpu().numpy(), out.w.cpu().numpy(), [0])
+    check_y(ref[:1], r.y, "eager")
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(stream):
+        with torch.cuda.graph(g, stream=stream):
+            moeq.moeq_moe_layer(rdesc, fdesc, x, dl.w_router, dl.bias, out, None, y, ws, stream)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        y.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(y.cpu().numpy(), ref), (variant, rep)
+        with torch.cuda.stream(stream):                    # eager work between the replays
+            moeq.moeq_moe_layer(rdesc, fdesc, x, dl.w_router, dl.bias, out, None, y, ws, stream)
+        torch.cuda.synchronize()
+        assert np.array_equal(y.cpu().numpy(), ref), (variant, rep, "eager")
+
+
 def _custom_cfg(**kw):
     base = dict(name="custom", seed=777, T=8, H=512, E=6, k=2, F=256, gating=syn.SOFTMAX_TOPK,
                 fmt_gate=syn.Q4_K, fmt_up=syn.Q4_K, fmt_down=syn.Q4_K)
