@@ -14,6 +14,14 @@
  *     on `stream`; nothing synchronises, allocates device memory, or reads the
  *     environment.  Calls that take a workspace use only that workspace for
  *     scratch; concurrent calls must not share one.
+ *   - moeq_expert_ffn and moeq_moe_layer may run a shared expert that is not
+ *     a slot of the routed launches (another shape or format, or the MFMA
+ *     path, up to 256 tokens) on a stream of the library's own for the
+ *     current device: default priority, created with two events on the
+ *     first such call made outside graph capture, kept until the process
+ *     ends.  It is ordered after `stream` and joined back into `stream` by
+ *     events before the call's last launch, so every effect of the call is
+ *     still ordered on `stream`, in graph capture too.
  *   - The caller owns every buffer; nothing is retained after the call.
  *   - Return value: MOEQ_OK (0) or a negative moeq_status.  All argument
  *     checks (sizes, NULLs, alignment, workspace size, supported formats)

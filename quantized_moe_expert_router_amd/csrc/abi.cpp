@@ -2,6 +2,7 @@
 // kernel dispatch.  Every check runs before anything is enqueued.
 #include <algorithm>
 #include <climits>
+#include <mutex>
 
 #include "../../include/moeq.h"
 #include "formats.hpp"
@@ -210,6 +211,61 @@ struct InlineRoute {
 
 int nper_of(int64_t E) { return E <= 256 ? 4 : E <= 512 ? 8 : E <= 1024 ? 16 : 64; }
 
+// Side stream of the current device for a shared expert launched apart from
+// the routed slots (default priority; created on first use, never while the
+// caller's stream is capturing a graph, where creating one is not allowed --
+// such a call then stays on one stream).  The events order it after the
+// caller's stream (fork) and the caller's stream after it (join); a lock
+// keeps each record-and-wait pair together when several host threads call.
+struct SideStream {
+  hipStream_t st = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+  bool ready = false;
+};
+constexpr int kSideDevices = 64;
+constexpr int64_t kSideMaxT = 256;
+std::mutex g_side_mu;
+SideStream g_side[kSideDevices];
+
+SideStream* side_of_current_device(hipStream_t s) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kSideDevices) return nullptr;
+  SideStream& sd = g_side[dev];
+  if (sd.ready) return &sd;
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(s, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone) return nullptr;
+  if (hipStreamCreateWithFlags(&sd.st, hipStreamNonBlocking) != hipSuccess) return nullptr;
+  if (hipEventCreateWithFlags(&sd.fork, hipEventDisableTiming) != hipSuccess ||
+      hipEventCreateWithFlags(&sd.join, hipEventDisableTiming) != hipSuccess) {
+    if (sd.fork != nullptr) hipEventDestroy(sd.fork);
+    hipStreamDestroy(sd.st);
+    sd = SideStream{};
+    return nullptr;
+  }
+  sd.ready = true;
+  return &sd;
+}
+
+// The stream the shared expert's launches go to: the side stream, ordered
+// after everything enqueued on s so far, or s itself.
+hipStream_t fork_side(hipStream_t s) {
+  std::lock_guard<std::mutex> lk(g_side_mu);
+  SideStream* sd = side_of_current_device(s);
+  if (sd == nullptr) return s;
+  if (hipEventRecord(sd->fork, s) != hipSuccess || hipStreamWaitEvent(sd->st, sd->fork, 0) != hipSuccess) return s;
+  return sd->st;
+}
+
+// s waits for everything enqueued on the side stream so far.
+int join_side(hipStream_t s) {
+  std::lock_guard<std::mutex> lk(g_side_mu);
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kSideDevices || !g_side[dev].ready) return -1;
+  SideStream& sd = g_side[dev];
+  if (hipEventRecord(sd.join, sd.st) != hipSuccess || hipStreamWaitEvent(s, sd.join, 0) != hipSuccess) return -1;
+  return 0;
+}
+
 // Enqueue the expert FFN (everything after the routing) on `s`.
 int ffn_enqueue(const moeq_ffn_desc* d, const void* x_q8K, const int32_t* topk_ids, const float* topk_w,
                 const int32_t* expert_offsets, const int32_t* pairs, const int32_t* active,
@@ -248,7 +304,7 @@ int ffn_enqueue(const moeq_ffn_desc* d, const void* x_q8K, const int32_t* topk_i
     }
     return a;
   };
-  auto gateup = [&](int mode, int fmt, int64_t F, int n_slots) -> int {
+  auto gateup = [&](int mode, int fmt, int64_t F, int n_slots, hipStream_t st) -> int {
     LaneGeo g;
     lane_geo(fmt, d->H, &g);
     GateUpArgs a = gu_args(mode, F, g);
@@ -256,9 +312,9 @@ int ffn_enqueue(const moeq_ffn_desc* d, const void* x_q8K, const int32_t* topk_i
     dim3 grid((unsigned)((F + rows_per_wg - 1) / rows_per_wg), (unsigned)n_slots);
     if (one) {
       const int nper = (ir != nullptr && mode != kModeShared) ? nper_of(d->E) : 0;
-      return launch_gateup1(fmt, nper, g.cpl, grid, a, s);
+      return launch_gateup1(fmt, nper, g.cpl, grid, a, st);
     }
-    return launch_gateup(fmt, tt, g.cpl, grid, a, s);
+    return launch_gateup(fmt, tt, g.cpl, grid, a, st);
   };
   auto down_args = [&](int mode, int fmt, int64_t F, LaneGeo* g) {
     lane_geo(fmt, F, g);
@@ -280,11 +336,11 @@ int ffn_enqueue(const moeq_ffn_desc* d, const void* x_q8K, const int32_t* topk_i
     a.y = y; a.accumulate = d->accumulate;
     return a;
   };
-  auto down = [&](int mode, int fmt, int64_t F, int n_slots) -> int {
+  auto down = [&](int mode, int fmt, int64_t F, int n_slots, hipStream_t st) -> int {
     LaneGeo g;
     DownArgs a = down_args(mode, fmt, F, &g);
     dim3 grid((unsigned)(d->H / kRowBlock), (unsigned)n_slots);
-    return launch_down(fmt, tt, g.cpl, grid, a, s);
+    return launch_down(fmt, tt, g.cpl, grid, a, st);
   };
   // int8 MFMA tiles: mode 0 = gate/up (+ q8_K(h)), mode 1 = down
   int4* tiles = (int4*)(wsb + L.off_tiles);
@@ -301,7 +357,7 @@ int ffn_enqueue(const moeq_ffn_desc* d, const void* x_q8K, const int32_t* topk_i
     return fg != FQ6K && fd != FQ6K && d->H / 256 <= kHfMaxBlocks && Fx / 256 <= kHfMaxBlocks &&
            tiles * (Fx / 256) < kHfMaxWorkgroups;
   };
-  auto mfma_launch = [&](int mode, bool shared_exp, bool thin) -> int {
+  auto mfma_launch = [&](int mode, bool shared_exp, bool thin, hipStream_t st) -> int {
     const bool hf = thin && hf_ok(shared_exp);
     MfmaArgs a{};
     a.shared = shared_exp ? 1 : 0;
@@ -341,7 +397,7 @@ int ffn_enqueue(const moeq_ffn_desc* d, const void* x_q8K, const int32_t* topk_i
     const int64_t nrb = gy;
     a.rb = std::max<int64_t>(1, std::min<int64_t>(nrb, (int64_t)gx * nrb / 2048));
     gy = (unsigned)((nrb + a.rb - 1) / a.rb);
-    return launch_mfma(fmt, mode, thin, hf, dim3(gx, gy), a, s);
+    return launch_mfma(fmt, mode, thin, hf, dim3(gx, gy), a, st);
   };
 
   if (mfma && !planned) {
@@ -349,22 +405,40 @@ int ffn_enqueue(const moeq_ffn_desc* d, const void* x_q8K, const int32_t* topk_i
                                s)))
       return rc;
   }
+  // A shared expert that is not a slot of the routed launches (another shape
+  // or format, or the MFMA path) runs its gate/up and down on the side
+  // stream, forked after everything above and joined before the combine: it
+  // reads only x, its own h rows and its own staged output rows.  Up to
+  // kSideMaxT tokens the routed launches leave most of the chip idle; past
+  // it they fill it and the shared expert stays on s.
+  const bool sh_apart = sh && (mfma || !same_shape) && d->T <= kSideMaxT;
+  const hipStream_t ss = sh_apart ? fork_side(s) : s;
   // gate/up: h[pair, f] = fl32(silu(g) u)  (dot-product path: fp32 h rows;
   // MFMA path: q8_K(h) rows straight away)
   const int n_routed_slots = one ? d->k : max_union;
+  // the shared expert goes first when it has a stream of its own (it starts
+  // at once), after the routed launches otherwise
+  auto shared_gateup = [&]() -> int {
+    if (!sh || (gemv && same_shape)) return 0;
+    return mfma ? mfma_launch(0, true, d->T <= kThinT, ss) : gateup(kModeShared, d->sh_fmt_gate, d->F_shared, 1, ss);
+  };
+  auto shared_down = [&]() -> int {
+    if (!sh || (gemv && same_shape)) return 0;
+    return mfma ? mfma_launch(1, true, d->T <= kThinT, ss) : down(kModeShared, d->sh_fmt_down, d->F_shared, 1, ss);
+  };
+  if (ss != s && (rc = shared_gateup())) return rc;
   if (gemv) {
     if (same_shape) {
-      if ((rc = gateup(kModeBoth, d->fmt_gate, d->F, n_routed_slots + 1))) return rc;
+      if ((rc = gateup(kModeBoth, d->fmt_gate, d->F, n_routed_slots + 1, s))) return rc;
     } else {
-      if ((rc = gateup(kModeRouted, d->fmt_gate, d->F, n_routed_slots))) return rc;
-      if (sh && (rc = gateup(kModeShared, d->sh_fmt_gate, d->F_shared, 1))) return rc;
+      if ((rc = gateup(kModeRouted, d->fmt_gate, d->F, n_routed_slots, s))) return rc;
     }
   }
   if (mfma) {
-    if (d->T > kThinT && (rc = mfma_launch(0, false, false))) return rc;
-    if ((rc = mfma_launch(0, false, true))) return rc;
-    if (sh && (rc = mfma_launch(0, true, d->T <= kThinT))) return rc;
+    if (d->T > kThinT && (rc = mfma_launch(0, false, false, s))) return rc;
+    if ((rc = mfma_launch(0, false, true, s))) return rc;
   }
+  if (ss == s && (rc = shared_gateup())) return rc;
   // down and the weighted combine
   if (one && (!sh || same_shape) && (d->k + (sh ? 1 : 0)) * (d->F / 256) <= kLdsQ8Blocks) {
     LaneGeo g;
@@ -374,19 +448,20 @@ int ffn_enqueue(const moeq_ffn_desc* d, const void* x_q8K, const int32_t* topk_i
     dim3 grid((unsigned)((d->H + rows_wg - 1) / rows_wg));
     return launch_down_rows1(d->fmt_down, g.cpl, grid, a, s);
   }
+  if (ss != s && (rc = shared_down())) return rc;
   if (gemv) {
     if (same_shape) {
-      if ((rc = down(kModeBoth, d->fmt_down, d->F, max_union + 1))) return rc;
+      if ((rc = down(kModeBoth, d->fmt_down, d->F, max_union + 1, s))) return rc;
     } else {
-      if ((rc = down(kModeRouted, d->fmt_down, d->F, max_union))) return rc;
-      if (sh && (rc = down(kModeShared, d->sh_fmt_down, d->F_shared, 1))) return rc;
+      if ((rc = down(kModeRouted, d->fmt_down, d->F, max_union, s))) return rc;
     }
   }
   if (mfma) {
-    if (d->T > kThinT && (rc = mfma_launch(1, false, false))) return rc;
-    if ((rc = mfma_launch(1, false, true))) return rc;
-    if (sh && (rc = mfma_launch(1, true, d->T <= kThinT))) return rc;
+    if (d->T > kThinT && (rc = mfma_launch(1, false, false, s))) return rc;
+    if ((rc = mfma_launch(1, false, true, s))) return rc;
   }
+  if (ss == s && (rc = shared_down())) return rc;
+  if (ss != s && (rc = join_side(s))) return rc;
   return launch_combine((const float*)(wsb + L.off_yp), d->T, d->H, d->k, sh ? 1 : 0, y, d->accumulate, s);
 }
 
