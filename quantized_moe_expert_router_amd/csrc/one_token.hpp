@@ -58,11 +58,9 @@ __device__ __forceinline__ void gateup1_body(const GateUpArgs& a, int bx, int sl
   } else {
     int e;
     if constexpr (NPER > 0) {
-      // One wave routes for the workgroup (the top-k from the logits, the
-      // same in every workgroup); the others wait for its result in LDS.
-      __shared__ uint64_t r_ptr[3];
-      __shared__ double r_wt;
-      if (wave == 0) {
+      // Every wave routes for itself (the same register top-k from the
+      // logits in every wave and workgroup), so no wave waits for another.
+      {
         uint64_t pg[NPER <= 8 ? NPER : 1], pu[NPER <= 8 ? NPER : 1], pd[NPER <= 8 ? NPER : 1];
         if constexpr (NPER <= 8) {
           // candidates' matrix pointers load with the logits; the winner's
@@ -78,7 +76,7 @@ __device__ __forceinline__ void gateup1_body(const GateUpArgs& a, int bx, int sl
         int my_i;
         float my_w;
         topk_wave_regs<NPER>(a.logits, a.E, a.k, a.gating, a.scale, my_i, my_w);
-        if (bx == 0 && slot == 0) write_routing_t1(a, my_i, my_w);
+        if (bx == 0 && slot == 0 && wave == 0) write_routing_t1(a, my_i, my_w);
         e = __builtin_amdgcn_readlane(my_i, slot);
         const float wsel = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, my_w), slot));
         uint64_t g0, u0, d0;
@@ -100,16 +98,11 @@ __device__ __forceinline__ void gateup1_body(const GateUpArgs& a, int bx, int sl
         } else {
           g0 = (uint64_t)a.gate[e]; u0 = (uint64_t)a.up[e]; d0 = (uint64_t)a.down[e];
         }
-        if (lane == 0) {
-          r_ptr[0] = g0; r_ptr[1] = u0; r_ptr[2] = d0;
-          r_wt = (double)wsel;
-        }
+        Wg = (const uint8_t*)g0;
+        Wu = (const uint8_t*)u0;
+        Wd = (const void*)d0;
+        wt = (double)wsel;
       }
-      __syncthreads();
-      Wg = (const uint8_t*)r_ptr[0];
-      Wu = (const uint8_t*)r_ptr[1];
-      Wd = (const void*)r_ptr[2];
-      wt = r_wt;
     } else {
       e = a.topk_ids[slot];
       wt = (double)a.topk_w[slot];
