@@ -339,12 +339,17 @@ def test_one_token_general_down_partial_residency(fused):
     assert any(lo[e] for e in run.ids[0]) and not all(lo[e] for e in run.ids[0])
 
 
-@pytest.mark.parametrize("variant", ["t1_other_shared", "t300_mfma_shared"])
+@pytest.mark.parametrize("variant", ["t1_same_shared", "t1_other_shared", "t300_mfma_shared"])
 def test_graph_replays_match_eager(variant):
     # the whole layer captured in a HIP graph and replayed several times, with
     # eager library work between the replays: every replay equals the eager
     # result bit for bit (same kernels, same order of every sum)
-    if variant == "t1_other_shared":
+    if variant == "t1_same_shared":
+        # the decode kernels: routing inline in gate/up, the shared expert as
+        # one more slot, down with the weighted sum
+        cfg = _custom_cfg(T=1, E=40, k=8, F=512, H=1024, fmt_down=syn.Q6_K, shared=True, F_shared=512,
+                          sh_fmt_gate=syn.Q4_K, sh_fmt_up=syn.Q4_K, sh_fmt_down=syn.Q6_K)
+    elif variant == "t1_other_shared":
         cfg = _custom_cfg(T=1, E=12, k=4, F=256, H=512, shared=True, F_shared=512, sh_fmt_gate=syn.Q8_0,
                           sh_fmt_up=syn.Q8_0, sh_fmt_down=syn.Q6_K)
     else:
