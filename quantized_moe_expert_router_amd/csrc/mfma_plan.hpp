@@ -20,23 +20,12 @@ __device__ __forceinline__ int wave_incl_scan(int v) {
   return v;
 }
 
-// Routed experts whose row count exceeds `thr`: experts with at most
-// kThinRows rows get one 8-row tile, the others 32-row tiles; a tile is
-// (expert, first row, rows, list offset), experts in union order (absent
-// experts too: their down tiles write zero rows).  Wave 0 of the workgroup
-// builds both lists with no barrier (active / offsets may have been written
-// by this workgroup before a barrier).  Lane l takes union entries
-// l*per .. l*per+per-1 to count tiles and write the 8-row ones; the 32-row
-// tiles are then written by all lanes, each a contiguous share of the list
-// (a hot expert's hundreds of tiles would otherwise fall to one lane): its
-// first tile's expert by binary search over the experts' first-tile indices
-// (ebase, LDS scratch of at least union size + 1 entries), then a walk.
-constexpr int kPlanMaxE = 4096;
-__device__ void mfma_plan_block(const int32_t* __restrict__ active, const int32_t* __restrict__ offsets,
-                                const MfmaPlan& p, int* ebase) {
-  if (threadIdx.x >= kWave) return;
+// The counting half of mfma_plan_block, by wave 0: tile counts, the 8-row
+// tiles, each expert's first 32-row tile index in ebase (ebase[na] = total),
+// and the two counts.
+__device__ __forceinline__ void plan_count(const int32_t* __restrict__ active, const int32_t* __restrict__ offsets,
+                                           const MfmaPlan& p, int* ebase, int na) {
   const int lane = lane_id();
-  const int na = active[0];
   const int per = (na + kWave - 1) / kWave;
   const int s0 = lane * per;
   int local = 0, tlocal = 0;
@@ -71,13 +60,31 @@ __device__ void mfma_plan_block(const int32_t* __restrict__ active, const int32_
       }
     }
   }
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-  const int tot_all = __builtin_amdgcn_readlane(inc, kWave - 1);
+}
+
+// Routed experts whose row count exceeds `thr`: experts with at most
+// kThinRows rows get one 8-row tile, the others 32-row tiles; a tile is
+// (expert, first row, rows, list offset), experts in union order (absent
+// experts too: their down tiles write zero rows).  Every thread of the
+// workgroup calls it (active / offsets may have been written by this
+// workgroup before a barrier).  Wave 0 counts: lane l takes union entries
+// l*per .. l*per+per-1 to count tiles and write the 8-row ones, and records
+// each expert's first-tile index (ebase, LDS scratch of at least union size
+// + 1 entries).  After a barrier the 32-row tiles are written by every thread
+// of the workgroup, each a contiguous share of the list (a hot expert's
+// hundreds of tiles would otherwise fall to one lane): its first tile's
+// expert by binary search over ebase, then a walk.
+constexpr int kPlanMaxE = 4096;
+__device__ void mfma_plan_block(const int32_t* __restrict__ active, const int32_t* __restrict__ offsets,
+                                const MfmaPlan& p, int* ebase) {
+  const int na = active[0];
+  if (threadIdx.x < kWave) plan_count(active, offsets, p, ebase, na);
+  __syncthreads();
+  const int tot_all = ebase[na];
   const int total = tot_all < p.max_tiles ? tot_all : p.max_tiles;
-  const int B = (total + kWave - 1) / kWave;
-  const int t_begin = lane * B, t_end = t_begin + B < total ? t_begin + B : total;
+  const int nthr = (int)blockDim.x;
+  const int B = (total + nthr - 1) / nthr;
+  const int t_begin = (int)threadIdx.x * B, t_end = t_begin + B < total ? t_begin + B : total;
   if (t_begin < t_end) {
     int lo = 0, hi = na;            // the last expert s with ebase[s] <= t_begin (its range is not empty)
     while (lo < hi) {
@@ -95,5 +102,4 @@ __device__ void mfma_plan_block(const int32_t* __restrict__ active, const int32_
     }
   }
 }
-
 }  // namespace moeq
