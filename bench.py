@@ -14,7 +14,8 @@ graphs as in the Strata summary's execution paragraph, and one graph for the
 whole cycle, the way a decode step runs the stack) and replayed.
 
 Output: one JSON line (metric, value = MoE-layer tokens/s, roofline of the
-expert FFN, cpu_baseline = the CPU oracle on the host cores).
+expert FFN, cpu_baseline = the CPU oracle on the host cores), with the 4-token
+verify, 16-token chunk and 8192-token prefill layers measured beside it.
 """
 import argparse
 import json
@@ -39,6 +40,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-verify", action="store_true", help="skip the verify (4-token) measurement")
     ap.add_argument("--no-prefill", action="store_true", help="skip the 8192-token prefill measurement")
+    ap.add_argument("--no-chunk", action="store_true", help="skip the 16-token chunk measurement")
     ap.add_argument("--prefill-steps", type=int, default=20)
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="first run a device copy of this many MiB (counter calibration for rocprofv3 --pmc)")
@@ -357,6 +359,10 @@ def main():
     verify = None
     if not args.no_verify:
         verify = secondary("verify", max(4, L // 4), max(8, args.steps // 4), max(4, args.warmup // 4), dev)
+    # ---- secondary: 16-token chunk (sigmoid top-6, Q2_K/Q4_K experts, Q8_0 shared expert)
+    chunk = None
+    if not args.no_chunk:
+        chunk = secondary("chunk16", max(4, L // 4), max(8, args.steps // 4), max(4, args.warmup // 4), dev)
     # ---- secondary: 8192-token prefill chunk (int8 MFMA grouped GEMM)
     prefill = None
     if not args.no_prefill:
@@ -389,6 +395,7 @@ def main():
                      "bytes_per_launch": ffn_bytes, "avg_launch_us": ffn_us},
         "cpu_baseline": cpu,
         "verify_b4": verify,
+        "chunk16_b16": chunk,
         "prefill_8192": prefill,
         "setup_s": setup_s,
     }
