@@ -285,76 +285,93 @@ void orc_dequant_q8K_row(const uint8_t* q8, int64_t cols, double* out)
 
 /* ---------------------------------------------------------------- router */
 
-static const double* g_sort_key;
+/* One expert's sort key: the order is (logit desc, index asc). */
+typedef struct {
+    double l;
+    int32_t e;
+} rank_item;
+
 static int cmp_rank(const void* a, const void* b)
 {
-    int ia = *(const int*)a, ib = *(const int*)b;
-    double la = g_sort_key[ia], lb = g_sort_key[ib];
-    if (la > lb) return -1;
-    if (la < lb) return 1;
-    return ia < ib ? -1 : (ia > ib);
+    const rank_item* x = (const rank_item*)a;
+    const rank_item* y = (const rank_item*)b;
+    if (x->l > y->l) return -1;
+    if (x->l < y->l) return 1;
+    return x->e < y->e ? -1 : (x->e > y->e);
+}
+
+/* Router of one token: logits, ids and weights as orc_route describes. */
+static int route_one(int64_t H, int64_t E, int k, int gating, double scale, const float* x,
+                     const float* Wr, const float* bias, double* logits, int32_t* ids, float* w,
+                     rank_item* order, double* l)
+{
+    int64_t e, i;
+    int s;
+    for (e = 0; e < E; e++) {
+        double acc = 0.0;
+        for (i = 0; i < H; i++)
+            acc += (double)Wr[e * H + i] * (double)x[i];
+        if (bias)
+            acc += (double)bias[e];
+        l[e] = acc;
+        order[e].l = acc;
+        order[e].e = (int32_t)e;
+        if (logits)
+            logits[e] = acc;
+    }
+    qsort(order, (size_t)E, sizeof(rank_item), cmp_rank);
+    for (s = 0; s < k; s++)
+        ids[s] = order[s].e;
+    if (gating == G_SOFTMAX_TOPK) {
+        double mx = order[0].l, z = 0.0;
+        for (s = 0; s < k; s++)
+            z += exp(order[s].l - mx);
+        for (s = 0; s < k; s++)
+            w[s] = (float)(exp(order[s].l - mx) / z * scale);
+    } else if (gating == G_SOFTMAX_ALL) {
+        double mx = order[0].l, z = 0.0;
+        for (e = 0; e < E; e++)
+            z += exp(l[e] - mx);
+        for (s = 0; s < k; s++)
+            w[s] = (float)(exp(order[s].l - mx) / z * scale);
+    } else if (gating == G_SIGMOID_TOPK) {
+        double z = 0.0;
+        for (s = 0; s < k; s++)
+            z += 1.0 / (1.0 + exp(-order[s].l));
+        for (s = 0; s < k; s++)
+            w[s] = (float)(1.0 / (1.0 + exp(-order[s].l)) / z * scale);
+    } else {
+        return -1;
+    }
+    return 0;
 }
 
 /*
  * Router for T tokens: logits (fp64, sequential sum, bias added last), the
  * top-k ids in rank order and fp32 gate weights (computed in fp64, times
- * `scale`, rounded once).  logits may be NULL.
+ * `scale`, rounded once).  logits may be NULL.  Tokens are independent and
+ * run in parallel (OpenMP); each keeps its own sort keys.
  */
 int orc_route(int64_t T, int64_t H, int64_t E, int k, int gating, double scale,
               const float* x, const float* Wr, const float* bias,
               double* logits, int32_t* ids, float* w)
 {
     int64_t t;
+    int bad = 0;
     if (k < 1 || k > E)
         return -1;
-    double* l = (double*)malloc(sizeof(double) * E);
-    int* order = (int*)malloc(sizeof(int) * E);
+    if (gating != G_SOFTMAX_TOPK && gating != G_SOFTMAX_ALL && gating != G_SIGMOID_TOPK)
+        return -1;
+#pragma omp parallel for schedule(static) reduction(| : bad)
     for (t = 0; t < T; t++) {
-        int64_t e, i;
-        int s;
-        for (e = 0; e < E; e++) {
-            double acc = 0.0;
-            for (i = 0; i < H; i++)
-                acc += (double)Wr[e * H + i] * (double)x[t * H + i];
-            if (bias)
-                acc += (double)bias[e];
-            l[e] = acc;
-            if (logits)
-                logits[t * E + e] = acc;
-        }
-        for (e = 0; e < E; e++)
-            order[e] = (int)e;
-        g_sort_key = l;
-        qsort(order, (size_t)E, sizeof(int), cmp_rank);
-        for (s = 0; s < k; s++)
-            ids[t * k + s] = order[s];
-        if (gating == G_SOFTMAX_TOPK) {
-            double mx = l[order[0]], z = 0.0;
-            for (s = 0; s < k; s++)
-                z += exp(l[order[s]] - mx);
-            for (s = 0; s < k; s++)
-                w[t * k + s] = (float)(exp(l[order[s]] - mx) / z * scale);
-        } else if (gating == G_SOFTMAX_ALL) {
-            double mx = l[order[0]], z = 0.0;
-            for (e = 0; e < E; e++)
-                z += exp(l[e] - mx);
-            for (s = 0; s < k; s++)
-                w[t * k + s] = (float)(exp(l[order[s]] - mx) / z * scale);
-        } else if (gating == G_SIGMOID_TOPK) {
-            double z = 0.0;
-            for (s = 0; s < k; s++)
-                z += 1.0 / (1.0 + exp(-l[order[s]]));
-            for (s = 0; s < k; s++)
-                w[t * k + s] = (float)(1.0 / (1.0 + exp(-l[order[s]])) / z * scale);
-        } else {
-            free(l);
-            free(order);
-            return -1;
-        }
+        rank_item* order = (rank_item*)malloc(sizeof(rank_item) * E);
+        double* l = (double*)malloc(sizeof(double) * E);
+        bad |= route_one(H, E, k, gating, scale, x + t * H, Wr, bias, logits ? logits + t * E : NULL,
+                         ids + t * k, w + t * k, order, l);
+        free(order);
+        free(l);
     }
-    free(l);
-    free(order);
-    return 0;
+    return bad ? -1 : 0;
 }
 
 /*
@@ -474,61 +491,80 @@ double orc_dot_intform(int fmt, const uint8_t* wrow, int64_t cols, const uint8_t
 
 /* ------------------------------------------------------------------- FFN */
 
-/* out[r] = sum_c W[r,c] * v[c], fp64, sequential; W dequantised row by row. */
-static void matvec(int fmt, const uint8_t* W, int64_t rows, int64_t cols, const double* v,
-                   double* out, double* rowbuf)
+/* sum_c a[c] * b[c], fp64, sequential in c. */
+static double dot_seq(const double* a, const double* b, int64_t n)
 {
-    int64_t r, c;
-    int64_t rb = cols / orc_block_weights(fmt) * orc_block_bytes(fmt);
-    for (r = 0; r < rows; r++) {
-        double acc = 0.0;
-        orc_dequant_row(fmt, W + r * rb, cols, rowbuf);
-        for (c = 0; c < cols; c++)
-            acc += rowbuf[c] * v[c];
-        out[r] = acc;
-    }
+    double acc = 0.0;
+    int64_t c;
+    for (c = 0; c < n; c++)
+        acc += a[c] * b[c];
+    return acc;
 }
 
+/* out[r] = sum_c W[r,c] * v[c], fp64, sequential; W dequantised row by row. */
 int orc_matvec(int fmt, const uint8_t* W, int64_t rows, int64_t cols, const double* v, double* out)
 {
-    double* rowbuf = (double*)malloc(sizeof(double) * cols);
-    if (cols % orc_block_weights(fmt)) {
-        free(rowbuf);
+    int64_t r, rb = cols / orc_block_weights(fmt) * orc_block_bytes(fmt);
+    double* rowbuf;
+    if (!orc_block_weights(fmt) || cols % orc_block_weights(fmt))
         return -1;
+    rowbuf = (double*)malloc(sizeof(double) * cols);
+    for (r = 0; r < rows; r++) {
+        orc_dequant_row(fmt, W + r * rb, cols, rowbuf);
+        out[r] = dot_seq(rowbuf, v, cols);
     }
-    matvec(fmt, W, rows, cols, v, out, rowbuf);
     free(rowbuf);
     return 0;
 }
 
+/* The dequantised [rows, cols] matrix in fp64 (rows in parallel). */
+static double* dequant_matrix(int fmt, const uint8_t* W, int64_t rows, int64_t cols)
+{
+    int64_t r, rb = cols / orc_block_weights(fmt) * orc_block_bytes(fmt);
+    double* out = (double*)malloc(sizeof(double) * rows * cols);
+#pragma omp parallel for schedule(static)
+    for (r = 0; r < rows; r++)
+        orc_dequant_row(fmt, W + r * rb, cols, out + r * cols);
+    return out;
+}
+
 static double silu64(double z) { return z / (1.0 + exp(-z)); }
+
+/* A dequantised expert: gate/up [F, H], down [H, F]. */
+typedef struct {
+    int64_t F;
+    double *g, *u, *d;
+} expert64;
 
 /*
  * One expert on one token.  xhat: dequantised q8_K(x) [H].  Writes
  * hq (q8_K(h), F/256 blocks), yp [H], and optionally g, u, h [F].
+ *   g = Wg xhat, u = Wu xhat (fp64), h = fl32(silu(g) u), hhat = q8_K(h)^,
+ *   yp = Wd hhat (fp64)
  */
-static void expert_one(int64_t H, int64_t F, int fg, int fu, int fd,
-                       const uint8_t* Wg, const uint8_t* Wu, const uint8_t* Wd,
-                       const double* xhat, uint8_t* hq, double* yp,
+static void expert_one(int64_t H, const expert64* X, const double* xhat, uint8_t* hq, double* yp,
                        double* g_out, double* u_out, float* h_out)
 {
+    const int64_t F = X->F;
     double* g = (double*)malloc(sizeof(double) * F);
     double* u = (double*)malloc(sizeof(double) * F);
     float* h = (float*)malloc(sizeof(float) * F);
     double* hhat = (double*)malloc(sizeof(double) * F);
-    double* rowbuf = (double*)malloc(sizeof(double) * (H > F ? H : F));
-    int64_t f;
-    matvec(fg, Wg, F, H, xhat, g, rowbuf);
-    matvec(fu, Wu, F, H, xhat, u, rowbuf);
+    int64_t f, r;
+    for (f = 0; f < F; f++)
+        g[f] = dot_seq(X->g + f * H, xhat, H);
+    for (f = 0; f < F; f++)
+        u[f] = dot_seq(X->u + f * H, xhat, H);
     for (f = 0; f < F; f++)
         h[f] = (float)(silu64(g[f]) * u[f]);
     orc_quantize_q8K_row(h, F, hq);
     orc_dequant_q8K_row(hq, F, hhat);
-    matvec(fd, Wd, H, F, hhat, yp, rowbuf);
+    for (r = 0; r < H; r++)
+        yp[r] = dot_seq(X->d + r * F, hhat, F);
     if (g_out) memcpy(g_out, g, sizeof(double) * F);
     if (u_out) memcpy(u_out, u, sizeof(double) * F);
     if (h_out) memcpy(h_out, h, sizeof(float) * F);
-    free(g); free(u); free(h); free(hhat); free(rowbuf);
+    free(g); free(u); free(h); free(hhat);
 }
 
 /*
@@ -541,6 +577,11 @@ static void expert_one(int64_t H, int64_t F, int fg, int fu, int fd,
  * gate/up/down: host arrays [E] of AoS matrices; NULL = not resident (its
  * pairs contribute nothing).  sh_*: shared expert or NULL.  shared_scale:
  * [T] or NULL (= 1).  ids / w: the router's output [T, k].
+ *
+ * Each pair (token, slot) is computed on its own (expert_one); the experts are
+ * visited one at a time, each dequantised once for all of its pairs, and then
+ * every token sums its slots in slot order, the shared expert last:
+ *   y[t] = fl32( sum_s w[t,s] * yp[t,s] + shared_scale[t] * yp[t,shared] )
  */
 int orc_expert_ffn(int64_t T, int64_t H, int64_t F, int64_t E, int k,
                    int fg, int fu, int fd,
@@ -551,59 +592,109 @@ int orc_expert_ffn(int64_t T, int64_t H, int64_t F, int64_t E, int k,
                    const int64_t* sel, int64_t n_sel,
                    float* y, uint8_t* hq, double* g_diag, double* u_diag, float* h_diag)
 {
-    int64_t n;
-    int64_t Fmax = (sh_gate && Fs > F) ? Fs : F;
-    int64_t hq_stride = Fmax / 256 * 292;
-    (void)E;
+    const int64_t Fmax = (sh_gate && Fs > F) ? Fs : F;
+    const int64_t hq_stride = Fmax / 256 * 292;
+    const int64_t n_slots = n_sel * (k + 1);
+    int64_t n, e, i;
+    double *xhat, *yp;
+    char* done;
+    int64_t *count, *start, *fill, *list;
     if (H % 256 || F % 256 || (sh_gate && Fs % 256))
         return -1;
-    for (n = 0; n < n_sel; n++)
+    for (n = 0; n < n_sel; n++) {
+        int s;
         if (sel[n] < 0 || sel[n] >= T)
             return -1;
-#pragma omp parallel for schedule(dynamic, 1)
+        for (s = 0; s < k; s++)
+            if (ids[sel[n] * k + s] < 0 || ids[sel[n] * k + s] >= E)
+                return -1;
+    }
+    if (hq)
+        memset(hq, 0, (size_t)(n_slots * hq_stride));
+
+    /* q8_K(x) of each selected token, dequantised */
+    xhat = (double*)malloc(sizeof(double) * n_sel * H);
+#pragma omp parallel for schedule(static)
     for (n = 0; n < n_sel; n++) {
-        int64_t t = sel[n], i;
-        int s;
         uint8_t* xq = (uint8_t*)malloc((size_t)(H / 256 * 292));
-        double* xhat = (double*)malloc(sizeof(double) * H);
+        orc_quantize_q8K_row(x + sel[n] * H, H, xq);
+        orc_dequant_q8K_row(xq, H, xhat + n * H);
+        free(xq);
+    }
+
+    /* the (token, slot) pairs of each expert; index E is the shared expert */
+    count = (int64_t*)calloc((size_t)(E + 2), sizeof(int64_t));
+    start = (int64_t*)calloc((size_t)(E + 2), sizeof(int64_t));
+    fill = (int64_t*)calloc((size_t)(E + 2), sizeof(int64_t));
+    list = (int64_t*)malloc(sizeof(int64_t) * (n_slots > 0 ? n_slots : 1));
+    for (n = 0; n < n_sel; n++) {
+        int s;
+        for (s = 0; s < k; s++)
+            count[ids[sel[n] * k + s]]++;
+        count[E]++;
+    }
+    for (e = 0; e <= E; e++)
+        start[e + 1] = start[e] + count[e];
+    for (n = 0; n < n_sel; n++) {
+        int s;
+        for (s = 0; s < k; s++) {
+            e = ids[sel[n] * k + s];
+            list[start[e] + fill[e]++] = n * (k + 1) + s;
+        }
+        list[start[E] + fill[E]++] = n * (k + 1) + k;
+    }
+
+    yp = (double*)calloc((size_t)(n_slots * H), sizeof(double));
+    done = (char*)calloc((size_t)(n_slots > 0 ? n_slots : 1), 1);
+    for (e = 0; e <= E; e++) {
+        expert64 X;
+        int64_t j;
+        int fmt_g, fmt_u, fmt_d;
+        const uint8_t *Wg, *Wu, *Wd;
+        if (count[e] == 0)
+            continue;
+        if (e < E) {
+            Wg = gate[e]; Wu = up[e]; Wd = down[e];
+            X.F = F; fmt_g = fg; fmt_u = fu; fmt_d = fd;
+        } else {
+            Wg = sh_gate; Wu = sh_up; Wd = sh_down;
+            X.F = Fs; fmt_g = sfg; fmt_u = sfu; fmt_d = sfd;
+        }
+        if (!Wg || !Wu || !Wd)
+            continue;                       /* not resident: its pairs add nothing */
+        X.g = dequant_matrix(fmt_g, Wg, X.F, H);
+        X.u = dequant_matrix(fmt_u, Wu, X.F, H);
+        X.d = dequant_matrix(fmt_d, Wd, H, X.F);
+#pragma omp parallel for schedule(dynamic, 1)
+        for (j = start[e]; j < start[e + 1]; j++) {
+            const int64_t p = list[j], pn = p / (k + 1);
+            expert_one(H, &X, xhat + pn * H, hq ? hq + p * hq_stride : NULL, yp + p * H,
+                       g_diag ? g_diag + p * Fmax : NULL, u_diag ? u_diag + p * Fmax : NULL,
+                       h_diag ? h_diag + p * Fmax : NULL);
+            done[p] = 1;
+        }
+        free(X.g); free(X.u); free(X.d);
+    }
+
+    /* the weighted sum of each token, slot order, shared expert last */
+#pragma omp parallel for schedule(static)
+    for (n = 0; n < n_sel; n++) {
+        const int64_t t = sel[n];
         double* acc = (double*)calloc((size_t)H, sizeof(double));
-        double* yp = (double*)malloc(sizeof(double) * H);
-        orc_quantize_q8K_row(x + t * H, H, xq);
-        orc_dequant_q8K_row(xq, H, xhat);
+        int s;
         for (s = 0; s <= k; s++) {
-            int64_t slot_base = (n * (k + 1) + s);
-            uint8_t* hqs = hq ? hq + slot_base * hq_stride : NULL;
-            uint8_t* tmp_hq = (uint8_t*)calloc((size_t)hq_stride, 1);
-            double* gd = g_diag ? g_diag + slot_base * Fmax : NULL;
-            double* ud = u_diag ? u_diag + slot_base * Fmax : NULL;
-            float* hd = h_diag ? h_diag + slot_base * Fmax : NULL;
+            const int64_t p = n * (k + 1) + s;
             double wt;
-            if (s < k) {
-                int e = ids[t * k + s];
-                if (!gate[e] || !up[e] || !down[e]) {
-                    if (hqs) memset(hqs, 0, (size_t)hq_stride);
-                    free(tmp_hq);
-                    continue;
-                }
-                expert_one(H, F, fg, fu, fd, gate[e], up[e], down[e], xhat, tmp_hq, yp, gd, ud, hd);
-                wt = (double)w[t * k + s];
-            } else {
-                if (!sh_gate || !sh_up || !sh_down) {
-                    if (hqs) memset(hqs, 0, (size_t)hq_stride);
-                    free(tmp_hq);
-                    continue;
-                }
-                expert_one(H, Fs, sfg, sfu, sfd, sh_gate, sh_up, sh_down, xhat, tmp_hq, yp, gd, ud, hd);
-                wt = shared_scale ? (double)shared_scale[t] : 1.0;
-            }
+            if (!done[p])
+                continue;
+            wt = s < k ? (double)w[t * k + s] : (shared_scale ? (double)shared_scale[t] : 1.0);
             for (i = 0; i < H; i++)
-                acc[i] += wt * yp[i];
-            if (hqs) memcpy(hqs, tmp_hq, (size_t)hq_stride);
-            free(tmp_hq);
+                acc[i] += wt * yp[p * H + i];
         }
         for (i = 0; i < H; i++)
             y[n * H + i] = (float)acc[i];
-        free(xq); free(xhat); free(acc); free(yp);
+        free(acc);
     }
+    free(xhat); free(yp); free(done); free(count); free(start); free(fill); free(list);
     return 0;
 }
