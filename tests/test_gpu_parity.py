@@ -13,6 +13,7 @@ import pytest
 import torch
 
 import oracle
+from guards import GuardedAlloc
 from quantized_moe_expert_router_amd import moeq
 from quantized_moe_expert_router_amd import synthetic as syn
 
@@ -47,22 +48,37 @@ def check_w(w_gpu, w_orc):
 
 class GpuRun:
     """One layer on the GPU: separate route + FFN calls, or (fused=True) the
-    single whole-layer call."""
+    single whole-layer call.  Every output and workspace the library sees is
+    a view inside a guarded allocation; the guards are checked after the call.
+    aux: give the FFN an auxiliary stream for a shared expert that runs apart
+    from the routed launches (else everything runs on one stream)."""
 
-    def __init__(self, layer, path=moeq.PATH_AUTO, present=None, shared_scale=None, x=None, fused=False):
+    def __init__(self, layer, path=moeq.PATH_AUTO, present=None, shared_scale=None, x=None, fused=False, aux=True):
         cfg = layer.cfg
         self.dl = moeq.DeviceLayer(layer, present=present)
         xs = layer.x if x is None else x
         self.x = dev(xs)
         T = xs.shape[0]
         ss = None if shared_scale is None else dev(shared_scale)
-        self.runner = moeq.LayerRunner(self.dl, T, path=path, shared_scale=ss)
+        rn = moeq.LayerRunner(self.dl, T, path=path, shared_scale=ss, aux=moeq.AuxStream() if aux else None)
+        ga = GuardedAlloc()
+        r = rn.route_out
+        r.logits = ga.empty((T, cfg.E), torch.float64, "logits")
+        r.ids = ga.empty((T, cfg.k), torch.int32, "topk_ids")
+        r.w = ga.empty((T, cfg.k), torch.float32, "topk_w")
+        r.offsets = ga.empty(cfg.E + 1, torch.int32, "offsets")
+        r.pairs = ga.empty(max(1, T * cfg.k), torch.int32, "pairs")
+        r.active = ga.empty(1 + min(cfg.E, T * cfg.k), torch.int32, "active")
+        rn.route_ws = ga.empty(rn.route_ws.numel(), torch.uint8, "route_ws")
+        rn.xq = ga.empty(tuple(rn.xq.shape), torch.uint8, "x_q8K")
+        rn.ffn_ws = ga.empty(rn.ffn_ws.numel(), torch.uint8, "ffn_ws")
+        rn.y = ga.empty((T, cfg.H), torch.float32, "y")
         if fused:
-            self.y = self.runner.layer(self.x)
-        else:
-            self.y = self.runner.forward(self.x)
-        torch.cuda.synchronize()
-        r = self.runner.route_out
+            rn.rdesc = moeq.RouteDesc(T, cfg.H, cfg.E, cfg.k, cfg.gating, 1.0)
+            rn.layer_ws = ga.empty(moeq.moeq_moe_layer_workspace(rn.rdesc, rn.desc), torch.uint8, "layer_ws")
+        self.runner, self.guards = rn, ga
+        self.y = rn.layer(self.x) if fused else rn.forward(self.x)
+        ga.check("layer" if fused else "calls")
         self.ids = r.ids.cpu().numpy()
         self.w = r.w.cpu().numpy()
         self.logits = r.logits.cpu().numpy()
@@ -70,8 +86,8 @@ class GpuRun:
         self.pairs = r.pairs.cpu().numpy()[:T * cfg.k]
         act = r.active.cpu().numpy()
         self.active = act[:1 + act[0]]
-        self.xq = None if fused else self.runner.xq.cpu().numpy()
-        hr, hs = self.runner.layer_h_view() if fused else moeq.moeq_ffn_h_view(self.runner.desc, self.runner.ffn_ws)
+        self.xq = None if fused else rn.xq.cpu().numpy()
+        hr, hs = rn.layer_h_view() if fused else moeq.moeq_ffn_h_view(rn.desc, rn.ffn_ws)
         self.hq_r = None if hr is None else hr.cpu().numpy()
         self.hq_s = None if hs is None else hs.cpu().numpy()
         self.yv = self.y.cpu().numpy()
@@ -86,12 +102,37 @@ def layer_of(name):
     return _layers[name]
 
 
-def sample_tokens(T, n, seed=0):
-    if T <= n:
-        return list(range(T))
-    rng = np.random.default_rng(seed)
-    s = set(rng.choice(T, n - 2, replace=False).tolist()) | {0, T - 1}
-    return sorted(s)
+_oracle_full = {}
+
+
+def oracle_of(name):
+    """The oracle's whole result for every token of a named layer (computed
+    once per session): logits, ids, gate weights, lists, q8_K(x), y and the
+    q8_K(h) bytes of every pair."""
+    if name not in _oracle_full:
+        layer = layer_of(name)
+        cfg = layer.cfg
+        say("oracle", name, "T=%d" % cfg.T)
+        lg, ids, w = oracle.route(layer.x, layer.w_router, layer.bias, cfg.k, cfg.gating)
+        off, pairs, active = oracle.lists(ids, cfg.E)
+        r = oracle.expert_ffn(layer, ids, w, range(cfg.T))
+        _oracle_full[name] = dict(logits=lg, ids=ids, w=w, offsets=off, pairs=pairs, active=active,
+                                  xq=oracle.quantize_q8K(layer.x), y=r.y, hq=r.hq)
+    return _oracle_full[name]
+
+
+def check_hq(run, hq_orc, cfg, what):
+    """q8_K(h) bytes of every (token, slot) pair and of every shared row."""
+    T, k = run.yv.shape[0], cfg.k
+    nbF = cfg.F // 256 * 292
+    got = run.hq_r[:, :nbF]
+    want = hq_orc[:, :k, :nbF].reshape(T * k, nbF)
+    if not np.array_equal(got, want):
+        bad = np.nonzero((got != want).any(axis=1))[0]
+        raise AssertionError((what, "q8_K(h) differs for %d pairs, first %s" % (len(bad), bad[:8].tolist())))
+    if cfg.shared:
+        nbs = cfg.F_shared // 256 * 292
+        assert np.array_equal(run.hq_s[:, :nbs], hq_orc[:, k, :nbs]), (what, "shared q8_K(h)")
 
 
 # ---------------------------------------------------------------- q8_K(x)
@@ -197,27 +238,24 @@ def test_route_many_tokens_ragged(T, E, H, with_bias):
 @pytest.mark.parametrize("fused", [False, True], ids=["calls", "layer"])
 @pytest.mark.parametrize("name", syn.CONFIG_ORDER)
 def test_layer_parity(name, fused, path):
+    """Every token of each layer shape against the oracle: logits, ids in rank
+    order, gate weights and lists; q8_K(x) and every pair's q8_K(h) bytes; y
+    over the whole [T, H]."""
     layer = layer_of(name)
     cfg = layer.cfg
+    o = oracle_of(name)
     say("layer", name, "fused" if fused else "calls", path, cfg)
     run = GpuRun(layer, path=PATHS[path], fused=fused)
-    sel = sample_tokens(cfg.T, 24)
-    ids, w = check_route(run, layer, sel)
-    full_ids = run.ids.copy()
-    full_ids[sel] = ids
-    full_w = run.w.copy()
-    full_w[sel] = w
+    assert np.array_equal(run.ids, o["ids"]), name
+    check_w(run.w, o["w"])
+    assert np.allclose(run.logits, o["logits"], rtol=0, atol=1e-12)
+    assert np.array_equal(run.offsets, o["offsets"])
+    assert np.array_equal(run.pairs, o["pairs"])
+    assert np.array_equal(run.active, o["active"])
     if run.xq is not None:
-        assert np.array_equal(run.xq[sel], oracle.quantize_q8K(layer.x[sel]))
-    r = oracle.expert_ffn(layer, full_ids, full_w, sel)
-    check_y(run.yv[sel], r.y, name)
-    nbF = cfg.F // 256 * 292
-    for n, t in enumerate(sel):
-        for s in range(cfg.k):
-            assert np.array_equal(run.hq_r[t * cfg.k + s, :nbF], r.hq[n, s, :nbF]), (name, t, s)
-        if cfg.shared:
-            nbs = cfg.F_shared // 256 * 292
-            assert np.array_equal(run.hq_s[t, :nbs], r.hq[n, cfg.k, :nbs]), (name, t, "shared")
+        assert np.array_equal(run.xq, o["xq"])
+    check_hq(run, o["hq"], cfg, name)
+    check_y(run.yv, o["y"], name)
 
 
 @pytest.mark.parametrize("name", ["tiny", "decode", "verify"])
@@ -241,9 +279,9 @@ def test_auto_path_choice_and_determinism(name):
 
 @pytest.mark.parametrize("name", ["chunk16", "prefill"])
 def test_mfma_and_gemv_agree_on_every_pair(name):
-    """At full size the oracle checks sampled tokens; here the two device paths
-    (independent integer schemes) must give the same q8_K(h) bytes for every
-    pair and agree on y everywhere, and the MFMA path must be deterministic."""
+    """Beside the oracle comparison: the two device paths (independent integer
+    schemes) give the same q8_K(h) bytes for every pair and agree on y
+    everywhere, and the MFMA path is deterministic."""
     layer = layer_of(name)
     cfg = layer.cfg
     say("mfma vs gemv every pair", name)
@@ -275,9 +313,8 @@ def test_null_partition_sums_to_full(name, path):
     b = GpuRun(hi_layer, present=[not v for v in lo], path=PATHS[path])
     s = a.yv.astype(np.float64) + b.yv.astype(np.float64)
     check_y(s, full.yv, "partition")
-    sel = sample_tokens(cfg.T, 6)
-    ro = oracle.expert_ffn(layer, full.ids, full.w, sel, present=lo)
-    check_y(a.yv[sel], ro.y, "half")
+    ro = oracle.expert_ffn(layer, full.ids, full.w, range(cfg.T), present=lo)
+    check_y(a.yv, ro.y, "half")
 
 
 def test_accumulate_and_shared_scale():
@@ -287,9 +324,8 @@ def test_accumulate_and_shared_scale():
     rng = np.random.default_rng(5)
     ss = rng.uniform(0.25, 2.0, cfg.T).astype(np.float32)
     run = GpuRun(layer, shared_scale=ss)
-    sel = [0, 7, 15]
-    r = oracle.expert_ffn(layer, run.ids, run.w, sel, shared_scale=ss)
-    check_y(run.yv[sel], r.y, "shared_scale")
+    r = oracle.expert_ffn(layer, run.ids, run.w, range(cfg.T), shared_scale=ss)
+    check_y(run.yv, r.y, "shared_scale")
     # accumulate: y += result
     desc = run.dl.ffn_desc(cfg.T, accumulate=1)
     y0 = rng.standard_normal((cfg.T, cfg.H)).astype(np.float32)
@@ -358,7 +394,7 @@ def test_graph_replays_match_eager(variant):
     layer = syn.gen_layer(cfg)
     say("graph replays", variant)
     dl = moeq.DeviceLayer(layer)
-    fdesc = dl.ffn_desc(cfg.T)
+    fdesc = dl.ffn_desc(cfg.T, aux=moeq.AuxStream())
     rdesc = moeq.RouteDesc(cfg.T, cfg.H, cfg.E, cfg.k, cfg.gating, 1.0)
     x = dev(layer.x.astype(np.float32))
     out = moeq.RouteOut(cfg.T, cfg.E, cfg.k, x.device)
@@ -385,6 +421,24 @@ def test_graph_replays_match_eager(variant):
             moeq.moeq_moe_layer(rdesc, fdesc, x, dl.w_router, dl.bias, out, None, y, ws, stream)
         torch.cuda.synchronize()
         assert np.array_equal(y.cpu().numpy(), ref), (variant, rep, "eager")
+
+
+@pytest.mark.parametrize("variant", ["t1_other_shared", "chunk16_mfma"])
+def test_aux_stream_and_single_stream_agree(variant):
+    # a shared expert apart from the routed launches: on the caller's
+    # auxiliary stream or on the call's own stream, the same kernels run in
+    # the same order per stream, so y and q8_K(h) are bit-identical
+    if variant == "t1_other_shared":
+        layer = syn.gen_layer(_custom_cfg(T=1, E=12, k=4, F=256, H=512, shared=True, F_shared=512,
+                                          sh_fmt_gate=syn.Q8_0, sh_fmt_up=syn.Q8_0, sh_fmt_down=syn.Q6_K))
+    else:
+        layer = layer_of("chunk16")
+    say("aux vs single stream", variant)
+    for fused in (False, True):
+        a = GpuRun(layer, fused=fused, aux=True)
+        b = GpuRun(layer, fused=fused, aux=False)
+        assert np.array_equal(a.yv, b.yv), (variant, fused)
+        assert np.array_equal(a.hq_r, b.hq_r) and np.array_equal(a.hq_s, b.hq_s), (variant, fused)
 
 
 def _custom_cfg(**kw):
