@@ -11,18 +11,25 @@
  * Conventions for every entry point:
  *   - Pointers are device memory unless marked (host).  `stream` is a
  *     hipStream_t (NULL = the null stream).  Work is enqueued asynchronously
- *     on `stream`; nothing synchronises, allocates device memory, or reads the
- *     environment.  Calls that take a workspace use only that workspace for
- *     scratch; concurrent calls must not share one.
- *   - moeq_expert_ffn and moeq_moe_layer may run a shared expert that is not
- *     a slot of the routed launches (another shape or format, or the MFMA
- *     path, up to 256 tokens) on a stream of the library's own for the
- *     current device: default priority, created with two events on the
- *     first such call made outside graph capture, kept until the process
- *     ends.  It is ordered after `stream` and joined back into `stream` by
- *     events before the call's last launch, so every effect of the call is
- *     still ordered on `stream`, in graph capture too.
- *   - The caller owns every buffer; nothing is retained after the call.
+ *     on `stream`; nothing synchronises, allocates device memory, creates a
+ *     stream or event, or reads the environment or any state of its own:
+ *     the library holds no mutable global state (the MoE kernels never
+ *     consult global state and every launch gets explicit per-expert
+ *     pointers: Pulsar README, 'How the streaming works'; session state is
+ *     preallocated by the caller: Strata summary, execution paragraph).
+ *     Calls that take a workspace use only that workspace for scratch;
+ *     concurrent calls must not share one.
+ *   - moeq_expert_ffn and moeq_moe_layer run a shared expert that is not a
+ *     slot of the routed launches (another shape or format, or the MFMA
+ *     path, up to 256 tokens) on the caller's auxiliary stream when the FFN
+ *     descriptor names one (aux_stream with two events, all caller-owned),
+ *     otherwise on `stream`.  The auxiliary stream is ordered after `stream`
+ *     and joined back into `stream` by the two events before the call's last
+ *     launch, so every effect of the call is still ordered on `stream`, in
+ *     graph capture too.  Calls that may run concurrently need their own
+ *     auxiliary stream and events.
+ *   - The caller owns every buffer, stream and event; nothing is retained
+ *     after the call.
  *   - Return value: MOEQ_OK (0) or a negative moeq_status.  All argument
  *     checks (sizes, NULLs, alignment, workspace size, supported formats)
  *     happen on the host before anything is enqueued; a failed check leaves
@@ -140,13 +147,26 @@ int moeq_route(const moeq_route_desc* d, const float* x, const float* w_router, 
                double* logits, int32_t* topk_ids, float* topk_w, int32_t* expert_offsets,
                int32_t* pairs, int32_t* active, void* x_q8K, void* ws, size_t ws_bytes, void* stream);
 
-/* Bytes of one packed [rows, cols] matrix of format fmt (0 if unsupported). */
+/*
+ * Bytes of one packed [rows, cols] matrix of format fmt (0 if unsupported or
+ * cols % 256 != 0).  Host arithmetic only.  The packed form is what an
+ * expert slab becomes once it is resident on the device (expert slabs are
+ * uploaded to the GPU as they arrive and the kernels get plain device
+ * pointers: Pulsar README, 'How the streaming works'; the K-quant expert
+ * formats: Pulsar README, 'Get a model').
+ */
 size_t moeq_packed_bytes(int32_t fmt, int64_t rows, int64_t cols);
 
 /*
  * One-time repack of n_mats exchange-format matrices [rows, cols] (stored
- * back to back in `aos`, any alignment) into the kernels' packed form
- * (n_mats * moeq_packed_bytes, back to back, 256-byte aligned).  cols % 256 == 0.
+ * back to back in `aos`, device memory, any alignment) into the kernels'
+ * packed form (n_mats * moeq_packed_bytes, back to back, 256-byte aligned,
+ * caller-owned).  cols % 256 == 0.  Done once when an expert slab becomes
+ * resident (Pulsar README, 'How the streaming works').  The packed bytes
+ * hold the same codes and scales, reordered so that each super-block loads
+ * as contiguous runs.  n_mats == 0 is a no-op; errors: MOEQ_E_UNSUPPORTED
+ * for an unknown format, MOEQ_E_INVALID for bad sizes, NULLs or packed not
+ * 256-byte aligned.
  */
 int moeq_pack_experts(int32_t fmt, const void* aos, int64_t n_mats, int64_t rows, int64_t cols,
                       void* packed, void* stream);
@@ -175,6 +195,13 @@ typedef struct {
     const void* sh_down;
     int32_t path;        /* moeq_path */
     int32_t accumulate;  /* 0: y = result, 1: y += result */
+    /* Optional caller-owned auxiliary stream (hipStream_t) and two events
+     * (hipEvent_t, made with hipEventDisableTiming) on the same device, for
+     * a shared expert that runs apart from the routed launches: all three
+     * NULL (everything on `stream`) or all three set (else MOEQ_E_INVALID). */
+    void* aux_stream;
+    void* aux_fork;
+    void* aux_join;
 } moeq_ffn_desc;
 
 /* Workspace bytes moeq_expert_ffn needs for this descriptor (host). */
@@ -220,17 +247,24 @@ int moeq_moe_layer(const moeq_route_desc* r, const moeq_ffn_desc* f, const float
                    size_t ws_bytes, void* stream);
 
 /*
- * Where a finished moeq_expert_ffn call left q8_K(h) inside `ws` (host
- * arithmetic only).  *hq_routed: [T*k] rows of F/256 blocks, row p = pair
- * t*k+slot (rows of absent experts are unspecified); *hq_shared: [T] rows of
- * F_shared/256 blocks, or NULL without a shared expert.
+ * Test hook (GPU kernel selftests against CPU references and a bit-exact
+ * gate: Pulsar README, 'Tests'): where a finished moeq_expert_ffn call left
+ * q8_K(h) inside `ws` (host arithmetic only, nothing is enqueued).
+ * *hq_routed: [T*k] rows of F/256 blocks, row p = pair t*k+slot (rows of
+ * absent experts are unspecified); *hq_shared: [T] rows of F_shared/256
+ * blocks, or NULL without a shared expert.  The pointers point into the
+ * caller's ws.  Errors: as the descriptor checks of moeq_expert_ffn, plus
+ * MOEQ_E_WORKSPACE when ws_bytes is below moeq_expert_ffn_workspace.
  */
 int moeq_ffn_h_view(const moeq_ffn_desc* d, void* ws, size_t ws_bytes, void** hq_routed,
                     void** hq_shared);
 
 /*
- * Test hook: the exact int32 sub-block dots of a packed matrix with q8_K rows,
- * computed by the same device dot routines the FFN uses.
+ * Test hook (GPU kernel selftests against CPU references: Pulsar README,
+ * 'Tests'; exact integer dots of K-quant weights with q8_K activations:
+ * Pulsar README, 'Fidelity notes'): the exact int32 sub-block dots of a
+ * packed matrix with q8_K rows, computed by the same device dot routines the
+ * dot-product (GEMV) kernels use.  Enqueued on `stream`; n_x == 0 is a no-op.
  *   packed_w [rows, cols] packed fmt; x_q8K [n_x, cols/256 blocks]
  *   out int32 [n_x, rows, cols/sub]: sum over sub-block j of code * q_x, where
  *   sub = 32 (Q4_K, Q8_0) or 16 (Q2_K, Q6_K) and code = q (Q4_K, Q2_K),

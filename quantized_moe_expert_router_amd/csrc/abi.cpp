@@ -2,7 +2,6 @@
 // kernel dispatch.  Every check runs before anything is enqueued.
 #include <algorithm>
 #include <climits>
-#include <mutex>
 
 #include "../../include/moeq.h"
 #include "formats.hpp"
@@ -122,6 +121,8 @@ int check_ffn_desc(const moeq_ffn_desc* d) {
   if (d->path != MOEQ_PATH_AUTO && d->path != MOEQ_PATH_GEMV && d->path != MOEQ_PATH_MFMA)
     return MOEQ_E_INVALID;
   if (d->accumulate != 0 && d->accumulate != 1) return MOEQ_E_INVALID;
+  const int naux = (d->aux_stream != nullptr) + (d->aux_fork != nullptr) + (d->aux_join != nullptr);
+  if (naux != 0 && naux != 3) return MOEQ_E_INVALID;
   LaneGeo g;
   if (!lane_geo(d->fmt_gate, d->H, &g) || !lane_geo(d->fmt_down, d->F, &g)) return MOEQ_E_UNSUPPORTED;
   if (nsh == 3 && (!lane_geo(d->sh_fmt_gate, d->H, &g) || !lane_geo(d->sh_fmt_down, d->F_shared, &g)))
@@ -211,58 +212,26 @@ struct InlineRoute {
 
 int nper_of(int64_t E) { return E <= 256 ? 4 : E <= 512 ? 8 : E <= 1024 ? 16 : 64; }
 
-// Side stream of the current device for a shared expert launched apart from
-// the routed slots (default priority; created on first use, never while the
-// caller's stream is capturing a graph, where creating one is not allowed --
-// such a call then stays on one stream).  The events order it after the
-// caller's stream (fork) and the caller's stream after it (join); a lock
-// keeps each record-and-wait pair together when several host threads call.
-struct SideStream {
-  hipStream_t st = nullptr;
-  hipEvent_t fork = nullptr, join = nullptr;
-  bool ready = false;
-};
-constexpr int kSideDevices = 64;
 constexpr int64_t kSideMaxT = 256;
-std::mutex g_side_mu;
-SideStream g_side[kSideDevices];
 
-SideStream* side_of_current_device(hipStream_t s) {
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kSideDevices) return nullptr;
-  SideStream& sd = g_side[dev];
-  if (sd.ready) return &sd;
-  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
-  if (hipStreamIsCapturing(s, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone) return nullptr;
-  if (hipStreamCreateWithFlags(&sd.st, hipStreamNonBlocking) != hipSuccess) return nullptr;
-  if (hipEventCreateWithFlags(&sd.fork, hipEventDisableTiming) != hipSuccess ||
-      hipEventCreateWithFlags(&sd.join, hipEventDisableTiming) != hipSuccess) {
-    if (sd.fork != nullptr) hipEventDestroy(sd.fork);
-    hipStreamDestroy(sd.st);
-    sd = SideStream{};
-    return nullptr;
-  }
-  sd.ready = true;
-  return &sd;
+// The caller's auxiliary stream and events (moeq_ffn_desc::aux_*), or none.
+bool has_aux(const moeq_ffn_desc* d) { return d->aux_stream != nullptr; }
+
+// The stream the shared expert's launches go to: the caller's auxiliary
+// stream, ordered after everything enqueued on s so far.
+int fork_aux(const moeq_ffn_desc* d, hipStream_t s, hipStream_t* out) {
+  hipEvent_t fork = (hipEvent_t)d->aux_fork;
+  hipStream_t aux = (hipStream_t)d->aux_stream;
+  if (hipEventRecord(fork, s) != hipSuccess || hipStreamWaitEvent(aux, fork, 0) != hipSuccess) return -1;
+  *out = aux;
+  return 0;
 }
 
-// The stream the shared expert's launches go to: the side stream, ordered
-// after everything enqueued on s so far, or s itself.
-hipStream_t fork_side(hipStream_t s) {
-  std::lock_guard<std::mutex> lk(g_side_mu);
-  SideStream* sd = side_of_current_device(s);
-  if (sd == nullptr) return s;
-  if (hipEventRecord(sd->fork, s) != hipSuccess || hipStreamWaitEvent(sd->st, sd->fork, 0) != hipSuccess) return s;
-  return sd->st;
-}
-
-// s waits for everything enqueued on the side stream so far.
-int join_side(hipStream_t s) {
-  std::lock_guard<std::mutex> lk(g_side_mu);
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kSideDevices || !g_side[dev].ready) return -1;
-  SideStream& sd = g_side[dev];
-  if (hipEventRecord(sd.join, sd.st) != hipSuccess || hipStreamWaitEvent(s, sd.join, 0) != hipSuccess) return -1;
+// s waits for everything enqueued on the auxiliary stream so far.
+int join_aux(const moeq_ffn_desc* d, hipStream_t s) {
+  hipEvent_t join = (hipEvent_t)d->aux_join;
+  if (hipEventRecord(join, (hipStream_t)d->aux_stream) != hipSuccess || hipStreamWaitEvent(s, join, 0) != hipSuccess)
+    return -1;
   return 0;
 }
 
@@ -406,13 +375,15 @@ int ffn_enqueue(const moeq_ffn_desc* d, const void* x_q8K, const int32_t* topk_i
       return rc;
   }
   // A shared expert that is not a slot of the routed launches (another shape
-  // or format, or the MFMA path) runs its gate/up and down on the side
-  // stream, forked after everything above and joined before the combine: it
-  // reads only x, its own h rows and its own staged output rows.  Up to
-  // kSideMaxT tokens the routed launches leave most of the chip idle; past
-  // it they fill it and the shared expert stays on s.
-  const bool sh_apart = sh && (mfma || !same_shape) && d->T <= kSideMaxT;
-  const hipStream_t ss = sh_apart ? fork_side(s) : s;
+  // or format, or the MFMA path) runs its gate/up and down on the caller's
+  // auxiliary stream when one is given, forked after everything above and
+  // joined before the combine: it reads only x, its own h rows and its own
+  // staged output rows.  Up to kSideMaxT tokens the routed launches leave
+  // most of the chip idle; past it they fill it and the shared expert stays
+  // on s.
+  const bool sh_apart = sh && (mfma || !same_shape) && d->T <= kSideMaxT && has_aux(d);
+  hipStream_t ss = s;
+  if (sh_apart && (rc = fork_aux(d, s, &ss))) return rc;
   // gate/up: h[pair, f] = fl32(silu(g) u)  (dot-product path: fp32 h rows;
   // MFMA path: q8_K(h) rows straight away)
   const int n_routed_slots = one ? d->k : max_union;
@@ -461,7 +432,7 @@ int ffn_enqueue(const moeq_ffn_desc* d, const void* x_q8K, const int32_t* topk_i
     if ((rc = mfma_launch(1, false, true, s))) return rc;
   }
   if (ss == s && (rc = shared_down())) return rc;
-  if (ss != s && (rc = join_side(s))) return rc;
+  if (ss != s && (rc = join_aux(d, s))) return rc;
   return launch_combine((const float*)(wsb + L.off_yp), d->T, d->H, d->k, sh ? 1 : 0, y, d->accumulate, s);
 }
 

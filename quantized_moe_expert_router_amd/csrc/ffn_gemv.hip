@@ -14,9 +14,10 @@
 // gate/up: h[pair, f] = fl32(silu(g) * u) with g, u the fp64 dots.
 // down:    q8_K(h) is rebuilt in registers by every wave that needs it (it is a
 //          pure function of h, so all waves agree bit for bit); each work item
-//          writes w * (W_d h^) in fp64 to a per-pair staging row, counts its
-//          arrival on its row block, and the last arrival sums the pairs of
-//          every token in slot order (then the shared expert) and rounds y.
+//          writes fl32(w * (W_d h^)) (the fp64 row dot times the gate weight,
+//          rounded once) to the pair's staging row.  A separate k_combine
+//          launch then sums the staged rows of every token in fp64, slot
+//          order and the shared expert last, and rounds y.
 #include "one_token.hpp"
 
 namespace moeq {

@@ -503,7 +503,7 @@ int launch_route(int64_t T, int64_t H, int64_t E, int k, int gating, float scale
   }
   uint8_t* wsb = (uint8_t*)ws;
   double* lg = logits ? logits : reinterpret_cast<double*>(wsb);
-  launch_logits(T, H, E, x, W, bias, lg, xq, s);
+  if (int rc = launch_logits(T, H, E, x, W, bias, lg, xq, s)) return rc;
   if (T <= kSmallT) {
     size_t lds = (size_t)(T * k + 2 * E + 2 * kSmallPairs + 3) * sizeof(int);   // either list path
     // up to 64 pairs: one wave per token and one for the lists, so fewer

@@ -46,7 +46,29 @@ class FfnDesc(ctypes.Structure):
                 ("down", ctypes.c_void_p), ("F_shared", ctypes.c_int64), ("sh_fmt_gate", ctypes.c_int32),
                 ("sh_fmt_up", ctypes.c_int32), ("sh_fmt_down", ctypes.c_int32), ("sh_gate", ctypes.c_void_p),
                 ("sh_up", ctypes.c_void_p), ("sh_down", ctypes.c_void_p), ("path", ctypes.c_int32),
-                ("accumulate", ctypes.c_int32)]
+                ("accumulate", ctypes.c_int32), ("aux_stream", ctypes.c_void_p), ("aux_fork", ctypes.c_void_p),
+                ("aux_join", ctypes.c_void_p)]
+
+
+class AuxStream:
+    """A caller-owned auxiliary stream (default priority) and the two events
+    moeq_ffn_desc.aux_* take: a shared expert launched apart from the routed
+    launches runs there, forked from and joined back into the call's stream.
+    Calls that may run concurrently need one each."""
+
+    def __init__(self, device=None):
+        self.stream = torch.cuda.Stream(device=device)
+        self.fork = torch.cuda.Event()
+        self.join = torch.cuda.Event()
+        self.fork.record(self.stream)          # torch creates an event at its first record
+        self.join.record(self.stream)
+        torch.cuda.synchronize(device)
+
+    def attach(self, desc: "FfnDesc") -> "FfnDesc":
+        desc.aux_stream = self.stream.cuda_stream
+        desc.aux_fork = self.fork.cuda_event
+        desc.aux_join = self.join.cuda_event
+        return desc
 
 
 _lib = None
@@ -282,7 +304,8 @@ class DeviceLayer:
                        pack1(layer.sh_up, cfg.sh_fmt_up, cfg.F_shared, cfg.H),
                        pack1(layer.sh_down, cfg.sh_fmt_down, cfg.H, cfg.F_shared))
 
-    def ffn_desc(self, T: int, path: int = PATH_AUTO, accumulate: int = 0, shared: bool = True) -> FfnDesc:
+    def ffn_desc(self, T: int, path: int = PATH_AUTO, accumulate: int = 0, shared: bool = True,
+                 aux: Optional[AuxStream] = None) -> FfnDesc:
         c = self.cfg
         d = FfnDesc()
         d.T, d.H, d.F, d.E, d.k = T, c.H, c.F, c.E, c.k
@@ -293,17 +316,21 @@ class DeviceLayer:
             d.sh_fmt_gate, d.sh_fmt_up, d.sh_fmt_down = c.sh_fmt_gate, c.sh_fmt_up, c.sh_fmt_down
             d.sh_gate, d.sh_up, d.sh_down = (p.data_ptr() for p in self.sh)
         d.path, d.accumulate = path, accumulate
+        if aux is not None:
+            aux.attach(d)
         return d
 
 
 class LayerRunner:
     """Preallocated buffers for route -> quantize -> ffn of one layer shape.
 
-    forward() enqueues the three library calls on the current stream and
-    allocates nothing (all buffers are made here).
+    forward() enqueues the library calls on the current stream and allocates
+    nothing (all buffers are made here).  With `aux`, a shared expert that
+    runs apart from the routed launches goes to that auxiliary stream.
     """
 
-    def __init__(self, dl: DeviceLayer, T: int, path: int = PATH_AUTO, shared_scale: Optional[torch.Tensor] = None):
+    def __init__(self, dl: DeviceLayer, T: int, path: int = PATH_AUTO, shared_scale: Optional[torch.Tensor] = None,
+                 aux: Optional[AuxStream] = None):
         c = dl.cfg
         self.dl, self.T = dl, T
         dev = dl.w_router.device
@@ -311,7 +338,8 @@ class LayerRunner:
         self.route_ws = torch.empty(max(256, moeq_route_workspace(T, c.H, c.E, c.k, c.gating)), dtype=torch.uint8,
                                     device=dev)
         self.xq = torch.empty((T, c.H // 256 * Q8K_BYTES), dtype=torch.uint8, device=dev)
-        self.desc = dl.ffn_desc(T, path=path)
+        self.aux = aux
+        self.desc = dl.ffn_desc(T, path=path, aux=aux)
         n = moeq_expert_ffn_workspace(self.desc)
         if n == 0:
             raise MoeqError("moeq_expert_ffn_workspace", MOEQ_E_UNSUPPORTED)

@@ -68,6 +68,8 @@ def _desc(**kw):
     (dict(path=5), moeq.MOEQ_E_INVALID),
     (dict(accumulate=2), moeq.MOEQ_E_INVALID),
     (dict(H=256 * 40), moeq.MOEQ_E_UNSUPPORTED),
+    (dict(aux_stream=0x3000), moeq.MOEQ_E_INVALID),            # auxiliary stream without its events
+    (dict(aux_fork=0x3000, aux_join=0x4000), moeq.MOEQ_E_INVALID),
 ])
 def test_ffn_rejects_bad_descriptors(kw, status):
     d = _desc(**kw)
