@@ -36,7 +36,9 @@ def parse():
     ap.add_argument("--steps", type=int, default=400)
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--layers", type=int, default=32)
-    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU oracle sample time")
+    ap.add_argument("--cpu-seconds", type=float, default=20.0,
+                    help="target CPU oracle time over all layer shapes (all cores and one core)")
+    ap.add_argument("--cpu-child", nargs=3, metavar=("CONFIG", "THREADS", "SECONDS"), help=argparse.SUPPRESS)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-verify", action="store_true", help="skip the verify (4-token) measurement")
     ap.add_argument("--no-prefill", action="store_true", help="skip the 8192-token prefill measurement")
@@ -111,9 +113,11 @@ def summarize_pmc(fetch_dir, write_dir, calib_mib):
     print(json.dumps(res, indent=1))
 
 
-def build_layers(cfg, L, device, T):
+def build_layers(cfg, L, device, T, aux):
     """Layer 0 from the numpy generator (the parity-tested one); layers 1..L-1
-    from the same recipe drawn with torch's seeded device generator."""
+    from the same recipe drawn with torch's seeded device generator.  Every
+    layer's FFN gets the auxiliary stream `aux` (for a shared expert that runs
+    apart from the routed launches)."""
     import torch
     from quantized_moe_expert_router_amd import moeq
     from quantized_moe_expert_router_amd import synthetic as syn
@@ -121,7 +125,7 @@ def build_layers(cfg, L, device, T):
     layers = []
     lay0 = syn.gen_layer(cfg)
     dl0 = moeq.DeviceLayer(lay0, device=device)
-    layers.append(dict(w_router=dl0.w_router, bias=dl0.bias, desc=dl0.ffn_desc(T), keep=dl0))
+    layers.append(dict(w_router=dl0.w_router, bias=dl0.bias, desc=dl0.ffn_desc(T, aux=aux), keep=dl0))
     gen = torch.Generator(device=device)
     for l in range(1, L):
         gen.manual_seed(cfg.seed * 1000 + l)
@@ -152,22 +156,33 @@ def build_layers(cfg, L, device, T):
             desc.F_shared = cfg.F_shared
             desc.sh_fmt_gate, desc.sh_fmt_up, desc.sh_fmt_down = cfg.sh_fmt_gate, cfg.sh_fmt_up, cfg.sh_fmt_down
             desc.sh_gate, desc.sh_up, desc.sh_down = sg.data_ptr(), su.data_ptr(), sd.data_ptr()
+        aux.attach(desc)
         layers.append(dict(w_router=wr, bias=dl0.bias, desc=desc, keep=keep))
     torch.cuda.synchronize()
     return layers
 
 
 class LayerCycle:
-    """L synthetic layers of one shape with T tokens each, their per-layer HIP
-    graphs and one graph for the whole cycle; run(n) replays exactly n layer
-    steps (one step = the whole hot path of one layer over its T tokens)."""
+    """L synthetic layers of one shape with T tokens each.  A layer step is the
+    whole hot path of one layer over its T tokens (one moeq_moe_layer call).
+
+    time(steps, warmup) captures one HIP graph of exactly `steps` layer steps,
+    layer (first + i) mod L for step i, and times one replay of it.  The
+    warm-up before it replays max(warmup, L) steps, so every timed layer was
+    last touched at least L - 1 layer steps earlier: with L layers whose
+    weights together exceed the 256 MB Infinity Cache, each step streams its
+    weights from HBM, as in a decoder stack.  The timed figure does not
+    depend on how `steps` relates to L.  time_per_layer_graphs() times the
+    same steps as one single-layer graph launch each (a graph per layer, as
+    the Strata summary's execution paragraph describes)."""
 
     def __init__(self, cfg, T, L, device):
         import numpy as np
         import torch
         from quantized_moe_expert_router_amd import moeq
         self.cfg, self.T, self.L = cfg, T, L
-        self.layers = build_layers(cfg, L, device, T)
+        self.aux = moeq.AuxStream(device)
+        self.layers = build_layers(cfg, L, device, T, self.aux)
         rng = np.random.default_rng(7)
         self.xs = [torch.from_numpy(rng.standard_normal((T, cfg.H)).astype(np.float32)).to(device)
                    for _ in range(L)]
@@ -179,18 +194,8 @@ class LayerCycle:
         for l in range(L):
             self.step(l)
         torch.cuda.synchronize()
-        stream = torch.cuda.Stream()
-        self.graphs = []
-        with torch.cuda.stream(stream):
-            for l in range(L):
-                g = torch.cuda.CUDAGraph()
-                with torch.cuda.graph(g, stream=stream):
-                    self.step(l, stream)
-                self.graphs.append(g)
-            self.cycle = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(self.cycle, stream=stream):
-                for l in range(L):
-                    self.step(l, stream)
+        self.stream = torch.cuda.Stream()
+        self.graphs = [self.capture(l, 1) for l in range(L)]
         torch.cuda.synchronize()
 
     def step(self, l, stream=None):
@@ -199,18 +204,40 @@ class LayerCycle:
         moeq.moeq_moe_layer(self.rdesc, lay["desc"], self.xs[l], lay["w_router"], lay["bias"], self.route_out, None,
                             self.y, self.ws, stream)
 
-    def run(self, n):
-        for _ in range(n // self.L):
-            self.cycle.replay()
-        for l in range(n % self.L):
-            self.graphs[l].replay()
+    def capture(self, first, n):
+        """One graph of n layer steps: layers first, first+1, ... (mod L)."""
+        import torch
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(self.stream):
+            with torch.cuda.graph(g, stream=self.stream):
+                for i in range(n):
+                    self.step((first + i) % self.L, self.stream)
+        return g
 
     def time(self, steps, warmup):
         import torch
-        self.run(warmup)
+        wsteps = max(warmup, self.L)
+        gw = self.capture(0, wsteps)
+        gt = self.capture(wsteps % self.L, steps)
+        torch.cuda.synchronize()
+        gw.replay()
         torch.cuda.synchronize()
         t0 = time.perf_counter()
-        self.run(steps)
+        gt.replay()
+        torch.cuda.synchronize()
+        dt = time.perf_counter() - t0
+        del gw, gt
+        return dt, wsteps
+
+    def time_per_layer_graphs(self, steps, warmup):
+        import torch
+        wsteps = max(warmup, self.L)
+        for i in range(wsteps):
+            self.graphs[i % self.L].replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(steps):
+            self.graphs[(wsteps + i) % self.L].replay()
         torch.cuda.synchronize()
         return time.perf_counter() - t0
 
@@ -255,6 +282,15 @@ def ffn_event_us(cyc, n_ev):
 INT8_PEAK_TOPS = 5000.0
 
 
+def layer_bytes_of(cfg, union):
+    """Algorithmic bytes of one layer step: the weights of the experts in the
+    union (each read once) and of the shared expert, the router weights, x in
+    and y out."""
+    from quantized_moe_expert_router_amd import synthetic as syn
+    w_bytes = union * syn.expert_bytes(cfg) + (syn.shared_bytes(cfg) if cfg.shared else 0)
+    return w_bytes, w_bytes + cfg.E * cfg.H * 4 + 2 * cfg.T * cfg.H * 4
+
+
 def secondary(name, L, steps, warmup, dev):
     """Whole-layer throughput of another workload (layers cycled so weights
     stream from HBM), its expert-FFN launch time, and the FFN's roofline
@@ -264,18 +300,18 @@ def secondary(name, L, steps, warmup, dev):
     from quantized_moe_expert_router_amd import synthetic as syn
     cfg = syn.CONFIGS[name]
     cyc = LayerCycle(cfg, cfg.T, L, dev)
-    dt = cyc.time(steps, warmup)
+    dt, _ = cyc.time(steps, warmup)
     ms = dt * 1e3 / steps
     ids = cyc.route_out.ids.cpu().numpy()
     union = len(set(ids.reshape(-1).tolist()))
     ffn_us = ffn_event_us(cyc, max(steps, 8))
-    w_bytes = union * syn.expert_bytes(cfg) + (syn.shared_bytes(cfg) if cfg.shared else 0)
-    layer_bytes = w_bytes + cfg.E * cfg.H * 4 + 2 * cfg.T * cfg.H * 4
+    w_bytes, layer_bytes = layer_bytes_of(cfg, union)
     pairs = cfg.T * cfg.k + (cfg.T if cfg.shared else 0)
     Fs = cfg.F_shared if cfg.shared else cfg.F
     ops = 2 * 3 * cfg.H * (cfg.T * cfg.k * cfg.F + (cfg.T * Fs if cfg.shared else 0))
     out = {"workload": cfg.name, "T": cfg.T, "tokens_per_s": cfg.T * steps / dt, "ms_per_step": ms,
-           "layers_cycled": L, "union": union, "pairs": pairs, "layer_hbm_gbs": layer_bytes / (ms * 1e-3) / 1e9,
+           "steps": steps, "layers_cycled": L, "union": union, "pairs": pairs,
+           "layer_hbm_gbs": layer_bytes / (ms * 1e-3) / 1e9,
            "ffn_us": ffn_us, "ffn_weight_gbs": w_bytes / (ffn_us * 1e-6) / 1e9,
            "ffn_int8_tops": ops / (ffn_us * 1e-6) / 1e12,
            "ffn_int8_mfma_frac": ops / (ffn_us * 1e-6) / 1e12 / INT8_PEAK_TOPS}
@@ -284,14 +320,28 @@ def secondary(name, L, steps, warmup, dev):
     return out
 
 
-def cpu_baseline(cfg, seconds):
-    """The CPU oracle, as it stands, on a bounded sample of decode tokens of layer 0."""
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_child(name, threads, seconds):
+    """Child process (OMP_NUM_THREADS = threads): the CPU oracle, as it stands,
+    on a bounded sample of tokens of the named layer shape (router + expert
+    FFN, the sample's tokens in one oracle call; tokens are independent rows,
+    so a decode shape's sample is a batch of decode tokens).  Prints one JSON
+    object."""
     import numpy as np
     import oracle
     from quantized_moe_expert_router_amd import synthetic as syn
 
-    lay = syn.gen_layer(cfg)
-    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    cfg = syn.CONFIGS[name]
+    lay = syn.gen_layer(cfg, T=1)
 
     def run(n, seed):
         x = syn.gen_x(cfg, seed, 0, T=n)
@@ -300,17 +350,52 @@ def cpu_baseline(cfg, seconds):
         oracle.expert_ffn(lay, ids, w, list(range(n)), x=x)
         return time.perf_counter() - t0
 
-    probe = max(threads, 8)
-    tp = run(probe, 4242)
-    n = int(max(probe, min(20000, probe * seconds / max(tp, 1e-3))))
-    dt = run(n, 4343)
-    return {"value": n / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": "%d decode tokens (route + expert FFN) of the 2048x256x8+shared layer, %.1f s wall, "
-                      "OpenMP over tokens" % (n, dt)}
+    n = 1
+    dt = run(n, 4242)
+    for it in range(3):
+        if dt >= seconds / 2:
+            break
+        n = min(1 << 16, max(n * 2, int(n * seconds / max(dt, 1e-4))))
+        dt = run(n, 4343 + it)
+    print(json.dumps({"tokens": n, "seconds": dt, "tokens_per_s": n / dt}), flush=True)
+
+
+def cpu_baseline(seconds):
+    """The CPU oracle on the host cores: every layer shape, on all cores and on
+    one core, each on a bounded sample of its tokens (a child process per run,
+    so OpenMP takes the stated thread count)."""
+    import subprocess
+    from quantized_moe_expert_router_amd import synthetic as syn
+    all_threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    per = {}
+    per_run = seconds / (2 * len(syn.CONFIG_ORDER))
+    for name in syn.CONFIG_ORDER:
+        cfg = syn.CONFIGS[name]
+        row = {"workload": cfg.name}
+        for label, th in (("all_cores", all_threads), ("one_core", 1)):
+            env = dict(os.environ, OMP_NUM_THREADS=str(th))
+            r = subprocess.run([sys.executable, os.path.abspath(__file__), "--cpu-child", name, str(th),
+                                str(per_run)], capture_output=True, text=True, env=env, timeout=600)
+            if r.returncode != 0:
+                raise RuntimeError("CPU oracle run failed for %s: %s" % (name, r.stderr[-2000:]))
+            res = json.loads(r.stdout.strip().splitlines()[-1])
+            row[label] = {"tokens_per_s": res["tokens_per_s"], "tokens": res["tokens"],
+                          "seconds": res["seconds"], "threads": th}
+        per[name] = row
+    d = per["decode"]["all_cores"]
+    return {"value": d["tokens_per_s"], "unit": "tokens/s", "cores": all_threads, "kind": "oracle",
+            "cpu_model": cpu_model(), "nproc": os.cpu_count(),
+            "sample": "%d decode tokens (router + expert FFN) of the hidden-2048, 256-expert top-8 + shared layer, "
+                      "%.2f s wall on %d OpenMP threads; per_config: every layer shape on all cores and on one "
+                      "core, a sample of its tokens each" % (d["tokens"], d["seconds"], all_threads),
+            "per_config": per}
 
 
 def main():
     args = parse()
+    if args.cpu_child:
+        cpu_child(args.cpu_child[0], int(args.cpu_child[1]), float(args.cpu_child[2]))
+        return
     if args.summarize_pmc:
         summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], args.calib_copy_mib or 256)
         return
@@ -318,9 +403,7 @@ def main():
         print("bench.py measures one GPU only: this build has no multi-GPU path (run with --gpus 1)",
               file=sys.stderr)
         sys.exit(2)
-    import numpy as np
     import torch
-    from quantized_moe_expert_router_amd import moeq
     from quantized_moe_expert_router_amd import synthetic as syn
 
     dev = "cuda:0"
@@ -337,13 +420,15 @@ def main():
     cyc = LayerCycle(cfg, 1, L, dev)
     setup_s = time.time() - t_setup
 
-    # ---- timed region: exactly `steps` whole layers (value)
-    dt = cyc.time(args.steps, args.warmup)
+    # ---- timed region: one graph of exactly `steps` whole layers (value)
+    dt, wsteps = cyc.time(args.steps, args.warmup)
     ms_per_step = dt * 1e3 / args.steps
     tokens_per_s = args.steps / dt
+    # ---- secondary: the same steps as one single-layer graph launch each
+    dt_pl = cyc.time_per_layer_graphs(args.steps, args.warmup)
 
     # ---- expert FFN launches timed with HIP events on their stream
-    ffn_us = ffn_event_us(cyc, args.steps)
+    ffn_us = ffn_event_us(cyc, max(args.steps, 32))
 
     # Algorithmic bytes of one expert FFN launch: the weights of the 8 selected
     # experts and the shared one, read once, plus q8_K(x) in and y out.
@@ -355,14 +440,16 @@ def main():
     del cyc
     torch.cuda.empty_cache()
 
+    sub_steps = max(8, args.steps // 4)
+    sub_warm = max(4, args.warmup // 4)
     # ---- secondary: MTP verify rows (4 tokens per step, union of experts)
     verify = None
     if not args.no_verify:
-        verify = secondary("verify", max(4, L // 4), max(8, args.steps // 4), max(4, args.warmup // 4), dev)
+        verify = secondary("verify", max(4, L // 4), sub_steps, sub_warm, dev)
     # ---- secondary: 16-token chunk (sigmoid top-6, Q2_K/Q4_K experts, Q8_0 shared expert)
     chunk = None
     if not args.no_chunk:
-        chunk = secondary("chunk16", max(4, L // 4), max(8, args.steps // 4), max(4, args.warmup // 4), dev)
+        chunk = secondary("chunk16", max(4, L // 4), sub_steps, sub_warm, dev)
     # ---- secondary: 8192-token prefill chunk (int8 MFMA grouped GEMM)
     prefill = None
     if not args.no_prefill:
@@ -370,7 +457,7 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(cfg, args.cpu_seconds)
+        cpu = cpu_baseline(args.cpu_seconds)
 
     out = {
         "metric": METRIC,
@@ -387,8 +474,12 @@ def main():
         "data": "synthetic",
         "config": {"workload": cfg.name, "T": 1, "H": cfg.H, "E": cfg.E, "k": cfg.k, "F": cfg.F,
                    "shared_F": cfg.F_shared, "gate_up": "Q4_K", "down": "Q6_K", "layers_cycled": L,
-                   "layer_bytes": layer_bytes, "parallelism": "single GPU"},
+                   "layer_bytes": layer_bytes, "parallelism": "single GPU",
+                   "timing": "one HIP graph of exactly `steps` layer steps cycling the layers, after a warm-up "
+                             "graph of %d layer steps (at least one whole cycle)" % wsteps},
         "layer_hbm_gbs": layer_bytes / (ms_per_step * 1e-3) / 1e9,
+        "per_layer_graphs": {"tokens_per_s": args.steps / dt_pl, "ms_per_step": dt_pl * 1e3 / args.steps,
+                             "note": "the same layer steps, one single-layer graph launch each"},
         "roofline": {"bound": "hbm", "kernel": "expert FFN (gate/up GEMV + down GEMV)",
                      "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic(),
