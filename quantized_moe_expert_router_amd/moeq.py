@@ -65,9 +65,13 @@ class AuxStream:
         torch.cuda.synchronize(device)
 
     def attach(self, desc: "FfnDesc") -> "FfnDesc":
+        """Put the stream and event handles into desc; desc keeps this object
+        alive (torch destroys an event with its Python object, which would
+        leave the descriptor with dangling handles)."""
         desc.aux_stream = self.stream.cuda_stream
         desc.aux_fork = self.fork.cuda_event
         desc.aux_join = self.join.cuda_event
+        desc._aux_owner = self
         return desc
 
 

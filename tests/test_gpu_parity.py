@@ -394,7 +394,8 @@ def test_graph_replays_match_eager(variant):
     layer = syn.gen_layer(cfg)
     say("graph replays", variant)
     dl = moeq.DeviceLayer(layer)
-    fdesc = dl.ffn_desc(cfg.T, aux=moeq.AuxStream())
+    aux = moeq.AuxStream()
+    fdesc = dl.ffn_desc(cfg.T, aux=aux)
     rdesc = moeq.RouteDesc(cfg.T, cfg.H, cfg.E, cfg.k, cfg.gating, 1.0)
     x = dev(layer.x.astype(np.float32))
     out = moeq.RouteOut(cfg.T, cfg.E, cfg.k, x.device)
