@@ -13,7 +13,8 @@
  *     hipStream_t (NULL = the null stream).  Work is enqueued asynchronously
  *     on `stream`; nothing synchronises, allocates device memory, creates a
  *     stream or event, or reads the environment or any state of its own:
- *     the library holds no mutable global state (the MoE kernels never
+ *     the library holds no mutable global state apart from the static
+ *     workspace of moeq_moe_layer_noalloc (the MoE kernels never
  *     consult global state and every launch gets explicit per-expert
  *     pointers: Pulsar README, 'How the streaming works'; session state is
  *     preallocated by the caller: Strata summary, execution paragraph).
@@ -74,7 +75,9 @@ typedef enum {
     MOEQ_E_INVALID = -1,      /* bad size, NULL pointer, misalignment */
     MOEQ_E_UNSUPPORTED = -2,  /* format / gating / path / shape not supported */
     MOEQ_E_WORKSPACE = -3,    /* workspace smaller than the query returns */
-    MOEQ_E_HIP = -4           /* a HIP launch or API call failed */
+    MOEQ_E_HIP = -4,          /* a HIP launch or API call failed */
+    MOEQ_E_STATIC_LIMIT = -5  /* moeq_moe_layer_noalloc: the call needs more than
+                                 MOEQ_NOALLOC_MAX_BYTES of workspace */
 } moeq_status;
 
 typedef enum { MOEQ_Q4_K = 1, MOEQ_Q6_K = 2, MOEQ_Q2_K = 3, MOEQ_Q8_0 = 4 } moeq_wfmt;
@@ -245,6 +248,27 @@ int moeq_moe_layer(const moeq_route_desc* r, const moeq_ffn_desc* f, const float
                    const float* bias, double* logits, int32_t* topk_ids, float* topk_w, int32_t* expert_offsets,
                    int32_t* pairs, int32_t* active, const float* shared_scale, float* y, void* ws,
                    size_t ws_bytes, void* stream);
+
+/*
+ * moeq_moe_layer without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  Same arguments, outputs and results as
+ * moeq_moe_layer, whose kernels it runs; the workspace is instead a static
+ * device array of MOEQ_NOALLOC_MAX_BYTES (32 MiB) inside the library, one
+ * per GPU, held from the library's load until the process ends.  The call
+ * allocates nothing; on its first call on a device (the current device) it
+ * looks up that device's array once.  Every call on a GPU shares that GPU's
+ * array, so calls whose work may overlap on one GPU race: order them (one
+ * stream, or events).  `stream` must belong to the current device (NULL =
+ * its null stream).  Errors: as moeq_moe_layer; MOEQ_E_STATIC_LIMIT when
+ * moeq_moe_layer_workspace(r, f) exceeds MOEQ_NOALLOC_MAX_BYTES (the request
+ * is rejected before anything is enqueued).  moeq_ffn_h_view does not apply.
+ */
+#define MOEQ_NOALLOC_MAX_BYTES ((size_t)32 << 20)
+int moeq_moe_layer_noalloc(const moeq_route_desc* r, const moeq_ffn_desc* f, const float* x,
+                           const float* w_router, const float* bias, double* logits, int32_t* topk_ids,
+                           float* topk_w, int32_t* expert_offsets, int32_t* pairs, int32_t* active,
+                           const float* shared_scale, float* y, void* stream);
 
 /*
  * Test hook (GPU kernel selftests against CPU references and a bit-exact

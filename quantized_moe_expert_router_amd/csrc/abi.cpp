@@ -141,6 +141,7 @@ const char* moeq_status_string(int status) {
     case MOEQ_E_UNSUPPORTED: return "unsupported format, gating, path or shape";
     case MOEQ_E_WORKSPACE: return "workspace too small";
     case MOEQ_E_HIP: return "HIP launch failed";
+    case MOEQ_E_STATIC_LIMIT: return "needs more workspace than the static 32 MiB of moeq_moe_layer_noalloc";
   }
   return "unknown status";
 }

@@ -17,6 +17,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmoeq.so")
 
 MOEQ_OK, MOEQ_E_INVALID, MOEQ_E_UNSUPPORTED, MOEQ_E_WORKSPACE, MOEQ_E_HIP = 0, -1, -2, -3, -4
+MOEQ_E_STATIC_LIMIT = -5
+NOALLOC_MAX_BYTES = 32 << 20
 Q4_K, Q6_K, Q2_K, Q8_0 = 1, 2, 3, 4
 SOFTMAX_TOPK, SOFTMAX_ALL, SIGMOID_TOPK = 0, 1, 2
 PATH_AUTO, PATH_GEMV, PATH_MFMA = 0, 1, 2
@@ -25,7 +27,8 @@ SUBBLOCK = {Q4_K: 32, Q6_K: 16, Q2_K: 16, Q8_0: 32}
 
 SYMBOLS = ["moeq_status_string", "moeq_quantize_q8K", "moeq_route_workspace", "moeq_route",
            "moeq_packed_bytes", "moeq_pack_experts", "moeq_expert_ffn_workspace", "moeq_expert_ffn",
-           "moeq_moe_layer_workspace", "moeq_moe_layer", "moeq_ffn_h_view", "moeq_debug_subdots"]
+           "moeq_moe_layer_workspace", "moeq_moe_layer", "moeq_ffn_h_view", "moeq_debug_subdots",
+           "moeq_moe_layer_noalloc"]
 
 
 class MoeqError(RuntimeError):
@@ -101,10 +104,12 @@ def lib() -> ctypes.CDLL:
         L.moeq_moe_layer_workspace.argtypes = [ctypes.POINTER(RouteDesc), ctypes.POINTER(FfnDesc)]
         L.moeq_moe_layer.argtypes = [ctypes.POINTER(RouteDesc), ctypes.POINTER(FfnDesc), vp, vp, vp, vp, vp, vp,
                                      vp, vp, vp, vp, vp, vp, sz, vp]
+        L.moeq_moe_layer_noalloc.argtypes = [ctypes.POINTER(RouteDesc), ctypes.POINTER(FfnDesc), vp, vp, vp, vp, vp,
+                                             vp, vp, vp, vp, vp, vp, vp]
         L.moeq_ffn_h_view.argtypes = [ctypes.POINTER(FfnDesc), vp, sz, ctypes.POINTER(vp), ctypes.POINTER(vp)]
         L.moeq_debug_subdots.argtypes = [i32, vp, i64, i64, vp, i64, vp, vp]
         for s in ("moeq_quantize_q8K", "moeq_route", "moeq_pack_experts", "moeq_expert_ffn", "moeq_moe_layer",
-                  "moeq_ffn_h_view", "moeq_debug_subdots"):
+                  "moeq_ffn_h_view", "moeq_debug_subdots", "moeq_moe_layer_noalloc"):
             getattr(L, s).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -230,6 +235,19 @@ def moeq_moe_layer(rdesc: RouteDesc, fdesc: FfnDesc, x: torch.Tensor, w_router: 
                               _ptr(out.logits), _ptr(out.ids), _ptr(out.w), _ptr(out.offsets), _ptr(out.pairs),
                               _ptr(out.active), _ptr(shared_scale), _ptr(y), _ptr(ws), ws.numel(), _stream(stream))
     _check("moeq_moe_layer", rc)
+    return y
+
+
+def moeq_moe_layer_noalloc(rdesc: RouteDesc, fdesc: FfnDesc, x: torch.Tensor, w_router: torch.Tensor,
+                           bias: Optional[torch.Tensor], out: "RouteOut", shared_scale: Optional[torch.Tensor],
+                           y: torch.Tensor, stream=None) -> torch.Tensor:
+    """The whole layer with the library's static per-GPU workspace (no
+    workspace argument; calls on one GPU must not overlap)."""
+    rc = lib().moeq_moe_layer_noalloc(ctypes.byref(rdesc), ctypes.byref(fdesc), _ptr(x), _ptr(w_router), _ptr(bias),
+                                      _ptr(out.logits), _ptr(out.ids), _ptr(out.w), _ptr(out.offsets),
+                                      _ptr(out.pairs), _ptr(out.active), _ptr(shared_scale), _ptr(y),
+                                      _stream(stream))
+    _check("moeq_moe_layer_noalloc", rc)
     return y
 
 

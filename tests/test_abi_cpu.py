@@ -142,3 +142,18 @@ def test_route_and_quantize_validation():
     assert L.moeq_pack_experts(9, 0x1000, 1, 1, 256, 0x2000, None) == moeq.MOEQ_E_UNSUPPORTED
     assert L.moeq_pack_experts(1, 0x1000, 1, 1, 256, 0x2010, None) == moeq.MOEQ_E_INVALID
     assert L.moeq_debug_subdots(1, 0x1000, 1, 300, 0x2000, 1, 0x3000, None) == moeq.MOEQ_E_INVALID
+
+
+def test_noalloc_layer_rejects_requests_beyond_its_static_workspace():
+    # the 8192-token prefill layer needs far more than the 32 MiB static
+    # workspace: rejected on the host before any device call
+    L = moeq.lib()
+    f = _desc(T=8192, H=2048, F=512, E=512, k=10, fmt_down=moeq.Q4_K)
+    r = moeq.RouteDesc(8192, 2048, 512, 10, 0, 1.0)
+    assert L.moeq_moe_layer_workspace(ctypes.byref(r), ctypes.byref(f)) > moeq.NOALLOC_MAX_BYTES
+    ptrs = [0x1000] * 12
+    ptrs[2] = ptrs[3] = None
+    assert L.moeq_moe_layer_noalloc(ctypes.byref(r), ctypes.byref(f), *ptrs, None) == moeq.MOEQ_E_STATIC_LIMIT
+    r2 = moeq.RouteDesc(8192, 2048, 512, 6, 0, 1.0)            # descriptors that disagree
+    assert L.moeq_moe_layer_noalloc(ctypes.byref(r2), ctypes.byref(f), *ptrs, None) == moeq.MOEQ_E_INVALID
+    assert moeq.status_string(moeq.MOEQ_E_STATIC_LIMIT) != "unknown status"
