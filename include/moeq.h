@@ -297,6 +297,26 @@ int moeq_ffn_h_view(const moeq_ffn_desc* d, void* ws, size_t ws_bytes, void** hq
 int moeq_debug_subdots(int32_t fmt, const void* packed_w, int64_t rows, int64_t cols,
                        const void* x_q8K, int64_t n_x, int32_t* out, void* stream);
 
+/*
+ * Test hook (a one-row GPU-versus-CPU integer arbiter: Pulsar README, 'What
+ * it does today', CPU-lane paragraph; GPU kernel selftests against CPU
+ * references: Pulsar README, 'Tests'): the exact integer parts of every
+ * super-block term, computed by the int8 MFMA tile code of the MFMA path (the
+ * same MFMA and unpack routines, the same LDS staging of q8_K rows).
+ *   packed_w [rows, cols] packed fmt, rows % 256 == 0; x_q8K [n_x, cols/256
+ *   blocks]; out int32 [n_x, rows, cols/256, 8], 16-byte aligned:
+ *     Q4_K, Q2_K: (S1, S2, 0...) with S1 = sum_j sc_j isum_j,
+ *                 S2 = sum_j m_j bsum_j (bsum over the sub-block's 32 / 16
+ *                 activations)
+ *     Q6_K:       (S1, S2, 0...) with S1 = sum_j sc_j isum_j over the codes
+ *                 q - 32 and S2 = sum_j sc_j bsum_j
+ *     Q8_0:       isum_b of the eight 32-blocks of the super-block
+ * Enqueued on `stream`; n_x == 0 is a no-op.  Errors: MOEQ_E_UNSUPPORTED for
+ * an unknown format, MOEQ_E_INVALID for bad sizes, NULLs or misalignment.
+ */
+int moeq_debug_mfma_sums(int32_t fmt, const void* packed_w, int64_t rows, int64_t cols,
+                         const void* x_q8K, int64_t n_x, int32_t* out, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

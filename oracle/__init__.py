@@ -54,6 +54,7 @@ def lib():
         L.orc_lists.argtypes = [i64, i32, i64, vp, vp, vp, vp]
         L.orc_lists.restype = None
         L.orc_subdots.argtypes = [i32, vp, i64, i64, vp, i64, vp]
+        L.orc_scales_matrix.argtypes = [i32, vp, i64, i64, vp, vp]
         L.orc_dot_intform.argtypes = [i32, vp, i64, vp]
         L.orc_dot_intform.restype = dbl
         L.orc_matvec.argtypes = [i32, vp, i64, i64, vp, vp]
@@ -165,6 +166,19 @@ def subdots(fmt: int, W: np.ndarray, rows: int, cols: int, xq: np.ndarray) -> np
     if lib().orc_subdots(fmt, _p(W), rows, cols, _p(xq), n_x, _p(out)):
         raise ValueError("orc_subdots failed")
     return out
+
+
+def scales_matrix(fmt: int, W: np.ndarray, rows: int, cols: int):
+    """(sc, m) int32 [rows, blocks per row, sub-blocks per block]: the decoded
+    sub-block scales and mins of every block."""
+    W = _c(W, np.uint8)
+    nblk = cols // BLOCK_W[fmt]
+    sc = np.zeros((rows, nblk, 16), np.int32)
+    m = np.zeros((rows, nblk, 16), np.int32)
+    if lib().orc_scales_matrix(fmt, _p(W), rows, cols, _p(sc), _p(m)):
+        raise ValueError("orc_scales_matrix failed")
+    nsub = BLOCK_W[fmt] // SUBBLOCK[fmt]
+    return sc[:, :, :nsub].copy(), m[:, :, :nsub].copy()
 
 
 def dot_intform(fmt: int, wrow: np.ndarray, cols: int, xq_row: np.ndarray) -> float:

@@ -411,6 +411,7 @@ int orc_subdots(int fmt, const uint8_t* w, int64_t rows, int64_t cols,
     int64_t nsub = cols / sbw, nblk = cols / bw, n, r, b;
     if (!bw || cols % 256)
         return -1;
+#pragma omp parallel for collapse(2) private(b) schedule(static)
     for (n = 0; n < n_x; n++)
         for (r = 0; r < rows; r++)
             for (b = 0; b < nblk; b++) {
@@ -430,6 +431,33 @@ int orc_subdots(int fmt, const uint8_t* w, int64_t rows, int64_t cols,
                     out[(n * rows + r) * nsub + b * (bw / sbw) + i] = acc;
                 }
             }
+    return 0;
+}
+
+/*
+ * The sub-block scales and mins of every block of a [rows, cols] matrix, as
+ * orc_block_codes decodes them: sc[((r * nblk) + b) * 16 + j] and m likewise
+ * for sub-block j of block b of row r (nblk = cols / block width; Q8_0 blocks
+ * have one sub-block with sc = 1, m = 0; unused entries are 0).
+ */
+int orc_scales_matrix(int fmt, const uint8_t* w, int64_t rows, int64_t cols, int32_t* sc, int32_t* m)
+{
+    int bw = orc_block_weights(fmt), bb = orc_block_bytes(fmt);
+    int64_t nblk, r, b;
+    if (!bw || cols % bw)
+        return -1;
+    nblk = cols / bw;
+    for (r = 0; r < rows; r++)
+        for (b = 0; b < nblk; b++) {
+            double d, dmin;
+            int s16[16] = {0}, m16[16] = {0}, q[256], j;
+            if (orc_block_codes(fmt, w + (r * nblk + b) * bb, &d, &dmin, s16, m16, q))
+                return -1;
+            for (j = 0; j < 16; j++) {
+                sc[(r * nblk + b) * 16 + j] = j < bw / orc_subblock(fmt) ? s16[j] : 0;
+                m[(r * nblk + b) * 16 + j] = j < bw / orc_subblock(fmt) ? m16[j] : 0;
+            }
+        }
     return 0;
 }
 

@@ -546,4 +546,15 @@ int moeq_debug_subdots(int32_t fmt, const void* packed_w, int64_t rows, int64_t 
   return hip_status(launch_subdots(fmt, packed_w, rows, cols, x_q8K, n_x, out, (hipStream_t)stream));
 }
 
+int moeq_debug_mfma_sums(int32_t fmt, const void* packed_w, int64_t rows, int64_t cols, const void* x_q8K,
+                         int64_t n_x, int32_t* out, void* stream) {
+  if (!fmt_ok(fmt)) return MOEQ_E_UNSUPPORTED;
+  if (rows <= 0 || rows % 256 || cols <= 0 || cols % 256 || n_x < 0) return MOEQ_E_INVALID;
+  if (n_x == 0) return MOEQ_OK;
+  if (!packed_w || !x_q8K || !out || !aligned(packed_w, 256) || !aligned(x_q8K, 4) || !aligned(out, 16))
+    return MOEQ_E_INVALID;
+  if ((n_x + 31) / 32 > INT32_MAX || rows / 256 > 65535) return MOEQ_E_UNSUPPORTED;
+  return hip_status(launch_mfma_ints(fmt, packed_w, rows, cols, x_q8K, n_x, out, (hipStream_t)stream));
+}
+
 }  // extern "C"

@@ -147,10 +147,11 @@ template <> struct Mf<FQ4K> {
     w.h = gld_u4(hb + lr * 16u);
     return w;
   }
+  // The exact integer parts of the super-block term for the lane's 16 results:
+  // s1 = sum_j sc_j isum_j, s2 = sum_j m_j bsum_j.
   // MFMA 2p+s: lane half g holds sub-block 2p+g, nibble s (elements 64p+32g+16s .. +15).
-  template <int NQ>
-  __device__ static void mac(const Wt& w, int g, const uint8_t* qrow, const v4i abs, const double* dxs,
-                             int n, double* acc) {
+  struct Ints { v16i s1, s2; };
+  __device__ __forceinline__ static Ints ints(const Wt& w, int g, const uint8_t* qrow, const v4i abs) {
     const uint64_t lo = (uint64_t)w.h.y | ((uint64_t)w.h.z << 32);
     const uint64_t hi = (uint64_t)w.h.z | ((uint64_t)w.h.w << 32);
     v16i plo = {0}, phi = {0};
@@ -183,8 +184,14 @@ template <> struct Mf<FQ4K> {
     const v16i z16 = {0};
     const v16i xl = mfma_k32(abs, g == 0 ? bm : zero, z16);
     const v16i xh = mfma_k32(abs, g == 1 ? bm : zero, z16);
+    return Ints{plo + 8 * phi, xl + 64 * xh};
+  }
+  template <int NQ>
+  __device__ static void mac(const Wt& w, int g, const uint8_t* qrow, const v4i abs, const double* dxs,
+                             int n, double* acc) {
+    const Ints I = ints(w, g, qrow, abs);
     const double d = half_bits_to_float(w.h.x & 0xFFFF), dmin = half_bits_to_float(w.h.x >> 16);
-    MOEQ_COMBINE(acc[r] += dx * (d * (double)(plo[r] + 8 * phi[r]) - dmin * (double)(xl[r] + 64 * xh[r])))
+    MOEQ_COMBINE(acc[r] += dx * (d * (double)I.s1[r] - dmin * (double)I.s2[r]))
   }
 };
 
@@ -205,11 +212,12 @@ template <> struct Mf<FQ2K> {
     w.dd = gld_u32(cb + ((uint32_t)kQ2KD + 4u * r));
     return w;
   }
+  // The exact integer parts of the super-block term: s1 = sum_j sc_j isum_j,
+  // s2 = sum_j m_j bsum_j.
   // MFMA p: lane half g holds sub-block 2p+g (elements 32p+16g .. +15), whose
   // 16 codes are word p of the half: element 4i + b at bits 8b + 2i.
-  template <int NQ>
-  __device__ static void mac(const Wt& w, int g, const uint8_t* qrow, const v4i abs, const double* dxs,
-                             int n, double* acc) {
+  struct Ints { v16i s1, s2; };
+  __device__ __forceinline__ static Ints ints(const Wt& w, int g, const uint8_t* qrow, const v4i abs) {
     typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
     const uint32_t sm[4] = {w.sm.x, w.sm.y, w.sm.z, w.sm.w};
     v16i P = {0};
@@ -233,8 +241,14 @@ template <> struct Mf<FQ2K> {
     const v16i z16 = {0};
     const v16i xl = mfma_k32(abs, g == 0 ? bm : zero, z16);
     const v16i xh = mfma_k32(abs, g == 1 ? bm : zero, z16);
+    return Ints{P, xl + 64 * xh};
+  }
+  template <int NQ>
+  __device__ static void mac(const Wt& w, int g, const uint8_t* qrow, const v4i abs, const double* dxs,
+                             int n, double* acc) {
+    const Ints I = ints(w, g, qrow, abs);
     const double d = half_bits_to_float(w.dd & 0xFFFF), dmin = half_bits_to_float(w.dd >> 16);
-    MOEQ_COMBINE(acc[r] += dx * (d * (double)P[r] - dmin * (double)(xl[r] + 64 * xh[r])))
+    MOEQ_COMBINE(acc[r] += dx * (d * (double)I.s1[r] - dmin * (double)I.s2[r]))
   }
 };
 
@@ -262,14 +276,14 @@ template <> struct Mf<FQ6K> {
     w.d = gld_u16(pd + rs.su * 2 + lr * 2u);
     return w;
   }
+  // The MFMA part of the super-block term: S1[r] = sum_j sc_j (sum q q_x)
+  // with the unsigned codes q, and the offset sum xl + 64 xh = sum_j sc_j bsum_j.
   // One 16-deep MFMA per sub-block jj: lane half g holds elements 16jj+8g .. +7
   // (low nibbles: word i = 2g+t of chunk jj/2, nibble jj%2; high pairs: word
   // jj%2 of chunk jj/2 in the high-pair plane, bits 2i).
-  template <int NQ>
-  __device__ static void mac(const Wt& w, int g, const uint8_t* qrow, const v4i abs, const double* dxs,
-                             int n, double* acc) {
+  __device__ __forceinline__ static void raw(const Wt& w, int g, const uint8_t* qrow, const v4i abs, int* S1,
+                                             v16i& xl, v16i& xh) {
     const uint32_t scw[4] = {w.sc.x, w.sc.y, w.sc.z, w.sc.w};
-    int S1[16];
 #pragma unroll
     for (int r = 0; r < 16; ++r) S1[r] = 0;
     const v16i z16 = {0};
@@ -294,8 +308,30 @@ template <> struct Mf<FQ6K> {
       __builtin_amdgcn_sched_barrier(0);   // keep one sub-block's results live at a time
     }
     const v4i bm = {(int)scw[0], (int)scw[1], (int)scw[2], (int)scw[3]}, zero = {0, 0, 0, 0};
-    const v16i xl = mfma_k32(abs, g == 0 ? bm : zero, z16);
-    const v16i xh = mfma_k32(abs, g == 1 ? bm : zero, z16);
+    xl = mfma_k32(abs, g == 0 ? bm : zero, z16);
+    xh = mfma_k32(abs, g == 1 ? bm : zero, z16);
+  }
+  // The exact integer parts of the super-block term: s1 = sum_j sc_j isum_j
+  // (isum over the codes q - 32), s2 = sum_j sc_j bsum_j.
+  struct Ints { v16i s1, s2; };
+  __device__ __forceinline__ static Ints ints(const Wt& w, int g, const uint8_t* qrow, const v4i abs) {
+    int S1[16];
+    v16i xl, xh;
+    raw(w, g, qrow, abs, S1, xl, xh);
+    Ints o;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      o.s2[r] = xl[r] + 64 * xh[r];
+      o.s1[r] = S1[r] - 32 * o.s2[r];
+    }
+    return o;
+  }
+  template <int NQ>
+  __device__ static void mac(const Wt& w, int g, const uint8_t* qrow, const v4i abs, const double* dxs,
+                             int n, double* acc) {
+    int S1[16];
+    v16i xl, xh;
+    raw(w, g, qrow, abs, S1, xl, xh);
     const double d = half_bits_to_float(w.d);
     MOEQ_COMBINE(acc[r] += dx * (d * (double)(S1[r] - 32 * (xl[r] + 64 * xh[r]))))
   }
@@ -316,15 +352,19 @@ template <> struct Mf<FQ80> {
     w.d = gld_u4(Wb + align256(nsb * 256) + rs.su * 16 + lr * 16u);
     return w;
   }
+  // The exact integer sum of 32-block b of the super-block: isum_b.
+  __device__ __forceinline__ static v16i block_ints(const Wt& w, int g, const uint8_t* qrow, int b) {
+    const v4i bq = {(int)w.q[b].x, (int)w.q[b].y, (int)w.q[b].z, (int)w.q[b].w};
+    const v16i z16 = {0};
+    return mfma_k32(lds_v4(qrow + 32 * b + 16 * g), bq, z16);
+  }
   template <int NQ>
   __device__ static void mac(const Wt& w, int g, const uint8_t* qrow, const v4i, const double* dxs,
                              int n, double* acc) {
     const uint32_t dw[4] = {w.d.x, w.d.y, w.d.z, w.d.w};
-    const v16i z16 = {0};
 #pragma unroll
     for (int b = 0; b < 8; ++b) {
-      const v4i bq = {(int)w.q[b].x, (int)w.q[b].y, (int)w.q[b].z, (int)w.q[b].w};
-      const v16i P = mfma_k32(lds_v4(qrow + 32 * b + 16 * g), bq, z16);
+      const v16i P = block_ints(w, g, qrow, b);
       const double db = half_bits_to_float(dw[b >> 1] >> (16 * (b & 1)));
       MOEQ_COMBINE(acc[r] += (dx * db) * (double)P[r])
     }
@@ -883,6 +923,78 @@ template <int FMT>
 __global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2, 8))) void k_mfma_hf_down(
     MfmaArgs a) {
   mfma_tile<FMT, 1, true, 8, 2, 8, true>(a);
+}
+
+// ------------------------------------------------------------ integer hook
+//
+// The exact integer parts of every super-block term, computed by the same
+// MFMA code the tiles run (Mf<F>::ints, Mf<Q8_0>::block_ints) on the same LDS
+// staging of the activation rows: for a packed matrix W [N, K] and n_x q8_K
+// rows, out[x][row][sb][0..7] holds (S1, S2, 0, 0, 0, 0, 0, 0) for Q4_K and
+// Q2_K (S1 = sum_j sc_j isum_j, S2 = sum_j m_j bsum_j), for Q6_K (S1 over the
+// codes q - 32, S2 = sum_j sc_j bsum_j), and the eight 32-block sums isum_b
+// for Q8_0.  Grid (ceil(n_x / 32), N / 256): 32 activation rows and 8 waves
+// of 32 weight rows per workgroup, one 256-block staged at a time.
+template <int FMT>
+__global__ __launch_bounds__(512) void k_mfma_ints(const uint8_t* __restrict__ W, int64_t N, int64_t K,
+                                                   const uint8_t* __restrict__ xq, int64_t n_x,
+                                                   int32_t* __restrict__ out) {
+  using M = Mf<FMT>;
+  __shared__ StageLds<32> S;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = lane_id(), g = lane >> 5;
+  const int64_t t0 = (int64_t)blockIdx.x * 32;
+  const int n = (int)((n_x - t0) < 32 ? (n_x - t0) : 32);
+  const int64_t nbK = K / 256;
+  const int64_t row = (int64_t)blockIdx.y * kMfRows + wave * 32 + (lane & 31);
+  const int ms = tid >> 4, piece = tid & 15;          // staging: tile row ms (0..31), 16-byte piece
+  const uint8_t* srow = ms < n ? xq + (t0 + ms) * nbK * kQ8KBytes : nullptr;
+  for (int64_t sb = 0; sb < nbK; ++sb) {
+    const StageRegs sr = stage_load<M::NBSP>(srow, sb, piece);
+    __syncthreads();                                  // the previous block's readers are done
+    stage_store<M::NBSP, 32>(S, sr, ms, piece);
+    __syncthreads();
+    const typename M::Wt w = M::load(W, N, nbK, row, sb, g);
+    const uint8_t* qrow = &S.qs[lane & 31][0];
+    int32_t* o = out + (t0 * N + row) * nbK * 8 + sb * 8;
+    const int64_t mstride = N * nbK * 8;
+    if constexpr (FMT == FQ80) {
+#pragma unroll
+      for (int b = 0; b < 8; ++b) {
+        const v16i P = M::block_ints(w, g, qrow, b);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int m = out_row(r, g);
+          if (m < n) o[m * mstride + b] = P[r];
+        }
+      }
+    } else {
+      const v4i abs = lds_v4(&S.bsp[lane & 31][g][0]);
+      const typename M::Ints I = M::ints(w, g, qrow, abs);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int m = out_row(r, g);
+        if (m < n) {
+          *reinterpret_cast<int4*>(o + m * mstride) = make_int4(I.s1[r], I.s2[r], 0, 0);
+          *reinterpret_cast<int4*>(o + m * mstride + 4) = make_int4(0, 0, 0, 0);
+        }
+      }
+    }
+  }
+}
+
+int launch_mfma_ints(int fmt, const void* W, int64_t N, int64_t K, const void* xq, int64_t n_x, int32_t* out,
+                     hipStream_t s) {
+  const dim3 grid((unsigned)((n_x + 31) / 32), (unsigned)(N / kMfRows));
+  const uint8_t* w8 = (const uint8_t*)W;
+  const uint8_t* x8 = (const uint8_t*)xq;
+  switch (fmt) {
+    case FQ4K: hipLaunchKernelGGL(k_mfma_ints<FQ4K>, grid, dim3(512), 0, s, w8, N, K, x8, n_x, out); break;
+    case FQ6K: hipLaunchKernelGGL(k_mfma_ints<FQ6K>, grid, dim3(512), 0, s, w8, N, K, x8, n_x, out); break;
+    case FQ2K: hipLaunchKernelGGL(k_mfma_ints<FQ2K>, grid, dim3(512), 0, s, w8, N, K, x8, n_x, out); break;
+    case FQ80: hipLaunchKernelGGL(k_mfma_ints<FQ80>, grid, dim3(512), 0, s, w8, N, K, x8, n_x, out); break;
+    default: return -2;
+  }
+  return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
 // Tile lists of the routed experts (one workgroup; see mfma_plan.hpp).

@@ -133,6 +133,9 @@ struct MfmaArgs {
 int launch_quantize_q8K(const float* x, int64_t rows, int64_t cols, void* out, hipStream_t s);
 int launch_pack(int fmt, const void* aos, int64_t n_mats, int64_t rows, int64_t cols, void* packed,
                 hipStream_t s);
+// Exact integer parts of the super-block terms by the MFMA tile code (test hook).
+int launch_mfma_ints(int fmt, const void* W, int64_t N, int64_t K, const void* xq, int64_t n_x, int32_t* out,
+                     hipStream_t s);
 int launch_subdots(int fmt, const void* w, int64_t rows, int64_t cols, const void* xq, int64_t n_x,
                    int32_t* out, hipStream_t s);
 size_t route_ws_bytes(int64_t T, int64_t E);

@@ -28,7 +28,7 @@ SUBBLOCK = {Q4_K: 32, Q6_K: 16, Q2_K: 16, Q8_0: 32}
 SYMBOLS = ["moeq_status_string", "moeq_quantize_q8K", "moeq_route_workspace", "moeq_route",
            "moeq_packed_bytes", "moeq_pack_experts", "moeq_expert_ffn_workspace", "moeq_expert_ffn",
            "moeq_moe_layer_workspace", "moeq_moe_layer", "moeq_ffn_h_view", "moeq_debug_subdots",
-           "moeq_moe_layer_noalloc"]
+           "moeq_moe_layer_noalloc", "moeq_debug_mfma_sums"]
 
 
 class MoeqError(RuntimeError):
@@ -108,8 +108,9 @@ def lib() -> ctypes.CDLL:
                                              vp, vp, vp, vp, vp, vp, vp]
         L.moeq_ffn_h_view.argtypes = [ctypes.POINTER(FfnDesc), vp, sz, ctypes.POINTER(vp), ctypes.POINTER(vp)]
         L.moeq_debug_subdots.argtypes = [i32, vp, i64, i64, vp, i64, vp, vp]
+        L.moeq_debug_mfma_sums.argtypes = [i32, vp, i64, i64, vp, i64, vp, vp]
         for s in ("moeq_quantize_q8K", "moeq_route", "moeq_pack_experts", "moeq_expert_ffn", "moeq_moe_layer",
-                  "moeq_ffn_h_view", "moeq_debug_subdots", "moeq_moe_layer_noalloc"):
+                  "moeq_ffn_h_view", "moeq_debug_subdots", "moeq_moe_layer_noalloc", "moeq_debug_mfma_sums"):
             getattr(L, s).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -272,6 +273,17 @@ def moeq_debug_subdots(fmt: int, packed_w: torch.Tensor, rows: int, cols: int, x
     out = torch.empty((n_x, rows, cols // SUBBLOCK[fmt]), dtype=torch.int32, device=packed_w.device)
     _check("moeq_debug_subdots", lib().moeq_debug_subdots(fmt, _ptr(packed_w), rows, cols, _ptr(x_q8K), n_x,
                                                           _ptr(out), _stream(stream)))
+    return out
+
+
+def moeq_debug_mfma_sums(fmt: int, packed_w: torch.Tensor, rows: int, cols: int, x_q8K: torch.Tensor,
+                         stream=None) -> torch.Tensor:
+    """int32 [n_x, rows, cols/256, 8]: the MFMA tiles' exact integer parts of
+    every super-block term (S1, S2 for the K-quants; the 32-block sums for Q8_0)."""
+    n_x = x_q8K.shape[0]
+    out = torch.empty((n_x, rows, cols // 256, 8), dtype=torch.int32, device=packed_w.device)
+    _check("moeq_debug_mfma_sums", lib().moeq_debug_mfma_sums(fmt, _ptr(packed_w), rows, cols, _ptr(x_q8K), n_x,
+                                                              _ptr(out), _stream(stream)))
     return out
 
 

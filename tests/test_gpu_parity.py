@@ -191,6 +191,95 @@ def test_subdots_bit_exact(fmt, rows, cols):
     assert np.array_equal(got.cpu().numpy(), oracle.subdots(fmt, W, rows, cols, xq))
 
 
+# ---------------------------------------------------------------- MFMA integer parts
+
+def _q8k_bsums(xq, cols):
+    """Block sums int64 [n, cols/256, 16] from q8_K bytes (i16 at byte 260 of a block)."""
+    b = np.ascontiguousarray(xq, np.uint8).reshape(xq.shape[0], cols // 256, 292)
+    return np.ascontiguousarray(b[:, :, 260:292]).view(np.int16).astype(np.int64)
+
+
+def oracle_sb_sums(fmt, W, rows, cols, xq):
+    """The super-block integer parts from the oracle's exact sub-block dots and
+    its decoded scales: (S1, S2, 0 ...) for the K-quants (Q6_K: S2 = sum_j sc_j
+    bsum_j), the eight 32-block sums for Q8_0; int64 [n, rows, cols/256, 8]."""
+    n, nsb = xq.shape[0], cols // 256
+    sd = oracle.subdots(fmt, W, rows, cols, xq).astype(np.int64)
+    out = np.zeros((n, rows, nsb, 8), np.int64)
+    if fmt == syn.Q8_0:
+        out[:] = sd.reshape(n, rows, nsb, 8)
+        return out
+    sc, m = oracle.scales_matrix(fmt, W, rows, cols)
+    nsub = sc.shape[2]
+    sd = sd.reshape(n, rows, nsb, nsub)
+    bs = _q8k_bsums(xq, cols)
+    if nsub == 8:                                       # 32-element sub-blocks: two 16-sums each
+        bs = bs.reshape(n, nsb, 8, 2).sum(-1)
+    out[..., 0] = (sd * sc[None].astype(np.int64)).sum(-1)
+    mul = sc if fmt == syn.Q6_K else m
+    out[..., 1] = (mul[None].astype(np.int64) * bs[:, None]).sum(-1)
+    return out
+
+
+@pytest.mark.parametrize("fmt", [moeq.Q4_K, moeq.Q6_K, moeq.Q2_K, moeq.Q8_0])
+@pytest.mark.parametrize("rows,cols,n_x", [(256, 256, 1), (512, 2304, 37), (256, 4096, 70)])
+def test_mfma_integer_parts_bit_exact(fmt, rows, cols, n_x):
+    """The MFMA tiles' exact integer parts (S1, S2 per super-block, or the
+    32-block sums of Q8_0) against the oracle's sub-block dots and scales:
+    ragged token tiles, extreme codes in row 0, extreme activations in x row 0."""
+    say("mfma integer parts", fmt, rows, cols, n_x)
+    rng = np.random.default_rng(fmt * 1000 + rows + n_x)
+    W = _extreme_blocks(fmt, rows, cols, rng)
+    x = rng.standard_normal((n_x, cols)).astype(np.float32)
+    x[0] = -127.0
+    xq = oracle.quantize_q8K(x)
+    packed = moeq.moeq_pack_experts(fmt, dev(W.reshape(-1)), 1, rows, cols)
+    got = moeq.moeq_debug_mfma_sums(fmt, packed, rows, cols, dev(xq))
+    torch.cuda.synchronize()
+    assert np.array_equal(got.cpu().numpy().astype(np.int64), oracle_sb_sums(fmt, W, rows, cols, xq))
+
+
+def test_mfma_integer_parts_prefill_sample():
+    """Prefill layer (8192 tokens): the MFMA integer parts of gate, up and down
+    for a seeded sample of 1024 routed (token, slot) pairs and 64 shared-expert
+    tokens, against the oracle.  Down takes the pair's q8_K(h) from the oracle."""
+    name = "prefill"
+    layer = layer_of(name)
+    cfg = layer.cfg
+    o = oracle_of(name)
+    say("mfma integer parts, prefill sample")
+    dl = moeq.DeviceLayer(layer)
+    ptr = {"gate": dl.gate_ptrs.cpu().numpy(), "up": dl.up_ptrs.cpu().numpy(), "down": dl.down_ptrs.cpu().numpy()}
+    rng = np.random.default_rng(1024)
+    flat = np.sort(rng.choice(cfg.T * cfg.k, 1024, replace=False))
+    toks, slots = flat // cfg.k, flat % cfg.k
+    experts = o["ids"][toks, slots]
+    nbF = cfg.F // 256 * 292
+    L = moeq.lib()
+
+    def check(fmt, wptr, W, rows, cols, xq, what):
+        xd = dev(xq)
+        out = torch.empty((xq.shape[0], rows, cols // 256, 8), dtype=torch.int32, device="cuda")
+        rc = L.moeq_debug_mfma_sums(fmt, int(wptr), rows, cols, xd.data_ptr(), xq.shape[0], out.data_ptr(), None)
+        assert rc == 0, rc
+        torch.cuda.synchronize()
+        assert np.array_equal(out.cpu().numpy().astype(np.int64), oracle_sb_sums(fmt, W, rows, cols, xq)), what
+
+    for e in np.unique(experts):
+        sel = experts == e
+        xq = o["xq"][toks[sel]]
+        hq = o["hq"][toks[sel], slots[sel], :nbF]
+        check(cfg.fmt_gate, ptr["gate"][e], layer.gate[e], cfg.F, cfg.H, xq, ("gate", e))
+        check(cfg.fmt_up, ptr["up"][e], layer.up[e], cfg.F, cfg.H, xq, ("up", e))
+        check(cfg.fmt_down, ptr["down"][e], layer.down[e], cfg.H, cfg.F, hq, ("down", e))
+    st = np.sort(rng.choice(cfg.T, 64, replace=False))
+    nbs = cfg.F_shared // 256 * 292
+    sg, su, sd = (p.data_ptr() for p in dl.sh)
+    check(cfg.sh_fmt_gate, sg, layer.sh_gate, cfg.F_shared, cfg.H, o["xq"][st], "shared gate")
+    check(cfg.sh_fmt_up, su, layer.sh_up, cfg.F_shared, cfg.H, o["xq"][st], "shared up")
+    check(cfg.sh_fmt_down, sd, layer.sh_down, cfg.H, cfg.F_shared, o["hq"][st, cfg.k, :nbs], "shared down")
+
+
 # ---------------------------------------------------------------- route
 
 def check_route(run, layer, sel):

@@ -95,6 +95,29 @@ def test_encode_decode_roundtrip_all_codes(fmt):
         assert list(q) == list(eq)
 
 
+@pytest.mark.parametrize("fmt", [Q4_K, Q2_K, Q6_K, Q8_0])
+def test_scales_matrix_returns_encoded_scales_and_mins(fmt):
+    """Every block's decoded sub-block scales and mins, for a matrix built by
+    the independent encoder from known codes."""
+    rng = np.random.default_rng(11 + fmt)
+    blocks = _all_values_blocks(fmt, rng)
+    rows = 2
+    per_row = len(blocks) // rows
+    bb = syn.BLOCK_BYTES[fmt]
+    W = pack_row(fmt, blocks[:rows * per_row]).reshape(rows, per_row * bb)
+    cols = per_row * syn.BLOCK_WEIGHTS[fmt]
+    sc, m = oracle.scales_matrix(fmt, W, rows, cols)
+    for n, args in enumerate(blocks[:rows * per_row]):
+        r, b = divmod(n, per_row)
+        if fmt in (Q4_K, Q2_K):
+            esc, em = args[2], args[3]
+        elif fmt == Q6_K:
+            esc, em = args[1], [0] * 16
+        else:
+            esc, em = [1], [0]
+        assert list(sc[r, b]) == list(esc) and list(m[r, b]) == list(em), (fmt, r, b)
+
+
 # ---------------------------------------------------------------------- q8_K
 
 def _q8k_fields(b):
