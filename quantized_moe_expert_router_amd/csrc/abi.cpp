@@ -327,7 +327,7 @@ int ffn_enqueue(const moeq_ffn_desc* d, const void* x_q8K, const int32_t* topk_i
     return fg != FQ6K && fd != FQ6K && d->H / 256 <= kHfMaxBlocks && Fx / 256 <= kHfMaxBlocks &&
            tiles * (Fx / 256) < kHfMaxWorkgroups;
   };
-  auto mfma_launch = [&](int mode, bool shared_exp, bool thin, hipStream_t st) -> int {
+  auto mfma_launch = [&](int mode, bool shared_exp, bool thin, hipStream_t st, bool fold = false) -> int {
     const bool hf = thin && hf_ok(shared_exp);
     MfmaArgs a{};
     a.shared = shared_exp ? 1 : 0;
@@ -336,6 +336,8 @@ int ffn_enqueue(const moeq_ffn_desc* d, const void* x_q8K, const int32_t* topk_i
     a.pairs = pairs; a.k = d->k; a.T = d->T;
     a.topk_w = topk_w; a.shared_scale = shared_scale;
     a.yp = (float*)(wsb + L.off_yp);
+    a.y = fold ? y : nullptr;
+    a.accumulate = d->accumulate;
     const int64_t Fx = shared_exp ? d->F_shared : d->F;
     const int64_t hq_stride = (Fx / 256) * kQ8KBytes;
     uint8_t* hq = shared_exp ? wsb + L.off_hqs : wsb + L.off_hq;
@@ -343,7 +345,10 @@ int ffn_enqueue(const moeq_ffn_desc* d, const void* x_q8K, const int32_t* topk_i
     a.hf_stride = L.Fmax;
     int fmt;
     const int tm = thin ? kThinT : 32;
-    unsigned gx = shared_exp ? (unsigned)((d->T + tm - 1) / tm) : (unsigned)(thin ? L.max_thin : L.max_tiles);
+    // routed 32-row tiles: a multiple of 8 workgroups at least as many as the
+    // tiles (the kernels map workgroups to tiles XCD by XCD)
+    unsigned gx = shared_exp ? (unsigned)((d->T + tm - 1) / tm)
+                             : (unsigned)(thin ? L.max_thin : (L.max_tiles + 7) / 8 * 8);
     unsigned gy;
     a.gate = d->gate; a.up = d->up; a.down = d->down;
     if (mode == 0) {
@@ -394,9 +399,14 @@ int ffn_enqueue(const moeq_ffn_desc* d, const void* x_q8K, const int32_t* topk_i
     if (!sh || (gemv && same_shape)) return 0;
     return mfma ? mfma_launch(0, true, d->T <= kThinT, ss) : gateup(kModeShared, d->sh_fmt_gate, d->F_shared, 1, ss);
   };
+  // A shared expert on the MFMA path (32-row tiles) that runs after the
+  // routed down launches on the same stream also does the combine (no
+  // k_combine launch).
+  const bool fold_combine = sh && mfma && !gemv && ss == s && d->T > kThinT;
   auto shared_down = [&]() -> int {
     if (!sh || (gemv && same_shape)) return 0;
-    return mfma ? mfma_launch(1, true, d->T <= kThinT, ss) : down(kModeShared, d->sh_fmt_down, d->F_shared, 1, ss);
+    return mfma ? mfma_launch(1, true, d->T <= kThinT, ss, fold_combine)
+                : down(kModeShared, d->sh_fmt_down, d->F_shared, 1, ss);
   };
   if (ss != s && (rc = shared_gateup())) return rc;
   if (gemv) {
@@ -434,6 +444,7 @@ int ffn_enqueue(const moeq_ffn_desc* d, const void* x_q8K, const int32_t* topk_i
   }
   if (ss == s && (rc = shared_down())) return rc;
   if (ss != s && (rc = join_aux(d, s))) return rc;
+  if (fold_combine) return 0;
   return launch_combine((const float*)(wsb + L.off_yp), d->T, d->H, d->k, sh ? 1 : 0, y, d->accumulate, s);
 }
 

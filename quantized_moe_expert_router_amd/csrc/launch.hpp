@@ -128,6 +128,8 @@ struct MfmaArgs {
   const float* topk_w;
   const float* shared_scale;
   float* yp;                    // mode 1: fp32 [T*k + T, H]
+  float* y;                     // shared mode 1 only: not null = the tiles also do the combine
+  int accumulate;               //   into y (y = or += the token's summed rows)
 };
 
 int launch_quantize_q8K(const float* x, int64_t rows, int64_t cols, void* out, hipStream_t s);
