@@ -9,9 +9,13 @@ gate/up dequant-dot, SwiGLU, q8_K(h), down dequant-dot, weighted combine with
 the shared expert) over one token.  Steps cycle through `--layers` distinct
 synthetic layers resident in HBM, so, as in a real decoder stack, a step's
 weights were last touched many steps earlier and stream from HBM rather than
-from the 256 MB Infinity Cache.  The layers are captured as HIP graphs (per-layer
-graphs as in the Strata summary's execution paragraph, and one graph for the
-whole cycle, the way a decode step runs the stack) and replayed.
+from the 256 MB Infinity Cache.  The timed steps are one moeq_moe_stack call
+(the MoE blocks of a decode step on a pre-norm residual stream: each layer
+routes and runs on the RMS norm of the stream and adds its output to it, so
+every layer's routing follows from the previous layers' outputs) captured as
+a HIP graph and replayed; the same steps as single-layer calls on fixed
+inputs, and as one single-layer graph each (per Strata summary's execution
+paragraph), are reported beside it.
 
 Output: one JSON line (metric, value = MoE-layer tokens/s, roofline of the
 expert FFN, cpu_baseline = the CPU oracle on the host cores), with the 4-token
@@ -186,6 +190,9 @@ class LayerCycle:
         rng = np.random.default_rng(7)
         self.xs = [torch.from_numpy(rng.standard_normal((T, cfg.H)).astype(np.float32)).to(device)
                    for _ in range(L)]
+        # RMS-norm gains of the stack's layers (around one)
+        self.norm_w = [torch.from_numpy((1.0 + 0.1 * rng.standard_normal(cfg.H)).astype(np.float32)).to(device)
+                       for _ in range(L)]
         self.route_out = moeq.RouteOut(T, cfg.E, cfg.k, device)
         self.y = torch.empty((T, cfg.H), dtype=torch.float32, device=device)
         self.rdesc = moeq.RouteDesc(T, cfg.H, cfg.E, cfg.k, cfg.gating, 1.0)
@@ -227,6 +234,47 @@ class LayerCycle:
         torch.cuda.synchronize()
         dt = time.perf_counter() - t0
         del gw, gt
+        return dt, wsteps
+
+    def capture_stack(self, first, n, y, out, ws):
+        """One graph of one stack call over n layers (first, first+1, ... mod L)
+        on the residual stream y (y = x, then y += MoE_l(RMSNorm_l(y)) per
+        layer)."""
+        import torch
+        from quantized_moe_expert_router_amd import moeq
+        idx = [(first + i) % self.L for i in range(n)]
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(self.stream):
+            with torch.cuda.graph(g, stream=self.stream):
+                moeq.moeq_moe_stack(self.rdesc, [self.layers[l]["desc"] for l in idx],
+                                    [self.layers[l]["w_router"] for l in idx], [self.layers[l]["bias"] for l in idx],
+                                    self.xs[first], out, y, ws, self.stream,
+                                    norm_ws=[self.norm_w[l] for l in idx], norm_eps=NORM_EPS)
+        return g
+
+    def time_stack(self, steps, warmup):
+        """The decode step as one stack call (moeq_moe_stack) of exactly
+        `steps` layers, after a warm-up stack of max(warmup, L) layers."""
+        import torch
+        from quantized_moe_expert_router_amd import moeq
+        wsteps = max(warmup, self.L)
+        n = max(wsteps, steps)
+        y = torch.empty_like(self.xs[0])
+        out = moeq.StackOut(n, self.T, self.cfg.E, self.cfg.k, y.device)
+        descs = [self.layers[i % self.L]["desc"] for i in range(min(n, self.L))]
+        ws = torch.empty(moeq.moeq_moe_stack_workspace(self.rdesc, descs), dtype=torch.uint8, device=y.device)
+        gw = self.capture_stack(0, wsteps, y, out, ws)
+        gt = self.capture_stack(wsteps % self.L, steps, y, out, ws)
+        torch.cuda.synchronize()
+        gw.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        gt.replay()
+        torch.cuda.synchronize()
+        dt = time.perf_counter() - t0
+        del gw, gt
+        if not bool(torch.isfinite(y).all()):
+            raise RuntimeError("the residual stream is not finite after the timed stack")
         return dt, wsteps
 
     def time_per_layer_graphs(self, steps, warmup):
@@ -280,6 +328,7 @@ def ffn_event_us(cyc, n_ev):
 
 
 INT8_PEAK_TOPS = 5000.0
+NORM_EPS = 1e-6
 
 
 def layer_bytes_of(cfg, union):
@@ -420,11 +469,14 @@ def main():
     cyc = LayerCycle(cfg, 1, L, dev)
     setup_s = time.time() - t_setup
 
-    # ---- timed region: one graph of exactly `steps` whole layers (value)
-    dt, wsteps = cyc.time(args.steps, args.warmup)
+    # ---- timed region: the decode step as one stack call of exactly `steps`
+    # layers on the residual stream (value)
+    dt, wsteps = cyc.time_stack(args.steps, args.warmup)
     ms_per_step = dt * 1e3 / args.steps
     tokens_per_s = args.steps / dt
-    # ---- secondary: the same steps as one single-layer graph launch each
+    # ---- secondaries: the same steps as single-layer calls in one graph, and
+    # as one single-layer graph launch each
+    dt_lc, _ = cyc.time(args.steps, args.warmup)
     dt_pl = cyc.time_per_layer_graphs(args.steps, args.warmup)
 
     # ---- expert FFN launches timed with HIP events on their stream
@@ -475,9 +527,13 @@ def main():
         "config": {"workload": cfg.name, "T": 1, "H": cfg.H, "E": cfg.E, "k": cfg.k, "F": cfg.F,
                    "shared_F": cfg.F_shared, "gate_up": "Q4_K", "down": "Q6_K", "layers_cycled": L,
                    "layer_bytes": layer_bytes, "parallelism": "single GPU",
-                   "timing": "one HIP graph of exactly `steps` layer steps cycling the layers, after a warm-up "
-                             "graph of %d layer steps (at least one whole cycle)" % wsteps},
+                   "timing": "one HIP graph of one moeq_moe_stack call over exactly `steps` layers cycling the "
+                             "layers on a pre-norm residual stream, after a warm-up stack of %d layers (at least "
+                             "one whole cycle)" % wsteps},
         "layer_hbm_gbs": layer_bytes / (ms_per_step * 1e-3) / 1e9,
+        "layer_calls_graph": {"tokens_per_s": args.steps / dt_lc, "ms_per_step": dt_lc * 1e3 / args.steps,
+                              "note": "the same layer steps as moeq_moe_layer calls on fixed per-layer inputs "
+                                      "in one graph"},
         "per_layer_graphs": {"tokens_per_s": args.steps / dt_pl, "ms_per_step": dt_pl * 1e3 / args.steps,
                              "note": "the same layer steps, one single-layer graph launch each"},
         "roofline": {"bound": "hbm", "kernel": "expert FFN (gate/up GEMV + down GEMV)",

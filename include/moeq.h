@@ -250,6 +250,58 @@ int moeq_moe_layer(const moeq_route_desc* r, const moeq_ffn_desc* f, const float
                    size_t ws_bytes, void* stream);
 
 /*
+ * RMS pre-norm of T token rows: out[t, i] = fl32((x[t, i] * r_t) * gamma[i]),
+ * r_t = 1 / sqrt(mean_i(x[t, i]^2) + eps), everything before the final
+ * rounding in fp64 (the squares are exact; only the order of the sum's
+ * additions is the kernel's).  This is the input normalisation of the
+ * pre-norm decoder blocks of the MoE models the engines run (Pulsar README
+ * and Strata summary: whole Qwen and DeepSeek-style models); the pages give
+ * the models, not this step, so its precision is this library's choice.  It
+ * is the glue between the MoE layers of moeq_moe_stack, exported so a caller
+ * can form the same layer input.
+ *   x, out  fp32 [T, H], 16-byte aligned; out may equal x (in place)
+ *   gamma   fp32 [H], 16-byte aligned, or NULL (all ones)
+ *   eps     finite, >= 0
+ * H a positive multiple of 256; T == 0 is a no-op.  Errors: MOEQ_E_INVALID.
+ */
+int moeq_rms_norm(const float* x, int64_t T, int64_t H, const float* gamma, float eps, float* out, void* stream);
+
+/*
+ * A stack of L MoE layers over the same T tokens on a pre-norm residual
+ * stream: y = x, then for l = 0 .. L-1, y += MoE_l(RMSNorm_l(y)).  These are
+ * the MoE blocks of a decode step run one after the other; the attention
+ * blocks between them belong to the model around this path, and per-layer
+ * launches are captured as one graph (Strata summary, execution paragraph).
+ * Layer l is exactly moeq_rms_norm(y, T, H, norm_w[l], norm_eps, xn) then
+ * moeq_moe_layer(r, f[l] with accumulate = 1, xn, w_router[l], bias[l], NULL
+ * logits, ..., y), with its routing outputs at offset l of each output array,
+ * and its results are bit-identical to those two calls.  For one token (H <=
+ * 4096, decode GEMV path) the norm is fused into the router launch: no
+ * normalised copy is written and the layer stays three kernels.  Without the
+ * norm, a chain of SwiGLU experts (quadratic in their input's scale) grows
+ * without bound.
+ *   f            host array [L] of FFN descriptors; every one agrees with r
+ *                on T, H, E, k and has accumulate == 0 (the stack accumulates)
+ *   w_router     host array [L] of device pointers fp32 [E, H] (16-byte aligned)
+ *   bias         host array [L] of device pointers fp32 [E] (entries may be NULL) or NULL
+ *   norm_w       host array [L] of device pointers fp32 [H] (16-byte aligned;
+ *                entries may be NULL = all ones) or NULL
+ *   norm_eps     finite, >= 0
+ *   shared_scale host array [L] of device pointers fp32 [T] (entries may be NULL) or NULL
+ *   x, y         fp32 [T, H], 16-byte aligned; y may equal x (in place)
+ *   topk_ids, topk_w [L, T, k]; expert_offsets [L, E+1];
+ *   pairs [L, max(1, T*k)]; active [L, 1 + min(E, T*k)]
+ * ws: moeq_moe_stack_workspace bytes (the largest layer workspace and room
+ * for the normalised rows), 256-byte aligned.  1 <= L <= 4096.  Errors as
+ * moeq_moe_layer.
+ */
+size_t moeq_moe_stack_workspace(const moeq_route_desc* r, const moeq_ffn_desc* f, int64_t L);
+int moeq_moe_stack(const moeq_route_desc* r, const moeq_ffn_desc* f, int64_t L, const float* const* w_router,
+                   const float* const* bias, const float* const* norm_w, float norm_eps, const float* x,
+                   int32_t* topk_ids, float* topk_w, int32_t* expert_offsets, int32_t* pairs, int32_t* active,
+                   const float* const* shared_scale, float* y, void* ws, size_t ws_bytes, void* stream);
+
+/*
  * moeq_moe_layer without a workspace argument, for callers that cannot
  * allocate device memory (code under HIP graph capture, tight serving loops,
  * harnesses that forbid hipMalloc).  Same arguments, outputs and results as

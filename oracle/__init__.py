@@ -50,6 +50,8 @@ def lib():
         L.orc_quantize_q8K.restype = None
         L.orc_dequant_q8K_row.argtypes = [vp, i64, vp]
         L.orc_dequant_q8K_row.restype = None
+        L.orc_rms_norm.argtypes = [vp, i64, i64, vp, dbl, vp]
+        L.orc_rms_norm.restype = None
         L.orc_route.argtypes = [i64, i64, i64, i32, i32, dbl, vp, vp, vp, vp, vp, vp]
         L.orc_lists.argtypes = [i64, i32, i64, vp, vp, vp, vp]
         L.orc_lists.restype = None
@@ -119,6 +121,20 @@ def quantize_q8K(x: np.ndarray) -> np.ndarray:
         raise ValueError("cols % 256")
     out = np.zeros((rows, cols // 256 * 292), np.uint8)
     lib().orc_quantize_q8K(_p(x), rows, cols, _p(out))
+    return out
+
+
+def rms_norm(x: np.ndarray, gamma: Optional[np.ndarray], eps: float) -> np.ndarray:
+    """RMS pre-norm of the rows of fp32 x [rows, cols]: fl32((x * r) * gamma),
+    r = 1 / sqrt(mean(x^2) + eps) in fp64 (the input of each MoE block of a
+    pre-norm residual stack)."""
+    x = _c(x, np.float32)
+    if x.ndim == 1:
+        x = x[None]
+    rows, cols = x.shape
+    g = None if gamma is None else _c(gamma, np.float32).reshape(cols)
+    out = np.zeros((rows, cols), np.float32)
+    lib().orc_rms_norm(_p(x), rows, cols, _p(g), float(eps), _p(out))
     return out
 
 

@@ -6,6 +6,7 @@
  * header, table or constant with the HIP library and never calls it.
  *
  * What it computes (one MoE layer, per token t):
+ *   (stack)        x = RMSNorm(y) of the residual stream y, then y += MoE(x)
  *   router logits  l[t,e] = sum_i Wr[e,i] * x[t,i] (+ b[e])         fp64
  *       (the router runs per layer on the resident input: Pulsar README,
  *        'How the streaming works'; the router stays in VRAM: Strata summary,
@@ -214,6 +215,29 @@ int orc_dequant_row(int fmt, const uint8_t* row, int64_t cols, double* out)
         if (dequant_block(fmt, row + b * bb, out + b * bw))
             return -1;
     return 0;
+}
+
+/* ------------------------------------------------------------------ pre-norm */
+
+/*
+ * RMS pre-norm of each row (the input of a pre-norm decoder's MoE block in a
+ * stack of layers; the pages run whole models of such blocks but do not
+ * spell this step out, so the precision is a reading):
+ *   r = 1 / sqrt(mean_i x_i^2 + eps), sequential fp64 sum of the squares;
+ *   out_i = fl32((x_i * r) * g_i), both products in fp64 (g NULL: g_i = 1).
+ */
+void orc_rms_norm(const float* x, int64_t rows, int64_t cols, const float* g, double eps, float* out)
+{
+    int64_t t, i;
+    for (t = 0; t < rows; t++) {
+        const float* xr = x + t * cols;
+        double ss = 0.0, r;
+        for (i = 0; i < cols; i++)
+            ss += (double)xr[i] * (double)xr[i];
+        r = 1.0 / sqrt(ss / (double)cols + eps);
+        for (i = 0; i < cols; i++)
+            out[t * cols + i] = (float)(((double)xr[i] * r) * (g ? (double)g[i] : 1.0));
+    }
 }
 
 /* ------------------------------------------------------------------ q8_K */

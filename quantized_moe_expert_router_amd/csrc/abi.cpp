@@ -1,6 +1,7 @@
 // C ABI of libmoeq: argument validation on the host, workspace layout, and
 // kernel dispatch.  Every check runs before anything is enqueued.
 #include <algorithm>
+#include <cfloat>
 #include <climits>
 
 #include "../../include/moeq.h"
@@ -15,6 +16,7 @@ namespace {
 constexpr int64_t kMaxE = 4096;
 static_assert(kMaxE <= kPlanMaxE, "the tile planner's LDS scratch holds kPlanMaxE + 1 entries");
 constexpr int kMaxK = 32;
+constexpr int64_t kMaxStack = 4096;   // layers per moeq_moe_stack call
 constexpr int kRowBlock = 64;     // rows per expert-major down work item
 
 bool fmt_ok(int f) { return f == MOEQ_Q4_K || f == MOEQ_Q6_K || f == MOEQ_Q2_K || f == MOEQ_Q8_0; }
@@ -492,6 +494,55 @@ size_t moeq_moe_layer_workspace(const moeq_route_desc* r, const moeq_ffn_desc* f
   return layer_layout(r, f).total;
 }
 
+namespace {
+// RMS pre-norm of the layer's input (a stack of layers): gains g (null: all
+// ones), eps; xn: room for the normalised rows [T, H] when they are written.
+struct NormIn {
+  const float* g;
+  double eps;
+  float* xn;
+};
+
+// Enqueue one whole layer (arguments already checked); with nrm, the layer's
+// input is the RMS pre-norm of x (fused into the router launch for one token).
+int layer_enqueue(const moeq_route_desc* r, const moeq_ffn_desc* f, const float* x, const float* w_router,
+                  const float* bias, double* logits, int32_t* topk_ids, float* topk_w, int32_t* expert_offsets,
+                  int32_t* pairs, int32_t* active, const float* shared_scale, float* y, uint8_t* wsb,
+                  hipStream_t s, const NormIn* nrm = nullptr) {
+  int rc;
+  const LayerLayout L = layer_layout(r, f);
+  void* xq = wsb + L.off_xq;
+  const bool one = r->T == 1 && gemv_max_of(f) >= 1;
+  if (nrm != nullptr && !(one && r->H <= kNorm1MaxH)) {
+    if ((rc = launch_rms_norm(x, r->T, r->H, nrm->g, nrm->eps, nrm->xn, s))) return hip_status(rc);
+    x = nrm->xn;
+    nrm = nullptr;
+  }
+  if (one) {
+    // one token: logits + q8_K(x) in one launch, then gate/up routes inline
+    double* lg = logits ? logits : (double*)(wsb + L.off_route);
+    rc = nrm ? launch_logits_norm1(r->H, r->E, x, nrm->g, nrm->eps, w_router, bias, lg, xq, s)
+             : launch_logits(1, r->H, r->E, x, w_router, bias, lg, xq, s);
+    if (rc) return hip_status(rc);
+    InlineRoute ir{lg, r->gating, r->scale, topk_ids, expert_offsets, pairs, active, topk_w};
+    return hip_status(ffn_enqueue(f, xq, topk_ids, topk_w, expert_offsets, pairs, active, shared_scale, y, wsb, &ir,
+                                  false, s));
+  }
+  // the routing kernel also builds the MFMA tile lists of the FFN (one launch fewer)
+  const FfnLayout FL = ffn_layout(f);
+  const int thr = gemv_max_of(f);
+  const bool mfma = f->T > thr;
+  const MfmaPlan plan{thr, (int)FL.max_tiles, (int4*)(wsb + L.off_ffn + FL.off_tiles),
+                      (int32_t*)(wsb + L.off_ffn + FL.off_count), (int4*)(wsb + L.off_ffn + FL.off_thin),
+                      (int32_t*)(wsb + L.off_ffn + FL.off_count) + 1};
+  if ((rc = launch_route(r->T, r->H, r->E, r->k, r->gating, r->scale, x, w_router, bias, logits, topk_ids, topk_w,
+                         expert_offsets, pairs, active, xq, wsb + L.off_route, s, mfma ? &plan : nullptr)))
+    return hip_status(rc);
+  return hip_status(ffn_enqueue(f, xq, topk_ids, topk_w, expert_offsets, pairs, active, shared_scale, y, wsb,
+                                nullptr, mfma, s));
+}
+}  // namespace
+
 int moeq_moe_layer(const moeq_route_desc* r, const moeq_ffn_desc* f, const float* x, const float* w_router,
                    const float* bias, double* logits, int32_t* topk_ids, float* topk_w, int32_t* expert_offsets,
                    int32_t* pairs, int32_t* active, const float* shared_scale, float* y, void* ws,
@@ -509,31 +560,90 @@ int moeq_moe_layer(const moeq_route_desc* r, const moeq_ffn_desc* f, const float
     return MOEQ_E_INVALID;
   if (logits && !aligned(logits, 8)) return MOEQ_E_INVALID;
   if (!ws || !aligned(ws, 256)) return MOEQ_E_INVALID;
-  const LayerLayout L = layer_layout(r, f);
-  if (ws_bytes < L.total) return MOEQ_E_WORKSPACE;
-  uint8_t* wsb = (uint8_t*)ws;
-  hipStream_t s = (hipStream_t)stream;
-  void* xq = wsb + L.off_xq;
-  if (r->T == 1 && gemv_max_of(f) >= 1) {
-    // one token: logits + q8_K(x) in one launch, then gate/up routes inline
-    double* lg = logits ? logits : (double*)(wsb + L.off_route);
-    if ((rc = launch_logits(1, r->H, r->E, x, w_router, bias, lg, xq, s))) return hip_status(rc);
-    InlineRoute ir{lg, r->gating, r->scale, topk_ids, expert_offsets, pairs, active, topk_w};
-    return hip_status(ffn_enqueue(f, xq, topk_ids, topk_w, expert_offsets, pairs, active, shared_scale, y, wsb, &ir,
-                                  false, s));
+  if (ws_bytes < layer_layout(r, f).total) return MOEQ_E_WORKSPACE;
+  return layer_enqueue(r, f, x, w_router, bias, logits, topk_ids, topk_w, expert_offsets, pairs, active, shared_scale,
+                       y, (uint8_t*)ws, (hipStream_t)stream);
+}
+
+namespace {
+// Workspace of a stack: the largest layer workspace (the layers run one after
+// the other on one stream), then the normalised input rows [T, H].
+struct StackLayout {
+  size_t off_xn, total;
+};
+StackLayout stack_layout(const moeq_route_desc* r, const moeq_ffn_desc* f, int64_t L) {
+  size_t b = 0;
+  for (int64_t l = 0; l < L; ++l) b = std::max(b, layer_layout(r, &f[l]).total);
+  return StackLayout{b, b + align256((size_t)r->T * r->H * sizeof(float))};
+}
+int check_stack(const moeq_route_desc* r, const moeq_ffn_desc* f, int64_t L) {
+  if (!r || !f || L < 1 || L > kMaxStack) return MOEQ_E_INVALID;
+  for (int64_t l = 0; l < L; ++l) {
+    const int rc = check_layer(r, &f[l]);
+    if (rc != MOEQ_OK) return rc;
+    if (f[l].accumulate != 0) return MOEQ_E_INVALID;
   }
-  // the routing kernel also builds the MFMA tile lists of the FFN (one launch fewer)
-  const FfnLayout FL = ffn_layout(f);
-  const int thr = gemv_max_of(f);
-  const bool mfma = f->T > thr;
-  const MfmaPlan plan{thr, (int)FL.max_tiles, (int4*)(wsb + L.off_ffn + FL.off_tiles),
-                      (int32_t*)(wsb + L.off_ffn + FL.off_count), (int4*)(wsb + L.off_ffn + FL.off_thin),
-                      (int32_t*)(wsb + L.off_ffn + FL.off_count) + 1};
-  if ((rc = launch_route(r->T, r->H, r->E, r->k, r->gating, r->scale, x, w_router, bias, logits, topk_ids, topk_w,
-                         expert_offsets, pairs, active, xq, wsb + L.off_route, s, mfma ? &plan : nullptr)))
-    return hip_status(rc);
-  return hip_status(ffn_enqueue(f, xq, topk_ids, topk_w, expert_offsets, pairs, active, shared_scale, y, wsb,
-                                nullptr, mfma, s));
+  return MOEQ_OK;
+}
+bool eps_ok(float eps) { return eps >= 0.0f && eps <= FLT_MAX; }   // finite, not negative (NaN fails)
+}  // namespace
+
+int moeq_rms_norm(const float* x, int64_t T, int64_t H, const float* gamma, float eps, float* out, void* stream) {
+  if (T < 0 || H <= 0 || H % 256 != 0 || !eps_ok(eps)) return MOEQ_E_INVALID;
+  if (T == 0) return MOEQ_OK;
+  if (!x || !out || !aligned(x, 16) || !aligned(out, 16) || (gamma && !aligned(gamma, 16))) return MOEQ_E_INVALID;
+  return hip_status(launch_rms_norm(x, T, H, gamma, (double)eps, out, (hipStream_t)stream));
+}
+
+size_t moeq_moe_stack_workspace(const moeq_route_desc* r, const moeq_ffn_desc* f, int64_t L) {
+  if (check_stack(r, f, L) != MOEQ_OK) return 0;
+  return stack_layout(r, f, L).total;
+}
+
+int moeq_moe_stack(const moeq_route_desc* r, const moeq_ffn_desc* f, int64_t L, const float* const* w_router,
+                   const float* const* bias, const float* const* norm_w, float norm_eps, const float* x,
+                   int32_t* topk_ids, float* topk_w, int32_t* expert_offsets, int32_t* pairs, int32_t* active,
+                   const float* const* shared_scale, float* y, void* ws, size_t ws_bytes, void* stream) {
+  int rc = check_stack(r, f, L);
+  if (rc != MOEQ_OK) return rc;
+  if (!w_router || !expert_offsets || !active || !eps_ok(norm_eps)) return MOEQ_E_INVALID;
+  const int64_t T = r->T, k = r->k, E = r->E;
+  const int64_t n_pairs = std::max<int64_t>(1, T * k), n_active = 1 + std::min<int64_t>(E, T * k);
+  hipStream_t s = (hipStream_t)stream;
+  if (T == 0) {
+    for (int64_t l = 0; l < L; ++l)
+      if ((rc = hip_status(launch_route(0, r->H, E, r->k, r->gating, r->scale, nullptr, nullptr, nullptr, nullptr,
+                                        nullptr, nullptr, expert_offsets + l * (E + 1), nullptr,
+                                        active + l * n_active, nullptr, nullptr, s))))
+        return rc;
+    return MOEQ_OK;
+  }
+  if (!x || !topk_ids || !topk_w || !pairs || !y) return MOEQ_E_INVALID;
+  if (!aligned(x, 16) || !aligned(y, 16)) return MOEQ_E_INVALID;
+  for (int64_t l = 0; l < L; ++l) {
+    if (!w_router[l] || !aligned(w_router[l], 16)) return MOEQ_E_INVALID;
+    if (bias && bias[l] && !aligned(bias[l], 4)) return MOEQ_E_INVALID;
+    if (norm_w && norm_w[l] && !aligned(norm_w[l], 16)) return MOEQ_E_INVALID;
+  }
+  if (!ws || !aligned(ws, 256)) return MOEQ_E_INVALID;
+  const StackLayout SL = stack_layout(r, f, L);
+  if (ws_bytes < SL.total) return MOEQ_E_WORKSPACE;
+  // the residual stream: y = x, then every layer reads y and adds its output
+  // to y (in place: a layer has consumed its input in its first launch, and
+  // writes y only in its last)
+  if (x != y && hipMemcpyAsync(y, x, (size_t)T * r->H * sizeof(float), hipMemcpyDeviceToDevice, s) != hipSuccess)
+    return MOEQ_E_HIP;
+  uint8_t* wsb = (uint8_t*)ws;
+  for (int64_t l = 0; l < L; ++l) {
+    moeq_ffn_desc fl = f[l];
+    fl.accumulate = 1;
+    const NormIn nrm{norm_w ? norm_w[l] : nullptr, (double)norm_eps, (float*)(wsb + SL.off_xn)};
+    if ((rc = layer_enqueue(r, &fl, y, w_router[l], bias ? bias[l] : nullptr, nullptr, topk_ids + l * T * k,
+                            topk_w + l * T * k, expert_offsets + l * (E + 1), pairs + l * n_pairs,
+                            active + l * n_active, shared_scale ? shared_scale[l] : nullptr, y, wsb, s, &nrm)))
+      return rc;
+  }
+  return MOEQ_OK;
 }
 
 int moeq_ffn_h_view(const moeq_ffn_desc* d, void* ws, size_t ws_bytes, void** hq_routed, void** hq_shared) {

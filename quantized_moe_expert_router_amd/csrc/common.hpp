@@ -193,20 +193,14 @@ __device__ __forceinline__ int q8_code(float x, float id) {
   return (int)v;
 }
 
-// q8_K of 256-block g of a row-major fp32 matrix with `cols` columns, by one
-// wave (4 elements per lane), identical to the definition: amax, then
-// id = 127/amax (correctly rounded), q = rint(x*id) clamped to +-127,
-// d = amax/127, per-16 sums; amax == 0 or an infinite id gives a zero block.
-__device__ __forceinline__ void quantize_block_wave(const float* __restrict__ x, int64_t cols, int64_t g,
-                                                    int64_t nblocks, uint8_t* __restrict__ out) {
-  if (g >= nblocks) return;
+// q8_K of one 256-block held by one wave (4 consecutive elements per lane),
+// identical to the definition: amax, then id = 127/amax (correctly rounded),
+// q = rint(x*id) clamped to +-127, d = amax/127, per-16 sums; amax == 0 or
+// an infinite id gives a zero block.
+__device__ __forceinline__ void quantize_block_vals(float4 v, uint8_t* __restrict__ o) {
   const int lane = lane_id();
-  const int64_t nb = cols / 256, row = g / nb, b = g % nb;
-  const float* xb = x + row * cols + b * 256 + 4 * lane;
-  const float4 v = gld_f4(xb);
   float amax = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
   amax = wave_max_f(amax);
-  uint8_t* o = out + g * kQ8KBytes;
   const float id = amax == 0.0f ? 0.0f : __fdiv_rn(127.0f, amax);
   const bool zero = amax == 0.0f || __builtin_isinf(id);
   int q0 = 0, q1 = 0, q2 = 0, q3 = 0;
@@ -218,6 +212,54 @@ __device__ __forceinline__ void quantize_block_wave(const float* __restrict__ x,
   s += dpp_all_i<kDppXor2>(s);
   if ((lane & 3) == 0) gst_i16(o + 260 + 2 * (lane >> 2), (int16_t)s);
   if (lane == 0) gst_f32(o, zero ? 0.0f : __fdiv_rn(amax, 127.0f));
+}
+
+// q8_K of 256-block g of a row-major fp32 matrix with `cols` columns, by one
+// wave.
+__device__ __forceinline__ void quantize_block_wave(const float* __restrict__ x, int64_t cols, int64_t g,
+                                                    int64_t nblocks, uint8_t* __restrict__ out) {
+  if (g >= nblocks) return;
+  const int64_t nb = cols / 256, row = g / nb, b = g % nb;
+  quantize_block_vals(gld_f4(x + row * cols + b * 256 + 4 * lane_id()), out + g * kQ8KBytes);
+}
+
+// RMS pre-norm of one token's residual row (the MoE block's input in a stack
+// of layers): r = 1 / sqrt(mean(x^2) + eps) in fp64, by one wave over `cols`
+// (a multiple of 256) fp32 values; every lane gets r.  Lane l adds the exact
+// fp64 squares of elements 256m + 4l .. 256m + 4l + 3 for m = 0, 1, ... in
+// that order, then the lanes' sums add in wave_sum's fixed order, so every
+// wave that computes r for the same row gets the same bits.
+__device__ __forceinline__ double row_rms_scale(const float* __restrict__ row, int64_t cols, double eps) {
+  constexpr int U = 8;                      // loads in flight per lane
+  const int lane = lane_id();
+  double ss = 0.0;
+  for (int64_t base = 0; base < cols; base += (int64_t)U * 4 * kWave) {
+    float4 v[U];
+    bool ok[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {           // a unit past the row reloads unit 0, left out below
+      const int64_t i = base + 4 * lane + (int64_t)u * 4 * kWave;
+      ok[u] = i < cols;
+      v[u] = gld_f4(row + (ok[u] ? i : 4 * lane));
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      double t = fma((double)v[u].x, (double)v[u].x, ss);
+      t = fma((double)v[u].y, (double)v[u].y, t);
+      t = fma((double)v[u].z, (double)v[u].z, t);
+      t = fma((double)v[u].w, (double)v[u].w, t);
+      ss = ok[u] ? t : ss;
+    }
+  }
+  ss = wave_sum(ss);
+  return 1.0 / sqrt(ss / (double)cols + eps);
+}
+// Normalised element: fl32((x * r) * g), both products in fp64.
+__device__ __forceinline__ float norm_elem(float x, double r, float g) {
+  return (float)(((double)x * r) * (double)g);
+}
+__device__ __forceinline__ float4 norm4(float4 v, double r, float4 g) {
+  return make_float4(norm_elem(v.x, r, g.x), norm_elem(v.y, r, g.y), norm_elem(v.z, r, g.z), norm_elem(v.w, r, g.w));
 }
 
 __host__ __device__ constexpr size_t align256(size_t n) { return (n + 255) & ~size_t(255); }

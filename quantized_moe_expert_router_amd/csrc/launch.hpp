@@ -133,6 +133,9 @@ struct MfmaArgs {
 };
 
 int launch_quantize_q8K(const float* x, int64_t rows, int64_t cols, void* out, hipStream_t s);
+// RMS pre-norm of token rows (g null: all ones) into out (fp32, 16-byte aligned rows).
+int launch_rms_norm(const float* x, int64_t rows, int64_t cols, const float* g, double eps, float* out,
+                    hipStream_t s);
 int launch_pack(int fmt, const void* aos, int64_t n_mats, int64_t rows, int64_t cols, void* packed,
                 hipStream_t s);
 // Exact integer parts of the super-block terms by the MFMA tile code (test hook).
@@ -143,6 +146,10 @@ int launch_subdots(int fmt, const void* w, int64_t rows, int64_t cols, const voi
 size_t route_ws_bytes(int64_t T, int64_t E);
 int launch_logits(int64_t T, int64_t H, int64_t E, const float* x, const float* W, const float* bias,
                   double* logits, void* xq, hipStream_t s);
+// One token: RMS pre-norm fused into the router logits and q8_K (H <= kNorm1MaxH).
+constexpr int64_t kNorm1MaxH = 4096;
+int launch_logits_norm1(int64_t H, int64_t E, const float* x, const float* g, double eps, const float* W,
+                        const float* bias, double* logits, void* xq, hipStream_t s);
 int launch_route(int64_t T, int64_t H, int64_t E, int k, int gating, float scale, const float* x,
                  const float* W, const float* bias, double* logits, int32_t* ids, float* w,
                  int32_t* offsets, int32_t* pairs, int32_t* active, void* xq, void* ws, hipStream_t s, const MfmaPlan* plan = nullptr);

@@ -236,6 +236,10 @@ __device__ __forceinline__ void down1_body(const DownArgs& a, int bx) {
   // (each slot's down matrix and weight): read it first, from the copy of
   // this workgroup's XCD, before the h loads are in flight.
   __shared__ const uint8_t* sfb;            // first resident slot's down matrix, null if none
+  // y (=|+=) result: the old y of this thread's output row is loaded now, with
+  // the slot records, so the final sum does not wait for a round trip
+  float y_old = 0.0f;
+  if (a.accumulate && threadIdx.x < rows_wg && row_base + threadIdx.x < a.H) y_old = gld_f32(a.y + row_base + threadIdx.x);
   const uint8_t* my_wd = nullptr;
   if (threadIdx.x < n_slots) {
     const SlotRec* rec = a.slots + (int64_t)(bx & (kSlotCopies - 1)) * (a.k + 1) + threadIdx.x;
@@ -263,7 +267,7 @@ __device__ __forceinline__ void down1_body(const DownArgs& a, int bx) {
   if (fb == nullptr) {                       // no resident slot: every pair adds nothing
     if (threadIdx.x < rows_wg) {
       const int64_t rr = row_base + threadIdx.x;
-      if (rr < a.H) gst_f32(a.y + rr, a.accumulate ? (float)((double)gld_f32(a.y + rr) + 0.0) : 0.0f);
+      if (rr < a.H) gst_f32(a.y + rr, a.accumulate ? (float)((double)y_old + 0.0) : 0.0f);
     }
     return;
   }
@@ -374,7 +378,7 @@ __device__ __forceinline__ void down1_body(const DownArgs& a, int bx) {
       double acc = 0.0;
       for (int p = 0; p < n_routed; ++p) acc += yps[p][threadIdx.x];
       if (a.has_shared) acc += yps[n_routed][threadIdx.x];
-      gst_f32(a.y + rr, a.accumulate ? (float)((double)gld_f32(a.y + rr) + acc) : (float)acc);
+      gst_f32(a.y + rr, a.accumulate ? (float)((double)y_old + acc) : (float)acc);
     }
   }
 }

@@ -18,6 +18,28 @@ int launch_quantize_q8K(const float* x, int64_t rows, int64_t cols, void* out, h
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
+// RMS pre-norm, one wave per token row: out = fl32((x * r) * g) with
+// r = 1 / sqrt(mean(x^2) + eps) in fp64; g null means all ones.
+__global__ __launch_bounds__(256) void k_rms_norm(const float* __restrict__ x, int64_t rows, int64_t cols,
+                                                  const float* __restrict__ g, double eps, float* __restrict__ out) {
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= rows) return;
+  const float* xr = x + row * cols;
+  const double r = row_rms_scale(xr, cols, eps);
+  for (int64_t i = 4 * lane_id(); i < cols; i += 4 * kWave) {
+    const float4 gv = g ? gld_f4(g + i) : make_float4(1.0f, 1.0f, 1.0f, 1.0f);
+    const float4 v = norm4(gld_f4(xr + i), r, gv);
+    *reinterpret_cast<float4*>(out + row * cols + i) = v;
+  }
+}
+
+int launch_rms_norm(const float* x, int64_t rows, int64_t cols, const float* g, double eps, float* out,
+                    hipStream_t s) {
+  if (rows == 0) return 0;
+  hipLaunchKernelGGL(k_rms_norm, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s, x, rows, cols, g, eps, out);
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
 // ------------------------------------------------------------------ repack
 
 __device__ __forceinline__ int q4k_code(const uint8_t* b, int e) {   // exchange Q4_K element

@@ -114,6 +114,71 @@ __global__ __launch_bounds__(256) void k_logits(const float* __restrict__ x, con
   }
 }
 
+// One token through the RMS pre-norm of a stack of layers: the same logits
+// as k_logits on xn = fl32((x * r) * g), r from the whole row
+// (row_rms_scale), and q8_K(xn) from the workgroups past the experts, with
+// no normalised copy written: every wave forms the xn elements it uses.  The
+// per-lane unit order, the wave sums and the order of the four partials are
+// k_logits' for one token (H <= 4096: one pass of up to four float4 units per
+// lane), so the logits are bit-identical to k_rms_norm followed by k_logits.
+// The router row's loads go out before the norm's row sum.
+__global__ __launch_bounds__(256) void k_logits_norm1(const float* __restrict__ x, const float* __restrict__ g,
+                                                      double eps, const float* __restrict__ W,
+                                                      const float* __restrict__ bias, int64_t H, int64_t E,
+                                                      double* __restrict__ logits, uint8_t* __restrict__ xq) {
+  const int wave = threadIdx.x >> 6, lane = lane_id();
+  const float4 ones = make_float4(1.0f, 1.0f, 1.0f, 1.0f);
+  if ((int64_t)blockIdx.x >= E) {
+    const int64_t blk = (int64_t)(blockIdx.x - E) * 4 + wave;
+    if (blk >= H / 256) return;
+    const int64_t i = blk * 256 + 4 * lane;
+    const float4 v = gld_f4(x + i);
+    const float4 gv = g ? gld_f4(g + i) : ones;
+    const double r = row_rms_scale(x, H, eps);
+    quantize_block_vals(norm4(v, r, gv), xq + blk * kQ8KBytes);
+    return;
+  }
+  __shared__ double part[4];
+  const int64_t e = blockIdx.x;
+  const int64_t n4 = H / 4, q4 = (n4 + 3) / 4;             // float4 units per wave (<= 256)
+  const int64_t i0 = wave * q4, i1 = (i0 + q4) < n4 ? (i0 + q4) : n4;
+  const float4* w4 = reinterpret_cast<const float4*>(W + e * H);
+  bool uv[4];
+  int64_t iu[4];
+  float4 w[4], xv[4], gv[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int64_t i = i0 + lane + u * kWave;
+    uv[u] = i < i1;
+    iu[u] = uv[u] ? i : i0;
+    w[u] = w4[iu[u]];
+  }
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    xv[u] = gld_f4(x + 4 * iu[u]);
+    gv[u] = g ? gld_f4(g + 4 * iu[u]) : ones;
+  }
+  const double r = row_rms_scale(x, H, eps);
+  double a = 0.0;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const float4 xn = norm4(xv[u], r, gv[u]);
+    double b = fma((double)w[u].x, (double)xn.x, a);
+    b = fma((double)w[u].y, (double)xn.y, b);
+    b = fma((double)w[u].z, (double)xn.z, b);
+    b = fma((double)w[u].w, (double)xn.w, b);
+    a = uv[u] ? b : a;
+  }
+  const double v = wave_sum(a);
+  if (lane == 0) part[wave] = v;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    double t = ((part[0] + part[1]) + part[2]) + part[3];
+    if (bias) t += (double)bias[e];
+    logits[e] = t;
+  }
+}
+
 // Logits of many tokens as a dense contraction on fp64 matrix cores:
 // v_mfma_f64_16x16x4f64 on exact fp64 copies of the fp32 operands, so every
 // product is exact and only the order of the fp64 additions differs from a
@@ -483,6 +548,15 @@ int launch_logits(int64_t T, int64_t H, int64_t E, const float* x, const float* 
   const int64_t tiles = (T + kLogitTok - 1) / kLogitTok;
   dim3 g1((unsigned)(E + nq), (unsigned)(tiles < 64 ? tiles : 64));
   hipLaunchKernelGGL(k_logits, g1, dim3(256), 0, s, x, W, bias, T, H, E, logits, (uint8_t*)xq);
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+int launch_logits_norm1(int64_t H, int64_t E, const float* x, const float* g, double eps, const float* W,
+                        const float* bias, double* logits, void* xq, hipStream_t s) {
+  if (H > kNorm1MaxH) return -1;
+  const int64_t nq = (H / 256 + 3) / 4;
+  hipLaunchKernelGGL(k_logits_norm1, dim3((unsigned)(E + nq)), dim3(256), 0, s, x, g, eps, W, bias, H, E, logits,
+                     (uint8_t*)xq);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 

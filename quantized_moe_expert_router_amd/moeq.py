@@ -28,7 +28,8 @@ SUBBLOCK = {Q4_K: 32, Q6_K: 16, Q2_K: 16, Q8_0: 32}
 SYMBOLS = ["moeq_status_string", "moeq_quantize_q8K", "moeq_route_workspace", "moeq_route",
            "moeq_packed_bytes", "moeq_pack_experts", "moeq_expert_ffn_workspace", "moeq_expert_ffn",
            "moeq_moe_layer_workspace", "moeq_moe_layer", "moeq_ffn_h_view", "moeq_debug_subdots",
-           "moeq_moe_layer_noalloc", "moeq_debug_mfma_sums"]
+           "moeq_moe_layer_noalloc", "moeq_debug_mfma_sums", "moeq_moe_stack_workspace", "moeq_moe_stack",
+           "moeq_rms_norm"]
 
 
 class MoeqError(RuntimeError):
@@ -104,13 +105,19 @@ def lib() -> ctypes.CDLL:
         L.moeq_moe_layer_workspace.argtypes = [ctypes.POINTER(RouteDesc), ctypes.POINTER(FfnDesc)]
         L.moeq_moe_layer.argtypes = [ctypes.POINTER(RouteDesc), ctypes.POINTER(FfnDesc), vp, vp, vp, vp, vp, vp,
                                      vp, vp, vp, vp, vp, vp, sz, vp]
+        L.moeq_moe_stack_workspace.restype = sz
+        L.moeq_moe_stack_workspace.argtypes = [ctypes.POINTER(RouteDesc), ctypes.POINTER(FfnDesc), i64]
+        L.moeq_moe_stack.argtypes = [ctypes.POINTER(RouteDesc), ctypes.POINTER(FfnDesc), i64, vp, vp, vp,
+                                     ctypes.c_float, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.moeq_rms_norm.argtypes = [vp, i64, i64, vp, ctypes.c_float, vp, vp]
         L.moeq_moe_layer_noalloc.argtypes = [ctypes.POINTER(RouteDesc), ctypes.POINTER(FfnDesc), vp, vp, vp, vp, vp,
                                              vp, vp, vp, vp, vp, vp, vp]
         L.moeq_ffn_h_view.argtypes = [ctypes.POINTER(FfnDesc), vp, sz, ctypes.POINTER(vp), ctypes.POINTER(vp)]
         L.moeq_debug_subdots.argtypes = [i32, vp, i64, i64, vp, i64, vp, vp]
         L.moeq_debug_mfma_sums.argtypes = [i32, vp, i64, i64, vp, i64, vp, vp]
         for s in ("moeq_quantize_q8K", "moeq_route", "moeq_pack_experts", "moeq_expert_ffn", "moeq_moe_layer",
-                  "moeq_ffn_h_view", "moeq_debug_subdots", "moeq_moe_layer_noalloc", "moeq_debug_mfma_sums"):
+                  "moeq_ffn_h_view", "moeq_debug_subdots", "moeq_moe_layer_noalloc", "moeq_debug_mfma_sums",
+                  "moeq_moe_stack", "moeq_rms_norm"):
             getattr(L, s).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -250,6 +257,63 @@ def moeq_moe_layer_noalloc(rdesc: RouteDesc, fdesc: FfnDesc, x: torch.Tensor, w_
                                       _stream(stream))
     _check("moeq_moe_layer_noalloc", rc)
     return y
+
+
+class StackOut:
+    """Per-layer routing outputs of a stack of L layers ([L, ...] each)."""
+
+    def __init__(self, L, T, E, k, device):
+        self.L, self.T, self.E, self.k = L, T, E, k
+        self.ids = torch.empty((L, T, k), dtype=torch.int32, device=device)
+        self.w = torch.empty((L, T, k), dtype=torch.float32, device=device)
+        self.offsets = torch.empty((L, E + 1), dtype=torch.int32, device=device)
+        self.pairs = torch.empty((L, max(1, T * k)), dtype=torch.int32, device=device)
+        self.active = torch.empty((L, 1 + min(E, T * k)), dtype=torch.int32, device=device)
+
+
+def _ffn_array(fdescs: Sequence[FfnDesc]):
+    arr = (FfnDesc * len(fdescs))()
+    for i, d in enumerate(fdescs):
+        ctypes.memmove(ctypes.byref(arr[i]), ctypes.byref(d), ctypes.sizeof(FfnDesc))
+    return arr
+
+
+def moeq_moe_stack_workspace(rdesc: RouteDesc, fdescs: Sequence[FfnDesc]) -> int:
+    return lib().moeq_moe_stack_workspace(ctypes.byref(rdesc), _ffn_array(fdescs), len(fdescs))
+
+
+def moeq_moe_stack(rdesc: RouteDesc, fdescs: Sequence[FfnDesc], w_routers: Sequence[torch.Tensor],
+                   biases: Optional[Sequence[Optional[torch.Tensor]]], x: torch.Tensor, out: StackOut,
+                   y: torch.Tensor, ws: torch.Tensor, stream=None,
+                   shared_scales: Optional[Sequence[Optional[torch.Tensor]]] = None,
+                   norm_ws: Optional[Sequence[Optional[torch.Tensor]]] = None, norm_eps: float = 1e-6) -> torch.Tensor:
+    """L layers on a pre-norm residual stream in one library call:
+    y = x, then y += MoE_l(RMSNorm_l(y)) for every layer."""
+    L = len(fdescs)
+    arr = _ffn_array(fdescs)
+    wr = (ctypes.c_void_p * L)(*[_ptr(w) for w in w_routers])
+    bs = None if biases is None else (ctypes.c_void_p * L)(*[_ptr(b) for b in biases])
+    nw = None if norm_ws is None else (ctypes.c_void_p * L)(*[_ptr(g) for g in norm_ws])
+    ss = None if shared_scales is None else (ctypes.c_void_p * L)(*[_ptr(t) for t in shared_scales])
+    rc = lib().moeq_moe_stack(ctypes.byref(rdesc), arr, L, wr, bs, nw, ctypes.c_float(norm_eps), _ptr(x),
+                              _ptr(out.ids), _ptr(out.w), _ptr(out.offsets), _ptr(out.pairs), _ptr(out.active), ss,
+                              _ptr(y), _ptr(ws), ws.numel(), _stream(stream))
+    _check("moeq_moe_stack", rc)
+    return y
+
+
+def moeq_rms_norm(x: torch.Tensor, gamma: Optional[torch.Tensor], eps: float, out: Optional[torch.Tensor] = None,
+                  stream=None) -> torch.Tensor:
+    """RMS pre-norm of the rows of x (fp32 [T, H]); gamma fp32 [H] or None."""
+    _need(x, torch.float32, "x")
+    if gamma is not None:
+        _need(gamma, torch.float32, "gamma")
+    T, H = x.shape
+    if out is None:
+        out = torch.empty_like(x)
+    _check("moeq_rms_norm", lib().moeq_rms_norm(_ptr(x), T, H, _ptr(gamma), ctypes.c_float(eps), _ptr(out),
+                                                _stream(stream)))
+    return out
 
 
 def moeq_ffn_h_view(desc: FfnDesc, ws: torch.Tensor):

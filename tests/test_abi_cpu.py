@@ -157,3 +157,41 @@ def test_noalloc_layer_rejects_requests_beyond_its_static_workspace():
     r2 = moeq.RouteDesc(8192, 2048, 512, 6, 0, 1.0)            # descriptors that disagree
     assert L.moeq_moe_layer_noalloc(ctypes.byref(r2), ctypes.byref(f), *ptrs, None) == moeq.MOEQ_E_INVALID
     assert moeq.status_string(moeq.MOEQ_E_STATIC_LIMIT) != "unknown status"
+
+
+def test_stack_call_validation():
+    L = moeq.lib()
+    r = moeq.RouteDesc(1, 2048, 256, 8, 0, 1.0)
+    fs = moeq._ffn_array([_desc(), _desc()])
+    one = L.moeq_moe_layer_workspace(ctypes.byref(r), ctypes.byref(_desc()))
+    need = L.moeq_moe_stack_workspace(ctypes.byref(r), fs, 2)
+    assert need == one + 2048 * 4                                   # plus the normalised rows
+    assert L.moeq_moe_stack_workspace(ctypes.byref(r), fs, 0) == 0
+    bad = moeq._ffn_array([_desc(), _desc(accumulate=1)])          # layers of a stack do not accumulate
+    assert L.moeq_moe_stack_workspace(ctypes.byref(r), bad, 2) == 0
+    wr = (ctypes.c_void_p * 2)(0x1000, 0x2000)
+    args = [0x1000, 0x3000, 0x4000, 0x5000, 0x6000, 0x7000, None, 0x8000]
+    eps = ctypes.c_float(1e-5)
+
+    def call(rd=r, wrs=wr, nw=None, e=eps, ws_bytes=need):
+        return L.moeq_moe_stack(ctypes.byref(rd), fs, 2, wrs, None, nw, e, *args, 0x100000, ws_bytes, None)
+
+    assert call(ws_bytes=need - 1) == moeq.MOEQ_E_WORKSPACE
+    assert call(wrs=(ctypes.c_void_p * 2)(0x1000, 0x2004)) == moeq.MOEQ_E_INVALID   # router weights 16-byte aligned
+    assert call(rd=moeq.RouteDesc(1, 2048, 256, 6, 0, 1.0)) == moeq.MOEQ_E_INVALID  # k disagrees with f
+    assert call(nw=(ctypes.c_void_p * 2)(None, 0x2008)) == moeq.MOEQ_E_INVALID     # norm gains 16-byte aligned
+    for e in (-1.0, float("inf"), float("nan")):
+        assert call(e=ctypes.c_float(e)) == moeq.MOEQ_E_INVALID
+
+
+def test_rms_norm_validation():
+    L = moeq.lib()
+    e = ctypes.c_float(1e-6)
+    assert L.moeq_rms_norm(0x1000, 2, 300, None, e, 0x2000, None) == moeq.MOEQ_E_INVALID    # H % 256
+    assert L.moeq_rms_norm(0x1000, -1, 256, None, e, 0x2000, None) == moeq.MOEQ_E_INVALID
+    assert L.moeq_rms_norm(None, 2, 256, None, e, 0x2000, None) == moeq.MOEQ_E_INVALID
+    assert L.moeq_rms_norm(0x1004, 2, 256, None, e, 0x2000, None) == moeq.MOEQ_E_INVALID  # x 16-byte aligned
+    assert L.moeq_rms_norm(0x1000, 2, 256, 0x3004, e, 0x2000, None) == moeq.MOEQ_E_INVALID
+    assert L.moeq_rms_norm(0x1000, 2, 256, None, ctypes.c_float(-1e-6), 0x2000, None) == moeq.MOEQ_E_INVALID
+    assert L.moeq_rms_norm(0x1000, 2, 256, None, ctypes.c_float(float("nan")), 0x2000, None) == moeq.MOEQ_E_INVALID
+    assert L.moeq_rms_norm(None, 0, 256, None, e, None, None) == 0                        # T == 0: no-op

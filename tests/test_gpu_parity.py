@@ -531,6 +531,193 @@ def test_aux_stream_and_single_stream_agree(variant):
         assert np.array_equal(a.hq_r, b.hq_r) and np.array_equal(a.hq_s, b.hq_s), (variant, fused)
 
 
+def check_residual(before, after, y_orc, what):
+    """A layer added to a residual stream: after = fl32(before + its output),
+    rounded once, so (after - before) matches the oracle's output within the y
+    tolerance plus one fp32 ulp of the stream per element."""
+    d = after.astype(np.float64) - before.astype(np.float64)
+    y_orc = np.asarray(y_orc, np.float64)
+    ulp = np.spacing(np.abs(after).astype(np.float32)).astype(np.float64)
+    rms = np.sqrt(np.mean(y_orc ** 2))
+    err = np.abs(d - y_orc)
+    assert np.all(err <= Y_MAX_ABS_RMS * rms + ulp), (what, float(np.max(err - ulp)), rms)
+    assert np.linalg.norm(d - y_orc) <= Y_REL_L2 * np.linalg.norm(y_orc) + np.linalg.norm(ulp), what
+
+
+NORM_EPS = float(np.float32(1e-5))
+
+
+@pytest.mark.parametrize("T,H", [(1, 256), (1, 4096), (3, 1024), (17, 2304), (0, 512)])
+def test_rms_norm_matches_oracle(T, H):
+    """The RMS pre-norm against the oracle: fp64 statistic, one fp32
+    rounding; only the order of the sum's additions differs, so the values
+    agree to one fp32 ulp (nearly all bit for bit).  In place gives the same
+    bits; gamma NULL means ones."""
+    say("rms_norm", T, H)
+    rng = np.random.default_rng(1000 + T * 7 + H)
+    x = (rng.standard_normal((T, H)) * rng.uniform(0.01, 100.0, (T, 1))).astype(np.float32)
+    g = (1.0 + 0.25 * rng.standard_normal(H)).astype(np.float32)
+    xd = dev(x) if T else torch.empty((0, H), dtype=torch.float32, device="cuda")
+    for gamma in (g, None):
+        gd = dev(gamma) if gamma is not None else None
+        ga = GuardedAlloc()
+        out = ga.empty((T, H), torch.float32, "out")
+        moeq.moeq_rms_norm(xd, gd, NORM_EPS, out)
+        torch.cuda.synchronize()
+        ga.check("rms_norm")
+        if T == 0:
+            continue
+        got = out.cpu().numpy()
+        ref = oracle.rms_norm(x, gamma, NORM_EPS)
+        ulp = np.spacing(np.abs(ref))
+        assert np.all(np.abs(got.astype(np.float64) - ref) <= ulp), (T, H)
+        assert np.mean(got == ref) > 0.999, (T, H)
+        inp = xd.clone()
+        moeq.moeq_rms_norm(inp, gd, NORM_EPS, inp)
+        torch.cuda.synchronize()
+        assert np.array_equal(inp.cpu().numpy(), got), (T, H, "in place")
+
+
+def _stack_norm_gains(cfg, L):
+    rng = np.random.default_rng(77)
+    # layer 1 without gains (all ones); the others with gains around one
+    return [None if l == 1 else (1.0 + 0.2 * rng.standard_normal(cfg.H)).astype(np.float32) for l in range(L)]
+
+
+@pytest.mark.parametrize("variant", ["decode_t1", "decode_t1_wide", "chunk_t16"])
+def test_stack_equals_layer_chain_and_oracle(variant):
+    """A stack of layers on a pre-norm residual stream in one call equals the
+    chain of single-layer calls (RMS norm of the stream, then the layer adding
+    into the stream) bit for bit, whether the norm is fused into the one-token
+    router launch (H <= 4096) or runs as its own kernel; every layer's norm and
+    MoE output match the oracle on that layer's GPU input; a graph of the stack
+    replays exactly."""
+    if variant == "decode_t1":
+        cfg = _custom_cfg(T=1, H=1024, E=64, k=8, F=512, fmt_down=syn.Q6_K, shared=True, F_shared=512,
+                          sh_fmt_gate=syn.Q4_K, sh_fmt_up=syn.Q4_K, sh_fmt_down=syn.Q6_K)
+        L = 4
+    elif variant == "decode_t1_wide":          # H past the fused norm's limit: the norm kernel runs first
+        cfg = _custom_cfg(T=1, H=4352, E=16, k=2, F=256, fmt_down=syn.Q4_K)
+        L = 3
+    else:
+        cfg = _custom_cfg(T=16, H=512, E=24, k=4, F=512, fmt_gate=syn.Q2_K, fmt_up=syn.Q2_K, fmt_down=syn.Q4_K,
+                          gating=syn.SIGMOID_TOPK, shared=True, F_shared=256, sh_fmt_gate=syn.Q8_0,
+                          sh_fmt_up=syn.Q8_0, sh_fmt_down=syn.Q8_0)
+        L = 3
+    say("stack", variant, L)
+    layers = [syn.gen_layer(cfg, layer=l) for l in range(L)]
+    dls = [moeq.DeviceLayer(lay) for lay in layers]
+    gains = _stack_norm_gains(cfg, L)
+    gd = [dev(g) if g is not None else None for g in gains]
+    aux = moeq.AuxStream()
+    fdescs = [dl.ffn_desc(cfg.T, aux=aux) for dl in dls]
+    fdescs_acc = [dl.ffn_desc(cfg.T, accumulate=1, aux=aux) for dl in dls]
+    rdesc = moeq.RouteDesc(cfg.T, cfg.H, cfg.E, cfg.k, cfg.gating, 1.0)
+    x = dev(layers[0].x)
+    ga = GuardedAlloc()
+    out = moeq.StackOut(L, cfg.T, cfg.E, cfg.k, "cuda")
+    out.ids = ga.empty((L, cfg.T, cfg.k), torch.int32, "ids")
+    out.w = ga.empty((L, cfg.T, cfg.k), torch.float32, "w")
+    out.offsets = ga.empty((L, cfg.E + 1), torch.int32, "offsets")
+    out.pairs = ga.empty((L, max(1, cfg.T * cfg.k)), torch.int32, "pairs")
+    out.active = ga.empty((L, 1 + min(cfg.E, cfg.T * cfg.k)), torch.int32, "active")
+    y = ga.empty((cfg.T, cfg.H), torch.float32, "y")
+    ws = ga.empty(moeq.moeq_moe_stack_workspace(rdesc, fdescs), torch.uint8, "ws")
+    wr = [dl.w_router for dl in dls]
+    bs = [dl.bias for dl in dls]
+    stream = torch.cuda.Stream()
+
+    def run_stack():
+        moeq.moeq_moe_stack(rdesc, fdescs, wr, bs, x, out, y, ws, stream, norm_ws=gd, norm_eps=NORM_EPS)
+
+    with torch.cuda.stream(stream):
+        run_stack()
+    ga.check("stack")
+    y_stack = y.cpu().numpy().copy()
+    assert np.all(np.isfinite(y_stack)), variant
+    # the chain of single-layer calls on the residual stream, and the oracle
+    # on each layer's GPU input
+    res = x.clone()
+    xn = torch.empty_like(res)
+    for l in range(L):
+        before = res.cpu().numpy().copy()
+        ro = moeq.RouteOut(cfg.T, cfg.E, cfg.k, "cuda", with_logits=False)
+        lws = torch.empty(moeq.moeq_moe_layer_workspace(rdesc, fdescs_acc[l]), dtype=torch.uint8, device="cuda")
+        with torch.cuda.stream(stream):
+            moeq.moeq_rms_norm(res, gd[l], NORM_EPS, xn, stream)
+            moeq.moeq_moe_layer(rdesc, fdescs_acc[l], xn, wr[l], bs[l], ro, None, res, lws, stream)
+        torch.cuda.synchronize()
+        xin = xn.cpu().numpy()
+        xn_orc = oracle.rms_norm(before, gains[l], NORM_EPS)
+        assert np.all(np.abs(xin.astype(np.float64) - xn_orc) <= np.spacing(np.abs(xn_orc))), (variant, l)
+        ids = ro.ids.cpu().numpy()
+        assert np.array_equal(out.ids[l].cpu().numpy(), ids), (variant, l)
+        assert np.array_equal(out.w[l].cpu().numpy(), ro.w.cpu().numpy()), (variant, l)
+        assert np.array_equal(out.offsets[l].cpu().numpy(), ro.offsets.cpu().numpy()), (variant, l)
+        assert np.array_equal(out.pairs[l].cpu().numpy()[:cfg.T * cfg.k], ro.pairs.cpu().numpy()[:cfg.T * cfg.k])
+        act, ract = out.active[l].cpu().numpy(), ro.active.cpu().numpy()
+        assert np.array_equal(act[:1 + act[0]], ract[:1 + ract[0]]), (variant, l)   # entries past the union: unspecified
+        _, oids, ow = oracle.route(xin, layers[l].w_router, layers[l].bias, cfg.k, cfg.gating)
+        assert np.array_equal(ids, oids), (variant, l)
+        check_w(ro.w.cpu().numpy(), ow)
+        r = oracle.expert_ffn(layers[l], oids, ow, range(cfg.T), x=xin)
+        check_residual(before, res.cpu().numpy(), r.y, (variant, l))
+    assert np.array_equal(y_stack, res.cpu().numpy()), variant
+    # graph replays of the stack, with eager work between them
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(stream):
+        with torch.cuda.graph(g, stream=stream):
+            run_stack()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        y.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(y.cpu().numpy(), y_stack), (variant, rep)
+        with torch.cuda.stream(stream):
+            run_stack()
+        torch.cuda.synchronize()
+        assert np.array_equal(y.cpu().numpy(), y_stack), (variant, rep, "eager")
+    ga.check("stack graph")
+
+
+def test_long_decode_stack_stays_bounded():
+    """Sixty-four pre-norm decode layers (sixteen distinct layers cycled) keep
+    the residual stream finite and of moderate size, and a later layer still
+    matches the oracle on its own input."""
+    cfg = _custom_cfg(T=1, H=1024, E=64, k=8, F=512, fmt_down=syn.Q6_K, shared=True, F_shared=512,
+                      sh_fmt_gate=syn.Q4_K, sh_fmt_up=syn.Q4_K, sh_fmt_down=syn.Q6_K)
+    n_distinct, L = 16, 64
+    say("long stack", L)
+    layers = [syn.gen_layer(cfg, layer=l) for l in range(n_distinct)]
+    dls = [moeq.DeviceLayer(lay) for lay in layers]
+    fd = [dls[l % n_distinct].ffn_desc(1) for l in range(L)]
+    rdesc = moeq.RouteDesc(1, cfg.H, cfg.E, cfg.k, cfg.gating, 1.0)
+    out = moeq.StackOut(L, 1, cfg.E, cfg.k, "cuda")
+    x = dev(layers[0].x)
+    y = torch.empty_like(x)
+    ws = torch.empty(moeq.moeq_moe_stack_workspace(rdesc, fd), dtype=torch.uint8, device="cuda")
+    wr = [dls[l % n_distinct].w_router for l in range(L)]
+    bs = [dls[l % n_distinct].bias for l in range(L)]
+    moeq.moeq_moe_stack(rdesc, fd[:L - 1], wr[:L - 1], bs[:L - 1], x, out, y, ws, norm_eps=NORM_EPS)
+    torch.cuda.synchronize()
+    before = y.cpu().numpy().copy()
+    assert np.all(np.isfinite(before))
+    rms0 = float(np.sqrt(np.mean(layers[0].x.astype(np.float64) ** 2)))
+    rms = float(np.sqrt(np.mean(before.astype(np.float64) ** 2)))
+    assert rms < 1e4 * rms0, (rms, rms0)
+    # the last layer on its own: one more stack layer on y in place
+    last = moeq.StackOut(1, 1, cfg.E, cfg.k, "cuda")
+    moeq.moeq_moe_stack(rdesc, fd[L - 1:], wr[L - 1:], bs[L - 1:], y, last, y, ws, norm_eps=NORM_EPS)
+    torch.cuda.synchronize()
+    lay = layers[(L - 1) % n_distinct]
+    xin = oracle.rms_norm(before, None, NORM_EPS)
+    _, oids, ow = oracle.route(xin, lay.w_router, lay.bias, cfg.k, cfg.gating)
+    assert np.array_equal(last.ids[0].cpu().numpy(), oids)
+    r = oracle.expert_ffn(lay, oids, ow, [0], x=xin)
+    check_residual(before, y.cpu().numpy(), r.y, "layer %d" % (L - 1))
+
+
 def _custom_cfg(**kw):
     base = dict(name="custom", seed=777, T=8, H=512, E=6, k=2, F=256, gating=syn.SOFTMAX_TOPK,
                 fmt_gate=syn.Q4_K, fmt_up=syn.Q4_K, fmt_down=syn.Q4_K)

@@ -541,3 +541,57 @@ def test_ffn_partition_of_experts_sums_to_full():
     b = oracle.expert_ffn(lay_ns, ids, w, [0], present=hi)
     s = a.y.astype(np.float64) + b.y.astype(np.float64)
     assert np.linalg.norm(s - full) <= 1e-6 * np.linalg.norm(full)
+
+
+# --------------------------------------------------------------- RMS pre-norm
+# The input of each MoE block of a pre-norm residual stack: the pages run
+# whole models of such blocks without spelling this step out, so the oracle
+# takes the plain reading (fp64 statistic, one fp32 rounding) and these pins
+# fix it by closed forms, invariants and a library routine.
+
+def test_rms_norm_closed_form_with_eps_and_gains():
+    # x = 1 everywhere, eps = 3: mean(x^2) + eps = 4, r = 1/2 exactly, so
+    # out = gamma / 2 exactly (a dropped eps gives gamma, a sum in place of
+    # the mean gives gamma / sqrt(cols + 3))
+    for cols in (256, 1000):
+        g = np.linspace(-3.0, 5.0, cols).astype(np.float32)
+        out = oracle.rms_norm(np.ones((2, cols), np.float32), g, 3.0)
+        assert np.array_equal(out, np.stack([g / 2, g / 2]))
+    # x = c e_0 (one non-zero), eps = 0: mean = c^2 / cols, out_0 = sqrt(cols) sign(c)
+    x = np.zeros((1, 1024), np.float32)
+    x[0, 0] = -7.5
+    out = oracle.rms_norm(x, None, 0.0)
+    assert out[0, 0] == -32.0 and not out[0, 1:].any()
+
+
+def test_rms_norm_invariants():
+    rng = np.random.default_rng(5)
+    x = (rng.standard_normal((6, 768)) * np.array([1e-3, 0.1, 1, 10, 1e3, 1e5])[:, None]).astype(np.float32)
+    out = oracle.rms_norm(x, None, 0.0)
+    # unit mean square (eps = 0) and signs kept
+    ms = np.mean(out.astype(np.float64) ** 2, axis=1)
+    assert np.all(np.abs(ms - 1.0) < 1e-6), ms
+    assert np.array_equal(np.sign(out), np.sign(x))
+    # a power-of-two scale of a row is exact in every step: bit-identical output
+    for k in (-6, 3, 11):
+        assert np.array_equal(oracle.rms_norm(x * np.float32(2.0 ** k), None, 0.0), out), k
+    # rows are independent; gains multiply after the norm (within one fp32 rounding)
+    assert np.array_equal(oracle.rms_norm(x[3:4], None, 0.0), out[3:4])
+    g = rng.uniform(0.5, 2.0, 768).astype(np.float32)
+    og = oracle.rms_norm(x, g, 0.0).astype(np.float64)
+    assert np.all(np.abs(og - out.astype(np.float64) * g) <= 2 * np.spacing(np.abs(og).astype(np.float32)))
+    # a zero row stays zero when eps > 0
+    assert not oracle.rms_norm(np.zeros((1, 256), np.float32), g[:256], 1e-6).any()
+
+
+def test_rms_norm_against_torch_functional():
+    # torch's own RMS norm (in fp64, rounded to fp32) within one fp32 ulp
+    import torch
+    rng = np.random.default_rng(9)
+    x = (rng.standard_normal((5, 2048)) * 3.0).astype(np.float32)
+    g = (1.0 + 0.3 * rng.standard_normal(2048)).astype(np.float32)
+    eps = float(np.float32(1e-5))
+    ref = torch.nn.functional.rms_norm(torch.from_numpy(x).double(), (2048,), torch.from_numpy(g).double(),
+                                       eps).float().numpy()
+    out = oracle.rms_norm(x, g, eps)
+    assert np.all(np.abs(out.astype(np.float64) - ref) <= np.spacing(np.abs(ref)))
