@@ -41,9 +41,10 @@
  *   - Inputs must be finite.
  *
  * Block formats.  The pages name the formats (Pulsar README, 'Get a model':
- * q2_K, q4_K, q6_K expert tensors, dense tensors requantised to q8_0;
- * 'Fidelity notes': activations quantised to q8_K with integer dots) but print
- * no byte layout, so the exchange layout is this library's own (little-endian):
+ * the routed-expert formats it reads, q2_K, q3_K, q4_K, q5_K and q6_K among
+ * them, dense tensors requantised to q8_0; 'Fidelity notes': activations
+ * quantised to q8_K with integer dots) but print no byte layout, so the
+ * exchange layout is this library's own (little-endian):
  *   q8_K  292 B / 256 : f32 d | i8 q[256] | i16 bsums[16]          x ~ d*q
  *   Q4_K  144 B / 256 : f16 d | f16 dmin | 12 B six-bit scales then mins
  *                       (bit stream) | 128 B quants (byte 32g+i = element
@@ -57,6 +58,14 @@
  *                       (byte 32h+i bits 2s..2s+1 = element 128h+32s+i)
  *                                                      w = d*sc_j*(q-32)
  *   Q8_0   34 B /  32 : f16 d | i8 q[32]                w = d*q
+ *   Q3_K  110 B / 256 : f16 d | 12 B six-bit scales (bit stream, stored
+ *                       sc_j + 32) | 64 B low pairs (byte 32h+i bits 2s..2s+1
+ *                       = element 128h+32s+i) | 32 B high bits (byte i bit b =
+ *                       element 32b+i); q = low + 4*high, sub-blocks of 16
+ *                                                      w = d*sc_j*(q-4)
+ *   Q5_K  176 B / 256 : Q4_K's 144 bytes (the low nibbles as its quants) | 32 B
+ *                       high bits (byte i bit b = element 32b+i); q = low +
+ *                       16*high, sub-blocks of 32      w = d*sc_j*q - dmin*m_j
  * A matrix [rows, cols] is rows of blocks back to back.  Kernels read a
  * repacked ("packed") form made once by moeq_pack_experts.
  */
@@ -80,7 +89,9 @@ typedef enum {
                                  MOEQ_NOALLOC_MAX_BYTES of workspace */
 } moeq_status;
 
-typedef enum { MOEQ_Q4_K = 1, MOEQ_Q6_K = 2, MOEQ_Q2_K = 3, MOEQ_Q8_0 = 4 } moeq_wfmt;
+typedef enum {
+    MOEQ_Q4_K = 1, MOEQ_Q6_K = 2, MOEQ_Q2_K = 3, MOEQ_Q8_0 = 4, MOEQ_Q3_K = 5, MOEQ_Q5_K = 6
+} moeq_wfmt;
 
 typedef enum {
     MOEQ_SOFTMAX_TOPK = 0,   /* softmax over the k selected logits */
@@ -343,8 +354,8 @@ int moeq_ffn_h_view(const moeq_ffn_desc* d, void* ws, size_t ws_bytes, void** hq
  * dot-product (GEMV) kernels use.  Enqueued on `stream`; n_x == 0 is a no-op.
  *   packed_w [rows, cols] packed fmt; x_q8K [n_x, cols/256 blocks]
  *   out int32 [n_x, rows, cols/sub]: sum over sub-block j of code * q_x, where
- *   sub = 32 (Q4_K, Q8_0) or 16 (Q2_K, Q6_K) and code = q (Q4_K, Q2_K),
- *   q-32 (Q6_K), signed q (Q8_0).
+ *   sub = 32 (Q4_K, Q5_K, Q8_0) or 16 (Q2_K, Q3_K, Q6_K) and code = q (Q4_K,
+ *   Q5_K, Q2_K), q-32 (Q6_K), q-4 (Q3_K), signed q (Q8_0).
  */
 int moeq_debug_subdots(int32_t fmt, const void* packed_w, int64_t rows, int64_t cols,
                        const void* x_q8K, int64_t n_x, int32_t* out, void* stream);
@@ -357,11 +368,11 @@ int moeq_debug_subdots(int32_t fmt, const void* packed_w, int64_t rows, int64_t 
  * same MFMA and unpack routines, the same LDS staging of q8_K rows).
  *   packed_w [rows, cols] packed fmt, rows % 256 == 0; x_q8K [n_x, cols/256
  *   blocks]; out int32 [n_x, rows, cols/256, 8], 16-byte aligned:
- *     Q4_K, Q2_K: (S1, S2, 0...) with S1 = sum_j sc_j isum_j,
+ *     Q4_K, Q5_K, Q2_K: (S1, S2, 0...) with S1 = sum_j sc_j isum_j,
  *                 S2 = sum_j m_j bsum_j (bsum over the sub-block's 32 / 16
  *                 activations)
- *     Q6_K:       (S1, S2, 0...) with S1 = sum_j sc_j isum_j over the codes
- *                 q - 32 and S2 = sum_j sc_j bsum_j
+ *     Q6_K, Q3_K: (S1, S2, 0...) with S1 = sum_j sc_j isum_j over the codes
+ *                 q - 32 (Q6_K) or q - 4 (Q3_K) and S2 = sum_j sc_j bsum_j
  *     Q8_0:       isum_b of the eight 32-blocks of the super-block
  * Enqueued on `stream`; n_x == 0 is a no-op.  Errors: MOEQ_E_UNSUPPORTED for
  * an unknown format, MOEQ_E_INVALID for bad sizes, NULLs or misalignment.

@@ -47,13 +47,20 @@
  *                 128h+64+i (high nibble); qh byte 32h+i: high 2 bits of element
  *                 128h+32s+i in bits 2s..2s+1; sub-blocks of 16; w = d*sc_j*(q-32)
  *   Q8_0   34 B : f16 d | i8 qs[32];  w = d*q
+ *   Q3_K  110 B : f16 d | u8 sc[12] (bit stream: 16 six-bit values, stored
+ *                 sc_j + 32) | u8 ql[64] (as Q2_K's qs: low 2 bits) | u8 qh[32]
+ *                 (byte i bit b: high bit of element 32b+i); q = low + 4*high;
+ *                 sub-blocks of 16; w = d*sc_j*(q-4)
+ *   Q5_K  176 B : the 144 bytes of Q4_K (its quants are the low nibbles) |
+ *                 u8 qh[32] (byte i bit b: bit 4 of element 32b+i); sub-blocks
+ *                 of 32; w = d*sc_j*q - dmin*m_j
  */
 #include <math.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
 
-enum { F_Q4_K = 1, F_Q6_K = 2, F_Q2_K = 3, F_Q8_0 = 4 };
+enum { F_Q4_K = 1, F_Q6_K = 2, F_Q2_K = 3, F_Q8_0 = 4, F_Q3_K = 5, F_Q5_K = 6 };
 enum { G_SOFTMAX_TOPK = 0, G_SOFTMAX_ALL = 1, G_SIGMOID_TOPK = 2 };
 
 /* ------------------------------------------------------------------ fp16 */
@@ -85,6 +92,8 @@ int orc_block_bytes(int fmt)
     case F_Q6_K: return 210;
     case F_Q2_K: return 84;
     case F_Q8_0: return 34;
+    case F_Q3_K: return 110;
+    case F_Q5_K: return 176;
     }
     return 0;
 }
@@ -99,13 +108,28 @@ int orc_subblock(int fmt)
     case F_Q6_K: return 16;
     case F_Q2_K: return 16;
     case F_Q8_0: return 32;
+    case F_Q3_K: return 16;
+    case F_Q5_K: return 32;
     }
     return 0;
 }
 
+/* The offset subtracted from the stored code: w = d*sc*(q - offset) (Q6_K, Q3_K). */
+static int code_offset(int fmt) { return fmt == F_Q6_K ? 32 : fmt == F_Q3_K ? 4 : 0; }
+
+/* Bits [pos, pos + n) of a little-endian byte stream. */
+static int stream_bits(const uint8_t* p, int pos, int n)
+{
+    int v = 0, bit;
+    for (bit = 0; bit < n; bit++)
+        v |= ((p[(pos + bit) >> 3] >> ((pos + bit) & 7)) & 1) << bit;
+    return v;
+}
+
 /*
  * Decode one block into integer codes.  q[] gets the quant code of every
- * element (Q6_K: 0..63 before the -32 offset; Q8_0: signed), sc[]/m[] the
+ * element (Q6_K: 0..63 before the -32 offset; Q3_K: 0..7 before the -4
+ * offset; Q8_0: signed), sc[]/m[] the
  * per-sub-block scale and min codes (m = 0 where the format has none),
  * d/dmin the fp16 super-scales as doubles.
  */
@@ -171,6 +195,33 @@ int orc_block_codes(int fmt, const uint8_t* b, double* d, double* dmin, int* sc,
                     q[128 * h + 32 * s + i] |= ((qh[32 * h + i] >> (2 * s)) & 3) << 4;
         return 0;
     }
+    case F_Q3_K: {
+        const uint8_t* ql = b + 14;
+        const uint8_t* qh = b + 78;
+        *d = orc_half_to_double(rd16(b));
+        *dmin = 0.0;
+        for (j = 0; j < 16; j++) {
+            sc[j] = stream_bits(b + 2, 6 * j, 6) - 32;
+            m[j] = 0;
+        }
+        for (h = 0; h < 2; h++)
+            for (s = 0; s < 4; s++)
+                for (i = 0; i < 32; i++)
+                    q[128 * h + 32 * s + i] = (ql[32 * h + i] >> (2 * s)) & 3;
+        for (s = 0; s < 8; s++)
+            for (i = 0; i < 32; i++)
+                q[32 * s + i] += 4 * ((qh[i] >> s) & 1);
+        return 0;
+    }
+    case F_Q5_K: {
+        const uint8_t* qh = b + 144;
+        if (orc_block_codes(F_Q4_K, b, d, dmin, sc, m, q))
+            return -1;
+        for (s = 0; s < 8; s++)
+            for (i = 0; i < 32; i++)
+                q[32 * s + i] += 16 * ((qh[i] >> s) & 1);
+        return 0;
+    }
     case F_Q8_0: {
         *d = orc_half_to_double(rd16(b));
         *dmin = 0.0;
@@ -196,8 +247,10 @@ static int dequant_block(int fmt, const uint8_t* b, double* out)
         int j = i / sb;
         switch (fmt) {
         case F_Q4_K:
+        case F_Q5_K:
         case F_Q2_K: out[i] = d * (double)sc[j] * (double)q[i] - dmin * (double)m[j]; break;
-        case F_Q6_K: out[i] = d * (double)sc[j] * (double)(q[i] - 32); break;
+        case F_Q6_K:
+        case F_Q3_K: out[i] = d * (double)sc[j] * (double)(q[i] - code_offset(fmt)); break;
         case F_Q8_0: out[i] = d * (double)q[i]; break;
         }
     }
@@ -426,7 +479,7 @@ void orc_lists(int64_t T, int k, int64_t E, const int32_t* ids,
 /*
  * Exact int32 dot of each sub-block of each weight row with each q8_K row:
  * out[n][r][j] = sum over sub-block j of (weight code) * q_x, where the weight
- * code is q (Q4_K, Q2_K), q-32 (Q6_K) or the signed q (Q8_0).
+ * code is q (Q4_K, Q5_K, Q2_K), q-32 (Q6_K), q-4 (Q3_K) or the signed q (Q8_0).
  */
 int orc_subdots(int fmt, const uint8_t* w, int64_t rows, int64_t cols,
                 const uint8_t* xq, int64_t n_x, int32_t* out)
@@ -448,7 +501,7 @@ int orc_subdots(int fmt, const uint8_t* w, int64_t rows, int64_t cols,
                     int e;
                     for (e = 0; e < sbw; e++) {
                         int64_t col = b * bw + i * sbw + e;
-                        int code = (fmt == F_Q6_K) ? q[i * sbw + e] - 32 : q[i * sbw + e];
+                        int code = q[i * sbw + e] - code_offset(fmt);
                         int qx = (int8_t)xq[n * (cols / 256) * 292 + (col / 256) * 292 + 4 + col % 256];
                         acc += code * qx;
                     }
@@ -487,8 +540,8 @@ int orc_scales_matrix(int fmt, const uint8_t* w, int64_t rows, int64_t cols, int
 
 /*
  * The integer formulation of one row dot, summed per 256 super-block in fp64:
- *   Q4_K/Q2_K: d_x * (d * sum_j sc_j isum_j - dmin * sum_j m_j bsum_j)
- *   Q6_K:      d_x * d * sum_j sc_j isum_j
+ *   Q4_K/Q5_K/Q2_K: d_x * (d * sum_j sc_j isum_j - dmin * sum_j m_j bsum_j)
+ *   Q6_K/Q3_K:      d_x * d * sum_j sc_j isum_j (isum over the codes q - offset)
  *   Q8_0:      d_x * sum_b d_b isum_b
  * Used only to check that it equals the fp64 dequantised dot.
  */
@@ -527,7 +580,7 @@ double orc_dot_intform(int fmt, const uint8_t* wrow, int64_t cols, const uint8_t
             for (j = 0; j < 256 / sbw; j++) {
                 int32_t is = 0, bs = 0;
                 for (e = 0; e < sbw; e++) {
-                    int code = (fmt == F_Q6_K) ? q[j * sbw + e] - 32 : q[j * sbw + e];
+                    int code = q[j * sbw + e] - code_offset(fmt);
                     is += code * qx[j * sbw + e];
                 }
                 for (e = 0; e < sbw / 16; e++)

@@ -26,15 +26,15 @@ from typing import Dict, List, Optional
 import numpy as np
 
 # Format ids (same values as the C header's moeq_wfmt).
-Q4_K, Q6_K, Q2_K, Q8_0 = 1, 2, 3, 4
-FMT_NAMES = {Q4_K: "Q4_K", Q6_K: "Q6_K", Q2_K: "Q2_K", Q8_0: "Q8_0"}
+Q4_K, Q6_K, Q2_K, Q8_0, Q3_K, Q5_K = 1, 2, 3, 4, 5, 6
+FMT_NAMES = {Q4_K: "Q4_K", Q6_K: "Q6_K", Q2_K: "Q2_K", Q8_0: "Q8_0", Q3_K: "Q3_K", Q5_K: "Q5_K"}
 
 # Gating ids (same values as moeq_gating).
 SOFTMAX_TOPK, SOFTMAX_ALL, SIGMOID_TOPK = 0, 1, 2
 
 # Bytes per block and weights per block of each exchange format.
-BLOCK_BYTES = {Q4_K: 144, Q6_K: 210, Q2_K: 84, Q8_0: 34}
-BLOCK_WEIGHTS = {Q4_K: 256, Q6_K: 256, Q2_K: 256, Q8_0: 32}
+BLOCK_BYTES = {Q4_K: 144, Q6_K: 210, Q2_K: 84, Q8_0: 34, Q3_K: 110, Q5_K: 176}
+BLOCK_WEIGHTS = {Q4_K: 256, Q6_K: 256, Q2_K: 256, Q8_0: 32, Q3_K: 256, Q5_K: 256}
 Q8K_BLOCK_BYTES = 292
 
 # Byte offsets of fp16 scale fields inside a block, with the draw range of each:
@@ -44,6 +44,8 @@ _FP16_FIELDS = {
     Q2_K: [(0, 1.0, 1e-3), (2, 1.5, 1e-3)],    # d, dmin
     Q6_K: [(0, 1.0, 1e-5)],                    # d
     Q8_0: [(0, 1.0, 1e-4)],                    # d
+    Q3_K: [(0, 1.0, 3e-4)],                    # d
+    Q5_K: [(0, 1.0, 5e-5), (2, 7.5, 5e-5)],    # d, dmin
 }
 
 # Stream roles, mixed into the seed so every tensor has an independent stream.

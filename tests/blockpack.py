@@ -12,10 +12,15 @@ Layouts (little-endian):
               (byte 64h+i = lo(128h+i) | lo(128h+64+i) << 4), 64 B high pairs
               (byte 32h+i bits 2s..2s+1 = hi(128h+32s+i))
   Q8_0  34 B: f16 d, 32 x int8
+  Q3_K 110 B: f16 d, 12 B bit stream (sixteen 6-bit values sc + 32), 64 B low
+              pairs (byte 32h+i bits 2s..2s+1 = low2(128h+32s+i)), 32 B high
+              bits (byte i bit b = bit 2 of element 32b+i); w = d*sc*(q-4)
+  Q5_K 176 B: the Q4_K bytes of the low nibbles, then 32 B high bits (byte i
+              bit b = bit 4 of element 32b+i)
 """
 import numpy as np
 
-Q4_K, Q6_K, Q2_K, Q8_0 = 1, 2, 3, 4
+Q4_K, Q6_K, Q2_K, Q8_0, Q3_K, Q5_K = 1, 2, 3, 4, 5, 6
 
 
 def f16_bytes(v: float) -> bytes:
@@ -66,7 +71,35 @@ def pack_q80(d, q) -> bytes:
     return f16_bytes(d) + np.array(q, dtype=np.int8).tobytes()
 
 
+def _high_bits(q, bit) -> bytes:
+    qh = bytearray(32)
+    for e in range(256):
+        qh[e % 32] |= ((int(q[e]) >> bit) & 1) << (e // 32)
+    return bytes(qh)
+
+
+def pack_q3k(d, sc, q) -> bytes:
+    """sc: sixteen signed scales in [-32, 31]; q: 256 codes in [0, 7]."""
+    assert len(sc) == 16 and len(q) == 256
+    bits = 0
+    for j in range(16):
+        assert -32 <= int(sc[j]) <= 31
+        bits |= (int(sc[j]) + 32) << (6 * j)
+    ql = bytearray(64)
+    for h in range(2):
+        for s in range(4):
+            for i in range(32):
+                ql[32 * h + i] |= (int(q[128 * h + 32 * s + i]) & 3) << (2 * s)
+    return f16_bytes(d) + bits.to_bytes(12, "little") + bytes(ql) + _high_bits(q, 2)
+
+
+def pack_q5k(d, dmin, sc, m, q) -> bytes:
+    """q: 256 codes in [0, 31]; the rest as Q4_K."""
+    assert all(0 <= int(v) < 32 for v in q)
+    return pack_q4k(d, dmin, sc, m, [int(v) & 15 for v in q]) + _high_bits(q, 4)
+
+
 def pack_row(fmt, blocks) -> np.ndarray:
     """blocks: list of per-block argument tuples for the format's packer."""
-    fn = {Q4_K: pack_q4k, Q2_K: pack_q2k, Q6_K: pack_q6k, Q8_0: pack_q80}[fmt]
+    fn = {Q4_K: pack_q4k, Q2_K: pack_q2k, Q6_K: pack_q6k, Q8_0: pack_q80, Q3_K: pack_q3k, Q5_K: pack_q5k}[fmt]
     return np.frombuffer(b"".join(fn(*b) for b in blocks), dtype=np.uint8).copy()

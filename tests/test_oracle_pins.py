@@ -15,7 +15,7 @@ import pytest
 from scipy import special
 
 import oracle
-from blockpack import Q2_K, Q4_K, Q6_K, Q8_0, pack_q2k, pack_q4k, pack_q6k, pack_q80, pack_row
+from blockpack import Q2_K, Q3_K, Q4_K, Q5_K, Q6_K, Q8_0, pack_q2k, pack_q4k, pack_q6k, pack_q80, pack_row
 from quantized_moe_expert_router_amd import synthetic as syn
 
 GOLDEN = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "blocks.json")))
@@ -66,6 +66,17 @@ def _all_values_blocks(fmt, rng):
             sc = [((v + 7 * j) % 256) - 128 for j in range(16)]
             q = [(v + i) % 64 for i in range(256)]
             out.append((0.125, sc, q))
+    elif fmt == Q3_K:
+        for v in range(64):
+            sc = [((v + 5 * j) % 64) - 32 for j in range(16)]
+            q = [(v + i) % 8 for i in range(256)]
+            out.append((0.125, sc, q))
+    elif fmt == Q5_K:
+        for v in range(64):
+            sc = [(v + j) % 64 for j in range(8)]
+            m = [(v + 3 * j + 1) % 64 for j in range(8)]
+            q = [(v + i) % 32 for i in range(256)]
+            out.append((float(rng.uniform(1, 2)) * 1e-3, float(rng.uniform(1, 2)) * 1e-3, sc, m, q))
     else:
         for v in range(8):
             q = [((v * 32 + i) % 256) - 128 for i in range(32)]
@@ -73,7 +84,7 @@ def _all_values_blocks(fmt, rng):
     return out
 
 
-@pytest.mark.parametrize("fmt", [Q4_K, Q2_K, Q6_K, Q8_0])
+@pytest.mark.parametrize("fmt", [Q4_K, Q2_K, Q6_K, Q8_0, Q3_K, Q5_K])
 def test_encode_decode_roundtrip_all_codes(fmt):
     rng = np.random.default_rng(7)
     blocks = _all_values_blocks(fmt, rng)
@@ -81,12 +92,13 @@ def test_encode_decode_roundtrip_all_codes(fmt):
     bb = syn.BLOCK_BYTES[fmt]
     for n, args in enumerate(blocks):
         d, dmin, sc, m, q = oracle.block_codes(fmt, row[n * bb:(n + 1) * bb])
-        if fmt in (Q4_K, Q2_K):
+        if fmt in (Q4_K, Q2_K, Q5_K):
             dd, dm, esc, em, eq = args
             assert dmin == float(np.float16(dm))
             assert list(m) == list(em)
-        elif fmt == Q6_K:
+        elif fmt in (Q6_K, Q3_K):
             dd, esc, eq = args
+            assert not m.any()
         else:
             dd, eq = args
             esc = [1]
@@ -95,7 +107,7 @@ def test_encode_decode_roundtrip_all_codes(fmt):
         assert list(q) == list(eq)
 
 
-@pytest.mark.parametrize("fmt", [Q4_K, Q2_K, Q6_K, Q8_0])
+@pytest.mark.parametrize("fmt", [Q4_K, Q2_K, Q6_K, Q8_0, Q3_K, Q5_K])
 def test_scales_matrix_returns_encoded_scales_and_mins(fmt):
     """Every block's decoded sub-block scales and mins, for a matrix built by
     the independent encoder from known codes."""
@@ -109,9 +121,9 @@ def test_scales_matrix_returns_encoded_scales_and_mins(fmt):
     sc, m = oracle.scales_matrix(fmt, W, rows, cols)
     for n, args in enumerate(blocks[:rows * per_row]):
         r, b = divmod(n, per_row)
-        if fmt in (Q4_K, Q2_K):
+        if fmt in (Q4_K, Q2_K, Q5_K):
             esc, em = args[2], args[3]
-        elif fmt == Q6_K:
+        elif fmt in (Q6_K, Q3_K):
             esc, em = args[1], [0] * 16
         else:
             esc, em = [1], [0]
@@ -222,6 +234,10 @@ def _unit_blocks(fmt, rng, nblk):
             out.append((1.0, 0.0, [1] * 16, [0] * 16, rng.integers(0, 4, 256)))
         elif fmt == Q6_K:
             out.append((1.0, [1] * 16, rng.integers(0, 64, 256)))
+        elif fmt == Q3_K:
+            out.append((1.0, [1] * 16, rng.integers(0, 8, 256)))
+        elif fmt == Q5_K:
+            out.append((1.0, 0.0, [1] * 8, [0] * 8, rng.integers(0, 32, 256)))
         else:
             for _ in range(8):
                 out.append((1.0, rng.integers(-128, 128, 32)))
@@ -229,10 +245,12 @@ def _unit_blocks(fmt, rng, nblk):
 
 
 def _unit_ints(fmt, blocks):
-    if fmt == Q4_K or fmt == Q2_K:
+    if fmt in (Q4_K, Q2_K, Q5_K):
         return np.concatenate([np.asarray(b[4]) for b in blocks])
     if fmt == Q6_K:
         return np.concatenate([np.asarray(b[2]) - 32 for b in blocks])
+    if fmt == Q3_K:
+        return np.concatenate([np.asarray(b[2]) - 4 for b in blocks])
     return np.concatenate([np.asarray(b[1]) for b in blocks])
 
 
@@ -243,7 +261,7 @@ def _int_grid_x(rng, n):
     return x
 
 
-@pytest.mark.parametrize("fmt", [Q4_K, Q2_K, Q6_K, Q8_0])
+@pytest.mark.parametrize("fmt", [Q4_K, Q2_K, Q6_K, Q8_0, Q3_K, Q5_K])
 def test_textbook_reduction_integer_matvec(fmt):
     """Unit scales, zero mins, d = d_x = 1: the dequantised dot is the plain integer matvec."""
     rng = np.random.default_rng(20 + fmt)
@@ -271,7 +289,7 @@ def test_textbook_reduction_integer_matvec(fmt):
     assert np.array_equal(sd, ref_sd)
 
 
-@pytest.mark.parametrize("fmt", [Q4_K, Q2_K, Q6_K, Q8_0])
+@pytest.mark.parametrize("fmt", [Q4_K, Q2_K, Q6_K, Q8_0, Q3_K, Q5_K])
 def test_integer_form_equals_fp64_dequant_dot(fmt):
     rng = np.random.default_rng(30 + fmt)
     rows, cols = 16, 1024
@@ -288,7 +306,7 @@ def test_integer_form_equals_fp64_dequant_dot(fmt):
 
 
 def test_cross_format_identity():
-    """Weights representable in Q4_K, Q2_K and Q8_0 give bit-identical fp64 dots."""
+    """Weights representable in Q4_K, Q2_K, Q3_K, Q5_K and Q8_0 give bit-identical fp64 dots."""
     rng = np.random.default_rng(40)
     cols = 512
     q2 = rng.integers(0, 4, cols)
@@ -298,15 +316,20 @@ def test_cross_format_identity():
     b4 = [(0.25, 0.25, [1] * 8, [1] * 8, q2[i * 256:(i + 1) * 256]) for i in range(2)]
     # Q8_0: d = 1/4, q = q2 - 1
     b8 = [(0.25, (q2[i * 32:(i + 1) * 32] - 1)) for i in range(cols // 32)]
+    # Q3_K: d = 1/4, sc = 1, q = q2 + 3  ->  (q2 + 3 - 4) / 4
+    b3 = [(0.25, [1] * 16, q2[i * 256:(i + 1) * 256] + 3) for i in range(2)]
+    # Q5_K: as Q4_K, the high bit never set
+    b5 = [(0.25, 0.25, [1] * 8, [1] * 8, q2[i * 256:(i + 1) * 256]) for i in range(2)]
     r2, r4, r8 = pack_row(Q2_K, b2), pack_row(Q4_K, b4), pack_row(Q8_0, b8)
+    r3, r5 = pack_row(Q3_K, b3), pack_row(Q5_K, b5)
     w2 = oracle.dequant_row(Q2_K, r2, cols)
     assert np.array_equal(w2, (q2 - 1) / 4.0)
-    assert np.array_equal(w2, oracle.dequant_row(Q4_K, r4, cols))
-    assert np.array_equal(w2, oracle.dequant_row(Q8_0, r8, cols))
+    for f, r in ((Q4_K, r4), (Q8_0, r8), (Q3_K, r3), (Q5_K, r5)):
+        assert np.array_equal(w2, oracle.dequant_row(f, r, cols)), f
     v = oracle.dequant_q8K(oracle.quantize_q8K(rng.standard_normal(cols).astype(np.float32)), cols)[0]
     a = oracle.matvec(Q2_K, r2, 1, cols, v)
-    assert np.array_equal(a, oracle.matvec(Q4_K, r4, 1, cols, v))
-    assert np.array_equal(a, oracle.matvec(Q8_0, r8, 1, cols, v))
+    for f, r in ((Q4_K, r4), (Q8_0, r8), (Q3_K, r3), (Q5_K, r5)):
+        assert np.array_equal(a, oracle.matvec(f, r, 1, cols, v)), f
 
 
 # -------------------------------------------------------------------- router
@@ -430,6 +453,14 @@ def _grid_matrix(fmt, rng, rows, cols):
                 q = rng.integers(0, 4, 256)
                 bl.append((2.0 ** -6, 2.0 ** -6, [2] * 16, [3] * 16, q))
                 ints.append(2 * q - 3)
+            elif fmt == Q3_K:     # w = 2^-6 * -3 * (q - 4)
+                q = rng.integers(0, 8, 256)
+                bl.append((2.0 ** -6, [-3] * 16, q))
+                ints.append(-3 * (q - 4))
+            elif fmt == Q5_K:     # w = 2^-6 * q - 2^-6 * 16
+                q = rng.integers(0, 32, 256)
+                bl.append((2.0 ** -6, 2.0 ** -6, [1] * 8, [16] * 8, q))
+                ints.append(q - 16)
             else:
                 for b in range(8):
                     q = rng.integers(-8, 9, 32)
@@ -439,7 +470,8 @@ def _grid_matrix(fmt, rng, rows, cols):
     return np.stack(blocks), np.concatenate(ints).reshape(rows, cols) * 2.0 ** -6
 
 
-@pytest.mark.parametrize("fmts", [(Q4_K, Q6_K, Q8_0), (Q2_K, Q4_K, Q2_K), (Q8_0, Q8_0, Q4_K)])
+@pytest.mark.parametrize("fmts", [(Q4_K, Q6_K, Q8_0), (Q2_K, Q4_K, Q2_K), (Q8_0, Q8_0, Q4_K),
+                                  (Q3_K, Q5_K, Q3_K), (Q5_K, Q3_K, Q5_K)])
 def test_ffn_special_case_reduces_to_numpy_and_scipy(fmts):
     """Grid weights and integer-grid x make every step checkable with numpy matmul,
     scipy's expit and a by-hand read of the q8_K(h) bytes."""
