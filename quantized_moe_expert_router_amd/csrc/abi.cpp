@@ -19,7 +19,9 @@ constexpr int kMaxK = 32;
 constexpr int64_t kMaxStack = 4096;   // layers per moeq_moe_stack call
 constexpr int kRowBlock = 64;     // rows per expert-major down work item
 
-bool fmt_ok(int f) { return f == MOEQ_Q4_K || f == MOEQ_Q6_K || f == MOEQ_Q2_K || f == MOEQ_Q8_0; }
+bool fmt_ok(int f) {
+  return f == MOEQ_Q4_K || f == MOEQ_Q6_K || f == MOEQ_Q2_K || f == MOEQ_Q8_0 || f == MOEQ_Q3_K || f == MOEQ_Q5_K;
+}
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 int hip_status(int rc) { return rc == 0 ? MOEQ_OK : (rc == -2 ? MOEQ_E_UNSUPPORTED : MOEQ_E_HIP); }
 
@@ -326,7 +328,7 @@ int ffn_enqueue(const moeq_ffn_desc* d, const void* x_q8K, const int32_t* topk_i
     const int fg = shared_exp ? d->sh_fmt_gate : d->fmt_gate, fd = shared_exp ? d->sh_fmt_down : d->fmt_down;
     const int64_t Fx = shared_exp ? d->F_shared : d->F;
     const int64_t tiles = shared_exp ? (d->T + kThinT - 1) / kThinT : L.max_thin;
-    return fg != FQ6K && fd != FQ6K && d->H / 256 <= kHfMaxBlocks && Fx / 256 <= kHfMaxBlocks &&
+    return !fmt_sub_scaled(fg) && !fmt_sub_scaled(fd) && d->H / 256 <= kHfMaxBlocks && Fx / 256 <= kHfMaxBlocks &&
            tiles * (Fx / 256) < kHfMaxWorkgroups;
   };
   auto mfma_launch = [&](int mode, bool shared_exp, bool thin, hipStream_t st, bool fold = false) -> int {

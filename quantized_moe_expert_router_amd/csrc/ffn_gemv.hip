@@ -474,6 +474,8 @@ __global__ __launch_bounds__(256) void k_down_rows1(DownArgs a) {
     case FQ6K: { MOEQ_SWITCH_TT(M, FQ6K) } break;             \
     case FQ2K: { MOEQ_SWITCH_TT(M, FQ2K) } break;             \
     case FQ80: { MOEQ_SWITCH_TT(M, FQ80) } break;             \
+    case FQ3K: { MOEQ_SWITCH_TT(M, FQ3K) } break;             \
+    case FQ5K: { MOEQ_SWITCH_TT(M, FQ5K) } break;             \
     default: return -2;                                       \
   }
 
@@ -508,6 +510,8 @@ int launch_gateup1(int fmt, int nper, int cpl, dim3 grid, const GateUpArgs& a, h
     case FQ6K: { MOEQ_G1_NP(FQ6K) } break;
     case FQ2K: { MOEQ_G1_NP(FQ2K) } break;
     case FQ80: { MOEQ_G1_NP(FQ80) } break;
+    case FQ3K: { MOEQ_G1_NP(FQ3K) } break;
+    case FQ5K: { MOEQ_G1_NP(FQ5K) } break;
     default: return -2;
   }
   return hipGetLastError() == hipSuccess ? 0 : -1;

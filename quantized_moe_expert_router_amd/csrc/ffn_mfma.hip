@@ -34,6 +34,12 @@
 //         (exact int32 dot of q with x), scaled by sc_j in int32; the -32 part
 //         is 32 * sum_j sc_j bsum_j, from the same split-sum MFMA pair.
 //   Q8_0  w = d_b*q: one MFMA per 32-block, scaled by d_b in fp64.
+//   Q3_K  w = d*sc_j*(q-4), signed six-bit sc, q < 8: as Q6_K (sc*q does not
+//         fit in int8): one 16-deep MFMA per sub-block on the codes q, scaled
+//         by sc_j in int32; the -4 part is 4 * sum_j sc_j bsum_j.
+//   Q5_K  w = d*sc_j*q - dmin*m_j, q = l + 16h < 32: Q4_K's two pre-scaled
+//         sums on the nibbles l plus a third on h*sc_j (< 64), chained on one
+//         accumulator: S1 = 8*(2*P_h + P_hi) + P_lo; the min term as Q4_K's.
 // term per super-block = d_x * (d * S1 - dmin * S2) in fp64, summed over the
 // super-blocks in order; h = fl32(silu(g) * u); y rows in fp32.
 #include <type_traits>
@@ -385,6 +391,174 @@ template <> struct Mf<FQ80> {
     }
   }
 };
+
+// Sum over the sub-blocks of sc_j * (the sub-block's exact MFMA dot), for
+// a format whose scale does not fit into pre-scaled int8 weights (Q3_K).  Two-deep pipeline: the MFMA of sub-block jj + 1 is issued before
+// the result of jj is scaled; the empty asm statement on the running sums
+// (with a memory clobber) ends each step, so the next step's LDS operand load
+// and MFMA stay behind it and at most two MFMA results are live.
+template <class M>
+__device__ __forceinline__ v16i sub_scaled_sum(const typename M::Wt& w, int g, const uint8_t* qrow) {
+  v16i acc = {0};
+  v16i prev = M::sub_mfma(w, g, qrow, 0);
+#pragma unroll
+  for (int jj = 1; jj <= M::NSUB; ++jj) {
+    v16i cur;
+    if (jj < M::NSUB) cur = M::sub_mfma(w, g, qrow, jj);
+    const int sc = M::sub_scale(w, jj - 1);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[r] += __mul24(sc, prev[r]);   // |sc| < 64, |P| < 2^17: exact
+    asm volatile("" : "+v"(acc) : : "memory");
+    if (jj < M::NSUB) prev = cur;
+  }
+  return acc;
+}
+
+template <> struct Mf<FQ3K> {
+  static constexpr int NBSP = 16, NSUB = 16;
+  struct Wt { uint4 l[4]; uint4 x[2]; uint4 sc; uint32_t d; };
+  // Every lane loads the row's whole super-block: all 16 low-pair words (one
+  // per sub-block), the 8 high-bit words, the scales and d.
+  __device__ static Wt load(const uint8_t* W, int64_t N, int64_t nbK, int64_t row, int64_t sb, int) {
+    const size_t nsb = (size_t)(N * nbK);
+    const RowSplit rs = row_split(row, nbK, sb);
+    const uint32_t lr = rs.r * (uint32_t)nbK;
+    const uint8_t* Wb = wave_uni_ptr(W);
+    const uint8_t* px = Wb + align256(nsb * 64);
+    const uint8_t* ps = px + align256(nsb * 32);
+    const uint8_t* pd = ps + align256(nsb * 16);
+    Wt w;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) w.l[k] = gld_u4(Wb + rs.su * 64 + (lr * 64u + 16u * (uint32_t)k));
+#pragma unroll
+    for (int k = 0; k < 2; ++k) w.x[k] = gld_u4(px + rs.su * 32 + (lr * 32u + 16u * (uint32_t)k));
+    w.sc = gld_u4(ps + rs.su * 16 + lr * 16u);
+    w.d = gld_u16(pd + rs.su * 2 + lr * 2u);
+    return w;
+  }
+  __device__ static uint32_t pick(const uint4& v, int i) { return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w; }
+  // Sub-block jj (16 elements): lane half g holds its elements 8g .. 8g+7,
+  // words i = 2g, 2g+1 of the sub-block's low-pair word, high bits 4(jj%2)+i
+  // of chunk jj/2's high word.
+  __device__ __forceinline__ static v16i sub_mfma(const Wt& w, int g, const uint8_t* qrow, int jj) {
+    const uint32_t lw = pick(w.l[jj >> 2], jj & 3);
+    const uint32_t hx = pick(w.x[jj >> 3], (jj >> 1) & 3);
+    uint32_t q[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const int i = 2 * g + t;
+      q[t] = ((lw >> (2 * i)) & 0x03030303u) | (((hx >> (4 * (jj & 1) + i)) & 0x01010101u) << 2);
+    }
+    const long b = (long)(((uint64_t)q[1] << 32) | q[0]);
+    const long a = *reinterpret_cast<const long*>(qrow + 16 * jj + 8 * g);
+    const v16i z16 = {0};
+    return mfma_k16(a, b, z16);
+  }
+  __device__ __forceinline__ static int sub_scale(const Wt& w, int jj) {
+    return (int)(int8_t)((pick(w.sc, jj >> 2) >> (8 * (jj & 3))) & 0xFF);
+  }
+  // The exact integer parts: s1 = sum_j sc_j isum_j over the codes q - 4,
+  // s2 = sum_j sc_j bsum_j (split-sum MFMA pair with the int8 scales).
+  struct Ints { v16i s1, s2; };
+  __device__ __forceinline__ static Ints ints(const Wt& w, int g, const uint8_t* qrow, const v4i abs) {
+    const v16i P = sub_scaled_sum<Mf<FQ3K>>(w, g, qrow);
+    const v16i z16 = {0};
+    const v4i bm = {(int)w.sc.x, (int)w.sc.y, (int)w.sc.z, (int)w.sc.w}, zero = {0, 0, 0, 0};
+    const v16i xl = mfma_k32(abs, g == 0 ? bm : zero, z16);
+    const v16i xh = mfma_k32(abs, g == 1 ? bm : zero, z16);
+    Ints o;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      o.s2[r] = xl[r] + 64 * xh[r];
+      o.s1[r] = P[r] - 4 * o.s2[r];
+    }
+    return o;
+  }
+  template <int NQ>
+  __device__ static void mac(const Wt& w, int g, const uint8_t* qrow, const v4i abs, const double* dxs,
+                             int n, double* acc) {
+    const Ints I = ints(w, g, qrow, abs);
+    const double d = half_bits_to_float(w.d);
+    MOEQ_COMBINE(acc[r] += dx * (d * (double)I.s1[r]))
+  }
+};
+
+template <> struct Mf<FQ5K> {
+  static constexpr int NBSP = 8;   // one block sum per 32-sub-block, as Q4_K
+  struct Wt { uint4 c[4]; uint4 x; uint4 h; };
+  // Q4_K's loads (lane half g: chunks 2p+g) plus that half's four bit-4 words
+  // (the plane keeps the words of chunks g, g+2, g+4, g+6 together).
+  __device__ static Wt load(const uint8_t* W, int64_t N, int64_t nbK, int64_t row, int64_t sb, int g) {
+    const size_t nsb = (size_t)(N * nbK);
+    const RowSplit rs = row_split(row, nbK, sb);
+    const uint32_t lr = rs.r * (uint32_t)nbK;
+    const uint8_t* Wb = wave_uni_ptr(W);
+    const uint8_t* px = Wb + align256(nsb * 128);
+    const uint8_t* ph = px + align256(nsb * 32);
+    Wt w;
+#pragma unroll
+    for (int p = 0; p < 4; ++p) w.c[p] = gld_u4(Wb + rs.su * 128 + (lr * 128u + 16u * (uint32_t)(2 * p + g)));
+    w.x = gld_u4(px + rs.su * 32 + (lr * 32u + 16u * (uint32_t)g));
+    w.h = gld_u4(ph + rs.su * 16 + lr * 16u);
+    return w;
+  }
+  // The exact integer parts: s1 = sum_j sc_j isum_j, s2 = sum_j m_j bsum_j.
+  // q = l + 16 h (l the nibble, h bit 4) and sc = 8 sh + sl (sh, sl < 8):
+  // sc_j isum_j = sum (l sl) x + 8 sum (l sh) x + 16 sum (h sc) x, every
+  // weight byte below 128.  The three sums run as one chain of MFMAs on one
+  // accumulator: the h*sc sum, doubled, is the input of the l*sh MFMAs, and
+  // that result times 8 the input of the l*sl MFMAs, so
+  // s1 = 8 (2 P_h + P_hi) + P_lo with a single running sum.
+  // MFMA 2p+s: lane half g holds sub-block 2p+g, nibble s.
+  struct Ints { v16i s1, s2; };
+  __device__ __forceinline__ static Ints ints(const Wt& w, int g, const uint8_t* qrow, const v4i abs) {
+    const uint64_t lo = (uint64_t)w.h.y | ((uint64_t)w.h.z << 32);
+    const uint64_t hi = (uint64_t)w.h.z | ((uint64_t)w.h.w << 32);
+    const uint32_t hx[4] = {w.x.x, w.x.y, w.x.z, w.x.w};
+    v16i acc = {0};
+#pragma unroll
+    for (int ph = 0; ph < 3; ++ph) {
+      if (ph > 0) acc = (ph == 1 ? 2 : 8) * acc;
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        const uint32_t sc = (uint32_t)(lo >> (6 * (2 * p + g))) & 63;
+        const uint32_t c[4] = {w.c[p].x, w.c[p].y, w.c[p].z, w.c[p].w};
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+          v4i b;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            if (ph == 0) b[i] = (int)bytes_times((hx[p] >> (4 * s + i)) & 0x01010101u, sc);
+            else b[i] = (int)bytes_times((c[i] >> (4 * s)) & 0x0F0F0F0Fu, ph == 1 ? sc >> 3 : sc & 7);
+          }
+          acc = mfma_k32(lds_v4(qrow + 64 * p + 32 * g + 16 * s), b, acc);
+        }
+      }
+    }
+    uint32_t m0 = 0, m1 = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      m0 |= (uint32_t)((hi >> (16 + 6 * j)) & 63) << (8 * j);
+      m1 |= (uint32_t)((hi >> (16 + 6 * (j + 4))) & 63) << (8 * j);
+    }
+    const v4i bm = {(int)m0, (int)m1, 0, 0}, zero = {0, 0, 0, 0};
+    const v16i z16 = {0};
+    const v16i xl = mfma_k32(abs, g == 0 ? bm : zero, z16);
+    const v16i xh = mfma_k32(abs, g == 1 ? bm : zero, z16);
+    return Ints{acc, xl + 64 * xh};
+  }
+  template <int NQ>
+  __device__ static void mac(const Wt& w, int g, const uint8_t* qrow, const v4i abs, const double* dxs,
+                             int n, double* acc) {
+    const Ints I = ints(w, g, qrow, abs);
+    const double d = half_bits_to_float(w.h.x & 0xFFFF), dmin = half_bits_to_float(w.h.x >> 16);
+    MOEQ_COMBINE(acc[r] += dx * (d * (double)I.s1[r] - dmin * (double)I.s2[r]))
+  }
+};
+
+// Formats whose tiles scale each sub-block's MFMA result in int32 (more
+// registers per lane): no 8-row ring or fp32-h kernels for them.
+template <int F> constexpr bool kSubScaled = F == FQ6K || F == FQ3K;
 
 // ------------------------------------------------------------ staging
 
@@ -1082,6 +1256,8 @@ int launch_mfma_ints(int fmt, const void* W, int64_t N, int64_t K, const void* x
     case FQ6K: hipLaunchKernelGGL(k_mfma_ints<FQ6K>, grid, dim3(512), 0, s, w8, N, K, x8, n_x, out); break;
     case FQ2K: hipLaunchKernelGGL(k_mfma_ints<FQ2K>, grid, dim3(512), 0, s, w8, N, K, x8, n_x, out); break;
     case FQ80: hipLaunchKernelGGL(k_mfma_ints<FQ80>, grid, dim3(512), 0, s, w8, N, K, x8, n_x, out); break;
+    case FQ3K: hipLaunchKernelGGL(k_mfma_ints<FQ3K>, grid, dim3(512), 0, s, w8, N, K, x8, n_x, out); break;
+    case FQ5K: hipLaunchKernelGGL(k_mfma_ints<FQ5K>, grid, dim3(512), 0, s, w8, N, K, x8, n_x, out); break;
     default: return -2;
   }
   return hipGetLastError() == hipSuccess ? 0 : -1;
@@ -1105,13 +1281,14 @@ int launch_mfma_plan(const int32_t* active, const int32_t* offsets, int thr, int
 
 namespace {
 
-// Kernel choice for one (format, mode, tile height): 8-row tiles of every
-// format but Q6_K (whose per-sub-block scaling needs more registers) run the
-// ring kernels when their activations fit in LDS, gate/up of Q2_K and Q8_0
-// on 16 waves; everything else runs the one-unit-ahead tiles.
+// Kernel choice for one (format, mode, tile height): 8-row tiles of the
+// formats with pre-scaled int8 weights (not Q6_K or Q3_K, whose
+// per-sub-block scaling needs more registers) run the ring kernels when their
+// activations fit in LDS, gate/up of Q2_K and Q8_0 on 16 waves; everything
+// else runs the one-unit-ahead tiles.
 template <int F, int MD, int TM>
 void launch_tile(dim3 grid, const MfmaArgs& a, int64_t nbK, bool hf, hipStream_t s) {
-  if constexpr (TM == 8 && F != FQ6K) {
+  if constexpr (TM == 8 && !kSubScaled<F>) {
     if (hf) {
       if constexpr (MD == 0) hipLaunchKernelGGL((k_mfma_hf_gateup<F>), grid, dim3(256), 0, s, a);
       else hipLaunchKernelGGL((k_mfma_hf_down<F>), grid, dim3(512), 0, s, a);
@@ -1148,13 +1325,16 @@ void launch_fmt(int mode, bool thin, bool hf, dim3 grid, const MfmaArgs& a, int6
 int launch_mfma(int fmt, int mode, bool thin, bool hf, dim3 grid, const MfmaArgs& a, hipStream_t s) {
   if (grid.x == 0 || grid.y == 0) return 0;
   const int64_t nbK = a.K / 256;
-  // the fp32-h kernels: resident 8-row tiles, not Q6_K (checked by the caller too)
-  if (hf && (!thin || fmt == FQ6K || nbK > kRes(8) || a.hf == nullptr)) return -2;
+  // the fp32-h kernels: resident 8-row tiles of the pre-scaled formats
+  // (checked by the caller too)
+  if (hf && (!thin || fmt_sub_scaled(fmt) || nbK > kRes(8) || a.hf == nullptr)) return -2;
   switch (fmt) {
     case FQ4K: launch_fmt<FQ4K>(mode, thin, hf, grid, a, nbK, s); break;
     case FQ6K: launch_fmt<FQ6K>(mode, thin, false, grid, a, nbK, s); break;
     case FQ2K: launch_fmt<FQ2K>(mode, thin, hf, grid, a, nbK, s); break;
     case FQ80: launch_fmt<FQ80>(mode, thin, hf, grid, a, nbK, s); break;
+    case FQ3K: launch_fmt<FQ3K>(mode, thin, false, grid, a, nbK, s); break;
+    case FQ5K: launch_fmt<FQ5K>(mode, thin, hf, grid, a, nbK, s); break;
     default: return -2;
   }
   return hipGetLastError() == hipSuccess ? 0 : -1;

@@ -31,6 +31,18 @@
 //         d 128 B at 2560: d, dmin at 4 (row % 32)
 //   Q8_0  plane Q 256 B/sb: chunk b = the 32 int8 quants of block b
 //         plane D  16 B/sb: eight fp16 d
+//   Q3_K  plane L  64 B/sb: chunk j = 2 words; word t = sub-block 2j+t, bits
+//           8b+2i = low pair of its element 4i+b
+//         plane X  32 B/sb: chunk j = 1 word, bit 8b+i = high bit of chunk
+//           element 4i+b (i = 0..7)
+//         plane S  16 B/sb: int8 scales (sc_j, the stored value - 32);
+//         plane D 2 B/sb: fp16 d
+//   Q5_K  plane Q 128 B/sb: Q4_K's, on the low nibbles
+//         plane X  32 B/sb: one word per chunk j, at word 4 (j % 2) + j / 2 (the
+//           even chunks first: a matrix-core lane half reads its four words
+//           at once); bits 8b+i / 8b+4+i = bit 4 of chunk elements 4i+b /
+//           16+4i+b (the two nibbles of word i, byte b)
+//         plane H  16 B/sb: the exchange header as is (d, dmin, 12 B scales)
 #pragma once
 #include "common.hpp"
 
@@ -55,6 +67,8 @@ __host__ __device__ inline Geo geo_of(int fmt) {
     case FQ6K: return Geo{32, 4, {128, 64, 16, 2}, 1};
     case FQ2K: return Geo{64, 1, {84, 0, 0, 0}, 32};   // one plane of 2688-byte units
     case FQ80: return Geo{32, 2, {256, 16, 0, 0}, 1};
+    case FQ3K: return Geo{32, 4, {64, 32, 16, 2}, 1};
+    case FQ5K: return Geo{32, 3, {128, 32, 16, 0}, 1};
   }
   return Geo{0, 0, {0, 0, 0, 0}, 1};
 }
@@ -213,6 +227,82 @@ template <> struct Fmt<FQ80> : RowMajor<32> {
   __device__ static double term(const W& w, int, const int* is, const int*, double dx) {
     double d = half_bits_to_float(w.d);
     return dx * (d * (double)is[0]);
+  }
+};
+
+// ---------------------------------------------------------------- Q3_K
+template <> struct Fmt<FQ3K> : RowMajor<32> {
+  static constexpr int WPC = 32, CPS = 8, XDW = 8, NBS = 2, SPC = 2;
+  __device__ static constexpr int sub_of(int j, int t) { return j * SPC + t; }
+  struct W { uint2 l; uint32_t x; uint32_t sc; uint32_t d; };
+  __device__ static W load(const uint8_t* m, int64_t rows, int64_t nb, int64_t row, int64_t sb, int j) {
+    const size_t nsb = (size_t)(rows * nb), sbi = (size_t)(row * nb + sb);
+    const uint8_t* px = m + align256(nsb * 64);
+    const uint8_t* ps = px + align256(nsb * 32);
+    const uint8_t* pd = ps + align256(nsb * 16);
+    W w;
+    w.l = gld_u2(m + sbi * 64 + 8 * j);
+    w.x = gld_u32(px + sbi * 32 + 4 * j);
+    w.sc = gld_u16(ps + sbi * 16 + 2 * j);
+    w.d = gld_u16(pd + sbi * 2);
+    return w;
+  }
+  // q = low pair | high bit << 2 (0..7), four elements per word
+  __device__ static void isums(const W& w, const int* xw, const int* bs, int* is) {
+    const uint32_t l[2] = {w.l.x, w.l.y};
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      int a = 0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t q = ((l[t] >> (2 * i)) & 0x03030303u) | (((w.x >> (4 * t + i)) & 0x01010101u) << 2);
+        a = dot4((int)q, xw[4 * t + i], a);
+      }
+      is[t] = a - 4 * bs[t];   // sum (q - 4) q_x
+    }
+  }
+  __device__ static double term(const W& w, int, const int* is, const int*, double dx) {
+    const int sa = (int)(int8_t)(w.sc & 0xFF), sb = (int)(int8_t)(w.sc >> 8);
+    const double d = half_bits_to_float(w.d);
+    return dx * (d * (double)(sa * is[0] + sb * is[1]));
+  }
+};
+
+// ---------------------------------------------------------------- Q5_K
+template <> struct Fmt<FQ5K> : RowMajor<32> {
+  static constexpr int WPC = 32, CPS = 8, XDW = 8, NBS = 2, SPC = 1;
+  __device__ static constexpr int sub_of(int j, int t) { return j * SPC + t; }
+  struct W { uint4 q; uint32_t x; uint4 h; };
+  __device__ static W load(const uint8_t* m, int64_t rows, int64_t nb, int64_t row, int64_t sb, int j) {
+    const size_t nsb = (size_t)(rows * nb), sbi = (size_t)(row * nb + sb);
+    const uint8_t* px = m + align256(nsb * 128);
+    const uint8_t* ph = px + align256(nsb * 32);
+    W w;
+    w.q = gld_u4(m + sbi * 128 + 16 * j);
+    w.x = gld_u32(px + sbi * 32 + 4 * (4 * (j & 1) + (j >> 1)));
+    w.h = gld_u4(ph + sbi * 16);
+    return w;
+  }
+  // q = nibble | bit 4 (0..31)
+  __device__ static void isums(const W& w, const int* xw, const int*, int* is) {
+    const uint32_t q[4] = {w.q.x, w.q.y, w.q.z, w.q.w};
+    int s = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t lo = (q[i] & 0x0F0F0F0Fu) | (((w.x >> i) & 0x01010101u) << 4);
+      const uint32_t hi = ((q[i] >> 4) & 0x0F0F0F0Fu) | (((w.x >> (4 + i)) & 0x01010101u) << 4);
+      s = dot4((int)lo, xw[i], s);
+      s = dot4((int)hi, xw[4 + i], s);
+    }
+    is[0] = s;
+  }
+  __device__ static double term(const W& w, int j, const int* is, const int* bs, double dx) {
+    const uint64_t lo = (uint64_t)w.h.y | ((uint64_t)w.h.z << 32);
+    const uint64_t hi = (uint64_t)w.h.z | ((uint64_t)w.h.w << 32);
+    const int sc = (int)((lo >> (6 * j)) & 63);
+    const int mn = (int)((hi >> (16 + 6 * j)) & 63);
+    const double d = half_bits_to_float(w.h.x & 0xFFFF), dmin = half_bits_to_float(w.h.x >> 16);
+    return dx * (d * (double)(sc * is[0]) - dmin * (double)(mn * (bs[0] + bs[1])));
   }
 };
 

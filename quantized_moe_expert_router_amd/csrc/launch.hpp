@@ -165,6 +165,8 @@ constexpr int kHfRows = 64;
 constexpr int kHfMaxBlocks = 16;   // K (256-blocks) up to which 8-row tiles keep their activations in LDS
 constexpr int64_t kHfMaxWorkgroups = 1024;   // fp32 h only while 256-row gate/up tiles x row blocks stay below this
 int launch_mfma(int fmt, int mode, bool thin, bool hf, dim3 grid, const MfmaArgs& a, hipStream_t s);
+// Formats whose MFMA tiles scale each sub-block's result in int32 (no fp32-h tiles).
+inline bool fmt_sub_scaled(int fmt) { return fmt == FQ6K || fmt == FQ3K; }
 int launch_combine(const float* yp, int64_t T, int64_t H, int k, int has_shared, float* y, int accumulate,
                    hipStream_t s);
 

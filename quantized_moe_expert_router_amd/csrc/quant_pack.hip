@@ -61,6 +61,21 @@ __device__ __forceinline__ int q6k_high2(const uint8_t* b, int e) {
   return (b[146 + 32 * h + i] >> (2 * s)) & 3;
 }
 
+// exchange Q3_K element: low pair (as Q2_K's quants, after a 14-byte head) and high bit
+__device__ __forceinline__ int q3k_low2(const uint8_t* b, int e) {
+  int h = e >> 7, r = e & 127, s = r >> 5, i = r & 31;
+  return (b[14 + 32 * h + i] >> (2 * s)) & 3;
+}
+__device__ __forceinline__ int q3k_high(const uint8_t* b, int e) { return (b[78 + (e & 31)] >> (e >> 5)) & 1; }
+// six-bit value j of the scale stream starting at p
+__device__ __forceinline__ int stream6(const uint8_t* p, int j) {
+  int v = 0;
+  for (int bit = 0; bit < 6; ++bit) v |= ((p[(6 * j + bit) >> 3] >> ((6 * j + bit) & 7)) & 1) << bit;
+  return v;
+}
+// exchange Q5_K element bit 4 (the plane after the Q4_K bytes)
+__device__ __forceinline__ int q5k_high(const uint8_t* b, int e) { return (b[144 + (e & 31)] >> (e >> 5)) & 1; }
+
 __device__ __forceinline__ void st_u32(uint8_t* p, uint32_t v) { *reinterpret_cast<uint32_t*>(p) = v; }
 
 template <int FMT>
@@ -73,7 +88,7 @@ __global__ __launch_bounds__(256) void k_pack(const uint8_t* __restrict__ aos, i
   const int64_t mat = gid / nsb, sbi = gid % nsb;
   const uint8_t* src = aos + gid * sb_bytes_aos;   // (mat*rows + r)*nb + s == gid
   uint8_t* m = packed + mat * mat_bytes;
-  if (FMT == FQ4K) {
+  if (FMT == FQ4K || FMT == FQ5K) {
     for (int j = 0; j < 8; ++j)
       for (int w = 0; w < 4; ++w) {
         uint32_t v = 0;
@@ -83,8 +98,38 @@ __global__ __launch_bounds__(256) void k_pack(const uint8_t* __restrict__ aos, i
         }
         st_u32(m + sbi * 128 + 16 * j + 4 * w, v);
       }
-    uint8_t* ph = m + align256(nsb * 128) + sbi * 16;
+    uint8_t* ph = m + align256(nsb * 128) + (FMT == FQ5K ? align256(nsb * 32) : 0) + sbi * 16;
     for (int i = 0; i < 16; ++i) ph[i] = src[i];
+    if (FMT == FQ5K) {
+      uint8_t* px = m + align256(nsb * 128);
+      for (int j = 0; j < 8; ++j) {
+        uint32_t v = 0;
+        for (int w = 0; w < 4; ++w)
+          for (int b = 0; b < 4; ++b)
+            v |= (uint32_t)(q5k_high(src, 32 * j + 4 * w + b) << (8 * b + w)) |
+                 (uint32_t)(q5k_high(src, 32 * j + 16 + 4 * w + b) << (8 * b + 4 + w));
+        st_u32(px + sbi * 32 + 4 * (4 * (j & 1) + (j >> 1)), v);
+      }
+    }
+  } else if (FMT == FQ3K) {
+    uint8_t* px = m + align256(nsb * 64);
+    uint8_t* ps = px + align256(nsb * 32);
+    uint8_t* pd = ps + align256(nsb * 16);
+    for (int j = 0; j < 8; ++j) {
+      for (int t = 0; t < 2; ++t) {
+        uint32_t v = 0;
+        for (int i = 0; i < 4; ++i)
+          for (int b = 0; b < 4; ++b) v |= (uint32_t)q3k_low2(src, 16 * (2 * j + t) + 4 * i + b) << (8 * b + 2 * i);
+        st_u32(m + sbi * 64 + 8 * j + 4 * t, v);
+      }
+      uint32_t v = 0;
+      for (int i = 0; i < 8; ++i)
+        for (int b = 0; b < 4; ++b) v |= (uint32_t)q3k_high(src, 32 * j + 4 * i + b) << (8 * b + i);
+      st_u32(px + sbi * 32 + 4 * j, v);
+    }
+    for (int j = 0; j < 16; ++j) ps[sbi * 16 + j] = (uint8_t)(int8_t)(stream6(src + 2, j) - 32);
+    pd[sbi * 2] = src[0];
+    pd[sbi * 2 + 1] = src[1];
   } else if (FMT == FQ6K) {
     uint8_t* px = m + align256(nsb * 128);
     uint8_t* ps = px + align256(nsb * 64);
@@ -148,6 +193,8 @@ int launch_pack(int fmt, const void* aos, int64_t n_mats, int64_t rows, int64_t 
     case FQ6K: hipLaunchKernelGGL(k_pack<FQ6K>, dim3(grid), dim3(256), 0, s, a, n_mats, rows, cols, p, mb, (int64_t)210); break;
     case FQ2K: hipLaunchKernelGGL(k_pack<FQ2K>, dim3(grid), dim3(256), 0, s, a, n_mats, rows, cols, p, mb, (int64_t)84); break;
     case FQ80: hipLaunchKernelGGL(k_pack<FQ80>, dim3(grid), dim3(256), 0, s, a, n_mats, rows, cols, p, mb, (int64_t)272); break;
+    case FQ3K: hipLaunchKernelGGL(k_pack<FQ3K>, dim3(grid), dim3(256), 0, s, a, n_mats, rows, cols, p, mb, (int64_t)110); break;
+    case FQ5K: hipLaunchKernelGGL(k_pack<FQ5K>, dim3(grid), dim3(256), 0, s, a, n_mats, rows, cols, p, mb, (int64_t)176); break;
     default: return -2;
   }
   return hipGetLastError() == hipSuccess ? 0 : -1;
@@ -187,6 +234,8 @@ int launch_subdots(int fmt, const void* w, int64_t rows, int64_t cols, const voi
     case FQ6K: hipLaunchKernelGGL(k_subdots<FQ6K>, dim3(grid), dim3(256), 0, s, W, rows, cols, X, n_x, out); break;
     case FQ2K: hipLaunchKernelGGL(k_subdots<FQ2K>, dim3(grid), dim3(256), 0, s, W, rows, cols, X, n_x, out); break;
     case FQ80: hipLaunchKernelGGL(k_subdots<FQ80>, dim3(grid), dim3(256), 0, s, W, rows, cols, X, n_x, out); break;
+    case FQ3K: hipLaunchKernelGGL(k_subdots<FQ3K>, dim3(grid), dim3(256), 0, s, W, rows, cols, X, n_x, out); break;
+    case FQ5K: hipLaunchKernelGGL(k_subdots<FQ5K>, dim3(grid), dim3(256), 0, s, W, rows, cols, X, n_x, out); break;
     default: return -2;
   }
   return hipGetLastError() == hipSuccess ? 0 : -1;

@@ -39,6 +39,10 @@ def test_packed_bytes_and_workspace_queries():
     # Q2_K is laid out in 2688-byte 32-row units: one row pads to a unit (256-byte aligned total)
     assert moeq.moeq_packed_bytes(moeq.Q2_K, 1, 256) == 2816
     assert moeq.moeq_packed_bytes(moeq.Q2_K, 1536, 4096) == 1536 * 16 * 84
+    # Q3_K planes 64 + 32 + 16 + 2 B per super-block, Q5_K 128 + 32 + 16, each 256-byte aligned
+    assert moeq.moeq_packed_bytes(moeq.Q3_K, 512, 2048) == 4096 * (64 + 32 + 16 + 2)
+    assert moeq.moeq_packed_bytes(moeq.Q5_K, 512, 2048) == 4096 * (128 + 32 + 16)
+    assert moeq.moeq_packed_bytes(moeq.Q3_K, 1, 256) == 4 * 256
     assert moeq.moeq_packed_bytes(9, 1, 256) == 0
     assert moeq.moeq_packed_bytes(moeq.Q4_K, 1, 100) == 0
     assert moeq.moeq_route_workspace(1, 2048, 256, 8, 0) > 0

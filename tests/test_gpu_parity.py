@@ -169,14 +169,16 @@ def _extreme_blocks(fmt, rows, cols, rng):
     # first row: all quant bits set (max codes) to probe int32 ranges
     bb = syn.BLOCK_BYTES[fmt]
     r0 = W[0].reshape(-1, bb)
-    keep = {1: 16, 3: 20, 2: 18, 4: 2}[fmt]
+    keep = {1: 16, 3: 20, 2: 18, 4: 2, 5: 2, 6: 16}[fmt]
     r0[:, keep:] = 0xFF
     if fmt == 2:
         r0[:, 2:18] = 0x80      # Q6_K scales -128
+    if fmt == 5 and rows > 1:   # Q3_K second row: every scale -32, every code 0 (q - 4 = -4)
+        W[1].reshape(-1, bb)[:, 2:] = 0
     return W
 
 
-@pytest.mark.parametrize("fmt", [moeq.Q4_K, moeq.Q6_K, moeq.Q2_K, moeq.Q8_0])
+@pytest.mark.parametrize("fmt", [moeq.Q4_K, moeq.Q6_K, moeq.Q2_K, moeq.Q8_0, moeq.Q3_K, moeq.Q5_K])
 @pytest.mark.parametrize("rows,cols", [(37, 768), (5, 2304), (64, 4096)])
 def test_subdots_bit_exact(fmt, rows, cols):
     say("subdots", fmt, rows, cols)
@@ -201,8 +203,9 @@ def _q8k_bsums(xq, cols):
 
 def oracle_sb_sums(fmt, W, rows, cols, xq):
     """The super-block integer parts from the oracle's exact sub-block dots and
-    its decoded scales: (S1, S2, 0 ...) for the K-quants (Q6_K: S2 = sum_j sc_j
-    bsum_j), the eight 32-block sums for Q8_0; int64 [n, rows, cols/256, 8]."""
+    its decoded scales: (S1, S2, 0 ...) for the K-quants (Q6_K, Q3_K: S2 =
+    sum_j sc_j bsum_j), the eight 32-block sums for Q8_0; int64 [n, rows,
+    cols/256, 8]."""
     n, nsb = xq.shape[0], cols // 256
     sd = oracle.subdots(fmt, W, rows, cols, xq).astype(np.int64)
     out = np.zeros((n, rows, nsb, 8), np.int64)
@@ -216,12 +219,12 @@ def oracle_sb_sums(fmt, W, rows, cols, xq):
     if nsub == 8:                                       # 32-element sub-blocks: two 16-sums each
         bs = bs.reshape(n, nsb, 8, 2).sum(-1)
     out[..., 0] = (sd * sc[None].astype(np.int64)).sum(-1)
-    mul = sc if fmt == syn.Q6_K else m
+    mul = sc if fmt in (syn.Q6_K, syn.Q3_K) else m
     out[..., 1] = (mul[None].astype(np.int64) * bs[:, None]).sum(-1)
     return out
 
 
-@pytest.mark.parametrize("fmt", [moeq.Q4_K, moeq.Q6_K, moeq.Q2_K, moeq.Q8_0])
+@pytest.mark.parametrize("fmt", [moeq.Q4_K, moeq.Q6_K, moeq.Q2_K, moeq.Q8_0, moeq.Q3_K, moeq.Q5_K])
 @pytest.mark.parametrize("rows,cols,n_x", [(256, 256, 1), (512, 2304, 37), (256, 4096, 70)])
 def test_mfma_integer_parts_bit_exact(fmt, rows, cols, n_x):
     """The MFMA tiles' exact integer parts (S1, S2 per super-block, or the
@@ -732,7 +735,8 @@ def _custom_cfg(**kw):
                                      "t1_softmax_all", "t1_sigmoid_e600", "ragged_tiles_q4k",
                                      "ragged_tiles_q2k_q6k_shared_q80", "ragged_tiles_q8_q4",
                                      "many_tiles_spanning_lanes", "thin_hf_q80_q4k", "t1_36_blocks_q2k",
-                                     "t1_42_blocks_shared_q6k"])
+                                     "t1_42_blocks_shared_q6k", "q3k_q5k_mix", "t1_q5k_q3k_shared",
+                                     "ragged_tiles_q5k_q3k", "thin_hf_q5k", "t1_full_q3k_q5k"])
 def test_edge_layers(variant, fused, path):
     say("edge", variant, fused, path)
     kw = {}
@@ -787,6 +791,24 @@ def test_edge_layers(variant, fused, path):
         # token on the general down kernel and the separate combine
         kw = dict(T=1, E=16, k=6, F=1536, H=768, fmt_down=syn.Q6_K, shared=True, F_shared=1536,
                   sh_fmt_gate=syn.Q4_K, sh_fmt_up=syn.Q4_K, sh_fmt_down=syn.Q6_K)
+    elif variant == "q3k_q5k_mix":
+        kw = dict(fmt_gate=syn.Q3_K, fmt_up=syn.Q3_K, fmt_down=syn.Q5_K, H=768, F=1536, T=5, E=9, k=3,
+                  shared=True, F_shared=256, sh_fmt_gate=syn.Q5_K, sh_fmt_up=syn.Q5_K, sh_fmt_down=syn.Q3_K)
+    elif variant == "t1_q5k_q3k_shared":
+        kw = dict(T=1, E=12, k=4, fmt_gate=syn.Q5_K, fmt_up=syn.Q5_K, fmt_down=syn.Q3_K, shared=True,
+                  F_shared=512, sh_fmt_gate=syn.Q3_K, sh_fmt_up=syn.Q3_K, sh_fmt_down=syn.Q5_K)
+    elif variant == "ragged_tiles_q5k_q3k":
+        # about 47 tokens per expert: 32-row tiles, the second ragged
+        kw = dict(T=70, E=3, k=2, F=512, H=768, fmt_gate=syn.Q5_K, fmt_up=syn.Q5_K, fmt_down=syn.Q3_K,
+                  shared=True, F_shared=256, sh_fmt_gate=syn.Q3_K, sh_fmt_up=syn.Q3_K, sh_fmt_down=syn.Q5_K)
+    elif variant == "thin_hf_q5k":
+        # a small union of 8-row tiles on the fp32-h kernels, all Q5_K
+        kw = dict(T=6, E=8, k=2, F=512, H=512, fmt_gate=syn.Q5_K, fmt_up=syn.Q5_K, fmt_down=syn.Q5_K,
+                  shared=True, F_shared=256, sh_fmt_gate=syn.Q5_K, sh_fmt_up=syn.Q5_K, sh_fmt_down=syn.Q5_K)
+    elif variant == "t1_full_q3k_q5k":
+        # the decode layer's shape (hidden 2048, 256 experts, top-8, shared) in Q3_K / Q5_K
+        kw = dict(T=1, H=2048, E=256, k=8, F=512, fmt_gate=syn.Q3_K, fmt_up=syn.Q3_K, fmt_down=syn.Q5_K,
+                  shared=True, F_shared=512, sh_fmt_gate=syn.Q5_K, sh_fmt_up=syn.Q5_K, sh_fmt_down=syn.Q3_K)
     cfg = _custom_cfg(**kw)
     layer = syn.gen_layer(cfg)
     if variant == "t1_ties":
