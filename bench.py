@@ -193,7 +193,10 @@ class LayerCycle:
         # RMS-norm gains of the stack's layers (around one)
         self.norm_w = [torch.from_numpy((1.0 + 0.1 * rng.standard_normal(cfg.H)).astype(np.float32)).to(device)
                        for _ in range(L)]
-        self.route_out = moeq.RouteOut(T, cfg.E, cfg.k, device)
+        # no logits output: the hot path needs ids, weights and lists only (from
+        # 257 tokens the router then runs its approximate contraction with
+        # exact rescoring)
+        self.route_out = moeq.RouteOut(T, cfg.E, cfg.k, device, with_logits=False)
         self.y = torch.empty((T, cfg.H), dtype=torch.float32, device=device)
         self.rdesc = moeq.RouteDesc(T, cfg.H, cfg.E, cfg.k, cfg.gating, 1.0)
         self.ws = torch.empty(moeq.moeq_moe_layer_workspace(self.rdesc, self.layers[0]["desc"]), dtype=torch.uint8,

@@ -156,6 +156,15 @@ size_t moeq_route_workspace(const moeq_route_desc* d);
  *            the router launch also quantises x exactly as moeq_quantize_q8K
  * T == 0 writes offsets = 0 and active[0] = 0.  ws: moeq_route_workspace bytes,
  * 256-byte aligned.
+ * Without a logits output (logits NULL), more than 256 tokens, H % 256 == 0,
+ * E <= 1024 and top-k gating (softmax or sigmoid over the k selected), the
+ * logits run as an approximate bf16 contraction whose error is bounded per
+ * logit, and only the experts that can still be among the k get exact fp64
+ * logits, from which the selection and the gate weights are made.  The pages
+ * run one router per chunk-layer (Pulsar README, DeepSeek-V4-Flash
+ * paragraph) and give no precision for it; this library keeps the selection
+ * that of fp64 logits either way, so the outputs are the same as with a
+ * logits output.
  */
 int moeq_route(const moeq_route_desc* d, const float* x, const float* w_router, const float* bias,
                double* logits, int32_t* topk_ids, float* topk_w, int32_t* expert_offsets,

@@ -159,7 +159,7 @@ int moeq_quantize_q8K(const float* x, int64_t rows, int64_t cols, void* out, voi
 
 size_t moeq_route_workspace(const moeq_route_desc* d) {
   if (!d || d->T < 0 || d->E < 1) return 0;
-  return route_ws_bytes(d->T, d->E);
+  return route_ws_bytes(d->T, d->E, d->H);
 }
 
 int moeq_route(const moeq_route_desc* d, const float* x, const float* w_router, const float* bias,
@@ -177,7 +177,7 @@ int moeq_route(const moeq_route_desc* d, const float* x, const float* w_router, 
     if (logits && !aligned(logits, 8)) return MOEQ_E_INVALID;
     if (x_q8K && (d->H % 256 || !aligned(x_q8K, 4))) return MOEQ_E_INVALID;
     if (!ws || !aligned(ws, 256)) return MOEQ_E_INVALID;
-    if (ws_bytes < route_ws_bytes(d->T, d->E)) return MOEQ_E_WORKSPACE;
+    if (ws_bytes < route_ws_bytes(d->T, d->E, d->H)) return MOEQ_E_WORKSPACE;
   }
   return hip_status(launch_route(d->T, d->H, d->E, d->k, d->gating, d->scale, x, w_router, bias, logits,
                                  topk_ids, topk_w, expert_offsets, pairs, active, x_q8K, ws,
@@ -476,7 +476,7 @@ LayerLayout layer_layout(const moeq_route_desc* r, const moeq_ffn_desc* f) {
   LayerLayout L{};
   size_t o = 0;
   L.off_ffn = o;   o += align256(ffn_layout(f).total);
-  L.off_route = o; o += align256(route_ws_bytes(r->T, r->E));
+  L.off_route = o; o += align256(route_ws_bytes(r->T, r->E, r->H));
   L.off_xq = o;    o += align256((size_t)r->T * (r->H / 256) * kQ8KBytes);
   L.total = o;
   return L;

@@ -143,7 +143,7 @@ int launch_mfma_ints(int fmt, const void* W, int64_t N, int64_t K, const void* x
                      hipStream_t s);
 int launch_subdots(int fmt, const void* w, int64_t rows, int64_t cols, const void* xq, int64_t n_x,
                    int32_t* out, hipStream_t s);
-size_t route_ws_bytes(int64_t T, int64_t E);
+size_t route_ws_bytes(int64_t T, int64_t E, int64_t H);
 int launch_logits(int64_t T, int64_t H, int64_t E, const float* x, const float* W, const float* bias,
                   double* logits, void* xq, hipStream_t s);
 // One token: RMS pre-norm fused into the router logits and q8_K (H <= kNorm1MaxH).

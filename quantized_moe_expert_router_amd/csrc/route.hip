@@ -258,6 +258,312 @@ __global__ __launch_bounds__(256) void k_logits_mfma(const float* __restrict__ x
     }
 }
 
+// ------------------------------------------------------------------
+// Many tokens without a logits output: an approximate contraction on bf16
+// matrix cores, then exact fp64 logits of the few experts that can still be
+// among the k (the router logits in fp32 with fp64 rescoring near the k-th:
+// the selection and the gate weights come from exact fp64 logits, so ids and
+// weights are those of the fp64 router).
+//
+// Operands: every fp32 value v is split as hi = bf16(v), lo = bf16(v - hi)
+// (round to nearest even; v - hi is exact), and the contraction sums
+// hi*hi + hi*lo + lo*hi with exact bf16 products into fp32, moved into an fp64
+// sum every kSegK elements of K.  Error of one logit (first order, u = 2^-24):
+//   split:        |v - hi - lo| <= 2^-18 |v|, |lo| <= 2^-9 |v| (1 + 2^-8), so
+//                 the dropped terms are below 3.1 * 2^-18 * sum |x_i w_i|
+//   accumulation: 3 * kSegK products per segment summed in fp32 (any order):
+//                 below 3.1 * kSegK * u * sum |x_i w_i|
+//   the fp32 result: u |sum|; the fp64 segment sums: negligible
+// and sum |x_i w_i| <= ||x|| ||w_e|| (Cauchy-Schwarz).  The bound is doubled
+// (kRouteGamma below) and also covers a rounding of the matrix unit's sums
+// toward zero.
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr int kSegK = 256;                       // fp32 accumulation segment of K
+constexpr double kRouteGamma = 2.0 * (3.1 * 3.814697265625e-06 + 3.1 * kSegK * 5.9604644775390625e-08 +
+                                      2.0 * 5.9604644775390625e-08);
+constexpr int kGt = 128, kGe = 128, kGk = 32, kGpad = 40;   // tile rows, K chunk, LDS row (bf16)
+constexpr int kRescoreMaxE = 1024;   // experts of the rescoring selection (16 logits per lane)
+constexpr int kRescoreMaxB = 8;      // 256-blocks of a token row held in registers (H <= 2048)
+
+__device__ __forceinline__ uint32_t bf16_bits_rne(float v) {
+  const uint32_t u = __float_as_uint(v);
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
+
+// Split of four values into hi / lo bf16 pairs, packed two per word.
+__device__ __forceinline__ void split4(float4 v, uint2& hi, uint2& lo) {
+  const float f[4] = {v.x, v.y, v.z, v.w};
+  uint32_t h[4], l[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    h[i] = bf16_bits_rne(f[i]);
+    l[i] = bf16_bits_rne(f[i] - bf16_bits_to_f32(h[i]));
+  }
+  hi = make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
+  lo = make_uint2(l[0] | (l[1] << 16), l[2] | (l[3] << 16));
+}
+
+// One pass over the rows of x ([T, H]) and of the router weights ([E, H]),
+// one wave per row: the bf16 hi / lo planes of every row, the fp64 Euclidean
+// norm of every row, and (x rows) q8_K of the row.
+__global__ __launch_bounds__(256) void k_router_split(const float* __restrict__ x, int64_t T,
+                                                      const float* __restrict__ W, int64_t E, int64_t H,
+                                                      uint16_t* __restrict__ xhl, uint16_t* __restrict__ whl,
+                                                      double* __restrict__ nx, double* __restrict__ nw,
+                                                      uint8_t* __restrict__ xq) {
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= T + E) return;
+  const bool isx = row < T;
+  const int64_t r = isx ? row : row - T;
+  const float* src = (isx ? x : W) + r * H;
+  uint16_t* hi = (isx ? xhl : whl) + r * H;
+  uint16_t* lo = hi + (isx ? T : E) * H;
+  const int lane = lane_id();
+  double ss = 0.0;
+  for (int64_t b = 0; b < H / 256; ++b) {
+    const int64_t i = b * 256 + 4 * lane;
+    const float4 v = gld_f4(src + i);
+    ss = fma((double)v.x, (double)v.x, ss);
+    ss = fma((double)v.y, (double)v.y, ss);
+    ss = fma((double)v.z, (double)v.z, ss);
+    ss = fma((double)v.w, (double)v.w, ss);
+    uint2 h, l;
+    split4(v, h, l);
+    *reinterpret_cast<uint2*>(hi + i) = h;
+    *reinterpret_cast<uint2*>(lo + i) = l;
+    if (isx && xq != nullptr) quantize_block_vals(v, xq + (r * (H / 256) + b) * kQ8KBytes);
+  }
+  ss = wave_sum(ss);
+  if (lane == 0) (isx ? nx : nw)[r] = sqrt(ss);
+}
+
+// Approximate logits[t, e] = sum_i x[t, i] W[e, i] (no bias) in fp32, from the
+// bf16 planes: v_mfma_f32_32x32x16_bf16 on 128-token x 128-expert workgroup
+// tiles, 8 waves of 32 tokens x 64 experts, K staged through two LDS stages 32
+// at a time.  Operand lanes: A lane l = x[m = l % 32][k = 8 (l / 32) .. +7],
+// B lane l = W[n = l % 32][same k]; result lane l, value r =
+// logit[8 (r / 4) + 4 (l / 32) + r % 4][l % 32].
+__global__ __launch_bounds__(512) void k_logits_bf16x3(const uint16_t* __restrict__ xhl,
+                                                       const uint16_t* __restrict__ whl, int64_t T, int64_t H,
+                                                       int64_t E, float* __restrict__ approx) {
+  __shared__ __align__(16) uint16_t As[2][2][kGt][kGpad];   // [stage][hi, lo][token][k]
+  __shared__ __align__(16) uint16_t Bs[2][2][kGe][kGpad];   // [stage][hi, lo][expert][k]
+  const int tid = threadIdx.x, wave = tid >> 6, lane = lane_id();
+  const int64_t t0 = (int64_t)blockIdx.x * kGt, e0 = (int64_t)blockIdx.y * kGe;
+  const int wt = (wave & 3) * 32, we = (wave >> 2) * 64;
+  // staging: 2 planes x 128 rows x 4 pieces of 8 bf16, for A and for B: two
+  // 16-byte pieces of each per thread
+  uint4 av[2], bv[2];
+  auto fetch = [&](int64_t k0) __attribute__((always_inline)) {
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int idx = tid + 512 * q, pl = idx >> 9, row = (idx >> 2) & 127, c = idx & 3;
+      const int64_t tr = t0 + row, er = e0 + row;
+      const uint4 z = make_uint4(0u, 0u, 0u, 0u);
+      av[q] = tr < T ? gld_u4(xhl + (pl * T + tr) * H + k0 + 8 * c) : z;
+      bv[q] = er < E ? gld_u4(whl + (pl * E + er) * H + k0 + 8 * c) : z;
+    }
+  };
+  f32x16 acc[2];
+  double sum[2][16];
+#pragma unroll
+  for (int n = 0; n < 2; ++n) {
+    acc[n] = (f32x16){0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int r = 0; r < 16; ++r) sum[n][r] = 0.0;
+  }
+  fetch(0);
+  int buf = 0;
+  for (int64_t k0 = 0; k0 < H; k0 += kGk, buf ^= 1) {
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int idx = tid + 512 * q, pl = idx >> 9, row = (idx >> 2) & 127, c = idx & 3;
+      *reinterpret_cast<uint4*>(&As[buf][pl][row][8 * c]) = av[q];
+      *reinterpret_cast<uint4*>(&Bs[buf][pl][row][8 * c]) = bv[q];
+    }
+    __syncthreads();
+    if (k0 + kGk < H) fetch(k0 + kGk);
+#pragma unroll
+    for (int ks = 0; ks < kGk / 16; ++ks) {
+      const int kk = 16 * ks + 8 * (lane >> 5);
+      const bf16x8 ah = *reinterpret_cast<const bf16x8*>(&As[buf][0][wt + (lane & 31)][kk]);
+      const bf16x8 al = *reinterpret_cast<const bf16x8*>(&As[buf][1][wt + (lane & 31)][kk]);
+#pragma unroll
+      for (int n = 0; n < 2; ++n) {
+        const bf16x8 bh = *reinterpret_cast<const bf16x8*>(&Bs[buf][0][we + 32 * n + (lane & 31)][kk]);
+        const bf16x8 bl = *reinterpret_cast<const bf16x8*>(&Bs[buf][1][we + 32 * n + (lane & 31)][kk]);
+        acc[n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, bh, acc[n], 0, 0, 0);
+        acc[n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, bl, acc[n], 0, 0, 0);
+        acc[n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, bh, acc[n], 0, 0, 0);
+      }
+    }
+    if ((k0 + kGk) % kSegK == 0 || k0 + kGk >= H) {      // end of a segment: into the fp64 sums
+#pragma unroll
+      for (int n = 0; n < 2; ++n)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          sum[n][r] += (double)acc[n][r];
+          acc[n][r] = 0.f;
+        }
+    }
+  }
+#pragma unroll
+  for (int n = 0; n < 2; ++n) {
+    const int64_t e = e0 + we + 32 * n + (lane & 31);
+    if (e >= E) continue;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int64_t t = t0 + wt + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+      if (t < T) approx[t * E + e] = (float)sum[n][r];
+    }
+  }
+}
+
+// Per token (one wave): from the approximate logits a_e (+ bias, in fp64) and
+// the bound eps_e = gamma ||x_t|| ||W_e|| (|exact - a_e| <= eps_e), the lower
+// bound L = the k-th largest of a_e - eps_e; every expert of the top k has
+// exact logit >= exact k-th >= L, so it is among the candidates a_e + eps_e
+// >= L (an expert tied with the k-th too).  The candidates' logits are then
+// computed exactly (fp64, + bias), the others set to -inf, and the register
+// top-k and gating run on them: the same ids and weights as from all exact
+// logits.  A non-finite bound makes every expert a candidate.
+template <int NPER>
+__global__ __launch_bounds__(256) void k_topk_rescore(const float* __restrict__ approx, const double* __restrict__ nx,
+                                                      const double* __restrict__ nw, const float* __restrict__ x,
+                                                      const float* __restrict__ W, const float* __restrict__ bias,
+                                                      int64_t T, int64_t E, int64_t H, int k, int gating,
+                                                      float scale, int32_t* __restrict__ ids,
+                                                      float* __restrict__ wout) {
+  const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  const int lane = lane_id();
+  const double xn = nx[t];
+  double a[NPER], eps[NPER];
+  int vi[NPER];
+#pragma unroll
+  for (int i = 0; i < NPER; ++i) {
+    const int64_t e = lane + (int64_t)kWave * i;
+    const int64_t ec = e < E ? e : E - 1;
+    const double av = (double)approx[t * E + ec] + (bias ? (double)bias[ec] : 0.0);
+    const double ev = kRouteGamma * xn * nw[ec] + 1e-300;
+    a[i] = e < E ? av : -INFINITY;
+    eps[i] = e < E ? ev : 0.0;
+    vi[i] = e < E ? (int)e : INT_MAX;
+  }
+  // L: k rounds of a wave arg-max over each lane's sorted lower bounds
+  double lb[NPER];
+  int li[NPER];
+#pragma unroll
+  for (int i = 0; i < NPER; ++i) { lb[i] = a[i] - eps[i]; li[i] = vi[i]; }
+#pragma unroll
+  for (int p = 0; p < NPER; ++p)
+#pragma unroll
+    for (int q = NPER - 1; q > p; --q) {
+      double hv = lb[q - 1];
+      int hi = li[q - 1];
+      better(hv, hi, lb[q], li[q]);
+      const bool sw = hi != li[q - 1];
+      const double lv = sw ? lb[q - 1] : lb[q];
+      const int lj = sw ? li[q - 1] : li[q];
+      lb[q - 1] = hv; li[q - 1] = hi; lb[q] = lv; li[q] = lj;
+    }
+  int head = 0;
+  double L = -INFINITY;
+  for (int s = 0; s < k; ++s) {
+    double best = lb[0];
+    int bi = li[0];
+#pragma unroll
+    for (int j = 1; j < NPER; ++j) {
+      best = head == j ? lb[j] : best;
+      bi = head == j ? li[j] : bi;
+    }
+    best = head < NPER ? best : -INFINITY;
+    bi = head < NPER ? bi : INT_MAX;
+    const int mine = bi;
+    wave_argmax(best, bi);
+    head += (mine == bi) ? 1 : 0;
+    L = best;
+  }
+  const bool all = !(L > -INFINITY) || !(xn < INFINITY);   // a non-finite bound: every expert
+  // the candidate list, in (i, lane) order: lane l's element i sits at
+  // position base_i + (candidates of set i below lane l)
+  // per wave: E fp64 exact logits, then E int32 candidate ids (dynamic LDS)
+  extern __shared__ __align__(8) uint8_t rlds[];
+  double* exw = reinterpret_cast<double*>(rlds) + (threadIdx.x >> 6) * E;
+  int* clw = reinterpret_cast<int*>(rlds + 4 * E * sizeof(double)) + (threadIdx.x >> 6) * E;
+  int pos[NPER];
+  bool cand[NPER];
+  int n = 0;
+#pragma unroll
+  for (int i = 0; i < NPER; ++i) {
+    const int64_t e = lane + (int64_t)kWave * i;
+    cand[i] = e < E && (all || !(a[i] + eps[i] < L));
+    const uint64_t m = __ballot(cand[i]);
+    pos[i] = n + __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+    if (cand[i]) clw[pos[i]] = (int)e;
+    n += __popcll(m);
+  }
+  __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): the list is in LDS before any lane reads it
+  __builtin_amdgcn_wave_barrier();
+  // the token's row in registers (H / 256 float4 per lane; a unit past the row
+  // reloads unit 0 and is left out of the sums)
+  const int nb = (int)(H / 256);
+  const float* xr = x + t * H;
+  float4 xv[kRescoreMaxB];
+#pragma unroll
+  for (int b = 0; b < kRescoreMaxB; ++b) xv[b] = gld_f4(xr + (b < nb ? b : 0) * 256 + 4 * lane);
+  // exact logits, two candidates at a time (all weight loads of both issued
+  // before the first FMA)
+  for (int c = 0; c < n; c += 2) {
+    const int e0 = clw[c], e1 = clw[c + 1 < n ? c + 1 : c];
+    const float* w0 = W + (int64_t)e0 * H;
+    const float* w1 = W + (int64_t)e1 * H;
+    float4 u0[kRescoreMaxB], u1[kRescoreMaxB];
+#pragma unroll
+    for (int b = 0; b < kRescoreMaxB; ++b) {
+      const int bb = b < nb ? b : 0;
+      u0[b] = gld_f4(w0 + bb * 256 + 4 * lane);
+      u1[b] = gld_f4(w1 + bb * 256 + 4 * lane);
+    }
+    double s0 = 0.0, s1 = 0.0;
+#pragma unroll
+    for (int b = 0; b < kRescoreMaxB; ++b) {
+      double d0 = fma((double)u0[b].x, (double)xv[b].x, s0);
+      d0 = fma((double)u0[b].y, (double)xv[b].y, d0);
+      d0 = fma((double)u0[b].z, (double)xv[b].z, d0);
+      d0 = fma((double)u0[b].w, (double)xv[b].w, d0);
+      double d1 = fma((double)u1[b].x, (double)xv[b].x, s1);
+      d1 = fma((double)u1[b].y, (double)xv[b].y, d1);
+      d1 = fma((double)u1[b].z, (double)xv[b].z, d1);
+      d1 = fma((double)u1[b].w, (double)xv[b].w, d1);
+      s0 = b < nb ? d0 : s0;
+      s1 = b < nb ? d1 : s1;
+    }
+    s0 = wave_sum(s0);
+    s1 = wave_sum(s1);
+    if (lane == 0) {
+      exw[c] = s0 + (bias ? (double)bias[e0] : 0.0);
+      if (c + 1 < n) exw[c + 1] = s1 + (bias ? (double)bias[e1] : 0.0);
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(0xc07f);
+  __builtin_amdgcn_wave_barrier();
+  double v[NPER];
+#pragma unroll
+  for (int i = 0; i < NPER; ++i) v[i] = cand[i] ? exw[pos[i]] : -INFINITY;
+  int my_i;
+  float my_w;
+  topk_wave_vals<NPER>(v, vi, E, k, gating, scale, my_i, my_w);
+  if (lane < k) {
+    gst_i32(ids + t * k + lane, my_i);
+    gst_f32(wout + t * k + lane, my_w);
+  }
+}
+
 template <int NPER>
 __device__ __forceinline__ void topk_row_wave(const double* __restrict__ row, int64_t E, int k, int gating, float scale,
                               int32_t* __restrict__ ids_out, float* __restrict__ w_out, int32_t* ids_lds) {
@@ -560,10 +866,45 @@ int launch_logits_norm1(int64_t H, int64_t E, const float* x, const float* g, do
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
-size_t route_ws_bytes(int64_t T, int64_t E) {
-  size_t b = align256((size_t)T * E * sizeof(double));
-  if (T > kSmallT) b += align256((size_t)((T + kChunkT - 1) / kChunkT) * E * sizeof(int32_t));
-  return b;
+// Route workspace: the logits (fp64 [T, E]; the fast path keeps its fp32
+// approximations there), the chunk histograms (more than kSmallT tokens), and
+// for the fast path the bf16 hi / lo planes of x and W and their row norms.
+struct RouteLayout {
+  size_t off_hist, off_xhl, off_whl, off_nx, off_nw, total;
+};
+// (up to 1024 experts: 16 logits per lane in registers; the token row in
+// registers: H <= 2048)
+bool fast_route_ok(int64_t T, int64_t E, int64_t H) {
+  return T > kSmallT && H % 256 == 0 && H <= 256 * kRescoreMaxB && E <= kRescoreMaxE;
+}
+RouteLayout route_layout(int64_t T, int64_t E, int64_t H) {
+  RouteLayout L{};
+  size_t o = align256((size_t)T * E * sizeof(double));
+  L.off_hist = o;
+  if (T > kSmallT) o += align256((size_t)((T + kChunkT - 1) / kChunkT) * E * sizeof(int32_t));
+  if (fast_route_ok(T, E, H)) {
+    L.off_xhl = o; o += align256((size_t)2 * T * H * sizeof(uint16_t));
+    L.off_whl = o; o += align256((size_t)2 * E * H * sizeof(uint16_t));
+    L.off_nx = o;  o += align256((size_t)T * sizeof(double));
+    L.off_nw = o;  o += align256((size_t)E * sizeof(double));
+  }
+  L.total = o;
+  return L;
+}
+
+size_t route_ws_bytes(int64_t T, int64_t E, int64_t H) { return route_layout(T, E, H).total; }
+
+// The token x expert lists of more than kSmallT tokens from their ids: chunk
+// histograms, one scan (offsets, union, MFMA tile lists), the scatter.
+int lists_many(int64_t T, int k, int64_t E, const int32_t* ids, int32_t* offsets, int32_t* pairs, int32_t* active,
+               uint8_t* hist_ws, hipStream_t s, const MfmaPlan& pl) {
+  const int64_t nch = (T + kChunkT - 1) / kChunkT;
+  int32_t* hist = reinterpret_cast<int32_t*>(hist_ws);
+  hipLaunchKernelGGL(k_hist, dim3((unsigned)nch), dim3(256), (size_t)E * sizeof(int), s, ids, T, k, E, hist);
+  hipLaunchKernelGGL(k_scan, dim3(1), dim3(1024), (size_t)(3 * E + 66) * sizeof(int), s, hist, nch, E, offsets,
+                     active, pl);
+  hipLaunchKernelGGL(k_scatter, dim3((unsigned)nch), dim3(64), (size_t)E * sizeof(int), s, ids, T, k, E, hist, pairs);
+  return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
 int launch_route(int64_t T, int64_t H, int64_t E, int k, int gating, float scale, const float* x,
@@ -576,6 +917,28 @@ int launch_route(int64_t T, int64_t H, int64_t E, int k, int gating, float scale
     return hipGetLastError() == hipSuccess ? 0 : -1;
   }
   uint8_t* wsb = (uint8_t*)ws;
+  const RouteLayout RL = route_layout(T, E, H);
+  if (logits == nullptr && gating != 1 && fast_route_ok(T, E, H)) {
+    // fast path: bf16 planes, norms and q8_K(x) in one pass; the approximate
+    // contraction; selection with exact rescoring; then the lists as below
+    uint16_t* xhl = reinterpret_cast<uint16_t*>(wsb + RL.off_xhl);
+    uint16_t* whl = reinterpret_cast<uint16_t*>(wsb + RL.off_whl);
+    double* nx = reinterpret_cast<double*>(wsb + RL.off_nx);
+    double* nw = reinterpret_cast<double*>(wsb + RL.off_nw);
+    float* approx = reinterpret_cast<float*>(wsb);
+    hipLaunchKernelGGL(k_router_split, dim3((unsigned)((T + E + 3) / 4)), dim3(256), 0, s, x, T, W, E, H, xhl, whl,
+                       nx, nw, (uint8_t*)xq);
+    hipLaunchKernelGGL(k_logits_bf16x3, dim3((unsigned)((T + kGt - 1) / kGt), (unsigned)((E + kGe - 1) / kGe)),
+                       dim3(512), 0, s, xhl, whl, T, H, E, approx);
+    const size_t lds = (size_t)4 * E * (sizeof(double) + sizeof(int));
+#define MOEQ_RESCORE(N) hipLaunchKernelGGL(k_topk_rescore<N>, dim3((unsigned)((T + 3) / 4)), dim3(256), lds, s, \
+                                            approx, nx, nw, x, W, bias, T, E, H, k, gating, scale, ids, w)
+    if (E <= 256) MOEQ_RESCORE(4);
+    else if (E <= 512) MOEQ_RESCORE(8);
+    else MOEQ_RESCORE(16);
+#undef MOEQ_RESCORE
+    return lists_many(T, k, E, ids, offsets, pairs, active, wsb + RL.off_hist, s, pl);
+  }
   double* lg = logits ? logits : reinterpret_cast<double*>(wsb);
   if (int rc = launch_logits(T, H, E, x, W, bias, lg, xq, s)) return rc;
   if (T <= kSmallT) {
@@ -591,8 +954,6 @@ int launch_route(int64_t T, int64_t H, int64_t E, int k, int gating, float scale
     else MOEQ_SEL(64);
 #undef MOEQ_SEL
   } else {
-    const int64_t nch = (T + kChunkT - 1) / kChunkT;
-    int32_t* hist = reinterpret_cast<int32_t*>(wsb + align256((size_t)T * E * sizeof(double)));
 #define MOEQ_TOPK(N) hipLaunchKernelGGL(k_topk<N>, dim3((unsigned)((T + 3) / 4)), dim3(256), 0, s, lg, T, E, k, \
                                          gating, scale, ids, w)
     if (E <= 256) MOEQ_TOPK(4);
@@ -600,11 +961,7 @@ int launch_route(int64_t T, int64_t H, int64_t E, int k, int gating, float scale
     else if (E <= 1024) MOEQ_TOPK(16);
     else MOEQ_TOPK(64);
 #undef MOEQ_TOPK
-    hipLaunchKernelGGL(k_hist, dim3((unsigned)nch), dim3(256), (size_t)E * sizeof(int), s, ids, T, k, E, hist);
-    hipLaunchKernelGGL(k_scan, dim3(1), dim3(1024), (size_t)(3 * E + 66) * sizeof(int), s, hist, nch, E, offsets,
-                       active, pl);
-    hipLaunchKernelGGL(k_scatter, dim3((unsigned)nch), dim3(64), (size_t)E * sizeof(int), s, ids, T, k, E,
-                       hist, pairs);
+    return lists_many(T, k, E, ids, offsets, pairs, active, wsb + RL.off_hist, s, pl);
   }
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }

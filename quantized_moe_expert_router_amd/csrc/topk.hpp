@@ -93,26 +93,14 @@ __device__ __forceinline__ bool topk_fast(const double* v, const int* vi, int k,
 // Lane s < k ends holding the s-th winner (id) and its gate weight: computed
 // in fp64 in parallel over the k lanes and normalised by a fixed-order wave
 // sum.
+// The same on logits already in registers: v[i], vi[i] = logit and index of
+// element lane + 64*i (-inf and INT_MAX past E).  Elements known not to be
+// among the winners may hold -inf with their index (softmax over all E then
+// needs every logit).
 template <int NPER>
-__device__ __forceinline__ void topk_wave_regs(const double* __restrict__ row, int64_t E, int k, int gating, float scale,
-                               int& my_i, float& my_w) {
+__device__ __forceinline__ void topk_wave_vals(const double* v, const int* vi, int64_t E, int k, int gating,
+                                               float scale, int& my_i, float& my_w) {
   const int lane = lane_id();
-  double v[NPER];
-  int vi[NPER];
-  // every load is issued (an element past E reloads element E - 1) before
-  // the first wait; then the elements past E become -inf
-#pragma unroll
-  for (int i = 0; i < NPER; ++i) {
-    const int64_t e = lane + (int64_t)kWave * i;
-    v[i] = gld_f64(row + (e < E ? e : E - 1));
-  }
-  __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-  for (int i = 0; i < NPER; ++i) {
-    const int64_t e = lane + (int64_t)kWave * i;
-    v[i] = e < E ? v[i] : -INFINITY;
-    vi[i] = e < E ? (int)e : INT_MAX;
-  }
   double my_v = 0.0;
   my_i = 0;
   if constexpr (NPER <= 8) {
@@ -185,6 +173,29 @@ __device__ __forceinline__ void topk_wave_regs(const double* __restrict__ row, i
     z = wave_sum(num);
   }
   my_w = (float)(num / z * (double)scale);
+}
+
+template <int NPER>
+__device__ __forceinline__ void topk_wave_regs(const double* __restrict__ row, int64_t E, int k, int gating, float scale,
+                               int& my_i, float& my_w) {
+  const int lane = lane_id();
+  double v[NPER];
+  int vi[NPER];
+  // every load is issued (an element past E reloads element E - 1) before
+  // the first wait; then the elements past E become -inf
+#pragma unroll
+  for (int i = 0; i < NPER; ++i) {
+    const int64_t e = lane + (int64_t)kWave * i;
+    v[i] = gld_f64(row + (e < E ? e : E - 1));
+  }
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int i = 0; i < NPER; ++i) {
+    const int64_t e = lane + (int64_t)kWave * i;
+    v[i] = e < E ? v[i] : -INFINITY;
+    vi[i] = e < E ? (int)e : INT_MAX;
+  }
+  topk_wave_vals<NPER>(v, vi, E, k, gating, scale, my_i, my_w);
 }
 
 }  // namespace moeq

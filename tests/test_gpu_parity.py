@@ -51,9 +51,12 @@ class GpuRun:
     single whole-layer call.  Every output and workspace the library sees is
     a view inside a guarded allocation; the guards are checked after the call.
     aux: give the FFN an auxiliary stream for a shared expert that runs apart
-    from the routed launches (else everything runs on one stream)."""
+    from the routed launches (else everything runs on one stream).
+    logits=False: no logits output (from 257 tokens the router then takes the
+    approximate contraction with exact rescoring)."""
 
-    def __init__(self, layer, path=moeq.PATH_AUTO, present=None, shared_scale=None, x=None, fused=False, aux=True):
+    def __init__(self, layer, path=moeq.PATH_AUTO, present=None, shared_scale=None, x=None, fused=False, aux=True,
+                 logits=True):
         cfg = layer.cfg
         self.dl = moeq.DeviceLayer(layer, present=present)
         xs = layer.x if x is None else x
@@ -63,7 +66,7 @@ class GpuRun:
         rn = moeq.LayerRunner(self.dl, T, path=path, shared_scale=ss, aux=moeq.AuxStream() if aux else None)
         ga = GuardedAlloc()
         r = rn.route_out
-        r.logits = ga.empty((T, cfg.E), torch.float64, "logits")
+        r.logits = ga.empty((T, cfg.E), torch.float64, "logits") if logits else None
         r.ids = ga.empty((T, cfg.k), torch.int32, "topk_ids")
         r.w = ga.empty((T, cfg.k), torch.float32, "topk_w")
         r.offsets = ga.empty(cfg.E + 1, torch.int32, "offsets")
@@ -81,7 +84,7 @@ class GpuRun:
         ga.check("layer" if fused else "calls")
         self.ids = r.ids.cpu().numpy()
         self.w = r.w.cpu().numpy()
-        self.logits = r.logits.cpu().numpy()
+        self.logits = r.logits.cpu().numpy() if logits else None
         self.offsets = r.offsets.cpu().numpy()
         self.pairs = r.pairs.cpu().numpy()[:T * cfg.k]
         act = r.active.cpu().numpy()
@@ -324,6 +327,97 @@ def test_route_many_tokens_ragged(T, E, H, with_bias):
     act = out.active.cpu().numpy()
     assert np.array_equal(act[:1 + act[0]], active)
     assert np.array_equal(xq.cpu().numpy(), oracle.quantize_q8K(x))
+
+
+def _fast_route_case(variant):
+    """Inputs for the router without a logits output (bf16 contraction plus
+    exact rescoring): (x, W, b, k, gating)."""
+    rng = np.random.default_rng(sum(map(ord, variant)))
+    T, E, H, k, gating, with_bias = {
+        "t257_e64": (257, 64, 256, 6, syn.SOFTMAX_TOPK, False),
+        "t1000_e513_bias": (1000, 513, 2048, 10, syn.SOFTMAX_TOPK, True),
+        "t700_e256_sigmoid": (700, 256, 1024, 6, syn.SIGMOID_TOPK, True),
+        "near_ties": (600, 96, 512, 8, syn.SOFTMAX_TOPK, True),
+        "scales_and_zero_rows": (400, 128, 768, 4, syn.SOFTMAX_TOPK, True),
+        "k_equals_E": (300, 8, 256, 8, syn.SIGMOID_TOPK, False),
+        "all_tied": (300, 40, 256, 5, syn.SOFTMAX_TOPK, False),
+    }[variant]
+    x = rng.standard_normal((T, H)).astype(np.float32)
+    W = (rng.standard_normal((E, H)) * 0.02).astype(np.float32)
+    b = (rng.standard_normal(E) * 0.1).astype(np.float32) if with_bias else None
+    if variant == "near_ties":
+        W[5] = W[3]                                            # exact ties
+        W[7] = W[2] * np.float32(1 + 2 ** -20)                 # far inside the error bound
+        W[9] = W[1]
+        W[9, ::7] += np.float32(1e-6)
+        b[5], b[9] = b[3], b[1]
+    if variant == "scales_and_zero_rows":
+        x[::5] *= np.float32(1e3)
+        x[1::5] *= np.float32(1e-3)
+        x[2::7] = 0.0                                          # logits = bias: ties broken by index
+        b[10:20] = b[10]
+    if variant == "all_tied":
+        W[:] = W[0]                                            # every expert ties: every one a candidate
+    return x, W, b, k, gating
+
+
+@pytest.mark.parametrize("variant", ["t257_e64", "t1000_e513_bias", "t700_e256_sigmoid", "near_ties",
+                                     "scales_and_zero_rows", "k_equals_E", "all_tied"])
+def test_route_without_logits_output(variant):
+    """Many tokens with no logits output: the approximate bf16 contraction
+    selects candidates with a proven error bound and rescoring in fp64 decides,
+    so ids, gate weights, lists and q8_K(x) equal the oracle's, with exact and
+    near ties, rows of very different scale, zero rows and all experts tied."""
+    x, W, b, k, gating = _fast_route_case(variant)
+    T, H = x.shape
+    E = W.shape[0]
+    say("route without logits", variant, T, E, H)
+    ga = GuardedAlloc()
+    out = moeq.RouteOut(T, E, k, "cuda", with_logits=False)
+    out.ids = ga.empty((T, k), torch.int32, "ids")
+    out.w = ga.empty((T, k), torch.float32, "w")
+    out.offsets = ga.empty(E + 1, torch.int32, "offsets")
+    out.pairs = ga.empty(max(1, T * k), torch.int32, "pairs")
+    out.active = ga.empty(1 + min(E, T * k), torch.int32, "active")
+    ws = ga.empty(max(256, moeq.moeq_route_workspace(T, H, E, k, gating)), torch.uint8, "ws")
+    xq = ga.empty((T, H // 256 * moeq.Q8K_BYTES), torch.uint8, "xq")
+    moeq.moeq_route(dev(x), dev(W), None if b is None else dev(b), k, gating, out=out, ws=ws, x_q8K=xq)
+    torch.cuda.synchronize()
+    ga.check("route without logits")
+    _, ids, w = oracle.route(x, W, b, k, gating)
+    got = out.ids.cpu().numpy()
+    if not np.array_equal(got, ids):
+        bad = np.nonzero((got != ids).any(axis=1))[0]
+        raise AssertionError((variant, "ids differ for %d tokens, first %s" % (len(bad), bad[:8].tolist())))
+    check_w(out.w.cpu().numpy(), w)
+    off, pairs, active = oracle.lists(ids, E)
+    assert np.array_equal(out.offsets.cpu().numpy(), off)
+    assert np.array_equal(out.pairs.cpu().numpy()[:T * k], pairs)
+    act = out.active.cpu().numpy()
+    assert np.array_equal(act[:1 + act[0]], active)
+    assert np.array_equal(xq.cpu().numpy(), oracle.quantize_q8K(x))
+
+
+@pytest.mark.parametrize("fused", [False, True], ids=["calls", "layer"])
+def test_prefill_layer_without_logits_output(fused):
+    """The 8192-token prefill layer with no logits output (the router's
+    approximate contraction and exact rescoring) against the oracle: ids, gate
+    weights, lists, q8_K(x), every pair's q8_K(h) and y."""
+    name = "prefill"
+    layer = layer_of(name)
+    cfg = layer.cfg
+    o = oracle_of(name)
+    say("prefill layer without logits", "fused" if fused else "calls")
+    run = GpuRun(layer, fused=fused, logits=False)
+    assert np.array_equal(run.ids, o["ids"]), name
+    check_w(run.w, o["w"])
+    assert np.array_equal(run.offsets, o["offsets"])
+    assert np.array_equal(run.pairs, o["pairs"])
+    assert np.array_equal(run.active, o["active"])
+    if run.xq is not None:
+        assert np.array_equal(run.xq, o["xq"])
+    check_hq(run, o["hq"], cfg, name)
+    check_y(run.yv, o["y"], name)
 
 
 @pytest.mark.parametrize("path", ["gemv", "mfma", "auto"])
