@@ -41,8 +41,8 @@
  *   - Inputs must be finite.
  *
  * Block formats.  The pages name the formats (Pulsar README, 'Get a model':
- * the routed-expert formats it reads, q2_K, q3_K, q4_K, q5_K and q6_K among
- * them, dense tensors requantised to q8_0; 'Fidelity notes': activations
+ * the routed-expert formats it reads, q2_K, q3_K, q4_0, q4_K, q5_K, q5_1 and
+ * q6_K among them, dense tensors requantised to q8_0; 'Fidelity notes': activations
  * quantised to q8_K with integer dots) but print no byte layout, so the
  * exchange layout is this library's own (little-endian):
  *   q8_K  292 B / 256 : f32 d | i8 q[256] | i16 bsums[16]          x ~ d*q
@@ -66,6 +66,10 @@
  *   Q5_K  176 B / 256 : Q4_K's 144 bytes (the low nibbles as its quants) | 32 B
  *                       high bits (byte i bit b = element 32b+i); q = low +
  *                       16*high, sub-blocks of 32      w = d*sc_j*q - dmin*m_j
+ *   Q4_0   18 B /  32 : f16 d | 16 B (byte i = element i low nibble, element
+ *                       16+i high nibble)              w = d*(q-8)
+ *   Q5_1   24 B /  32 : f16 d | f16 m | 4 B (bit i = bit 4 of element i) |
+ *                       16 B nibbles as Q4_0           w = d*q + m
  * A matrix [rows, cols] is rows of blocks back to back.  Kernels read a
  * repacked ("packed") form made once by moeq_pack_experts.
  */
@@ -90,7 +94,8 @@ typedef enum {
 } moeq_status;
 
 typedef enum {
-    MOEQ_Q4_K = 1, MOEQ_Q6_K = 2, MOEQ_Q2_K = 3, MOEQ_Q8_0 = 4, MOEQ_Q3_K = 5, MOEQ_Q5_K = 6
+    MOEQ_Q4_K = 1, MOEQ_Q6_K = 2, MOEQ_Q2_K = 3, MOEQ_Q8_0 = 4, MOEQ_Q3_K = 5, MOEQ_Q5_K = 6,
+    MOEQ_Q4_0 = 7, MOEQ_Q5_1 = 8
 } moeq_wfmt;
 
 typedef enum {
@@ -363,8 +368,9 @@ int moeq_ffn_h_view(const moeq_ffn_desc* d, void* ws, size_t ws_bytes, void** hq
  * dot-product (GEMV) kernels use.  Enqueued on `stream`; n_x == 0 is a no-op.
  *   packed_w [rows, cols] packed fmt; x_q8K [n_x, cols/256 blocks]
  *   out int32 [n_x, rows, cols/sub]: sum over sub-block j of code * q_x, where
- *   sub = 32 (Q4_K, Q5_K, Q8_0) or 16 (Q2_K, Q3_K, Q6_K) and code = q (Q4_K,
- *   Q5_K, Q2_K), q-32 (Q6_K), q-4 (Q3_K), signed q (Q8_0).
+ *   sub = 32 (Q4_K, Q5_K, Q8_0, Q4_0, Q5_1) or 16 (Q2_K, Q3_K, Q6_K) and
+ *   code = q (Q4_K, Q5_K, Q2_K, Q5_1), q-32 (Q6_K), q-4 (Q3_K), q-8 (Q4_0),
+ *   signed q (Q8_0).
  */
 int moeq_debug_subdots(int32_t fmt, const void* packed_w, int64_t rows, int64_t cols,
                        const void* x_q8K, int64_t n_x, int32_t* out, void* stream);
@@ -382,7 +388,9 @@ int moeq_debug_subdots(int32_t fmt, const void* packed_w, int64_t rows, int64_t 
  *                 activations)
  *     Q6_K, Q3_K: (S1, S2, 0...) with S1 = sum_j sc_j isum_j over the codes
  *                 q - 32 (Q6_K) or q - 4 (Q3_K) and S2 = sum_j sc_j bsum_j
- *     Q8_0:       isum_b of the eight 32-blocks of the super-block
+ *     Q8_0, Q4_0, Q5_1: isum_b of the eight 32-blocks of the super-block
+ *                 (over q - 8 for Q4_0, over q for Q5_1, whose min term
+ *                 m_b bsum_b is not part of it)
  * Enqueued on `stream`; n_x == 0 is a no-op.  Errors: MOEQ_E_UNSUPPORTED for
  * an unknown format, MOEQ_E_INVALID for bad sizes, NULLs or misalignment.
  */

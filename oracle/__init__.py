@@ -75,9 +75,9 @@ def _c(a, dtype):
     return np.ascontiguousarray(a, dtype=dtype)
 
 
-SUBBLOCK = {1: 32, 2: 16, 3: 16, 4: 32, 5: 16, 6: 32}
-BLOCK_W = {1: 256, 2: 256, 3: 256, 4: 32, 5: 256, 6: 256}
-BLOCK_B = {1: 144, 2: 210, 3: 84, 4: 34, 5: 110, 6: 176}
+SUBBLOCK = {1: 32, 2: 16, 3: 16, 4: 32, 5: 16, 6: 32, 7: 32, 8: 32}
+BLOCK_W = {1: 256, 2: 256, 3: 256, 4: 32, 5: 256, 6: 256, 7: 32, 8: 32}
+BLOCK_B = {1: 144, 2: 210, 3: 84, 4: 34, 5: 110, 6: 176, 7: 18, 8: 24}
 
 
 def half_to_double(h: int) -> float:

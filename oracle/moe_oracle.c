@@ -54,13 +54,17 @@
  *   Q5_K  176 B : the 144 bytes of Q4_K (its quants are the low nibbles) |
  *                 u8 qh[32] (byte i bit b: bit 4 of element 32b+i); sub-blocks
  *                 of 32; w = d*sc_j*q - dmin*m_j
+ *   Q4_0   18 B : f16 d | u8 qs[16] (byte i: element i low nibble, element
+ *                 16+i high nibble);  w = d*(q-8)
+ *   Q5_1   24 B : f16 d | f16 m | u8 qh[4] (bit i of the little-endian word:
+ *                 bit 4 of element i) | u8 qs[16] as Q4_0;  w = d*q + m
  */
 #include <math.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
 
-enum { F_Q4_K = 1, F_Q6_K = 2, F_Q2_K = 3, F_Q8_0 = 4, F_Q3_K = 5, F_Q5_K = 6 };
+enum { F_Q4_K = 1, F_Q6_K = 2, F_Q2_K = 3, F_Q8_0 = 4, F_Q3_K = 5, F_Q5_K = 6, F_Q4_0 = 7, F_Q5_1 = 8 };
 enum { G_SOFTMAX_TOPK = 0, G_SOFTMAX_ALL = 1, G_SIGMOID_TOPK = 2 };
 
 /* ------------------------------------------------------------------ fp16 */
@@ -94,11 +98,13 @@ int orc_block_bytes(int fmt)
     case F_Q8_0: return 34;
     case F_Q3_K: return 110;
     case F_Q5_K: return 176;
+    case F_Q4_0: return 18;
+    case F_Q5_1: return 24;
     }
     return 0;
 }
 
-int orc_block_weights(int fmt) { return fmt == F_Q8_0 ? 32 : 256; }
+int orc_block_weights(int fmt) { return (fmt == F_Q8_0 || fmt == F_Q4_0 || fmt == F_Q5_1) ? 32 : 256; }
 
 /* Elements per sub-block: the unit that carries one scale (and min). */
 int orc_subblock(int fmt)
@@ -110,12 +116,14 @@ int orc_subblock(int fmt)
     case F_Q8_0: return 32;
     case F_Q3_K: return 16;
     case F_Q5_K: return 32;
+    case F_Q4_0: return 32;
+    case F_Q5_1: return 32;
     }
     return 0;
 }
 
-/* The offset subtracted from the stored code: w = d*sc*(q - offset) (Q6_K, Q3_K). */
-static int code_offset(int fmt) { return fmt == F_Q6_K ? 32 : fmt == F_Q3_K ? 4 : 0; }
+/* The offset subtracted from the stored code: w = d*sc*(q - offset) (Q6_K, Q3_K, Q4_0). */
+static int code_offset(int fmt) { return fmt == F_Q6_K ? 32 : fmt == F_Q3_K ? 4 : fmt == F_Q4_0 ? 8 : 0; }
 
 /* Bits [pos, pos + n) of a little-endian byte stream. */
 static int stream_bits(const uint8_t* p, int pos, int n)
@@ -129,7 +137,7 @@ static int stream_bits(const uint8_t* p, int pos, int n)
 /*
  * Decode one block into integer codes.  q[] gets the quant code of every
  * element (Q6_K: 0..63 before the -32 offset; Q3_K: 0..7 before the -4
- * offset; Q8_0: signed), sc[]/m[] the
+ * offset; Q4_0: 0..15 before the -8 offset; Q8_0: signed), sc[]/m[] the
  * per-sub-block scale and min codes (m = 0 where the format has none),
  * d/dmin the fp16 super-scales as doubles.
  */
@@ -222,6 +230,22 @@ int orc_block_codes(int fmt, const uint8_t* b, double* d, double* dmin, int* sc,
                 q[32 * s + i] += 16 * ((qh[i] >> s) & 1);
         return 0;
     }
+    case F_Q4_0:
+    case F_Q5_1: {
+        const uint8_t* qs = b + (fmt == F_Q4_0 ? 2 : 8);
+        *d = orc_half_to_double(rd16(b));
+        *dmin = fmt == F_Q5_1 ? orc_half_to_double(rd16(b + 2)) : 0.0;   /* Q5_1: the min m */
+        sc[0] = 1;
+        m[0] = 0;
+        for (i = 0; i < 16; i++) {
+            q[i] = qs[i] & 15;
+            q[16 + i] = qs[i] >> 4;
+        }
+        if (fmt == F_Q5_1)
+            for (i = 0; i < 32; i++)
+                q[i] += 16 * ((b[4 + i / 8] >> (i % 8)) & 1);
+        return 0;
+    }
     case F_Q8_0: {
         *d = orc_half_to_double(rd16(b));
         *dmin = 0.0;
@@ -250,7 +274,9 @@ static int dequant_block(int fmt, const uint8_t* b, double* out)
         case F_Q5_K:
         case F_Q2_K: out[i] = d * (double)sc[j] * (double)q[i] - dmin * (double)m[j]; break;
         case F_Q6_K:
-        case F_Q3_K: out[i] = d * (double)sc[j] * (double)(q[i] - code_offset(fmt)); break;
+        case F_Q3_K:
+        case F_Q4_0: out[i] = d * (double)sc[j] * (double)(q[i] - code_offset(fmt)); break;
+        case F_Q5_1: out[i] = d * (double)q[i] + dmin; break;
         case F_Q8_0: out[i] = d * (double)q[i]; break;
         }
     }
@@ -479,7 +505,8 @@ void orc_lists(int64_t T, int k, int64_t E, const int32_t* ids,
 /*
  * Exact int32 dot of each sub-block of each weight row with each q8_K row:
  * out[n][r][j] = sum over sub-block j of (weight code) * q_x, where the weight
- * code is q (Q4_K, Q5_K, Q2_K), q-32 (Q6_K), q-4 (Q3_K) or the signed q (Q8_0).
+ * code is q (Q4_K, Q5_K, Q2_K, Q5_1), q-32 (Q6_K), q-4 (Q3_K), q-8 (Q4_0) or
+ * the signed q (Q8_0).
  */
 int orc_subdots(int fmt, const uint8_t* w, int64_t rows, int64_t cols,
                 const uint8_t* xq, int64_t n_x, int32_t* out)
@@ -542,7 +569,8 @@ int orc_scales_matrix(int fmt, const uint8_t* w, int64_t rows, int64_t cols, int
  * The integer formulation of one row dot, summed per 256 super-block in fp64:
  *   Q4_K/Q5_K/Q2_K: d_x * (d * sum_j sc_j isum_j - dmin * sum_j m_j bsum_j)
  *   Q6_K/Q3_K:      d_x * d * sum_j sc_j isum_j (isum over the codes q - offset)
- *   Q8_0:      d_x * sum_b d_b isum_b
+ *   Q8_0/Q4_0/Q5_1: d_x * sum_b (d_b isum_b + m_b bsum_b), isum over q - offset,
+ *                   m_b the Q5_1 min (0 otherwise)
  * Used only to check that it equals the fp64 dequantised dot.
  */
 double orc_dot_intform(int fmt, const uint8_t* wrow, int64_t cols, const uint8_t* xq)
@@ -558,17 +586,17 @@ double orc_dot_intform(int fmt, const uint8_t* wrow, int64_t cols, const uint8_t
         memcpy(&dxf, xb, 4);
         memcpy(bsums, xb + 260, 32);
         dx = (double)dxf;
-        if (fmt == F_Q8_0) {
+        if (orc_block_weights(fmt) == 32) {
             double acc = 0.0;
             int b;
             for (b = 0; b < 8; b++) {
                 double d, dmin;
                 int sc[1], m[1], q[32], e;
-                int32_t is = 0;
-                orc_block_codes(fmt, wrow + (sb * 8 + b) * 34, &d, &dmin, sc, m, q);
+                int32_t is = 0, bs = bsums[2 * b] + bsums[2 * b + 1];
+                orc_block_codes(fmt, wrow + (sb * 8 + b) * orc_block_bytes(fmt), &d, &dmin, sc, m, q);
                 for (e = 0; e < 32; e++)
-                    is += q[e] * qx[b * 32 + e];
-                acc += d * (double)is;
+                    is += (q[e] - code_offset(fmt)) * qx[b * 32 + e];
+                acc += d * (double)is + dmin * (double)bs;   /* dmin: Q5_1's min, else 0 */
             }
             total += dx * acc;
         } else {

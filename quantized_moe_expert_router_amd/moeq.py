@@ -19,11 +19,11 @@ LIB_PATH = os.path.join(_HERE, "libmoeq.so")
 MOEQ_OK, MOEQ_E_INVALID, MOEQ_E_UNSUPPORTED, MOEQ_E_WORKSPACE, MOEQ_E_HIP = 0, -1, -2, -3, -4
 MOEQ_E_STATIC_LIMIT = -5
 NOALLOC_MAX_BYTES = 32 << 20
-Q4_K, Q6_K, Q2_K, Q8_0, Q3_K, Q5_K = 1, 2, 3, 4, 5, 6
+Q4_K, Q6_K, Q2_K, Q8_0, Q3_K, Q5_K, Q4_0, Q5_1 = 1, 2, 3, 4, 5, 6, 7, 8
 SOFTMAX_TOPK, SOFTMAX_ALL, SIGMOID_TOPK = 0, 1, 2
 PATH_AUTO, PATH_GEMV, PATH_MFMA = 0, 1, 2
 Q8K_BYTES = 292
-SUBBLOCK = {Q4_K: 32, Q6_K: 16, Q2_K: 16, Q8_0: 32, Q3_K: 16, Q5_K: 32}
+SUBBLOCK = {Q4_K: 32, Q6_K: 16, Q2_K: 16, Q8_0: 32, Q3_K: 16, Q5_K: 32, Q4_0: 32, Q5_1: 32}
 
 SYMBOLS = ["moeq_status_string", "moeq_quantize_q8K", "moeq_route_workspace", "moeq_route",
            "moeq_packed_bytes", "moeq_pack_experts", "moeq_expert_ffn_workspace", "moeq_expert_ffn",

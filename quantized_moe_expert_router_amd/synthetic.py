@@ -26,15 +26,16 @@ from typing import Dict, List, Optional
 import numpy as np
 
 # Format ids (same values as the C header's moeq_wfmt).
-Q4_K, Q6_K, Q2_K, Q8_0, Q3_K, Q5_K = 1, 2, 3, 4, 5, 6
-FMT_NAMES = {Q4_K: "Q4_K", Q6_K: "Q6_K", Q2_K: "Q2_K", Q8_0: "Q8_0", Q3_K: "Q3_K", Q5_K: "Q5_K"}
+Q4_K, Q6_K, Q2_K, Q8_0, Q3_K, Q5_K, Q4_0, Q5_1 = 1, 2, 3, 4, 5, 6, 7, 8
+FMT_NAMES = {Q4_K: "Q4_K", Q6_K: "Q6_K", Q2_K: "Q2_K", Q8_0: "Q8_0", Q3_K: "Q3_K", Q5_K: "Q5_K", Q4_0: "Q4_0",
+             Q5_1: "Q5_1"}
 
 # Gating ids (same values as moeq_gating).
 SOFTMAX_TOPK, SOFTMAX_ALL, SIGMOID_TOPK = 0, 1, 2
 
 # Bytes per block and weights per block of each exchange format.
-BLOCK_BYTES = {Q4_K: 144, Q6_K: 210, Q2_K: 84, Q8_0: 34, Q3_K: 110, Q5_K: 176}
-BLOCK_WEIGHTS = {Q4_K: 256, Q6_K: 256, Q2_K: 256, Q8_0: 32, Q3_K: 256, Q5_K: 256}
+BLOCK_BYTES = {Q4_K: 144, Q6_K: 210, Q2_K: 84, Q8_0: 34, Q3_K: 110, Q5_K: 176, Q4_0: 18, Q5_1: 24}
+BLOCK_WEIGHTS = {Q4_K: 256, Q6_K: 256, Q2_K: 256, Q8_0: 32, Q3_K: 256, Q5_K: 256, Q4_0: 32, Q5_1: 32}
 Q8K_BLOCK_BYTES = 292
 
 # Byte offsets of fp16 scale fields inside a block, with the draw range of each:
@@ -46,6 +47,8 @@ _FP16_FIELDS = {
     Q8_0: [(0, 1.0, 1e-4)],                    # d
     Q3_K: [(0, 1.0, 3e-4)],                    # d
     Q5_K: [(0, 1.0, 5e-5), (2, 7.5, 5e-5)],    # d, dmin
+    Q4_0: [(0, 1.0, 5e-3)],                    # d
+    Q5_1: [(0, 1.0, 2e-3), (2, -16.0, 2e-3)],  # d, m (negative: the block's values centre on zero)
 }
 
 # Stream roles, mixed into the seed so every tensor has an independent stream.

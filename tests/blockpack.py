@@ -17,10 +17,13 @@ Layouts (little-endian):
               bits (byte i bit b = bit 2 of element 32b+i); w = d*sc*(q-4)
   Q5_K 176 B: the Q4_K bytes of the low nibbles, then 32 B high bits (byte i
               bit b = bit 4 of element 32b+i)
+  Q4_0  18 B: f16 d, 16 B (byte i = element i | element 16+i << 4); w = d*(q-8)
+  Q5_1  24 B: f16 d, f16 m, 4 B (bit i = bit 4 of element i), 16 B as Q4_0;
+              w = d*q + m
 """
 import numpy as np
 
-Q4_K, Q6_K, Q2_K, Q8_0, Q3_K, Q5_K = 1, 2, 3, 4, 5, 6
+Q4_K, Q6_K, Q2_K, Q8_0, Q3_K, Q5_K, Q4_0, Q5_1 = 1, 2, 3, 4, 5, 6, 7, 8
 
 
 def f16_bytes(v: float) -> bytes:
@@ -99,7 +102,25 @@ def pack_q5k(d, dmin, sc, m, q) -> bytes:
     return pack_q4k(d, dmin, sc, m, [int(v) & 15 for v in q]) + _high_bits(q, 4)
 
 
+def _nibbles32(q) -> bytes:
+    return bytes((int(q[i]) & 15) | ((int(q[16 + i]) & 15) << 4) for i in range(16))
+
+
+def pack_q40(d, q) -> bytes:
+    """q: 32 codes in [0, 15]."""
+    assert len(q) == 32 and all(0 <= int(v) < 16 for v in q)
+    return f16_bytes(d) + _nibbles32(q)
+
+
+def pack_q51(d, m, q) -> bytes:
+    """q: 32 codes in [0, 31]; m: the block's min (added)."""
+    assert len(q) == 32 and all(0 <= int(v) < 32 for v in q)
+    qh = sum(((int(q[i]) >> 4) & 1) << i for i in range(32)).to_bytes(4, "little")
+    return f16_bytes(d) + f16_bytes(m) + qh + _nibbles32(q)
+
+
 def pack_row(fmt, blocks) -> np.ndarray:
     """blocks: list of per-block argument tuples for the format's packer."""
-    fn = {Q4_K: pack_q4k, Q2_K: pack_q2k, Q6_K: pack_q6k, Q8_0: pack_q80, Q3_K: pack_q3k, Q5_K: pack_q5k}[fmt]
+    fn = {Q4_K: pack_q4k, Q2_K: pack_q2k, Q6_K: pack_q6k, Q8_0: pack_q80, Q3_K: pack_q3k, Q5_K: pack_q5k,
+          Q4_0: pack_q40, Q5_1: pack_q51}[fmt]
     return np.frombuffer(b"".join(fn(*b) for b in blocks), dtype=np.uint8).copy()

@@ -43,7 +43,7 @@ def test_packed_bytes_and_workspace_queries():
     assert moeq.moeq_packed_bytes(moeq.Q3_K, 512, 2048) == 4096 * (64 + 32 + 16 + 2)
     assert moeq.moeq_packed_bytes(moeq.Q5_K, 512, 2048) == 4096 * (128 + 32 + 16)
     assert moeq.moeq_packed_bytes(moeq.Q3_K, 1, 256) == 4 * 256
-    assert moeq.moeq_packed_bytes(9, 1, 256) == 0
+    assert moeq.moeq_packed_bytes(99, 1, 256) == 0
     assert moeq.moeq_packed_bytes(moeq.Q4_K, 1, 100) == 0
     assert moeq.moeq_route_workspace(1, 2048, 256, 8, 0) > 0
 
@@ -65,7 +65,7 @@ def _desc(**kw):
     (dict(k=0), moeq.MOEQ_E_INVALID),
     (dict(k=33), moeq.MOEQ_E_INVALID),
     (dict(E=4097), moeq.MOEQ_E_INVALID),
-    (dict(fmt_down=7), moeq.MOEQ_E_UNSUPPORTED),
+    (dict(fmt_down=99), moeq.MOEQ_E_UNSUPPORTED),
     (dict(fmt_up=moeq.Q2_K), moeq.MOEQ_E_UNSUPPORTED),
     (dict(gate=0), moeq.MOEQ_E_INVALID),
     (dict(sh_gate=0x2000, F_shared=512, sh_fmt_gate=1, sh_fmt_up=1, sh_fmt_down=1), moeq.MOEQ_E_INVALID),
@@ -143,7 +143,7 @@ def test_route_and_quantize_validation():
     assert L.moeq_quantize_q8K(None, 2, 256, 0x2000, None) == moeq.MOEQ_E_INVALID
     assert L.moeq_quantize_q8K(0x1004, 2, 256, 0x2000, None) == moeq.MOEQ_E_INVALID   # x 16-byte aligned
     assert L.moeq_quantize_q8K(0x1000, 0, 256, 0x2000, None) == 0
-    assert L.moeq_pack_experts(9, 0x1000, 1, 1, 256, 0x2000, None) == moeq.MOEQ_E_UNSUPPORTED
+    assert L.moeq_pack_experts(99, 0x1000, 1, 1, 256, 0x2000, None) == moeq.MOEQ_E_UNSUPPORTED
     assert L.moeq_pack_experts(1, 0x1000, 1, 1, 256, 0x2010, None) == moeq.MOEQ_E_INVALID
     assert L.moeq_debug_subdots(1, 0x1000, 1, 300, 0x2000, 1, 0x3000, None) == moeq.MOEQ_E_INVALID
 

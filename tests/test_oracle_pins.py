@@ -15,7 +15,7 @@ import pytest
 from scipy import special
 
 import oracle
-from blockpack import Q2_K, Q3_K, Q4_K, Q5_K, Q6_K, Q8_0, pack_q2k, pack_q4k, pack_q6k, pack_q80, pack_row
+from blockpack import Q2_K, Q3_K, Q4_0, Q4_K, Q5_1, Q5_K, Q6_K, Q8_0, pack_q2k, pack_q4k, pack_q6k, pack_q80, pack_row
 from quantized_moe_expert_router_amd import synthetic as syn
 
 GOLDEN = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "blocks.json")))
@@ -77,6 +77,13 @@ def _all_values_blocks(fmt, rng):
             m = [(v + 3 * j + 1) % 64 for j in range(8)]
             q = [(v + i) % 32 for i in range(256)]
             out.append((float(rng.uniform(1, 2)) * 1e-3, float(rng.uniform(1, 2)) * 1e-3, sc, m, q))
+    elif fmt == Q4_0:
+        for v in range(16):
+            out.append((float(rng.uniform(1, 2)) * 1e-2, [(v + i) % 16 for i in range(32)]))
+    elif fmt == Q5_1:
+        for v in range(32):
+            out.append((float(rng.uniform(1, 2)) * 1e-2, -float(rng.uniform(1, 2)) * 1e-1,
+                        [(v + 3 * i) % 32 for i in range(32)]))
     else:
         for v in range(8):
             q = [((v * 32 + i) % 256) - 128 for i in range(32)]
@@ -84,7 +91,7 @@ def _all_values_blocks(fmt, rng):
     return out
 
 
-@pytest.mark.parametrize("fmt", [Q4_K, Q2_K, Q6_K, Q8_0, Q3_K, Q5_K])
+@pytest.mark.parametrize("fmt", [Q4_K, Q2_K, Q6_K, Q8_0, Q3_K, Q5_K, Q4_0, Q5_1])
 def test_encode_decode_roundtrip_all_codes(fmt):
     rng = np.random.default_rng(7)
     blocks = _all_values_blocks(fmt, rng)
@@ -99,6 +106,10 @@ def test_encode_decode_roundtrip_all_codes(fmt):
         elif fmt in (Q6_K, Q3_K):
             dd, esc, eq = args
             assert not m.any()
+        elif fmt == Q5_1:
+            dd, dm, eq = args
+            assert dmin == float(np.float16(dm))           # the min, added
+            esc = [1]
         else:
             dd, eq = args
             esc = [1]
@@ -107,7 +118,7 @@ def test_encode_decode_roundtrip_all_codes(fmt):
         assert list(q) == list(eq)
 
 
-@pytest.mark.parametrize("fmt", [Q4_K, Q2_K, Q6_K, Q8_0, Q3_K, Q5_K])
+@pytest.mark.parametrize("fmt", [Q4_K, Q2_K, Q6_K, Q8_0, Q3_K, Q5_K, Q4_0, Q5_1])
 def test_scales_matrix_returns_encoded_scales_and_mins(fmt):
     """Every block's decoded sub-block scales and mins, for a matrix built by
     the independent encoder from known codes."""
@@ -238,6 +249,12 @@ def _unit_blocks(fmt, rng, nblk):
             out.append((1.0, [1] * 16, rng.integers(0, 8, 256)))
         elif fmt == Q5_K:
             out.append((1.0, 0.0, [1] * 8, [0] * 8, rng.integers(0, 32, 256)))
+        elif fmt == Q4_0:
+            for _ in range(8):
+                out.append((1.0, rng.integers(0, 16, 32)))
+        elif fmt == Q5_1:
+            for _ in range(8):
+                out.append((1.0, 0.0, rng.integers(0, 32, 32)))
         else:
             for _ in range(8):
                 out.append((1.0, rng.integers(-128, 128, 32)))
@@ -251,6 +268,10 @@ def _unit_ints(fmt, blocks):
         return np.concatenate([np.asarray(b[2]) - 32 for b in blocks])
     if fmt == Q3_K:
         return np.concatenate([np.asarray(b[2]) - 4 for b in blocks])
+    if fmt == Q4_0:
+        return np.concatenate([np.asarray(b[1]) - 8 for b in blocks])
+    if fmt == Q5_1:
+        return np.concatenate([np.asarray(b[2]) for b in blocks])
     return np.concatenate([np.asarray(b[1]) for b in blocks])
 
 
@@ -261,7 +282,7 @@ def _int_grid_x(rng, n):
     return x
 
 
-@pytest.mark.parametrize("fmt", [Q4_K, Q2_K, Q6_K, Q8_0, Q3_K, Q5_K])
+@pytest.mark.parametrize("fmt", [Q4_K, Q2_K, Q6_K, Q8_0, Q3_K, Q5_K, Q4_0, Q5_1])
 def test_textbook_reduction_integer_matvec(fmt):
     """Unit scales, zero mins, d = d_x = 1: the dequantised dot is the plain integer matvec."""
     rng = np.random.default_rng(20 + fmt)
@@ -289,7 +310,7 @@ def test_textbook_reduction_integer_matvec(fmt):
     assert np.array_equal(sd, ref_sd)
 
 
-@pytest.mark.parametrize("fmt", [Q4_K, Q2_K, Q6_K, Q8_0, Q3_K, Q5_K])
+@pytest.mark.parametrize("fmt", [Q4_K, Q2_K, Q6_K, Q8_0, Q3_K, Q5_K, Q4_0, Q5_1])
 def test_integer_form_equals_fp64_dequant_dot(fmt):
     rng = np.random.default_rng(30 + fmt)
     rows, cols = 16, 1024
@@ -306,7 +327,7 @@ def test_integer_form_equals_fp64_dequant_dot(fmt):
 
 
 def test_cross_format_identity():
-    """Weights representable in Q4_K, Q2_K, Q3_K, Q5_K and Q8_0 give bit-identical fp64 dots."""
+    """Weights representable in every format give bit-identical fp64 dots."""
     rng = np.random.default_rng(40)
     cols = 512
     q2 = rng.integers(0, 4, cols)
@@ -320,15 +341,19 @@ def test_cross_format_identity():
     b3 = [(0.25, [1] * 16, q2[i * 256:(i + 1) * 256] + 3) for i in range(2)]
     # Q5_K: as Q4_K, the high bit never set
     b5 = [(0.25, 0.25, [1] * 8, [1] * 8, q2[i * 256:(i + 1) * 256]) for i in range(2)]
+    # Q4_0: d = 1/4, q = q2 + 7  ->  (q2 + 7 - 8) / 4;  Q5_1: d = 1/4, m = -1/4, q = q2
+    b40 = [(0.25, q2[i * 32:(i + 1) * 32] + 7) for i in range(cols // 32)]
+    b51 = [(0.25, -0.25, q2[i * 32:(i + 1) * 32]) for i in range(cols // 32)]
     r2, r4, r8 = pack_row(Q2_K, b2), pack_row(Q4_K, b4), pack_row(Q8_0, b8)
-    r3, r5 = pack_row(Q3_K, b3), pack_row(Q5_K, b5)
+    r3, r5, r40, r51 = pack_row(Q3_K, b3), pack_row(Q5_K, b5), pack_row(Q4_0, b40), pack_row(Q5_1, b51)
+    others = ((Q4_K, r4), (Q8_0, r8), (Q3_K, r3), (Q5_K, r5), (Q4_0, r40), (Q5_1, r51))
     w2 = oracle.dequant_row(Q2_K, r2, cols)
     assert np.array_equal(w2, (q2 - 1) / 4.0)
-    for f, r in ((Q4_K, r4), (Q8_0, r8), (Q3_K, r3), (Q5_K, r5)):
+    for f, r in others:
         assert np.array_equal(w2, oracle.dequant_row(f, r, cols)), f
     v = oracle.dequant_q8K(oracle.quantize_q8K(rng.standard_normal(cols).astype(np.float32)), cols)[0]
     a = oracle.matvec(Q2_K, r2, 1, cols, v)
-    for f, r in ((Q4_K, r4), (Q8_0, r8), (Q3_K, r3), (Q5_K, r5)):
+    for f, r in others:
         assert np.array_equal(a, oracle.matvec(f, r, 1, cols, v)), f
 
 
@@ -461,6 +486,16 @@ def _grid_matrix(fmt, rng, rows, cols):
                 q = rng.integers(0, 32, 256)
                 bl.append((2.0 ** -6, 2.0 ** -6, [1] * 8, [16] * 8, q))
                 ints.append(q - 16)
+            elif fmt == Q4_0:     # w = 2^-6 * (q - 8)
+                for b in range(8):
+                    q = rng.integers(0, 16, 32)
+                    bl.append((2.0 ** -6, q))
+                    ints.append(q - 8)
+            elif fmt == Q5_1:     # w = 2^-6 * q - 2^-6 * 16
+                for b in range(8):
+                    q = rng.integers(0, 32, 32)
+                    bl.append((2.0 ** -6, -(2.0 ** -2), q))
+                    ints.append(q - 16)
             else:
                 for b in range(8):
                     q = rng.integers(-8, 9, 32)
@@ -471,7 +506,7 @@ def _grid_matrix(fmt, rng, rows, cols):
 
 
 @pytest.mark.parametrize("fmts", [(Q4_K, Q6_K, Q8_0), (Q2_K, Q4_K, Q2_K), (Q8_0, Q8_0, Q4_K),
-                                  (Q3_K, Q5_K, Q3_K), (Q5_K, Q3_K, Q5_K)])
+                                  (Q3_K, Q5_K, Q3_K), (Q5_K, Q3_K, Q5_K), (Q4_0, Q5_1, Q4_0), (Q5_1, Q4_0, Q5_1)])
 def test_ffn_special_case_reduces_to_numpy_and_scipy(fmts):
     """Grid weights and integer-grid x make every step checkable with numpy matmul,
     scipy's expit and a by-hand read of the q8_K(h) bytes."""
