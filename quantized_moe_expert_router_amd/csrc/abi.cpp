@@ -20,7 +20,8 @@ constexpr int64_t kMaxStack = 4096;   // layers per moeq_moe_stack call
 constexpr int kRowBlock = 64;     // rows per expert-major down work item
 
 bool fmt_ok(int f) {
-  return f == MOEQ_Q4_K || f == MOEQ_Q6_K || f == MOEQ_Q2_K || f == MOEQ_Q8_0 || f == MOEQ_Q3_K || f == MOEQ_Q5_K;
+  return f == MOEQ_Q4_K || f == MOEQ_Q6_K || f == MOEQ_Q2_K || f == MOEQ_Q8_0 || f == MOEQ_Q3_K || f == MOEQ_Q5_K ||
+         f == MOEQ_Q4_0 || f == MOEQ_Q5_1;
 }
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 int hip_status(int rc) { return rc == 0 ? MOEQ_OK : (rc == -2 ? MOEQ_E_UNSUPPORTED : MOEQ_E_HIP); }

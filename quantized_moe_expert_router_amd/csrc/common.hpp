@@ -8,7 +8,7 @@ namespace moeq {
 constexpr int kWave = 64;
 constexpr int kQ8KBytes = 292;   // f32 d | i8 q[256] | i16 bsums[16]
 
-enum FmtId : int { FQ4K = 1, FQ6K = 2, FQ2K = 3, FQ80 = 4, FQ3K = 5, FQ5K = 6 };
+enum FmtId : int { FQ4K = 1, FQ6K = 2, FQ2K = 3, FQ80 = 4, FQ3K = 5, FQ5K = 6, FQ40 = 7, FQ51 = 8 };
 
 __device__ __forceinline__ int dot4(int a, int b, int acc) {
   return __builtin_amdgcn_sdot4(a, b, acc, false);

@@ -476,6 +476,8 @@ __global__ __launch_bounds__(256) void k_down_rows1(DownArgs a) {
     case FQ80: { MOEQ_SWITCH_TT(M, FQ80) } break;             \
     case FQ3K: { MOEQ_SWITCH_TT(M, FQ3K) } break;             \
     case FQ5K: { MOEQ_SWITCH_TT(M, FQ5K) } break;             \
+    case FQ40: { MOEQ_SWITCH_TT(M, FQ40) } break;             \
+    case FQ51: { MOEQ_SWITCH_TT(M, FQ51) } break;             \
     default: return -2;                                       \
   }
 
@@ -512,6 +514,8 @@ int launch_gateup1(int fmt, int nper, int cpl, dim3 grid, const GateUpArgs& a, h
     case FQ80: { MOEQ_G1_NP(FQ80) } break;
     case FQ3K: { MOEQ_G1_NP(FQ3K) } break;
     case FQ5K: { MOEQ_G1_NP(FQ5K) } break;
+    case FQ40: { MOEQ_G1_NP(FQ40) } break;
+    case FQ51: { MOEQ_G1_NP(FQ51) } break;
     default: return -2;
   }
   return hipGetLastError() == hipSuccess ? 0 : -1;

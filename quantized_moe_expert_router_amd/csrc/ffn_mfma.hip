@@ -34,6 +34,9 @@
 //         (exact int32 dot of q with x), scaled by sc_j in int32; the -32 part
 //         is 32 * sum_j sc_j bsum_j, from the same split-sum MFMA pair.
 //   Q8_0  w = d_b*q: one MFMA per 32-block, scaled by d_b in fp64.
+//   Q4_0  w = d_b*(q-8): as Q8_0 on the bytes q - 8.
+//   Q5_1  w = d_b*q + m_b: as Q8_0 on the bytes q, plus one MFMA of the
+//         activations against ones for the block sum the min multiplies.
 //   Q3_K  w = d*sc_j*(q-4), signed six-bit sc, q < 8: as Q6_K (sc*q does not
 //         fit in int8): one 16-deep MFMA per sub-block on the codes q, scaled
 //         by sc_j in int32; the -4 part is 4 * sum_j sc_j bsum_j.
@@ -553,6 +556,90 @@ template <> struct Mf<FQ5K> {
     const Ints I = ints(w, g, qrow, abs);
     const double d = half_bits_to_float(w.h.x & 0xFFFF), dmin = half_bits_to_float(w.h.x >> 16);
     MOEQ_COMBINE(acc[r] += dx * (d * (double)I.s1[r] - dmin * (double)I.s2[r]))
+  }
+};
+
+// Q4_0 and Q5_1: every lane loads the row's eight 16-byte quant chunks (its
+// lane half takes one nibble of each) and the scales, as Q8_0.
+__device__ __forceinline__ uint32_t pick4(const uint4& v, int i) {
+  return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
+}
+
+template <> struct Mf<FQ40> {
+  static constexpr int NBSP = 0;
+  struct Wt { uint4 q[8]; uint4 d; };
+  __device__ static Wt load(const uint8_t* W, int64_t N, int64_t nbK, int64_t row, int64_t sb, int) {
+    const size_t nsb = (size_t)(N * nbK);
+    const RowSplit rs = row_split(row, nbK, sb);
+    const uint32_t lr = rs.r * (uint32_t)nbK;
+    const uint8_t* Wb = wave_uni_ptr(W);
+    Wt w;
+#pragma unroll
+    for (int b = 0; b < 8; ++b) w.q[b] = gld_u4(Wb + rs.su * 128 + (lr * 128u + 16u * (uint32_t)b));
+    w.d = gld_u4(Wb + align256(nsb * 128) + rs.su * 16 + lr * 16u);
+    return w;
+  }
+  // The exact integer sum of 32-block b over the codes q - 8: nibble g of the
+  // block's words, biased to signed bytes ((v + 0x78) ^ 0x80 = v - 8 for v < 16).
+  __device__ __forceinline__ static v16i block_ints(const Wt& w, int g, const uint8_t* qrow, int b) {
+    v4i bq;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      bq[i] = (int)((((pick4(w.q[b], i) >> (4 * g)) & 0x0F0F0F0Fu) + 0x78787878u) ^ 0x80808080u);
+    const v16i z16 = {0};
+    return mfma_k32(lds_v4(qrow + 32 * b + 16 * g), bq, z16);
+  }
+  template <int NQ>
+  __device__ static void mac(const Wt& w, int g, const uint8_t* qrow, const v4i, const double* dxs,
+                             int n, double* acc) {
+#pragma unroll
+    for (int b = 0; b < 8; ++b) {
+      const v16i P = block_ints(w, g, qrow, b);
+      const double db = half_bits_to_float(pick4(w.d, b >> 1) >> (16 * (b & 1)));
+      MOEQ_COMBINE(acc[r] += (dx * db) * (double)P[r])
+    }
+  }
+};
+
+template <> struct Mf<FQ51> {
+  static constexpr int NBSP = 0;
+  struct Wt { uint4 q[8]; uint4 xd[4]; };   // xd[k]: (bit-4 word, d | m) of blocks 2k, 2k+1
+  __device__ static Wt load(const uint8_t* W, int64_t N, int64_t nbK, int64_t row, int64_t sb, int) {
+    const size_t nsb = (size_t)(N * nbK);
+    const RowSplit rs = row_split(row, nbK, sb);
+    const uint32_t lr = rs.r * (uint32_t)nbK;
+    const uint8_t* Wb = wave_uni_ptr(W);
+    const uint8_t* pxd = Wb + align256(nsb * 128);
+    Wt w;
+#pragma unroll
+    for (int b = 0; b < 8; ++b) w.q[b] = gld_u4(Wb + rs.su * 128 + (lr * 128u + 16u * (uint32_t)b));
+#pragma unroll
+    for (int k = 0; k < 4; ++k) w.xd[k] = gld_u4(pxd + rs.su * 64 + (lr * 64u + 16u * (uint32_t)k));
+    return w;
+  }
+  // The exact integer sum of 32-block b over the codes q = nibble | bit 4.
+  __device__ __forceinline__ static v16i block_ints(const Wt& w, int g, const uint8_t* qrow, int b) {
+    const uint32_t hx = pick4(w.xd[b >> 1], 2 * (b & 1));
+    v4i bq;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      bq[i] = (int)(((pick4(w.q[b], i) >> (4 * g)) & 0x0F0F0F0Fu) | (((hx >> (4 * g + i)) & 0x01010101u) << 4));
+    const v16i z16 = {0};
+    return mfma_k32(lds_v4(qrow + 32 * b + 16 * g), bq, z16);
+  }
+  template <int NQ>
+  __device__ static void mac(const Wt& w, int g, const uint8_t* qrow, const v4i, const double* dxs,
+                             int n, double* acc) {
+    const v4i ones = {0x01010101, 0x01010101, 0x01010101, 0x01010101};
+    const v16i z16 = {0};
+#pragma unroll
+    for (int b = 0; b < 8; ++b) {
+      const v16i P = block_ints(w, g, qrow, b);
+      const v16i S = mfma_k32(lds_v4(qrow + 32 * b + 16 * g), ones, z16);   // the block's activation sums
+      const uint32_t dmw = pick4(w.xd[b >> 1], 2 * (b & 1) + 1);
+      const double db = half_bits_to_float(dmw & 0xFFFF), mb = half_bits_to_float(dmw >> 16);
+      MOEQ_COMBINE(acc[r] += dx * (db * (double)P[r] + mb * (double)S[r]))
+    }
   }
 };
 
@@ -1162,7 +1249,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_pe
 }
 // 8-row tiles with resident activations and RING weight units in flight per
 // wave (the memory-bound verify unions and small chunks).
-template <int FMT> constexpr int kRing = FMT == FQ80 ? 2 : 4;
+template <int FMT> constexpr int kRing = (FMT == FQ80 || FMT == FQ40 || FMT == FQ51) ? 2 : 4;
 template <int FMT, int MODE>
 __global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2, 8))) void k_mfma_ring(
     MfmaArgs a) {
@@ -1197,7 +1284,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_pe
 // rows, out[x][row][sb][0..7] holds (S1, S2, 0, 0, 0, 0, 0, 0) for Q4_K and
 // Q2_K (S1 = sum_j sc_j isum_j, S2 = sum_j m_j bsum_j), for Q6_K (S1 over the
 // codes q - 32, S2 = sum_j sc_j bsum_j), and the eight 32-block sums isum_b
-// for Q8_0.  Grid (ceil(n_x / 32), N / 256): 32 activation rows and 8 waves
+// for Q8_0, Q4_0 (over q - 8) and Q5_1 (over q).  Grid (ceil(n_x / 32), N / 256): 32 activation rows and 8 waves
 // of 32 weight rows per workgroup, one 256-block staged at a time.
 template <int FMT>
 __global__ __launch_bounds__(512) void k_mfma_ints(const uint8_t* __restrict__ W, int64_t N, int64_t K,
@@ -1221,7 +1308,7 @@ __global__ __launch_bounds__(512) void k_mfma_ints(const uint8_t* __restrict__ W
     const uint8_t* qrow = &S.qs[lane & 31][0];
     int32_t* o = out + (t0 * N + row) * nbK * 8 + sb * 8;
     const int64_t mstride = N * nbK * 8;
-    if constexpr (FMT == FQ80) {
+    if constexpr (FMT == FQ80 || FMT == FQ40 || FMT == FQ51) {
 #pragma unroll
       for (int b = 0; b < 8; ++b) {
         const v16i P = M::block_ints(w, g, qrow, b);
@@ -1258,6 +1345,8 @@ int launch_mfma_ints(int fmt, const void* W, int64_t N, int64_t K, const void* x
     case FQ80: hipLaunchKernelGGL(k_mfma_ints<FQ80>, grid, dim3(512), 0, s, w8, N, K, x8, n_x, out); break;
     case FQ3K: hipLaunchKernelGGL(k_mfma_ints<FQ3K>, grid, dim3(512), 0, s, w8, N, K, x8, n_x, out); break;
     case FQ5K: hipLaunchKernelGGL(k_mfma_ints<FQ5K>, grid, dim3(512), 0, s, w8, N, K, x8, n_x, out); break;
+    case FQ40: hipLaunchKernelGGL(k_mfma_ints<FQ40>, grid, dim3(512), 0, s, w8, N, K, x8, n_x, out); break;
+    case FQ51: hipLaunchKernelGGL(k_mfma_ints<FQ51>, grid, dim3(512), 0, s, w8, N, K, x8, n_x, out); break;
     default: return -2;
   }
   return hipGetLastError() == hipSuccess ? 0 : -1;
@@ -1335,6 +1424,8 @@ int launch_mfma(int fmt, int mode, bool thin, bool hf, dim3 grid, const MfmaArgs
     case FQ80: launch_fmt<FQ80>(mode, thin, hf, grid, a, nbK, s); break;
     case FQ3K: launch_fmt<FQ3K>(mode, thin, false, grid, a, nbK, s); break;
     case FQ5K: launch_fmt<FQ5K>(mode, thin, hf, grid, a, nbK, s); break;
+    case FQ40: launch_fmt<FQ40>(mode, thin, hf, grid, a, nbK, s); break;
+    case FQ51: launch_fmt<FQ51>(mode, thin, hf, grid, a, nbK, s); break;
     default: return -2;
   }
   return hipGetLastError() == hipSuccess ? 0 : -1;

@@ -43,6 +43,13 @@
 //           at once); bits 8b+i / 8b+4+i = bit 4 of chunk elements 4i+b /
 //           16+4i+b (the two nibbles of word i, byte b)
 //         plane H  16 B/sb: the exchange header as is (d, dmin, 12 B scales)
+//   Q4_0  plane Q 128 B/sb: chunk b = the 16 quant bytes of 32-block b as is
+//           (byte i = element i low nibble, element 16+i high nibble)
+//         plane D  16 B/sb: eight fp16 d
+//   Q5_1  plane Q 128 B/sb: as Q4_0
+//         plane XD 64 B/sb: two words per block: the bit-4 word (bits 8b+i /
+//           8b+4+i = bit 4 of block elements 4i+b / 16+4i+b, as a Q5_K
+//           chunk's word), then fp16 d | fp16 m << 16
 #pragma once
 #include "common.hpp"
 
@@ -69,6 +76,8 @@ __host__ __device__ inline Geo geo_of(int fmt) {
     case FQ80: return Geo{32, 2, {256, 16, 0, 0}, 1};
     case FQ3K: return Geo{32, 4, {64, 32, 16, 2}, 1};
     case FQ5K: return Geo{32, 3, {128, 32, 16, 0}, 1};
+    case FQ40: return Geo{32, 2, {128, 16, 0, 0}, 1};
+    case FQ51: return Geo{32, 2, {128, 64, 0, 0}, 1};
   }
   return Geo{0, 0, {0, 0, 0, 0}, 1};
 }
@@ -303,6 +312,68 @@ template <> struct Fmt<FQ5K> : RowMajor<32> {
     const int mn = (int)((hi >> (16 + 6 * j)) & 63);
     const double d = half_bits_to_float(w.h.x & 0xFFFF), dmin = half_bits_to_float(w.h.x >> 16);
     return dx * (d * (double)(sc * is[0]) - dmin * (double)(mn * (bs[0] + bs[1])));
+  }
+};
+
+// ---------------------------------------------------------------- Q4_0
+template <> struct Fmt<FQ40> : RowMajor<32> {
+  static constexpr int WPC = 32, CPS = 8, XDW = 8, NBS = 2, SPC = 1;
+  __device__ static constexpr int sub_of(int j, int t) { return j * SPC + t; }
+  struct W { uint4 q; uint32_t d; };
+  __device__ static W load(const uint8_t* m, int64_t rows, int64_t nb, int64_t row, int64_t sb, int b) {
+    const size_t nsb = (size_t)(rows * nb), sbi = (size_t)(row * nb + sb);
+    W w;
+    w.q = gld_u4(m + sbi * 128 + 16 * b);
+    w.d = gld_u16(m + align256(nsb * 128) + sbi * 16 + 2 * b);
+    return w;
+  }
+  // sum (q - 8) q_x = sum q q_x - 8 (the block's activation sum)
+  __device__ static void isums(const W& w, const int* xw, const int* bs, int* is) {
+    const uint32_t q[4] = {w.q.x, w.q.y, w.q.z, w.q.w};
+    int s = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      s = dot4((int)(q[i] & 0x0F0F0F0Fu), xw[i], s);
+      s = dot4((int)((q[i] >> 4) & 0x0F0F0F0Fu), xw[4 + i], s);
+    }
+    is[0] = s - 8 * (bs[0] + bs[1]);
+  }
+  __device__ static double term(const W& w, int, const int* is, const int*, double dx) {
+    return dx * (half_bits_to_float(w.d) * (double)is[0]);
+  }
+};
+
+// ---------------------------------------------------------------- Q5_1
+template <> struct Fmt<FQ51> : RowMajor<32> {
+  static constexpr int WPC = 32, CPS = 8, XDW = 8, NBS = 2, SPC = 1;
+  __device__ static constexpr int sub_of(int j, int t) { return j * SPC + t; }
+  struct W { uint4 q; uint32_t x; uint32_t dm; };
+  __device__ static W load(const uint8_t* m, int64_t rows, int64_t nb, int64_t row, int64_t sb, int b) {
+    const size_t nsb = (size_t)(rows * nb), sbi = (size_t)(row * nb + sb);
+    W w;
+    w.q = gld_u4(m + sbi * 128 + 16 * b);
+    const uint2 xd = gld_u2(m + align256(nsb * 128) + sbi * 64 + 8 * b);
+    w.x = xd.x;
+    w.dm = xd.y;
+    return w;
+  }
+  // q = nibble | bit 4 (0..31)
+  __device__ static void isums(const W& w, const int* xw, const int*, int* is) {
+    const uint32_t q[4] = {w.q.x, w.q.y, w.q.z, w.q.w};
+    int s = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t lo = (q[i] & 0x0F0F0F0Fu) | (((w.x >> i) & 0x01010101u) << 4);
+      const uint32_t hi = ((q[i] >> 4) & 0x0F0F0F0Fu) | (((w.x >> (4 + i)) & 0x01010101u) << 4);
+      s = dot4((int)lo, xw[i], s);
+      s = dot4((int)hi, xw[4 + i], s);
+    }
+    is[0] = s;
+  }
+  // d q + m summed against the block: d isum + m bsum
+  __device__ static double term(const W& w, int, const int* is, const int* bs, double dx) {
+    const double d = half_bits_to_float(w.dm & 0xFFFF), mn = half_bits_to_float(w.dm >> 16);
+    return dx * (d * (double)is[0] + mn * (double)(bs[0] + bs[1]));
   }
 };
 

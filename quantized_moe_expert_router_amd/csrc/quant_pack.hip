@@ -169,6 +169,28 @@ __global__ __launch_bounds__(256) void k_pack(const uint8_t* __restrict__ aos, i
       }
     for (int i = 0; i < 16; ++i) U[kQ2KScales + 16 * r + i] = src[4 + i];
     for (int i = 0; i < 4; ++i) U[kQ2KD + 4 * r + i] = src[i];
+  } else if (FMT == FQ40 || FMT == FQ51) {
+    // eight 18- or 24-byte blocks per super-block: the quant bytes as they are,
+    // Q5_1's bit-4 word rearranged for v_dot4, and the scales
+    const int bb = FMT == FQ40 ? 18 : 24, qo = FMT == FQ40 ? 2 : 8;
+    uint8_t* p2 = m + align256(nsb * 128);
+    for (int b = 0; b < 8; ++b) {
+      const uint8_t* blk = src + bb * b;
+      for (int i = 0; i < 16; ++i) m[sbi * 128 + 16 * b + i] = blk[qo + i];
+      if (FMT == FQ40) {
+        p2[sbi * 16 + 2 * b] = blk[0];
+        p2[sbi * 16 + 2 * b + 1] = blk[1];
+      } else {
+        const uint32_t qh = (uint32_t)blk[4] | ((uint32_t)blk[5] << 8) | ((uint32_t)blk[6] << 16) |
+                            ((uint32_t)blk[7] << 24);
+        uint32_t v = 0;
+        for (int w = 0; w < 4; ++w)
+          for (int c = 0; c < 4; ++c)
+            v |= (((qh >> (4 * w + c)) & 1u) << (8 * c + w)) | (((qh >> (16 + 4 * w + c)) & 1u) << (8 * c + 4 + w));
+        st_u32(p2 + sbi * 64 + 8 * b, v);
+        for (int i = 0; i < 4; ++i) p2[sbi * 64 + 8 * b + 4 + i] = blk[i];
+      }
+    }
   } else {  // Q8_0: eight 34-byte blocks per super-block
     uint8_t* pd = m + align256(nsb * 256);
     for (int b = 0; b < 8; ++b) {
@@ -195,6 +217,8 @@ int launch_pack(int fmt, const void* aos, int64_t n_mats, int64_t rows, int64_t 
     case FQ80: hipLaunchKernelGGL(k_pack<FQ80>, dim3(grid), dim3(256), 0, s, a, n_mats, rows, cols, p, mb, (int64_t)272); break;
     case FQ3K: hipLaunchKernelGGL(k_pack<FQ3K>, dim3(grid), dim3(256), 0, s, a, n_mats, rows, cols, p, mb, (int64_t)110); break;
     case FQ5K: hipLaunchKernelGGL(k_pack<FQ5K>, dim3(grid), dim3(256), 0, s, a, n_mats, rows, cols, p, mb, (int64_t)176); break;
+    case FQ40: hipLaunchKernelGGL(k_pack<FQ40>, dim3(grid), dim3(256), 0, s, a, n_mats, rows, cols, p, mb, (int64_t)144); break;
+    case FQ51: hipLaunchKernelGGL(k_pack<FQ51>, dim3(grid), dim3(256), 0, s, a, n_mats, rows, cols, p, mb, (int64_t)192); break;
     default: return -2;
   }
   return hipGetLastError() == hipSuccess ? 0 : -1;
@@ -236,6 +260,8 @@ int launch_subdots(int fmt, const void* w, int64_t rows, int64_t cols, const voi
     case FQ80: hipLaunchKernelGGL(k_subdots<FQ80>, dim3(grid), dim3(256), 0, s, W, rows, cols, X, n_x, out); break;
     case FQ3K: hipLaunchKernelGGL(k_subdots<FQ3K>, dim3(grid), dim3(256), 0, s, W, rows, cols, X, n_x, out); break;
     case FQ5K: hipLaunchKernelGGL(k_subdots<FQ5K>, dim3(grid), dim3(256), 0, s, W, rows, cols, X, n_x, out); break;
+    case FQ40: hipLaunchKernelGGL(k_subdots<FQ40>, dim3(grid), dim3(256), 0, s, W, rows, cols, X, n_x, out); break;
+    case FQ51: hipLaunchKernelGGL(k_subdots<FQ51>, dim3(grid), dim3(256), 0, s, W, rows, cols, X, n_x, out); break;
     default: return -2;
   }
   return hipGetLastError() == hipSuccess ? 0 : -1;

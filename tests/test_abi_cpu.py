@@ -43,6 +43,8 @@ def test_packed_bytes_and_workspace_queries():
     assert moeq.moeq_packed_bytes(moeq.Q3_K, 512, 2048) == 4096 * (64 + 32 + 16 + 2)
     assert moeq.moeq_packed_bytes(moeq.Q5_K, 512, 2048) == 4096 * (128 + 32 + 16)
     assert moeq.moeq_packed_bytes(moeq.Q3_K, 1, 256) == 4 * 256
+    assert moeq.moeq_packed_bytes(moeq.Q4_0, 512, 2048) == 4096 * (128 + 16)
+    assert moeq.moeq_packed_bytes(moeq.Q5_1, 512, 2048) == 4096 * (128 + 64)
     assert moeq.moeq_packed_bytes(99, 1, 256) == 0
     assert moeq.moeq_packed_bytes(moeq.Q4_K, 1, 100) == 0
     assert moeq.moeq_route_workspace(1, 2048, 256, 8, 0) > 0

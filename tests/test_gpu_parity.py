@@ -172,7 +172,7 @@ def _extreme_blocks(fmt, rows, cols, rng):
     # first row: all quant bits set (max codes) to probe int32 ranges
     bb = syn.BLOCK_BYTES[fmt]
     r0 = W[0].reshape(-1, bb)
-    keep = {1: 16, 3: 20, 2: 18, 4: 2, 5: 2, 6: 16}[fmt]
+    keep = {1: 16, 3: 20, 2: 18, 4: 2, 5: 2, 6: 16, 7: 2, 8: 4}[fmt]
     r0[:, keep:] = 0xFF
     if fmt == 2:
         r0[:, 2:18] = 0x80      # Q6_K scales -128
@@ -181,7 +181,8 @@ def _extreme_blocks(fmt, rows, cols, rng):
     return W
 
 
-@pytest.mark.parametrize("fmt", [moeq.Q4_K, moeq.Q6_K, moeq.Q2_K, moeq.Q8_0, moeq.Q3_K, moeq.Q5_K])
+@pytest.mark.parametrize("fmt", [moeq.Q4_K, moeq.Q6_K, moeq.Q2_K, moeq.Q8_0, moeq.Q3_K, moeq.Q5_K, moeq.Q4_0,
+                                 moeq.Q5_1])
 @pytest.mark.parametrize("rows,cols", [(37, 768), (5, 2304), (64, 4096)])
 def test_subdots_bit_exact(fmt, rows, cols):
     say("subdots", fmt, rows, cols)
@@ -212,7 +213,7 @@ def oracle_sb_sums(fmt, W, rows, cols, xq):
     n, nsb = xq.shape[0], cols // 256
     sd = oracle.subdots(fmt, W, rows, cols, xq).astype(np.int64)
     out = np.zeros((n, rows, nsb, 8), np.int64)
-    if fmt == syn.Q8_0:
+    if fmt in (syn.Q8_0, syn.Q4_0, syn.Q5_1):          # the eight 32-block sums (Q5_1: over q)
         out[:] = sd.reshape(n, rows, nsb, 8)
         return out
     sc, m = oracle.scales_matrix(fmt, W, rows, cols)
@@ -227,7 +228,8 @@ def oracle_sb_sums(fmt, W, rows, cols, xq):
     return out
 
 
-@pytest.mark.parametrize("fmt", [moeq.Q4_K, moeq.Q6_K, moeq.Q2_K, moeq.Q8_0, moeq.Q3_K, moeq.Q5_K])
+@pytest.mark.parametrize("fmt", [moeq.Q4_K, moeq.Q6_K, moeq.Q2_K, moeq.Q8_0, moeq.Q3_K, moeq.Q5_K, moeq.Q4_0,
+                                 moeq.Q5_1])
 @pytest.mark.parametrize("rows,cols,n_x", [(256, 256, 1), (512, 2304, 37), (256, 4096, 70)])
 def test_mfma_integer_parts_bit_exact(fmt, rows, cols, n_x):
     """The MFMA tiles' exact integer parts (S1, S2 per super-block, or the
@@ -830,7 +832,8 @@ def _custom_cfg(**kw):
                                      "ragged_tiles_q2k_q6k_shared_q80", "ragged_tiles_q8_q4",
                                      "many_tiles_spanning_lanes", "thin_hf_q80_q4k", "t1_36_blocks_q2k",
                                      "t1_42_blocks_shared_q6k", "q3k_q5k_mix", "t1_q5k_q3k_shared",
-                                     "ragged_tiles_q5k_q3k", "thin_hf_q5k", "t1_full_q3k_q5k"])
+                                     "ragged_tiles_q5k_q3k", "thin_hf_q5k", "t1_full_q3k_q5k", "q40_q51_mix",
+                                     "t1_q51_q40_shared", "ragged_tiles_q40_q51", "thin_hf_q51", "t1_full_q40_q51"])
 def test_edge_layers(variant, fused, path):
     say("edge", variant, fused, path)
     kw = {}
@@ -903,6 +906,21 @@ def test_edge_layers(variant, fused, path):
         # the decode layer's shape (hidden 2048, 256 experts, top-8, shared) in Q3_K / Q5_K
         kw = dict(T=1, H=2048, E=256, k=8, F=512, fmt_gate=syn.Q3_K, fmt_up=syn.Q3_K, fmt_down=syn.Q5_K,
                   shared=True, F_shared=512, sh_fmt_gate=syn.Q5_K, sh_fmt_up=syn.Q5_K, sh_fmt_down=syn.Q3_K)
+    elif variant == "q40_q51_mix":
+        kw = dict(fmt_gate=syn.Q4_0, fmt_up=syn.Q4_0, fmt_down=syn.Q5_1, H=768, F=1536, T=5, E=9, k=3,
+                  shared=True, F_shared=256, sh_fmt_gate=syn.Q5_1, sh_fmt_up=syn.Q5_1, sh_fmt_down=syn.Q4_0)
+    elif variant == "t1_q51_q40_shared":
+        kw = dict(T=1, E=12, k=4, fmt_gate=syn.Q5_1, fmt_up=syn.Q5_1, fmt_down=syn.Q4_0, shared=True,
+                  F_shared=512, sh_fmt_gate=syn.Q4_0, sh_fmt_up=syn.Q4_0, sh_fmt_down=syn.Q5_1)
+    elif variant == "ragged_tiles_q40_q51":
+        kw = dict(T=70, E=3, k=2, F=512, H=768, fmt_gate=syn.Q4_0, fmt_up=syn.Q4_0, fmt_down=syn.Q5_1,
+                  shared=True, F_shared=256, sh_fmt_gate=syn.Q5_1, sh_fmt_up=syn.Q5_1, sh_fmt_down=syn.Q4_0)
+    elif variant == "thin_hf_q51":
+        kw = dict(T=6, E=8, k=2, F=512, H=512, fmt_gate=syn.Q5_1, fmt_up=syn.Q5_1, fmt_down=syn.Q5_1,
+                  shared=True, F_shared=256, sh_fmt_gate=syn.Q4_0, sh_fmt_up=syn.Q4_0, sh_fmt_down=syn.Q5_1)
+    elif variant == "t1_full_q40_q51":
+        kw = dict(T=1, H=2048, E=256, k=8, F=512, fmt_gate=syn.Q4_0, fmt_up=syn.Q4_0, fmt_down=syn.Q5_1,
+                  shared=True, F_shared=512, sh_fmt_gate=syn.Q5_1, sh_fmt_up=syn.Q5_1, sh_fmt_down=syn.Q4_0)
     cfg = _custom_cfg(**kw)
     layer = syn.gen_layer(cfg)
     if variant == "t1_ties":
