@@ -972,3 +972,54 @@ def test_empty_batch():
     moeq.moeq_route(x, dl.w_router, None, cfg.k, cfg.gating, out=out)
     torch.cuda.synchronize()
     assert not out.offsets.cpu().numpy().any() and out.active.cpu().numpy()[0] == 0
+
+
+# ---------------------------------------------------------------- fuzz sweep
+
+FUZZ_FMTS = [syn.Q4_K, syn.Q6_K, syn.Q2_K, syn.Q8_0, syn.Q3_K, syn.Q5_K, syn.Q4_0, syn.Q5_1]
+
+
+def _fuzz_case(seed):
+    """A random layer shape, formats, gating, shared expert, path, call form
+    and logits output, drawn from the seed."""
+    r = np.random.default_rng(9000 + seed)
+    T = int(r.choice([1, 1, 2, 4, 5, 17, 40, 300, 300]))
+    E = int(r.integers(2, 81))
+    k = int(r.integers(1, min(8, E) + 1))
+    H = int(r.choice([256, 512, 768, 1024]))
+    F = int(r.choice([256, 512, 768]))
+    fg, fd = (int(v) for v in r.choice(FUZZ_FMTS, 2))
+    kw = dict(name="fuzz%d" % seed, seed=5000 + seed, T=T, H=H, E=E, k=k, F=F,
+              gating=int(r.choice([syn.SOFTMAX_TOPK, syn.SOFTMAX_ALL, syn.SIGMOID_TOPK])),
+              fmt_gate=fg, fmt_up=fg, fmt_down=fd)
+    if r.random() < 0.5:
+        sg, sd = (int(v) for v in r.choice(FUZZ_FMTS, 2))
+        kw.update(shared=True, F_shared=int(r.choice([256, 512])), sh_fmt_gate=sg, sh_fmt_up=sg, sh_fmt_down=sd)
+    path = str(r.choice(["auto", "gemv", "mfma"]))
+    fused = bool(r.random() < 0.5)
+    logits = bool(r.random() < 0.5)
+    return syn.LayerConfig(**kw), path, fused, logits
+
+
+@pytest.mark.parametrize("seed", range(64))
+def test_fuzz_random_layers(seed):
+    """A sweep of seeded random layers: shapes, every format on gate/up and
+    down and on a shared expert, every gating, forced or automatic path,
+    separate or whole-layer calls, with or without a logits output; ids,
+    weights, lists, every q8_K(h) byte and y against the oracle."""
+    cfg, path, fused, logits = _fuzz_case(seed)
+    say("fuzz", seed, cfg, path, fused, logits)
+    layer = syn.gen_layer(cfg)
+    run = GpuRun(layer, path=PATHS[path], fused=fused, logits=logits)
+    sel = list(range(cfg.T))
+    lg, ids, w = oracle.route(layer.x, layer.w_router, layer.bias, cfg.k, cfg.gating)
+    assert np.array_equal(run.ids, ids), seed
+    check_w(run.w, w)
+    if logits:
+        assert np.allclose(run.logits, lg, rtol=0, atol=1e-12)
+    off, pairs, active = oracle.lists(ids, cfg.E)
+    assert np.array_equal(run.offsets, off) and np.array_equal(run.pairs, pairs)
+    assert np.array_equal(run.active, active)
+    r = oracle.expert_ffn(layer, ids, w, sel)
+    check_hq(run, r.hq, cfg, "fuzz %d" % seed)
+    check_y(run.yv, r.y, "fuzz %d" % seed)
