@@ -192,9 +192,12 @@ size_t moeq_packed_bytes(int32_t fmt, int64_t rows, int64_t cols);
  * caller-owned).  cols % 256 == 0.  Done once when an expert slab becomes
  * resident (Pulsar README, 'How the streaming works').  The packed bytes
  * hold the same codes and scales, reordered so that each super-block loads
- * as contiguous runs.  n_mats == 0 is a no-op; errors: MOEQ_E_UNSUPPORTED
- * for an unknown format, MOEQ_E_INVALID for bad sizes, NULLs or packed not
- * 256-byte aligned.
+ * as contiguous runs.  A fused gate_up tensor (Pulsar README, 'Get a
+ * model': fused gate_up tensors) of an expert, [2F, H] with the gate rows
+ * first, is two [F, H] matrices back to back: packed with n_mats = 2 per
+ * expert, the first packed matrix is its gate and the second its up.
+ * n_mats == 0 is a no-op; errors: MOEQ_E_UNSUPPORTED for an unknown format,
+ * MOEQ_E_INVALID for bad sizes, NULLs or packed not 256-byte aligned.
  */
 int moeq_pack_experts(int32_t fmt, const void* aos, int64_t n_mats, int64_t rows, int64_t cols,
                       void* packed, void* stream);

@@ -359,9 +359,12 @@ class DeviceLayer:
 
     `layer` is a synthetic LayerData (numpy exchange-format bytes).  `present`
     marks experts resident in this instance (others get NULL pointers).
+    fused_gate_up: take each expert's gate and up as one fused exchange tensor
+    [2F, H] (gate rows, then up rows), packed as two matrices per expert.
     """
 
-    def __init__(self, layer, device="cuda", present: Optional[Sequence[bool]] = None, stream=None):
+    def __init__(self, layer, device="cuda", present: Optional[Sequence[bool]] = None, stream=None,
+                 fused_gate_up: bool = False):
         cfg = layer.cfg
         self.cfg = cfg
         self.device = device
@@ -388,8 +391,27 @@ class DeviceLayer:
             self._bufs.append(t)
             return t
 
-        self.gate_ptrs = pack_all(layer.gate, cfg.fmt_gate, cfg.F, cfg.H)
-        self.up_ptrs = pack_all(layer.up, cfg.fmt_up, cfg.F, cfg.H)
+        if fused_gate_up:
+            # one exchange tensor [2F, H] per expert is two [F, H] matrices back
+            # to back: one pack call with two matrices per expert
+            import numpy as np
+            idx = [e for e in range(E) if have[e]]
+            gp, up = torch.zeros(E, dtype=torch.int64), torch.zeros(E, dtype=torch.int64)
+            if idx:
+                fused = np.stack([np.concatenate([layer.gate[e], layer.up[e]]) for e in idx])
+                aos = torch.from_numpy(np.ascontiguousarray(fused)).to(device)
+                packed = moeq_pack_experts(cfg.fmt_gate, aos, 2 * len(idx), cfg.F, cfg.H, stream=stream)
+                pb = moeq_packed_bytes(cfg.fmt_gate, cfg.F, cfg.H)
+                self._bufs.append(packed)
+                for n, e in enumerate(idx):
+                    gp[e] = packed.data_ptr() + 2 * n * pb
+                    up[e] = packed.data_ptr() + (2 * n + 1) * pb
+                del aos
+            self.gate_ptrs, self.up_ptrs = gp.to(device), up.to(device)
+            self._bufs += [self.gate_ptrs, self.up_ptrs]
+        else:
+            self.gate_ptrs = pack_all(layer.gate, cfg.fmt_gate, cfg.F, cfg.H)
+            self.up_ptrs = pack_all(layer.up, cfg.fmt_up, cfg.F, cfg.H)
         self.down_ptrs = pack_all(layer.down, cfg.fmt_down, cfg.H, cfg.F)
         self.sh = None
         if cfg.shared and layer.sh_gate is not None:

@@ -974,6 +974,39 @@ def test_empty_batch():
     assert not out.offsets.cpu().numpy().any() and out.active.cpu().numpy()[0] == 0
 
 
+@pytest.mark.parametrize("fmt", [syn.Q4_K, syn.Q2_K, syn.Q5_1])
+def test_fused_gate_up_tensors(fmt):
+    """Experts given as fused gate_up exchange tensors [2F, H] (gate rows
+    first), packed with two matrices per expert: the packed gate and up bytes
+    equal those packed apart, and the layer's outputs are bit-identical."""
+    cfg = _custom_cfg(T=6, E=10, k=3, F=512, H=768, fmt_gate=fmt, fmt_up=fmt, fmt_down=syn.Q6_K)
+    layer = syn.gen_layer(cfg)
+    say("fused gate_up", fmt)
+    a = moeq.DeviceLayer(layer)
+    b = moeq.DeviceLayer(layer, fused_gate_up=True)
+    pb = moeq.moeq_packed_bytes(fmt, cfg.F, cfg.H)
+
+    def bytes_at(ptrs, e):
+        base = int(ptrs[e].item())
+        buf = next(t for t in b._bufs + a._bufs if t.dtype == torch.uint8 and
+                   t.data_ptr() <= base < t.data_ptr() + t.numel())
+        off = base - buf.data_ptr()
+        return buf[off:off + pb].cpu().numpy()
+
+    for e in range(cfg.E):
+        assert np.array_equal(bytes_at(a.gate_ptrs, e), bytes_at(b.gate_ptrs, e)), e
+        assert np.array_equal(bytes_at(a.up_ptrs, e), bytes_at(b.up_ptrs, e)), e
+    for path in (moeq.PATH_GEMV, moeq.PATH_MFMA):
+        ys = []
+        for dl in (a, b):
+            rn = moeq.LayerRunner(dl, cfg.T, path=path)
+            ys.append(rn.forward(dev(layer.x)).cpu().numpy())
+        assert np.array_equal(ys[0], ys[1]), path
+    r = oracle.expert_ffn(layer, *oracle.route(layer.x, layer.w_router, layer.bias, cfg.k, cfg.gating)[1:],
+                          range(cfg.T))
+    check_y(ys[1], r.y, "fused gate_up")
+
+
 # ---------------------------------------------------------------- fuzz sweep
 
 FUZZ_FMTS = [syn.Q4_K, syn.Q6_K, syn.Q2_K, syn.Q8_0, syn.Q3_K, syn.Q5_K, syn.Q4_0, syn.Q5_1]
