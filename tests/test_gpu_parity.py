@@ -563,7 +563,7 @@ def test_one_token_general_down_partial_residency(fused):
     assert any(lo[e] for e in run.ids[0]) and not all(lo[e] for e in run.ids[0])
 
 
-@pytest.mark.parametrize("variant", ["t1_same_shared", "t1_other_shared", "t300_mfma_shared"])
+@pytest.mark.parametrize("variant", ["t1_same_shared", "t1_other_shared", "t300_mfma_shared", "t300_no_logits"])
 def test_graph_replays_match_eager(variant):
     # the whole layer captured in a HIP graph and replayed several times, with
     # eager library work between the replays: every replay equals the eager
@@ -576,9 +576,13 @@ def test_graph_replays_match_eager(variant):
     elif variant == "t1_other_shared":
         cfg = _custom_cfg(T=1, E=12, k=4, F=256, H=512, shared=True, F_shared=512, sh_fmt_gate=syn.Q8_0,
                           sh_fmt_up=syn.Q8_0, sh_fmt_down=syn.Q6_K)
-    else:
+    elif variant == "t300_mfma_shared":
         cfg = _custom_cfg(T=300, E=10, k=3, F=512, H=512, shared=True, F_shared=512, sh_fmt_gate=syn.Q4_K,
                           sh_fmt_up=syn.Q4_K, sh_fmt_down=syn.Q4_K)
+    else:
+        # no logits output: the router's bf16 contraction, rescoring and lists
+        cfg = _custom_cfg(T=300, E=70, k=6, F=512, H=1024, gating=syn.SIGMOID_TOPK, shared=True, F_shared=256,
+                          sh_fmt_gate=syn.Q5_K, sh_fmt_up=syn.Q5_K, sh_fmt_down=syn.Q3_K)
     layer = syn.gen_layer(cfg)
     say("graph replays", variant)
     dl = moeq.DeviceLayer(layer)
@@ -586,7 +590,7 @@ def test_graph_replays_match_eager(variant):
     fdesc = dl.ffn_desc(cfg.T, aux=aux)
     rdesc = moeq.RouteDesc(cfg.T, cfg.H, cfg.E, cfg.k, cfg.gating, 1.0)
     x = dev(layer.x.astype(np.float32))
-    out = moeq.RouteOut(cfg.T, cfg.E, cfg.k, x.device)
+    out = moeq.RouteOut(cfg.T, cfg.E, cfg.k, x.device, with_logits=variant != "t300_no_logits")
     ws = torch.empty(moeq.moeq_moe_layer_workspace(rdesc, fdesc), dtype=torch.uint8, device=x.device)
     y = torch.empty((cfg.T, cfg.H), dtype=torch.float32, device=x.device)
     stream = torch.cuda.Stream()
@@ -594,6 +598,11 @@ def test_graph_replays_match_eager(variant):
         moeq.moeq_moe_layer(rdesc, fdesc, x, dl.w_router, dl.bias, out, None, y, ws, stream)
     torch.cuda.synchronize()
     ref = y.cpu().numpy().copy()
+    if variant == "t300_no_logits":
+        _, oids, ow = oracle.route(layer.x, layer.w_router, layer.bias, cfg.k, cfg.gating)
+        assert np.array_equal(out.ids.cpu().numpy(), oids)
+        check_w(out.w.cpu().numpy(), ow)
+    ids_ref = out.ids.cpu().numpy().copy()
     r = oracle.expert_ffn(layer, out.ids.cpu().numpy(), out.w.cpu().numpy(), [0])
     check_y(ref[:1], r.y, "eager")
     g = torch.cuda.CUDAGraph()
@@ -603,9 +612,11 @@ def test_graph_replays_match_eager(variant):
     torch.cuda.synchronize()
     for rep in range(3):
         y.fill_(float("nan"))
+        out.ids.fill_(-1)
         g.replay()
         torch.cuda.synchronize()
         assert np.array_equal(y.cpu().numpy(), ref), (variant, rep)
+        assert np.array_equal(out.ids.cpu().numpy(), ids_ref), (variant, rep)
         with torch.cuda.stream(stream):                    # eager work between the replays
             moeq.moeq_moe_layer(rdesc, fdesc, x, dl.w_router, dl.bias, out, None, y, ws, stream)
         torch.cuda.synchronize()
