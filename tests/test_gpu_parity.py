@@ -694,7 +694,7 @@ def _stack_norm_gains(cfg, L):
     return [None if l == 1 else (1.0 + 0.2 * rng.standard_normal(cfg.H)).astype(np.float32) for l in range(L)]
 
 
-@pytest.mark.parametrize("variant", ["decode_t1", "decode_t1_wide", "chunk_t16"])
+@pytest.mark.parametrize("variant", ["decode_t1", "decode_t1_wide", "chunk_t16", "prefill_t300"])
 def test_stack_equals_layer_chain_and_oracle(variant):
     """A stack of layers on a pre-norm residual stream in one call equals the
     chain of single-layer calls (RMS norm of the stream, then the layer adding
@@ -709,11 +709,16 @@ def test_stack_equals_layer_chain_and_oracle(variant):
     elif variant == "decode_t1_wide":          # H past the fused norm's limit: the norm kernel runs first
         cfg = _custom_cfg(T=1, H=4352, E=16, k=2, F=256, fmt_down=syn.Q4_K)
         L = 3
-    else:
+    elif variant == "chunk_t16":
         cfg = _custom_cfg(T=16, H=512, E=24, k=4, F=512, fmt_gate=syn.Q2_K, fmt_up=syn.Q2_K, fmt_down=syn.Q4_K,
                           gating=syn.SIGMOID_TOPK, shared=True, F_shared=256, sh_fmt_gate=syn.Q8_0,
                           sh_fmt_up=syn.Q8_0, sh_fmt_down=syn.Q8_0)
         L = 3
+    else:                                      # more than 256 tokens: the router without a logits output
+        cfg = _custom_cfg(T=300, H=768, E=40, k=5, F=512, fmt_gate=syn.Q5_K, fmt_up=syn.Q5_K, fmt_down=syn.Q4_0,
+                          shared=True, F_shared=256, sh_fmt_gate=syn.Q4_K, sh_fmt_up=syn.Q4_K,
+                          sh_fmt_down=syn.Q6_K)
+        L = 2
     say("stack", variant, L)
     layers = [syn.gen_layer(cfg, layer=l) for l in range(L)]
     dls = [moeq.DeviceLayer(lay) for lay in layers]
