@@ -56,7 +56,9 @@ def parse():
     return ap.parse_args()
 
 
-KERNEL_SOURCES = ["common.hpp", "formats.hpp", "topk.hpp", "one_token.hpp", "ffn_gemv.hip", "route.hip"]
+# the sources of the two launches the traffic counters measure (k_gateup1 with
+# ids given, k_down_rows1)
+KERNEL_SOURCES = ["common.hpp", "formats.hpp", "topk.hpp", "one_token.hpp", "ffn_gemv.hip", "launch.hpp"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_ffn_hbm_traffic.json")
 
 
