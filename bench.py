@@ -19,7 +19,9 @@ paragraph), are reported beside it.
 
 Output: one JSON line (metric, value = MoE-layer tokens/s, roofline of the
 expert FFN, cpu_baseline = the CPU oracle on the host cores), with the 4-token
-verify, 16-token chunk and 8192-token prefill layers measured beside it.
+verify, 16-token chunk and 8192-token prefill layers measured beside it, and
+the measured ceilings (a 4 GiB streaming read, an int8 MFMA loop) that the
+rooflines are also read against.
 """
 import argparse
 import json
@@ -48,6 +50,7 @@ def parse():
     ap.add_argument("--no-prefill", action="store_true", help="skip the 8192-token prefill measurement")
     ap.add_argument("--no-chunk", action="store_true", help="skip the 16-token chunk measurement")
     ap.add_argument("--prefill-steps", type=int, default=20)
+    ap.add_argument("--no-ceilings", action="store_true", help="skip the measured HBM and int8-MFMA ceilings")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="first run a device copy of this many MiB (counter calibration for rocprofv3 --pmc)")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -334,6 +337,65 @@ def ffn_event_us(cyc, n_ev):
 
 INT8_PEAK_TOPS = 5000.0
 NORM_EPS = 1e-6
+CEIL_READ_BYTES = 4 << 30
+CEIL_READ_BLOCKS = 1 << 19
+CEIL_MFMA_BLOCKS = 4096
+CEIL_MFMA_ITERS = 2000
+
+
+def measure_ceilings(dev, reps=10):
+    """Measured ceilings of the two rooflines, read beside the nominal peaks:
+    a streaming read of a 4 GiB buffer with the plain 16-byte global loads the
+    kernels use (GB/s), and a register-only loop of independent int8 MFMAs
+    (TOPS).  Each is the median of `reps` launches timed with HIP events on
+    the stream they run on, after two untimed ones."""
+    import numpy as np
+    import torch
+    from quantized_moe_expert_router_amd import moeq
+    st = torch.cuda.current_stream()
+    buf = torch.zeros(CEIL_READ_BYTES, dtype=torch.uint8, device=dev)
+    sums = torch.empty(CEIL_READ_BLOCKS, dtype=torch.int64, device=dev)
+    flags = torch.empty(4 * CEIL_MFMA_BLOCKS, dtype=torch.int32, device=dev)
+    L = moeq.lib()
+    sp = st.cuda_stream
+
+    def read():
+        moeq._check("moeq_ceiling_read", L.moeq_ceiling_read(buf.data_ptr(), CEIL_READ_BYTES, CEIL_READ_BLOCKS,
+                                                             sums.data_ptr(), sp))
+
+    def mfma():
+        moeq._check("moeq_ceiling_mfma_i8", L.moeq_ceiling_mfma_i8(CEIL_MFMA_ITERS, CEIL_MFMA_BLOCKS,
+                                                                   flags.data_ptr(), sp))
+
+    def median_ms(fn):
+        fn()
+        fn()
+        ts = []
+        for _ in range(reps):
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record(st)
+            fn()
+            b.record(st)
+            b.synchronize()
+            ts.append(a.elapsed_time(b))
+        return float(np.median(ts))
+
+    t_read = median_ms(read)
+    t_mfma = median_ms(mfma)
+    assert int(sums.sum().item()) == 0, "ceiling read: the zero buffer summed to a nonzero value"
+    assert bool((flags == 128 * CEIL_MFMA_ITERS).all().item()), "ceiling MFMA loop: wrong step count"
+    ops = CEIL_MFMA_BLOCKS * 4 * CEIL_MFMA_ITERS * 4 * 2 * 32 * 32 * 32
+    del buf
+    torch.cuda.empty_cache()
+    return {"hbm_read": {"value": CEIL_READ_BYTES / (t_read * 1e-3) / 1e9, "unit": "GB/s",
+                         "bytes": CEIL_READ_BYTES, "launch_us": t_read * 1e3,
+                         "kernel": "moeq_ceiling_read: plain 16-byte global loads, grid-stride, "
+                                   "%d workgroups x 256 threads, 4 loads in flight per thread" % CEIL_READ_BLOCKS},
+            "int8_mfma": {"value": ops / (t_mfma * 1e-3) / 1e12, "unit": "TOPS", "ops": ops,
+                          "launch_us": t_mfma * 1e3,
+                          "kernel": "moeq_ceiling_mfma_i8: 4 independent v_mfma_i32_32x32x32_i8 chains per wave, "
+                                    "%d workgroups x 4 waves, %d steps" % (CEIL_MFMA_BLOCKS, CEIL_MFMA_ITERS)}}
 
 
 def layer_bytes_of(cfg, union):
@@ -512,6 +574,15 @@ def main():
     if not args.no_prefill:
         prefill = secondary("prefill", 2, args.prefill_steps, 2, dev)
 
+    ceil = None
+    if not args.no_ceilings:
+        ceil = measure_ceilings(dev)
+        if prefill is not None:
+            prefill["ffn_int8_frac_of_measured"] = prefill["ffn_int8_tops"] / ceil["int8_mfma"]["value"]
+        for sec in (verify, chunk):
+            if sec is not None:
+                sec["ffn_weight_frac_of_measured"] = sec["ffn_weight_gbs"] / ceil["hbm_read"]["value"]
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(args.cpu_seconds)
@@ -544,7 +615,9 @@ def main():
         "roofline": {"bound": "hbm", "kernel": "expert FFN (gate/up GEMV + down GEMV)",
                      "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic(),
-                     "bytes_per_launch": ffn_bytes, "avg_launch_us": ffn_us},
+                     "bytes_per_launch": ffn_bytes, "avg_launch_us": ffn_us,
+                     "frac_of_measured": achieved / ceil["hbm_read"]["value"] if ceil else None},
+        "ceilings": ceil,
         "cpu_baseline": cpu,
         "verify_b4": verify,
         "chunk16_b16": chunk,

@@ -400,6 +400,31 @@ int moeq_debug_subdots(int32_t fmt, const void* packed_w, int64_t rows, int64_t 
 int moeq_debug_mfma_sums(int32_t fmt, const void* packed_w, int64_t rows, int64_t cols,
                          const void* x_q8K, int64_t n_x, int32_t* out, void* stream);
 
+/*
+ * Measurement helpers: the ceilings that the kernels' rooflines are read
+ * against beside the nominal peaks (the pages judge their own multi-row
+ * kernels by profiler utilisation of the memory units and of DRAM: Pulsar
+ * README, ThinkingCap paragraph).  Neither touches any other state.
+ *
+ * moeq_ceiling_read: reads every 16-byte word of buf (device, 16-byte
+ *   aligned; bytes a positive multiple of 16) once, with n_blocks workgroups
+ *   of 256 threads in a grid-stride loop of plain 16-byte global loads, four
+ *   in flight per thread.  Workgroup b writes the wrapping 64-bit sum of the
+ *   32-bit words it read to out[b] (device, n_blocks uint64 entries, 8-byte
+ *   aligned), so the sum of out modulo 2^64 is the sum of all 32-bit words of
+ *   buf.  The achieved bandwidth is bytes over the launch's duration.
+ * moeq_ceiling_mfma_i8: n_blocks workgroups of 4 waves; each wave runs iters
+ *   steps of four independent v_mfma_i32_32x32x32_i8 on registers holding
+ *   bytes of 1 (4 * 65536 integer operations per step, no memory traffic)
+ *   and writes 128 * iters modulo 2^32 to out[4 b + w] (device, 4 * n_blocks
+ *   int32 entries, 4-byte aligned) for wave w of workgroup b.
+ * Both enqueue on `stream`.  Errors: MOEQ_E_INVALID for a NULL or misaligned
+ * pointer, bytes <= 0 or not a multiple of 16, n_blocks outside 1..2^22, or
+ * iters < 1; MOEQ_E_HIP when the launch fails.
+ */
+int moeq_ceiling_read(const void* buf, int64_t bytes, int32_t n_blocks, uint64_t* out, void* stream);
+int moeq_ceiling_mfma_i8(int64_t iters, int32_t n_blocks, int32_t* out, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

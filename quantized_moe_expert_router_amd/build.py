@@ -10,7 +10,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmoeq.so")
-SOURCES = ["quant_pack.hip", "route.hip", "ffn_gemv.hip", "ffn_mfma.hip", "abi.cpp", "static_ws.hip"]
+SOURCES = ["quant_pack.hip", "route.hip", "ffn_gemv.hip", "ffn_mfma.hip", "ceilings.hip", "abi.cpp",
+           "static_ws.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["-O3", "-std=c++17", "-fPIC", "--offload-arch=gfx950", "-Wall",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

@@ -8,6 +8,7 @@
 #include "formats.hpp"
 #include "launch.hpp"
 #include "mfma_plan.hpp"
+#include "ceilings.hpp"
 
 using namespace moeq;
 
@@ -679,6 +680,18 @@ int moeq_debug_mfma_sums(int32_t fmt, const void* packed_w, int64_t rows, int64_
     return MOEQ_E_INVALID;
   if ((n_x + 31) / 32 > INT32_MAX || rows / 256 > 65535) return MOEQ_E_UNSUPPORTED;
   return hip_status(launch_mfma_ints(fmt, packed_w, rows, cols, x_q8K, n_x, out, (hipStream_t)stream));
+}
+
+int moeq_ceiling_read(const void* buf, int64_t bytes, int32_t n_blocks, uint64_t* out, void* stream) {
+  if (!buf || !out || !aligned(buf, 16) || !aligned(out, 8)) return MOEQ_E_INVALID;
+  if (bytes <= 0 || bytes % 16 || n_blocks < 1 || n_blocks > kCeilMaxBlocks) return MOEQ_E_INVALID;
+  return hip_status(launch_ceiling_read(buf, bytes, n_blocks, out, (hipStream_t)stream));
+}
+
+int moeq_ceiling_mfma_i8(int64_t iters, int32_t n_blocks, int32_t* out, void* stream) {
+  if (!out || !aligned(out, 4)) return MOEQ_E_INVALID;
+  if (iters < 1 || n_blocks < 1 || n_blocks > kCeilMaxBlocks) return MOEQ_E_INVALID;
+  return hip_status(launch_ceiling_mfma_i8(iters, n_blocks, out, (hipStream_t)stream));
 }
 
 }  // extern "C"

@@ -29,7 +29,7 @@ SYMBOLS = ["moeq_status_string", "moeq_quantize_q8K", "moeq_route_workspace", "m
            "moeq_packed_bytes", "moeq_pack_experts", "moeq_expert_ffn_workspace", "moeq_expert_ffn",
            "moeq_moe_layer_workspace", "moeq_moe_layer", "moeq_ffn_h_view", "moeq_debug_subdots",
            "moeq_moe_layer_noalloc", "moeq_debug_mfma_sums", "moeq_moe_stack_workspace", "moeq_moe_stack",
-           "moeq_rms_norm"]
+           "moeq_rms_norm", "moeq_ceiling_read", "moeq_ceiling_mfma_i8"]
 
 
 class MoeqError(RuntimeError):
@@ -115,9 +115,11 @@ def lib() -> ctypes.CDLL:
         L.moeq_ffn_h_view.argtypes = [ctypes.POINTER(FfnDesc), vp, sz, ctypes.POINTER(vp), ctypes.POINTER(vp)]
         L.moeq_debug_subdots.argtypes = [i32, vp, i64, i64, vp, i64, vp, vp]
         L.moeq_debug_mfma_sums.argtypes = [i32, vp, i64, i64, vp, i64, vp, vp]
+        L.moeq_ceiling_read.argtypes = [vp, i64, i32, vp, vp]
+        L.moeq_ceiling_mfma_i8.argtypes = [i64, i32, vp, vp]
         for s in ("moeq_quantize_q8K", "moeq_route", "moeq_pack_experts", "moeq_expert_ffn", "moeq_moe_layer",
                   "moeq_ffn_h_view", "moeq_debug_subdots", "moeq_moe_layer_noalloc", "moeq_debug_mfma_sums",
-                  "moeq_moe_stack", "moeq_rms_norm"):
+                  "moeq_moe_stack", "moeq_rms_norm", "moeq_ceiling_read", "moeq_ceiling_mfma_i8"):
             getattr(L, s).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -348,6 +350,23 @@ def moeq_debug_mfma_sums(fmt: int, packed_w: torch.Tensor, rows: int, cols: int,
     out = torch.empty((n_x, rows, cols // 256, 8), dtype=torch.int32, device=packed_w.device)
     _check("moeq_debug_mfma_sums", lib().moeq_debug_mfma_sums(fmt, _ptr(packed_w), rows, cols, _ptr(x_q8K), n_x,
                                                               _ptr(out), _stream(stream)))
+    return out
+
+
+def moeq_ceiling_read(buf: torch.Tensor, n_blocks: int, stream=None) -> torch.Tensor:
+    """uint64 [n_blocks] partial sums (as int64) of the 32-bit words of buf,
+    read once by the streaming-read ceiling kernel."""
+    out = torch.empty(n_blocks, dtype=torch.int64, device=buf.device)
+    _check("moeq_ceiling_read", lib().moeq_ceiling_read(_ptr(buf), buf.numel() * buf.element_size(), n_blocks,
+                                                        _ptr(out), _stream(stream)))
+    return out
+
+
+def moeq_ceiling_mfma_i8(iters: int, n_blocks: int, device, stream=None) -> torch.Tensor:
+    """int32 [4 * n_blocks]: 128 * iters (mod 2^32) per wave of the int8 MFMA
+    loop ceiling kernel."""
+    out = torch.empty(4 * n_blocks, dtype=torch.int32, device=device)
+    _check("moeq_ceiling_mfma_i8", lib().moeq_ceiling_mfma_i8(iters, n_blocks, _ptr(out), _stream(stream)))
     return out
 
 

@@ -201,3 +201,20 @@ def test_rms_norm_validation():
     assert L.moeq_rms_norm(0x1000, 2, 256, None, ctypes.c_float(-1e-6), 0x2000, None) == moeq.MOEQ_E_INVALID
     assert L.moeq_rms_norm(0x1000, 2, 256, None, ctypes.c_float(float("nan")), 0x2000, None) == moeq.MOEQ_E_INVALID
     assert L.moeq_rms_norm(None, 0, 256, None, e, None, None) == 0                        # T == 0: no-op
+
+
+def test_ceiling_calls_validation():
+    L = moeq.lib()
+    ok = 0x100000
+    assert L.moeq_ceiling_read(None, 1 << 20, 64, ok, None) == moeq.MOEQ_E_INVALID
+    assert L.moeq_ceiling_read(ok, 1 << 20, 64, None, None) == moeq.MOEQ_E_INVALID
+    assert L.moeq_ceiling_read(ok + 8, 1 << 20, 64, ok, None) == moeq.MOEQ_E_INVALID     # buffer 16-byte aligned
+    assert L.moeq_ceiling_read(ok, 1 << 20, 64, ok + 4, None) == moeq.MOEQ_E_INVALID     # sums 8-byte aligned
+    for nbytes in (0, -16, 24):
+        assert L.moeq_ceiling_read(ok, nbytes, 64, ok, None) == moeq.MOEQ_E_INVALID
+    for nb in (0, -1, (1 << 22) + 1):
+        assert L.moeq_ceiling_read(ok, 1 << 20, nb, ok, None) == moeq.MOEQ_E_INVALID
+        assert L.moeq_ceiling_mfma_i8(4, nb, ok, None) == moeq.MOEQ_E_INVALID
+    assert L.moeq_ceiling_mfma_i8(0, 64, ok, None) == moeq.MOEQ_E_INVALID
+    assert L.moeq_ceiling_mfma_i8(4, 64, None, None) == moeq.MOEQ_E_INVALID
+    assert L.moeq_ceiling_mfma_i8(4, 64, ok + 2, None) == moeq.MOEQ_E_INVALID
