@@ -267,9 +267,16 @@ int moeq_expert_ffn(const moeq_ffn_desc* d, const void* x_q8K, const int32_t* to
  * workgroup takes the top-k from the logits itself and one workgroup writes
  * the routing outputs; down with the weighted combine.  Each launch boundary
  * is the only synchronisation (per-layer launches are the floor of a decode
- * step: Strata summary, execution paragraph).  For more tokens it runs the two
- * calls back to back.  logits may be NULL; the FFN's q8_K(h) view
- * (moeq_ffn_h_view with f and this ws) stays valid after the call.
+ * step: Strata summary, execution paragraph).  A chunk of 2..8 tokens with at
+ * most 64 (token, slot) pairs and at most 512 experts, every expert on the
+ * int8 matrix-core path in its fp32-h 8-row tiles (the MTP verify rows: one
+ * router readback and one expert union per chunk-layer, Pulsar README,
+ * DeepSeek-V4-Flash paragraph), routes the same way: router logits with
+ * q8_K(x), then gate/up tiles that each select the chunk's experts from the
+ * logits and form its union themselves (one workgroup writes the routing
+ * outputs), down, the combine.  Other shapes run the two calls back to back.
+ * Outputs are the same on every route.  logits may be NULL; the FFN's q8_K(h)
+ * view (moeq_ffn_h_view with f and this ws) stays valid after the call.
  */
 size_t moeq_moe_layer_workspace(const moeq_route_desc* r, const moeq_ffn_desc* f);
 int moeq_moe_layer(const moeq_route_desc* r, const moeq_ffn_desc* f, const float* x, const float* w_router,

@@ -9,6 +9,7 @@
 #include "launch.hpp"
 #include "mfma_plan.hpp"
 #include "ceilings.hpp"
+#include "route_small.hpp"
 
 using namespace moeq;
 
@@ -106,6 +107,22 @@ FfnLayout ffn_layout(const moeq_ffn_desc* d) {
   L.off_count = o; o += 256;                     // [0]: 32-row tiles, [1]: 8-row tiles
   L.total = o;
   return L;
+}
+
+// The routed 8-row tiles take the fp32-h variant (see launch_mfma) when both
+// of their launches can and the tiles are few (256-row gate/up workgroups
+// would not fill the chip; with many tiles the q8_K(h) epilogue is faster).
+bool routed_thin_hf(const moeq_ffn_desc* d) {
+  return !fmt_sub_scaled(d->fmt_gate) && !fmt_sub_scaled(d->fmt_down) && d->H / 256 <= kHfMaxBlocks &&
+         d->F / 256 <= kHfMaxBlocks && ffn_layout(d).max_thin * (d->F / 256) < kHfMaxWorkgroups;
+}
+
+// Chunks of 2..8 tokens with at most 64 pairs and at most 512 experts, every
+// expert on the MFMA path in fp32-h 8-row tiles, route inline in their first
+// gate/up launch (route_small.hpp) instead of in a selection launch.
+bool small_route_ok(const moeq_ffn_desc* d) {
+  if (d->T < 2 || d->T > kSmallRouteMaxT || d->T * d->k > kSmallPairs || d->E > kSmallRouteMaxE) return false;
+  return gemv_max_of(d) == 0 && routed_thin_hf(d);
 }
 
 int check_ffn_desc(const moeq_ffn_desc* d) {
@@ -257,6 +274,7 @@ int ffn_enqueue(const moeq_ffn_desc* d, const void* x_q8K, const int32_t* topk_i
   const bool mfma = d->T > thr;                  // any expert on the MFMA path
   const int tt = one ? 1 : 4;
   const int max_union = (int)std::min<int64_t>(d->E, d->T * d->k);
+  const bool small_ir = ir != nullptr && !one;   // inline routing of a small chunk (small_route_ok)
   int rc;
 
   auto gu_args = [&](int mode, int64_t F, const LaneGeo& g) {
@@ -327,11 +345,10 @@ int ffn_enqueue(const moeq_ffn_desc* d, const void* x_q8K, const int32_t* topk_i
   // gate/up workgroups would not fill the chip; with many tiles the q8_K(h)
   // epilogue is faster)
   auto hf_ok = [&](bool shared_exp) {
-    const int fg = shared_exp ? d->sh_fmt_gate : d->fmt_gate, fd = shared_exp ? d->sh_fmt_down : d->fmt_down;
-    const int64_t Fx = shared_exp ? d->F_shared : d->F;
-    const int64_t tiles = shared_exp ? (d->T + kThinT - 1) / kThinT : L.max_thin;
-    return !fmt_sub_scaled(fg) && !fmt_sub_scaled(fd) && d->H / 256 <= kHfMaxBlocks && Fx / 256 <= kHfMaxBlocks &&
-           tiles * (Fx / 256) < kHfMaxWorkgroups;
+    if (!shared_exp) return routed_thin_hf(d);
+    const int64_t tiles = (d->T + kThinT - 1) / kThinT;
+    return !fmt_sub_scaled(d->sh_fmt_gate) && !fmt_sub_scaled(d->sh_fmt_down) && d->H / 256 <= kHfMaxBlocks &&
+           d->F_shared / 256 <= kHfMaxBlocks && tiles * (d->F_shared / 256) < kHfMaxWorkgroups;
   };
   auto mfma_launch = [&](int mode, bool shared_exp, bool thin, hipStream_t st, bool fold = false) -> int {
     const bool hf = thin && hf_ok(shared_exp);
@@ -378,6 +395,13 @@ int ffn_enqueue(const moeq_ffn_desc* d, const void* x_q8K, const int32_t* topk_i
     const int64_t nrb = gy;
     a.rb = std::max<int64_t>(1, std::min<int64_t>(nrb, (int64_t)gx * nrb / 2048));
     gy = (unsigned)((nrb + a.rb - 1) / a.rb);
+    if (mode == 0 && thin && !shared_exp && small_ir) {
+      // a small chunk: these tiles route inline (and write the routing
+      // outputs and the 8-row tile list the down launch reads)
+      const SmallRoute sr{ir->logits, d->E, ir->gating, ir->scale, ir->ids, ir->w, ir->offsets, ir->pairs,
+                          ir->active, MfmaPlan{thr, (int)L.max_tiles, tiles, tcount, thin_tiles, tcount + 1}};
+      return launch_mfma_route_gateup(fmt, dim3(gx, gy), a, sr, st);
+    }
     return launch_mfma(fmt, mode, thin, hf, dim3(gx, gy), a, st);
   };
 
@@ -531,6 +555,15 @@ int layer_enqueue(const moeq_route_desc* r, const moeq_ffn_desc* f, const float*
     InlineRoute ir{lg, r->gating, r->scale, topk_ids, expert_offsets, pairs, active, topk_w};
     return hip_status(ffn_enqueue(f, xq, topk_ids, topk_w, expert_offsets, pairs, active, shared_scale, y, wsb, &ir,
                                   false, s));
+  }
+  if (small_route_ok(f)) {
+    // a small chunk: logits + q8_K(x) in one launch, then the first gate/up
+    // launch routes inline (no selection launch)
+    double* lg = logits ? logits : (double*)(wsb + L.off_route);
+    if ((rc = launch_logits(r->T, r->H, r->E, x, w_router, bias, lg, xq, s))) return hip_status(rc);
+    InlineRoute ir{lg, r->gating, r->scale, topk_ids, expert_offsets, pairs, active, topk_w};
+    return hip_status(ffn_enqueue(f, xq, topk_ids, topk_w, expert_offsets, pairs, active, shared_scale, y, wsb, &ir,
+                                  true, s));
   }
   // the routing kernel also builds the MFMA tile lists of the FFN (one launch fewer)
   const FfnLayout FL = ffn_layout(f);

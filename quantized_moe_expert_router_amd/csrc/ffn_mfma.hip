@@ -50,6 +50,7 @@
 #include "formats.hpp"
 #include "mfma_plan.hpp"
 #include "launch.hpp"
+#include "route_small.hpp"
 
 namespace moeq {
 
@@ -877,6 +878,39 @@ __device__ __forceinline__ void combine_block(const float* __restrict__ yp, int6
 //   yp[row] = fl32(gate weight * y).
 // TM: activation rows a tile stages (32; or 8 for experts with at most 8 rows,
 //   whose MFMA rows 8..31 are zero and whose combine covers only 8 rows).
+// The tile of this workgroup: for the shared expert, tokens t0 .. t0+n-1 of
+// block row blockIdx.x; for routed experts, tile list entry j (expert e, rows
+// t0 .. t0+n-1 of its list at list_off).  32-row tiles run in XCD-aware
+// order: workgroup b runs on XCD b % 8, and XCD x takes the x-th contiguous
+// eighth of the expert-ordered tile list, so the tiles of one expert run side
+// by side on one XCD and share its L2 for the expert's weights (the grid is a
+// multiple of 8 covering the list).  Measured at prefill size: gate/up
+// fetches 0.84 GB past L2 instead of 1.93 GB, down 0.39 GB instead of
+// 0.89 GB (the algorithmic bytes).  8-row tiles have one tile per expert:
+// plain order.  False: no tile for this workgroup.
+template <int TM>
+__device__ __forceinline__ bool pick_tile(const MfmaArgs& a, int& e, int& t0, int& n, int64_t& list_off) {
+  e = -1;
+  list_off = 0;
+  if (a.shared) {
+    t0 = (int)blockIdx.x * TM;
+    if (t0 >= a.T) return false;
+    n = (int)((a.T - t0) < TM ? (a.T - t0) : TM);
+    return true;
+  }
+  const int cnt = *a.count, b = (int)blockIdx.x;
+  int j = b;
+  if constexpr (TM == 32) {
+    const int per = (cnt + 7) >> 3;
+    j = (b & 7) * per + (b >> 3);
+    if ((b >> 3) >= per) return false;
+  }
+  if (j >= cnt) return false;
+  const int4 tl = a.tiles[j];
+  e = tl.x; t0 = tl.y; n = tl.z; list_off = tl.w;
+  return true;
+}
+
 // RES: the whole activation tile fits in LDS (K up to kRes(TM) 256-blocks), so
 //   the k-loop runs without barriers; otherwise the blocks stream through a
 //   double-buffered stage (one barrier per block).
@@ -899,8 +933,13 @@ static_assert(kRes(8) == kHfMaxBlocks, "resident 8-row tiles");
 //   after staging its rows of a row block, the tile also does the combine of
 //   its tokens over those columns into y (combine_block), so no separate
 //   combine launch is needed.
-template <int FMT, int MODE, bool RES, int TM, int RING, int NW = 8, bool HF = false, bool COMB = false>
-__device__ __forceinline__ void mfma_tile(const MfmaArgs& a) {
+// RNPER > 0 (fp32-h gate/up of small chunks): the workgroup routes the chunk
+//   inline from the logits (route_small_tile, top-k with RNPER logits per
+//   lane) and takes its tile and pair rows from that, not from the lists.
+template <int FMT, int MODE, bool RES, int TM, int RING, int NW = 8, bool HF = false, bool COMB = false,
+          int RNPER = 0>
+__device__ __forceinline__ void mfma_tile(const MfmaArgs& a, const SmallRoute* rt = nullptr) {
+  static_assert(RNPER == 0 || (MODE == 0 && HF && TM == kThinRows), "inline routing: fp32-h 8-row gate/up");
   static_assert(NW == 8 || (NW == 16 && MODE == 0 && RES && RING > 1) || (NW == 4 && MODE == 0 && HF),
                 "split waves: resident gate/up ring");
   static_assert(!HF || (RES && RING > 1), "fp32 h: resident ring tiles");
@@ -919,30 +958,16 @@ __device__ __forceinline__ void mfma_tile(const MfmaArgs& a) {
   __shared__ __align__(16) uint8_t zrow[kQsStride];   // A rows past the tile height read zeros
 
   // ---- tile: expert (or the shared expert) and its rows t0 .. t0+n-1
-  int e = -1, t0, n;
-  int64_t list_off = 0;
-  if (a.shared) {
-    t0 = (int)blockIdx.x * TM;
-    if (t0 >= a.T) return;
-    n = (int)((a.T - t0) < TM ? (a.T - t0) : TM);
+  int e, t0 = 0, n;
+  int64_t list_off;
+  const int* rkey = nullptr;   // inline routing: sorted pair keys (expert << 6 | pair) in LDS
+  if constexpr (RNPER > 0) {
+    __shared__ int r_ids[kSmallPairs], r_key[kSmallPairs], r_act[kSmallPairs + 1], r_ebase[kSmallPairs + 1];
+    __shared__ int r_off[kSmallRouteMaxE + 1];
+    if (!route_small_tile<RNPER>(*rt, a.T, a.k, r_ids, r_key, r_act, r_off, r_ebase, e, n, list_off)) return;
+    rkey = r_key;
   } else {
-    // 32-row tiles in XCD-aware order: workgroup b runs on XCD b % 8, and XCD
-    // x takes the x-th contiguous eighth of the expert-ordered tile list, so
-    // the tiles of one expert run side by side on one XCD and share its L2
-    // for the expert's weights (the grid is a multiple of 8 covering the
-    // list).  Measured at prefill size: gate/up fetches 0.84 GB past L2
-    // instead of 1.93 GB, down 0.39 GB instead of 0.89 GB (the algorithmic
-    // bytes).  8-row tiles have one tile per expert: plain order.
-    const int cnt = *a.count, b = (int)blockIdx.x;
-    int j = b;
-    if constexpr (TM == 32) {
-      const int per = (cnt + 7) >> 3;
-      j = (b & 7) * per + (b >> 3);
-      if ((b >> 3) >= per) return;
-    }
-    if (j >= cnt) return;
-    const int4 tl = a.tiles[j];
-    e = tl.x; t0 = tl.y; n = tl.z; list_off = tl.w;
+    if (!pick_tile<TM>(a, e, t0, n, list_off)) return;
   }
   const int64_t nrb = a.N / RB;
   const int64_t rb0 = (int64_t)blockIdx.y * a.rb;
@@ -985,7 +1010,7 @@ __device__ __forceinline__ void mfma_tile(const MfmaArgs& a) {
         orr = MODE == 0 ? (int64_t)(t0 + tid) : a.T * a.k + t0 + tid;
         wt = a.shared_scale != nullptr ? (double)a.shared_scale[t0 + tid] : 1.0;
       } else {
-        const int p = a.pairs[list_off + t0 + tid];
+        const int p = rkey != nullptr ? (rkey[list_off + t0 + tid] & 63) : a.pairs[list_off + t0 + tid];
         ridx = MODE == 0 ? p / a.k : p;
         orr = p;
         wt = MODE == 1 ? (double)a.topk_w[p] : 0.0;
@@ -1275,6 +1300,12 @@ __global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_pe
     MfmaArgs a) {
   mfma_tile<FMT, 1, true, 8, 2, 8, true>(a);
 }
+// the same gate/up tiles of a small chunk, routing inline
+template <int FMT, int NPER>
+__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(3, 8))) void
+k_mfma_hf_gateup_route(MfmaArgs a, SmallRoute r) {
+  mfma_tile<FMT, 0, true, 8, 2, 4, true, false, NPER>(a, &r);
+}
 
 // ------------------------------------------------------------ integer hook
 //
@@ -1410,6 +1441,28 @@ void launch_fmt(int mode, bool thin, bool hf, dim3 grid, const MfmaArgs& a, int6
 }
 
 }  // namespace
+
+int launch_mfma_route_gateup(int fmt, dim3 grid, const MfmaArgs& a, const SmallRoute& r, hipStream_t s) {
+  if (grid.x == 0 || grid.y == 0) return 0;
+  if (a.T < 2 || a.T > kSmallRouteMaxT || a.T * a.k > kSmallPairs || r.E > kSmallRouteMaxE) return -2;
+  if (a.K / 256 > kRes(8) || a.hf == nullptr || a.shared) return -2;
+#define MOEQ_RG(F, N) hipLaunchKernelGGL((k_mfma_hf_gateup_route<F, N>), grid, dim3(256), 0, s, a, r)
+#define MOEQ_RG_FMT(F) \
+  if (r.E <= 256) MOEQ_RG(F, 4); \
+  else MOEQ_RG(F, 8);
+  switch (fmt) {
+    case FQ4K: MOEQ_RG_FMT(FQ4K) break;
+    case FQ2K: MOEQ_RG_FMT(FQ2K) break;
+    case FQ80: MOEQ_RG_FMT(FQ80) break;
+    case FQ5K: MOEQ_RG_FMT(FQ5K) break;
+    case FQ40: MOEQ_RG_FMT(FQ40) break;
+    case FQ51: MOEQ_RG_FMT(FQ51) break;
+    default: return -2;
+  }
+#undef MOEQ_RG_FMT
+#undef MOEQ_RG
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
 
 int launch_mfma(int fmt, int mode, bool thin, bool hf, dim3 grid, const MfmaArgs& a, hipStream_t s) {
   if (grid.x == 0 || grid.y == 0) return 0;

@@ -9,6 +9,7 @@
 #include "launch.hpp"
 #include "topk.hpp"
 #include "mfma_plan.hpp"
+#include "route_small.hpp"
 
 namespace moeq {
 
@@ -639,59 +640,6 @@ __device__ void offsets_and_union(int* cnt, int64_t E, int32_t* offsets, int32_t
     active[0] = ftot;
     if (loff) loff[E] = tot;
     if (lact) lact[0] = ftot;
-  }
-}
-
-// Lists of at most 64 (token, slot) pairs p = t*k + slot, from their experts
-// in LDS: ordered by expert and, inside an expert, by p (the counting-sort
-// order), pair p's list position is its rank by the key (expert, p) -- keys
-// are distinct, so the ranks are a permutation.  Wave 0 ranks the pairs
-// (keys broadcast lane by lane), writes the pair list and the sorted keys,
-// and takes the union as the first key of every expert in that order; then
-// every thread finds offsets[e] (the pairs with a smaller expert) by binary
-// search in the sorted keys.  The union and offsets also go to LDS (lact,
-// loff) for the tile lists that may follow.
-constexpr int kSmallPairs = 64;
-__device__ void small_lists(const int* ids_s, int P, int64_t E, int32_t* __restrict__ offsets,
-                            int32_t* __restrict__ pairs, int32_t* __restrict__ active, int* skey, int* loff,
-                            int* lact) {
-  if (threadIdx.x < kWave) {
-    const int lane = lane_id();
-    const int key = lane < P ? ((ids_s[lane] << 6) | lane) : INT_MAX;
-    int rank = 0;
-    for (int q = 0; q < P; ++q) rank += __builtin_amdgcn_readlane(key, q) < key;
-    if (lane < P) {
-      skey[rank] = key;
-      gst_i32(pairs + rank, lane);
-    }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    const int ex = lane < P ? skey[lane] >> 6 : -1;
-    const int prev = lane > 0 && lane < P ? skey[lane - 1] >> 6 : -1;
-    const bool first = lane < P && ex != prev;
-    const uint64_t bal = __ballot(first);
-    const int idx = __popcll(bal & ((1ull << lane) - 1ull));
-    if (first) {
-      lact[1 + idx] = ex;
-      gst_i32(active + 1 + idx, ex);
-    }
-    if (lane == 0) {
-      lact[0] = __popcll(bal);
-      gst_i32(active, __popcll(bal));
-    }
-  }
-  __syncthreads();
-  for (int64_t e = threadIdx.x; e <= E; e += blockDim.x) {
-    const int ke = (int)e << 6;
-    int lo = 0, hi = P;                     // first sorted position whose key is >= (e, 0)
-    while (lo < hi) {
-      const int mid = (lo + hi) >> 1;
-      if (skey[mid] < ke) lo = mid + 1;
-      else hi = mid;
-    }
-    loff[e] = lo;
-    gst_i32(offsets + e, lo);
   }
 }
 

@@ -976,6 +976,56 @@ def test_edge_layers(variant, fused, path):
             assert np.array_equal(run.hq_s[t, :nbs], r.hq[t, cfg.k, :nbs]), (variant, t, "shared")
 
 
+@pytest.mark.parametrize("variant", ["t2_e16_sigmoid_shared", "t8_k8_e512_q4k", "t4_e300_q5k_q40", "t5_k7_e7_q51",
+                                     "t3_softmax_all_e100_q80_q2k", "t4_ties_across_lanes_and_slots"])
+def test_small_chunk_inline_route_matches_calls(variant):
+    """A chunk of 2..8 tokens with at most 64 (token, slot) pairs and at most
+    512 experts, on fp32-h 8-row tiles, routes inline in its first gate/up
+    launch under the layer call (every workgroup selects the experts and forms
+    the union itself, one writes the routing outputs); the separate route and
+    FFN calls take the selection launch.  Both must give the same routing
+    outputs, q8_K(h) bytes and y bit for bit, and match the oracle."""
+    say("small chunk inline route", variant)
+    kw = dict(t2_e16_sigmoid_shared=dict(T=2, E=16, k=3, gating=syn.SIGMOID_TOPK, F=512, shared=True, F_shared=256,
+                                         sh_fmt_gate=syn.Q8_0, sh_fmt_up=syn.Q8_0, sh_fmt_down=syn.Q4_K),
+              t8_k8_e512_q4k=dict(T=8, E=512, k=8, F=256),
+              t4_e300_q5k_q40=dict(T=4, E=300, k=6, H=768, F=512, fmt_gate=syn.Q5_K, fmt_up=syn.Q5_K,
+                                   fmt_down=syn.Q4_0),
+              t5_k7_e7_q51=dict(T=5, E=7, k=7, fmt_gate=syn.Q5_1, fmt_up=syn.Q5_1, fmt_down=syn.Q5_1),
+              t3_softmax_all_e100_q80_q2k=dict(T=3, E=100, k=4, gating=syn.SOFTMAX_ALL, F=512, fmt_gate=syn.Q8_0,
+                                               fmt_up=syn.Q8_0, fmt_down=syn.Q2_K),
+              t4_ties_across_lanes_and_slots=dict(T=4, E=130, k=5))[variant]
+    cfg = _custom_cfg(**kw)
+    layer = syn.gen_layer(cfg)
+    if variant == "t4_ties_across_lanes_and_slots":
+        # three experts with the same router row, large enough to win for every
+        # token: exact ties between lanes 1 and 2 and register slots 0, 1, 2
+        # (element e sits in lane e % 64, slot e / 64)
+        tied = layer.x.mean(axis=0) * 0.02
+        for e in (1, 66, 129):
+            layer.w_router[e] = tied
+    calls = GpuRun(layer, path=moeq.PATH_MFMA, fused=False)
+    fused = GpuRun(layer, path=moeq.PATH_MFMA, fused=True)
+    for name in ("ids", "w", "logits", "offsets", "pairs", "active", "yv"):
+        a, b = getattr(calls, name), getattr(fused, name)
+        assert a.dtype == b.dtype and np.array_equal(a.view(np.uint8), b.view(np.uint8)), (variant, name)
+    nbF = cfg.F // 256 * 292
+    assert np.array_equal(calls.hq_r[:cfg.T * cfg.k, :nbF], fused.hq_r[:cfg.T * cfg.k, :nbF])
+    if cfg.shared:
+        nbs = cfg.F_shared // 256 * 292
+        assert np.array_equal(calls.hq_s[:cfg.T, :nbs], fused.hq_s[:cfg.T, :nbs])
+    sel = list(range(cfg.T))
+    ids, w = check_route(fused, layer, sel)
+    r = oracle.expert_ffn(layer, ids, w, sel)
+    check_y(fused.yv, r.y, variant)
+    for t in sel:
+        for s_ in range(cfg.k):
+            assert np.array_equal(fused.hq_r[t * cfg.k + s_, :nbF], r.hq[t, s_, :nbF])
+    if variant == "t4_ties_across_lanes_and_slots":
+        for t in sel:
+            assert list(ids[t][:3]) == [1, 66, 129]            # tied winners first, lower index first
+
+
 def test_empty_batch():
     say("empty batch")
     cfg = _custom_cfg(T=1)
