@@ -962,9 +962,9 @@ __device__ __forceinline__ void mfma_tile(const MfmaArgs& a, const SmallRoute* r
   int64_t list_off;
   const int* rkey = nullptr;   // inline routing: sorted pair keys (expert << 6 | pair) in LDS
   if constexpr (RNPER > 0) {
-    __shared__ int r_ids[kSmallPairs], r_key[kSmallPairs], r_act[kSmallPairs + 1], r_ebase[kSmallPairs + 1];
-    __shared__ int r_off[kSmallRouteMaxE + 1];
-    if (!route_small_tile<RNPER>(*rt, a.T, a.k, r_ids, r_key, r_act, r_off, r_ebase, e, n, list_off)) return;
+    __shared__ int r_ids[kSmallPairs], r_key[kSmallPairs], r_act[kSmallPairs + 1], r_pos[kSmallPairs + 1];
+    __shared__ int r_ebase[kSmallPairs + 1], r_off[kSmallRouteMaxE + 1];
+    if (!route_small_tile<RNPER>(*rt, a.T, a.k, r_ids, r_key, r_act, r_pos, r_off, r_ebase, e, n, list_off)) return;
     rkey = r_key;
   } else {
     if (!pick_tile<TM>(a, e, t0, n, list_off)) return;

@@ -22,11 +22,13 @@ namespace moeq {
 // offsets[e] (the pairs with a smaller expert) by binary search in the sorted
 // keys.  Sorted keys, union and offsets go to LDS (skey, lact, loff); the
 // pair list, union and offsets also go to memory unless those pointers are
-// null.  Ends without a barrier after the offsets.
+// null.  With lpos, union entry i's first sorted position goes to lpos[i]
+// (lpos[union size] = P); a null loff skips the offsets (offsets must then be
+// null too).  Ends without a barrier after the offsets.
 constexpr int kSmallPairs = 64;
 __device__ __forceinline__ void small_lists(const int* ids_s, int P, int64_t E, int32_t* __restrict__ offsets,
                                             int32_t* __restrict__ pairs, int32_t* __restrict__ active, int* skey,
-                                            int* loff, int* lact) {
+                                            int* loff, int* lact, int* lpos = nullptr) {
   if (threadIdx.x < kWave) {
     const int lane = lane_id();
     const int key = lane < P ? ((ids_s[lane] << 6) | lane) : INT_MAX;
@@ -46,14 +48,17 @@ __device__ __forceinline__ void small_lists(const int* ids_s, int P, int64_t E, 
     const int idx = __popcll(bal & ((1ull << lane) - 1ull));
     if (first) {
       lact[1 + idx] = ex;
+      if (lpos) lpos[idx] = lane;
       if (active) gst_i32(active + 1 + idx, ex);
     }
     if (lane == 0) {
       lact[0] = __popcll(bal);
+      if (lpos) lpos[__popcll(bal)] = P;
       if (active) gst_i32(active, __popcll(bal));
     }
   }
   __syncthreads();
+  if (loff == nullptr) return;
   for (int64_t e = threadIdx.x; e <= E; e += blockDim.x) {
     const int ke = (int)e << 6;
     int lo = 0, hi = P;                     // first sorted position whose key is >= (e, 0)
@@ -89,15 +94,16 @@ struct SmallRoute {
 int launch_mfma_route_gateup(int fmt, dim3 grid, const MfmaArgs& a, const SmallRoute& r, hipStream_t s);
 
 // The routing of a small chunk by one workgroup (every thread calls it; the
-// LDS arrays hold kSmallPairs, kSmallPairs, kSmallPairs + 1, E + 1 and
-// kSmallPairs + 1 ints): each wave takes tokens wave, wave + waves, ... and
-// selects their experts from the logits; then the lists in LDS.  Workgroup
-// (0, 0) writes the ids, gate weights, lists and the MFMA tile lists to
-// memory.  The workgroup's tile is union entry blockIdx.x: its expert e, rows
-// n and list offset; false when the union has no such entry.
+// LDS arrays hold kSmallPairs, kSmallPairs, kSmallPairs + 1, kSmallPairs + 1,
+// E + 1 and kSmallPairs + 1 ints): each wave takes tokens wave, wave + waves,
+// ... and selects their experts from the logits; then the sorted pairs and
+// the union in LDS.  Workgroup (0, 0) also forms the offsets of every expert
+// and writes the ids, gate weights, lists and the MFMA tile lists to memory.
+// The workgroup's tile is union entry blockIdx.x: its expert e, rows n and
+// list offset; false when the union has no such entry.
 template <int NPER>
 __device__ __forceinline__ bool route_small_tile(const SmallRoute& r, int64_t T, int k, int* ids_s, int* skey,
-                                                 int* lact, int* loff, int* ebase, int& e, int& n,
+                                                 int* lact, int* lpos, int* loff, int* ebase, int& e, int& n,
                                                  int64_t& list_off) {
   const int lane = lane_id(), wv = threadIdx.x >> 6, nw = blockDim.x >> 6;
   const bool writer = blockIdx.x == 0 && blockIdx.y == 0;
@@ -115,14 +121,14 @@ __device__ __forceinline__ bool route_small_tile(const SmallRoute& r, int64_t T,
   }
   __syncthreads();
   small_lists(ids_s, (int)(T * k), r.E, writer ? r.offsets : nullptr, writer ? r.pairs : nullptr,
-              writer ? r.active : nullptr, skey, loff, lact);
+              writer ? r.active : nullptr, skey, writer ? loff : nullptr, lact, lpos);
   __syncthreads();
   if (writer) mfma_plan_block(lact, loff, r.plan, ebase);
-  const int na = lact[0];
-  if ((int)blockIdx.x >= na) return false;
-  e = lact[1 + blockIdx.x];
-  list_off = loff[e];
-  n = loff[e + 1] - loff[e];
+  const int na = lact[0], j = (int)blockIdx.x;
+  if (j >= na) return false;
+  e = lact[1 + j];
+  list_off = lpos[j];
+  n = lpos[j + 1] - lpos[j];
   return true;
 }
 
