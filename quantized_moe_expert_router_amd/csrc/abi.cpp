@@ -424,18 +424,23 @@ int ffn_enqueue(const moeq_ffn_desc* d, const void* x_q8K, const int32_t* topk_i
   // MFMA path: q8_K(h) rows straight away)
   const int n_routed_slots = one ? d->k : max_union;
   // the shared expert goes first when it has a stream of its own (it starts
-  // at once), after the routed launches otherwise
+  // at once), after the routed launches otherwise.  Beside the routed
+  // launches, a shared expert of up to 16 tokens takes 8-row fp32-h tiles:
+  // two of them give its gate/up and down several times the workgroups of one
+  // 32-row tile (its weights are read once per tile), so it no longer trails
+  // the routed launches, whose workgroups hold the CUs.
+  const bool sh_thin = d->T <= kThinT || (ss != s && d->T <= 2 * kThinT && hf_ok(true));
   auto shared_gateup = [&]() -> int {
     if (!sh || (gemv && same_shape)) return 0;
-    return mfma ? mfma_launch(0, true, d->T <= kThinT, ss) : gateup(kModeShared, d->sh_fmt_gate, d->F_shared, 1, ss);
+    return mfma ? mfma_launch(0, true, sh_thin, ss) : gateup(kModeShared, d->sh_fmt_gate, d->F_shared, 1, ss);
   };
   // A shared expert on the MFMA path (32-row tiles) that runs after the
   // routed down launches on the same stream also does the combine (no
   // k_combine launch).
-  const bool fold_combine = sh && mfma && !gemv && ss == s && d->T > kThinT;
+  const bool fold_combine = sh && mfma && !gemv && ss == s && !sh_thin;
   auto shared_down = [&]() -> int {
     if (!sh || (gemv && same_shape)) return 0;
-    return mfma ? mfma_launch(1, true, d->T <= kThinT, ss, fold_combine)
+    return mfma ? mfma_launch(1, true, sh_thin, ss, fold_combine)
                 : down(kModeShared, d->sh_fmt_down, d->F_shared, 1, ss);
   };
   if (ss != s && (rc = shared_gateup())) return rc;
