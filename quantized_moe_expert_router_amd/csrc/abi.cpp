@@ -420,6 +420,14 @@ int ffn_enqueue(const moeq_ffn_desc* d, const void* x_q8K, const int32_t* topk_i
   const bool sh_apart = sh && (mfma || !same_shape) && d->T <= kSideMaxT && has_aux(d);
   hipStream_t ss = s;
   if (sh_apart && (rc = fork_aux(d, s, &ss))) return rc;
+  // Past kSideMaxT tokens the shared expert stays on s; the 8-row tiles of the
+  // experts with few rows then run on the auxiliary stream beside the 32-row
+  // tiles (they read the lists and write only their own pairs' rows), joined
+  // before the shared expert's down tiles or the combine, which read every
+  // staged row.
+  const bool thin_apart = mfma && !sh_apart && d->T > kSideMaxT && has_aux(d);
+  hipStream_t ts = s;
+  if (thin_apart && (rc = fork_aux(d, s, &ts))) return rc;
   // gate/up: h[pair, f] = fl32(silu(g) u)  (dot-product path: fp32 h rows;
   // MFMA path: q8_K(h) rows straight away)
   const int n_routed_slots = one ? d->k : max_union;
@@ -453,7 +461,7 @@ int ffn_enqueue(const moeq_ffn_desc* d, const void* x_q8K, const int32_t* topk_i
   }
   if (mfma) {
     if (d->T > kThinT && (rc = mfma_launch(0, false, false, s))) return rc;
-    if ((rc = mfma_launch(0, false, true, s))) return rc;
+    if ((rc = mfma_launch(0, false, true, ts))) return rc;
   }
   if (ss == s && (rc = shared_gateup())) return rc;
   // down and the weighted combine
@@ -475,8 +483,9 @@ int ffn_enqueue(const moeq_ffn_desc* d, const void* x_q8K, const int32_t* topk_i
   }
   if (mfma) {
     if (d->T > kThinT && (rc = mfma_launch(1, false, false, s))) return rc;
-    if ((rc = mfma_launch(1, false, true, s))) return rc;
+    if ((rc = mfma_launch(1, false, true, ts))) return rc;
   }
+  if (thin_apart && (rc = join_aux(d, s))) return rc;
   if (ss == s && (rc = shared_down())) return rc;
   if (ss != s && (rc = join_aux(d, s))) return rc;
   if (fold_combine) return 0;
