@@ -869,15 +869,6 @@ __device__ __forceinline__ void combine_block(const float* __restrict__ yp, int6
   }
 }
 
-// ------------------------------------------------------------ the kernel
-//
-// MODE 0 (gate/up): A = q8_K(x) rows of the tile's tokens, W0 = gate, W1 = up;
-//   epilogue per 256-row block: h = fl32(silu(g) u) into LDS, then q8_K(h) of
-//   the block (one q8_K block per tile row) into hq.
-// MODE 1 (down): A = q8_K(h) rows of the tile's pairs, W0 = down; epilogue
-//   yp[row] = fl32(gate weight * y).
-// TM: activation rows a tile stages (32; or 8 for experts with at most 8 rows,
-//   whose MFMA rows 8..31 are zero and whose combine covers only 8 rows).
 // The tile of this workgroup: for the shared expert, tokens t0 .. t0+n-1 of
 // block row blockIdx.x; for routed experts, tile list entry j (expert e, rows
 // t0 .. t0+n-1 of its list at list_off).  32-row tiles run in XCD-aware
@@ -911,6 +902,15 @@ __device__ __forceinline__ bool pick_tile(const MfmaArgs& a, int& e, int& t0, in
   return true;
 }
 
+// ------------------------------------------------------------ the kernel
+//
+// MODE 0 (gate/up): A = q8_K(x) rows of the tile's tokens, W0 = gate, W1 = up;
+//   epilogue per 256-row block: h = fl32(silu(g) u) into LDS, then q8_K(h) of
+//   the block (one q8_K block per tile row) into hq.
+// MODE 1 (down): A = q8_K(h) rows of the tile's pairs, W0 = down; epilogue
+//   yp[row] = fl32(gate weight * y).
+// TM: activation rows a tile stages (32; or 8 for experts with at most 8 rows,
+//   whose MFMA rows 8..31 are zero and whose combine covers only 8 rows).
 // RES: the whole activation tile fits in LDS (K up to kRes(TM) 256-blocks), so
 //   the k-loop runs without barriers; otherwise the blocks stream through a
 //   double-buffered stage (one barrier per block).
