@@ -67,23 +67,34 @@ int gemv_max_of(const moeq_ffn_desc* d) {
   return d->T == 1 ? INT32_MAX : 0;
 }
 
-// Upper bound on the MFMA tiles of the routed experts: sum over experts with
-// more than thr rows of ceil(n_e / 32) <= (T*k + 31 * U) / 32, with U the
+// Chunks of at most kAllThinT tokens put every routed expert in 8-row tiles
+// (at most two per expert): no expert then needs a 32-row tile, and the two
+// 32-row launches, which would find no tile, are left out.
+constexpr int kThinT = kThinRows;    // rows of the MFMA tiles of experts with few rows
+constexpr int kAllThinT = 2 * kThinT;
+// The most rows an expert may have and still take 8-row tiles.
+int thin_max_of(const moeq_ffn_desc* d) { return d->T <= kAllThinT ? kAllThinT : kThinT; }
+
+// Upper bound on the 32-row MFMA tiles of the routed experts: sum over experts
+// with more than thr rows of ceil(n_e / 32) <= (T*k + 31 * U) / 32, with U the
 // number of such experts.
 int64_t mfma_max_tiles(const moeq_ffn_desc* d, int thr) {
   const int64_t P = d->T * d->k;
-  if (d->T <= thr) return 0;
+  if (d->T <= thr || d->T <= kAllThinT) return 0;
   const int64_t U = std::min<int64_t>(d->E, P / (thr + 1));
   return (P + 31 * U) / 32 + 1;
 }
-// Upper bound on the experts with more than thr rows (one 8-row tile each when
-// they have at most 8).
-int64_t mfma_max_experts(const moeq_ffn_desc* d, int thr) {
+// Upper bound on the 8-row MFMA tiles: one per expert with more than thr rows
+// when only experts of at most 8 rows take them; otherwise (every expert,
+// n_e <= T rows) sum ceil(n_e / 8) <= U + (T*k - U) / 8 (each tile past an
+// expert's first takes 8 more rows) and <= U * ceil(T / 8).
+int64_t mfma_max_thin(const moeq_ffn_desc* d, int thr) {
   const int64_t P = d->T * d->k;
   if (d->T <= thr) return 0;
-  return std::min<int64_t>(d->E, P / (thr + 1));
+  const int64_t U = std::min<int64_t>(d->E, P / (thr + 1));
+  if (thin_max_of(d) == kThinT) return U;
+  return std::min<int64_t>(U + (P - U) / kThinT, U * ((d->T + kThinT - 1) / kThinT));
 }
-constexpr int kThinT = 8;   // rows of the MFMA tiles of experts with at most 8 rows
 
 struct FfnLayout {
   int64_t Fmax, nrows, max_tiles, max_thin;
@@ -95,7 +106,7 @@ FfnLayout ffn_layout(const moeq_ffn_desc* d) {
   L.Fmax = sh ? std::max(d->F, d->F_shared) : d->F;
   L.nrows = d->T * d->k + d->T;
   L.max_tiles = mfma_max_tiles(d, gemv_max_of(d));
-  L.max_thin = mfma_max_experts(d, gemv_max_of(d));
+  L.max_thin = mfma_max_thin(d, gemv_max_of(d));
   size_t o = 0;
   L.off_h = o;   o += align256((size_t)L.nrows * L.Fmax * sizeof(float));
   L.off_yp = o;  o += align256((size_t)L.nrows * d->H * sizeof(float));
@@ -107,6 +118,13 @@ FfnLayout ffn_layout(const moeq_ffn_desc* d) {
   L.off_count = o; o += 256;                     // [0]: 32-row tiles, [1]: 8-row tiles
   L.total = o;
   return L;
+}
+
+// The MFMA tile lists of the FFN workspace at wsb.
+MfmaPlan ffn_plan(const moeq_ffn_desc* d, const FfnLayout& L, uint8_t* wsb) {
+  int32_t* count = (int32_t*)(wsb + L.off_count);
+  return MfmaPlan{gemv_max_of(d), (int)L.max_tiles, (int4*)(wsb + L.off_tiles), count,
+                  (int4*)(wsb + L.off_thin), count + 1, thin_max_of(d)};
 }
 
 // The routed 8-row tiles take the fp32-h variant (see launch_mfma) when both
@@ -399,16 +417,14 @@ int ffn_enqueue(const moeq_ffn_desc* d, const void* x_q8K, const int32_t* topk_i
       // a small chunk: these tiles route inline (and write the routing
       // outputs and the 8-row tile list the down launch reads)
       const SmallRoute sr{ir->logits, d->E, ir->gating, ir->scale, ir->ids, ir->w, ir->offsets, ir->pairs,
-                          ir->active, MfmaPlan{thr, (int)L.max_tiles, tiles, tcount, thin_tiles, tcount + 1}};
+                          ir->active, ffn_plan(d, L, wsb)};
       return launch_mfma_route_gateup(fmt, dim3(gx, gy), a, sr, st);
     }
     return launch_mfma(fmt, mode, thin, hf, dim3(gx, gy), a, st);
   };
 
   if (mfma && !planned) {
-    if ((rc = launch_mfma_plan(active, expert_offsets, thr, (int)L.max_tiles, tiles, tcount, thin_tiles, tcount + 1,
-                               s)))
-      return rc;
+    if ((rc = launch_mfma_plan(active, expert_offsets, ffn_plan(d, L, wsb), s))) return rc;
   }
   // A shared expert that is not a slot of the routed launches (another shape
   // or format, or the MFMA path) runs its gate/up and down on the caller's
@@ -460,7 +476,7 @@ int ffn_enqueue(const moeq_ffn_desc* d, const void* x_q8K, const int32_t* topk_i
     }
   }
   if (mfma) {
-    if (d->T > kThinT && (rc = mfma_launch(0, false, false, s))) return rc;
+    if (L.max_tiles > 0 && (rc = mfma_launch(0, false, false, s))) return rc;
     if ((rc = mfma_launch(0, false, true, ts))) return rc;
   }
   if (ss == s && (rc = shared_gateup())) return rc;
@@ -482,7 +498,7 @@ int ffn_enqueue(const moeq_ffn_desc* d, const void* x_q8K, const int32_t* topk_i
     }
   }
   if (mfma) {
-    if (d->T > kThinT && (rc = mfma_launch(1, false, false, s))) return rc;
+    if (L.max_tiles > 0 && (rc = mfma_launch(1, false, false, s))) return rc;
     if ((rc = mfma_launch(1, false, true, ts))) return rc;
   }
   if (thin_apart && (rc = join_aux(d, s))) return rc;
@@ -583,9 +599,7 @@ int layer_enqueue(const moeq_route_desc* r, const moeq_ffn_desc* f, const float*
   const FfnLayout FL = ffn_layout(f);
   const int thr = gemv_max_of(f);
   const bool mfma = f->T > thr;
-  const MfmaPlan plan{thr, (int)FL.max_tiles, (int4*)(wsb + L.off_ffn + FL.off_tiles),
-                      (int32_t*)(wsb + L.off_ffn + FL.off_count), (int4*)(wsb + L.off_ffn + FL.off_thin),
-                      (int32_t*)(wsb + L.off_ffn + FL.off_count) + 1};
+  const MfmaPlan plan = ffn_plan(f, FL, wsb + L.off_ffn);
   if ((rc = launch_route(r->T, r->H, r->E, r->k, r->gating, r->scale, x, w_router, bias, logits, topk_ids, topk_w,
                          expert_offsets, pairs, active, xq, wsb + L.off_route, s, mfma ? &plan : nullptr)))
     return hip_status(rc);

@@ -1385,17 +1385,13 @@ int launch_mfma_ints(int fmt, const void* W, int64_t N, int64_t K, const void* x
 
 // Tile lists of the routed experts (one workgroup; see mfma_plan.hpp).
 __global__ __launch_bounds__(64) void k_mfma_plan(const int32_t* __restrict__ active,
-                                                    const int32_t* __restrict__ offsets, int thr, int max_tiles,
-                                                    int4* __restrict__ tiles, int32_t* __restrict__ count,
-                                                    int4* __restrict__ thin, int32_t* __restrict__ thin_count) {
+                                                    const int32_t* __restrict__ offsets, MfmaPlan p) {
   __shared__ int ebase[kPlanMaxE + 1];
-  mfma_plan_block(active, offsets, MfmaPlan{thr, max_tiles, tiles, count, thin, thin_count}, ebase);
+  mfma_plan_block(active, offsets, p, ebase);
 }
 
-int launch_mfma_plan(const int32_t* active, const int32_t* offsets, int thr, int max_tiles, int4* tiles,
-                     int32_t* count, int4* thin, int32_t* thin_count, hipStream_t s) {
-  hipLaunchKernelGGL(k_mfma_plan, dim3(1), dim3(64), 0, s, active, offsets, thr, max_tiles, tiles, count, thin,
-                     thin_count);
+int launch_mfma_plan(const int32_t* active, const int32_t* offsets, const MfmaPlan& p, hipStream_t s) {
+  hipLaunchKernelGGL(k_mfma_plan, dim3(1), dim3(64), 0, s, active, offsets, p);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 

@@ -96,13 +96,15 @@ struct DownArgs {
 // activation rows come from the plan (routed experts) or cover all T tokens
 // (shared expert).
 // Where and how the MFMA tile lists are built: experts with more than thr
-// rows, at most max_tiles 32-row tiles.
+// rows; those with at most thin_max rows take ceil(rows / 8) 8-row tiles,
+// the others 32-row tiles (at most max_tiles of them).
 struct MfmaPlan {
   int thr, max_tiles;
   int4* tiles;
   int32_t* count;
   int4* thin;
   int32_t* thin_count;
+  int thin_max;
 };
 
 struct MfmaArgs {
@@ -157,8 +159,7 @@ int launch_gateup(int fmt, int tt, int cpl, dim3 grid, const GateUpArgs& a, hipS
 int launch_gateup1(int fmt, int nper, int cpl, dim3 grid, const GateUpArgs& a, hipStream_t s);
 int launch_down(int fmt, int tt, int cpl, dim3 grid, const DownArgs& a, hipStream_t s);
 int launch_down_rows1(int fmt, int cpl, dim3 grid, const DownArgs& a, hipStream_t s);
-int launch_mfma_plan(const int32_t* active, const int32_t* offsets, int thr, int max_tiles, int4* tiles,
-                     int32_t* count, int4* thin, int32_t* thin_count, hipStream_t s);
+int launch_mfma_plan(const int32_t* active, const int32_t* offsets, const MfmaPlan& p, hipStream_t s);
 // hf: the fp32-h variant (8-row resident tiles of formats other than Q6_K;
 // mode 0 workgroups then cover kHfRows weight rows instead of 256).
 constexpr int kHfRows = 64;

@@ -7,7 +7,7 @@
 namespace moeq {
 
 constexpr int kTileT = 32;         // activation rows (tokens / pairs) per tile
-constexpr int kThinRows = 8;       // experts with at most this many rows get one 8-row tile
+constexpr int kThinRows = 8;       // rows of the tiles of experts with few rows
 
 // Inclusive prefix sum over the 64 lanes of a wave.
 __device__ __forceinline__ int wave_incl_scan(int v) {
@@ -21,8 +21,8 @@ __device__ __forceinline__ int wave_incl_scan(int v) {
 }
 
 // The counting half of mfma_plan_block, by wave 0: tile counts, the 8-row
-// tiles, each expert's first 32-row tile index in ebase (ebase[na] = total),
-// and the two counts.
+// tiles (ceil(rows / 8) per expert, consecutive), each expert's first 32-row
+// tile index in ebase (ebase[na] = total), and the two counts.
 __device__ __forceinline__ void plan_count(const int32_t* __restrict__ active, const int32_t* __restrict__ offsets,
                                            const MfmaPlan& p, int* ebase, int na) {
   const int lane = lane_id();
@@ -35,7 +35,7 @@ __device__ __forceinline__ void plan_count(const int32_t* __restrict__ active, c
       const int e = active[1 + s];
       const int ne = offsets[e + 1] - offsets[e];
       if (ne > p.thr) {
-        if (ne <= kThinRows) ++tlocal;
+        if (ne <= p.thin_max) tlocal += (ne + kThinRows - 1) / kThinRows;
         else local += (ne + kTileT - 1) / kTileT;
       }
     }
@@ -53,8 +53,9 @@ __device__ __forceinline__ void plan_count(const int32_t* __restrict__ active, c
       const int e = active[1 + s];
       const int ne = offsets[e + 1] - offsets[e];
       ebase[s] = base;
-      if (ne > p.thr && ne <= kThinRows) {
-        p.thin[tbase++] = make_int4(e, 0, ne, offsets[e]);
+      if (ne > p.thr && ne <= p.thin_max) {
+        for (int t0 = 0; t0 < ne; t0 += kThinRows)
+          p.thin[tbase++] = make_int4(e, t0, ne - t0 < kThinRows ? ne - t0 : kThinRows, offsets[e]);
       } else if (ne > p.thr) {
         base += (ne + kTileT - 1) / kTileT;
       }
@@ -63,7 +64,7 @@ __device__ __forceinline__ void plan_count(const int32_t* __restrict__ active, c
 }
 
 // Routed experts whose row count exceeds `thr`: experts with at most
-// kThinRows rows get one 8-row tile, the others 32-row tiles; a tile is
+// p.thin_max rows get 8-row tiles, the others 32-row tiles; a tile is
 // (expert, first row, rows, list offset), experts in union order (absent
 // experts too: their down tiles write zero rows).  Every thread of the
 // workgroup calls it (active / offsets may have been written by this

@@ -859,7 +859,7 @@ int launch_route(int64_t T, int64_t H, int64_t E, int k, int gating, float scale
                  const float* W, const float* bias, double* logits, int32_t* ids, float* w,
                  int32_t* offsets, int32_t* pairs, int32_t* active, void* xq, void* ws, hipStream_t s,
                  const MfmaPlan* plan) {
-  const MfmaPlan pl = plan != nullptr ? *plan : MfmaPlan{0, 0, nullptr, nullptr, nullptr, nullptr};
+  const MfmaPlan pl = plan != nullptr ? *plan : MfmaPlan{0, 0, nullptr, nullptr, nullptr, nullptr, kThinRows};
   if (T == 0) {
     hipLaunchKernelGGL(k_empty_lists, dim3(1), dim3(256), 0, s, E, offsets, active);
     return hipGetLastError() == hipSuccess ? 0 : -1;

@@ -849,7 +849,8 @@ def _custom_cfg(**kw):
                                      "many_tiles_spanning_lanes", "thin_hf_q80_q4k", "t1_36_blocks_q2k",
                                      "t1_42_blocks_shared_q6k", "q3k_q5k_mix", "t1_q5k_q3k_shared",
                                      "ragged_tiles_q5k_q3k", "thin_hf_q5k", "t1_full_q3k_q5k", "q40_q51_mix",
-                                     "t1_q51_q40_shared", "ragged_tiles_q40_q51", "thin_hf_q51", "t1_full_q40_q51"])
+                                     "t1_q51_q40_shared", "ragged_tiles_q40_q51", "thin_hf_q51", "t1_full_q40_q51",
+                                     "hot_t13_two_thin_tiles", "hot_t16_full_thin_tiles_q6k", "t16_e3_thin_only_q2k"])
 def test_edge_layers(variant, fused, path):
     say("edge", variant, fused, path)
     kw = {}
@@ -937,6 +938,18 @@ def test_edge_layers(variant, fused, path):
     elif variant == "t1_full_q40_q51":
         kw = dict(T=1, H=2048, E=256, k=8, F=512, fmt_gate=syn.Q4_0, fmt_up=syn.Q4_0, fmt_down=syn.Q5_1,
                   shared=True, F_shared=512, sh_fmt_gate=syn.Q5_1, sh_fmt_up=syn.Q5_1, sh_fmt_down=syn.Q4_0)
+    elif variant == "hot_t13_two_thin_tiles":
+        # 9..16 tokens take 8-row tiles only: the expert every token picks has
+        # 13 rows, two tiles (8 + 5 rows) of the fp32-h kernels
+        kw = dict(T=13, E=10, k=3, F=512, H=768, shared=True, F_shared=256, sh_fmt_gate=syn.Q8_0,
+                  sh_fmt_up=syn.Q8_0, sh_fmt_down=syn.Q4_K)
+    elif variant == "hot_t16_full_thin_tiles_q6k":
+        # 16 rows of one expert: two full 8-row tiles, Q6_K down (the q8_K(h) epilogue kernels)
+        kw = dict(T=16, E=6, k=2, F=512, H=512, fmt_down=syn.Q6_K, gating=syn.SIGMOID_TOPK)
+    elif variant == "t16_e3_thin_only_q2k":
+        # 32 pairs over 3 experts: every expert 9..16 rows, two 8-row tiles each, the second ragged
+        kw = dict(seed=772, T=16, E=3, k=2, F=768, H=512, fmt_gate=syn.Q2_K, fmt_up=syn.Q2_K, fmt_down=syn.Q4_K,
+                  shared=True, F_shared=512, sh_fmt_gate=syn.Q4_K, sh_fmt_up=syn.Q4_K, sh_fmt_down=syn.Q2_K)
     cfg = _custom_cfg(**kw)
     layer = syn.gen_layer(cfg)
     if variant == "t1_ties":
@@ -949,7 +962,7 @@ def test_edge_layers(variant, fused, path):
         layer.w_router[69] = x0 * 0.01
         layer.w_router[0] = x0 * 0.005
         layer.w_router[64] = x0 * 0.005
-    if variant == "one_expert_all_tokens":
+    if variant == "one_expert_all_tokens" or variant.startswith("hot_"):
         layer.w_router[3] = layer.x.mean(axis=0) * 10            # expert 3 wins for every token
     if variant == "ties":
         cfg = _custom_cfg(E=3, k=2, T=4)
@@ -960,8 +973,10 @@ def test_edge_layers(variant, fused, path):
     ids, w = check_route(run, layer, sel)
     if variant == "t1_ties":
         assert list(ids[0][:4]) == [3, 69, 0, 64]
-    if variant == "one_expert_all_tokens":
+    if variant == "one_expert_all_tokens" or variant.startswith("hot_"):
         assert np.all(ids[:, 0] == 3)
+    if variant == "t16_e3_thin_only_q2k":
+        assert np.all(np.bincount(ids.ravel(), minlength=3) > 8)
     if variant == "ties":
         for t in range(cfg.T):
             assert 2 not in ids[t] or 0 in ids[t]
