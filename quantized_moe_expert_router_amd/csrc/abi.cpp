@@ -277,11 +277,28 @@ int join_aux(const moeq_ffn_desc* d, hipStream_t s) {
   return 0;
 }
 
+// A shared expert that is not a slot of the routed launches (another shape
+// or format, or the MFMA path) runs on the caller's auxiliary stream, up to
+// kSideMaxT tokens, when one is given.
+bool shared_apart(const moeq_ffn_desc* d) {
+  const bool sh = d->sh_gate != nullptr;
+  const bool same_shape = sh && d->sh_fmt_gate == d->fmt_gate && d->sh_fmt_down == d->fmt_down &&
+                          d->F_shared == d->F;
+  const bool mfma = d->T > gemv_max_of(d);
+  return sh && (mfma || !same_shape) && d->T <= kSideMaxT && has_aux(d);
+}
+
+// What ffn_enqueue enqueues: everything (the shared expert forked at its
+// start when it runs apart), or, when the caller has recorded the fork event
+// on s earlier (before the selection), the shared expert's launches on the
+// auxiliary stream only, or everything else (joined before the combine).
+enum FfnPart { kFfnAll, kFfnSharedApart, kFfnRoutedWithForked };
+
 // Enqueue the expert FFN (everything after the routing) on `s`.
 int ffn_enqueue(const moeq_ffn_desc* d, const void* x_q8K, const int32_t* topk_ids, const float* topk_w,
                 const int32_t* expert_offsets, const int32_t* pairs, const int32_t* active,
                 const float* shared_scale, float* y, uint8_t* wsb, const InlineRoute* ir, bool planned,
-                hipStream_t s) {
+                hipStream_t s, FfnPart part = kFfnAll) {
   const FfnLayout L = ffn_layout(d);
   const bool sh = d->sh_gate != nullptr;
   const bool same_shape = sh && d->sh_fmt_gate == d->fmt_gate && d->sh_fmt_down == d->fmt_down &&
@@ -423,7 +440,7 @@ int ffn_enqueue(const moeq_ffn_desc* d, const void* x_q8K, const int32_t* topk_i
     return launch_mfma(fmt, mode, thin, hf, dim3(gx, gy), a, st);
   };
 
-  if (mfma && !planned) {
+  if (mfma && !planned && part != kFfnSharedApart) {
     if ((rc = launch_mfma_plan(active, expert_offsets, ffn_plan(d, L, wsb), s))) return rc;
   }
   // A shared expert that is not a slot of the routed launches (another shape
@@ -433,9 +450,11 @@ int ffn_enqueue(const moeq_ffn_desc* d, const void* x_q8K, const int32_t* topk_i
   // staged output rows.  Up to kSideMaxT tokens the routed launches leave
   // most of the chip idle; past it they fill it and the shared expert stays
   // on s.
-  const bool sh_apart = sh && (mfma || !same_shape) && d->T <= kSideMaxT && has_aux(d);
+  const bool sh_apart = shared_apart(d);
+  if (part != kFfnAll && !sh_apart) return -2;
   hipStream_t ss = s;
-  if (sh_apart && (rc = fork_aux(d, s, &ss))) return rc;
+  if (sh_apart && part == kFfnAll && (rc = fork_aux(d, s, &ss))) return rc;
+  if (part != kFfnAll) ss = (hipStream_t)d->aux_stream;
   // Past kSideMaxT tokens the shared expert stays on s; the 8-row tiles of the
   // experts with few rows then run on the auxiliary stream beside the 32-row
   // tiles (they read the lists and write only their own pairs' rows), joined
@@ -467,7 +486,13 @@ int ffn_enqueue(const moeq_ffn_desc* d, const void* x_q8K, const int32_t* topk_i
     return mfma ? mfma_launch(1, true, sh_thin, ss, fold_combine)
                 : down(kModeShared, d->sh_fmt_down, d->F_shared, 1, ss);
   };
-  if (ss != s && (rc = shared_gateup())) return rc;
+  if (part == kFfnSharedApart) {
+    // the auxiliary stream waits for the fork point the caller recorded
+    if (hipStreamWaitEvent(ss, (hipEvent_t)d->aux_fork, 0) != hipSuccess) return -1;
+    if ((rc = shared_gateup())) return rc;
+    return shared_down();
+  }
+  if (ss != s && part == kFfnAll && (rc = shared_gateup())) return rc;
   if (gemv) {
     if (same_shape) {
       if ((rc = gateup(kModeBoth, d->fmt_gate, d->F, n_routed_slots + 1, s))) return rc;
@@ -489,7 +514,7 @@ int ffn_enqueue(const moeq_ffn_desc* d, const void* x_q8K, const int32_t* topk_i
     dim3 grid((unsigned)((d->H + rows_wg - 1) / rows_wg));
     return launch_down_rows1(d->fmt_down, g.cpl, grid, a, s);
   }
-  if (ss != s && (rc = shared_down())) return rc;
+  if (ss != s && part == kFfnAll && (rc = shared_down())) return rc;
   if (gemv) {
     if (same_shape) {
       if ((rc = down(kModeBoth, d->fmt_down, d->F, max_union + 1, s))) return rc;
@@ -600,6 +625,24 @@ int layer_enqueue(const moeq_route_desc* r, const moeq_ffn_desc* f, const float*
   const int thr = gemv_max_of(f);
   const bool mfma = f->T > thr;
   const MfmaPlan plan = ffn_plan(f, FL, wsb + L.off_ffn);
+  if (shared_apart(f)) {
+    // A shared expert that runs apart needs only q8_K(x): it forks after the
+    // logits launch, not after the selection, so it starts earlier.  The
+    // selection is enqueued before the shared expert's launches, so that a
+    // captured graph keeps the routed chain on the queue of the launches
+    // before it (a chain that changes queue waits about 10 us at each change).
+    double* lg = logits ? logits : (double*)(wsb + L.off_route);
+    if ((rc = launch_logits(r->T, r->H, r->E, x, w_router, bias, lg, xq, s))) return hip_status(rc);
+    if (hipEventRecord((hipEvent_t)f->aux_fork, s) != hipSuccess) return MOEQ_E_HIP;
+    if ((rc = launch_route(r->T, r->H, r->E, r->k, r->gating, r->scale, x, w_router, bias, lg, topk_ids, topk_w,
+                           expert_offsets, pairs, active, xq, wsb + L.off_route, s, mfma ? &plan : nullptr, true)))
+      return hip_status(rc);
+    if ((rc = ffn_enqueue(f, xq, topk_ids, topk_w, expert_offsets, pairs, active, shared_scale, y, wsb, nullptr,
+                          mfma, s, kFfnSharedApart)))
+      return hip_status(rc);
+    return hip_status(ffn_enqueue(f, xq, topk_ids, topk_w, expert_offsets, pairs, active, shared_scale, y, wsb,
+                                  nullptr, mfma, s, kFfnRoutedWithForked));
+  }
   if ((rc = launch_route(r->T, r->H, r->E, r->k, r->gating, r->scale, x, w_router, bias, logits, topk_ids, topk_w,
                          expert_offsets, pairs, active, xq, wsb + L.off_route, s, mfma ? &plan : nullptr)))
     return hip_status(rc);

@@ -152,9 +152,12 @@ int launch_logits(int64_t T, int64_t H, int64_t E, const float* x, const float* 
 constexpr int64_t kNorm1MaxH = 4096;
 int launch_logits_norm1(int64_t H, int64_t E, const float* x, const float* g, double eps, const float* W,
                         const float* bias, double* logits, void* xq, hipStream_t s);
+// have_logits (at most 256 tokens, logits given): the logits and q8_K(x)
+// are already enqueued; only the selection and lists are.
 int launch_route(int64_t T, int64_t H, int64_t E, int k, int gating, float scale, const float* x,
                  const float* W, const float* bias, double* logits, int32_t* ids, float* w,
-                 int32_t* offsets, int32_t* pairs, int32_t* active, void* xq, void* ws, hipStream_t s, const MfmaPlan* plan = nullptr);
+                 int32_t* offsets, int32_t* pairs, int32_t* active, void* xq, void* ws, hipStream_t s,
+                 const MfmaPlan* plan = nullptr, bool have_logits = false);
 int launch_gateup(int fmt, int tt, int cpl, dim3 grid, const GateUpArgs& a, hipStream_t s);
 int launch_gateup1(int fmt, int nper, int cpl, dim3 grid, const GateUpArgs& a, hipStream_t s);
 int launch_down(int fmt, int tt, int cpl, dim3 grid, const DownArgs& a, hipStream_t s);

@@ -858,7 +858,7 @@ int lists_many(int64_t T, int k, int64_t E, const int32_t* ids, int32_t* offsets
 int launch_route(int64_t T, int64_t H, int64_t E, int k, int gating, float scale, const float* x,
                  const float* W, const float* bias, double* logits, int32_t* ids, float* w,
                  int32_t* offsets, int32_t* pairs, int32_t* active, void* xq, void* ws, hipStream_t s,
-                 const MfmaPlan* plan) {
+                 const MfmaPlan* plan, bool have_logits) {
   const MfmaPlan pl = plan != nullptr ? *plan : MfmaPlan{0, 0, nullptr, nullptr, nullptr, nullptr, kThinRows};
   if (T == 0) {
     hipLaunchKernelGGL(k_empty_lists, dim3(1), dim3(256), 0, s, E, offsets, active);
@@ -888,7 +888,10 @@ int launch_route(int64_t T, int64_t H, int64_t E, int k, int gating, float scale
     return lists_many(T, k, E, ids, offsets, pairs, active, wsb + RL.off_hist, s, pl);
   }
   double* lg = logits ? logits : reinterpret_cast<double*>(wsb);
-  if (int rc = launch_logits(T, H, E, x, W, bias, lg, xq, s)) return rc;
+  if (have_logits && (logits == nullptr || T > kSmallT)) return -2;
+  if (!have_logits) {
+    if (int rc = launch_logits(T, H, E, x, W, bias, lg, xq, s)) return rc;
+  }
   if (T <= kSmallT) {
     size_t lds = (size_t)(T * k + 2 * E + 2 * kSmallPairs + 3) * sizeof(int);   // either list path
     // up to 64 pairs: one wave per token and one for the lists, so fewer
