@@ -25,7 +25,9 @@
  *     path, up to 256 tokens) on the caller's auxiliary stream when the FFN
  *     descriptor names one (aux_stream with two events, all caller-owned),
  *     otherwise on `stream`.  The auxiliary stream is ordered after `stream`
- *     and joined back into `stream` by the two events before the call's last
+ *     (in moeq_moe_layer, when a selection launch runs, after the router
+ *     logits launch, so the shared expert runs beside the selection) and
+ *     joined back into `stream` by the two events before the call's last
  *     launch, so every effect of the call is still ordered on `stream`, in
  *     graph capture too.  Calls that may run concurrently need their own
  *     auxiliary stream and events.
