@@ -563,7 +563,8 @@ def test_one_token_general_down_partial_residency(fused):
     assert any(lo[e] for e in run.ids[0]) and not all(lo[e] for e in run.ids[0])
 
 
-@pytest.mark.parametrize("variant", ["t1_same_shared", "t1_other_shared", "t300_mfma_shared", "t300_no_logits"])
+@pytest.mark.parametrize("variant", ["t1_same_shared", "t1_other_shared", "t16_shared_forked_after_logits",
+                                     "t300_mfma_shared", "t300_no_logits"])
 def test_graph_replays_match_eager(variant):
     # the whole layer captured in a HIP graph and replayed several times, with
     # eager library work between the replays: every replay equals the eager
@@ -576,6 +577,12 @@ def test_graph_replays_match_eager(variant):
     elif variant == "t1_other_shared":
         cfg = _custom_cfg(T=1, E=12, k=4, F=256, H=512, shared=True, F_shared=512, sh_fmt_gate=syn.Q8_0,
                           sh_fmt_up=syn.Q8_0, sh_fmt_down=syn.Q6_K)
+    elif variant == "t16_shared_forked_after_logits":
+        # a selection launch and a shared expert on the auxiliary stream forked
+        # right after the logits launch (8-row tiles only)
+        cfg = _custom_cfg(T=16, E=24, k=4, F=512, H=512, fmt_gate=syn.Q2_K, fmt_up=syn.Q2_K, fmt_down=syn.Q4_K,
+                          gating=syn.SIGMOID_TOPK, shared=True, F_shared=512, sh_fmt_gate=syn.Q8_0,
+                          sh_fmt_up=syn.Q8_0, sh_fmt_down=syn.Q8_0)
     elif variant == "t300_mfma_shared":
         cfg = _custom_cfg(T=300, E=10, k=3, F=512, H=512, shared=True, F_shared=512, sh_fmt_gate=syn.Q4_K,
                           sh_fmt_up=syn.Q4_K, sh_fmt_down=syn.Q4_K)
@@ -623,22 +630,37 @@ def test_graph_replays_match_eager(variant):
         assert np.array_equal(y.cpu().numpy(), ref), (variant, rep, "eager")
 
 
-@pytest.mark.parametrize("variant", ["t1_other_shared", "chunk16_mfma"])
+@pytest.mark.parametrize("variant", ["t1_other_shared", "chunk16_mfma", "t100_mfma_32row_tiles_shared",
+                                     "t5_gemv_other_shared"])
 def test_aux_stream_and_single_stream_agree(variant):
     # a shared expert apart from the routed launches: on the caller's
     # auxiliary stream or on the call's own stream, the same kernels run in
-    # the same order per stream, so y and q8_K(h) are bit-identical
+    # the same order per stream, so y and q8_K(h) are bit-identical (in the
+    # whole-layer call with a selection launch, the shared expert forks right
+    # after the logits launch)
+    path = moeq.PATH_AUTO
     if variant == "t1_other_shared":
         layer = syn.gen_layer(_custom_cfg(T=1, E=12, k=4, F=256, H=512, shared=True, F_shared=512,
                                           sh_fmt_gate=syn.Q8_0, sh_fmt_up=syn.Q8_0, sh_fmt_down=syn.Q6_K))
+    elif variant == "t100_mfma_32row_tiles_shared":
+        # 100 tokens over 24 experts (5 to 12 rows each): 32-row and 8-row routed tiles beside the shared expert
+        layer = syn.gen_layer(_custom_cfg(T=100, E=24, k=2, F=512, H=512, shared=True, F_shared=256,
+                                          sh_fmt_gate=syn.Q8_0, sh_fmt_up=syn.Q8_0, sh_fmt_down=syn.Q4_K))
+    elif variant == "t5_gemv_other_shared":
+        layer = syn.gen_layer(_custom_cfg(T=5, E=9, k=3, F=512, H=512, shared=True, F_shared=256,
+                                          sh_fmt_gate=syn.Q6_K, sh_fmt_up=syn.Q6_K, sh_fmt_down=syn.Q8_0))
+        path = PATHS["gemv"]
     else:
         layer = layer_of("chunk16")
     say("aux vs single stream", variant)
     for fused in (False, True):
-        a = GpuRun(layer, fused=fused, aux=True)
-        b = GpuRun(layer, fused=fused, aux=False)
+        a = GpuRun(layer, fused=fused, aux=True, path=path)
+        b = GpuRun(layer, fused=fused, aux=False, path=path)
         assert np.array_equal(a.yv, b.yv), (variant, fused)
         assert np.array_equal(a.hq_r, b.hq_r) and np.array_equal(a.hq_s, b.hq_s), (variant, fused)
+        if variant != "chunk16_mfma":
+            r = oracle.expert_ffn(layer, a.ids, a.w, range(layer.cfg.T))
+            check_y(a.yv, r.y, variant)
 
 
 def check_residual(before, after, y_orc, what):
