@@ -277,6 +277,23 @@ int join_aux(const moeq_ffn_desc* d, hipStream_t s) {
   return 0;
 }
 
+// The shared expert's tiles take the fp32-h variant when both of its
+// launches can and its tiles are few (as routed_thin_hf).
+bool shared_thin_hf(const moeq_ffn_desc* d) {
+  const int64_t tiles = (d->T + kThinT - 1) / kThinT;
+  return !fmt_sub_scaled(d->sh_fmt_gate) && !fmt_sub_scaled(d->sh_fmt_down) && d->H / 256 <= kHfMaxBlocks &&
+         d->F_shared / 256 <= kHfMaxBlocks && tiles * (d->F_shared / 256) < kHfMaxWorkgroups;
+}
+
+// A chunk of 9 to 16 tokens on the MFMA path whose routed and shared tiles
+// are all fp32-h 8-row tiles: both go into the same gate/up and down
+// launches (launch_mfma_hf2), with no auxiliary stream.
+bool shared_in_routed_launches(const moeq_ffn_desc* d) {
+  if (d->sh_gate == nullptr || d->T <= kThinT || d->T > kAllThinT || gemv_max_of(d) != 0) return false;
+  return routed_thin_hf(d) && shared_thin_hf(d) && mfma_hf2_pair(d->fmt_gate, d->sh_fmt_gate) &&
+         mfma_hf2_pair(d->fmt_down, d->sh_fmt_down);
+}
+
 // A shared expert that is not a slot of the routed launches (another shape
 // or format, or the MFMA path) runs on the caller's auxiliary stream, up to
 // kSideMaxT tokens, when one is given.
@@ -285,7 +302,7 @@ bool shared_apart(const moeq_ffn_desc* d) {
   const bool same_shape = sh && d->sh_fmt_gate == d->fmt_gate && d->sh_fmt_down == d->fmt_down &&
                           d->F_shared == d->F;
   const bool mfma = d->T > gemv_max_of(d);
-  return sh && (mfma || !same_shape) && d->T <= kSideMaxT && has_aux(d);
+  return sh && (mfma || !same_shape) && d->T <= kSideMaxT && has_aux(d) && !shared_in_routed_launches(d);
 }
 
 // What ffn_enqueue enqueues: everything (the shared expert forked at its
@@ -379,14 +396,11 @@ int ffn_enqueue(const moeq_ffn_desc* d, const void* x_q8K, const int32_t* topk_i
   // when both of their launches can take it and the tiles are few (256-row
   // gate/up workgroups would not fill the chip; with many tiles the q8_K(h)
   // epilogue is faster)
-  auto hf_ok = [&](bool shared_exp) {
-    if (!shared_exp) return routed_thin_hf(d);
-    const int64_t tiles = (d->T + kThinT - 1) / kThinT;
-    return !fmt_sub_scaled(d->sh_fmt_gate) && !fmt_sub_scaled(d->sh_fmt_down) && d->H / 256 <= kHfMaxBlocks &&
-           d->F_shared / 256 <= kHfMaxBlocks && tiles * (d->F_shared / 256) < kHfMaxWorkgroups;
-  };
-  auto mfma_launch = [&](int mode, bool shared_exp, bool thin, hipStream_t st, bool fold = false) -> int {
-    const bool hf = thin && hf_ok(shared_exp);
+  auto hf_ok = [&](bool shared_exp) { return shared_exp ? shared_thin_hf(d) : routed_thin_hf(d); };
+  // The arguments and grid of one MFMA launch (fmt, hf and the grid returned).
+  auto mfma_prep = [&](int mode, bool shared_exp, bool thin, bool fold, int& fmt, bool& hf, unsigned& gx,
+                       unsigned& gy) -> MfmaArgs {
+    hf = thin && hf_ok(shared_exp);
     MfmaArgs a{};
     a.shared = shared_exp ? 1 : 0;
     a.tiles = thin ? thin_tiles : tiles;
@@ -401,13 +415,10 @@ int ffn_enqueue(const moeq_ffn_desc* d, const void* x_q8K, const int32_t* topk_i
     uint8_t* hq = shared_exp ? wsb + L.off_hqs : wsb + L.off_hq;
     a.hf = (float*)(wsb + L.off_h) + (shared_exp ? d->T * d->k * L.Fmax : 0);
     a.hf_stride = L.Fmax;
-    int fmt;
     const int tm = thin ? kThinT : 32;
     // routed 32-row tiles: a multiple of 8 workgroups at least as many as the
     // tiles (the kernels map workgroups to tiles XCD by XCD)
-    unsigned gx = shared_exp ? (unsigned)((d->T + tm - 1) / tm)
-                             : (unsigned)(thin ? L.max_thin : (L.max_tiles + 7) / 8 * 8);
-    unsigned gy;
+    gx = shared_exp ? (unsigned)((d->T + tm - 1) / tm) : (unsigned)(thin ? L.max_thin : (L.max_tiles + 7) / 8 * 8);
     a.gate = d->gate; a.up = d->up; a.down = d->down;
     if (mode == 0) {
       fmt = shared_exp ? d->sh_fmt_gate : d->fmt_gate;
@@ -430,6 +441,13 @@ int ffn_enqueue(const moeq_ffn_desc* d, const void* x_q8K, const int32_t* topk_i
     const int64_t nrb = gy;
     a.rb = std::max<int64_t>(1, std::min<int64_t>(nrb, (int64_t)gx * nrb / 2048));
     gy = (unsigned)((nrb + a.rb - 1) / a.rb);
+    return a;
+  };
+  auto mfma_launch = [&](int mode, bool shared_exp, bool thin, hipStream_t st, bool fold = false) -> int {
+    int fmt;
+    bool hf;
+    unsigned gx, gy;
+    const MfmaArgs a = mfma_prep(mode, shared_exp, thin, fold, fmt, hf, gx, gy);
     if (mode == 0 && thin && !shared_exp && small_ir) {
       // a small chunk: these tiles route inline (and write the routing
       // outputs and the 8-row tile list the down launch reads)
@@ -472,7 +490,8 @@ int ffn_enqueue(const moeq_ffn_desc* d, const void* x_q8K, const int32_t* topk_i
   // two of them give its gate/up and down several times the workgroups of one
   // 32-row tile (its weights are read once per tile), so it no longer trails
   // the routed launches, whose workgroups hold the CUs.
-  const bool sh_thin = d->T <= kThinT || (ss != s && d->T <= 2 * kThinT && hf_ok(true));
+  const bool dual = shared_in_routed_launches(d);
+  const bool sh_thin = d->T <= kThinT || ((ss != s || dual) && d->T <= 2 * kThinT && hf_ok(true));
   auto shared_gateup = [&]() -> int {
     if (!sh || (gemv && same_shape)) return 0;
     return mfma ? mfma_launch(0, true, sh_thin, ss) : gateup(kModeShared, d->sh_fmt_gate, d->F_shared, 1, ss);
@@ -486,6 +505,20 @@ int ffn_enqueue(const moeq_ffn_desc* d, const void* x_q8K, const int32_t* topk_i
     return mfma ? mfma_launch(1, true, sh_thin, ss, fold_combine)
                 : down(kModeShared, d->sh_fmt_down, d->F_shared, 1, ss);
   };
+  if (dual) {
+    // the routed and the shared expert's 8-row tiles in one gate/up and one
+    // down launch (the shared tiles first), then the combine
+    for (int mode = 0; mode < 2; ++mode) {
+      int fr, fs;
+      bool hr, hs;
+      unsigned gxr, gyr, gxs, gys;
+      const MfmaArgs ar = mfma_prep(mode, false, true, false, fr, hr, gxr, gyr);
+      const MfmaArgs as = mfma_prep(mode, true, true, false, fs, hs, gxs, gys);
+      if (!hr || !hs) return -2;
+      if ((rc = launch_mfma_hf2(mode, fr, fs, dim3(gxs + gxr, std::max(gyr, gys)), ar, as, (int)gxs, s))) return rc;
+    }
+    return launch_combine((const float*)(wsb + L.off_yp), d->T, d->H, d->k, 1, y, d->accumulate, s);
+  }
   if (part == kFfnSharedApart) {
     // the auxiliary stream waits for the fork point the caller recorded
     if (hipStreamWaitEvent(ss, (hipEvent_t)d->aux_fork, 0) != hipSuccess) return -1;

@@ -869,8 +869,18 @@ __device__ __forceinline__ void combine_block(const float* __restrict__ yp, int6
   }
 }
 
-// The tile of this workgroup: for the shared expert, tokens t0 .. t0+n-1 of
-// block row blockIdx.x; for routed experts, tile list entry j (expert e, rows
+// LDS of the tile code, one object per (type, tag) and kernel: it depends on
+// the tile's shape, not on the weight format, so a kernel that runs the tiles
+// of two formats (a workgroup takes one or the other) holds one copy.
+template <class T, int TAG>
+__device__ __forceinline__ T& lds_var() {
+  __shared__ __align__(16) T v;
+  return v;
+}
+
+// The tile of this workgroup (b: its tile index, blockIdx.x unless a kernel
+// runs two tile lists): for the shared expert, tokens t0 .. t0+n-1 of
+// block row b; for routed experts, tile list entry j (expert e, rows
 // t0 .. t0+n-1 of its list at list_off).  32-row tiles run in XCD-aware
 // order: workgroup b runs on XCD b % 8, and XCD x takes the x-th contiguous
 // eighth of the expert-ordered tile list, so the tiles of one expert run side
@@ -880,16 +890,16 @@ __device__ __forceinline__ void combine_block(const float* __restrict__ yp, int6
 // 0.89 GB (the algorithmic bytes).  8-row tiles have one tile per expert:
 // plain order.  False: no tile for this workgroup.
 template <int TM>
-__device__ __forceinline__ bool pick_tile(const MfmaArgs& a, int& e, int& t0, int& n, int64_t& list_off) {
+__device__ __forceinline__ bool pick_tile(const MfmaArgs& a, int b, int& e, int& t0, int& n, int64_t& list_off) {
   e = -1;
   list_off = 0;
   if (a.shared) {
-    t0 = (int)blockIdx.x * TM;
+    t0 = b * TM;
     if (t0 >= a.T) return false;
     n = (int)((a.T - t0) < TM ? (a.T - t0) : TM);
     return true;
   }
-  const int cnt = *a.count, b = (int)blockIdx.x;
+  const int cnt = *a.count;
   int j = b;
   if constexpr (TM == 32) {
     const int per = (cnt + 7) >> 3;
@@ -938,7 +948,7 @@ static_assert(kRes(8) == kHfMaxBlocks, "resident 8-row tiles");
 //   lane) and takes its tile and pair rows from that, not from the lists.
 template <int FMT, int MODE, bool RES, int TM, int RING, int NW = 8, bool HF = false, bool COMB = false,
           int RNPER = 0>
-__device__ __forceinline__ void mfma_tile(const MfmaArgs& a, const SmallRoute* rt = nullptr) {
+__device__ __forceinline__ void mfma_tile(const MfmaArgs& a, const SmallRoute* rt = nullptr, int tile_b = -1) {
   static_assert(RNPER == 0 || (MODE == 0 && HF && TM == kThinRows), "inline routing: fp32-h 8-row gate/up");
   static_assert(NW == 8 || (NW == 16 && MODE == 0 && RES && RING > 1) || (NW == 4 && MODE == 0 && HF),
                 "split waves: resident gate/up ring");
@@ -950,12 +960,12 @@ __device__ __forceinline__ void mfma_tile(const MfmaArgs& a, const SmallRoute* r
   constexpr int NT = 64 * NW;
   using M = Mf<FMT>;
   constexpr int NQ = TM / 8;
-  __shared__ StageLds<TM> L[RES ? kRes(TM) : 2];
-  __shared__ int64_t orow[TM];
-  __shared__ double owt[TM];
-  __shared__ const uint8_t* srows[TM];
-  __shared__ uint8_t* vrows[TM];                      // HF mode 1: q8_K(h) view rows (workgroup row 0 only)
-  __shared__ __align__(16) uint8_t zrow[kQsStride];   // A rows past the tile height read zeros
+  auto& L = lds_var<StageLds<TM>[RES ? kRes(TM) : 2], 0>();
+  auto& orow = lds_var<int64_t[TM], 1>();
+  auto& owt = lds_var<double[TM], 2>();
+  auto& srows = lds_var<const uint8_t* [TM], 3>();
+  auto& vrows = lds_var<uint8_t* [TM], 4>();            // HF mode 1: q8_K(h) view rows (workgroup row 0 only)
+  auto& zrow = lds_var<uint8_t[kQsStride], 5>();        // A rows past the tile height read zeros
 
   // ---- tile: expert (or the shared expert) and its rows t0 .. t0+n-1
   int e, t0 = 0, n;
@@ -967,7 +977,7 @@ __device__ __forceinline__ void mfma_tile(const MfmaArgs& a, const SmallRoute* r
     if (!route_small_tile<RNPER>(*rt, a.T, a.k, r_ids, r_key, r_act, r_pos, r_off, r_ebase, e, n, list_off)) return;
     rkey = r_key;
   } else {
-    if (!pick_tile<TM>(a, e, t0, n, list_off)) return;
+    if (!pick_tile<TM>(a, tile_b >= 0 ? tile_b : (int)blockIdx.x, e, t0, n, list_off)) return;
   }
   const int64_t nrb = a.N / RB;
   const int64_t rb0 = (int64_t)blockIdx.y * a.rb;
@@ -1113,7 +1123,7 @@ __device__ __forceinline__ void mfma_tile(const MfmaArgs& a, const SmallRoute* r
           if constexpr (MODE == 0 && HF) {
             // h = fl32(silu(g) u) straight to the fp32 h rows
             if constexpr (SPLIT) {
-              __shared__ double gxh[TM][RB];
+              auto& gxh = lds_var<double[TM][RB], 6>();
               if (wmat == 0) {
 #pragma unroll
                 for (int r = 0; r < 4 * NQ; ++r) gxh[out_row(r, g)][lrow] = acc0[r];
@@ -1135,9 +1145,9 @@ __device__ __forceinline__ void mfma_tile(const MfmaArgs& a, const SmallRoute* r
               }
             }
           } else if constexpr (MODE == 0) {
-            __shared__ float hs2[TM][kMfRows + 4];
+            auto& hs2 = lds_var<float[TM][kMfRows + 4], 7>();
             if constexpr (NW == 16) {
-              __shared__ double gx[TM][kMfRows];
+              auto& gx = lds_var<double[TM][kMfRows], 8>();
               if (wmat == 0) {
 #pragma unroll
                 for (int r = 0; r < 4 * NQ; ++r) gx[out_row(r, g)][lrow] = acc0[r];
@@ -1233,7 +1243,7 @@ __device__ __forceinline__ void mfma_tile(const MfmaArgs& a, const SmallRoute* r
 
     if constexpr (MODE == 0) {
       // h = fl32(silu(g) u) -> LDS, then q8_K per tile row over this row block
-      __shared__ float hs[TM][kMfRows + 4];
+      auto& hs = lds_var<float[TM][kMfRows + 4], 9>();
 #pragma unroll
       for (int r = 0; r < 4 * NQ; ++r) hs[out_row(r, g)][lrow] = (float)(silu64(acc0[r]) * acc1[r]);
       __syncthreads();
@@ -1299,6 +1309,23 @@ template <int FMT>
 __global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2, 8))) void k_mfma_hf_down(
     MfmaArgs a) {
   mfma_tile<FMT, 1, true, 8, 2, 8, true>(a);
+}
+// The routed 8-row fp32-h tiles and the shared expert's in one launch (a
+// chunk of 9 to 16 tokens, so no auxiliary stream and no fork or join):
+// workgroups blockIdx.x < nsh take shared tile blockIdx.x, the others routed
+// tile blockIdx.x - nsh; the two formats' tiles share one LDS layout.  The
+// shared tiles come first in every grid row, so they are dispatched first.
+template <int FR, int FS>
+__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(3, 8))) void
+k_mfma_hf_gateup2(MfmaArgs a, MfmaArgs sa, int nsh) {
+  if ((int)blockIdx.x < nsh) mfma_tile<FS, 0, true, 8, 2, 4, true>(sa, nullptr, (int)blockIdx.x);
+  else mfma_tile<FR, 0, true, 8, 2, 4, true>(a, nullptr, (int)blockIdx.x - nsh);
+}
+template <int FR, int FS>
+__global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2, 8))) void
+k_mfma_hf_down2(MfmaArgs a, MfmaArgs sa, int nsh) {
+  if ((int)blockIdx.x < nsh) mfma_tile<FS, 1, true, 8, 2, 8, true>(sa, nullptr, (int)blockIdx.x);
+  else mfma_tile<FR, 1, true, 8, 2, 8, true>(a, nullptr, (int)blockIdx.x - nsh);
 }
 // the same gate/up tiles of a small chunk, routing inline
 template <int FMT, int NPER>
@@ -1457,6 +1484,44 @@ int launch_mfma_route_gateup(int fmt, dim3 grid, const MfmaArgs& a, const SmallR
   }
 #undef MOEQ_RG_FMT
 #undef MOEQ_RG
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+// Format pairs of the two-list fp32-h kernels: a shared expert in Q8_0 or
+// in the routed experts' format.
+namespace {
+constexpr bool hf_fmt(int f) { return f == FQ4K || f == FQ2K || f == FQ80 || f == FQ5K || f == FQ40 || f == FQ51; }
+template <int FR, int FS>
+void launch_hf2_pair(int mode, dim3 grid, const MfmaArgs& a, const MfmaArgs& sa, int nsh, hipStream_t s) {
+  if (mode == 0) hipLaunchKernelGGL((k_mfma_hf_gateup2<FR, FS>), grid, dim3(256), 0, s, a, sa, nsh);
+  else hipLaunchKernelGGL((k_mfma_hf_down2<FR, FS>), grid, dim3(512), 0, s, a, sa, nsh);
+}
+template <int FR>
+int launch_hf2_fr(int mode, int fmt_s, dim3 grid, const MfmaArgs& a, const MfmaArgs& sa, int nsh, hipStream_t s) {
+  if (fmt_s == FQ80) launch_hf2_pair<FR, FQ80>(mode, grid, a, sa, nsh, s);
+  else if (fmt_s == FR) launch_hf2_pair<FR, FR>(mode, grid, a, sa, nsh, s);
+  else return -2;
+  return 0;
+}
+}  // namespace
+
+bool mfma_hf2_pair(int fmt_r, int fmt_s) { return hf_fmt(fmt_r) && (fmt_s == FQ80 || fmt_s == fmt_r); }
+
+int launch_mfma_hf2(int mode, int fmt_r, int fmt_s, dim3 grid, const MfmaArgs& a, const MfmaArgs& sa, int nsh,
+                    hipStream_t s) {
+  if (grid.x == 0 || grid.y == 0) return 0;
+  if (!mfma_hf2_pair(fmt_r, fmt_s) || !a.hf || !sa.hf || a.K / 256 > kRes(8) || sa.K / 256 > kRes(8)) return -2;
+  int rc;
+  switch (fmt_r) {
+    case FQ4K: rc = launch_hf2_fr<FQ4K>(mode, fmt_s, grid, a, sa, nsh, s); break;
+    case FQ2K: rc = launch_hf2_fr<FQ2K>(mode, fmt_s, grid, a, sa, nsh, s); break;
+    case FQ80: rc = launch_hf2_fr<FQ80>(mode, fmt_s, grid, a, sa, nsh, s); break;
+    case FQ5K: rc = launch_hf2_fr<FQ5K>(mode, fmt_s, grid, a, sa, nsh, s); break;
+    case FQ40: rc = launch_hf2_fr<FQ40>(mode, fmt_s, grid, a, sa, nsh, s); break;
+    case FQ51: rc = launch_hf2_fr<FQ51>(mode, fmt_s, grid, a, sa, nsh, s); break;
+    default: return -2;
+  }
+  if (rc) return rc;
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 

@@ -169,6 +169,12 @@ constexpr int kHfRows = 64;
 constexpr int kHfMaxBlocks = 16;   // K (256-blocks) up to which 8-row tiles keep their activations in LDS
 constexpr int64_t kHfMaxWorkgroups = 1024;   // fp32 h only while 256-row gate/up tiles x row blocks stay below this
 int launch_mfma(int fmt, int mode, bool thin, bool hf, dim3 grid, const MfmaArgs& a, hipStream_t s);
+// The routed 8-row fp32-h tiles (a) and the shared expert's (sa, nsh tiles)
+// in one launch (mode 0 gate/up, 1 down); grid.x = nsh + routed tiles.  -2
+// when the format pair has no such kernel (mfma_hf2_pair).
+bool mfma_hf2_pair(int fmt_r, int fmt_s);
+int launch_mfma_hf2(int mode, int fmt_r, int fmt_s, dim3 grid, const MfmaArgs& a, const MfmaArgs& sa, int nsh,
+                    hipStream_t s);
 // Formats whose MFMA tiles scale each sub-block's result in int32 (no fp32-h tiles).
 inline bool fmt_sub_scaled(int fmt) { return fmt == FQ6K || fmt == FQ3K; }
 int launch_combine(const float* yp, int64_t T, int64_t H, int k, int has_shared, float* y, int accumulate,

@@ -564,7 +564,7 @@ def test_one_token_general_down_partial_residency(fused):
 
 
 @pytest.mark.parametrize("variant", ["t1_same_shared", "t1_other_shared", "t16_shared_forked_after_logits",
-                                     "t300_mfma_shared", "t300_no_logits"])
+                                     "t13_shared_in_routed_launches", "t300_mfma_shared", "t300_no_logits"])
 def test_graph_replays_match_eager(variant):
     # the whole layer captured in a HIP graph and replayed several times, with
     # eager library work between the replays: every replay equals the eager
@@ -578,10 +578,16 @@ def test_graph_replays_match_eager(variant):
         cfg = _custom_cfg(T=1, E=12, k=4, F=256, H=512, shared=True, F_shared=512, sh_fmt_gate=syn.Q8_0,
                           sh_fmt_up=syn.Q8_0, sh_fmt_down=syn.Q6_K)
     elif variant == "t16_shared_forked_after_logits":
-        # a selection launch and a shared expert on the auxiliary stream forked
-        # right after the logits launch (8-row tiles only)
+        # a selection launch and a shared expert (Q6_K gate/up: no fp32-h
+        # tiles) on the auxiliary stream, forked right after the logits launch
         cfg = _custom_cfg(T=16, E=24, k=4, F=512, H=512, fmt_gate=syn.Q2_K, fmt_up=syn.Q2_K, fmt_down=syn.Q4_K,
-                          gating=syn.SIGMOID_TOPK, shared=True, F_shared=512, sh_fmt_gate=syn.Q8_0,
+                          gating=syn.SIGMOID_TOPK, shared=True, F_shared=512, sh_fmt_gate=syn.Q6_K,
+                          sh_fmt_up=syn.Q6_K, sh_fmt_down=syn.Q8_0)
+    elif variant == "t13_shared_in_routed_launches":
+        # 9 to 16 tokens, routed and shared 8-row fp32-h tiles in the same
+        # gate/up and down launches (no auxiliary stream used)
+        cfg = _custom_cfg(T=13, E=24, k=4, F=512, H=512, fmt_gate=syn.Q2_K, fmt_up=syn.Q2_K, fmt_down=syn.Q4_K,
+                          gating=syn.SIGMOID_TOPK, shared=True, F_shared=768, sh_fmt_gate=syn.Q8_0,
                           sh_fmt_up=syn.Q8_0, sh_fmt_down=syn.Q8_0)
     elif variant == "t300_mfma_shared":
         cfg = _custom_cfg(T=300, E=10, k=3, F=512, H=512, shared=True, F_shared=512, sh_fmt_gate=syn.Q4_K,
@@ -630,8 +636,8 @@ def test_graph_replays_match_eager(variant):
         assert np.array_equal(y.cpu().numpy(), ref), (variant, rep, "eager")
 
 
-@pytest.mark.parametrize("variant", ["t1_other_shared", "chunk16_mfma", "t100_mfma_32row_tiles_shared",
-                                     "t5_gemv_other_shared"])
+@pytest.mark.parametrize("variant", ["t1_other_shared", "chunk16_mfma", "t16_shared_q6k_apart",
+                                     "t100_mfma_32row_tiles_shared", "t5_gemv_other_shared"])
 def test_aux_stream_and_single_stream_agree(variant):
     # a shared expert apart from the routed launches: on the caller's
     # auxiliary stream or on the call's own stream, the same kernels run in
@@ -646,6 +652,12 @@ def test_aux_stream_and_single_stream_agree(variant):
         # 100 tokens over 24 experts (5 to 12 rows each): 32-row and 8-row routed tiles beside the shared expert
         layer = syn.gen_layer(_custom_cfg(T=100, E=24, k=2, F=512, H=512, shared=True, F_shared=256,
                                           sh_fmt_gate=syn.Q8_0, sh_fmt_up=syn.Q8_0, sh_fmt_down=syn.Q4_K))
+    elif variant == "t16_shared_q6k_apart":
+        # 16 tokens whose shared expert has no fp32-h tiles (Q6_K gate/up): on
+        # the auxiliary stream, not in the routed launches
+        layer = syn.gen_layer(_custom_cfg(T=16, E=24, k=4, F=512, H=512, fmt_gate=syn.Q2_K, fmt_up=syn.Q2_K,
+                                          fmt_down=syn.Q4_K, shared=True, F_shared=512, sh_fmt_gate=syn.Q6_K,
+                                          sh_fmt_up=syn.Q6_K, sh_fmt_down=syn.Q8_0))
     elif variant == "t5_gemv_other_shared":
         layer = syn.gen_layer(_custom_cfg(T=5, E=9, k=3, F=512, H=512, shared=True, F_shared=256,
                                           sh_fmt_gate=syn.Q6_K, sh_fmt_up=syn.Q6_K, sh_fmt_down=syn.Q8_0))
@@ -872,7 +884,8 @@ def _custom_cfg(**kw):
                                      "t1_42_blocks_shared_q6k", "q3k_q5k_mix", "t1_q5k_q3k_shared",
                                      "ragged_tiles_q5k_q3k", "thin_hf_q5k", "t1_full_q3k_q5k", "q40_q51_mix",
                                      "t1_q51_q40_shared", "ragged_tiles_q40_q51", "thin_hf_q51", "t1_full_q40_q51",
-                                     "hot_t13_two_thin_tiles", "hot_t16_full_thin_tiles_q6k", "t16_e3_thin_only_q2k"])
+                                     "hot_t13_two_thin_tiles", "hot_t16_full_thin_tiles_q6k", "t16_e3_thin_only_q2k",
+                                     "t10_q5k_shared_q5k_one_launch", "t12_q40_q51_shared_q80_one_launch"])
 def test_edge_layers(variant, fused, path):
     say("edge", variant, fused, path)
     kw = {}
@@ -972,6 +985,13 @@ def test_edge_layers(variant, fused, path):
         # 32 pairs over 3 experts: every expert 9..16 rows, two 8-row tiles each, the second ragged
         kw = dict(seed=772, T=16, E=3, k=2, F=768, H=512, fmt_gate=syn.Q2_K, fmt_up=syn.Q2_K, fmt_down=syn.Q4_K,
                   shared=True, F_shared=512, sh_fmt_gate=syn.Q4_K, sh_fmt_up=syn.Q4_K, sh_fmt_down=syn.Q2_K)
+    elif variant == "t10_q5k_shared_q5k_one_launch":
+        # 9 to 16 tokens: routed and shared fp32-h 8-row tiles in the same launches (one format)
+        kw = dict(T=10, E=7, k=3, F=512, H=768, fmt_gate=syn.Q5_K, fmt_up=syn.Q5_K, fmt_down=syn.Q5_K,
+                  shared=True, F_shared=256, sh_fmt_gate=syn.Q5_K, sh_fmt_up=syn.Q5_K, sh_fmt_down=syn.Q5_K)
+    elif variant == "t12_q40_q51_shared_q80_one_launch":
+        kw = dict(T=12, E=9, k=2, F=768, H=512, fmt_gate=syn.Q4_0, fmt_up=syn.Q4_0, fmt_down=syn.Q5_1,
+                  shared=True, F_shared=512, sh_fmt_gate=syn.Q8_0, sh_fmt_up=syn.Q8_0, sh_fmt_down=syn.Q8_0)
     cfg = _custom_cfg(**kw)
     layer = syn.gen_layer(cfg)
     if variant == "t1_ties":
