@@ -285,11 +285,12 @@ bool shared_thin_hf(const moeq_ffn_desc* d) {
          d->F_shared / 256 <= kHfMaxBlocks && tiles * (d->F_shared / 256) < kHfMaxWorkgroups;
 }
 
-// A chunk of 9 to 16 tokens on the MFMA path whose routed and shared tiles
+// A chunk of 2 to 16 tokens on the MFMA path whose routed and shared tiles
 // are all fp32-h 8-row tiles: both go into the same gate/up and down
-// launches (launch_mfma_hf2), with no auxiliary stream.
+// launches (launch_mfma_hf2, or launch_mfma_route_gateup2 when the chunk
+// routes inline), with no auxiliary stream.
 bool shared_in_routed_launches(const moeq_ffn_desc* d) {
-  if (d->sh_gate == nullptr || d->T <= kThinT || d->T > kAllThinT || gemv_max_of(d) != 0) return false;
+  if (d->sh_gate == nullptr || d->T < 2 || d->T > kAllThinT || gemv_max_of(d) != 0) return false;
   return routed_thin_hf(d) && shared_thin_hf(d) && mfma_hf2_pair(d->fmt_gate, d->sh_fmt_gate) &&
          mfma_hf2_pair(d->fmt_down, d->sh_fmt_down);
 }
@@ -515,7 +516,15 @@ int ffn_enqueue(const moeq_ffn_desc* d, const void* x_q8K, const int32_t* topk_i
       const MfmaArgs ar = mfma_prep(mode, false, true, false, fr, hr, gxr, gyr);
       const MfmaArgs as = mfma_prep(mode, true, true, false, fs, hs, gxs, gys);
       if (!hr || !hs) return -2;
-      if ((rc = launch_mfma_hf2(mode, fr, fs, dim3(gxs + gxr, std::max(gyr, gys)), ar, as, (int)gxs, s))) return rc;
+      const dim3 grid(gxs + gxr, std::max(gyr, gys));
+      if (mode == 0 && small_ir) {
+        // the routed tiles route inline (as in mfma_launch)
+        const SmallRoute sr{ir->logits, d->E, ir->gating, ir->scale, ir->ids, ir->w, ir->offsets, ir->pairs,
+                            ir->active, ffn_plan(d, L, wsb)};
+        if ((rc = launch_mfma_route_gateup2(fr, fs, grid, ar, as, sr, (int)gxs, s))) return rc;
+      } else if ((rc = launch_mfma_hf2(mode, fr, fs, grid, ar, as, (int)gxs, s))) {
+        return rc;
+      }
     }
     return launch_combine((const float*)(wsb + L.off_yp), d->T, d->H, d->k, 1, y, d->accumulate, s);
   }

@@ -974,7 +974,9 @@ __device__ __forceinline__ void mfma_tile(const MfmaArgs& a, const SmallRoute* r
   if constexpr (RNPER > 0) {
     __shared__ int r_ids[kSmallPairs], r_key[kSmallPairs], r_act[kSmallPairs + 1], r_pos[kSmallPairs + 1];
     __shared__ int r_ebase[kSmallPairs + 1], r_off[kSmallRouteMaxE + 1];
-    if (!route_small_tile<RNPER>(*rt, a.T, a.k, r_ids, r_key, r_act, r_pos, r_off, r_ebase, e, n, list_off)) return;
+    if (!route_small_tile<RNPER>(*rt, a.T, a.k, r_ids, r_key, r_act, r_pos, r_off, r_ebase,
+                                 tile_b >= 0 ? tile_b : (int)blockIdx.x, e, n, list_off))
+      return;
     rkey = r_key;
   } else {
     if (!pick_tile<TM>(a, tile_b >= 0 ? tile_b : (int)blockIdx.x, e, t0, n, list_off)) return;
@@ -1333,6 +1335,13 @@ __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_pe
 k_mfma_hf_gateup_route(MfmaArgs a, SmallRoute r) {
   mfma_tile<FMT, 0, true, 8, 2, 4, true, false, NPER>(a, &r);
 }
+// and with the shared expert's tiles in the same launch (as k_mfma_hf_gateup2)
+template <int FR, int FS, int NPER>
+__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(3, 8))) void
+k_mfma_hf_gateup_route2(MfmaArgs a, MfmaArgs sa, SmallRoute r, int nsh) {
+  if ((int)blockIdx.x < nsh) mfma_tile<FS, 0, true, 8, 2, 4, true>(sa, nullptr, (int)blockIdx.x);
+  else mfma_tile<FR, 0, true, 8, 2, 4, true, false, NPER>(a, &r, (int)blockIdx.x - nsh);
+}
 
 // ------------------------------------------------------------ integer hook
 //
@@ -1506,6 +1515,43 @@ int launch_hf2_fr(int mode, int fmt_s, dim3 grid, const MfmaArgs& a, const MfmaA
 }  // namespace
 
 bool mfma_hf2_pair(int fmt_r, int fmt_s) { return hf_fmt(fmt_r) && (fmt_s == FQ80 || fmt_s == fmt_r); }
+
+namespace {
+template <int FR, int FS>
+void launch_route2_pair(dim3 grid, const MfmaArgs& a, const MfmaArgs& sa, const SmallRoute& r, int nsh,
+                        hipStream_t s) {
+  if (r.E <= 256) hipLaunchKernelGGL((k_mfma_hf_gateup_route2<FR, FS, 4>), grid, dim3(256), 0, s, a, sa, r, nsh);
+  else hipLaunchKernelGGL((k_mfma_hf_gateup_route2<FR, FS, 8>), grid, dim3(256), 0, s, a, sa, r, nsh);
+}
+template <int FR>
+int launch_route2_fr(int fmt_s, dim3 grid, const MfmaArgs& a, const MfmaArgs& sa, const SmallRoute& r, int nsh,
+                     hipStream_t s) {
+  if (fmt_s == FQ80) launch_route2_pair<FR, FQ80>(grid, a, sa, r, nsh, s);
+  else if (fmt_s == FR) launch_route2_pair<FR, FR>(grid, a, sa, r, nsh, s);
+  else return -2;
+  return 0;
+}
+}  // namespace
+
+int launch_mfma_route_gateup2(int fmt_r, int fmt_s, dim3 grid, const MfmaArgs& a, const MfmaArgs& sa,
+                              const SmallRoute& r, int nsh, hipStream_t s) {
+  if (grid.x == 0 || grid.y == 0) return 0;
+  if (a.T < 2 || a.T > kSmallRouteMaxT || a.T * a.k > kSmallPairs || r.E > kSmallRouteMaxE) return -2;
+  if (!mfma_hf2_pair(fmt_r, fmt_s) || !a.hf || !sa.hf || a.shared || !sa.shared) return -2;
+  if (a.K / 256 > kRes(8) || sa.K / 256 > kRes(8)) return -2;
+  int rc;
+  switch (fmt_r) {
+    case FQ4K: rc = launch_route2_fr<FQ4K>(fmt_s, grid, a, sa, r, nsh, s); break;
+    case FQ2K: rc = launch_route2_fr<FQ2K>(fmt_s, grid, a, sa, r, nsh, s); break;
+    case FQ80: rc = launch_route2_fr<FQ80>(fmt_s, grid, a, sa, r, nsh, s); break;
+    case FQ5K: rc = launch_route2_fr<FQ5K>(fmt_s, grid, a, sa, r, nsh, s); break;
+    case FQ40: rc = launch_route2_fr<FQ40>(fmt_s, grid, a, sa, r, nsh, s); break;
+    case FQ51: rc = launch_route2_fr<FQ51>(fmt_s, grid, a, sa, r, nsh, s); break;
+    default: return -2;
+  }
+  if (rc) return rc;
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
 
 int launch_mfma_hf2(int mode, int fmt_r, int fmt_s, dim3 grid, const MfmaArgs& a, const MfmaArgs& sa, int nsh,
                     hipStream_t s) {

@@ -92,6 +92,10 @@ struct SmallRoute {
   MfmaPlan plan;          // the 8-row tile list the down launch reads, written by the same workgroup
 };
 int launch_mfma_route_gateup(int fmt, dim3 grid, const MfmaArgs& a, const SmallRoute& r, hipStream_t s);
+// The same with the shared expert's nsh fp32-h tiles (sa) in the first
+// workgroups of every grid row (format pairs as mfma_hf2_pair).
+int launch_mfma_route_gateup2(int fmt_r, int fmt_s, dim3 grid, const MfmaArgs& a, const MfmaArgs& sa,
+                              const SmallRoute& r, int nsh, hipStream_t s);
 
 // The routing of a small chunk by one workgroup (every thread calls it; the
 // LDS arrays hold kSmallPairs, kSmallPairs, kSmallPairs + 1, kSmallPairs + 1,
@@ -99,14 +103,16 @@ int launch_mfma_route_gateup(int fmt, dim3 grid, const MfmaArgs& a, const SmallR
 // ... and selects their experts from the logits; then the sorted pairs and
 // the union in LDS.  Workgroup (0, 0) also forms the offsets of every expert
 // and writes the ids, gate weights, lists and the MFMA tile lists to memory.
-// The workgroup's tile is union entry blockIdx.x: its expert e, rows n and
-// list offset; false when the union has no such entry.
+// The workgroup's tile is union entry j (blockIdx.x unless the launch also
+// holds other tiles; the writer is the workgroup of entry 0 in grid row 0):
+// its expert e, rows n and list offset; false when the union has no such
+// entry.
 template <int NPER>
 __device__ __forceinline__ bool route_small_tile(const SmallRoute& r, int64_t T, int k, int* ids_s, int* skey,
-                                                 int* lact, int* lpos, int* loff, int* ebase, int& e, int& n,
+                                                 int* lact, int* lpos, int* loff, int* ebase, int j, int& e, int& n,
                                                  int64_t& list_off) {
   const int lane = lane_id(), wv = threadIdx.x >> 6, nw = blockDim.x >> 6;
-  const bool writer = blockIdx.x == 0 && blockIdx.y == 0;
+  const bool writer = j == 0 && blockIdx.y == 0;
   for (int64_t t = wv; t < T; t += nw) {
     int my_i;
     float my_w;
@@ -124,7 +130,7 @@ __device__ __forceinline__ bool route_small_tile(const SmallRoute& r, int64_t T,
               writer ? r.active : nullptr, skey, writer ? loff : nullptr, lact, lpos);
   __syncthreads();
   if (writer) mfma_plan_block(lact, loff, r.plan, ebase);
-  const int na = lact[0], j = (int)blockIdx.x;
+  const int na = lact[0];
   if (j >= na) return false;
   e = lact[1 + j];
   list_off = lpos[j];

@@ -1034,7 +1034,8 @@ def test_edge_layers(variant, fused, path):
 
 
 @pytest.mark.parametrize("variant", ["t2_e16_sigmoid_shared", "t8_k8_e512_q4k", "t4_e300_q5k_q40", "t5_k7_e7_q51",
-                                     "t3_softmax_all_e100_q80_q2k", "t4_ties_across_lanes_and_slots"])
+                                     "t3_softmax_all_e100_q80_q2k", "t4_ties_across_lanes_and_slots",
+                                     "t4_e300_q5k_shared_q5k", "t6_q51_shared_q40_apart"])
 def test_small_chunk_inline_route_matches_calls(variant):
     """A chunk of 2..8 tokens with at most 64 (token, slot) pairs and at most
     512 experts, on fp32-h 8-row tiles, routes inline in its first gate/up
@@ -1051,7 +1052,15 @@ def test_small_chunk_inline_route_matches_calls(variant):
               t5_k7_e7_q51=dict(T=5, E=7, k=7, fmt_gate=syn.Q5_1, fmt_up=syn.Q5_1, fmt_down=syn.Q5_1),
               t3_softmax_all_e100_q80_q2k=dict(T=3, E=100, k=4, gating=syn.SOFTMAX_ALL, F=512, fmt_gate=syn.Q8_0,
                                                fmt_up=syn.Q8_0, fmt_down=syn.Q2_K),
-              t4_ties_across_lanes_and_slots=dict(T=4, E=130, k=5))[variant]
+              t4_ties_across_lanes_and_slots=dict(T=4, E=130, k=5),
+              # the shared expert's tiles in the routing gate/up launch (top-k with 8 logits per lane)
+              t4_e300_q5k_shared_q5k=dict(T=4, E=300, k=6, H=768, F=512, fmt_gate=syn.Q5_K, fmt_up=syn.Q5_K,
+                                          fmt_down=syn.Q5_K, shared=True, F_shared=512, sh_fmt_gate=syn.Q5_K,
+                                          sh_fmt_up=syn.Q5_K, sh_fmt_down=syn.Q5_K),
+              # a shared format pair with no two-format kernel: the shared expert on the auxiliary stream
+              t6_q51_shared_q40_apart=dict(T=6, E=20, k=4, fmt_gate=syn.Q5_1, fmt_up=syn.Q5_1, fmt_down=syn.Q5_1,
+                                           shared=True, F_shared=256, sh_fmt_gate=syn.Q4_0, sh_fmt_up=syn.Q4_0,
+                                           sh_fmt_down=syn.Q5_1))[variant]
     cfg = _custom_cfg(**kw)
     layer = syn.gen_layer(cfg)
     if variant == "t4_ties_across_lanes_and_slots":
