@@ -472,7 +472,18 @@ int ffn_enqueue(const moeq_ffn_desc* d, const void* x_q8K, const int32_t* topk_i
   const bool sh_apart = shared_apart(d);
   if (part != kFfnAll && !sh_apart) return -2;
   hipStream_t ss = s;
-  if (sh_apart && part == kFfnAll && (rc = fork_aux(d, s, &ss))) return rc;
+  // One token: the routed gate/up (a few hundred workgroups, the chip is not
+  // full) is captured before the shared expert's launches, so that a
+  // captured graph keeps it on the queue of the launch before it; the fork
+  // event is recorded first, so the shared expert still waits for nothing
+  // more than before.
+  const bool routed_first = sh_apart && one && part == kFfnAll;
+  if (routed_first) {
+    if (hipEventRecord((hipEvent_t)d->aux_fork, s) != hipSuccess) return -1;
+    ss = (hipStream_t)d->aux_stream;
+  } else if (sh_apart && part == kFfnAll && (rc = fork_aux(d, s, &ss))) {
+    return rc;
+  }
   if (part != kFfnAll) ss = (hipStream_t)d->aux_stream;
   // Past kSideMaxT tokens the shared expert stays on s; the 8-row tiles of the
   // experts with few rows then run on the auxiliary stream beside the 32-row
@@ -534,13 +545,17 @@ int ffn_enqueue(const moeq_ffn_desc* d, const void* x_q8K, const int32_t* topk_i
     if ((rc = shared_gateup())) return rc;
     return shared_down();
   }
-  if (ss != s && part == kFfnAll && (rc = shared_gateup())) return rc;
+  if (ss != s && part == kFfnAll && !routed_first && (rc = shared_gateup())) return rc;
   if (gemv) {
     if (same_shape) {
       if ((rc = gateup(kModeBoth, d->fmt_gate, d->F, n_routed_slots + 1, s))) return rc;
     } else {
       if ((rc = gateup(kModeRouted, d->fmt_gate, d->F, n_routed_slots, s))) return rc;
     }
+  }
+  if (routed_first) {
+    if (hipStreamWaitEvent(ss, (hipEvent_t)d->aux_fork, 0) != hipSuccess) return -1;
+    if ((rc = shared_gateup())) return rc;
   }
   if (mfma) {
     if (L.max_tiles > 0 && (rc = mfma_launch(0, false, false, s))) return rc;
