@@ -886,7 +886,8 @@ def _custom_cfg(**kw):
                                      "ragged_tiles_q5k_q3k", "thin_hf_q5k", "t1_full_q3k_q5k", "q40_q51_mix",
                                      "t1_q51_q40_shared", "ragged_tiles_q40_q51", "thin_hf_q51", "t1_full_q40_q51",
                                      "hot_t13_two_thin_tiles", "hot_t16_full_thin_tiles_q6k", "t16_e3_thin_only_q2k",
-                                     "t10_q5k_shared_q5k_one_launch", "t12_q40_q51_shared_q80_one_launch"])
+                                     "t10_q5k_shared_q5k_one_launch", "t12_q40_q51_shared_q80_one_launch",
+                                     "t16_k8_128_pairs", "t32_k4_128_pairs_32row_tiles"])
 def test_edge_layers(variant, fused, path):
     say("edge", variant, fused, path)
     kw = {}
@@ -990,6 +991,13 @@ def test_edge_layers(variant, fused, path):
         # 9 to 16 tokens: routed and shared fp32-h 8-row tiles in the same launches (one format)
         kw = dict(T=10, E=7, k=3, F=512, H=768, fmt_gate=syn.Q5_K, fmt_up=syn.Q5_K, fmt_down=syn.Q5_K,
                   shared=True, F_shared=256, sh_fmt_gate=syn.Q5_K, sh_fmt_up=syn.Q5_K, sh_fmt_down=syn.Q5_K)
+    elif variant == "t16_k8_128_pairs":
+        # 128 (token, slot) pairs: the selection's block-wide counting sort, the shared expert in the routed launches
+        kw = dict(T=16, E=30, k=8, F=512, H=512, shared=True, F_shared=256, sh_fmt_gate=syn.Q8_0,
+                  sh_fmt_up=syn.Q8_0, sh_fmt_down=syn.Q8_0)
+    elif variant == "t32_k4_128_pairs_32row_tiles":
+        # 128 pairs over 32 tokens (the selection waves take two tokens each), 32-row tiles
+        kw = dict(T=32, E=6, k=4, F=512, H=512)
     elif variant == "t12_q40_q51_shared_q80_one_launch":
         kw = dict(T=12, E=9, k=2, F=768, H=512, fmt_gate=syn.Q4_0, fmt_up=syn.Q4_0, fmt_down=syn.Q5_1,
                   shared=True, F_shared=512, sh_fmt_gate=syn.Q8_0, sh_fmt_up=syn.Q8_0, sh_fmt_down=syn.Q8_0)
