@@ -565,7 +565,8 @@ def test_one_token_general_down_partial_residency(fused):
 
 
 @pytest.mark.parametrize("variant", ["t1_same_shared", "t1_other_shared", "t16_shared_forked_after_logits",
-                                     "t13_shared_in_routed_launches", "t300_mfma_shared", "t300_no_logits"])
+                                     "t13_shared_in_routed_launches", "t4_shared_inline_route_one_launch",
+                                     "t300_mfma_shared", "t300_no_logits"])
 def test_graph_replays_match_eager(variant):
     # the whole layer captured in a HIP graph and replayed several times, with
     # eager library work between the replays: every replay equals the eager
@@ -590,6 +591,10 @@ def test_graph_replays_match_eager(variant):
         cfg = _custom_cfg(T=13, E=24, k=4, F=512, H=512, fmt_gate=syn.Q2_K, fmt_up=syn.Q2_K, fmt_down=syn.Q4_K,
                           gating=syn.SIGMOID_TOPK, shared=True, F_shared=768, sh_fmt_gate=syn.Q8_0,
                           sh_fmt_up=syn.Q8_0, sh_fmt_down=syn.Q8_0)
+    elif variant == "t4_shared_inline_route_one_launch":
+        # 2 to 8 tokens: the routed tiles route inline and the shared tiles share their launches
+        cfg = _custom_cfg(T=4, E=40, k=6, F=512, H=1024, fmt_gate=syn.Q2_K, fmt_up=syn.Q2_K, fmt_down=syn.Q4_K,
+                          shared=True, F_shared=512, sh_fmt_gate=syn.Q8_0, sh_fmt_up=syn.Q8_0, sh_fmt_down=syn.Q8_0)
     elif variant == "t300_mfma_shared":
         cfg = _custom_cfg(T=300, E=10, k=3, F=512, H=512, shared=True, F_shared=512, sh_fmt_gate=syn.Q4_K,
                           sh_fmt_up=syn.Q4_K, sh_fmt_down=syn.Q4_K)
