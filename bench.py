@@ -516,7 +516,7 @@ def main():
         summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], args.calib_copy_mib or 256)
         return
     if args.gpus != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path (run with --gpus 1)",
+        print("bench.py measures one GPU only: the library has no multi-GPU path (run with --gpus 1)",
               file=sys.stderr)
         sys.exit(2)
     import torch
