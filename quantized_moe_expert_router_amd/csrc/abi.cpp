@@ -662,7 +662,7 @@ int layer_enqueue(const moeq_route_desc* r, const moeq_ffn_desc* f, const float*
     // one token: logits + q8_K(x) in one launch, then gate/up routes inline
     double* lg = logits ? logits : (double*)(wsb + L.off_route);
     rc = nrm ? launch_logits_norm1(r->H, r->E, x, nrm->g, nrm->eps, w_router, bias, lg, xq, s)
-             : launch_logits(1, r->H, r->E, x, w_router, bias, lg, xq, s);
+             : launch_logits(1, r->H, r->E, x, w_router, bias, lg, xq, s, nullptr);
     if (rc) return hip_status(rc);
     InlineRoute ir{lg, r->gating, r->scale, topk_ids, expert_offsets, pairs, active, topk_w};
     return hip_status(ffn_enqueue(f, xq, topk_ids, topk_w, expert_offsets, pairs, active, shared_scale, y, wsb, &ir,
@@ -672,7 +672,8 @@ int layer_enqueue(const moeq_route_desc* r, const moeq_ffn_desc* f, const float*
     // a small chunk: logits + q8_K(x) in one launch, then the first gate/up
     // launch routes inline (no selection launch)
     double* lg = logits ? logits : (double*)(wsb + L.off_route);
-    if ((rc = launch_logits(r->T, r->H, r->E, x, w_router, bias, lg, xq, s))) return hip_status(rc);
+    if ((rc = launch_logits(r->T, r->H, r->E, x, w_router, bias, lg, xq, s,
+                                 wsb + L.off_route + route_part_off(r->T, r->E, r->H)))) return hip_status(rc);
     InlineRoute ir{lg, r->gating, r->scale, topk_ids, expert_offsets, pairs, active, topk_w};
     return hip_status(ffn_enqueue(f, xq, topk_ids, topk_w, expert_offsets, pairs, active, shared_scale, y, wsb, &ir,
                                   true, s));
@@ -689,7 +690,8 @@ int layer_enqueue(const moeq_route_desc* r, const moeq_ffn_desc* f, const float*
     // captured graph keeps the routed chain on the queue of the launches
     // before it (a chain that changes queue waits about 10 us at each change).
     double* lg = logits ? logits : (double*)(wsb + L.off_route);
-    if ((rc = launch_logits(r->T, r->H, r->E, x, w_router, bias, lg, xq, s))) return hip_status(rc);
+    if ((rc = launch_logits(r->T, r->H, r->E, x, w_router, bias, lg, xq, s,
+                                 wsb + L.off_route + route_part_off(r->T, r->E, r->H)))) return hip_status(rc);
     if (hipEventRecord((hipEvent_t)f->aux_fork, s) != hipSuccess) return MOEQ_E_HIP;
     if ((rc = launch_route(r->T, r->H, r->E, r->k, r->gating, r->scale, x, w_router, bias, lg, topk_ids, topk_w,
                            expert_offsets, pairs, active, xq, wsb + L.off_route, s, mfma ? &plan : nullptr, true)))

@@ -146,8 +146,10 @@ int launch_mfma_ints(int fmt, const void* W, int64_t N, int64_t K, const void* x
 int launch_subdots(int fmt, const void* w, int64_t rows, int64_t cols, const void* xq, int64_t n_x,
                    int32_t* out, hipStream_t s);
 size_t route_ws_bytes(int64_t T, int64_t E, int64_t H);
+// part: scratch of the split-K logits (route workspace at route_part_off), or null
 int launch_logits(int64_t T, int64_t H, int64_t E, const float* x, const float* W, const float* bias,
-                  double* logits, void* xq, hipStream_t s);
+                  double* logits, void* xq, hipStream_t s, void* part);
+size_t route_part_off(int64_t T, int64_t E, int64_t H);
 // One token: RMS pre-norm fused into the router logits and q8_K (H <= kNorm1MaxH).
 constexpr int64_t kNorm1MaxH = 4096;
 int launch_logits_norm1(int64_t H, int64_t E, const float* x, const float* g, double eps, const float* W,

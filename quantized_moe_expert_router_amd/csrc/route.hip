@@ -15,6 +15,7 @@ namespace moeq {
 
 constexpr int kLogitTok = 16;       // tokens per logits tile
 constexpr int kSmallT = 256;        // single-workgroup selection + lists up to this many tokens
+constexpr int kTopkParT = 64;       // from this many tokens the top-k has a launch of its own
 constexpr int kChunkT = 128;        // tokens per chunk of the multi-kernel lists path
 constexpr int kMfmaRouteT = 256;    // from this many tokens the logits run on fp64 matrix cores
 
@@ -649,14 +650,18 @@ __global__ __launch_bounds__(1024) void k_select_small(const double* __restrict_
                                                        int k, int gating, float scale, int32_t* __restrict__ ids,
                                                        float* __restrict__ w, int32_t* __restrict__ offsets,
                                                        int32_t* __restrict__ pairs, int32_t* __restrict__ active,
-                                                       MfmaPlan plan) {
+                                                       MfmaPlan plan, int ids_in) {
   extern __shared__ int lds[];
   int* ids_s = lds;                                           // [T*k]
   int* cnt = ids_s + T * k;                                   // [E]
   int* scan_tmp = cnt + E;                                    // [64]
   const int wv = threadIdx.x >> 6, nw = blockDim.x >> 6;
-  for (int64_t t = wv; t < T; t += nw)
-    topk_row_wave<NPER>(logits + t * E, E, k, gating, scale, ids + t * k, w + t * k, ids_s + t * k);
+  if (ids_in) {   // ids and weights already written by k_topk (one wave per token)
+    for (int64_t p = threadIdx.x; p < T * k; p += blockDim.x) ids_s[p] = gld_i32(ids + p);
+  } else {
+    for (int64_t t = wv; t < T; t += nw)
+      topk_row_wave<NPER>(logits + t * E, E, k, gating, scale, ids + t * k, w + t * k, ids_s + t * k);
+  }
   if (T * k <= kSmallPairs) {
     int* skey = ids_s + T * k;                                // [64]
     int* lact = skey + kSmallPairs;                           // [65]
@@ -788,8 +793,114 @@ __global__ void k_empty_lists(int64_t E, int32_t* offsets, int32_t* active) {
   if (threadIdx.x == 0) active[0] = 0;
 }
 
+// Logits of a chunk of kSplitT to kMfmaRouteT - 1 tokens on fp64 matrix
+// cores, with K split over the grid so that the launch fills the chip: the
+// per-expert kernel above re-reads every token row once per expert (a
+// 200-token chunk at hidden 4096 moves about 0.8 GB from L2 that way), and a
+// 64 x 64 tile over the whole of K leaves all but a few CUs idle.
+// Workgroup (token tile of 16, expert tile of 64, K slice z): each wave one
+// 16 x 16 block, v_mfma_f64_16x16x4f64 on exact fp64 copies of the fp32
+// operands.  Lane l loads 16 bytes of its row (token or expert l % 16) at
+// k0 + 4 (l / 16); step j of the four MFMAs takes component j, so the four
+// steps cover k0 .. k0 + 15 once each, with the same k on both operands.  A
+// row past T or E reloads the last row and its results are dropped.  The
+// slice's sums go to part[z][t][e]; k_logits_sum adds the slices.
+constexpr int kSplitT = 40;          // from this many tokens (below kMfmaRouteT) the split-K logits
+constexpr int kSplitMax = 16;        // K slices at most
+constexpr int kSplitTok = 16, kSplitExp = 64;
+
+struct LogitSplit { int64_t slices, kc; };
+__host__ __device__ inline LogitSplit logit_split(int64_t T, int64_t E, int64_t H) {
+  const int64_t tiles = ((T + kSplitTok - 1) / kSplitTok) * ((E + kSplitExp - 1) / kSplitExp);
+  int64_t sl = (512 + tiles - 1) / tiles;
+  sl = sl < 1 ? 1 : (sl > kSplitMax ? kSplitMax : sl);
+  int64_t kc = (H + sl - 1) / sl;
+  kc = (kc + 15) / 16 * 16;
+  return LogitSplit{(H + kc - 1) / kc, kc};
+}
+inline bool logit_split_ok(int64_t T, int64_t H) { return T >= kSplitT && T < kMfmaRouteT && H % 16 == 0; }
+
+__global__ __launch_bounds__(256) void k_logits_split(const float* __restrict__ x, const float* __restrict__ W,
+                                                      int64_t T, int64_t H, int64_t E, int64_t kc,
+                                                      double* __restrict__ part) {
+  const int wave = threadIdx.x >> 6, lane = lane_id();
+  const int64_t t0 = (int64_t)blockIdx.x * kSplitTok, e0 = (int64_t)blockIdx.y * kSplitExp + 16 * wave;
+  const int64_t kb = (int64_t)blockIdx.z * kc, ke = (kb + kc) < H ? (kb + kc) : H;
+  const int r16 = lane & 15, kq = lane >> 4;
+  const int64_t tr = (t0 + r16) < T ? (t0 + r16) : T - 1;
+  const int64_t er = (e0 + r16) < E ? (e0 + r16) : E - 1;
+  const float* xr = x + tr * H + 4 * kq;
+  const float* wr = W + er * H + 4 * kq;
+  v4d acc = (v4d){0.0, 0.0, 0.0, 0.0};
+  // four 16-wide K steps per round: all eight loads out before the MFMAs
+  for (int64_t k0 = kb; k0 < ke; k0 += 64) {
+    float4 xv[4], wv[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int64_t k = (k0 + 16 * u) < ke ? (k0 + 16 * u) : k0;
+      xv[u] = gld_f4(xr + k);
+      wv[u] = gld_f4(wr + k);
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      if (k0 + 16 * u >= ke) break;   // uniform over the wave
+      acc = __builtin_amdgcn_mfma_f64_16x16x4f64((double)xv[u].x, (double)wv[u].x, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f64_16x16x4f64((double)xv[u].y, (double)wv[u].y, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f64_16x16x4f64((double)xv[u].z, (double)wv[u].z, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f64_16x16x4f64((double)xv[u].w, (double)wv[u].w, acc, 0, 0, 0);
+    }
+  }
+  // result lane l, value r: token 4 r + l / 16, expert l % 16
+  const int64_t e = e0 + r16;
+  double* pz = part + (int64_t)blockIdx.z * T * E;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int64_t t = t0 + 4 * r + kq;
+    if (t < T && e < E) pz[t * E + e] = acc[r];
+  }
+}
+
+// logits[t, e] = ((part[0] + part[1]) + ...) + bias[e], slices in order;
+// workgroups past the outputs quantise x to q8_K (one wave per 256-block).
+__global__ __launch_bounds__(256) void k_logits_sum(const double* __restrict__ part, int64_t slices, int64_t T,
+                                                    int64_t E, const float* __restrict__ bias,
+                                                    double* __restrict__ logits, const float* __restrict__ x,
+                                                    int64_t H, uint8_t* __restrict__ xq) {
+  const int64_t nout = T * E, nb = (nout + 255) / 256;
+  if ((int64_t)blockIdx.x >= nb) {
+    quantize_block_wave(x, H, ((int64_t)blockIdx.x - nb) * 4 + (threadIdx.x >> 6), T * (H / 256), xq);
+    return;
+  }
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= nout) return;
+  double p[kSplitMax];
+#pragma unroll
+  for (int z = 0; z < kSplitMax; ++z) p[z] = z < slices ? part[z * nout + i] : 0.0;
+  double v = p[0];
+#pragma unroll
+  for (int z = 1; z < kSplitMax; ++z)
+    if (z < slices) v += p[z];
+  if (bias) v += (double)bias[i % E];
+  logits[i] = v;
+}
+
+size_t logit_part_bytes(int64_t T, int64_t E, int64_t H) {
+  return logit_split_ok(T, H) ? (size_t)logit_split(T, E, H).slices * T * E * sizeof(double) : 0;
+}
+
 int launch_logits(int64_t T, int64_t H, int64_t E, const float* x, const float* W, const float* bias,
-                  double* logits, void* xq, hipStream_t s) {
+                  double* logits, void* xq, hipStream_t s, void* part) {
+  if (part != nullptr && logit_split_ok(T, H)) {
+    const LogitSplit sp = logit_split(T, E, H);
+    dim3 g((unsigned)((T + kSplitTok - 1) / kSplitTok), (unsigned)((E + kSplitExp - 1) / kSplitExp),
+           (unsigned)sp.slices);
+    hipLaunchKernelGGL(k_logits_split, g, dim3(256), 0, s, x, W, T, H, E, sp.kc, (double*)part);
+    if (hipGetLastError() != hipSuccess) return -1;
+    const int64_t nq = xq ? (T * (H / 256) + 3) / 4 : 0;
+    hipLaunchKernelGGL(k_logits_sum, dim3((unsigned)((T * E + 255) / 256 + nq)), dim3(256), 0, s,
+                       (const double*)part, sp.slices, T, E, bias, logits, x, H, (uint8_t*)xq);
+    return hipGetLastError() == hipSuccess ? 0 : -1;
+  }
   if (T >= kMfmaRouteT) {
     // many tokens: the router is a dense contraction (matrix cores); q8_K(x)
     // in its own launch
@@ -818,7 +929,7 @@ int launch_logits_norm1(int64_t H, int64_t E, const float* x, const float* g, do
 // approximations there), the chunk histograms (more than kSmallT tokens), and
 // for the fast path the bf16 hi / lo planes of x and W and their row norms.
 struct RouteLayout {
-  size_t off_hist, off_xhl, off_whl, off_nx, off_nw, total;
+  size_t off_hist, off_xhl, off_whl, off_nx, off_nw, off_part, total;
 };
 // (up to 1024 experts: 16 logits per lane in registers; the token row in
 // registers: H <= 2048)
@@ -836,9 +947,11 @@ RouteLayout route_layout(int64_t T, int64_t E, int64_t H) {
     L.off_nx = o;  o += align256((size_t)T * sizeof(double));
     L.off_nw = o;  o += align256((size_t)E * sizeof(double));
   }
+  L.off_part = o; o += align256(logit_part_bytes(T, E, H));
   L.total = o;
   return L;
 }
+size_t route_part_off(int64_t T, int64_t E, int64_t H) { return route_layout(T, E, H).off_part; }
 
 size_t route_ws_bytes(int64_t T, int64_t E, int64_t H) { return route_layout(T, E, H).total; }
 
@@ -890,15 +1003,27 @@ int launch_route(int64_t T, int64_t H, int64_t E, int k, int gating, float scale
   double* lg = logits ? logits : reinterpret_cast<double*>(wsb);
   if (have_logits && (logits == nullptr || T > kSmallT)) return -2;
   if (!have_logits) {
-    if (int rc = launch_logits(T, H, E, x, W, bias, lg, xq, s)) return rc;
+    if (int rc = launch_logits(T, H, E, x, W, bias, lg, xq, s, wsb + RL.off_part)) return rc;
   }
   if (T <= kSmallT) {
     size_t lds = (size_t)(T * k + 2 * E + 2 * kSmallPairs + 3) * sizeof(int);   // either list path
     // up to 64 pairs: one wave per token and one for the lists, so fewer
     // waves (cheaper barriers); more pairs: block scans over 1024 threads
     const unsigned nt = T * k <= kSmallPairs ? (unsigned)(64 * std::min<int64_t>(16, std::max<int64_t>(4, T))) : 1024u;
+    // from kTopkParT tokens the top-k runs one wave per token in its own launch
+    // (the selection workgroup would take the tokens 16 at a time)
+    const int ids_in = T >= kTopkParT ? 1 : 0;
+    if (ids_in) {
+#define MOEQ_TOPK(N) hipLaunchKernelGGL(k_topk<N>, dim3((unsigned)((T + 3) / 4)), dim3(256), 0, s, lg, T, E, k, \
+                                         gating, scale, ids, w)
+      if (E <= 256) MOEQ_TOPK(4);
+      else if (E <= 512) MOEQ_TOPK(8);
+      else if (E <= 1024) MOEQ_TOPK(16);
+      else MOEQ_TOPK(64);
+#undef MOEQ_TOPK
+    }
 #define MOEQ_SEL(N) hipLaunchKernelGGL(k_select_small<N>, dim3(1), dim3(nt), lds, s, lg, T, E, k, gating, \
-                                        scale, ids, w, offsets, pairs, active, pl)
+                                        scale, ids, w, offsets, pairs, active, pl, ids_in)
     if (E <= 256) MOEQ_SEL(4);
     else if (E <= 512) MOEQ_SEL(8);
     else if (E <= 1024) MOEQ_SEL(16);
