@@ -15,7 +15,7 @@ namespace moeq {
 
 constexpr int kLogitTok = 16;       // tokens per logits tile
 constexpr int kSmallT = 256;        // single-workgroup selection + lists up to this many tokens
-constexpr int kTopkParT = 64;       // from this many tokens the top-k has a launch of its own
+constexpr int kTopkParT = 24;       // from this many tokens the top-k has a launch of its own
 constexpr int kChunkT = 128;        // tokens per chunk of the multi-kernel lists path
 constexpr int kMfmaRouteT = 256;    // from this many tokens the logits run on fp64 matrix cores
 
