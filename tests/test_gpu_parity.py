@@ -332,6 +332,35 @@ def test_route_many_tokens_ragged(T, E, H, with_bias):
     assert np.array_equal(xq.cpu().numpy(), oracle.quantize_q8K(x))
 
 
+@pytest.mark.parametrize("T,E,H,with_bias", [(24, 64, 256, False), (40, 70, 512, True), (63, 256, 4096, True),
+                                              (100, 64, 272, False), (48, 32, 100, True), (255, 513, 2048, True)])
+def test_route_mid_chunk(T, E, H, with_bias):
+    """24 to 255 tokens: the top-k in a launch of its own before the lists,
+    and from 40 tokens (hidden a multiple of 16) the split-K logits whose
+    slice-sum launch also quantises x; ragged token and expert tiles.
+    Logits, ids, weights, lists and q8_K(x) must match."""
+    say("route mid chunk", T, E, H, with_bias)
+    rng = np.random.default_rng(7 * T + E)
+    x = rng.standard_normal((T, H)).astype(np.float32)
+    W = (rng.standard_normal((E, H)) * 0.02).astype(np.float32)
+    b = (rng.standard_normal(E) * 0.1).astype(np.float32) if with_bias else None
+    k = 6
+    xq = torch.empty(T * (H // 256) * moeq.Q8K_BYTES, dtype=torch.uint8, device="cuda") if H % 256 == 0 else None
+    out = moeq.moeq_route(dev(x), dev(W), None if b is None else dev(b), k, syn.SOFTMAX_TOPK, x_q8K=xq)
+    torch.cuda.synchronize()
+    lg, ids, w = oracle.route(x, W, b, k, syn.SOFTMAX_TOPK)
+    assert np.allclose(out.logits.cpu().numpy(), lg, rtol=0, atol=1e-12)
+    assert np.array_equal(out.ids.cpu().numpy(), ids)
+    check_w(out.w.cpu().numpy(), w)
+    off, pairs, active = oracle.lists(ids, E)
+    assert np.array_equal(out.offsets.cpu().numpy(), off)
+    assert np.array_equal(out.pairs.cpu().numpy()[:T * k], pairs)
+    act = out.active.cpu().numpy()
+    assert np.array_equal(act[:1 + act[0]], active)
+    if xq is not None:
+        assert np.array_equal(xq.cpu().numpy().reshape(T, -1), oracle.quantize_q8K(x).reshape(T, -1))
+
+
 def _fast_route_case(variant):
     """Inputs for the router without a logits output (bf16 contraction plus
     exact rescoring): (x, W, b, k, gating)."""
